@@ -1,0 +1,44 @@
+"""Seeded synthetic inputs shared by the tests, the on-device sweep and bench.py.
+
+This module holds no step of the method: it only draws random numbers with
+torch's CPU generator. The distributions stand in for the pages' workload (randn bf16
+activations and weights of DeepSeek-V3 projection shapes, block GEMM benchmark page §4.1):
+  W  = randn(N, K) * 0.02                       fp32, generator seed
+  cols = randperm(K)[:round(0.02 K)]            generator seed + 1 (outlier channels)
+  X  = randn(M_max, K); X[:, cols] *= 20; bf16  generator seed + 2
+Each smaller M takes the first M rows of the M_max draw, so inputs nest across M.
+"""
+from __future__ import annotations
+
+import torch
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def weights(N: int, K: int, seed: int = 0) -> torch.Tensor:
+    """fp32 [N, K] ~ N(0, 0.02^2)."""
+    return torch.randn((N, K), generator=_gen(seed), dtype=torch.float32) * 0.02
+
+
+def outlier_columns(K: int, seed: int = 0, frac: float = 0.02) -> torch.Tensor:
+    n = int(round(frac * K))
+    return torch.randperm(K, generator=_gen(seed + 1))[:n]
+
+
+def activations(M: int, K: int, seed: int = 0, m_max: int | None = None) -> torch.Tensor:
+    """bf16 [M, K] ~ N(0, 1) with 2% outlier columns scaled x20 (rows 0..M-1 of an
+    m_max-row draw)."""
+    m_max = max(M, m_max or M)
+    x = torch.randn((m_max, K), generator=_gen(seed + 2), dtype=torch.float32)
+    cols = outlier_columns(K, seed)
+    x[:, cols] *= 20.0
+    return x[:M].to(torch.bfloat16).contiguous()
+
+
+def bf16_bits(x: torch.Tensor):
+    """The uint16 bit patterns of a bf16 tensor, as a numpy array (for the CPU oracle)."""
+    return x.contiguous().view(torch.int16).numpy().view("uint16")

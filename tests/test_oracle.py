@@ -1,0 +1,332 @@
+"""Pins of the CPU oracle against things other than itself (CPU only, "not gpu").
+
+Each test names what fixes the expected value: the e4m3fn format definition, a library
+codec (torch.float8_e4m3fn, numpy int64/fp64 matmul), brute force, closed forms, exact
+special cases, or figures printed on the pages.
+"""
+import json
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_w8a8_amd import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden")
+
+
+def _f(v):
+    return float(v) if not isinstance(v, str) else float(v)
+
+
+# ------------------------------------------------------------------------ codec
+
+def test_decode_all_codes_format_definition(orc):
+    """P1: decode follows the format (subnormals m*2^-9, normals (8+m)*2^(E-10)), is
+    strictly increasing over 0x00..0x7E and mirrors in sign; 0x7F/0xFF are NaN."""
+    vals = [orc.e4m3_decode(c) for c in range(256)]
+    assert np.isnan(vals[0x7F]) and np.isnan(vals[0xFF])
+    assert vals[0x7E] == 448.0 and vals[0x08] == 2.0 ** -6 and vals[0x01] == 2.0 ** -9
+    assert vals[0x07] == 7 * 2.0 ** -9 and vals[0x38] == 1.0 and vals[0x00] == 0.0
+    pos = vals[:0x7F]
+    assert all(b > a for a, b in zip(pos, pos[1:]))
+    for c in range(0x7F):
+        assert vals[c | 0x80] == -vals[c]
+    assert np.signbit(vals[0x80])
+
+
+def test_decode_matches_torch_float8(orc):
+    """P1: decode equals the library codec torch.float8_e4m3fn on all 256 codes."""
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([orc.e4m3_decode(c) for c in range(256)])
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    assert np.array_equal(ref[~both_nan], got[~both_nan])
+
+
+def test_roundtrip_all_codes(orc):
+    """P1: every non-NaN code decodes and re-encodes to itself (including -0 = 0x80)."""
+    for c in range(256):
+        v = orc.e4m3_decode(c)
+        if np.isnan(v):
+            assert orc.e4m3_encode(np.float32("nan")) == 0x7F
+            continue
+        assert orc.e4m3_encode(np.float32(v)) == c, hex(c)
+
+
+def test_worked_encodings(orc):
+    """P3: worked encodings derived from the format definition (tests/golden)."""
+    g = json.load(open(os.path.join(GOLDEN, "e4m3_worked.json")))
+    for case in g["cases"]:
+        assert orc.e4m3_encode(np.float32(_f(case["x"]))) == int(case["code"], 16), case
+    for case in g["int8_cases"]:
+        assert orc.int8_encode(np.float32(_f(case["x"]))) == case["code"], case
+
+
+def test_encode_matches_torch_in_range(orc):
+    """P2 (library): within |x| <= 464 the saturating reading and torch's non-saturating
+    float8_e4m3fn cast agree; compare on every bf16 pattern in range and on fp32 values
+    that sit on, just above and just below each rounding midpoint."""
+    bits = np.arange(1 << 16, dtype=np.uint32) << 16
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) <= 464)]
+    v = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    v = v[np.isfinite(v)]
+    v = np.unique(v)
+    mids = ((v[1:].astype(np.float64) + v[:-1]) / 2).astype(np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(np.inf)),
+                           np.nextafter(mids, np.float32(-np.inf))])
+    near = near[np.abs(near) <= 464]
+    rng = np.random.default_rng(0)
+    rnd = (rng.standard_normal(200000) * 50).astype(np.float32)
+    rnd = rnd[np.abs(rnd) <= 464]
+    allx = np.concatenate([x, near, -near, rnd])
+    ref = torch.from_numpy(allx).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = orc.e4m3_encode_array(allx)
+    assert np.array_equal(got, ref)
+
+
+def test_encode_exhaustive_bruteforce(orc, tmp_path):
+    """P2 (brute force): all 2^32 fp32 patterns against a nearest-value search written
+    from the format definition (tests/native/e4m3_exhaustive.c)."""
+    exe = tmp_path / "e4m3_exhaustive"
+    src = os.path.join(HERE, "native", "e4m3_exhaustive.c")
+    libdir = os.path.dirname(orc.LIB_PATH)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-std=c11", "-o", str(exe), src, "-L" + libdir,
+                    "-loracle", "-Wl,-rpath," + libdir, "-lm"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0 and r.stdout.strip() == "0", r.stderr
+
+
+def test_int8_encode_library(orc):
+    """int8 codes equal numpy's round-half-even (np.rint) clamped to [-127, 127]."""
+    rng = np.random.default_rng(1)
+    y = np.concatenate([(rng.standard_normal(100000) * 80).astype(np.float32),
+                        np.arange(-300, 300, 0.5, dtype=np.float32)])
+    ref = np.clip(np.rint(y.astype(np.float64)), -127, 127).astype(np.int8)
+    assert np.array_equal(orc.int8_encode_array(y), ref)
+
+
+def test_bf16_rne_library(orc):
+    """bf16 rounding equals torch's float32 -> bfloat16 cast (round to nearest even)."""
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 1e3,
+                        (np.arange(1 << 16, dtype=np.uint32) << 16 | 0x8000).view(np.float32),
+                        (np.arange(1 << 16, dtype=np.uint32) << 16 | 0x7FFF).view(np.float32)])
+    x = x[np.isfinite(x)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.f32_to_bf16_bits_array(x), ref)
+
+
+# ------------------------------------------------------------------ quantizers
+
+def _dequant_fp8(q):
+    return torch.from_numpy(np.ascontiguousarray(q)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_group_quant_invariants(orc):
+    """P4: per group, scale = amax/448 (amax from numpy), the largest |code| is 0x7E
+    (decodes to 448), and every code is the e4m3 value nearest to x/scale (brute force
+    over all 254 finite codes)."""
+    x = synth.activations(6, 1536, seed=3)
+    bits = synth.bf16_bits(x)
+    q, s = orc.quant_groups(bits)
+    xf = x.float().numpy().reshape(6, 12, 128)
+    amax = np.abs(xf).max(axis=2)
+    assert np.array_equal(s, (amax / np.float32(448)).astype(np.float32))
+    mags = (q.reshape(6, 12, 128) & 0x7F).max(axis=2)
+    assert (mags == 0x7E).all()
+    codes = np.arange(256, dtype=np.uint8)
+    vals = _dequant_fp8(codes)
+    finite = np.isfinite(vals)
+    y = (xf / s[:, :, None]).astype(np.float32).astype(np.float64).ravel()
+    deq = _dequant_fp8(q).ravel()
+    # nearest: no finite code is strictly closer to y than the chosen one
+    dist = np.abs(vals[finite][None, :] - y[:, None]).min(axis=1)
+    assert np.array_equal(np.abs(deq - y), dist)
+
+
+def test_group_quant_dequant_error_bound(orc):
+    """P4: |dec(q)*s - x| <= half a code step: 2^-4 |x| for normal codes, 2^-10 s below."""
+    x = synth.activations(16, 7168, seed=4)
+    q, s = orc.quant_groups(synth.bf16_bits(x))
+    xf = x.double().numpy()
+    srep = np.repeat(s.astype(np.float64), 128, axis=1)
+    err = np.abs(_dequant_fp8(q) * srep - xf)
+    bound = np.maximum(2.0 ** -4 * np.abs(xf), 2.0 ** -10 * srep) * (1 + 1e-6)
+    assert (err <= bound).all()
+
+
+def test_group_quant_special_groups(orc):
+    """All-zero group -> codes 0 and scale eps/448; -0 keeps its sign; a NaN group gets a
+    NaN scale and NaN codes; an Inf group gets an Inf scale, signed-zero codes and NaN
+    codes for the infinities; int8: max |q| = 127 and scale = amax/127."""
+    x = np.zeros((4, 256), dtype=np.float32)
+    x[0, 5] = -0.0
+    x[1, :128] = np.linspace(-3, 3, 128)
+    x[1, 200] = np.nan
+    x[2, 3] = np.inf
+    x[2, 4] = -2.0
+    x[2, 130] = -np.inf
+    x[3, :] = np.linspace(-1, 5, 256)
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bits = bits.copy()
+    bits[0, 5] = 0x8000
+    q, s = orc.quant_groups(bits)
+    eps = np.float32(1e-10)
+    assert s[0, 0] == np.float32(eps / np.float32(448)) and s[0, 1] == s[0, 0]
+    assert q[0, 5] == 0x80 and (np.delete(q[0], 5) == 0).all()
+    assert np.isnan(s[1, 1]) and (q[1, 128:] == 0x7F).all() and not np.isnan(s[1, 0])
+    assert np.isinf(s[2, 0]) and np.isinf(s[2, 1])
+    assert q[2, 3] == 0x7F and q[2, 4] == 0x80 and q[2, 130] == 0x7F and q[2, 0] == 0x00
+    qi, si = orc.quant_groups(bits, qtype=orc.INT8)
+    assert np.abs(qi[3]).max() == 127 and si[3, 1] == np.float32(np.float32(5.0) / np.float32(127))
+    assert (qi[1, 128:] == 0).all() and np.isnan(si[1, 1])
+
+
+def test_block_quant_invariants(orc):
+    """P4 for weight blocks: scale = block amax / 448, one 0x7E-magnitude code per block
+    at least, and codes nearest to w/scale (checked by the dequant error bound)."""
+    w = synth.weights(256, 384, seed=5).numpy()
+    q, s = orc.quant_blocks(w)
+    blocks = w.reshape(2, 128, 3, 128).transpose(0, 2, 1, 3)
+    amax = np.abs(blocks).max(axis=(2, 3))
+    assert np.array_equal(s, (amax / np.float32(448)).astype(np.float32))
+    qb = q.reshape(2, 128, 3, 128).transpose(0, 2, 1, 3)
+    assert ((qb & 0x7F).max(axis=(2, 3)) == 0x7E).all()
+    srep = np.repeat(np.repeat(s.astype(np.float64), 128, 0), 128, 1)
+    err = np.abs(_dequant_fp8(q) * srep - w)
+    assert (err <= np.maximum(2.0 ** -4 * np.abs(w), 2.0 ** -10 * srep) * (1 + 1e-6)).all()
+    qi, si = orc.quant_blocks(w, qtype=orc.INT8)
+    assert np.abs(qi).max() == 127
+
+
+# ------------------------------------------------------------------------ GEMM
+
+def _quantized_case(M, N, K, seed, qtype):
+    import oracle as orc
+    x = synth.activations(M, K, seed=seed)
+    w = synth.weights(N, K, seed=seed).numpy()
+    qa, sa = orc.quant_groups(synth.bf16_bits(x), qtype=qtype)
+    qw, sw = orc.quant_blocks(w, qtype=qtype)
+    return qa, sa, qw, sw
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (3, 256, 384), (8, 128, 384), (8, 256, 128)])
+def test_gemm_vs_fp64_dequant_matmul(orc, M, N, K):
+    """P5: against an fp64 dequantize-then-matmul written with library routines (torch's
+    e4m3fn decode, numpy fp64 matmul): |C32 - D| <= 1e-5 * rms(D)."""
+    qa, sa, qw, sw = _quantized_case(M, N, K, 7, orc.FP8)
+    c32, c16 = orc.block_gemm(qa, sa, qw, sw)
+    a = _dequant_fp8(qa) * np.repeat(sa.astype(np.float64), 128, axis=1)
+    b = _dequant_fp8(qw) * np.repeat(np.repeat(sw.astype(np.float64), 128, 0), 128, 1)
+    d = a @ b.T
+    rms = np.sqrt((d * d).mean())
+    assert np.abs(c32 - d).max() <= 1e-5 * rms
+    # the oracle's own brute force agrees with the library one
+    assert np.abs(orc.dequant_gemm_f64(qa, sa, qw, sw) - d).max() <= 1e-12 * rms
+
+
+def test_gemm_exact_integer_case(orc):
+    """P6: codes restricted to e4m3 integers |v| <= 8 and every scale 2^-4: every partial
+    sum is an integer multiple of 2^-8 below 2^24 ulps, so any correct evaluation equals
+    the integer matmul (numpy int64) times 2^-8 exactly, and bf16 out = torch's RNE cast."""
+    rng = np.random.default_rng(11)
+    ints = np.arange(-8, 9)
+    enc = {int(v): torch.tensor([float(v)]).to(torch.float8_e4m3fn).view(torch.uint8).item()
+           for v in ints}
+    M, N, K = 5, 256, 512
+    ia = rng.integers(-8, 9, size=(M, K))
+    iw = rng.integers(-8, 9, size=(N, K))
+    qa = np.vectorize(enc.get)(ia).astype(np.uint8)
+    qw = np.vectorize(enc.get)(iw).astype(np.uint8)
+    sa = np.full((M, K // 128), 2.0 ** -4, dtype=np.float32)
+    sw = np.full((N // 128, K // 128), 2.0 ** -4, dtype=np.float32)
+    c32, c16 = orc.block_gemm(qa, sa, qw, sw)
+    exact = (ia.astype(np.int64) @ iw.T.astype(np.int64)).astype(np.float64) * 2.0 ** -8
+    assert np.array_equal(c32.astype(np.float64), exact)
+    ref16 = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).view(torch.int16)
+    assert np.array_equal(c16, ref16.numpy().view(np.uint16))
+
+
+def test_gemm_one_hot_rows(orc):
+    """P6: a token row that is the code 1.0 at column k (scale 1) reproduces the weight
+    column k dequantized: C[m, n] = fp32(dec(qw[n, k]) * sw[n/128, k/128])."""
+    _, _, qw, sw = _quantized_case(1, 256, 384, 13, orc.FP8)
+    M, K = 4, 384
+    ks = [0, 127, 200, 383]
+    qa = np.zeros((M, K), dtype=np.uint8)
+    for m, k in enumerate(ks):
+        qa[m, k] = 0x38
+    sa = np.ones((M, K // 128), dtype=np.float32)
+    c32, _ = orc.block_gemm(qa, sa, qw, sw)
+    for m, k in enumerate(ks):
+        ref = (_dequant_fp8(qw[:, k]).astype(np.float32) * np.repeat(sw[:, k // 128], 128))
+        assert np.array_equal(c32[m], ref.astype(np.float32))
+
+
+def test_int8_partials_vs_numpy(orc):
+    """P7: int8 per-block int32 partials equal numpy int64 matmuls of the code blocks."""
+    qa, sa, qw, sw = _quantized_case(7, 256, 512, 17, orc.INT8)
+    part = orc.block_partials_i32(qa, qw)
+    for kb in range(4):
+        ref = qa[:, kb * 128:(kb + 1) * 128].astype(np.int64) @ \
+            qw[:, kb * 128:(kb + 1) * 128].astype(np.int64).T
+        assert np.array_equal(part[kb].astype(np.int64), ref)
+    # and the int8 GEMM is the exact partials rescaled: compare with fp64 dequant matmul
+    c32, _ = orc.block_gemm(qa, sa, qw, sw, qtype=orc.INT8)
+    d = orc.dequant_gemm_f64(qa, sa, qw, sw, qtype=orc.INT8)
+    a = qa.astype(np.float64) * np.repeat(sa.astype(np.float64), 128, axis=1)
+    b = qw.astype(np.float64) * np.repeat(np.repeat(sw.astype(np.float64), 128, 0), 128, 1)
+    assert np.abs(d - a @ b.T).max() <= 1e-12 * np.abs(d).max()
+    assert np.abs(c32 - d).max() <= 1e-5 * np.sqrt((d * d).mean())
+
+
+def test_gemm_sampled_matches_full(orc):
+    qa, sa, qw, sw = _quantized_case(9, 384, 256, 19, orc.FP8)
+    c32, _ = orc.block_gemm(qa, sa, qw, sw)
+    rng = np.random.default_rng(0)
+    ms = rng.integers(0, 9, 100)
+    ns = rng.integers(0, 384, 100)
+    assert np.array_equal(orc.block_gemm_sampled(qa, sa, qw, sw, ms, ns), c32[ms, ns])
+
+
+def test_calc_diff_closed_forms():
+    """calc_diff (block GEMM benchmark page §4.4): 0 for equal tensors, 2 for x vs -x,
+    1 - 2*2/(1+4) = 0.2 for x vs 2x."""
+    from oracle.metrics import calc_diff
+    x = np.random.default_rng(3).standard_normal(1000)
+    assert calc_diff(x, x) == pytest.approx(0.0, abs=1e-15)
+    assert calc_diff(x, -x) == pytest.approx(2.0)
+    assert calc_diff(x, 2 * x) == pytest.approx(0.2)
+
+
+def test_calc_diff_matches_pages_accuracy(orc):
+    """P8: on the pages' setup (randn bf16 A (64, 7168) and B (4096, 7168), seed 42, B per
+    128x128 block and A per 1x128 group quantized to e4m3fn, C_ref = bf16 A @ B^T) the
+    pages print an average calc_diff of 0.000684 for all three kernels (block GEMM benchmark
+    page §3.3). The oracle's bf16 output must land at that level: [6.0e-4, 7.7e-4]."""
+    from oracle.metrics import bf16_bits_to_f32, calc_diff
+    g = torch.Generator().manual_seed(42)
+    m, n, k = 64, 4096, 7168
+    A = torch.randn((m, k), generator=g).to(torch.bfloat16)
+    B = torch.randn((n, k), generator=g).to(torch.bfloat16)
+    c_ref = (A @ B.t()).float().numpy()
+    qa, sa = orc.quant_groups(synth.bf16_bits(A))
+    qw, sw = orc.quant_blocks(B.float().numpy())
+    _, c16 = orc.block_gemm(qa, sa, qw, sw)
+    d = calc_diff(bf16_bits_to_f32(c16), c_ref)
+    assert 6.0e-4 <= d <= 7.7e-4, d
+
+
+# ------------------------------------------------------------------ selection
+
+def test_nearest_m_rule_pages_examples():
+    """P9: the config page's examples (M=37 -> 32, M=2050 -> 2048) and tie/end cases."""
+    from oracle.select import nearest_bucket
+    g = json.load(open(os.path.join(GOLDEN, "nearest_m.json")))
+    for m, want in g["examples"] + g["ties"] + g["ends"]:
+        assert nearest_bucket(m, g["grid"]) == want, (m, want)
