@@ -1,0 +1,302 @@
+"""Benchmark of the block-scaled W8A8 hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: for every M of the
+workload, per-token-group quantization of the bf16 activations (bfq_quant_tokens) followed
+by the block-scaled GEMM against pre-quantized weights (bfq_block_gemm, tile chosen by
+bfq_select_tile). Weights are quantized on the device before timing (the offline step of
+the block GEMM benchmark page §4.1). Inputs are resident in HBM when timing starts.
+
+Default workload: N=24576, K=7168 (DeepSeek-V3 wide MoE up-projection) over the 18-point M
+grid 1..4096. To keep the weight stream honest against the 256 MB Infinity Cache, launches
+rotate over R copies of the weights (default 2 -> 352 MB working set).
+
+Prints ONE JSON line (metric, value = GEMM TFLOPS over the whole step including the
+quantization time, per-M detail, roofline of the dominant kernel, CPU-oracle baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+if REPO not in sys.path:
+    sys.path.insert(0, REPO)
+
+METRIC = "block-FP8 GEMM TFLOPS & HBM GB/s vs M (1-4096) at DeepSeek-V3 N/K, 1 MI355X"
+
+M_GRID = [1, 2, 4, 8, 16, 24, 32, 48, 64, 96, 128, 256, 512, 1024, 1536, 2048, 3072, 4096]
+WORKLOADS = {
+    "mgrid": {"shapes": [(24576, 7168)], "M": M_GRID, "qtype": "fp8",
+              "desc": "block-FP8 linear N=24576 K=7168, M grid 1..4096 (18 points): "
+                      "token-group quant + block GEMM per M"},
+    "decode": {"shapes": [(7168, 1536), (1536, 7168)],
+               "M": [1, 2, 4, 8, 16, 24, 32, 48, 64, 96, 128], "qtype": "fp8",
+               "desc": "decode sweep (N,K) in {(7168,1536),(1536,7168)}, M 1..128"},
+    "dense": {"shapes": [(4096, 7168), (7168, 18432), (18432, 7168)], "M": [8, 64, 128, 4096],
+              "qtype": "fp8", "desc": "dense comparison shapes, M in {8,64,128,4096}"},
+    "int8": {"shapes": [(1536, 7168)], "M": [1, 16, 128, 1024, 4096], "qtype": "int8",
+             "desc": "int8_w8a8 block variant N=1536 K=7168"},
+    "tiny": {"shapes": [(1536, 1536)], "M": [8], "qtype": "fp8", "desc": "M=8 N=1536 K=1536"},
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def tile_key(t) -> str:
+    d = t.as_dict()
+    return "v{variant}_bm{bm}_bn{bn}_w{waves_m}x{waves_n}_s{stages}_g{group_m}_k{split_k}".format(**d)
+
+
+def run_gpu(args, wl):
+    import torch
+
+    from block_scaled_w8a8_amd import bfq, perf, synth
+
+    dev = torch.device("cuda:0")
+    qd = bfq.BFQ_E4M3FN if wl["qtype"] == "fp8" else bfq.BFQ_INT8
+    m_max = max(wl["M"])
+    shapes = []
+    host = {}
+    for (N, K) in wl["shapes"]:
+        log(f"[bench] setup N={N} K={K}: generating and quantizing weights on the device")
+        w = synth.weights(N, K, seed=0)
+        x = synth.activations(m_max, K, seed=0)
+        wd = w.to(dev)
+        copies = []
+        for r in range(args.rotate):
+            qw, sw = bfq.quant_weight_blocks(wd, q_dtype=qd)
+            copies.append((qw, sw))
+        del wd
+        xd = x.to(dev)
+        qa = torch.empty((m_max, K), dtype=torch.uint8 if qd == bfq.BFQ_E4M3FN else torch.int8,
+                         device=dev)
+        sa = torch.empty((m_max, K // 128), dtype=torch.float32, device=dev)
+        out = torch.empty((m_max, N), dtype=torch.bfloat16, device=dev)
+        plans = []
+        for M in wl["M"]:
+            st, tile = bfq.bfq_select_tile(M, N, K, qd, bfq.BFQ_BF16)
+            ws_bytes = bfq.bfq_gemm_workspace_bytes(M, N, K, tile)
+            plans.append((M, tile, ws_bytes, st))
+        ws_max = max(p[2] for p in plans)
+        ws = torch.empty(max(ws_max, 16), dtype=torch.uint8, device=dev)
+        shapes.append(dict(N=N, K=K, copies=copies, xd=xd, qa=qa, sa=sa, out=out, plans=plans,
+                           ws=ws, ws_max=ws_max))
+        host[(N, K)] = (w, x)
+    torch.cuda.synchronize()
+
+    launch_counter = [0]
+
+    def one_step(events=None):
+        for sh in shapes:
+            N, K = sh["N"], sh["K"]
+            for (M, tile, ws_bytes, _st) in sh["plans"]:
+                qw, sw = sh["copies"][launch_counter[0] % len(sh["copies"])]
+                launch_counter[0] += 1
+                if events is not None:
+                    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                    e0.record()
+                bfq.bfq_quant_tokens(sh["xd"][:M], sh["qa"][:M], sh["sa"][:M],
+                                     scale_ld=K // 128)
+                if events is not None:
+                    e1.record()
+                bfq.bfq_block_gemm(sh["qa"][:M], sh["sa"][:M], qw, sw, sh["out"][:M],
+                                   a_scale_ld=K // 128, tile=tile, workspace=sh["ws"],
+                                   workspace_bytes=sh["ws_max"])
+                if events is not None:
+                    e2.record()
+                    events.append((N, K, M, tile_key(tile), e0, e1, e2))
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    eager_out = [sh["out"].clone() for sh in shapes]
+
+    # One step captured as a HIP graph: the timed region replays it, so host launch cost
+    # (ctypes + Python, ~10 us per call) does not leak into the measurement.
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        launch_counter[0] = 0
+        with torch.cuda.graph(graph):
+            one_step()
+        torch.cuda.synchronize()
+
+    def replay():
+        if graph is not None:
+            graph.replay()
+        else:
+            one_step()
+
+    # timed region: wall clock around exactly `steps` steps, fenced by synchronize
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for sh, ref in zip(shapes, eager_out):          # replayed graph == eager result
+        if not torch.equal(sh["out"], ref):
+            raise RuntimeError("graph replay output differs from the eager step")
+
+    # Per-launch durations: HIP events around every launch on the launch stream. A spin
+    # kernel holds the stream while the host enqueues the step, so the events time the
+    # kernels back to back rather than the host's launch cadence.
+    spin_ratio = None
+    if hasattr(torch.cuda, "_sleep"):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        spin_ratio = a.elapsed_time(b) * 1e-3 / 1_000_000      # seconds per spin cycle
+    events = []
+    enqueue_s = 0.002
+    for _ in range(args.steps):
+        torch.cuda.synchronize()
+        if spin_ratio:
+            torch.cuda._sleep(int(2.0 * enqueue_s / spin_ratio))
+        h0 = time.perf_counter()
+        one_step(events)
+        enqueue_s = max(enqueue_s, time.perf_counter() - h0)
+    torch.cuda.synchronize()
+
+    per = {}
+    for (N, K, M, key, e0, e1, e2) in events:
+        r = per.setdefault((N, K, M), {"key": key, "q": [], "g": []})
+        r["q"].append(e0.elapsed_time(e1) * 1e-3)
+        r["g"].append(e1.elapsed_time(e2) * 1e-3)
+
+    flops_step = sum(perf.gemm_flops(M, sh["N"], sh["K"]) for sh in shapes
+                     for (M, *_r) in sh["plans"])
+    step_s = wall / args.steps
+    rows = []
+    groups = {}
+    for sh in shapes:
+        N, K = sh["N"], sh["K"]
+        for (M, tile, ws_bytes, st) in sh["plans"]:
+            r = per[(N, K, M)]
+            g = sum(r["g"]) / len(r["g"])
+            q = sum(r["q"]) / len(r["q"])
+            rows.append({
+                "M": M, "N": N, "K": K, "tile": tile.as_dict(), "tuned": st == 0,
+                "gemm_us": round(g * 1e6, 2), "quant_us": round(q * 1e6, 2),
+                "tflops": round(perf.tflops(M, N, K, g), 2),
+                "gbs_page": round(perf.gbs_page(M, N, K, g), 1),
+                "gbs_all": round(perf.gbs_all(M, N, K, g), 1),
+                "bound": perf.bound(M, N, K),
+                "roofline_frac": round(perf.roofline_time_s(M, N, K) / g, 4),
+                "quant_gbs": round(perf.quant_bytes(M, K) / q / 1e9, 1),
+            })
+            gr = groups.setdefault(r["key"], {"t": 0.0, "n": 0, "flops": 0.0, "bytes": 0.0})
+            gr["t"] += sum(r["g"])
+            gr["n"] += len(r["g"])
+            gr["flops"] += perf.gemm_flops(M, N, K) * len(r["g"])
+            gr["bytes"] += perf.gemm_bytes_all(M, N, K) * len(r["g"])
+    dom_key = max(groups, key=lambda k: groups[k]["t"])
+    dom = groups[dom_key]
+    t_flop = dom["flops"] / (perf.FP8_PEAK_TFLOPS * 1e12)
+    t_byte = dom["bytes"] / (perf.HBM_PEAK_GBS * 1e9)
+    peak_tf = perf.FP8_PEAK_TFLOPS if wl["qtype"] == "fp8" else perf.INT8_PEAK_TOPS
+    if t_flop >= t_byte:
+        achieved = dom["flops"] / dom["t"] / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_tf, 4)}
+    else:
+        achieved = dom["bytes"] / dom["t"] / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": perf.HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / perf.HBM_PEAK_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = dom_key
+    roof["launches"] = dom["n"]
+    roof["avg_launch_us"] = round(dom["t"] / dom["n"] * 1e6, 2)
+    return {
+        "value": flops_step / step_s / 1e12,
+        "ms_per_step": step_s * 1e3,
+        "rows": rows,
+        "roofline": roof,
+        "host": host,
+    }
+
+
+def cpu_baseline(wl, host, target_s: float):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload: the
+    quantization and GEMM of a few token rows of the largest M against the full weights."""
+    import numpy as np
+
+    import oracle
+    from block_scaled_w8a8_amd import perf, synth
+
+    qt = oracle.FP8 if wl["qtype"] == "fp8" else oracle.INT8
+    (N, K) = wl["shapes"][0]
+    w, x = host[(N, K)]
+    log(f"[bench] cpu baseline: oracle weight quantization N={N} K={K} (untimed)")
+    qw, sw = oracle.quant_blocks(w.numpy(), qtype=qt)
+    xb = synth.bf16_bits(x)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        qa, sa = oracle.quant_groups(np.ascontiguousarray(xb[:rows]), qtype=qt)
+        oracle.block_gemm(qa, sa, qw, sw, qtype=qt)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    rows = int(max(1, min(xb.shape[0], target_s / max(t1, 1e-6))))
+    log(f"[bench] cpu baseline: {rows} rows (1 row took {t1:.2f} s)")
+    t = run(rows)
+    return {"value": perf.gemm_flops(rows, N, K) / t / 1e12, "unit": "TFLOPS",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"quant + GEMM of {rows} token rows against the full N={N} K={K} "
+                      f"weights ({t:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mgrid", choices=sorted(WORKLOADS))
+    ap.add_argument("--rotate", type=int, default=2, help="weight copies rotated per launch")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+    wl = WORKLOADS[args.workload]
+    res = run_gpu(args, wl)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, res["host"], args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": round(res["value"], 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3fn" if wl["qtype"] == "fp8" else "int8",
+        "data": "synthetic",
+        "config": {"workload": wl["desc"], "shapes_NK": wl["shapes"], "M": wl["M"],
+                   "block_shape": [128, 128], "out_dtype": "bf16",
+                   "weight_copies_rotated": args.rotate},
+        "roofline": res["roofline"],
+        "cpu_baseline": cpu,
+        "per_m": res["rows"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

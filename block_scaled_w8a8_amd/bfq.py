@@ -1,0 +1,300 @@
+"""ctypes binding of libbfq (include/bfq.h): the same entry-point names, argument marshalling
+only. Every step of the computation runs in the HIP kernels of libbfq.so; PyTorch supplies
+device memory (tensor.data_ptr()) and the current HIP stream. There is no fallback: if the
+library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import warnings
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbfq.so")
+
+# status codes (bfq_status)
+BFQ_OK = 0
+BFQ_WARN_DEFAULT_TILE = 1
+BFQ_ERR_NULL = -1
+BFQ_ERR_SHAPE = -2
+BFQ_ERR_DTYPE = -3
+BFQ_ERR_ALIGN = -4
+BFQ_ERR_WORKSPACE = -5
+BFQ_ERR_TILE = -6
+BFQ_ERR_TABLE = -7
+BFQ_ERR_HIP = -8
+BFQ_ERR_ARG = -9
+
+# dtypes (bfq_dtype)
+BFQ_BF16, BFQ_FP16, BFQ_FP32, BFQ_E4M3FN, BFQ_INT8, BFQ_INT32 = range(6)
+# scale layouts (bfq_scale_layout)
+BFQ_SCALES_ROW_MAJOR = 0
+BFQ_SCALES_COL_MAJOR = 1
+
+DEFAULT_EPS = 1e-10
+BLOCK_SHAPE = (128, 128)
+
+EXPORTED = (
+    "bfq_quant_tokens", "bfq_quant_weight_blocks", "bfq_select_tile",
+    "bfq_gemm_workspace_bytes", "bfq_block_gemm", "bfq_load_tile_table",
+    "bfq_num_tile_candidates", "bfq_get_tile_candidate", "bfq_status_string",
+    "bfq_last_error", "bfq_debug_block_partials_i32", "bfq_debug_encode",
+)
+
+
+class bfq_tile(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("bm", ctypes.c_int32), ("bn", ctypes.c_int32),
+                ("bk", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32),
+                ("stages", ctypes.c_int32), ("group_m", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
+
+    FIELDS = ("variant", "bm", "bn", "bk", "split_k", "waves_m", "waves_n", "stages", "group_m")
+
+    def as_dict(self) -> dict:
+        return {f: int(getattr(self, f)) for f in self.FIELDS}
+
+    @classmethod
+    def from_dict(cls, d: dict) -> "bfq_tile":
+        t = cls()
+        t.bk = 128
+        t.split_k = 1
+        t.waves_m = 1
+        t.stages = 2
+        t.group_m = 1
+        for k, v in d.items():
+            if k in cls.FIELDS:
+                setattr(t, k, int(v))
+        return t
+
+
+class BfqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}: {last_error()}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libbfq.so not found at {LIB_PATH}; build it with "
+            "`python -m block_scaled_w8a8_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                            ctypes.c_size_t)
+    tp = ctypes.POINTER(bfq_tile)
+    bs = ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "bfq_quant_tokens": (i32, [p, i64, i64, i32, i32, p, p, i32, i64, f32, p]),
+        "bfq_quant_weight_blocks": (i32, [p, i64, i64, bs, i32, p, p, f32, p]),
+        "bfq_select_tile": (i32, [i64, i64, i64, bs, i32, i32, tp]),
+        "bfq_gemm_workspace_bytes": (sz, [i64, i64, i64, tp]),
+        "bfq_block_gemm": (i32, [p, p, i32, i64, p, p, p, i64, i64, i64, bs, i32, i32, tp, p,
+                                 sz, p]),
+        "bfq_load_tile_table": (i32, [ctypes.c_char_p]),
+        "bfq_num_tile_candidates": (i32, [i32]),
+        "bfq_get_tile_candidate": (i32, [i32, i32, tp]),
+        "bfq_status_string": (ctypes.c_char_p, [i32]),
+        "bfq_last_error": (ctypes.c_char_p, []),
+        "bfq_debug_block_partials_i32": (i32, [p, p, p, i64, i64, i64, p]),
+        "bfq_debug_encode": (i32, [p, i64, i32, p, p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+lib = _load()
+
+_warned: set = set()
+
+
+def status_string(s: int) -> str:
+    return lib.bfq_status_string(int(s)).decode()
+
+
+def last_error() -> str:
+    return lib.bfq_last_error().decode()
+
+
+def _check(status: int, where: str, warn_key=None) -> int:
+    if status < 0:
+        raise BfqError(status, where)
+    if status > 0 and warn_key not in _warned:
+        _warned.add(warn_key)
+        warnings.warn(f"{where}: {status_string(status)} (no tuned tile for {warn_key}; "
+                      "using the default tile)", RuntimeWarning, stacklevel=3)
+    return status
+
+
+def _block_shape(block_shape=BLOCK_SHAPE):
+    return (ctypes.c_int32 * 2)(*block_shape)
+
+
+def _ptr(t) -> int:
+    """Device address of a tensor (or an int address / None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _qdtype(t) -> int:
+    import torch
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return BFQ_E4M3FN
+    if t.dtype == torch.int8:
+        return BFQ_INT8
+    raise TypeError(f"code tensor dtype {t.dtype} is neither e4m3fn/uint8 nor int8")
+
+
+def _odtype(t) -> int:
+    import torch
+    return {torch.bfloat16: BFQ_BF16, torch.float16: BFQ_FP16, torch.float32: BFQ_FP32}[t.dtype]
+
+
+# ----------------------------------------------------------------------- entry points
+
+def bfq_quant_tokens(x, q, scales, layout=BFQ_SCALES_ROW_MAJOR, scale_ld=None,
+                     eps=DEFAULT_EPS, group_size=128, stream=None) -> int:
+    """x: bf16 [M, K]; q: uint8/float8_e4m3fn (e4m3fn codes) or int8 [M, K];
+    scales: fp32, [M, ld] (row-major) or [K/128, ld] (column-major)."""
+    M, K = x.shape
+    if scale_ld is None:
+        scale_ld = scales.stride(0)
+    st = lib.bfq_quant_tokens(_ptr(x), M, K, group_size, _qdtype(q), _ptr(q), _ptr(scales),
+                              layout, scale_ld, eps, _stream(stream))
+    return _check(st, "bfq_quant_tokens")
+
+
+def bfq_quant_weight_blocks(w, q, scales, eps=DEFAULT_EPS, block_shape=BLOCK_SHAPE,
+                            stream=None) -> int:
+    """w: fp32 [N, K]; q: codes [N, K]; scales: fp32 [N/128, K/128]."""
+    N, K = w.shape
+    st = lib.bfq_quant_weight_blocks(_ptr(w), N, K, _block_shape(block_shape), _qdtype(q),
+                                     _ptr(q), _ptr(scales), eps, _stream(stream))
+    return _check(st, "bfq_quant_weight_blocks")
+
+
+def bfq_select_tile(M, N, K, in_dtype=BFQ_E4M3FN, out_dtype=BFQ_BF16,
+                    block_shape=BLOCK_SHAPE):
+    """Returns (status, bfq_tile)."""
+    t = bfq_tile()
+    st = lib.bfq_select_tile(M, N, K, _block_shape(block_shape), in_dtype, out_dtype,
+                             ctypes.byref(t))
+    if st < 0:
+        raise BfqError(st, "bfq_select_tile")
+    return st, t
+
+
+def bfq_gemm_workspace_bytes(M, N, K, tile=None) -> int:
+    return int(lib.bfq_gemm_workspace_bytes(M, N, K, ctypes.byref(tile) if tile else None))
+
+
+def bfq_block_gemm(a_q, a_scales, w_q, w_scales, out, a_layout=BFQ_SCALES_ROW_MAJOR,
+                   a_scale_ld=None, tile=None, workspace=None, workspace_bytes=None,
+                   block_shape=BLOCK_SHAPE, stream=None) -> int:
+    """a_q [M, K] codes, w_q [N, K] codes, a_scales per layout, w_scales [N/128, K/128],
+    out [M, N] (bf16 / fp16 / fp32). Returns the status (>= 0)."""
+    M, K = a_q.shape
+    N = w_q.shape[0]
+    if a_scale_ld is None:
+        a_scale_ld = a_scales.stride(0)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.bfq_block_gemm(_ptr(a_q), _ptr(a_scales), a_layout, a_scale_ld, _ptr(w_q),
+                            _ptr(w_scales), _ptr(out), M, N, K, _block_shape(block_shape),
+                            _qdtype(a_q), _odtype(out), ctypes.byref(tile) if tile else None,
+                            _ptr(workspace), workspace_bytes, _stream(stream))
+    return _check(st, "bfq_block_gemm", warn_key=(N, K))
+
+
+def bfq_load_tile_table(path=None) -> int:
+    st = lib.bfq_load_tile_table(path.encode() if path else None)
+    return _check(st, "bfq_load_tile_table")
+
+
+def bfq_num_tile_candidates(in_dtype=BFQ_E4M3FN) -> int:
+    return int(lib.bfq_num_tile_candidates(in_dtype))
+
+
+def bfq_get_tile_candidate(index, in_dtype=BFQ_E4M3FN) -> bfq_tile:
+    t = bfq_tile()
+    _check(lib.bfq_get_tile_candidate(in_dtype, index, ctypes.byref(t)), "bfq_get_tile_candidate")
+    return t
+
+
+def bfq_status_string(s: int) -> str:
+    return status_string(s)
+
+
+def bfq_last_error() -> str:
+    return last_error()
+
+
+def bfq_debug_block_partials_i32(a_q, w_q, partials, stream=None) -> int:
+    M, K = a_q.shape
+    N = w_q.shape[0]
+    st = lib.bfq_debug_block_partials_i32(_ptr(a_q), _ptr(w_q), _ptr(partials), M, N, K,
+                                          _stream(stream))
+    return _check(st, "bfq_debug_block_partials_i32")
+
+
+def bfq_debug_encode(x, codes, q_dtype=BFQ_E4M3FN, stream=None) -> int:
+    st = lib.bfq_debug_encode(_ptr(x), x.numel(), q_dtype, _ptr(codes), _stream(stream))
+    return _check(st, "bfq_debug_encode")
+
+
+# ------------------------------------------------------------ allocating conveniences
+
+def quant_tokens(x, q_dtype=BFQ_E4M3FN, layout=BFQ_SCALES_ROW_MAJOR, eps=DEFAULT_EPS,
+                 stream=None):
+    """Allocate (q, scales) with torch and run bfq_quant_tokens. Returns (q, scales)."""
+    import torch
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8 if q_dtype == BFQ_E4M3FN else torch.int8,
+                    device=x.device)
+    if layout == BFQ_SCALES_ROW_MAJOR:
+        s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    else:
+        s = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
+    bfq_quant_tokens(x, q, s, layout=layout, scale_ld=s.stride(0), eps=eps, stream=stream)
+    return q, s
+
+
+def quant_weight_blocks(w, q_dtype=BFQ_E4M3FN, eps=DEFAULT_EPS, stream=None):
+    import torch
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.uint8 if q_dtype == BFQ_E4M3FN else torch.int8,
+                    device=w.device)
+    s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    bfq_quant_weight_blocks(w, q, s, eps=eps, stream=stream)
+    return q, s
+
+
+def block_gemm(a_q, a_scales, w_q, w_scales, out_dtype=None, a_layout=BFQ_SCALES_ROW_MAJOR,
+               tile=None, stream=None):
+    """Allocate out (and split-K workspace) with torch and run bfq_block_gemm."""
+    import torch
+    out_dtype = out_dtype or torch.bfloat16
+    M, K = a_q.shape
+    N = w_q.shape[0]
+    out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    if tile is None:
+        st, tile = bfq_select_tile(M, N, K, _qdtype(a_q), _odtype(out))
+        _check(st, "bfq_select_tile", warn_key=(N, K))
+    ws_bytes = bfq_gemm_workspace_bytes(M, N, K, tile)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=a_q.device) if ws_bytes else None
+    bfq_block_gemm(a_q, a_scales, w_q, w_scales, out, a_layout=a_layout, tile=tile,
+                   workspace=ws, workspace_bytes=ws_bytes, stream=stream)
+    return out

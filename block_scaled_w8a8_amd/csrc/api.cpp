@@ -1,0 +1,435 @@
+// Host side of libbfq: the C-ABI entry points of include/bfq.h — argument validation before
+// any launch, tile selection (table + default rule), kernel dispatch and status reporting.
+//
+// Pages cited by title and section:
+//   [BENCH]  "vLLM DeepGEMM FP8 Block GEMM 基准测试 ..." §4.1-§4.2 (operations, layouts,
+//            preallocated output; the dispatch precondition of bf16 output, N a multiple of
+//            64 and K a multiple of 128)
+//   [CONFIG] "vLLM 量化 Kernel 配置机制 ..." §4.1-§4.2 (lookup, nearest M, warning + default)
+//   [HELION] "Building a High-Performance and Portable vLLM Linear Backend with Helion",
+//            kernel section (swap-AB below 32 tokens on Hopper; split-K for small M/N)
+#include <dlfcn.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <fstream>
+#include <mutex>
+#include <sstream>
+#include <string>
+
+#include "bfq_internal.h"
+#include "tile_table.h"
+
+using namespace bfq;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bfq_status fail(bfq_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ------------------------------------------------------------------ tile table ----
+std::mutex g_table_mu;
+TileTable g_table;
+bool g_table_loaded = false;
+
+std::string default_table_path() {
+    const char* env = std::getenv("BFQ_TILE_TABLE");
+    if (env && *env) return env;
+    Dl_info info;
+    if (dladdr((void*)&default_table_path, &info) && info.dli_fname) {
+        std::string so = info.dli_fname;
+        size_t slash = so.rfind('/');
+        std::string dir = slash == std::string::npos ? "." : so.substr(0, slash);
+        return dir + "/tables/gfx950.json";
+    }
+    return "tables/gfx950.json";
+}
+
+bool read_file(const std::string& path, std::string& text) {
+    std::ifstream f(path, std::ios::binary);
+    if (!f) return false;
+    std::ostringstream ss;
+    ss << f.rdbuf();
+    text = ss.str();
+    return true;
+}
+
+const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype);
+
+// Every table tile must name a compiled kernel; otherwise the table is rejected.
+bool validate_table(const TileTable& t, std::string& err) {
+    for (auto& e : t.entries)
+        for (auto& b : e.second) {
+            if (!find_kernel(b.second, e.first.qtype, O_BF16)) {
+                err = "table entry N=" + std::to_string(e.first.N) + " K=" +
+                      std::to_string(e.first.K) + " M=" + std::to_string(b.first) +
+                      " names a tile that is not compiled";
+                return false;
+            }
+            if (b.second.split_k < 1 || b.second.split_k > 256) {
+                err = "table entry has split_k outside [1, 256]";
+                return false;
+            }
+        }
+    return true;
+}
+
+bfq_status load_table_locked(const std::string& path, bool strict) {
+    std::string text, err;
+    TileTable t;
+    if (!read_file(path, text)) {
+        if (strict) return fail(BFQ_ERR_TABLE, "cannot read tile table '" + path + "'");
+        g_table = TileTable{};
+        g_table_loaded = true;
+        return BFQ_OK;
+    }
+    if (!parse_tile_table(text, t, err) || !validate_table(t, err)) {
+        if (strict) return fail(BFQ_ERR_TABLE, "tile table '" + path + "': " + err);
+        g_table = TileTable{};
+        g_table_loaded = true;
+        return BFQ_OK;
+    }
+    g_table = std::move(t);
+    g_table_loaded = true;
+    return BFQ_OK;
+}
+
+void ensure_table() {
+    std::lock_guard<std::mutex> lk(g_table_mu);
+    if (!g_table_loaded) load_table_locked(default_table_path(), false);
+}
+
+// ------------------------------------------------------------------ registry ----
+bool same_shape(const bfq_tile& a, const bfq_tile& b) {
+    if (a.variant != b.variant || a.bm != b.bm || a.bn != b.bn || a.waves_n != b.waves_n ||
+        a.stages != b.stages)
+        return false;
+    if (a.variant == 0) return a.waves_m == b.waves_m && a.group_m == b.group_m;
+    return true;
+}
+
+const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype) {
+    if (t.bk != 0 && t.bk != 128) return nullptr;
+    int n = 0;
+    const KernelEntry* list = t.variant == 0 ? std_kernels(&n) : t.variant == 1 ? swapab_kernels(&n) : nullptr;
+    for (int i = 0; list && i < n; ++i)
+        if (list[i].qtype == qtype && list[i].otype == otype && same_shape(list[i].tile, t))
+            return &list[i];
+    return nullptr;
+}
+
+constexpr int64_t kNumCUs = 256;   // MI355X: 8 XCDs x 32 CUs
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compiled-in default ([CONFIG] §4.1: no tuned entry -> a fixed default config). Below 32
+// tokens the swap-AB streaming kernel ([HELION]: the Hopper rule dispatches swap-AB for
+// M < 32), else the standard kernel with the largest tile that still yields one workgroup
+// per CU. Split-K is added until the grid covers the CUs, keeping >= 4 K blocks per split.
+bfq_tile default_tile(int64_t M, int64_t N, int64_t K) {
+    const int64_t KB = K / 128;
+    bfq_tile t{};
+    t.bk = 128;
+    t.split_k = 1;
+    int64_t ctas;
+    if (M < 32) {
+        t.variant = 1;
+        t.bm = M <= 16 ? 16 : 32;
+        t.bn = 128;
+        t.waves_m = 1;
+        t.waves_n = 4;
+        t.stages = 4;
+        t.group_m = 1;
+        ctas = ceil_div(N, t.bn) * ceil_div(M, t.bm);
+    } else {
+        static const int shapes[4][4] = {{256, 256, 4, 2}, {128, 256, 2, 2}, {128, 128, 2, 2}, {64, 128, 1, 2}};
+        int pick = 3;
+        for (int i = 0; i < 4; ++i)
+            if (ceil_div(M, shapes[i][0]) * ceil_div(N, shapes[i][1]) >= kNumCUs) { pick = i; break; }
+        t.variant = 0;
+        t.bm = shapes[pick][0];
+        t.bn = shapes[pick][1];
+        t.waves_m = shapes[pick][2];
+        t.waves_n = shapes[pick][3];
+        t.stages = 2;
+        t.group_m = 8;
+        ctas = ceil_div(M, t.bm) * ceil_div(N, t.bn);
+    }
+    while (ctas * t.split_k < kNumCUs && KB / (t.split_k * 2) >= 4) t.split_k *= 2;
+    return t;
+}
+
+int qtype_of(bfq_dtype d) { return d == BFQ_E4M3FN ? Q_FP8 : Q_INT8; }
+
+int otype_of(bfq_dtype d) { return d == BFQ_BF16 ? O_BF16 : d == BFQ_FP16 ? O_FP16 : O_FP32; }
+
+bfq_status select_tile(int64_t M, int64_t N, int64_t K, int qtype, bfq_tile* out) {
+    ensure_table();
+    {
+        std::lock_guard<std::mutex> lk(g_table_mu);
+        auto it = g_table.entries.find(TableKey{N, K, qtype});
+        if (it != g_table.entries.end()) {
+            *out = it->second.at(nearest_bucket(it->second, M));
+            out->bk = 128;
+            return BFQ_OK;
+        }
+    }
+    *out = default_tile(M, N, K);
+    if (std::getenv("BFQ_LOG"))
+        std::fprintf(stderr, "[bfq] no tuned entry for N=%lld K=%lld; using default tile\n",
+                     (long long)N, (long long)K);
+    return BFQ_WARN_DEFAULT_TILE;
+}
+
+bool block_shape_ok(const int32_t* bs) { return bs && bs[0] == 128 && bs[1] == 128; }
+
+size_t workspace_for(int64_t M, int64_t N, const bfq_tile& t) {
+    return t.split_k > 1 ? (size_t)t.split_k * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+}  // namespace
+
+// ================================================================== C-ABI ====
+
+extern "C" {
+
+const char* bfq_status_string(bfq_status s) {
+    switch (s) {
+        case BFQ_OK: return "BFQ_OK";
+        case BFQ_WARN_DEFAULT_TILE: return "BFQ_WARN_DEFAULT_TILE";
+        case BFQ_ERR_NULL: return "BFQ_ERR_NULL";
+        case BFQ_ERR_SHAPE: return "BFQ_ERR_SHAPE";
+        case BFQ_ERR_DTYPE: return "BFQ_ERR_DTYPE";
+        case BFQ_ERR_ALIGN: return "BFQ_ERR_ALIGN";
+        case BFQ_ERR_WORKSPACE: return "BFQ_ERR_WORKSPACE";
+        case BFQ_ERR_TILE: return "BFQ_ERR_TILE";
+        case BFQ_ERR_TABLE: return "BFQ_ERR_TABLE";
+        case BFQ_ERR_HIP: return "BFQ_ERR_HIP";
+        case BFQ_ERR_ARG: return "BFQ_ERR_ARG";
+    }
+    return "BFQ_UNKNOWN_STATUS";
+}
+
+const char* bfq_last_error(void) { return g_last_error.c_str(); }
+
+bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t group_size,
+                            bfq_dtype q_dtype, void* q, float* scales, bfq_scale_layout layout,
+                            int64_t scale_ld, float eps, void* stream) {
+    if (M != 0 && (!x_bf16 || !q || !scales))
+        return fail(BFQ_ERR_NULL, "x, q and scales must be non-NULL");
+    if (q_dtype != BFQ_E4M3FN && q_dtype != BFQ_INT8)
+        return fail(BFQ_ERR_DTYPE, "q_dtype must be BFQ_E4M3FN or BFQ_INT8");
+    if (group_size != 128) return fail(BFQ_ERR_SHAPE, "group_size must be 128");
+    if (M < 0 || K <= 0 || K % 128 != 0)
+        return fail(BFQ_ERR_SHAPE, "need M >= 0 and K a positive multiple of 128");
+    if (M > 0x7FFFFFFF) return fail(BFQ_ERR_SHAPE, "M exceeds 2^31 - 1");
+    if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(scales, 4))
+        return fail(BFQ_ERR_ALIGN, "x and q must be 16-byte aligned, scales 4-byte aligned");
+    if (!(eps > 0.0f) || eps > 3.0e38f) return fail(BFQ_ERR_ARG, "eps must be positive and finite");
+    const int64_t G = K / 128;
+    int64_t sm, sg;
+    if (layout == BFQ_SCALES_ROW_MAJOR) {
+        if (scale_ld < G) return fail(BFQ_ERR_SHAPE, "row-major scale_ld must be >= K/128");
+        sm = scale_ld; sg = 1;
+    } else if (layout == BFQ_SCALES_COL_MAJOR) {
+        if (scale_ld < M) return fail(BFQ_ERR_SHAPE, "column-major scale_ld must be >= M");
+        sm = 1; sg = scale_ld;
+    } else {
+        return fail(BFQ_ERR_ARG, "unknown scale layout");
+    }
+    if (M == 0) return BFQ_OK;
+    hipError_t e = launch_quant_tokens(x_bf16, q, scales, M, K, qtype_of(q_dtype), sm, sg, eps,
+                                       (hipStream_t)stream);
+    if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
+    return BFQ_OK;
+}
+
+bfq_status bfq_quant_weight_blocks(const float* w, int64_t N, int64_t K,
+                                   const int32_t block_shape[2], bfq_dtype q_dtype, void* q,
+                                   float* scales, float eps, void* stream) {
+    if (!w || !q || !scales || !block_shape)
+        return fail(BFQ_ERR_NULL, "w, q, scales and block_shape must be non-NULL");
+    if (q_dtype != BFQ_E4M3FN && q_dtype != BFQ_INT8)
+        return fail(BFQ_ERR_DTYPE, "q_dtype must be BFQ_E4M3FN or BFQ_INT8");
+    if (!block_shape_ok(block_shape)) return fail(BFQ_ERR_SHAPE, "block_shape must be {128, 128}");
+    if (N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0)
+        return fail(BFQ_ERR_SHAPE, "N and K must be non-negative multiples of 128");
+    if (N / 128 > 65535 || K / 128 > 0x7FFFFFFF) return fail(BFQ_ERR_SHAPE, "N or K too large");
+    if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scales, 4))
+        return fail(BFQ_ERR_ALIGN, "w and q must be 16-byte aligned, scales 4-byte aligned");
+    if (!(eps > 0.0f) || eps > 3.0e38f) return fail(BFQ_ERR_ARG, "eps must be positive and finite");
+    if (N == 0 || K == 0) return BFQ_OK;
+    hipError_t e = launch_quant_weight_blocks(w, q, scales, N, K, qtype_of(q_dtype), eps,
+                                              (hipStream_t)stream);
+    if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
+    return BFQ_OK;
+}
+
+bfq_status bfq_select_tile(int64_t M, int64_t N, int64_t K, const int32_t block_shape[2],
+                           bfq_dtype in_dtype, bfq_dtype out_dtype, bfq_tile* tile_out) {
+    if (!tile_out || !block_shape) return fail(BFQ_ERR_NULL, "tile_out and block_shape must be non-NULL");
+    if (!block_shape_ok(block_shape)) return fail(BFQ_ERR_SHAPE, "block_shape must be {128, 128}");
+    if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8)
+        return fail(BFQ_ERR_DTYPE, "in_dtype must be BFQ_E4M3FN or BFQ_INT8");
+    if (out_dtype != BFQ_BF16 && out_dtype != BFQ_FP16 && out_dtype != BFQ_FP32)
+        return fail(BFQ_ERR_DTYPE, "out_dtype must be BF16, FP16 or FP32");
+    if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
+        return fail(BFQ_ERR_SHAPE, "need M >= 0 and N, K positive multiples of 128");
+    return select_tile(M, N, K, qtype_of(in_dtype), tile_out);
+}
+
+size_t bfq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const bfq_tile* tile) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    bfq_tile t;
+    if (tile) t = *tile;
+    else select_tile(M, N, K, Q_FP8, &t);
+    return workspace_for(M, N, t);
+}
+
+bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
+                          int64_t a_scale_ld, const void* w_q, const float* w_scales, void* out,
+                          int64_t M, int64_t N, int64_t K, const int32_t block_shape[2],
+                          bfq_dtype in_dtype, bfq_dtype out_dtype, const bfq_tile* tile,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (!w_q || !w_scales || !block_shape || (M != 0 && (!a_q || !a_scales || !out)))
+        return fail(BFQ_ERR_NULL, "a_q, a_scales, w_q, w_scales, out and block_shape must be non-NULL");
+    if (!block_shape_ok(block_shape)) return fail(BFQ_ERR_SHAPE, "block_shape must be {128, 128}");
+    if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8)
+        return fail(BFQ_ERR_DTYPE, "in_dtype must be BFQ_E4M3FN or BFQ_INT8");
+    if (out_dtype != BFQ_BF16 && out_dtype != BFQ_FP16 && out_dtype != BFQ_FP32)
+        return fail(BFQ_ERR_DTYPE, "out_dtype must be BF16, FP16 or FP32");
+    if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
+        return fail(BFQ_ERR_SHAPE, "need M >= 0 and N, K positive multiples of 128");
+    if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF)
+        return fail(BFQ_ERR_SHAPE, "M, N and K must be below 2^31");
+    if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(out, 16) || !aligned(a_scales, 4) ||
+        !aligned(w_scales, 4) || !aligned(workspace, 16))
+        return fail(BFQ_ERR_ALIGN, "codes, out and workspace must be 16-byte aligned, scales 4-byte");
+    const int64_t KB = K / 128;
+    int64_t ssm, ssk;
+    if (a_layout == BFQ_SCALES_ROW_MAJOR) {
+        if (a_scale_ld < KB) return fail(BFQ_ERR_SHAPE, "row-major a_scale_ld must be >= K/128");
+        ssm = a_scale_ld; ssk = 1;
+    } else if (a_layout == BFQ_SCALES_COL_MAJOR) {
+        if (a_scale_ld < M) return fail(BFQ_ERR_SHAPE, "column-major a_scale_ld must be >= M");
+        ssm = 1; ssk = a_scale_ld;
+    } else {
+        return fail(BFQ_ERR_ARG, "unknown scale layout");
+    }
+    const int qtype = qtype_of(in_dtype), otype = otype_of(out_dtype);
+    bfq_status status = BFQ_OK;
+    bfq_tile t;
+    if (tile) {
+        t = *tile;
+    } else {
+        status = select_tile(M, N, K, qtype, &t);
+    }
+    const KernelEntry* ke = find_kernel(t, qtype, otype);
+    if (!ke) return fail(BFQ_ERR_TILE, "tile does not name a compiled kernel for this dtype pair");
+    if (t.split_k < 1 || t.split_k > 256 || t.split_k > KB)
+        return fail(BFQ_ERR_TILE, "split_k must be in [1, min(256, K/128)]");
+    const size_t need = workspace_for(M, N, t);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(BFQ_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
+    // grid-size limits of the launchers
+    if (t.variant == 0) {
+        int64_t tiles = ceil_div(M, t.bm) * ceil_div(N, t.bn);
+        if (tiles > 0x7FFFFFFF) return fail(BFQ_ERR_SHAPE, "too many output tiles");
+    } else if (ceil_div(M, t.bm) > 65535) {
+        return fail(BFQ_ERR_SHAPE, "M too large for the swap-AB kernel; use a standard tile");
+    }
+    if (M == 0) return status;
+
+    GemmArgs ga;
+    ga.a = a_q;
+    ga.sa = a_scales;
+    ga.sa_stride_m = ssm;
+    ga.sa_stride_k = ssk;
+    ga.w = w_q;
+    ga.sw = w_scales;
+    ga.out = out;
+    ga.partials = static_cast<float*>(workspace);
+    ga.M = M;
+    ga.N = N;
+    ga.K = K;
+    ga.split = t.split_k;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = ke->launch(ga, s);
+    if (e == hipSuccess && t.split_k > 1)
+        e = launch_splitk_reduce(ga.partials, out, M, N, t.split_k, otype, s);
+    if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
+    if (std::getenv("BFQ_TRACE"))
+        std::fprintf(stderr, "[bfq] gemm M=%lld N=%lld K=%lld variant=%d bm=%d bn=%d split=%d\n",
+                     (long long)M, (long long)N, (long long)K, t.variant, t.bm, t.bn, t.split_k);
+    return status;
+}
+
+bfq_status bfq_load_tile_table(const char* json_path) {
+    std::lock_guard<std::mutex> lk(g_table_mu);
+    if (!json_path) return load_table_locked(default_table_path(), false);
+    return load_table_locked(json_path, true);
+}
+
+int32_t bfq_num_tile_candidates(bfq_dtype in_dtype) {
+    if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8) return 0;
+    const int q = qtype_of(in_dtype);
+    int n0 = 0, n1 = 0, count = 0;
+    const KernelEntry* a = std_kernels(&n0);
+    const KernelEntry* b = swapab_kernels(&n1);
+    for (int i = 0; i < n0; ++i) count += (a[i].qtype == q && a[i].otype == O_BF16);
+    for (int i = 0; i < n1; ++i) count += (b[i].qtype == q && b[i].otype == O_BF16);
+    return count;
+}
+
+bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, int32_t index, bfq_tile* tile_out) {
+    if (!tile_out) return fail(BFQ_ERR_NULL, "tile_out must be non-NULL");
+    if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8)
+        return fail(BFQ_ERR_DTYPE, "in_dtype must be BFQ_E4M3FN or BFQ_INT8");
+    const int q = qtype_of(in_dtype);
+    int n0 = 0, n1 = 0, count = 0;
+    const KernelEntry* lists[2] = {std_kernels(&n0), swapab_kernels(&n1)};
+    const int ns[2] = {n0, n1};
+    for (int l = 0; l < 2; ++l)
+        for (int i = 0; i < ns[l]; ++i) {
+            if (lists[l][i].qtype != q || lists[l][i].otype != O_BF16) continue;
+            if (count == index) { *tile_out = lists[l][i].tile; return BFQ_OK; }
+            ++count;
+        }
+    return fail(BFQ_ERR_ARG, "candidate index out of range");
+}
+
+bfq_status bfq_debug_block_partials_i32(const void* a_q, const void* w_q, int32_t* partials,
+                                        int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!w_q || (M != 0 && (!a_q || !partials)))
+        return fail(BFQ_ERR_NULL, "a_q, w_q and partials must be non-NULL");
+    if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
+        return fail(BFQ_ERR_SHAPE, "need M >= 0 and N, K positive multiples of 128");
+    if ((M + 15) / 16 > 65535 || K / 128 > 65535) return fail(BFQ_ERR_SHAPE, "shape too large");
+    if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(partials, 16))
+        return fail(BFQ_ERR_ALIGN, "buffers must be 16-byte aligned");
+    if (M == 0) return BFQ_OK;
+    hipError_t e = launch_block_partials_i32(a_q, w_q, partials, M, N, K, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
+    return BFQ_OK;
+}
+
+bfq_status bfq_debug_encode(const float* x, int64_t n, bfq_dtype q_dtype, void* codes,
+                            void* stream) {
+    if (!x || !codes) return fail(BFQ_ERR_NULL, "x and codes must be non-NULL");
+    if (q_dtype != BFQ_E4M3FN && q_dtype != BFQ_INT8)
+        return fail(BFQ_ERR_DTYPE, "q_dtype must be BFQ_E4M3FN or BFQ_INT8");
+    if (n < 0 || (n + 1023) / 1024 > 0x7FFFFFFF) return fail(BFQ_ERR_SHAPE, "bad element count");
+    if (!aligned(x, 16) || !aligned(codes, 4)) return fail(BFQ_ERR_ALIGN, "x 16-byte, codes 4-byte aligned");
+    if (n == 0) return BFQ_OK;
+    hipError_t e = launch_debug_encode(x, n, qtype_of(q_dtype), codes, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
+    return BFQ_OK;
+}
+
+}  // extern "C"

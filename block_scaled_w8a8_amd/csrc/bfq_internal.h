@@ -1,0 +1,59 @@
+// Internal declarations of libbfq: kernel launchers and the registry of compiled GEMM
+// configurations. Not part of the public C-ABI (include/bfq.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bfq.h"
+
+namespace bfq {
+
+enum QType { Q_FP8 = 0, Q_INT8 = 1 };
+enum OType { O_BF16 = 0, O_FP16 = 1, O_FP32 = 2 };
+
+hipError_t launch_quant_tokens(const void* x, void* q, float* scales, int64_t M, int64_t K,
+                               int qtype, int64_t s_stride_m, int64_t s_stride_g, float eps,
+                               hipStream_t stream);
+hipError_t launch_quant_weight_blocks(const float* w, void* q, float* scales, int64_t N,
+                                      int64_t K, int qtype, float eps, hipStream_t stream);
+hipError_t launch_debug_encode(const float* x, int64_t n, int qtype, void* out,
+                               hipStream_t stream);
+
+// Arguments of one block-GEMM launch, shared by every kernel variant.
+struct GemmArgs {
+    const void* a;          // [M][K] codes
+    const float* sa;        // activation scales
+    int64_t sa_stride_m;    // element stride between tokens
+    int64_t sa_stride_k;    // element stride between K blocks
+    const void* w;          // [N][K] codes
+    const float* sw;        // [N/128][K/128]
+    void* out;              // [M][N]
+    float* partials;        // split-K fp32 partials [split][M][N] (split > 1)
+    int64_t M, N, K;
+    int split;              // K-block chunks
+};
+
+typedef hipError_t (*GemmLaunchFn)(const GemmArgs& args, hipStream_t stream);
+
+// A compiled kernel configuration. `tile.split_k` is 1 here; split_k is a launch argument.
+struct KernelEntry {
+    bfq_tile tile;
+    int qtype;              // Q_FP8 / Q_INT8
+    int otype;              // O_BF16 / O_FP16 / O_FP32 (output of a split=1 launch)
+    GemmLaunchFn launch;    // writes `out` (split==1) or `partials` (split>1)
+};
+
+// Registries filled by the kernel translation units.
+const KernelEntry* std_kernels(int* count);
+const KernelEntry* swapab_kernels(int* count);
+
+// Deterministic split-K reduction: out[m][n] = sum_{s=0..split-1} partials[s][m][n], in
+// ascending s, converted once to the output dtype.
+hipError_t launch_splitk_reduce(const float* partials, void* out, int64_t M, int64_t N,
+                                int split, int otype, hipStream_t stream);
+
+// int8 per-K-block int32 partials [K/128][M][N] (test support).
+hipError_t launch_block_partials_i32(const void* a, const void* w, int32_t* out, int64_t M,
+                                     int64_t N, int64_t K, hipStream_t stream);
+
+}  // namespace bfq

@@ -1,0 +1,117 @@
+// Device-side helpers shared by the gfx950 kernels of libbfq: vector types, the e4m3fn and
+// int8 element encoders, bf16/fp16 output conversion and the MFMA wrappers.
+//
+// Pages cited by title and section:
+//   [BENCH]  "vLLM DeepGEMM FP8 Block GEMM 基准测试：DeepSeek DeepGEMM 对比 Triton 与 CUTLASS
+//             的块量化 GEMM 内核解析"
+//   [PR]     vLLM pull request 42153 (per_token_group_quant 2-D grid)
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bfq_internal.h"
+
+namespace bfq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+constexpr float kFp8Max = 448.0f;    // largest finite e4m3fn value
+constexpr float kInt8Max = 127.0f;   // symmetric int8 range [-127, 127]
+
+template <int QT> __device__ __forceinline__ constexpr float qmax() {
+    return QT == Q_FP8 ? kFp8Max : kInt8Max;
+}
+
+// ---------------------------------------------------------------- encoders ----
+// Two fp32 values -> two e4m3fn codes in the low 16 bits (a in bits 0..7, b in 8..15).
+// gfx950's conversion rounds to nearest even into the OCP e4m3fn format. Callers pass only
+// finite values of magnitude below 464 (the midpoint above 448), so saturation never
+// matters; NaN/Inf groups are handled by the callers without this instruction.
+__device__ __forceinline__ uint32_t enc_fp8x2(float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Four fp32 values -> four e4m3fn codes packed little-endian in one word.
+__device__ __forceinline__ uint32_t enc_fp8x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// fp32 -> int8 code: round half to even, clamp to [-127, 127]. Finite inputs only.
+__device__ __forceinline__ uint32_t enc_i8(float y) {
+    float r = __builtin_rintf(y);
+    r = __builtin_fminf(__builtin_fmaxf(r, -kInt8Max), kInt8Max);
+    return (uint32_t)((int)r) & 0xFFu;
+}
+
+__device__ __forceinline__ uint32_t enc_i8x4(float a, float b, float c, float d) {
+    return enc_i8(a) | (enc_i8(b) << 8) | (enc_i8(c) << 16) | (enc_i8(d) << 24);
+}
+
+// ---------------------------------------------------------------- conversions ----
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN 0x7FC0.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return (f != f) ? 0x7FC0u : r;
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    _Float16 h = (_Float16)f;   // RNE
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// ---------------------------------------------------------------- MFMA ----
+// D(16x16, fp32) = A(16x128 e4m3) * B(128x16 e4m3). Lane l supplies row (l % 16) of A and
+// column (l % 16) of B, each as 32 bytes of the 128-long K slice; both operands use the
+// same K placement, so the product is the full 128-term dot product. Output: lane l holds
+// D[4*(l/16) + i][l % 16], i = 0..3.
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
+    v4f z = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+// int8: D(16x16, int32) += A(16x64) * B(64x16); 16 bytes of K per lane.
+__device__ __forceinline__ v4i mfma_i8_16x16x64(const v4i& a, const v4i& b, const v4i& c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- LDS DMA ----
+// 16 bytes per lane from global memory straight into LDS: the wave writes 1 KB at
+// lds_base + lane * 16 (lds_base must be wave-uniform).
+__device__ __forceinline__ void load_lds_16(const void* gsrc, uint8_t* lds_base, uint32_t off) {
+    const uint32_t u = __builtin_amdgcn_readfirstlane(off);
+    __builtin_amdgcn_global_load_lds(gsrc, lds_base + u, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------- output store ----
+// Store four consecutive output values of one row.
+template <int OT> __device__ __forceinline__ void store4(void* out, int64_t idx, v4f v) {
+    if constexpr (OT == O_FP32) {
+        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(out) + idx) = v;
+    } else {
+        uint32_t b0, b1, b2, b3;
+        if constexpr (OT == O_BF16) {
+            b0 = f32_to_bf16_bits(v.x); b1 = f32_to_bf16_bits(v.y);
+            b2 = f32_to_bf16_bits(v.z); b3 = f32_to_bf16_bits(v.w);
+        } else {
+            b0 = f32_to_f16_bits(v.x); b1 = f32_to_f16_bits(v.y);
+            b2 = f32_to_f16_bits(v.z); b3 = f32_to_f16_bits(v.w);
+        }
+        uint2 p;
+        p.x = b0 | (b1 << 16);
+        p.y = b2 | (b3 << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + idx) = p;
+    }
+}
+
+}  // namespace bfq

@@ -1,0 +1,232 @@
+// Quantization kernels for gfx950: per-token-group activation quantization (bf16 -> e4m3fn
+// or int8 codes + one fp32 scale per 1x128 group), per-128x128-block weight quantization
+// (fp32 -> codes + one fp32 scale per block), and the element-encoder probe used by tests.
+//
+// Pages cited by title and section:
+//   [BENCH] "vLLM DeepGEMM FP8 Block GEMM 基准测试 ..." §4.1 (per_token_group_quant_fp8,
+//           per_block_cast_to_fp8: scale = amax / fp8_max per group or block)
+//   [PR]    vLLM pull request 42153 — what the group kernel is parameterised by (group size,
+//           eps, min/max code) and its point that index arithmetic should be compile-time
+//           constants rather than runtime divisions.
+//
+// Group kernel layout (wave64): 16 lanes own one 128-element group, 8 bf16 (16 bytes) per
+// lane, so one wave covers 4 groups of one token row per pass and each 16-byte load is
+// fully coalesced. The group's absolute maximum is formed on the raw bf16 bits
+// (|x| = bits & 0x7FFF; as unsigned integers NaN > Inf > every finite magnitude), which
+// makes a NaN anywhere in the group win the reduction, then reduced over the 16 lanes.
+#include "bfq_internal.h"
+#include "device_common.h"
+
+namespace bfq {
+
+constexpr int kQuantWaves = 4;        // waves per workgroup
+constexpr int kQuantPasses = 2;       // 4-group passes per wave (loads issued together)
+constexpr int kGroupsPerWave = 4 * kQuantPasses;
+constexpr int kGroupsPerBlock = kQuantWaves * kGroupsPerWave;
+
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    us2 x = __builtin_bit_cast(us2, a), y = __builtin_bit_cast(us2, b);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+
+// Encode 8 values x[0..7] divided by scale s; finite-amax groups only.
+template <int QT>
+__device__ __forceinline__ uint2 encode8(const float* x, float s) {
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = x[i] / s;     // IEEE division
+    uint2 r;
+    if constexpr (QT == Q_FP8) {
+        r.x = enc_fp8x4(y[0], y[1], y[2], y[3]);
+        r.y = enc_fp8x4(y[4], y[5], y[6], y[7]);
+    } else {
+        r.x = enc_i8x4(y[0], y[1], y[2], y[3]);
+        r.y = enc_i8x4(y[4], y[5], y[6], y[7]);
+    }
+    return r;
+}
+
+// Groups whose amax is Inf or NaN. NaN amax: every code is NaN (0x7F) / 0 (int8).
+// Inf amax: the scale is Inf, finite values divide to a signed zero, +-Inf to NaN.
+template <int QT>
+__device__ __forceinline__ uint2 encode8_special(const float* x, bool nan_group) {
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t code;
+        if (nan_group || __builtin_isinf(x[i])) code = (QT == Q_FP8) ? 0x7Fu : 0u;
+        else code = (QT == Q_FP8) ? ((__float_as_uint(x[i]) >> 24) & 0x80u) : 0u;
+        b[i] = code;
+    }
+    uint2 r;
+    r.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    r.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    return r;
+}
+
+template <int QT>
+__global__ __launch_bounds__(64 * kQuantWaves) void quant_tokens_kernel(
+    const uint4* __restrict__ x, uint2* __restrict__ q, float* __restrict__ scales,
+    int64_t M, int64_t K, int64_t G, int64_t s_stride_m, int64_t s_stride_g, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t m = blockIdx.x;
+    const int part = lane & 15;                         // 16-byte slice within the group
+    const int64_t g0 = (int64_t)blockIdx.y * kGroupsPerBlock + wave * kGroupsPerWave + (lane >> 4);
+    (void)M;
+
+    uint4 raw[kQuantPasses];
+#pragma unroll
+    for (int u = 0; u < kQuantPasses; ++u) {
+        int64_t g = g0 + 4 * u;
+        if (g < G) raw[u] = x[(m * K + g * 128) / 8 + part];
+        else raw[u] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kQuantPasses; ++u) {
+        int64_t g = g0 + 4 * u;
+        uint32_t mx = max_u16x2(max_u16x2(raw[u].x & 0x7FFF7FFFu, raw[u].y & 0x7FFF7FFFu),
+                                max_u16x2(raw[u].z & 0x7FFF7FFFu, raw[u].w & 0x7FFF7FFFu));
+        mx = max(mx & 0xFFFFu, mx >> 16);
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 8, 16));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4, 16));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2, 16));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1, 16));
+        if (g >= G) continue;
+
+        float xv[8] = {bf16_lo(raw[u].x), bf16_hi(raw[u].x), bf16_lo(raw[u].y), bf16_hi(raw[u].y),
+                       bf16_lo(raw[u].z), bf16_hi(raw[u].z), bf16_lo(raw[u].w), bf16_hi(raw[u].w)};
+        float s;
+        uint2 codes;
+        if (mx < 0x7F80u) {                              // finite amax
+            float amax = __uint_as_float(mx << 16);
+            s = (amax > eps ? amax : eps) / qmax<QT>();
+            codes = encode8<QT>(xv, s);
+        } else {
+            bool nan_group = mx > 0x7F80u;
+            s = nan_group ? __uint_as_float(0x7FC00000u) : __uint_as_float(0x7F800000u);
+            codes = encode8_special<QT>(xv, nan_group);
+        }
+        q[(m * K + g * 128) / 8 + part] = codes;
+        if (part == 0) scales[m * s_stride_m + g * s_stride_g] = s;
+    }
+}
+
+// One workgroup per 128x128 weight block; 256 threads, 64 values each.
+template <int QT>
+__global__ __launch_bounds__(256) void quant_weight_blocks_kernel(
+    const float* __restrict__ w, uint8_t* __restrict__ q, float* __restrict__ scales,
+    int64_t N, int64_t K, float eps) {
+    const int64_t nb = blockIdx.y, kb = blockIdx.x, KB = K / 128;
+    const int t = threadIdx.x;
+    const int col4 = t & 31;          // float4 column within the 128-wide block row
+    const int row0 = t >> 5;          // 8 rows per pass, 16 passes
+    (void)N;
+    __shared__ uint32_t red[4];
+
+    float4 v[16];
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        int64_t r = nb * 128 + row0 + 8 * i;
+        v[i] = *reinterpret_cast<const float4*>(w + r * K + kb * 128 + col4 * 4);
+        mx = max(mx, __float_as_uint(v[i].x) & 0x7FFFFFFFu);
+        mx = max(mx, __float_as_uint(v[i].y) & 0x7FFFFFFFu);
+        mx = max(mx, __float_as_uint(v[i].z) & 0x7FFFFFFFu);
+        mx = max(mx, __float_as_uint(v[i].w) & 0x7FFFFFFFu);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    if ((t & 63) == 0) red[t >> 6] = mx;
+    __syncthreads();
+    mx = max(max(red[0], red[1]), max(red[2], red[3]));
+
+    float s;
+    const bool finite = mx < 0x7F800000u;
+    const bool nan_block = mx > 0x7F800000u;
+    if (finite) {
+        float amax = __uint_as_float(mx);
+        s = (amax > eps ? amax : eps) / qmax<QT>();
+    } else {
+        s = nan_block ? __uint_as_float(0x7FC00000u) : __uint_as_float(0x7F800000u);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        int64_t r = nb * 128 + row0 + 8 * i;
+        float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t word;
+        if (finite) {
+            float y0 = e[0] / s, y1 = e[1] / s, y2 = e[2] / s, y3 = e[3] / s;
+            word = (QT == Q_FP8) ? enc_fp8x4(y0, y1, y2, y3) : enc_i8x4(y0, y1, y2, y3);
+        } else {
+            word = 0;
+            for (int j = 0; j < 4; ++j) {
+                uint32_t c;
+                if (nan_block || __builtin_isinf(e[j])) c = (QT == Q_FP8) ? 0x7Fu : 0u;
+                else c = (QT == Q_FP8) ? ((__float_as_uint(e[j]) >> 24) & 0x80u) : 0u;
+                word |= c << (8 * j);
+            }
+        }
+        *reinterpret_cast<uint32_t*>(q + r * K + kb * 128 + col4 * 4) = word;
+    }
+    if (t == 0) scales[nb * KB + kb] = s;
+}
+
+template <int QT>
+__global__ __launch_bounds__(256) void debug_encode_kernel(const float* __restrict__ x,
+                                                           uint8_t* __restrict__ out, int64_t n) {
+    int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i + 4 <= n) {
+        float4 v = *reinterpret_cast<const float4*>(x + i);
+        uint32_t w = (QT == Q_FP8) ? enc_fp8x4(v.x, v.y, v.z, v.w) : enc_i8x4(v.x, v.y, v.z, v.w);
+        *reinterpret_cast<uint32_t*>(out + i) = w;
+    } else {
+        for (int64_t j = i; j < n; ++j)
+            out[j] = (uint8_t)((QT == Q_FP8) ? enc_fp8x2(x[j], 0.0f) : enc_i8(x[j]));
+    }
+}
+
+// ---------------------------------------------------------------- launchers ----
+
+hipError_t launch_quant_tokens(const void* x, void* q, float* scales, int64_t M, int64_t K,
+                               int qtype, int64_t s_stride_m, int64_t s_stride_g, float eps,
+                               hipStream_t stream) {
+    const int64_t G = K / 128;
+    dim3 grid((unsigned)M, (unsigned)((G + kGroupsPerBlock - 1) / kGroupsPerBlock));
+    dim3 block(64 * kQuantWaves);
+    if (qtype == Q_FP8)
+        hipLaunchKernelGGL(quant_tokens_kernel<Q_FP8>, grid, block, 0, stream,
+                           (const uint4*)x, (uint2*)q, scales, M, K, G, s_stride_m, s_stride_g, eps);
+    else
+        hipLaunchKernelGGL(quant_tokens_kernel<Q_INT8>, grid, block, 0, stream,
+                           (const uint4*)x, (uint2*)q, scales, M, K, G, s_stride_m, s_stride_g, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_blocks(const float* w, void* q, float* scales, int64_t N,
+                                      int64_t K, int qtype, float eps, hipStream_t stream) {
+    dim3 grid((unsigned)(K / 128), (unsigned)(N / 128));
+    if (qtype == Q_FP8)
+        hipLaunchKernelGGL(quant_weight_blocks_kernel<Q_FP8>, grid, dim3(256), 0, stream, w,
+                           (uint8_t*)q, scales, N, K, eps);
+    else
+        hipLaunchKernelGGL(quant_weight_blocks_kernel<Q_INT8>, grid, dim3(256), 0, stream, w,
+                           (uint8_t*)q, scales, N, K, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_encode(const float* x, int64_t n, int qtype, void* out,
+                               hipStream_t stream) {
+    int64_t threads = (n + 3) / 4;
+    dim3 grid((unsigned)((threads + 255) / 256));
+    if (qtype == Q_FP8)
+        hipLaunchKernelGGL(debug_encode_kernel<Q_FP8>, grid, dim3(256), 0, stream, x,
+                           (uint8_t*)out, n);
+    else
+        hipLaunchKernelGGL(debug_encode_kernel<Q_INT8>, grid, dim3(256), 0, stream, x,
+                           (uint8_t*)out, n);
+    return hipGetLastError();
+}
+
+}  // namespace bfq

@@ -1,0 +1,58 @@
+"""Throughput formulas of the block GEMM and the quantizer, and the MI355X peaks they are
+priced against.
+
+The pages' formulas (block GEMM benchmark page, "vLLM DeepGEMM FP8 Block GEMM 基准测试 ...",
+§4.3): TFLOPS = 2*m*n*k / t / 1e12 and GB/s = (m*k + k*n + 2*m*n) / t, i.e. fp8 inputs of one
+byte per element, a bf16 output, and no scale bytes. ``gemm_bytes_all`` also counts the
+fp32 scales and the real output width; it is the algorithmic byte count used for the
+roofline.
+"""
+from __future__ import annotations
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
+
+
+def gemm_flops(m: int, n: int, k: int) -> float:
+    return 2.0 * m * n * k
+
+
+def gemm_bytes_page(m: int, n: int, k: int) -> float:
+    """The pages' byte count: fp8 A and B, bf16 C; scales not counted."""
+    return float(m * k + k * n + 2 * m * n)
+
+
+def gemm_bytes_all(m: int, n: int, k: int, out_bytes: int = 2) -> float:
+    """Every byte the method must move once: codes, fp32 scales, output."""
+    return float(m * k + n * k + 4 * m * (k // 128) + 4 * (n // 128) * (k // 128)
+                 + out_bytes * m * n)
+
+
+def quant_bytes(m: int, k: int) -> float:
+    """bf16 in, one code byte out, one fp32 scale per 128 elements."""
+    return float(2 * m * k + m * k + 4 * m * (k // 128))
+
+
+def tflops(m: int, n: int, k: int, seconds: float) -> float:
+    return gemm_flops(m, n, k) / seconds / 1e12
+
+
+def gbs_page(m: int, n: int, k: int, seconds: float) -> float:
+    return gemm_bytes_page(m, n, k) / seconds / 1e9
+
+
+def gbs_all(m: int, n: int, k: int, seconds: float, out_bytes: int = 2) -> float:
+    return gemm_bytes_all(m, n, k, out_bytes) / seconds / 1e9
+
+
+def roofline_time_s(m: int, n: int, k: int, out_bytes: int = 2) -> float:
+    """Lower bound on the GEMM time on MI355X: max(bytes / HBM peak, flops / FP8 peak)."""
+    return max(gemm_bytes_all(m, n, k, out_bytes) / (HBM_PEAK_GBS * 1e9),
+               gemm_flops(m, n, k) / (FP8_PEAK_TFLOPS * 1e12))
+
+
+def bound(m: int, n: int, k: int, out_bytes: int = 2) -> str:
+    t_mem = gemm_bytes_all(m, n, k, out_bytes) / (HBM_PEAK_GBS * 1e9)
+    t_mma = gemm_flops(m, n, k) / (FP8_PEAK_TFLOPS * 1e12)
+    return "hbm" if t_mem >= t_mma else "mfma"

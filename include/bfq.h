@@ -1,0 +1,153 @@
+/*
+ * bfq.h — C-ABI of libbfq: block-scaled W8A8 (e4m3fn / int8) linear layer on MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *   [BENCH]  "vLLM DeepGEMM FP8 Block GEMM 基准测试：DeepSeek DeepGEMM 对比 Triton 与 CUTLASS
+ *             的块量化 GEMM 内核解析" (blog.gitcode.com)
+ *   [CONFIG] "vLLM 量化 Kernel 配置机制：W8A8 Block FP8 Triton 内核的调优、选择与回退原理"
+ *             (blog.gitcode.com)
+ *   [PR]     vLLM pull request 42153, per_token_group_quant 2-D grid (prhub.com.cn)
+ *   [HELION] "Building a High-Performance and Portable vLLM Linear Backend with Helion"
+ *             (PyTorch blog, translated)
+ *
+ * Conventions for every entry point:
+ *  - Device pointers unless marked "host". Every buffer is allocated and freed by the
+ *    caller; the library never allocates, frees or synchronizes device memory. It owns only
+ *    its host-side tile table.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is enqueued
+ *    asynchronously; the call returns once the launches are enqueued.
+ *  - All arguments are validated before anything is enqueued. On a negative status nothing
+ *    was launched and no output was touched; bfq_last_error() holds a detail string
+ *    (thread-local). A positive status is success with a warning.
+ *  - M = 0 is valid and launches nothing.
+ *  - Shapes are int64; K and N must be multiples of 128, and x/q/w/out 16-byte aligned.
+ *  - Two calls on one stream are ordered; calls on different streams that share an output
+ *    or workspace race.
+ */
+#ifndef BFQ_H
+#define BFQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BFQ_OK = 0,
+    BFQ_WARN_DEFAULT_TILE = 1,  /* success; no tuned entry for (N,K,dtype): default tile used */
+    BFQ_ERR_NULL = -1,          /* a required pointer is NULL */
+    BFQ_ERR_SHAPE = -2,         /* M<0, K or N not a multiple of 128, group/block not 128 */
+    BFQ_ERR_DTYPE = -3,         /* unsupported input/output dtype */
+    BFQ_ERR_ALIGN = -4,         /* pointer not 16-byte aligned (scales: 4-byte) */
+    BFQ_ERR_WORKSPACE = -5,     /* workspace smaller than bfq_gemm_workspace_bytes() */
+    BFQ_ERR_TILE = -6,          /* explicit tile is not one of the compiled kernels */
+    BFQ_ERR_TABLE = -7,         /* tile table file missing or malformed */
+    BFQ_ERR_HIP = -8,           /* a HIP runtime call or launch failed */
+    BFQ_ERR_ARG = -9            /* invalid scalar argument (eps, enum value, index) */
+} bfq_status;
+
+typedef enum {
+    BFQ_BF16 = 0,
+    BFQ_FP16 = 1,
+    BFQ_FP32 = 2,
+    BFQ_E4M3FN = 3,   /* OCP float8 e4m3fn, max 448 */
+    BFQ_INT8 = 4,     /* symmetric int8 in [-127, 127] */
+    BFQ_INT32 = 5
+} bfq_dtype;
+
+/* Layout of per-(token, group) activation scales, [BENCH] §4.1 (row-major for the Triton
+ * kernel, column-major for CUTLASS/DeepGEMM). */
+typedef enum {
+    BFQ_SCALES_ROW_MAJOR = 0,  /* s[m * ld + g], ld >= K/128 */
+    BFQ_SCALES_COL_MAJOR = 1   /* s[g * ld + m], ld >= M     */
+} bfq_scale_layout;
+
+/* One launch configuration of the block GEMM ([CONFIG] §2: per-M launch parameters).
+ *   variant 0 "standard": bm x bn output tile per workgroup, A and W tiles staged through
+ *             LDS (double-buffered), waves_m x waves_n waves, group_m = grouped tile order.
+ *   variant 1 "swap_ab": the weight rows stream straight from HBM into the wide MFMA
+ *             operand and the bm tokens ride in the narrow one; the output tile is formed
+ *             transposed and stored back row-major ([HELION] kernel section).
+ *   split_k  : K blocks split into split_k contiguous chunks (>= 1), fp32 partials reduced
+ *             in a fixed order ([HELION] kernel section).
+ *   stages   : LDS stages (variant 0) or weight prefetch depth in K blocks (variant 1).
+ *   bk is always 128 (one scale block per K step). */
+typedef struct {
+    int32_t variant, bm, bn, bk, split_k, waves_m, waves_n, stages, group_m, reserved[3];
+} bfq_tile;
+
+/* Per-token-group quantization ([BENCH] §4.1 per_token_group_quant_fp8; [PR] kernel
+ * arguments eps/min_8bit/max_8bit). For each row m and 128-wide group g of x:
+ *   scale = max(amax, eps) / Qmax   (Qmax = 448 for E4M3FN, 127 for INT8; IEEE division)
+ *   q     = encode(x / scale)       (IEEE division; e4m3fn: RNE, saturating; int8: RNE,
+ *                                    clamp [-127, 127])
+ * A group containing NaN gets a NaN scale and codes 0x7F (e4m3fn) or 0 (int8).
+ *   x_bf16 [M][K] row-major bf16; q [M][K] row-major codes (1 byte);
+ *   scales: fp32, layout per `layout` with leading dimension scale_ld.
+ * group_size must be 128; q_dtype must be BFQ_E4M3FN or BFQ_INT8. */
+bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t group_size,
+                            bfq_dtype q_dtype, void* q, float* scales, bfq_scale_layout layout,
+                            int64_t scale_ld, float eps, void* stream);
+
+/* Per-block weight quantization, the offline step before the GEMM ([BENCH] §4.1
+ * per_block_cast_to_fp8 with fp32 scales): for each block_shape[0] x block_shape[1] block of
+ * w [N][K] (fp32, row-major): scale = max(amax, eps)/Qmax, q = encode(w / scale).
+ *   q [N][K] codes; scales [N/128][K/128] row-major fp32. block_shape must be {128,128}. */
+bfq_status bfq_quant_weight_blocks(const float* w, int64_t N, int64_t K,
+                                   const int32_t block_shape[2] /* host */, bfq_dtype q_dtype,
+                                   void* q, float* scales, float eps, void* stream);
+
+/* Tile selection ([CONFIG] §4.1-§4.2): exact (N, K, dtype) entry of the loaded tile table,
+ * then the bucket nearest to M (ties to the smaller bucket; M past the grid -> last bucket).
+ * No entry -> the compiled-in default rule and BFQ_WARN_DEFAULT_TILE ([CONFIG] §4.1 warns
+ * and falls back to a default config). tile_out is a host pointer. */
+bfq_status bfq_select_tile(int64_t M, int64_t N, int64_t K, const int32_t block_shape[2],
+                           bfq_dtype in_dtype, bfq_dtype out_dtype, bfq_tile* tile_out);
+
+/* Bytes of device workspace bfq_block_gemm needs for this shape and tile (split-K fp32
+ * partials: split_k * M * N * 4 when split_k > 1, else 0). tile NULL -> selected tile. */
+size_t bfq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const bfq_tile* tile);
+
+/* Block-scaled GEMM ([BENCH] §4.2, w8a8 block-scaled matmul):
+ *   out[m][n] = sum_kb ( sum_{k in kb} a_q[m][k] * w_q[n][k] ) * a_scales[m, kb] * w_scales[n/128][kb]
+ * with exact per-block products, an fp32 accumulator and one rounding to out_dtype.
+ *   a_q [M][K] codes, w_q [N][K] codes (both K-contiguous, "NT");
+ *   a_scales per a_layout/a_scale_ld; w_scales [N/128][K/128] row-major;
+ *   out [M][N] row-major, out_dtype BF16 | FP16 | FP32.
+ *   tile NULL -> bfq_select_tile; workspace may be NULL when the tile needs none.
+ * Returns BFQ_WARN_DEFAULT_TILE when tile was NULL and the default rule was used. */
+bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
+                          int64_t a_scale_ld, const void* w_q, const float* w_scales,
+                          void* out, int64_t M, int64_t N, int64_t K,
+                          const int32_t block_shape[2] /* host */, bfq_dtype in_dtype,
+                          bfq_dtype out_dtype, const bfq_tile* tile /* host */,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Load a tile table (JSON, host path) and replace the current one ([CONFIG] §2 schema:
+ * per (N, K, dtype, block_shape) a map "M bucket -> launch parameters"). Must not run
+ * concurrently with other calls. NULL reloads the default location. */
+bfq_status bfq_load_tile_table(const char* json_path);
+
+/* Number of compiled kernel configurations for in_dtype, and the i-th one (split_k = 1;
+ * any split_k >= 1 may be combined with it). Used by the on-device sweep. */
+int32_t bfq_num_tile_candidates(bfq_dtype in_dtype);
+bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, int32_t index, bfq_tile* tile_out);
+
+const char* bfq_status_string(bfq_status s);
+const char* bfq_last_error(void);
+
+/* Test support: int8 per-K-block int32 partials, layout [K/128][M][N] (exact). */
+bfq_status bfq_debug_block_partials_i32(const void* a_q, const void* w_q, int32_t* partials,
+                                        int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Test support: the element encoder the quantizers use, applied to n fp32 values that are
+ * finite with |x| < 464 (e4m3fn) or finite (int8). codes [n] bytes. */
+bfq_status bfq_debug_encode(const float* x, int64_t n, bfq_dtype q_dtype, void* codes,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BFQ_H */

@@ -1,0 +1,200 @@
+"""CPU tests of the C-ABI library: it loads, exports every entry point include/bfq.h
+declares, validates arguments before any launch, and selects tiles per the tile table and
+the default rule. No compute call is made (no GPU here)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+REPO = os.path.dirname(HERE)
+
+
+def _declared_entry_points():
+    text = open(os.path.join(REPO, "include", "bfq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bfq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(bfq):
+    names = _declared_entry_points()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(bfq.lib, n), n
+    assert set(names) == set(bfq.EXPORTED)
+
+
+def test_status_strings(bfq):
+    for code in range(-9, 2):
+        assert bfq.status_string(code).startswith("BFQ_")
+
+
+BS = (ctypes.c_int32 * 2)(128, 128)
+FAKE = 1 << 20          # a 16-byte aligned non-NULL address; never dereferenced here
+
+
+def _gemm(bfq, **kw):
+    a = dict(a_q=FAKE, a_scales=FAKE, a_layout=0, a_scale_ld=56, w_q=FAKE, w_scales=FAKE,
+             out=FAKE, M=0, N=1536, K=7168, block_shape=BS, in_dtype=bfq.BFQ_E4M3FN,
+             out_dtype=bfq.BFQ_BF16, tile=None, workspace=None, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return bfq.lib.bfq_block_gemm(*a.values())
+
+
+def test_gemm_validation_errors_without_launch(bfq):
+    assert _gemm(bfq, w_q=None) == bfq.BFQ_ERR_NULL
+    assert _gemm(bfq, M=5, a_q=None) == bfq.BFQ_ERR_NULL
+    assert _gemm(bfq, K=7000) == bfq.BFQ_ERR_SHAPE
+    assert _gemm(bfq, N=1000) == bfq.BFQ_ERR_SHAPE
+    assert _gemm(bfq, M=-1) == bfq.BFQ_ERR_SHAPE
+    assert _gemm(bfq, block_shape=(ctypes.c_int32 * 2)(128, 64)) == bfq.BFQ_ERR_SHAPE
+    assert _gemm(bfq, in_dtype=bfq.BFQ_BF16) == bfq.BFQ_ERR_DTYPE
+    assert _gemm(bfq, out_dtype=bfq.BFQ_INT8) == bfq.BFQ_ERR_DTYPE
+    assert _gemm(bfq, w_q=FAKE + 8) == bfq.BFQ_ERR_ALIGN
+    assert _gemm(bfq, a_scales=FAKE + 2) == bfq.BFQ_ERR_ALIGN
+    assert _gemm(bfq, a_scale_ld=10) == bfq.BFQ_ERR_SHAPE
+    assert _gemm(bfq, M=64, a_layout=1, a_scale_ld=63) == bfq.BFQ_ERR_SHAPE
+    assert _gemm(bfq, a_layout=7) == bfq.BFQ_ERR_ARG
+    bad = bfq.bfq_tile.from_dict({"variant": 0, "bm": 96, "bn": 96, "waves_m": 2, "waves_n": 2})
+    assert _gemm(bfq, tile=ctypes.pointer(bad)) == bfq.BFQ_ERR_TILE
+    t = bfq.bfq_get_tile_candidate(0)
+    t.split_k = 4
+    assert _gemm(bfq, M=64, tile=ctypes.pointer(t)) == bfq.BFQ_ERR_WORKSPACE
+    t.split_k = 57      # more splits than K blocks
+    assert _gemm(bfq, M=64, tile=ctypes.pointer(t)) == bfq.BFQ_ERR_TILE
+    assert "split_k" in bfq.last_error()
+    # M = 0 is valid and launches nothing
+    assert _gemm(bfq, M=0) >= 0
+
+
+def test_quant_validation_errors_without_launch(bfq):
+    q = bfq.lib.bfq_quant_tokens
+    args = [FAKE, 4, 7168, 128, bfq.BFQ_E4M3FN, FAKE, FAKE, 0, 56, 1e-10, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["x", "M", "K", "group", "qd", "q", "s", "layout", "ld", "eps", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return q(*a)
+
+    assert call(x=None) == bfq.BFQ_ERR_NULL
+    assert call(K=100) == bfq.BFQ_ERR_SHAPE
+    assert call(group=64) == bfq.BFQ_ERR_SHAPE
+    assert call(qd=bfq.BFQ_BF16) == bfq.BFQ_ERR_DTYPE
+    assert call(x=FAKE + 2) == bfq.BFQ_ERR_ALIGN
+    assert call(ld=55) == bfq.BFQ_ERR_SHAPE
+    assert call(layout=1, ld=3) == bfq.BFQ_ERR_SHAPE
+    assert call(eps=0.0) == bfq.BFQ_ERR_ARG
+    assert call(eps=float("nan")) == bfq.BFQ_ERR_ARG
+    assert call(M=0, x=None, q=None, s=None) == bfq.BFQ_OK
+    w = bfq.lib.bfq_quant_weight_blocks
+    assert w(FAKE, 256, 256, (ctypes.c_int32 * 2)(64, 128), bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, None) == bfq.BFQ_ERR_SHAPE
+    assert w(FAKE, 250, 256, BS, bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, None) == bfq.BFQ_ERR_SHAPE
+    assert w(None, 256, 256, BS, bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, None) == bfq.BFQ_ERR_NULL
+    assert w(FAKE, 0, 256, BS, bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, None) == bfq.BFQ_OK
+
+
+def test_candidates_enumerate(bfq):
+    for qd in (bfq.BFQ_E4M3FN, bfq.BFQ_INT8):
+        n = bfq.bfq_num_tile_candidates(qd)
+        assert n >= 4
+        seen = set()
+        for i in range(n):
+            t = bfq.bfq_get_tile_candidate(i, qd)
+            assert t.split_k == 1 and t.bk == 128 and t.variant in (0, 1)
+            seen.add(tuple(t.as_dict().values()))
+        assert len(seen) == n
+    with pytest.raises(bfq.BfqError):
+        bfq.bfq_get_tile_candidate(10_000)
+
+
+def _table(entries):
+    return json.dumps({"device": "gfx950", "entries": entries})
+
+
+def test_table_nearest_m_and_fallback(bfq, tmp_path):
+    """The config page's lookup (§4.1-§4.2): exact (N, K, dtype) key, nearest M bucket
+    (M=37 -> 32, M=2050 -> 2048, ties to the smaller bucket), default + warning on a miss."""
+    grid = json.load(open(os.path.join(HERE, "golden", "nearest_m.json")))
+    cands = [bfq.bfq_get_tile_candidate(i).as_dict() for i in range(bfq.bfq_num_tile_candidates())]
+    cfgs = {str(m): dict(cands[i % len(cands)], split_k=1 + (i % 3)) for i, m in enumerate(grid["grid"])}
+    p = tmp_path / "t.json"
+    p.write_text(_table([{"N": 1536, "K": 7168, "dtype": "fp8_w8a8", "block_shape": [128, 128],
+                          "configs": cfgs}]))
+    try:
+        assert bfq.bfq_load_tile_table(str(p)) == bfq.BFQ_OK
+        for m, want in grid["examples"] + grid["ties"] + grid["ends"]:
+            st, t = bfq.bfq_select_tile(m, 1536, 7168)
+            assert st == bfq.BFQ_OK
+            exp = cfgs[str(want)]
+            assert t.as_dict() == dict(exp, bk=128), (m, want)
+        st, t = bfq.bfq_select_tile(64, 4096, 7168)           # no entry for this shape
+        assert st == bfq.BFQ_WARN_DEFAULT_TILE
+        st, t = bfq.bfq_select_tile(64, 1536, 7168, in_dtype=bfq.BFQ_INT8)   # dtype is part of the key
+        assert st == bfq.BFQ_WARN_DEFAULT_TILE
+    finally:
+        bfq.bfq_load_tile_table(None)
+
+
+@pytest.mark.parametrize("text,why", [
+    ("{", "truncated"),
+    ('{"entries": [{"N": 1536, "K": 7168, "dtype": "fp9", "configs": {"1": {}}}]}', "dtype"),
+    ('{"entries": [{"N": 1536, "K": 7168, "dtype": "fp8_w8a8", "configs": {"x": {}}}]}', "key"),
+    ('{"entries": [{"N": 1536, "K": 7168, "dtype": "fp8_w8a8", "configs": {"1": '
+     '{"variant": 0, "bm": 96, "bn": 96, "waves_m": 2, "waves_n": 2}}}]}', "uncompiled tile"),
+    ('{"entries": [{"N": 1536, "K": 7168, "dtype": "fp8_w8a8", "block_shape": [64, 128],'
+     ' "configs": {"1": {"variant": 1, "bm": 16, "bn": 128, "waves_m": 1, "waves_n": 4, '
+     '"stages": 4}}}]}', "block shape"),
+])
+def test_bad_tables_rejected(bfq, tmp_path, text, why):
+    p = tmp_path / "bad.json"
+    p.write_text(text)
+    with pytest.raises(bfq.BfqError) as e:
+        bfq.bfq_load_tile_table(str(p))
+    assert e.value.status == bfq.BFQ_ERR_TABLE, why
+    with pytest.raises(bfq.BfqError):
+        bfq.bfq_load_tile_table(str(tmp_path / "missing.json"))
+    bfq.bfq_load_tile_table(None)
+
+
+def test_default_rule(bfq, tmp_path):
+    """With no tuned entry: swap-AB streaming below 32 tokens (the Hopper rule of the Helion
+    page), the standard tile otherwise; split-K only while the grid is short of 256 CUs."""
+    p = tmp_path / "empty.json"
+    p.write_text(_table([]))
+    bfq.bfq_load_tile_table(str(p))
+    try:
+        for M in (1, 8, 16, 31):
+            st, t = bfq.bfq_select_tile(M, 24576, 7168)
+            assert st == bfq.BFQ_WARN_DEFAULT_TILE and t.variant == 1
+        for M in (32, 64, 4096):
+            st, t = bfq.bfq_select_tile(M, 24576, 7168)
+            assert t.variant == 0
+        st, t = bfq.bfq_select_tile(4096, 24576, 7168)
+        assert t.split_k == 1 and (t.bm, t.bn) == (256, 256)
+        st, t = bfq.bfq_select_tile(1, 1536, 7168)
+        assert t.split_k > 1
+    finally:
+        bfq.bfq_load_tile_table(None)
+
+
+def test_metric_formulas_reproduce_pages_table():
+    """P10: the pages' TFLOPS and GB/s formulas (block GEMM benchmark page §4.3) recompute
+    every printed row of §3.2 from its (m, n, k, us) within the rounding of the print."""
+    from block_scaled_w8a8_amd import perf
+    rows = [l.strip().split(",") for l in open(os.path.join(HERE, "golden", "h100_block_fp8_rows.csv"))
+            if l.strip() and not l.startswith("#") and not l.startswith("impl")]
+    assert len(rows) == 48
+    for impl, m, n, k, us, tf, gbs in rows:
+        m, n, k, t = int(m), int(n), int(k), float(us) * 1e-6
+        assert perf.tflops(m, n, k, t) == pytest.approx(float(tf), rel=0.008, abs=0.06)
+        assert perf.gbs_page(m, n, k, t) == pytest.approx(float(gbs), rel=0.008)
+    # the averages the page prints (§3.3) are the arithmetic means of the 16 rows
+    for impl, avg_tf, avg_gbs in [("deepgemm", 310.98, 1052.10), ("triton", 144.30, 715.60),
+                                  ("cutlass", 286.78, 1076.67)]:
+        sel = [r for r in rows if r[0] == impl]
+        assert sum(float(r[5]) for r in sel) / 16 == pytest.approx(avg_tf, abs=0.01)
+        assert sum(float(r[6]) for r in sel) / 16 == pytest.approx(avg_gbs, abs=0.01)

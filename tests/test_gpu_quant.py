@@ -1,0 +1,179 @@
+"""GPU parity of the quantizers (through the C-ABI) against the CPU oracle: codes and fp32
+scales must be bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_w8a8_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _codes_np(t):
+    return t.cpu().numpy()
+
+
+def _gpu_quant_tokens(bfq, x_cpu, qdtype, layout, ld_pad=0):
+    dev = torch.device("cuda:0")
+    x = x_cpu.to(dev)
+    M, K = x.shape
+    if qdtype == bfq.BFQ_E4M3FN:
+        q = torch.full((M, K), 0xAA, dtype=torch.uint8, device=dev)   # prefill: unwritten shows
+    else:
+        q = torch.full((M, K), 77, dtype=torch.int8, device=dev)
+    G = K // 128
+    if layout == bfq.BFQ_SCALES_ROW_MAJOR:
+        s = torch.full((M, G + ld_pad), float("nan"), dtype=torch.float32, device=dev)
+    else:
+        s = torch.full((G, M + ld_pad), float("nan"), dtype=torch.float32, device=dev)
+    bfq.bfq_quant_tokens(x, q, s, layout=layout, scale_ld=s.stride(0))
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    s = s[:, :G] if layout == bfq.BFQ_SCALES_ROW_MAJOR else s[:, :M].T.copy()
+    return q.cpu().numpy(), s
+
+
+SHAPES = [(8, 1536), (1, 7168), (24, 1536), (37, 7168), (128, 7168), (64, 18432), (1024, 7168),
+          (4096, 7168), (4096, 18432), (3, 128), (5, 640)]
+
+
+@pytest.mark.parametrize("M,K", SHAPES)
+@pytest.mark.parametrize("qname", ["fp8", "int8"])
+def test_quant_tokens_bit_exact(bfq, orc, M, K, qname):
+    print(f"quant_tokens M={M} K={K} {qname}", flush=True)
+    qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
+    ot = orc.FP8 if qname == "fp8" else orc.INT8
+    x = synth.activations(M, K, seed=M + K)
+    qg, sg = _gpu_quant_tokens(bfq, x, qd, bfq.BFQ_SCALES_ROW_MAJOR)
+    qo, so = orc.quant_groups(synth.bf16_bits(x), qtype=ot)
+    assert np.array_equal(qg.view(np.uint8), qo.view(np.uint8))
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
+
+
+@pytest.mark.parametrize("layout", ["row", "col"])
+def test_quant_tokens_layouts_and_ld(bfq, orc, layout):
+    M, K = 33, 1536
+    lay = bfq.BFQ_SCALES_ROW_MAJOR if layout == "row" else bfq.BFQ_SCALES_COL_MAJOR
+    x = synth.activations(M, K, seed=9)
+    qg, sg = _gpu_quant_tokens(bfq, x, bfq.BFQ_E4M3FN, lay, ld_pad=5)
+    qo, so = orc.quant_groups(synth.bf16_bits(x))
+    assert np.array_equal(qg, qo)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
+
+
+def _special_input():
+    """Rows of bf16 bit patterns covering zero/-0, NaN, +-Inf, subnormal bf16, huge and
+    tiny magnitudes, and groups below eps."""
+    rng = np.random.default_rng(5)
+    M, K = 12, 512
+    b = (rng.standard_normal((M, K)).astype(np.float32))
+    bits = torch.from_numpy(b).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    bits[0, :] = 0
+    bits[0, 7] = 0x8000                 # -0
+    bits[1, 130] = 0x7FC0               # NaN in group 1
+    bits[2, 3] = 0x7F80                 # +Inf
+    bits[2, 260] = 0xFF80               # -Inf in group 2
+    bits[3, :] = rng.integers(0, 0x80, K) | (rng.integers(0, 2, K) << 15)   # bf16 subnormals
+    bits[4, :128] = 0x7F7F              # max finite bf16
+    bits[4, 1] = 0x0001                 # tiny next to huge
+    bits[5, :] = 0x2E00                 # ~2.9e-11: below eps
+    bits[6, :] = rng.integers(0, 0x7F80, K) | (rng.integers(0, 2, K) << 15)  # any finite
+    bits[7, :] = 0x3F80                 # all 1.0
+    bits[8, 0] = 0xFFC1                 # negative NaN with payload
+    return bits
+
+
+@pytest.mark.parametrize("qname", ["fp8", "int8"])
+def test_quant_tokens_special_values(bfq, orc, qname):
+    bits = _special_input()
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
+    ot = orc.FP8 if qname == "fp8" else orc.INT8
+    qg, sg = _gpu_quant_tokens(bfq, x, qd, bfq.BFQ_SCALES_ROW_MAJOR)
+    qo, so = orc.quant_groups(bits, qtype=ot)
+    assert np.array_equal(qg.view(np.uint8), qo.view(np.uint8))
+    nan_g, nan_o = np.isnan(sg), np.isnan(so)
+    assert np.array_equal(nan_g, nan_o)
+    assert np.array_equal(sg[~nan_g].view(np.uint32), so[~nan_o].view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K", [(1536, 1536), (7168, 1536), (1536, 7168), (4096, 7168),
+                                 (24576, 7168), (256, 384)])
+@pytest.mark.parametrize("qname", ["fp8", "int8"])
+def test_quant_weight_blocks_bit_exact(bfq, orc, N, K, qname):
+    if N * K > 50_000_000 and qname == "int8":
+        pytest.skip("the large shape is covered by the fp8 case")
+    print(f"quant_weight_blocks N={N} K={K} {qname}", flush=True)
+    qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
+    ot = orc.FP8 if qname == "fp8" else orc.INT8
+    w = synth.weights(N, K, seed=N ^ K)
+    wg = w.to("cuda:0")
+    q = torch.empty((N, K), dtype=torch.uint8 if qname == "fp8" else torch.int8, device="cuda:0")
+    s = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda:0")
+    bfq.bfq_quant_weight_blocks(wg, q, s)
+    torch.cuda.synchronize()
+    qo, so = orc.quant_blocks(w.numpy(), qtype=ot)
+    assert np.array_equal(q.cpu().numpy().view(np.uint8), qo.view(np.uint8))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+
+
+def test_weight_blocks_special_values(bfq, orc):
+    w = synth.weights(256, 256, seed=1).numpy().copy()
+    w[0:128, 0:128] = 0.0
+    w[5, 130] = np.nan
+    w[200, 7] = np.inf
+    w[201, 8] = -np.inf
+    w[130:256, 130:256] *= 1e-30
+    wg = torch.from_numpy(w).to("cuda:0")
+    q = torch.empty((256, 256), dtype=torch.uint8, device="cuda:0")
+    s = torch.empty((2, 2), dtype=torch.float32, device="cuda:0")
+    bfq.bfq_quant_weight_blocks(wg, q, s)
+    torch.cuda.synchronize()
+    qo, so = orc.quant_blocks(w)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    sg = s.cpu().numpy()
+    assert np.array_equal(np.isnan(sg), np.isnan(so))
+    assert np.array_equal(sg[~np.isnan(sg)].view(np.uint32), so[~np.isnan(so)].view(np.uint32))
+
+
+def _encode_class_inputs():
+    """Every fp32 value whose top 16 bits take all 2^16 patterns and whose low 16 bits are
+    one of {0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF}: the e4m3 rounding decision depends on
+    the sign, exponent, the mantissa bits down to the round bit (all within the top 16)
+    and on whether any lower bit is set (sticky), and these low patterns give both sticky
+    values next to every round-bit state. Restricted to finite |x| < 464."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    u = (hi[:, None] | lows[None, :]).ravel()
+    x = u.view(np.float32)
+    return x[np.isfinite(x) & (np.abs(x) < 464)].copy()
+
+
+def test_device_fp8_encoder_all_rounding_classes(bfq, orc):
+    x = _encode_class_inputs()
+    xg = torch.from_numpy(x).to("cuda:0")
+    out = torch.empty(x.size, dtype=torch.uint8, device="cuda:0")
+    bfq.bfq_debug_encode(xg, out, bfq.BFQ_E4M3FN)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = orc.e4m3_encode_array(x)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(ref[i])) for i in bad[:8]]
+
+
+def test_device_int8_encoder(bfq, orc):
+    rng = np.random.default_rng(3)
+    x = np.concatenate([np.arange(-300, 300, 0.25, dtype=np.float32),
+                        (rng.standard_normal(1 << 20) * 100).astype(np.float32)])
+    xg = torch.from_numpy(x).to("cuda:0")
+    out = torch.empty(x.size, dtype=torch.int8, device="cuda:0")
+    bfq.bfq_debug_encode(xg, out, bfq.BFQ_INT8)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), orc.int8_encode_array(x))
+
+
+def test_quant_tokens_m0_is_noop(bfq):
+    x = torch.empty((0, 1536), dtype=torch.bfloat16, device="cuda:0")
+    q = torch.empty((0, 1536), dtype=torch.uint8, device="cuda:0")
+    s = torch.empty((0, 12), dtype=torch.float32, device="cuda:0")
+    assert bfq.bfq_quant_tokens(x, q, s, scale_ld=12) == bfq.BFQ_OK
