@@ -49,7 +49,7 @@ def log(*a):
 
 def tile_key(t) -> str:
     d = t.as_dict()
-    return "v{variant}_bm{bm}_bn{bn}_w{waves_m}x{waves_n}_s{stages}_g{group_m}_k{split_k}".format(**d)
+    return "v{variant}_bm{bm}_bn{bn}_w{waves_m}x{waves_n}_s{stages}_c{sched}_g{group_m}_r{raster}_k{split_k}".format(**d)
 
 
 def run_gpu(args, wl):

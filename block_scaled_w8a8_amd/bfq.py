@@ -47,9 +47,11 @@ class bfq_tile(ctypes.Structure):
                 ("bk", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32),
                 ("stages", ctypes.c_int32), ("group_m", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 3)]
+                ("sched", ctypes.c_int32), ("raster", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
-    FIELDS = ("variant", "bm", "bn", "bk", "split_k", "waves_m", "waves_n", "stages", "group_m")
+    FIELDS = ("variant", "bm", "bn", "bk", "split_k", "waves_m", "waves_n", "stages", "group_m",
+              "sched", "raster")
 
     def as_dict(self) -> dict:
         return {f: int(getattr(self, f)) for f in self.FIELDS}

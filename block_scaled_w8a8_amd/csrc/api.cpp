@@ -72,8 +72,9 @@ bool validate_table(const TileTable& t, std::string& err) {
                       " names a tile that is not compiled";
                 return false;
             }
-            if (b.second.split_k < 1 || b.second.split_k > 256) {
-                err = "table entry has split_k outside [1, 256]";
+            if (b.second.split_k < 1 || b.second.split_k > 256 || b.second.group_m < 1 ||
+                b.second.raster < 0 || b.second.raster > 1) {
+                err = "table entry has split_k outside [1, 256], group_m < 1 or raster not 0/1";
                 return false;
             }
         }
@@ -110,7 +111,7 @@ bool same_shape(const bfq_tile& a, const bfq_tile& b) {
     if (a.variant != b.variant || a.bm != b.bm || a.bn != b.bn || a.waves_n != b.waves_n ||
         a.stages != b.stages)
         return false;
-    if (a.variant == 0) return a.waves_m == b.waves_m && a.group_m == b.group_m;
+    if (a.variant == 0) return a.waves_m == b.waves_m && a.sched == b.sched;
     return true;
 }
 
@@ -306,8 +307,9 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
         return fail(BFQ_ERR_DTYPE, "out_dtype must be BF16, FP16 or FP32");
     if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
         return fail(BFQ_ERR_SHAPE, "need M >= 0 and N, K positive multiples of 128");
-    if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF)
-        return fail(BFQ_ERR_SHAPE, "M, N and K must be below 2^31");
+    if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > (1 << 23))
+        return fail(BFQ_ERR_SHAPE, "M and N must be below 2^31 and K at most 2^23");
+    if (a_scale_ld > (1 << 23)) return fail(BFQ_ERR_SHAPE, "a_scale_ld must be at most 2^23");
     if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(out, 16) || !aligned(a_scales, 4) ||
         !aligned(w_scales, 4) || !aligned(workspace, 16))
         return fail(BFQ_ERR_ALIGN, "codes, out and workspace must be 16-byte aligned, scales 4-byte");
@@ -334,6 +336,8 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     if (!ke) return fail(BFQ_ERR_TILE, "tile does not name a compiled kernel for this dtype pair");
     if (t.split_k < 1 || t.split_k > 256 || t.split_k > KB)
         return fail(BFQ_ERR_TILE, "split_k must be in [1, min(256, K/128)]");
+    if (t.variant == 0 && (t.group_m < 1 || t.raster < 0 || t.raster > 1))
+        return fail(BFQ_ERR_TILE, "group_m must be >= 1 and raster 0 or 1");
     const size_t need = workspace_for(M, N, t);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(BFQ_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
@@ -359,6 +363,8 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     ga.N = N;
     ga.K = K;
     ga.split = t.split_k;
+    ga.group_m = t.group_m;
+    ga.raster = t.raster;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = ke->launch(ga, s);
     if (e == hipSuccess && t.split_k > 1)

@@ -31,11 +31,13 @@ struct GemmArgs {
     float* partials;        // split-K fp32 partials [split][M][N] (split > 1)
     int64_t M, N, K;
     int split;              // K-block chunks
+    int group_m;            // tile rows per group of the grouped order (standard kernel)
+    int raster;             // 0: XCD-contiguous tile ranges, 1: plain order (standard kernel)
 };
 
 typedef hipError_t (*GemmLaunchFn)(const GemmArgs& args, hipStream_t stream);
 
-// A compiled kernel configuration. `tile.split_k` is 1 here; split_k is a launch argument.
+// A compiled kernel configuration. split_k, group_m and raster are launch arguments.
 struct KernelEntry {
     bfq_tile tile;
     int qtype;              // Q_FP8 / Q_INT8

@@ -83,6 +83,26 @@ __device__ __forceinline__ v4i mfma_i8_16x16x64(const v4i& a, const v4i& b, cons
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------- buffer access ----
+// Raw buffer resource over [base, base + bytes): loads past `bytes` return zero, which the
+// GEMM kernels use for rows beyond M or N. bytes < 2^32.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// lds_base + lds_off + 16 * l (lds_off wave-uniform). voff per lane, soff uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_base,
+                                      uint32_t lds_off, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(lds_base + lds_off), 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
 // ---------------------------------------------------------------- LDS DMA ----
 // 16 bytes per lane from global memory straight into LDS: the wave writes 1 KB at
 // lds_base + lane * 16 (lds_base must be wave-uniform).

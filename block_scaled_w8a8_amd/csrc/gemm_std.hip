@@ -20,22 +20,28 @@
 //    second, so each lane ends up owning one token row and four consecutive output columns:
 //    one scale product per lane and sub-tile row, and 8-byte (bf16) row-contiguous stores.
 //  * LDS rows are 128 bytes (one K block); the 16-byte chunk c of row r is stored at slot
-//    c ^ (r & 7) so the 16 rows a fragment read touches fall in different banks.
+//    c ^ swz(r) so the 16 rows a fragment read touches fall in different banks.
 //  * Workgroup ids are remapped so that each XCD (ids i, i+8, i+16, ...) owns a contiguous
-//    range of tiles, ordered in groups of GROUP_M tile rows, keeping shared A/W panels in
+//    range of tiles, ordered in groups of group_m tile rows, keeping shared A/W panels in
 //    that XCD's L2.
 #include "bfq_internal.h"
 #include "device_common.h"
 
 namespace bfq {
 
-// Tile id -> (pid_m, pid_n): contiguous range per XCD, then grouped order within it.
+// Tile id -> (pid_m, pid_n). raster 0: workgroup ids are dealt round-robin to the 8 XCDs, so
+// ids are first remapped to give each XCD a contiguous range of tiles; raster 1: no remap.
+// Then the grouped order: GROUP_M tile rows at a time, column by column within the group.
 __device__ __forceinline__ void tile_coords(int64_t bid, int64_t tiles_m, int64_t tiles_n,
-                                            int group_m, int64_t& pid_m, int64_t& pid_n) {
+                                            int group_m, int raster, int64_t& pid_m,
+                                            int64_t& pid_n) {
     const int64_t T = tiles_m * tiles_n;
-    const int64_t xcd = bid & 7, local = bid >> 3;
-    const int64_t base = T >> 3, rem = T & 7;
-    const int64_t j = xcd * base + (xcd < rem ? xcd : rem) + local;
+    int64_t j = bid;
+    if (raster == 0) {
+        const int64_t xcd = bid & 7, local = bid >> 3;
+        const int64_t base = T >> 3, rem = T & 7;
+        j = xcd * base + (xcd < rem ? xcd : rem) + local;
+    }
     const int64_t per_group = (int64_t)group_m * tiles_n;
     const int64_t gid = j / per_group;
     const int64_t first_m = gid * group_m;
@@ -45,7 +51,13 @@ __device__ __forceinline__ void tile_coords(int64_t bid, int64_t tiles_m, int64_
     pid_n = in_group / gsize;
 }
 
-template <int BM, int BN, int WM, int WN, int QT, int OT, int GROUP_M>
+// LDS slot of 16-byte chunk c in region row r: c ^ swz(r). Fragment reads touch 16
+// consecutive rows (a multiple of 16 apart) at one chunk index; with this swizzle those 16
+// reads hit 16 distinct (row parity, slot) pairs, i.e. distinct banks whether the LDS serves
+// 8 lanes x 16 B or 16 lanes x 16 B per cycle. It depends only on r & 15.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     constexpr int NWAVES = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;      // wave tile (tokens x weight rows)
@@ -53,67 +65,63 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     constexpr int STAGE = (BM + BN) * 128;         // bytes per LDS stage
     constexpr int CHUNKS = (BM + BN) / 8;          // 1 KB load chunks per stage
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(BM % 16 == 0, "the W region must start on a 16-row boundary");
     static_assert(128 % TN == 0, "a wave's columns must lie in one 128-wide scale block");
     static_assert(CHUNKS % NWAVES == 0, "load chunks must divide evenly over waves");
+    static_assert((BM / 8) % NWAVES == 0, "A chunks must divide evenly over waves");
+    static_assert(NWAVES % 2 == 0, "the swizzle phase of a lane's chunks needs an even wave count");
     constexpr int CPW = CHUNKS / NWAVES;
+    constexpr int CPW_A = BM / 8 / NWAVES;                 // chunks i < CPW_A hold A rows
 
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
 
     const int64_t M = p.M, N = p.N, K = p.K, KB = K / 128;
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     int64_t pid_m, pid_n;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, GROUP_M, pid_m, pid_n);
+    tile_coords(blockIdx.x, tiles_m, tiles_n, p.group_m, p.raster, pid_m, pid_n);
     const int64_t m0 = pid_m * BM, n0 = pid_n * BN;
 
     const int split = p.split, z = blockIdx.z;
     const int64_t kb_begin = (int64_t)z * KB / split, kb_end = (int64_t)(z + 1) * KB / split;
 
-    const uint8_t* A = static_cast<const uint8_t*>(p.a);
-    const uint8_t* W = static_cast<const uint8_t*>(p.w);
+    // Buffer resources over this tile's rows: rows past M (N) read as zero and are never
+    // stored, so ragged tiles need no clamping. K <= 2^23 keeps every offset below 2^32.
+    const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
+    const int64_t rows_w = (N - n0) < BN ? (N - n0) : BN;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(static_cast<const uint8_t*>(p.a) + m0 * K, (uint32_t)(rows_a * K));
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(static_cast<const uint8_t*>(p.w) + n0 * K, (uint32_t)(rows_w * K));
 
-    // Per-lane global source rows for this wave's load chunks (clamped into range so no
-    // load ever leaves the buffers; clamped rows are never stored).
-    const uint8_t* src[CPW];
-    uint32_t lds_off[CPW];
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-        const int chunk = wave + NWAVES * i;
-        const int r = chunk * 8 + (lane >> 3);                 // row within A rows then W rows
-        const int slot = lane & 7;
-        const int c = slot ^ (lane >> 3);                      // (r & 7) == lane >> 3
-        if (r < BM) {
-            int64_t m = m0 + r;
-            m = m < M ? m : M - 1;
-            src[i] = A + m * K + c * 16;
-        } else {
-            int64_t n = n0 + (r - BM);
-            n = n < N ? n : N - 1;
-            src[i] = W + n * K + c * 16;
-        }
-        lds_off[i] = (uint32_t)(chunk * 1024);
-    }
-
+    // Load chunk i of this wave covers region rows 8*(wave + NWAVES*i) .. +7; lane l writes
+    // LDS slot (l & 7) of row +(l >> 3), which holds global chunk (l & 7) ^ swz(row). As
+    // NWAVES is even, swz(row) = (l >> 3) ^ (wave & 1) for every i, so one per-lane byte
+    // offset serves all chunks and the chunk index goes into the scalar offset.
+    const uint32_t dma_voff = (uint32_t)(((lane >> 3) + wave * 8) * K +
+                                         (((lane & 7) ^ (lane >> 3) ^ (wave & 1)) << 4));
     auto issue_stage = [&](int64_t kb, int stage) {
+        const uint32_t skb = (uint32_t)(kb * 128);
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
-            load_lds_16(src[i] + kb * 128, lds, lds_off[i] + stage * STAGE);
+            const uint32_t lds_off = (uint32_t)((wave + NWAVES * i) * 1024 + stage * STAGE);
+            if (i < CPW_A)
+                dma16(ra, lds, lds_off, dma_voff, skb + (uint32_t)(NWAVES * i * 8 * K));
+            else
+                dma16(rw, lds, lds_off, dma_voff, skb + (uint32_t)((NWAVES * i - BM / 8) * 8 * K));
         }
     };
 
-    // Token rows this lane owns in each sub-tile row, and their scale addresses.
-    const float* sa_ptr[SM];
-#pragma unroll
-    for (int sm = 0; sm < SM; ++sm) {
-        int64_t m = m0 + wm * TM + sm * 16 + (lane & 15);
-        m = m < M ? m : M - 1;
-        sa_ptr[sm] = p.sa + m * p.sa_stride_m;
-    }
+    // Activation scales through a buffer: lane part (its token row) + uniform part.
+    const int frow = lane & 15;
+    const int fgrp = lane >> 4;
+    const int64_t ssm = p.sa_stride_m, ssk = p.sa_stride_k;
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
+        p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + (KB - 1) * ssk + 1) * 4));
+    const uint32_t sa_voff = (uint32_t)((wm * TM + frow) * ssm * 4);
     const int64_t nb = (n0 + wn * TN < N ? n0 + wn * TN : N - 1) / 128;
-    const float* sw_row = p.sw + nb * KB;
+    const float* sw_row = p.sw + nb * KB;                      // uniform: scalar loads
 
     v4f acc[SM][SN];
 #pragma unroll
@@ -121,10 +129,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
 #pragma unroll
         for (int sn = 0; sn < SN; ++sn) acc[sm][sn] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Fragment read offsets: lane l reads row (l % 16) of a sub-tile; chunk pair for fp8,
-    // single chunk per K half for int8.
-    const int frow = lane & 15;
-    const int fgrp = lane >> 4;
+    // Per-lane LDS byte offsets of the fragment rows (sub-tile 0), chunk slots resolved.
+    // A sub-tile row sm adds sm*2048, a W sub-tile sn adds sn*2048 (swz depends on r & 15).
+    const int fsw = swz(frow);
+    const uint32_t a_row = (uint32_t)((wm * TM + frow) * 128);
+    const uint32_t w_row = (uint32_t)((BM + wn * TN + frow) * 128);
 
     // Scales of the next K block are loaded one iteration ahead, before that block's
     // global->LDS loads, so waiting for them never waits for the tile prefetch.
@@ -132,18 +141,99 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     auto load_scales = [&](int64_t kb) {
         sw_next = sw_row[kb];
 #pragma unroll
-        for (int sm = 0; sm < SM; ++sm) sa_next[sm] = sa_ptr[sm][kb * p.sa_stride_k];
+        for (int sm = 0; sm < SM; ++sm)
+            sa_next[sm] = buf_f32(rsa, sa_voff, (uint32_t)((kb * ssk + sm * 16 * ssm) * 4));
     };
 
-    if (kb_begin < kb_end) {
-        load_scales(kb_begin);
-        issue_stage(kb_begin, 0);
-        wait_vmem_all();
-        __syncthreads();
-    }
+    auto lds16 = [&](uint32_t off) { return *reinterpret_cast<const v4i*>(lds + off); };
 
-    for (int64_t kb = kb_begin; kb < kb_end; ++kb) {
-        const int stage = (int)((kb - kb_begin) & 1);
+    // One K block on LDS stage `stage`: fragments from LDS, MFMA, scale fusion.
+    auto compute = [&](uint32_t sbase, const float (&c)[SM]) {
+        if constexpr (QT == Q_FP8) {
+            const uint32_t s0 = (uint32_t)(((2 * fgrp) ^ fsw) << 4);
+            const uint32_t s1 = (uint32_t)(((2 * fgrp + 1) ^ fsw) << 4);
+            const uint32_t abase = sbase + a_row, wbase = sbase + w_row;
+            v8i af[SM];
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm) {
+                const v4i lo = lds16(abase + sm * 2048 + s0);
+                const v4i hi = lds16(abase + sm * 2048 + s1);
+                af[sm] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            }
+            auto fma4 = [&](v4f& a, const v4f& q, float cc) {
+                a.x = __builtin_fmaf(q.x, cc, a.x);
+                a.y = __builtin_fmaf(q.y, cc, a.y);
+                a.z = __builtin_fmaf(q.z, cc, a.z);
+                a.w = __builtin_fmaf(q.w, cc, a.w);
+            };
+            auto read_w = [&](int sn) {
+                const v4i lo = lds16(wbase + sn * 2048 + s0);
+                const v4i hi = lds16(wbase + sn * 2048 + s1);
+                return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            };
+            if constexpr (SCHED == 0) {
+                // per W sub-tile: read it, its MFMAs, their scale FMAs
+#pragma unroll
+                for (int sn = 0; sn < SN; ++sn) {
+                    const v8i wf = read_w(sn);
+#pragma unroll
+                    for (int sm = 0; sm < SM; ++sm) fma4(acc[sm][sn], mfma_fp8_16x16x128(wf, af[sm]), c[sm]);
+                }
+            } else {
+                // software-pipelined: MFMAs of sub-tile sn, the read of sn+1, then the scale
+                // FMAs of sn-1 (whose MFMAs finished while sn's were issued); the group
+                // barriers pin that interleave so the register allocator cannot serialise it
+                v8i wf = read_w(0);
+                v4f pb[2][SM];
+#pragma unroll
+                for (int sn = 0; sn < SN; ++sn) {
+#pragma unroll
+                    for (int sm = 0; sm < SM; ++sm) pb[sn & 1][sm] = mfma_fp8_16x16x128(wf, af[sm]);
+                    if (sn + 1 < SN) wf = read_w(sn + 1);
+                    if (sn > 0) {
+#pragma unroll
+                        for (int sm = 0; sm < SM; ++sm) fma4(acc[sm][sn - 1], pb[(sn - 1) & 1][sm], c[sm]);
+                    }
+                }
+#pragma unroll
+                for (int sm = 0; sm < SM; ++sm) fma4(acc[sm][SN - 1], pb[(SN - 1) & 1][sm], c[sm]);
+#pragma unroll
+                for (int sn = 0; sn < SN; ++sn) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, SM, 0);          // MFMA
+                    if (sn + 1 < SN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+                    if (sn > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4 * SM, 0);   // VALU
+                }
+                __builtin_amdgcn_sched_group_barrier(0x002, 4 * SM, 0);
+            }
+        } else {
+            const uint32_t s0 = (uint32_t)(((fgrp) ^ fsw) << 4);
+            const uint32_t s1 = (uint32_t)(((4 + fgrp) ^ fsw) << 4);
+            const uint32_t abase = sbase + a_row, wbase = sbase + w_row;
+            v4i af[SM][2];
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm) {
+                af[sm][0] = lds16(abase + sm * 2048 + s0);
+                af[sm][1] = lds16(abase + sm * 2048 + s1);
+            }
+#pragma unroll
+            for (int sn = 0; sn < SN; ++sn) {
+                const v4i w0 = lds16(wbase + sn * 2048 + s0);
+                const v4i w1 = lds16(wbase + sn * 2048 + s1);
+#pragma unroll
+                for (int sm = 0; sm < SM; ++sm) {
+                    v4i pi = mfma_i8_16x16x64(w0, af[sm][0], v4i{0, 0, 0, 0});
+                    pi = mfma_i8_16x16x64(w1, af[sm][1], pi);
+                    v4f& a = acc[sm][sn];
+                    a.x = __builtin_fmaf((float)pi.x, c[sm], a.x);
+                    a.y = __builtin_fmaf((float)pi.y, c[sm], a.y);
+                    a.z = __builtin_fmaf((float)pi.z, c[sm], a.z);
+                    a.w = __builtin_fmaf((float)pi.w, c[sm], a.w);
+                }
+            }
+        }
+    };
+
+    auto kblock = [&](int64_t kb, int stage) {
         float c[SM];
 #pragma unroll
         for (int sm = 0; sm < SM; ++sm) c[sm] = sa_next[sm] * sw_next;
@@ -151,61 +241,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
             load_scales(kb + 1);
             issue_stage(kb + 1, stage ^ 1);
         }
-
-        const uint8_t* sA = lds + stage * STAGE;
-        const uint8_t* sW = sA + BM * 128;
-
-        if constexpr (QT == Q_FP8) {
-            v8i af[SM];
-#pragma unroll
-            for (int sm = 0; sm < SM; ++sm) {
-                const int r = wm * TM + sm * 16 + frow;
-                const v4i lo = *reinterpret_cast<const v4i*>(sA + r * 128 + (((2 * fgrp) ^ (r & 7)) << 4));
-                const v4i hi = *reinterpret_cast<const v4i*>(sA + r * 128 + (((2 * fgrp + 1) ^ (r & 7)) << 4));
-                af[sm] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            }
-#pragma unroll
-            for (int sn = 0; sn < SN; ++sn) {
-                const int r = wn * TN + sn * 16 + frow;
-                const v4i lo = *reinterpret_cast<const v4i*>(sW + r * 128 + (((2 * fgrp) ^ (r & 7)) << 4));
-                const v4i hi = *reinterpret_cast<const v4i*>(sW + r * 128 + (((2 * fgrp + 1) ^ (r & 7)) << 4));
-                const v8i wf = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-                for (int sm = 0; sm < SM; ++sm) {
-                    const v4f pb = mfma_fp8_16x16x128(wf, af[sm]);
-                    acc[sm][sn].x = __builtin_fmaf(pb.x, c[sm], acc[sm][sn].x);
-                    acc[sm][sn].y = __builtin_fmaf(pb.y, c[sm], acc[sm][sn].y);
-                    acc[sm][sn].z = __builtin_fmaf(pb.z, c[sm], acc[sm][sn].z);
-                    acc[sm][sn].w = __builtin_fmaf(pb.w, c[sm], acc[sm][sn].w);
-                }
-            }
-        } else {
-            v4i af[SM][2];
-#pragma unroll
-            for (int sm = 0; sm < SM; ++sm) {
-                const int r = wm * TM + sm * 16 + frow;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    af[sm][h] = *reinterpret_cast<const v4i*>(sA + r * 128 + (((4 * h + fgrp) ^ (r & 7)) << 4));
-            }
-#pragma unroll
-            for (int sn = 0; sn < SN; ++sn) {
-                const int r = wn * TN + sn * 16 + frow;
-                const v4i w0 = *reinterpret_cast<const v4i*>(sW + r * 128 + (((fgrp) ^ (r & 7)) << 4));
-                const v4i w1 = *reinterpret_cast<const v4i*>(sW + r * 128 + (((4 + fgrp) ^ (r & 7)) << 4));
-#pragma unroll
-                for (int sm = 0; sm < SM; ++sm) {
-                    v4i pi = mfma_i8_16x16x64(w0, af[sm][0], v4i{0, 0, 0, 0});
-                    pi = mfma_i8_16x16x64(w1, af[sm][1], pi);
-                    acc[sm][sn].x = __builtin_fmaf((float)pi.x, c[sm], acc[sm][sn].x);
-                    acc[sm][sn].y = __builtin_fmaf((float)pi.y, c[sm], acc[sm][sn].y);
-                    acc[sm][sn].z = __builtin_fmaf((float)pi.z, c[sm], acc[sm][sn].z);
-                    acc[sm][sn].w = __builtin_fmaf((float)pi.w, c[sm], acc[sm][sn].w);
-                }
-            }
-        }
+        compute((uint32_t)(stage * STAGE), c);
         wait_vmem_all();
         __syncthreads();
+    };
+
+    if (kb_begin < kb_end) {
+        load_scales(kb_begin);
+        issue_stage(kb_begin, 0);
+        wait_vmem_all();
+        __syncthreads();
+        for (int64_t kb = kb_begin; kb < kb_end; ++kb) kblock(kb, (int)((kb - kb_begin) & 1));
     }
 
     // Epilogue: lane owns token m and columns n..n+3 of each sub-tile.
@@ -223,7 +269,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     }
 }
 
-template <int BM, int BN, int WM, int WN, int QT, int OT, int GROUP_M>
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED>
 hipError_t launch_std(const GemmArgs& a, hipStream_t stream) {
     constexpr int STAGE = (BM + BN) * 128;
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
@@ -231,32 +277,36 @@ hipError_t launch_std(const GemmArgs& a, hipStream_t stream) {
     static bool attr_set = false;   // one-time opt-in to more than 64 KB of LDS
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&gemm_std_kernel<BM, BN, WM, WN, QT, OT, GROUP_M>),
+            reinterpret_cast<const void*>(&gemm_std_kernel<BM, BN, WM, WN, QT, OT, SCHED>),
             hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((gemm_std_kernel<BM, BN, WM, WN, QT, OT, GROUP_M>), grid,
+    hipLaunchKernelGGL((gemm_std_kernel<BM, BN, WM, WN, QT, OT, SCHED>), grid,
                        dim3(64 * WM * WN), 2 * STAGE, stream, a);
     return hipGetLastError();
 }
 
-#define BFQ_STD_ENTRY(BM, BN, WM, WN, GM, QT, OT)                                        \
-    KernelEntry{bfq_tile{0, BM, BN, 128, 1, WM, WN, 2, GM, {0, 0, 0}}, QT, OT,            \
-                &launch_std<BM, BN, WM, WN, QT, OT, GM>}
+#define BFQ_STD_ENTRY(BM, BN, WM, WN, GM, SC, QT, OT)                                    \
+    KernelEntry{bfq_tile{0, BM, BN, 128, 1, WM, WN, 2, GM, SC, 0, 0}, QT, OT,             \
+                &launch_std<BM, BN, WM, WN, QT, OT, SC>}
 
-#define BFQ_STD_ALL_OUT(BM, BN, WM, WN, GM, QT)                                           \
-    BFQ_STD_ENTRY(BM, BN, WM, WN, GM, QT, O_BF16), BFQ_STD_ENTRY(BM, BN, WM, WN, GM, QT, O_FP16), \
-        BFQ_STD_ENTRY(BM, BN, WM, WN, GM, QT, O_FP32)
+#define BFQ_STD_ALL_OUT(BM, BN, WM, WN, GM, SC, QT)                                       \
+    BFQ_STD_ENTRY(BM, BN, WM, WN, GM, SC, QT, O_BF16),                                    \
+        BFQ_STD_ENTRY(BM, BN, WM, WN, GM, SC, QT, O_FP16),                                \
+        BFQ_STD_ENTRY(BM, BN, WM, WN, GM, SC, QT, O_FP32)
 
 static const KernelEntry kStdKernels[] = {
-    BFQ_STD_ALL_OUT(256, 256, 4, 2, 8, Q_FP8),
-    BFQ_STD_ALL_OUT(128, 256, 2, 2, 8, Q_FP8),
-    BFQ_STD_ALL_OUT(128, 128, 2, 2, 8, Q_FP8),
-    BFQ_STD_ALL_OUT(64, 128, 1, 2, 8, Q_FP8),
-    BFQ_STD_ALL_OUT(256, 256, 4, 2, 8, Q_INT8),
-    BFQ_STD_ALL_OUT(128, 128, 2, 2, 8, Q_INT8),
-    BFQ_STD_ALL_OUT(64, 128, 1, 2, 8, Q_INT8),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 8, 0, Q_FP8),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 8, 1, Q_FP8),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 8, 0, Q_FP8),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 8, 1, Q_FP8),
+    BFQ_STD_ALL_OUT(256, 128, 4, 1, 8, 1, Q_FP8),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 8, 0, Q_FP8),
+    BFQ_STD_ALL_OUT(64, 128, 1, 2, 8, 0, Q_FP8),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 8, 0, Q_INT8),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 8, 0, Q_INT8),
+    BFQ_STD_ALL_OUT(64, 128, 1, 2, 8, 0, Q_INT8),
 };
 
 const KernelEntry* std_kernels(int* count) {

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_swapab_kernel(GemmArgs p) {
     static_assert(128 % NWR == 0, "a wave's rows must lie in one 128-row scale block");
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int frow = lane & 15, fgrp = lane >> 4;
 
     const int64_t M = p.M, N = p.N, K = p.K, KB = K / 128;
@@ -67,6 +67,9 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_swapab_kernel(GemmArgs p) {
     float swb[D];
 
     auto fetch = [&](int slot, int64_t kb) {
+        swb[slot] = sw_row[kb];
+#pragma unroll
+        for (int sm = 0; sm < SM; ++sm) sab[slot][sm] = sa_ptr[sm][kb * p.sa_stride_k];
 #pragma unroll
         for (int sn = 0; sn < SN; ++sn) {
             wbuf[slot][sn][0] = *reinterpret_cast<const v4i*>(wrow[sn] + kb * 128);
@@ -76,9 +79,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_swapab_kernel(GemmArgs p) {
         for (int sm = 0; sm < SM; ++sm) {
             abuf[slot][sm][0] = *reinterpret_cast<const v4i*>(arow[sm] + kb * 128);
             abuf[slot][sm][1] = *reinterpret_cast<const v4i*>(arow[sm] + kb * 128 + 64);
-            sab[slot][sm] = sa_ptr[sm][kb * p.sa_stride_k];
         }
-        swb[slot] = sw_row[kb];
     };
 
     v4f acc[SM][SN];
@@ -87,45 +88,60 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_swapab_kernel(GemmArgs p) {
 #pragma unroll
         for (int sn = 0; sn < SN; ++sn) acc[sm][sn] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    if (wave_live) {
+    auto consume = [&](int i) {
 #pragma unroll
-        for (int i = 0; i < D; ++i)
-            if (kb_begin + i < kb_end) fetch(i, kb_begin + i);
-
-        for (int64_t kb0 = kb_begin; kb0 < kb_end; kb0 += D) {
+        for (int sm = 0; sm < SM; ++sm) {
+            const float c = sab[i][sm] * swb[i];
 #pragma unroll
-            for (int i = 0; i < D; ++i) {
-                const int64_t kb = kb0 + i;
-                if (kb < kb_end) {
-#pragma unroll
-                    for (int sm = 0; sm < SM; ++sm) {
-                        const float c = sab[i][sm] * swb[i];
-#pragma unroll
-                        for (int sn = 0; sn < SN; ++sn) {
-                            v4f pb;
-                            if constexpr (QT == Q_FP8) {
-                                const v4i* w2 = wbuf[i][sn];
-                                const v4i* a2 = abuf[i][sm];
-                                const v8i wf = v8i{w2[0].x, w2[0].y, w2[0].z, w2[0].w,
-                                                   w2[1].x, w2[1].y, w2[1].z, w2[1].w};
-                                const v8i af = v8i{a2[0].x, a2[0].y, a2[0].z, a2[0].w,
-                                                   a2[1].x, a2[1].y, a2[1].z, a2[1].w};
-                                pb = mfma_fp8_16x16x128(wf, af);
-                            } else {
-                                v4i pi = mfma_i8_16x16x64(wbuf[i][sn][0], abuf[i][sm][0], v4i{0, 0, 0, 0});
-                                pi = mfma_i8_16x16x64(wbuf[i][sn][1], abuf[i][sm][1], pi);
-                                pb = v4f{(float)pi.x, (float)pi.y, (float)pi.z, (float)pi.w};
-                            }
-                            acc[sm][sn].x = __builtin_fmaf(pb.x, c, acc[sm][sn].x);
-                            acc[sm][sn].y = __builtin_fmaf(pb.y, c, acc[sm][sn].y);
-                            acc[sm][sn].z = __builtin_fmaf(pb.z, c, acc[sm][sn].z);
-                            acc[sm][sn].w = __builtin_fmaf(pb.w, c, acc[sm][sn].w);
-                        }
-                    }
-                    if (kb + D < kb_end) fetch(i, kb + D);
+            for (int sn = 0; sn < SN; ++sn) {
+                v4f pb;
+                if constexpr (QT == Q_FP8) {
+                    const v4i* w2 = wbuf[i][sn];
+                    const v4i* a2 = abuf[i][sm];
+                    const v8i wf = v8i{w2[0].x, w2[0].y, w2[0].z, w2[0].w,
+                                       w2[1].x, w2[1].y, w2[1].z, w2[1].w};
+                    const v8i af = v8i{a2[0].x, a2[0].y, a2[0].z, a2[0].w,
+                                       a2[1].x, a2[1].y, a2[1].z, a2[1].w};
+                    pb = mfma_fp8_16x16x128(wf, af);
+                } else {
+                    v4i pi = mfma_i8_16x16x64(wbuf[i][sn][0], abuf[i][sm][0], v4i{0, 0, 0, 0});
+                    pi = mfma_i8_16x16x64(wbuf[i][sn][1], abuf[i][sm][1], pi);
+                    pb = v4f{(float)pi.x, (float)pi.y, (float)pi.z, (float)pi.w};
                 }
+                acc[sm][sn].x = __builtin_fmaf(pb.x, c, acc[sm][sn].x);
+                acc[sm][sn].y = __builtin_fmaf(pb.y, c, acc[sm][sn].y);
+                acc[sm][sn].z = __builtin_fmaf(pb.z, c, acc[sm][sn].z);
+                acc[sm][sn].w = __builtin_fmaf(pb.w, c, acc[sm][sn].w);
             }
         }
+    };
+
+    if (wave_live && kb_begin < kb_end) {
+        // Ring of D K-blocks in flight. The steady-state loop is branch-free: a refill past
+        // the end of this split re-reads its last block (never used), so the compiler can
+        // count outstanding loads exactly instead of draining the queue at every join.
+        const int64_t kb_last = kb_end - 1;
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            const int64_t kb = kb_begin + i;
+            fetch(i, kb < kb_last ? kb : kb_last);
+        }
+        int64_t kb0 = kb_begin;
+        for (; kb0 + D <= kb_end; kb0 += D) {
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                // keep each slot's work in its own stage: the scheduler must not hoist the
+                // scale products of later slots (that would wait for every load in flight)
+                __builtin_amdgcn_sched_barrier(0);
+                consume(i);
+                const int64_t nk = kb0 + i + D;
+                fetch(i, nk < kb_last ? nk : kb_last);
+            }
+        }
+        const int rem = (int)(kb_end - kb0);
+#pragma unroll
+        for (int i = 0; i < D; ++i)
+            if (i < rem) consume(i);
 
 #pragma unroll
         for (int sm = 0; sm < SM; ++sm) {
@@ -151,7 +167,7 @@ hipError_t launch_swapab(const GemmArgs& a, hipStream_t stream) {
 }
 
 #define BFQ_SAB_ENTRY(MT, NWR, NW, D, QT, OT)                                              \
-    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, 1, NW, D, 1, {0, 0, 0}}, QT, OT,          \
+    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, 1, NW, D, 1, 0, 0, 0}, QT, OT,          \
                 &launch_swapab<MT, NWR, NW, D, QT, OT>}
 #define BFQ_SAB_ALL_OUT(MT, NWR, NW, D, QT)                                                \
     BFQ_SAB_ENTRY(MT, NWR, NW, D, QT, O_BF16), BFQ_SAB_ENTRY(MT, NWR, NW, D, QT, O_FP16),   \
@@ -160,6 +176,10 @@ hipError_t launch_swapab(const GemmArgs& a, hipStream_t stream) {
 static const KernelEntry kSwapabKernels[] = {
     BFQ_SAB_ALL_OUT(16, 32, 4, 4, Q_FP8),
     BFQ_SAB_ALL_OUT(16, 16, 4, 8, Q_FP8),
+    BFQ_SAB_ALL_OUT(16, 16, 8, 8, Q_FP8),
+    BFQ_SAB_ALL_OUT(16, 32, 8, 4, Q_FP8),
+    BFQ_SAB_ALL_OUT(16, 64, 4, 2, Q_FP8),
+    BFQ_SAB_ALL_OUT(16, 32, 4, 8, Q_FP8),
     BFQ_SAB_ALL_OUT(32, 32, 4, 4, Q_FP8),
     BFQ_SAB_ALL_OUT(64, 32, 4, 2, Q_FP8),
     BFQ_SAB_ALL_OUT(16, 32, 4, 4, Q_INT8),

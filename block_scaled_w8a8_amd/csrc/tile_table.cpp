@@ -179,12 +179,12 @@ bool parse_tile_table(const std::string& text, TileTable& out, std::string& err)
                 return false;
             }
             if (kv.second.kind != JVal::OBJ) { err = "config is not an object"; return false; }
-            int64_t f[8];
-            const char* names[8] = {"variant", "bm", "bn", "split_k", "waves_m", "waves_n",
-                                    "stages", "group_m"};
-            const int64_t dflt[8] = {0, 0, 0, 1, 1, 1, 2, 1};
-            const bool req[8] = {true, true, true, false, true, true, false, false};
-            for (int j = 0; j < 8; ++j)
+            int64_t f[10];
+            const char* names[10] = {"variant", "bm", "bn", "split_k", "waves_m", "waves_n",
+                                     "stages", "group_m", "sched", "raster"};
+            const int64_t dflt[10] = {0, 0, 0, 1, 1, 1, 2, 1, 0, 0};
+            const bool req[10] = {true, true, true, false, true, true, false, false, false, false};
+            for (int j = 0; j < 10; ++j)
                 if (!get_int(kv.second, names[j], f[j], req[j], dflt[j], err)) return false;
             bfq_tile tl{};
             tl.variant = (int32_t)f[0];
@@ -196,6 +196,8 @@ bool parse_tile_table(const std::string& text, TileTable& out, std::string& err)
             tl.waves_n = (int32_t)f[5];
             tl.stages = (int32_t)f[6];
             tl.group_m = (int32_t)f[7];
+            tl.sched = (int32_t)f[8];
+            tl.raster = (int32_t)f[9];
             buckets[(int64_t)m] = tl;
         }
         if (buckets.empty()) { err = "entry has no configs"; return false; }

@@ -1,0 +1,284 @@
+"""On-device tile sweep that fills the tile table, and a single-shape runner for profiling.
+
+  python -m block_scaled_w8a8_amd.sweep tune  [--shapes N,K ...] [--dtype fp8|int8] [--out PATH]
+  python -m block_scaled_w8a8_amd.sweep run   --M 4096 --N 24576 --K 7168 [--tile JSON] [--iters 50]
+  python -m block_scaled_w8a8_amd.sweep copy  [--bytes N]   (byte-counter calibration)
+
+`tune` follows the tuning flow of the config-mechanism page ("vLLM 量化 Kernel 配置机制 ...",
+§3.3): for every (N, K) and every M of the 18-point grid, every compiled kernel configuration
+(combined with split-K factors) is launched after warm-up and timed with events; the fastest
+one whose output agrees with a reference configuration is kept. Configurations the library
+rejects (grid or workspace limits) are skipped, like the page's OutOfResources candidates.
+Results are written to a JSON tile table after every shape, and shapes already present in the
+output file are skipped, so an interrupted sweep resumes where it stopped.
+
+Timing rotates over enough copies of the weights and activations to exceed the 256 MB
+Infinity Cache, so the weight stream is measured from HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_TABLE = os.path.join(HERE, "tables", "gfx950.json")
+M_GRID = [1, 2, 4, 8, 16, 24, 32, 48, 64, 96, 128, 256, 512, 1024, 1536, 2048, 3072, 4096]
+DEFAULT_SHAPES = {"fp8": [(24576, 7168), (7168, 1536), (1536, 7168), (4096, 7168), (7168, 18432),
+                          (18432, 7168), (1536, 1536)],
+                  "int8": [(1536, 7168)]}
+SPLITS = (1, 2, 3, 4, 6, 8, 12, 16)
+GROUPS = (4, 8, 16)
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Problem:
+    """Device buffers for one (N, K) and the largest M, with rotation copies."""
+
+    def __init__(self, N, K, m_max, qname, rotate=None):
+        import torch
+
+        from . import bfq, synth
+        self.N, self.K, self.qname = N, K, qname
+        self.qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
+        dev = torch.device("cuda:0")
+        x = synth.activations(m_max, K, seed=0).to(dev)
+        w = synth.weights(N, K, seed=0).to(dev)
+        qw, sw = bfq.quant_weight_blocks(w, q_dtype=self.qd)
+        qa, sa = bfq.quant_tokens(x, q_dtype=self.qd)
+        del w, x
+        foot = N * K + m_max * K
+        if rotate is None:
+            rotate = max(1, min(8, -(-(2 * MALL_BYTES) // max(foot, 1))))
+        self.sets = [(qa, sa, qw, sw)]
+        for _ in range(rotate - 1):
+            self.sets.append((qa.clone(), sa.clone(), qw.clone(), sw.clone()))
+        self.out = torch.empty((m_max, N), dtype=torch.bfloat16, device=dev)
+        self.out32 = torch.empty((m_max, N), dtype=torch.float32, device=dev)
+        self.ws = None
+        self.ws_bytes = 0
+        torch.cuda.synchronize()
+
+    def workspace(self, nbytes):
+        import torch
+        if nbytes > self.ws_bytes:
+            self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+            self.ws_bytes = nbytes
+        return self.ws
+
+    def launch(self, M, tile, i=0, out32=False):
+        from . import bfq
+        qa, sa, qw, sw = self.sets[i % len(self.sets)]
+        need = bfq.bfq_gemm_workspace_bytes(M, self.N, self.K, tile)
+        ws = self.workspace(need) if need else None
+        out = self.out32 if out32 else self.out
+        return bfq.bfq_block_gemm(qa[:M], sa[:M], qw, sw, out[:M], tile=tile, workspace=ws,
+                                  workspace_bytes=need)
+
+    def time_us(self, M, tile, warmup=3, iters=20, reps=3):
+        """Median over reps of the mean time of `iters` back-to-back launches, replayed from a
+        captured graph (no host launch cost between kernels); rotation over the copies."""
+        import torch
+        for i in range(warmup):
+            self.launch(M, tile, i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(iters):
+                self.launch(M, tile, i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        res = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            res.append(a.elapsed_time(b) * 1e3 / iters)
+        del g
+        res.sort()
+        return res[len(res) // 2]
+
+
+def candidates(qd, M, N, K):
+    from . import bfq
+    out = []
+    KB = K // 128
+    for i in range(bfq.bfq_num_tile_candidates(qd)):
+        t = bfq.bfq_get_tile_candidate(i, qd)
+        if t.variant == 1 and M > 4 * t.bm:
+            continue                       # streaming kernel re-reads W per token tile
+        if t.variant == 0 and M <= 16 and t.bm > 64:
+            continue
+        orders = [(8, 0)] if t.variant == 1 else [(g, r) for g in GROUPS for r in (0, 1)]
+        for s in SPLITS:
+            if s > KB or KB // s < 2:
+                continue
+            for g, r in orders:
+                d = t.as_dict()
+                d["split_k"] = s
+                if t.variant == 0:
+                    d["group_m"], d["raster"] = g, r
+                out.append(bfq.bfq_tile.from_dict(d))
+    return out
+
+
+def agrees(a, b) -> bool:
+    """Parity gate between two fp32 outputs of the same inputs (different tiles): relative
+    Frobenius <= 1e-3 and max |diff| <= 2^-7 rms + 1e-3."""
+    import torch
+    a64, b64 = a.double(), b.double()
+    den = torch.linalg.norm(b64)
+    rf = float(torch.linalg.norm(a64 - b64) / den) if den > 0 else float(torch.linalg.norm(a64))
+    rms = float(torch.sqrt((b64 * b64).mean()))
+    md = float((a64 - b64).abs().max())
+    return rf <= 1e-3 and md <= 2.0 ** -7 * rms + 1e-3
+
+
+def tune_shape(N, K, qname, grid, budget_s):
+    import torch
+
+    from . import bfq
+    prob = Problem(N, K, max(grid), qname)
+    results = {}
+    for M in grid:
+        t0 = time.time()
+        _, ref_tile = bfq.bfq_select_tile(M, N, K, prob.qd, bfq.BFQ_FP32)
+        prob.launch(M, ref_tile, out32=True)
+        torch.cuda.synchronize()
+        ref = prob.out32[:M].clone()
+        best = None
+        trials = []
+        for tile in candidates(prob.qd, M, N, K):
+            if time.time() - t0 > budget_s:
+                break
+            try:
+                prob.launch(M, tile, out32=True)
+                torch.cuda.synchronize()
+            except bfq.BfqError:
+                continue                           # rejected: limits of this configuration
+            if not agrees(prob.out32[:M], ref):
+                log(f"  parity gate rejected {tile.as_dict()} at M={M}")
+                continue
+            us = prob.time_us(M, tile)
+            trials.append((us, tile.as_dict()))
+            if best is None or us < best[0]:
+                best = (us, tile)
+        trials.sort(key=lambda t: t[0])
+        for us, d in trials[:4]:
+            log(f"    {us:9.2f} us  {d}")
+        results[M] = (best[0], best[1].as_dict())
+        d = best[1].as_dict()
+        log(f"  N={N} K={K} M={M:5d}: {best[0]:9.2f} us  variant={d['variant']} bm={d['bm']} "
+            f"bn={d['bn']} split={d['split_k']} ({time.time() - t0:.1f} s)")
+    del prob
+    torch.cuda.empty_cache()
+    return results
+
+
+def load_table(path):
+    if os.path.exists(path):
+        with open(path) as f:
+            return json.load(f)
+    return {"device": "gfx950", "entries": []}
+
+
+def save_table(path, table):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    tmp = path + ".tmp"
+    with open(tmp, "w") as f:
+        json.dump(table, f, indent=1)
+    os.replace(tmp, path)
+
+
+def cmd_tune(args):
+    qname = args.dtype
+    shapes = [tuple(int(v) for v in s.split(",")) for s in args.shapes] if args.shapes \
+        else DEFAULT_SHAPES[qname]
+    table = load_table(args.out)
+    dname = "fp8_w8a8" if qname == "fp8" else "int8_w8a8"
+    done = {(e["N"], e["K"], e["dtype"]) for e in table["entries"]}
+    for (N, K) in shapes:
+        if (N, K, dname) in done and not args.force:
+            log(f"[sweep] N={N} K={K} {dname}: already in {args.out}, skipped")
+            continue
+        log(f"[sweep] N={N} K={K} {dname}")
+        res = tune_shape(N, K, qname, args.grid or M_GRID, args.budget)
+        entry = {"N": N, "K": K, "dtype": dname, "block_shape": [128, 128],
+                 "configs": {str(M): {k: v for k, v in t.items() if k != "bk"}
+                             for M, (us, t) in res.items()},
+                 "us": {str(M): round(us, 3) for M, (us, t) in res.items()}}
+        table["entries"] = [e for e in table["entries"]
+                            if (e["N"], e["K"], e["dtype"]) != (N, K, dname)] + [entry]
+        save_table(args.out, table)
+    print(json.dumps({"table": args.out, "entries": len(table["entries"])}))
+
+
+def cmd_run(args):
+    import torch
+
+    from . import bfq
+    prob = Problem(args.N, args.K, args.M, args.dtype, rotate=args.rotate)
+    if args.tile:
+        tile = bfq.bfq_tile.from_dict(json.loads(args.tile))
+    else:
+        _, tile = bfq.bfq_select_tile(args.M, args.N, args.K, prob.qd, bfq.BFQ_BF16)
+    us = prob.time_us(args.M, tile, warmup=3, iters=args.iters, reps=1)
+    from . import perf
+    s = us * 1e-6
+    print(json.dumps({"M": args.M, "N": args.N, "K": args.K, "tile": tile.as_dict(), "us": us,
+                      "tflops": perf.tflops(args.M, args.N, args.K, s),
+                      "gbs_all": perf.gbs_all(args.M, args.N, args.K, s)}), flush=True)
+    torch.cuda.synchronize()
+
+
+def cmd_copy(args):
+    """A plain device-to-device copy of known size: the reference the HBM byte counters
+    (FETCH_SIZE / WRITE_SIZE) are scaled against."""
+    import torch
+    n = args.bytes
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    torch.cuda.synchronize()
+    for _ in range(args.iters):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "iters": args.iters}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("tune")
+    t.add_argument("--shapes", nargs="*")
+    t.add_argument("--dtype", default="fp8", choices=["fp8", "int8"])
+    t.add_argument("--grid", type=int, nargs="*")
+    t.add_argument("--out", default=DEFAULT_TABLE)
+    t.add_argument("--budget", type=float, default=20.0, help="seconds per (shape, M)")
+    t.add_argument("--force", action="store_true")
+    r = sub.add_parser("run")
+    r.add_argument("--M", type=int, required=True)
+    r.add_argument("--N", type=int, required=True)
+    r.add_argument("--K", type=int, required=True)
+    r.add_argument("--dtype", default="fp8", choices=["fp8", "int8"])
+    r.add_argument("--tile")
+    r.add_argument("--iters", type=int, default=50)
+    r.add_argument("--rotate", type=int, default=None)
+    c = sub.add_parser("copy")
+    c.add_argument("--bytes", type=int, default=1 << 30)
+    c.add_argument("--iters", type=int, default=3)
+    args = ap.parse_args()
+    {"tune": cmd_tune, "run": cmd_run, "copy": cmd_copy}[args.cmd](args)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,7 +20,8 @@
  *    was launched and no output was touched; bfq_last_error() holds a detail string
  *    (thread-local). A positive status is success with a warning.
  *  - M = 0 is valid and launches nothing.
- *  - Shapes are int64; K and N must be multiples of 128, and x/q/w/out 16-byte aligned.
+ *  - Shapes are int64; K and N must be multiples of 128 (GEMM: K <= 2^23, scale ld <= 2^23),
+ *    and x/q/w/out 16-byte aligned.
  *  - Two calls on one stream are ordered; calls on different streams that share an output
  *    or workspace race.
  */
@@ -73,9 +74,14 @@ typedef enum {
  *   split_k  : K blocks split into split_k contiguous chunks (>= 1), fp32 partials reduced
  *             in a fixed order ([HELION] kernel section).
  *   stages   : LDS stages (variant 0) or weight prefetch depth in K blocks (variant 1).
+ *   sched    : variant 0 instruction schedule: 0 = each sub-tile's scale FMAs right after its
+ *             MFMAs, 1 = software-pipelined (FMAs one sub-tile behind the MFMAs).
+ *   group_m, raster: variant 0 tile order (launch arguments, any group_m >= 1): raster 0
+ *             gives each of the 8 XCDs a contiguous range of tiles, raster 1 does not.
  *   bk is always 128 (one scale block per K step). */
 typedef struct {
-    int32_t variant, bm, bn, bk, split_k, waves_m, waves_n, stages, group_m, reserved[3];
+    int32_t variant, bm, bn, bk, split_k, waves_m, waves_n, stages, group_m, sched, raster,
+        reserved;
 } bfq_tile;
 
 /* Per-token-group quantization ([BENCH] §4.1 per_token_group_quant_fp8; [PR] kernel
