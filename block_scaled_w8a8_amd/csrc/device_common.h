@@ -99,6 +99,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_bas
         r, (__attribute__((address_space(3))) void*)(lds_base + lds_off), 16, voff, soff, 0, 0);
 }
 
+// 4 bytes per lane into LDS (lane l -> lds_base + lds_off + 4 l): used to touch lines ahead.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds_base,
+                                     uint32_t lds_off, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(lds_base + lds_off), 4, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
@@ -112,6 +119,13 @@ __device__ __forceinline__ void load_lds_16(const void* gsrc, uint8_t* lds_base,
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most N vector-memory operations remain outstanding (they complete in issue
+// order, so everything but the N most recent has landed).
+template <int N> __device__ __forceinline__ void wait_vmem_keep_n() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+#define wait_vmem_keep(N) wait_vmem_keep_n<(N)>()
 
 // ---------------------------------------------------------------- output store ----
 // Store four consecutive output values of one row.

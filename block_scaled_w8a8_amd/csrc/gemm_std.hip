@@ -57,7 +57,7 @@ __device__ __forceinline__ void tile_coords(int64_t bid, int64_t tiles_m, int64_
 // 8 lanes x 16 B or 16 lanes x 16 B per cycle. It depends only on r & 15.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED>
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     constexpr int NWAVES = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;      // wave tile (tokens x weight rows)
@@ -110,6 +110,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
                 dma16(ra, lds, lds_off, dma_voff, skb + (uint32_t)(NWAVES * i * 8 * K));
             else
                 dma16(rw, lds, lds_off, dma_voff, skb + (uint32_t)((NWAVES * i - BM / 8) * 8 * K));
+        }
+    };
+
+    // STAGES == 3: besides the two LDS stages, the 128-byte line of every tile row for
+    // K block kb+2 is touched one block early with a 4-byte DMA into a per-wave scratch slot
+    // of LDS, so the next block's tile loads hit L2. Each lane covers one row.
+    static_assert(STAGES == 2 || STAGES == 3, "two LDS stages, optionally one L2 stage");
+    constexpr int PF_ROUNDS = (BM + BN + 64 * NWAVES - 1) / (64 * NWAVES);
+    static_assert(BM % 64 == 0, "prefetch rounds split A and W rows on 64-row boundaries");
+    const uint32_t lane_k = (uint32_t)(lane * K);
+    auto prefetch_l2 = [&](int64_t kb) {
+        const uint32_t skb = (uint32_t)(kb * 128);
+        const uint32_t scratch = (uint32_t)(2 * STAGE + wave * 256);
+#pragma unroll
+        for (int j = 0; j < PF_ROUNDS; ++j) {
+            const int row0 = (j * NWAVES + wave) * 64;          // uniform
+            if (row0 < BM)
+                dma4(ra, lds, scratch, lane_k, skb + (uint32_t)(row0 * K));
+            else if (row0 < BM + BN)
+                dma4(rw, lds, scratch, lane_k, skb + (uint32_t)((row0 - BM) * K));
         }
     };
 
@@ -241,17 +261,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
             load_scales(kb + 1);
             issue_stage(kb + 1, stage ^ 1);
         }
+        if constexpr (STAGES == 3) {
+            // near the end this re-touches the last block (harmless, keeps the loop uniform)
+            __builtin_amdgcn_sched_barrier(0);
+            prefetch_l2(kb + 2 < kb_end ? kb + 2 : kb_end - 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         compute((uint32_t)(stage * STAGE), c);
-        wait_vmem_all();
+        // the L2 touches (issued last) may stay in flight; everything before them must land
+        if constexpr (STAGES == 3) wait_vmem_keep(PF_ROUNDS);
+        else wait_vmem_all();
         __syncthreads();
     };
 
     if (kb_begin < kb_end) {
         load_scales(kb_begin);
         issue_stage(kb_begin, 0);
+        if constexpr (STAGES == 3) prefetch_l2(kb_begin + 1 < kb_end ? kb_begin + 1 : kb_begin);
         wait_vmem_all();
         __syncthreads();
         for (int64_t kb = kb_begin; kb < kb_end; ++kb) kblock(kb, (int)((kb - kb_begin) & 1));
+        wait_vmem_all();      // no LDS DMA may still be in flight when the wave ends
     }
 
     // Epilogue: lane owns token m and columns n..n+3 of each sub-tile.
@@ -269,44 +299,46 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     }
 }
 
-template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED>
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
 hipError_t launch_std(const GemmArgs& a, hipStream_t stream) {
     constexpr int STAGE = (BM + BN) * 128;
+    constexpr int LDS_BYTES = 2 * STAGE + (STAGES > 2 ? 256 * WM * WN : 0);
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     dim3 grid((unsigned)tiles, 1, (unsigned)a.split);
     static bool attr_set = false;   // one-time opt-in to more than 64 KB of LDS
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&gemm_std_kernel<BM, BN, WM, WN, QT, OT, SCHED>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
+            reinterpret_cast<const void*>(&gemm_std_kernel<BM, BN, WM, WN, QT, OT, SCHED, STAGES>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((gemm_std_kernel<BM, BN, WM, WN, QT, OT, SCHED>), grid,
-                       dim3(64 * WM * WN), 2 * STAGE, stream, a);
+    hipLaunchKernelGGL((gemm_std_kernel<BM, BN, WM, WN, QT, OT, SCHED, STAGES>), grid,
+                       dim3(64 * WM * WN), LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 
-#define BFQ_STD_ENTRY(BM, BN, WM, WN, GM, SC, QT, OT)                                    \
-    KernelEntry{bfq_tile{0, BM, BN, 128, 1, WM, WN, 2, GM, SC, 0, 0}, QT, OT,             \
-                &launch_std<BM, BN, WM, WN, QT, OT, SC>}
+#define BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, OT)                                    \
+    KernelEntry{bfq_tile{0, BM, BN, 128, 1, WM, WN, ST, 8, SC, 0, 0}, QT, OT,             \
+                &launch_std<BM, BN, WM, WN, QT, OT, SC, ST>}
 
-#define BFQ_STD_ALL_OUT(BM, BN, WM, WN, GM, SC, QT)                                       \
-    BFQ_STD_ENTRY(BM, BN, WM, WN, GM, SC, QT, O_BF16),                                    \
-        BFQ_STD_ENTRY(BM, BN, WM, WN, GM, SC, QT, O_FP16),                                \
-        BFQ_STD_ENTRY(BM, BN, WM, WN, GM, SC, QT, O_FP32)
+#define BFQ_STD_ALL_OUT(BM, BN, WM, WN, ST, SC, QT)                                       \
+    BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_BF16),                                    \
+        BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_FP16),                                \
+        BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_FP32)
 
 static const KernelEntry kStdKernels[] = {
-    BFQ_STD_ALL_OUT(256, 256, 4, 2, 8, 0, Q_FP8),
-    BFQ_STD_ALL_OUT(256, 256, 4, 2, 8, 1, Q_FP8),
-    BFQ_STD_ALL_OUT(128, 256, 2, 2, 8, 0, Q_FP8),
-    BFQ_STD_ALL_OUT(128, 256, 2, 2, 8, 1, Q_FP8),
-    BFQ_STD_ALL_OUT(256, 128, 4, 1, 8, 1, Q_FP8),
-    BFQ_STD_ALL_OUT(128, 128, 2, 2, 8, 0, Q_FP8),
-    BFQ_STD_ALL_OUT(64, 128, 1, 2, 8, 0, Q_FP8),
-    BFQ_STD_ALL_OUT(256, 256, 4, 2, 8, 0, Q_INT8),
-    BFQ_STD_ALL_OUT(128, 128, 2, 2, 8, 0, Q_INT8),
-    BFQ_STD_ALL_OUT(64, 128, 1, 2, 8, 0, Q_INT8),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 3, 1, Q_FP8),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 0, Q_FP8),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 3, 1, Q_FP8),
+    BFQ_STD_ALL_OUT(256, 128, 4, 1, 3, 1, Q_FP8),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 0, Q_FP8),
+    BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 0, Q_FP8),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_INT8),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 0, Q_INT8),
+    BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 0, Q_INT8),
 };
 
 const KernelEntry* std_kernels(int* count) {

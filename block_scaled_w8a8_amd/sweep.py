@@ -30,7 +30,7 @@ DEFAULT_SHAPES = {"fp8": [(24576, 7168), (7168, 1536), (1536, 7168), (4096, 7168
                           (18432, 7168), (1536, 1536)],
                   "int8": [(1536, 7168)]}
 SPLITS = (1, 2, 3, 4, 6, 8, 12, 16)
-GROUPS = (4, 8, 16)
+NUM_CUS = 256
 MALL_BYTES = 256 << 20
 
 
@@ -110,24 +110,31 @@ class Problem:
 
 
 def candidates(qd, M, N, K):
+    """Compiled kernels x split-K factors x tile orders worth timing at this shape: the
+    streaming kernel only while it re-reads the weights at most 4 times, split-K only while
+    the grid is short of 4 workgroups per CU, tile orders only for multi-tile grids."""
     from . import bfq
     out = []
     KB = K // 128
     for i in range(bfq.bfq_num_tile_candidates(qd)):
         t = bfq.bfq_get_tile_candidate(i, qd)
         if t.variant == 1 and M > 4 * t.bm:
-            continue                       # streaming kernel re-reads W per token tile
+            continue
         if t.variant == 0 and M <= 16 and t.bm > 64:
             continue
-        orders = [(8, 0)] if t.variant == 1 else [(g, r) for g in GROUPS for r in (0, 1)]
+        if t.variant == 1:
+            ctas = -(-N // t.bn) * -(-M // t.bm)
+            orders = [(1, 0)]
+        else:
+            ctas = -(-M // t.bm) * -(-N // t.bn)
+            orders = [(8, 0), (2, 1)] if ctas >= 64 else [(8, 0)]
         for s in SPLITS:
-            if s > KB or KB // s < 2:
+            if s > KB or KB // s < 2 or (s > 1 and ctas * s > 4 * NUM_CUS):
                 continue
             for g, r in orders:
                 d = t.as_dict()
                 d["split_k"] = s
-                if t.variant == 0:
-                    d["group_m"], d["raster"] = g, r
+                d["group_m"], d["raster"] = g, r
                 out.append(bfq.bfq_tile.from_dict(d))
     return out
 
