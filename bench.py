@@ -47,6 +47,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_name(t, qtype: str, out: str = "bf16") -> str:
+    """The demangled name of the device kernel a tile launches (as rocprofv3 prints it)."""
+    q = 0 if qtype == "fp8" else 1
+    o = {"bf16": 0, "fp16": 1, "fp32": 2}[out]
+    d = t.as_dict()
+    if d["variant"] == 0:
+        return (f"bfq::gemm_std_kernel<{d['bm']}, {d['bn']}, {d['waves_m']}, {d['waves_n']}, "
+                f"{q}, {o}, {d['sched']}, {d['stages']}>")
+    nwr = d["bn"] // d["waves_n"]
+    return f"bfq::gemm_swapab_kernel<{d['bm']}, {nwr}, {d['waves_n']}, {d['stages']}, {q}, {o}>"
+
+
+def grid_threads(t, M, N) -> int:
+    d = t.as_dict()
+    if d["variant"] == 0:
+        wg = -(-M // d["bm"]) * -(-N // d["bn"]) * d["split_k"]
+        return wg * 64 * d["waves_m"] * d["waves_n"]
+    wg = -(-N // d["bn"]) * -(-M // d["bm"]) * d["split_k"]
+    return wg * 64 * d["waves_n"]
+
+
 def tile_key(t) -> str:
     d = t.as_dict()
     return "v{variant}_bm{bm}_bn{bn}_w{waves_m}x{waves_n}_s{stages}_c{sched}_g{group_m}_r{raster}_k{split_k}".format(**d)
@@ -192,7 +213,10 @@ def run_gpu(args, wl):
                 "roofline_frac": round(perf.roofline_time_s(M, N, K) / g, 4),
                 "quant_gbs": round(perf.quant_bytes(M, K) / q / 1e9, 1),
             })
-            gr = groups.setdefault(r["key"], {"t": 0.0, "n": 0, "flops": 0.0, "bytes": 0.0})
+            gr = groups.setdefault(r["key"], {"t": 0.0, "n": 0, "flops": 0.0, "bytes": 0.0,
+                                              "name": kernel_name(tile, wl["qtype"]),
+                                              "grids": set()})
+            gr["grids"].add(grid_threads(tile, M, N))
             gr["t"] += sum(r["g"])
             gr["n"] += len(r["g"])
             gr["flops"] += perf.gemm_flops(M, N, K) * len(r["g"])
@@ -210,8 +234,10 @@ def run_gpu(args, wl):
         achieved = dom["bytes"] / dom["t"] / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": perf.HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / perf.HBM_PEAK_GBS, 4)}
-    roof["traffic"] = None
-    roof["kernel"] = dom_key
+    roof["traffic"] = traffic_for(args, dom, wl)
+    roof["kernel"] = dom["name"]
+    roof["tile"] = dom_key
+    roof["grid_threads"] = sorted(dom["grids"])
     roof["launches"] = dom["n"]
     roof["avg_launch_us"] = round(dom["t"] / dom["n"] * 1e6, 2)
     return {
@@ -221,6 +247,21 @@ def run_gpu(args, wl):
         "roofline": roof,
         "host": host,
     }
+
+
+def traffic_for(args, dom, wl):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 --pmc summary,
+    if it was taken on this kernel (same name, same grid sizes, same kernel sources)."""
+    from block_scaled_w8a8_amd import profile_summary
+    path = os.path.join(REPO, "profiles", f"gemm_traffic_{args.workload}.txt")
+    if not os.path.exists(path):
+        return None
+    t = profile_summary.read_traffic(path)
+    if (t.get("kernel_sources") != profile_summary.source_hash()
+            or dom["name"] not in t.get("kernel", "")
+            or t.get("grid_threads") != ",".join(str(g) for g in sorted(dom["grids"]))):
+        return None
+    return float(t["hbm_bytes_per_dispatch"])
 
 
 def cpu_baseline(wl, host, target_s: float):
@@ -261,7 +302,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mgrid", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=2, help="weight copies rotated per launch")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     args = ap.parse_args()
