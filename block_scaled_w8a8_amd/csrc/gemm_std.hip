@@ -72,12 +72,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     static_assert(NWAVES % 2 == 0, "the swizzle phase of a lane's chunks needs an even wave count");
     constexpr int CPW = CHUNKS / NWAVES;
     constexpr int CPW_A = BM / 8 / NWAVES;                 // chunks i < CPW_A hold A rows
+    // Scale staging in LDS after the tile stages (and the L2-touch scratch): per stage BM
+    // activation scales ordered [wave row][lane row][sub-tile row], then 64 weight-scale slots.
+    constexpr int SC_BASE = 2 * STAGE + (STAGES > 2 ? 256 * NWAVES : 0);
+    constexpr int SC_STAGE = (BM + 64) * 4;
+    static_assert(BM % 64 == 0 && BM / 64 <= NWAVES, "one activation-scale DMA per wave");
 
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
+    const int frow = lane & 15;     // fragment row within a 16-row sub-tile
+    const int fgrp = lane >> 4;     // 32-byte K group (fp8) / 16-byte K chunk (int8)
 
     const int64_t M = p.M, N = p.N, K = p.K, KB = K / 128;
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -95,6 +102,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(static_cast<const uint8_t*>(p.a) + m0 * K, (uint32_t)(rows_a * K));
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(static_cast<const uint8_t*>(p.w) + n0 * K, (uint32_t)(rows_w * K));
 
+    // Scale buffers. Activation-scale DMA slot s = wave*64 + lane holds token row
+    // r(s) = wm*TM + sm*16 + frow for s = wm*TM + frow*SM + sm, so each lane later reads its
+    // SM scales as one contiguous LDS vector. Rows past M and blocks past N read as zero.
+    const int64_t ssm = p.sa_stride_m, ssk = p.sa_stride_k;
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
+        p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + (KB - 1) * ssk + 1) * 4));
+    uint32_t sa_dma_voff;
+    {
+        const int sl = wave * 64 + lane;
+        const int swm = sl / TM, rem = sl % TM;
+        const int r = swm * TM + (rem % SM) * 16 + rem / SM;
+        sa_dma_voff = (uint32_t)(r * ssm * 4);
+    }
+    const int64_t nb0 = n0 / 128, nbs = (rows_w + 127) / 128;
+    const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.sw + nb0 * KB, (uint32_t)(nbs * KB * 4));
+    const uint32_t sw_dma_voff = (uint32_t)(lane * KB * 4);
+    const uint32_t sa_lds = (uint32_t)((wm * TM + frow * SM) * 4);
+    const uint32_t sw_lds = (uint32_t)(BM * 4 + ((wn * TN) / 128) * 4);
+
     // Load chunk i of this wave covers region rows 8*(wave + NWAVES*i) .. +7; lane l writes
     // LDS slot (l & 7) of row +(l >> 3), which holds global chunk (l & 7) ^ swz(row). As
     // NWAVES is even, swz(row) = (l >> 3) ^ (wave & 1) for every i, so one per-lane byte
@@ -103,6 +129,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
                                          (((lane & 7) ^ (lane >> 3) ^ (wave & 1)) << 4));
     auto issue_stage = [&](int64_t kb, int stage) {
         const uint32_t skb = (uint32_t)(kb * 128);
+        // scales of block kb: waves 0 .. BM/64-1 fetch 64 activation scales each, wave 0 also
+        // the weight scales of the tile's 128-row blocks
+        const uint32_t sc = (uint32_t)(SC_BASE + stage * SC_STAGE);
+        if (wave < BM / 64)
+            dma4(rsa, lds, sc + wave * 256, sa_dma_voff, (uint32_t)(kb * ssk * 4));
+        if (wave == 0) dma4(rsw, lds, sc + BM * 4, sw_dma_voff, (uint32_t)(kb * 4));
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const uint32_t lds_off = (uint32_t)((wave + NWAVES * i) * 1024 + stage * STAGE);
@@ -133,16 +165,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
         }
     };
 
-    // Activation scales through a buffer: lane part (its token row) + uniform part.
-    const int frow = lane & 15;
-    const int fgrp = lane >> 4;
-    const int64_t ssm = p.sa_stride_m, ssk = p.sa_stride_k;
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
-        p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + (KB - 1) * ssk + 1) * 4));
-    const uint32_t sa_voff = (uint32_t)((wm * TM + frow) * ssm * 4);
-    const int64_t nb = (n0 + wn * TN < N ? n0 + wn * TN : N - 1) / 128;
-    const float* sw_row = p.sw + nb * KB;                      // uniform: scalar loads
-
     v4f acc[SM][SN];
 #pragma unroll
     for (int sm = 0; sm < SM; ++sm)
@@ -154,16 +176,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     const int fsw = swz(frow);
     const uint32_t a_row = (uint32_t)((wm * TM + frow) * 128);
     const uint32_t w_row = (uint32_t)((BM + wn * TN + frow) * 128);
-
-    // Scales of the next K block are loaded one iteration ahead, before that block's
-    // global->LDS loads, so waiting for them never waits for the tile prefetch.
-    float sa_next[SM], sw_next = 0.f;
-    auto load_scales = [&](int64_t kb) {
-        sw_next = sw_row[kb];
-#pragma unroll
-        for (int sm = 0; sm < SM; ++sm)
-            sa_next[sm] = buf_f32(rsa, sa_voff, (uint32_t)((kb * ssk + sm * 16 * ssm) * 4));
-    };
 
     auto lds16 = [&](uint32_t off) { return *reinterpret_cast<const v4i*>(lds + off); };
 
@@ -255,12 +267,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
 
     auto kblock = [&](int64_t kb, int stage) {
         float c[SM];
+        {
+            const uint32_t sc = (uint32_t)(SC_BASE + stage * SC_STAGE);
+            const float swv = *reinterpret_cast<const float*>(lds + sc + sw_lds);
+            if constexpr (SM == 4) {
+                const v4f sa4 = *reinterpret_cast<const v4f*>(lds + sc + sa_lds);
+                c[0] = sa4.x * swv; c[1] = sa4.y * swv; c[2] = sa4.z * swv; c[3] = sa4.w * swv;
+            } else {
 #pragma unroll
-        for (int sm = 0; sm < SM; ++sm) c[sm] = sa_next[sm] * sw_next;
-        if (kb + 1 < kb_end) {
-            load_scales(kb + 1);
-            issue_stage(kb + 1, stage ^ 1);
+                for (int sm = 0; sm < SM; ++sm)
+                    c[sm] = *reinterpret_cast<const float*>(lds + sc + sa_lds + sm * 4) * swv;
+            }
         }
+        if (kb + 1 < kb_end) issue_stage(kb + 1, stage ^ 1);
         if constexpr (STAGES == 3) {
             // near the end this re-touches the last block (harmless, keeps the loop uniform)
             __builtin_amdgcn_sched_barrier(0);
@@ -275,7 +294,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     };
 
     if (kb_begin < kb_end) {
-        load_scales(kb_begin);
         issue_stage(kb_begin, 0);
         if constexpr (STAGES == 3) prefetch_l2(kb_begin + 1 < kb_end ? kb_begin + 1 : kb_begin);
         wait_vmem_all();
@@ -302,7 +320,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
 template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
 hipError_t launch_std(const GemmArgs& a, hipStream_t stream) {
     constexpr int STAGE = (BM + BN) * 128;
-    constexpr int LDS_BYTES = 2 * STAGE + (STAGES > 2 ? 256 * WM * WN : 0);
+    constexpr int LDS_BYTES = 2 * STAGE + (STAGES > 2 ? 256 * WM * WN : 0) + 2 * (BM + 64) * 4;
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     dim3 grid((unsigned)tiles, 1, (unsigned)a.split);
     static bool attr_set = false;   // one-time opt-in to more than 64 KB of LDS

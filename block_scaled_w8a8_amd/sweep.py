@@ -41,7 +41,7 @@ def log(*a):
 class Problem:
     """Device buffers for one (N, K) and the largest M, with rotation copies."""
 
-    def __init__(self, N, K, m_max, qname, rotate=None):
+    def __init__(self, N, K, m_max, qname, rotate=None, layout="col"):
         import torch
 
         from . import bfq, synth
@@ -51,7 +51,8 @@ class Problem:
         x = synth.activations(m_max, K, seed=0).to(dev)
         w = synth.weights(N, K, seed=0).to(dev)
         qw, sw = bfq.quant_weight_blocks(w, q_dtype=self.qd)
-        qa, sa = bfq.quant_tokens(x, q_dtype=self.qd)
+        self.layout = bfq.BFQ_SCALES_COL_MAJOR if layout == "col" else bfq.BFQ_SCALES_ROW_MAJOR
+        qa, sa = bfq.quant_tokens(x, q_dtype=self.qd, layout=self.layout)
         del w, x
         foot = N * K + m_max * K
         if rotate is None:
@@ -78,7 +79,9 @@ class Problem:
         need = bfq.bfq_gemm_workspace_bytes(M, self.N, self.K, tile)
         ws = self.workspace(need) if need else None
         out = self.out32 if out32 else self.out
-        return bfq.bfq_block_gemm(qa[:M], sa[:M], qw, sw, out[:M], tile=tile, workspace=ws,
+        sa_m = sa if self.layout == bfq.BFQ_SCALES_COL_MAJOR else sa[:M]
+        return bfq.bfq_block_gemm(qa[:M], sa_m, qw, sw, out[:M], a_layout=self.layout,
+                                  a_scale_ld=sa.stride(0), tile=tile, workspace=ws,
                                   workspace_bytes=need)
 
     def time_us(self, M, tile, warmup=3, iters=20, reps=3):
@@ -234,7 +237,7 @@ def cmd_run(args):
     import torch
 
     from . import bfq
-    prob = Problem(args.N, args.K, args.M, args.dtype, rotate=args.rotate)
+    prob = Problem(args.N, args.K, args.M, args.dtype, rotate=args.rotate, layout=args.layout)
     if args.tile:
         tile = bfq.bfq_tile.from_dict(json.loads(args.tile))
     else:
@@ -280,6 +283,7 @@ def main():
     r.add_argument("--tile")
     r.add_argument("--iters", type=int, default=50)
     r.add_argument("--rotate", type=int, default=None)
+    r.add_argument("--layout", default="col", choices=["row", "col"], help="activation scales")
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=1 << 30)
     c.add_argument("--iters", type=int, default=3)
