@@ -81,6 +81,7 @@ def run_gpu(args, wl):
     dev = torch.device("cuda:0")
     qd = bfq.BFQ_E4M3FN if wl["qtype"] == "fp8" else bfq.BFQ_INT8
     m_max = max(wl["M"])
+    col = args.scale_layout == "col"
     shapes = []
     host = {}
     for (N, K) in wl["shapes"]:
@@ -96,7 +97,8 @@ def run_gpu(args, wl):
         xd = x.to(dev)
         qa = torch.empty((m_max, K), dtype=torch.uint8 if qd == bfq.BFQ_E4M3FN else torch.int8,
                          device=dev)
-        sa = torch.empty((m_max, K // 128), dtype=torch.float32, device=dev)
+        sa = torch.empty((K // 128, m_max) if col else (m_max, K // 128), dtype=torch.float32,
+                         device=dev)
         out = torch.empty((m_max, N), dtype=torch.bfloat16, device=dev)
         plans = []
         for M in wl["M"]:
@@ -121,12 +123,14 @@ def run_gpu(args, wl):
                 if events is not None:
                     e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
                     e0.record()
-                bfq.bfq_quant_tokens(sh["xd"][:M], sh["qa"][:M], sh["sa"][:M],
-                                     scale_ld=K // 128)
+                lay = bfq.BFQ_SCALES_COL_MAJOR if col else bfq.BFQ_SCALES_ROW_MAJOR
+                sa_m = sh["sa"] if col else sh["sa"][:M]
+                bfq.bfq_quant_tokens(sh["xd"][:M], sh["qa"][:M], sa_m, layout=lay,
+                                     scale_ld=sh["sa"].stride(0))
                 if events is not None:
                     e1.record()
-                bfq.bfq_block_gemm(sh["qa"][:M], sh["sa"][:M], qw, sw, sh["out"][:M],
-                                   a_scale_ld=K // 128, tile=tile, workspace=sh["ws"],
+                bfq.bfq_block_gemm(sh["qa"][:M], sa_m, qw, sw, sh["out"][:M], a_layout=lay,
+                                   a_scale_ld=sh["sa"].stride(0), tile=tile, workspace=sh["ws"],
                                    workspace_bytes=sh["ws_max"])
                 if events is not None:
                     e2.record()
@@ -305,6 +309,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--scale-layout", default="col", choices=["row", "col"],
+                    help="activation-scale layout written by the quantizer and read by the GEMM")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -331,7 +337,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl["desc"], "shapes_NK": wl["shapes"], "M": wl["M"],
                    "block_shape": [128, 128], "out_dtype": "bf16",
-                   "weight_copies_rotated": args.rotate},
+                   "weight_copies_rotated": args.rotate,
+                   "activation_scale_layout": args.scale_layout + "_major"},
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "per_m": res["rows"],

@@ -242,6 +242,14 @@ def cmd_run(args):
         tile = bfq.bfq_tile.from_dict(json.loads(args.tile))
     else:
         _, tile = bfq.bfq_select_tile(args.M, args.N, args.K, prob.qd, bfq.BFQ_BF16)
+    if args.eager:
+        # plain launches, no graph: for counter collection, which wants one dispatch per call
+        for i in range(args.eager):
+            prob.launch(args.M, tile, i)
+        torch.cuda.synchronize()
+        print(json.dumps({"M": args.M, "N": args.N, "K": args.K, "tile": tile.as_dict(),
+                          "eager_launches": args.eager}), flush=True)
+        return
     us = prob.time_us(args.M, tile, warmup=3, iters=args.iters, reps=1)
     from . import perf
     s = us * 1e-6
@@ -283,6 +291,7 @@ def main():
     r.add_argument("--tile")
     r.add_argument("--iters", type=int, default=50)
     r.add_argument("--rotate", type=int, default=None)
+    r.add_argument("--eager", type=int, default=0, help="launch this many times without timing")
     r.add_argument("--layout", default="col", choices=["row", "col"], help="activation scales")
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=1 << 30)
