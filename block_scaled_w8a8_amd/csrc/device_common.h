@@ -84,8 +84,9 @@ __device__ __forceinline__ v4i mfma_i8_16x16x64(const v4i& a, const v4i& b, cons
 }
 
 // ---------------------------------------------------------------- buffer access ----
-// Raw buffer resource over [base, base + bytes): loads past `bytes` return zero, which the
-// GEMM kernels use for rows beyond M or N. bytes < 2^32.
+// Raw buffer resource over [base, base + bytes): loads whose offset (per-lane voffset plus
+// scalar soffset; on gfx950 both count) reaches `bytes` return zero, which the GEMM kernels
+// use for rows beyond M or N. bytes < 2^32.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                              0x00020000);
@@ -110,6 +111,11 @@ __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// 16 bytes per lane from a buffer into registers (zero past the resource's end).
+__device__ __forceinline__ v4i buf_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // ---------------------------------------------------------------- LDS DMA ----
 // 16 bytes per lane from global memory straight into LDS: the wave writes 1 KB at
 // lds_base + lane * 16 (lds_base must be wave-uniform).
@@ -126,6 +132,63 @@ template <int N> __device__ __forceinline__ void wait_vmem_keep_n() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 #define wait_vmem_keep(N) wait_vmem_keep_n<(N)>()
+
+// Workgroup barrier without the memory fence of __syncthreads (whose release semantics
+// drain every outstanding global load). For LDS written by DMA the caller first waits for
+// its own DMAs with an explicit vmcnt; LDS is coherent within the workgroup, so the barrier
+// alone publishes the data. The memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// 8-byte LDS read, complete when it returns. Written as inline asm because for a plain load
+// the compiler, unable to tell which LDS bytes an in-flight LDS DMA writes, waits for every
+// outstanding vector-memory operation first. The caller guarantees (by its own vmcnt wait and
+// barrier) that the bytes read are not being written.
+__device__ __forceinline__ float2 lds_read_f32x2(const uint8_t* lds_base, uint32_t off) {
+    const uint32_t addr = (uint32_t)(uintptr_t)(
+        (__attribute__((address_space(3))) const uint8_t*)(lds_base + off));
+    uint64_t v;
+    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return __builtin_bit_cast(float2, v);
+}
+
+// 16-byte form of lds_read_f32x2.
+__device__ __forceinline__ v4f lds_read_f32x4(const uint8_t* lds_base, uint32_t off) {
+    const uint32_t addr = (uint32_t)(uintptr_t)(
+        (__attribute__((address_space(3))) const uint8_t*)(lds_base + off));
+    v4f v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+// ---------------------------------------------------------------- tile order, LDS swizzle ----
+// Tile id -> (pid_m, pid_n). raster 0: workgroup ids are dealt round-robin to the 8 XCDs, so
+// ids are first remapped to give each XCD a contiguous range of tiles; raster 1: no remap.
+// Then the grouped order: GROUP_M tile rows at a time, column by column within the group.
+__device__ __forceinline__ void tile_coords(int64_t bid, int64_t tiles_m, int64_t tiles_n,
+                                            int group_m, int raster, int64_t& pid_m,
+                                            int64_t& pid_n) {
+    const int64_t T = tiles_m * tiles_n;
+    int64_t j = bid;
+    if (raster == 0) {
+        const int64_t xcd = bid & 7, local = bid >> 3;
+        const int64_t base = T >> 3, rem = T & 7;
+        j = xcd * base + (xcd < rem ? xcd : rem) + local;
+    }
+    const int64_t per_group = (int64_t)group_m * tiles_n;
+    const int64_t gid = j / per_group;
+    const int64_t first_m = gid * group_m;
+    const int64_t gsize = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int64_t in_group = j - gid * per_group;
+    pid_m = first_m + in_group % gsize;
+    pid_n = in_group / gsize;
+}
+
+// LDS slot of 16-byte chunk c in region row r: c ^ swz(r). Fragment reads touch 16
+// consecutive rows (a multiple of 16 apart) at one chunk index; with this swizzle those 16
+// reads hit 16 distinct (row parity, slot) pairs, i.e. distinct banks whether the LDS serves
+// 8 lanes x 16 B or 16 lanes x 16 B per cycle. It depends only on r & 15.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // ---------------------------------------------------------------- output store ----
 // Store four consecutive output values of one row.

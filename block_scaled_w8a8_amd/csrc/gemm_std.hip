@@ -29,34 +29,6 @@
 
 namespace bfq {
 
-// Tile id -> (pid_m, pid_n). raster 0: workgroup ids are dealt round-robin to the 8 XCDs, so
-// ids are first remapped to give each XCD a contiguous range of tiles; raster 1: no remap.
-// Then the grouped order: GROUP_M tile rows at a time, column by column within the group.
-__device__ __forceinline__ void tile_coords(int64_t bid, int64_t tiles_m, int64_t tiles_n,
-                                            int group_m, int raster, int64_t& pid_m,
-                                            int64_t& pid_n) {
-    const int64_t T = tiles_m * tiles_n;
-    int64_t j = bid;
-    if (raster == 0) {
-        const int64_t xcd = bid & 7, local = bid >> 3;
-        const int64_t base = T >> 3, rem = T & 7;
-        j = xcd * base + (xcd < rem ? xcd : rem) + local;
-    }
-    const int64_t per_group = (int64_t)group_m * tiles_n;
-    const int64_t gid = j / per_group;
-    const int64_t first_m = gid * group_m;
-    const int64_t gsize = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
-    const int64_t in_group = j - gid * per_group;
-    pid_m = first_m + in_group % gsize;
-    pid_n = in_group / gsize;
-}
-
-// LDS slot of 16-byte chunk c in region row r: c ^ swz(r). Fragment reads touch 16
-// consecutive rows (a multiple of 16 apart) at one chunk index; with this swizzle those 16
-// reads hit 16 distinct (row parity, slot) pairs, i.e. distinct banks whether the LDS serves
-// 8 lanes x 16 B or 16 lanes x 16 B per cycle. It depends only on r & 15.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
 template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     constexpr int NWAVES = WM * WN;
