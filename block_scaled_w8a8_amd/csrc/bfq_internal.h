@@ -48,7 +48,6 @@ struct KernelEntry {
 // Registries filled by the kernel translation units.
 const KernelEntry* std_kernels(int* count);
 const KernelEntry* swapab_kernels(int* count);
-const KernelEntry* ring_kernels(int* count);
 
 // Deterministic split-K reduction: out[m][n] = sum_{s=0..split-1} partials[s][m][n], in
 // ascending s, converted once to the output dtype.

@@ -111,11 +111,6 @@ __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
-// 16 bytes per lane from a buffer into registers (zero past the resource's end).
-__device__ __forceinline__ v4i buf_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
 // ---------------------------------------------------------------- LDS DMA ----
 // 16 bytes per lane from global memory straight into LDS: the wave writes 1 KB at
 // lds_base + lane * 16 (lds_base must be wave-uniform).
@@ -132,34 +127,6 @@ template <int N> __device__ __forceinline__ void wait_vmem_keep_n() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 #define wait_vmem_keep(N) wait_vmem_keep_n<(N)>()
-
-// Workgroup barrier without the memory fence of __syncthreads (whose release semantics
-// drain every outstanding global load). For LDS written by DMA the caller first waits for
-// its own DMAs with an explicit vmcnt; LDS is coherent within the workgroup, so the barrier
-// alone publishes the data. The memory clobber keeps the compiler from moving LDS accesses
-// across it.
-__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
-
-// 8-byte LDS read, complete when it returns. Written as inline asm because for a plain load
-// the compiler, unable to tell which LDS bytes an in-flight LDS DMA writes, waits for every
-// outstanding vector-memory operation first. The caller guarantees (by its own vmcnt wait and
-// barrier) that the bytes read are not being written.
-__device__ __forceinline__ float2 lds_read_f32x2(const uint8_t* lds_base, uint32_t off) {
-    const uint32_t addr = (uint32_t)(uintptr_t)(
-        (__attribute__((address_space(3))) const uint8_t*)(lds_base + off));
-    uint64_t v;
-    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
-    return __builtin_bit_cast(float2, v);
-}
-
-// 16-byte form of lds_read_f32x2.
-__device__ __forceinline__ v4f lds_read_f32x4(const uint8_t* lds_base, uint32_t off) {
-    const uint32_t addr = (uint32_t)(uintptr_t)(
-        (__attribute__((address_space(3))) const uint8_t*)(lds_base + off));
-    v4f v;
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
-    return v;
-}
 
 // ---------------------------------------------------------------- tile order, LDS swizzle ----
 // Tile id -> (pid_m, pid_n). raster 0: workgroup ids are dealt round-robin to the 8 XCDs, so

@@ -19,8 +19,8 @@ import hashlib
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("csrc/gemm_std.hip", "csrc/gemm_swapab.hip", "csrc/gemm_ring.hip",
-                  "csrc/quant.hip", "csrc/device_common.h")
+KERNEL_SOURCES = ("csrc/gemm_std.hip", "csrc/gemm_swapab.hip", "csrc/quant.hip",
+                  "csrc/device_common.h")
 
 
 def source_hash() -> str:

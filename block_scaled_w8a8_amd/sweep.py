@@ -123,7 +123,7 @@ def candidates(qd, M, N, K):
         t = bfq.bfq_get_tile_candidate(i, qd)
         if t.variant == 1 and M > 4 * t.bm:
             continue
-        if t.variant in (0, 2) and M <= 16 and t.bm > 64:
+        if t.variant == 0 and M <= 16 and t.bm > 64:
             continue
         if t.variant == 1:
             ctas = -(-N // t.bn) * -(-M // t.bm)

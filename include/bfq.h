@@ -72,16 +72,12 @@ typedef enum {
  *   variant 1 "swap_ab": the weight rows stream straight from HBM into the wide MFMA
  *             operand and the bm tokens ride in the narrow one; the output tile is formed
  *             transposed and stored back row-major ([HELION] kernel section).
- *   variant 2 "ring": bm = 32 * waves_m tokens x bn weight rows per workgroup; the weight
- *             tiles stream through a 4-slot LDS ring and each wave loads its 32 tokens straight
- *             into registers, so loads are issued two to three K blocks ahead of use.
  *   split_k  : K blocks split into split_k contiguous chunks (>= 1), fp32 partials reduced
  *             in a fixed order ([HELION] kernel section).
- *   stages   : LDS stages (variant 0), weight prefetch depth in K blocks (variant 1), LDS
- *             ring slots (variant 2, always 4).
- *   sched    : variants 0 and 2 instruction schedule: 0 = each sub-tile's scale FMAs right
- *             after its MFMAs, 1 = software-pipelined (FMAs one sub-tile behind the MFMAs).
- *   group_m, raster: variants 0 and 2 tile order (launch arguments, any group_m >= 1): raster 0
+ *   stages   : LDS stages (variant 0) or weight prefetch depth in K blocks (variant 1).
+ *   sched    : variant 0 instruction schedule: 0 = each sub-tile's scale FMAs right after its
+ *             MFMAs, 1 = software-pipelined (FMAs one sub-tile behind the MFMAs).
+ *   group_m, raster: variant 0 tile order (launch arguments, any group_m >= 1): raster 0
  *             gives each of the 8 XCDs a contiguous range of tiles, raster 1 does not.
  *   bk is always 128 (one scale block per K step). */
 typedef struct {

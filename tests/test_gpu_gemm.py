@@ -91,37 +91,6 @@ def test_every_candidate_and_split_parity(bfq, orc, qname):
 
 
 @pytest.mark.parametrize("qname", ["fp8", "int8"])
-def test_ring_kernel_k_tails(bfq, orc, qname):
-    """The ring kernel (variant 2) issues token fragments two K blocks ahead and weight tiles
-    three ahead, clamping past the end of its K range: K = 7 blocks with split_k 1, 2, 5, 7
-    gives per-workgroup block counts 7, 3..4, 1..2 and 1, covering the prologue alone, the
-    unrolled loop and both tail lengths; M and N ragged against the 256-row tiles; both
-    activation-scale layouts."""
-    from oracle import metrics
-    qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
-    qt = orc.FP8 if qname == "fp8" else orc.INT8
-    M, N, K = 300, 640, 896
-    host = _case(orc, M, N, K, 23, qt)
-    ref32, _ = orc.block_gemm(*host, qtype=qt)
-    qa, sa, qw, sw = _to_dev(*host)
-    sa_col = sa.t().contiguous()
-    rings = [t for t in _candidates(bfq, qd) if t.variant == 2]
-    assert rings, "no ring kernel compiled for " + qname
-    for t in rings:
-        for s in (1, 2, 5, 7):
-            for col in (False, True):
-                tile = _with_split(t, s)
-                what = (qname, tile.as_dict(), "col" if col else "row")
-                print("ring", what, flush=True)
-                if col:
-                    o = _run(bfq, (qa, sa, qw, sw), torch.float32, tile=tile,
-                             a_layout=bfq.BFQ_SCALES_COL_MAJOR, sa_override=sa_col)
-                else:
-                    o = _run(bfq, (qa, sa, qw, sw), torch.float32, tile=tile)
-                _check_fp32(metrics, o.cpu().numpy(), ref32, what)
-
-
-@pytest.mark.parametrize("qname", ["fp8", "int8"])
 def test_exact_integer_case_every_candidate(bfq, orc, qname):
     """P6 on the device: integer-valued codes with |v| <= 8 and power-of-two scales make
     every partial exact, so the fp32 output must equal the integer matmul bit for bit for
