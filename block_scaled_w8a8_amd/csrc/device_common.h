@@ -16,6 +16,7 @@ namespace bfq {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr float kFp8Max = 448.0f;    // largest finite e4m3fn value
@@ -76,6 +77,13 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
     v4f z = {0.f, 0.f, 0.f, 0.f};
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+// D(32x32, fp32) = A(32x64 e4m3) * B(64x32 e4m3) + C. Lane l supplies row (l % 32) of A and
+// column (l % 32) of B, 32 bytes of the 64-long K slice each (same placement for both).
+// Output: lane l holds D[8*j + 4*(l/32) + i][l % 32] in element 4*j + i (i, j = 0..3).
+__device__ __forceinline__ v16f mfma_fp8_32x32x64(const v8i& a, const v8i& b, const v16f& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // int8: D(16x16, int32) += A(16x64) * B(64x16); 16 bytes of K per lane.

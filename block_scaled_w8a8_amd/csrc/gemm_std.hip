@@ -16,6 +16,9 @@
 //  * MFMA v_mfma_f32_16x16x128_f8f6f4 (e4m3) or v_mfma_i32_16x16x64_i8 (int8): one fp8
 //    MFMA covers one whole 128-wide K block for a 16x16 sub-tile, so its result is the
 //    block partial P and the scale step is acc = fma(P, sa[m,kb]*sw[nb,kb], acc).
+//    sched 2 instead uses 32x32 sub-tiles: two v_mfma_f32_32x32x64_f8f6f4 per K block
+//    (each weight fragment feeds twice the MFMA work per LDS read; a lane owns one token and
+//    four groups of four output columns).
 //  * The weight fragment sits in the MFMA's first operand and the token fragment in the
 //    second, so each lane ends up owning one token row and four consecutive output columns:
 //    one scale product per lane and sub-tile row, and 8-byte (bf16) row-contiguous stores.
@@ -24,6 +27,8 @@
 //  * Workgroup ids are remapped so that each XCD (ids i, i+8, i+16, ...) owns a contiguous
 //    range of tiles, ordered in groups of group_m tile rows, keeping shared A/W panels in
 //    that XCD's L2.
+#include <type_traits>
+
 #include "bfq_internal.h"
 #include "device_common.h"
 
@@ -33,7 +38,12 @@ template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     constexpr int NWAVES = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;      // wave tile (tokens x weight rows)
-    constexpr int SM = TM / 16, SN = TN / 16;      // 16x16 sub-tiles per wave
+    // sched 2: 32x32x64 MFMAs (two per K block and sub-tile), else 16x16 MFMAs
+    constexpr int MF = SCHED == 2 ? 32 : 16;       // sub-tile edge
+    constexpr int SM = TM / MF, SN = TN / MF;      // MF x MF sub-tiles per wave
+    static_assert(SCHED != 2 || (QT == Q_FP8 && TM % 32 == 0 && TN % 32 == 0),
+                  "the 32x32 schedule is fp8 only and needs 32-multiple wave tiles");
+    using AccT = typename std::conditional<MF == 32, v16f, v4f>::type;
     constexpr int STAGE = (BM + BN) * 128;         // bytes per LDS stage
     constexpr int CHUNKS = (BM + BN) / 8;          // 1 KB load chunks per stage
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
@@ -55,8 +65,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
-    const int frow = lane & 15;     // fragment row within a 16-row sub-tile
-    const int fgrp = lane >> 4;     // 32-byte K group (fp8) / 16-byte K chunk (int8)
+    const int frow = lane & (MF - 1);   // fragment row within a sub-tile
+    const int fgrp = lane >> 4;         // 16x16: 32-byte K group (fp8) / 16-byte K chunk (int8)
+    const int khalf = lane >> 5;        // 32x32: 32-byte K group within a 64-wide K half
 
     const int64_t M = p.M, N = p.N, K = p.K, KB = K / 128;
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -75,7 +86,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(static_cast<const uint8_t*>(p.w) + n0 * K, (uint32_t)(rows_w * K));
 
     // Scale buffers. Activation-scale DMA slot s = wave*64 + lane holds token row
-    // r(s) = wm*TM + sm*16 + frow for s = wm*TM + frow*SM + sm, so each lane later reads its
+    // r(s) = wm*TM + sm*MF + frow for s = wm*TM + frow*SM + sm, so each lane later reads its
     // SM scales as one contiguous LDS vector. Rows past M and blocks past N read as zero.
     const int64_t ssm = p.sa_stride_m, ssk = p.sa_stride_k;
     const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
@@ -84,7 +95,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     {
         const int sl = wave * 64 + lane;
         const int swm = sl / TM, rem = sl % TM;
-        const int r = swm * TM + (rem % SM) * 16 + rem / SM;
+        const int r = swm * TM + (rem % SM) * MF + rem / SM;
         sa_dma_voff = (uint32_t)(r * ssm * 4);
     }
     const int64_t nb0 = n0 / 128, nbs = (rows_w + 127) / 128;
@@ -137,14 +148,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
         }
     };
 
-    v4f acc[SM][SN];
+    AccT acc[SM][SN];
 #pragma unroll
     for (int sm = 0; sm < SM; ++sm)
 #pragma unroll
-        for (int sn = 0; sn < SN; ++sn) acc[sm][sn] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int sn = 0; sn < SN; ++sn) acc[sm][sn] = AccT{};
 
     // Per-lane LDS byte offsets of the fragment rows (sub-tile 0), chunk slots resolved.
-    // A sub-tile row sm adds sm*2048, a W sub-tile sn adds sn*2048 (swz depends on r & 15).
+    // A sub-tile row sm adds sm*MF*128, a W sub-tile sn adds sn*MF*128 (swz depends on r & 15).
     const int fsw = swz(frow);
     const uint32_t a_row = (uint32_t)((wm * TM + frow) * 128);
     const uint32_t w_row = (uint32_t)((BM + wn * TN + frow) * 128);
@@ -153,7 +164,66 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
 
     // One K block on LDS stage `stage`: fragments from LDS, MFMA, scale fusion.
     auto compute = [&](uint32_t sbase, const float (&c)[SM]) {
-        if constexpr (QT == Q_FP8) {
+        if constexpr (MF == 32) {
+            // Lane l covers row l % 32 of each 32-row sub-tile and, in K half h, the 16-byte
+            // chunks 4h + 2*(l/32) and 4h + 2*(l/32) + 1. Each W fragment feeds SM pairs of
+            // MFMAs (64 K each) whose sum is the block partial of a 32x32 sub-tile.
+            uint32_t slo[2], shi[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                slo[h] = (uint32_t)(((4 * h + 2 * khalf) ^ fsw) << 4);
+                shi[h] = (uint32_t)(((4 * h + 2 * khalf + 1) ^ fsw) << 4);
+            }
+            const uint32_t abase = sbase + a_row, wbase = sbase + w_row;
+            auto frag = [&](uint32_t base, int h) {
+                const v4i lo = lds16(base + slo[h]);
+                const v4i hi = lds16(base + shi[h]);
+                return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            };
+            v8i af[SM][2];
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm) {
+                af[sm][0] = frag(abase + sm * 4096, 0);
+                af[sm][1] = frag(abase + sm * 4096, 1);
+            }
+            // Pairs p = sn*SM + sm in order. Software-pipelined: pair p's two MFMAs go out,
+            // then (on a new W sub-tile) the next W fragment's reads, then the 16 scale FMAs
+            // of pair p-1, whose product has finished while p's MFMAs were issued. Two
+            // product buffers and two W fragments alternate; group barriers pin the order.
+            constexpr int P = SM * SN;
+            v8i wf[2][2];
+            wf[0][0] = frag(wbase, 0);
+            wf[0][1] = frag(wbase, 1);
+            v16f qb[2];
+            auto scale_fma = [&](int pp) {
+                v16f& a = acc[pp % SM][pp / SM];
+                const v16f& q = qb[pp & 1];
+                const float cc = c[pp % SM];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) a[e] = __builtin_fmaf(q[e], cc, a[e]);
+            };
+#pragma unroll
+            for (int pp = 0; pp < P; ++pp) {
+                const int sn = pp / SM, sm = pp % SM;
+                const v8i(&w)[2] = wf[sn & 1];
+                qb[pp & 1] = mfma_fp8_32x32x64(w[0], af[sm][0], v16f{});
+                qb[pp & 1] = mfma_fp8_32x32x64(w[1], af[sm][1], qb[pp & 1]);
+                if (sm == 0 && sn + 1 < SN) {
+                    wf[(sn + 1) & 1][0] = frag(wbase + (sn + 1) * 4096, 0);
+                    wf[(sn + 1) & 1][1] = frag(wbase + (sn + 1) * 4096, 1);
+                }
+                if (pp > 0) scale_fma(pp - 1);
+            }
+            scale_fma(P - 1);
+#pragma unroll
+            for (int pp = 0; pp < P; ++pp) {
+                const int sn = pp / SM, sm = pp % SM;
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                       // MFMA
+                if (sm == 0 && sn + 1 < SN) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+                if (pp > 0) __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);          // VALU
+            }
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        } else if constexpr (QT == Q_FP8) {
             const uint32_t s0 = (uint32_t)(((2 * fgrp) ^ fsw) << 4);
             const uint32_t s1 = (uint32_t)(((2 * fgrp + 1) ^ fsw) << 4);
             const uint32_t abase = sbase + a_row, wbase = sbase + w_row;
@@ -274,17 +344,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
         wait_vmem_all();      // no LDS DMA may still be in flight when the wave ends
     }
 
-    // Epilogue: lane owns token m and columns n..n+3 of each sub-tile.
+    // Epilogue: lane owns token m and, per sub-tile, columns n..n+3 (16x16) or the four
+    // column groups 8j + 4*(l/32) .. +3, j = 0..3 (32x32).
 #pragma unroll
     for (int sm = 0; sm < SM; ++sm) {
-        const int64_t m = m0 + wm * TM + sm * 16 + frow;
+        const int64_t m = m0 + wm * TM + sm * MF + frow;
         if (m >= M) continue;
 #pragma unroll
         for (int sn = 0; sn < SN; ++sn) {
-            const int64_t n = n0 + wn * TN + sn * 16 + 4 * fgrp;
-            if (n >= N) continue;
-            if (split == 1) store4<OT>(p.out, m * N + n, acc[sm][sn]);
-            else store4<O_FP32>(p.partials, ((int64_t)z * M + m) * N + n, acc[sm][sn]);
+            if constexpr (MF == 32) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t n = n0 + wn * TN + sn * 32 + 8 * j + 4 * khalf;
+                    if (n >= N) continue;
+                    const AccT& a = acc[sm][sn];
+                    const v4f v = {a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]};
+                    if (split == 1) store4<OT>(p.out, m * N + n, v);
+                    else store4<O_FP32>(p.partials, ((int64_t)z * M + m) * N + n, v);
+                }
+            } else {
+                const int64_t n = n0 + wn * TN + sn * 16 + 4 * fgrp;
+                if (n >= N) continue;
+                if (split == 1) store4<OT>(p.out, m * N + n, acc[sm][sn]);
+                else store4<O_FP32>(p.partials, ((int64_t)z * M + m) * N + n, acc[sm][sn]);
+            }
         }
     }
 }
@@ -321,6 +404,8 @@ static const KernelEntry kStdKernels[] = {
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8),
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8),
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 3, 1, Q_FP8),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 2, Q_FP8),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 2, Q_FP8),
     BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 0, Q_FP8),
     BFQ_STD_ALL_OUT(128, 256, 2, 2, 3, 1, Q_FP8),
     BFQ_STD_ALL_OUT(256, 128, 4, 1, 3, 1, Q_FP8),

@@ -76,7 +76,8 @@ typedef enum {
  *             in a fixed order ([HELION] kernel section).
  *   stages   : LDS stages (variant 0) or weight prefetch depth in K blocks (variant 1).
  *   sched    : variant 0 instruction schedule: 0 = each sub-tile's scale FMAs right after its
- *             MFMAs, 1 = software-pipelined (FMAs one sub-tile behind the MFMAs).
+ *             MFMAs, 1 = software-pipelined (FMAs one sub-tile behind the MFMAs), 2 = 32x32
+ *             sub-tiles (two 32x32x64 MFMAs per K block, FMAs one pair behind; fp8 only).
  *   group_m, raster: variant 0 tile order (launch arguments, any group_m >= 1): raster 0
  *             gives each of the 8 XCDs a contiguous range of tiles, raster 1 does not.
  *   bk is always 128 (one scale block per K step). */
