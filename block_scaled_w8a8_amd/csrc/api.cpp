@@ -111,14 +111,17 @@ bool same_shape(const bfq_tile& a, const bfq_tile& b) {
     if (a.variant != b.variant || a.bm != b.bm || a.bn != b.bn || a.waves_n != b.waves_n ||
         a.stages != b.stages)
         return false;
-    if (a.variant == 0) return a.waves_m == b.waves_m && a.sched == b.sched;
+    if (a.variant == 0 || a.variant == 2) return a.waves_m == b.waves_m && a.sched == b.sched;
     return true;
 }
 
 const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype) {
     if (t.bk != 0 && t.bk != 128) return nullptr;
     int n = 0;
-    const KernelEntry* list = t.variant == 0 ? std_kernels(&n) : t.variant == 1 ? swapab_kernels(&n) : nullptr;
+    const KernelEntry* list = t.variant == 0   ? std_kernels(&n)
+                              : t.variant == 1 ? swapab_kernels(&n)
+                              : t.variant == 2 ? streamk_kernels(&n)
+                                               : nullptr;
     for (int i = 0; list && i < n; ++i)
         if (list[i].qtype == qtype && list[i].otype == otype && same_shape(list[i].tile, t))
             return &list[i];
@@ -191,6 +194,10 @@ bfq_status select_tile(int64_t M, int64_t N, int64_t K, int qtype, bfq_tile* out
 bool block_shape_ok(const int32_t* bs) { return bs && bs[0] == 128 && bs[1] == 128; }
 
 size_t workspace_for(int64_t M, int64_t N, const bfq_tile& t) {
+    if (t.variant == 2) {
+        if (M == 0 || t.bm <= 0 || t.bn <= 0) return 0;
+        return streamk_workspace_bytes(t.bm, t.bn, streamk_grid());
+    }
     return t.split_k > 1 ? (size_t)t.split_k * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
@@ -340,13 +347,15 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     if (!ke) return fail(BFQ_ERR_TILE, "tile does not name a compiled kernel for this dtype pair");
     if (t.split_k < 1 || t.split_k > 256 || t.split_k > KB)
         return fail(BFQ_ERR_TILE, "split_k must be in [1, min(256, K/128)]");
-    if (t.variant == 0 && (t.group_m < 1 || t.raster < 0 || t.raster > 1))
+    if (t.variant == 2 && t.split_k != 1)
+        return fail(BFQ_ERR_TILE, "the stream-K schedule (variant 2) takes split_k = 1");
+    if (t.variant != 1 && (t.group_m < 1 || t.raster < 0 || t.raster > 1))
         return fail(BFQ_ERR_TILE, "group_m must be >= 1 and raster 0 or 1");
     const size_t need = workspace_for(M, N, t);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(BFQ_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
     // grid-size limits of the launchers
-    if (t.variant == 0) {
+    if (t.variant != 1) {
         int64_t tiles = ceil_div(M, t.bm) * ceil_div(N, t.bn);
         if (tiles > 0x7FFFFFFF) return fail(BFQ_ERR_SHAPE, "too many output tiles");
     } else if (ceil_div(M, t.bm) > 65535) {
@@ -369,6 +378,8 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     ga.split = t.split_k;
     ga.group_m = t.group_m;
     ga.raster = t.raster;
+    ga.dp_tiles = 0;
+    ga.sk_slots = nullptr;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = ke->launch(ga, s);
     if (e == hipSuccess && t.split_k > 1)
@@ -389,9 +400,9 @@ bfq_status bfq_load_tile_table(const char* json_path) {
 int32_t bfq_num_tile_candidates(bfq_dtype in_dtype) {
     if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8) return 0;
     const int q = qtype_of(in_dtype);
-    int ns[2] = {0, 0}, count = 0;
-    const KernelEntry* lists[2] = {std_kernels(&ns[0]), swapab_kernels(&ns[1])};
-    for (int l = 0; l < 2; ++l)
+    int ns[3] = {0, 0, 0}, count = 0;
+    const KernelEntry* lists[3] = {std_kernels(&ns[0]), swapab_kernels(&ns[1]), streamk_kernels(&ns[2])};
+    for (int l = 0; l < 3; ++l)
         for (int i = 0; i < ns[l]; ++i) count += (lists[l][i].qtype == q && lists[l][i].otype == O_BF16);
     return count;
 }
@@ -401,9 +412,9 @@ bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, int32_t index, bfq_tile* t
     if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8)
         return fail(BFQ_ERR_DTYPE, "in_dtype must be BFQ_E4M3FN or BFQ_INT8");
     const int q = qtype_of(in_dtype);
-    int ns[2] = {0, 0}, count = 0;
-    const KernelEntry* lists[2] = {std_kernels(&ns[0]), swapab_kernels(&ns[1])};
-    for (int l = 0; l < 2; ++l)
+    int ns[3] = {0, 0, 0}, count = 0;
+    const KernelEntry* lists[3] = {std_kernels(&ns[0]), swapab_kernels(&ns[1]), streamk_kernels(&ns[2])};
+    for (int l = 0; l < 3; ++l)
         for (int i = 0; i < ns[l]; ++i) {
             if (lists[l][i].qtype != q || lists[l][i].otype != O_BF16) continue;
             if (count == index) { *tile_out = lists[l][i].tile; return BFQ_OK; }

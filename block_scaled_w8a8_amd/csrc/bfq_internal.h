@@ -33,6 +33,9 @@ struct GemmArgs {
     int split;              // K-block chunks
     int group_m;            // tile rows per group of the grouped order (standard kernel)
     int raster;             // 0: XCD-contiguous tile ranges, 1: plain order (standard kernel)
+    // stream-K schedule (variant 2) only:
+    int64_t dp_tiles;       // tiles [0, dp_tiles) taken whole, in rounds of the grid size
+    float* sk_slots;        // [grid][2][BM*BN] fp32 partial tiles
 };
 
 typedef hipError_t (*GemmLaunchFn)(const GemmArgs& args, hipStream_t stream);
@@ -48,6 +51,14 @@ struct KernelEntry {
 // Registries filled by the kernel translation units.
 const KernelEntry* std_kernels(int* count);
 const KernelEntry* swapab_kernels(int* count);
+const KernelEntry* streamk_kernels(int* count);
+
+// Stream-K: workspace (two fp32 partial-tile slots per workgroup of a `grid`-workgroup grid),
+// the split of `tiles` into whole-tile rounds and the stream-K remainder, and the grid size
+// (the device's compute units).
+size_t streamk_workspace_bytes(int bm, int bn, int grid);
+int64_t streamk_dp_tiles(int64_t tiles, int grid);
+int streamk_grid();
 
 // Deterministic split-K reduction: out[m][n] = sum_{s=0..split-1} partials[s][m][n], in
 // ascending s, converted once to the output dtype.

@@ -119,6 +119,15 @@ __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// 16 bytes per lane between registers and a buffer (loads past the end return zero).
+__device__ __forceinline__ v4f buf_load_v4f(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_store_v4f(__amdgpu_buffer_rsrc_t r, v4f v, uint32_t voff,
+                                              uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, voff, soff, 0);
+}
+
 // ---------------------------------------------------------------- LDS DMA ----
 // 16 bytes per lane from global memory straight into LDS: the wave writes 1 KB at
 // lds_base + lane * 16 (lds_base must be wave-uniform).
@@ -135,6 +144,13 @@ template <int N> __device__ __forceinline__ void wait_vmem_keep_n() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 #define wait_vmem_keep(N) wait_vmem_keep_n<(N)>()
+
+// A workgroup-uniform 64-bit value, stated as such (kept in scalar registers).
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // ---------------------------------------------------------------- tile order, LDS swizzle ----
 // Tile id -> (pid_m, pid_n). raster 0: workgroup ids are dealt round-robin to the 8 XCDs, so

@@ -34,16 +34,37 @@
 
 namespace bfq {
 
-template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
-    constexpr int NWAVES = WM * WN;
-    constexpr int TM = BM / WM, TN = BN / WN;      // wave tile (tokens x weight rows)
+// Wave-tile geometry of one configuration.
+template <int BM, int BN, int WM, int WN, int SCHED>
+struct StdShape {
+    static constexpr int NWAVES = WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;   // wave tile (tokens x weight rows)
     // sched 2: 32x32x64 MFMAs (two per K block and sub-tile), else 16x16 MFMAs
-    constexpr int MF = SCHED == 2 ? 32 : 16;       // sub-tile edge
-    constexpr int SM = TM / MF, SN = TN / MF;      // MF x MF sub-tiles per wave
+    static constexpr int MF = SCHED == 2 ? 32 : 16;    // sub-tile edge
+    static constexpr int SM = TM / MF, SN = TN / MF;   // MF x MF sub-tiles per wave
+    using AccT = typename std::conditional<MF == 32, v16f, v4f>::type;
+    // LDS: two tile stages, the optional L2-touch scratch, two scale stages
+    static constexpr int STAGE = (BM + BN) * 128;
+    static constexpr int lds_bytes(int stages) {
+        return 2 * STAGE + (stages > 2 ? 256 * NWAVES : 0) + 2 * (BM + 64) * 4;
+    }
+};
+
+// K blocks [kb_begin, kb_end) of the output tile at (m0, n0) into acc (zeroed here). Every
+// wave of the workgroup calls it with the same arguments; it leaves no LDS DMA in flight and
+// ends on a barrier, so the next call may reuse the LDS at once.
+template <int BM, int BN, int WM, int WN, int QT, int SCHED, int STAGES>
+__device__ __forceinline__ void std_tile(
+    const GemmArgs& p, uint8_t* lds, int64_t m0, int64_t n0, int64_t kb_begin, int64_t kb_end,
+    typename StdShape<BM, BN, WM, WN, SCHED>::AccT (&acc)[StdShape<BM, BN, WM, WN, SCHED>::SM]
+                                                          [StdShape<BM, BN, WM, WN, SCHED>::SN]) {
+    using Shape = StdShape<BM, BN, WM, WN, SCHED>;
+    constexpr int NWAVES = Shape::NWAVES;
+    constexpr int TM = Shape::TM, TN = Shape::TN;
+    constexpr int MF = Shape::MF, SM = Shape::SM, SN = Shape::SN;
+    using AccT = typename Shape::AccT;
     static_assert(SCHED != 2 || (QT == Q_FP8 && TM % 32 == 0 && TN % 32 == 0),
                   "the 32x32 schedule is fp8 only and needs 32-multiple wave tiles");
-    using AccT = typename std::conditional<MF == 32, v16f, v4f>::type;
     constexpr int STAGE = (BM + BN) * 128;         // bytes per LDS stage
     constexpr int CHUNKS = (BM + BN) / 8;          // 1 KB load chunks per stage
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
@@ -60,8 +81,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     constexpr int SC_STAGE = (BM + 64) * 4;
     static_assert(BM % 64 == 0 && BM / 64 <= NWAVES, "one activation-scale DMA per wave");
 
-    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
@@ -70,13 +89,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     const int khalf = lane >> 5;        // 32x32: 32-byte K group within a 64-wide K half
 
     const int64_t M = p.M, N = p.N, K = p.K, KB = K / 128;
-    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    int64_t pid_m, pid_n;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, p.group_m, p.raster, pid_m, pid_n);
-    const int64_t m0 = pid_m * BM, n0 = pid_n * BN;
-
-    const int split = p.split, z = blockIdx.z;
-    const int64_t kb_begin = (int64_t)z * KB / split, kb_end = (int64_t)(z + 1) * KB / split;
 
     // Buffer resources over this tile's rows: rows past M (N) read as zero and are never
     // stored, so ragged tiles need no clamping. K <= 2^23 keeps every offset below 2^32.
@@ -148,7 +160,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
         }
     };
 
-    AccT acc[SM][SN];
 #pragma unroll
     for (int sm = 0; sm < SM; ++sm)
 #pragma unroll
@@ -343,9 +354,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
         for (int64_t kb = kb_begin; kb < kb_end; ++kb) kblock(kb, (int)((kb - kb_begin) & 1));
         wait_vmem_all();      // no LDS DMA may still be in flight when the wave ends
     }
+}
 
-    // Epilogue: lane owns token m and, per sub-tile, columns n..n+3 (16x16) or the four
-    // column groups 8j + 4*(l/32) .. +3, j = 0..3 (32x32).
+// Store a tile's accumulators: element (m, n) goes to base[base_off + m*N + n] as OT.
+// Lane owns token m and, per sub-tile, columns n..n+3 (16x16) or the four column groups
+// 8j + 4*(l/32) .. +3, j = 0..3 (32x32).
+template <int OT, int BM, int BN, int WM, int WN, int SCHED>
+__device__ __forceinline__ void std_store(
+    void* base, int64_t base_off, int64_t M, int64_t N, int64_t m0, int64_t n0,
+    const typename StdShape<BM, BN, WM, WN, SCHED>::AccT (
+        &acc)[StdShape<BM, BN, WM, WN, SCHED>::SM][StdShape<BM, BN, WM, WN, SCHED>::SN]) {
+    using Shape = StdShape<BM, BN, WM, WN, SCHED>;
+    constexpr int TM = Shape::TM, TN = Shape::TN, MF = Shape::MF, SM = Shape::SM, SN = Shape::SN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int frow = lane & (MF - 1), fgrp = lane >> 4, khalf = lane >> 5;
 #pragma unroll
     for (int sm = 0; sm < SM; ++sm) {
         const int64_t m = m0 + wm * TM + sm * MF + frow;
@@ -357,25 +381,226 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
                 for (int j = 0; j < 4; ++j) {
                     const int64_t n = n0 + wn * TN + sn * 32 + 8 * j + 4 * khalf;
                     if (n >= N) continue;
-                    const AccT& a = acc[sm][sn];
+                    const auto& a = acc[sm][sn];
                     const v4f v = {a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]};
-                    if (split == 1) store4<OT>(p.out, m * N + n, v);
-                    else store4<O_FP32>(p.partials, ((int64_t)z * M + m) * N + n, v);
+                    store4<OT>(base, base_off + m * N + n, v);
                 }
             } else {
                 const int64_t n = n0 + wn * TN + sn * 16 + 4 * fgrp;
                 if (n >= N) continue;
-                if (split == 1) store4<OT>(p.out, m * N + n, acc[sm][sn]);
-                else store4<O_FP32>(p.partials, ((int64_t)z * M + m) * N + n, acc[sm][sn]);
+                store4<OT>(base, base_off + m * N + n, acc[sm][sn]);
             }
         }
     }
 }
 
+// One workgroup per (tile, K split): grid = tiles x 1 x split.
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
+    using Shape = StdShape<BM, BN, WM, WN, SCHED>;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+    const int64_t M = p.M, N = p.N, KB = p.K / 128;
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int64_t pid_m, pid_n;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, p.group_m, p.raster, pid_m, pid_n);
+    const int64_t m0 = pid_m * BM, n0 = pid_n * BN;
+    const int split = p.split, z = blockIdx.z;
+    const int64_t kb_begin = (int64_t)z * KB / split, kb_end = (int64_t)(z + 1) * KB / split;
+    typename Shape::AccT acc[Shape::SM][Shape::SN];
+    std_tile<BM, BN, WM, WN, QT, SCHED, STAGES>(p, lds, m0, n0, kb_begin, kb_end, acc);
+    if (split == 1) std_store<OT, BM, BN, WM, WN, SCHED>(p.out, 0, M, N, m0, n0, acc);
+    else std_store<O_FP32, BM, BN, WM, WN, SCHED>(p.partials, (int64_t)z * M * N, M, N, m0, n0, acc);
+}
+
+// Stream-K schedule ("variant 2"): a persistent grid of G workgroups (one per CU) takes
+// tiles [0, dp_tiles) whole, in rounds of G, then splits the K blocks of the remaining tiles
+// evenly: workgroup w owns iterations [w*I/G, (w+1)*I/G) of the I = (tiles - dp_tiles) * KB
+// (tile, K block) iterations, in tile-major order, so it may end with part of a tile and
+// start with part of another. This fills the last, partial wave of tiles that a plain grid
+// leaves half idle. A tile one workgroup covers whole is stored at once; a partial tile is
+// parked, as fp32 in the thread's own register order, in the workgroup's slot (0 for the
+// first tile of its range, 1 for the last), and a second kernel on the same stream sums each
+// split tile's segments in K order and stores it. The kernel boundary publishes the slots,
+// so no workgroup ever waits for or synchronises with another, and the sum order is fixed,
+// so results are deterministic.
+// The iterations are spread over the first Gs = min(G, I) workgroups, so each of those owns at
+// least one; the owner of iteration x is max{w : floor(w*I/Gs) <= x} = ceil((x+1)*Gs/I) - 1,
+// and a tile's segments are exactly the owners of its first through last iteration.
+template <int BM, int BN, int WM, int WN, int SCHED>
+struct SlotIO {
+    using Shape = StdShape<BM, BN, WM, WN, SCHED>;
+    using AccT = typename Shape::AccT;
+    static constexpr int SM = Shape::SM, SN = Shape::SN, NT = 64 * WM * WN;
+    static constexpr int64_t SLOT = (int64_t)BM * BN;   // floats per partial-tile slot
+    // AccT element (sm, sn) is NQ 16-byte pieces; piece q of thread tid sits at byte
+    // ((sm*SN + sn)*NQ + q)*NT*16 + tid*16 of the slot: coalesced, one per-lane offset plus a
+    // constant scalar offset per access.
+    static constexpr int NQ = sizeof(AccT) / 16;
+    static __device__ __forceinline__ v4f piece(const AccT& a, int q) {
+        if constexpr (NQ == 1) { (void)q; return a; }
+        else return v4f{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+    }
+    static __device__ __forceinline__ void set_piece(AccT& a, int q, const v4f& v) {
+        if constexpr (NQ == 1) { (void)q; a = v; }
+        else { a[4 * q] = v.x; a[4 * q + 1] = v.y; a[4 * q + 2] = v.z; a[4 * q + 3] = v.w; }
+    }
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(float* slots, int64_t slot) {
+        return make_rsrc(slots + uniform_i64(slot) * SLOT, (uint32_t)(SLOT * 4));
+    }
+    static __device__ __forceinline__ void park(float* slots, int64_t slot, const AccT (&acc)[SM][SN]) {
+        const __amdgpu_buffer_rsrc_t r = rsrc(slots, slot);
+        const uint32_t voff = threadIdx.x * 16;
+#pragma unroll
+        for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+            for (int sn = 0; sn < SN; ++sn)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    buf_store_v4f(r, piece(acc[sm][sn], q), voff, (uint32_t)(((sm * SN + sn) * NQ + q) * NT * 16));
+    }
+    // acc = slot (first) or acc + slot
+    static __device__ __forceinline__ void add(float* slots, int64_t slot, bool first, AccT (&acc)[SM][SN]) {
+        const __amdgpu_buffer_rsrc_t r = rsrc(slots, slot);
+        const uint32_t voff = threadIdx.x * 16;
+#pragma unroll
+        for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+            for (int sn = 0; sn < SN; ++sn)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const v4f v = buf_load_v4f(r, voff, (uint32_t)(((sm * SN + sn) * NQ + q) * NT * 16));
+                    set_piece(acc[sm][sn], q, first ? v : piece(acc[sm][sn], q) + v);
+                }
+    }
+};
+
+// Iteration-range helpers shared by the stream-K kernel and its fixup kernel.
+__device__ __forceinline__ int64_t sk_owner(int64_t x, int64_t G, int64_t I) {
+    return ((x + 1) * G + I - 1) / I - 1;
+}
+
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_streamk_kernel(GemmArgs p) {
+    using Shape = StdShape<BM, BN, WM, WN, SCHED>;
+    using IO = SlotIO<BM, BN, WM, WN, SCHED>;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+    const int64_t M = p.M, N = p.N, KB = p.K / 128;
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t G = gridDim.x, w = blockIdx.x;
+    typename Shape::AccT acc[Shape::SM][Shape::SN];
+
+    // Work items in order: this workgroup's whole tiles t = w, w+G, ... < dp_tiles (with G a
+    // multiple of 8, tile t runs on the XCD that tile_coords assumes), then its stream-K
+    // iteration range. One call site of the tile routine keeps the register budget of the
+    // plain kernel.
+    const int64_t n_whole = w < p.dp_tiles ? (p.dp_tiles - w + G - 1) / G : 0;
+    const int64_t I = (tiles - p.dp_tiles) * KB;
+    const int64_t Gs = I < G ? I : G;
+    const int64_t it_lo = w < Gs ? w * I / Gs : 0, it_hi = w < Gs ? (w + 1) * I / Gs : 0;
+    int64_t it = it_lo;
+    for (int64_t item = 0;; ++item) {
+        int64_t t, ts = 0, k0 = 0, k1 = KB;
+        if (item < n_whole) {
+            t = w + item * G;
+        } else {
+            if (it >= it_hi) break;
+            ts = it / KB;
+            k0 = it - ts * KB;
+            k1 = (KB - k0) <= (it_hi - it) ? KB : k0 + (it_hi - it);
+            t = p.dp_tiles + ts;
+            it += k1 - k0;
+        }
+        int64_t pm, pn;
+        tile_coords(uniform_i64(t), tiles_m, tiles_n, p.group_m, p.raster, pm, pn);
+        const int64_t m0 = uniform_i64(pm * BM), n0 = uniform_i64(pn * BN);
+        k0 = uniform_i64(k0);
+        k1 = uniform_i64(k1);
+        std_tile<BM, BN, WM, WN, QT, SCHED, STAGES>(p, lds, m0, n0, k0, k1, acc);
+        if (k0 == 0 && k1 == KB) std_store<OT, BM, BN, WM, WN, SCHED>(p.out, 0, M, N, m0, n0, acc);
+        else IO::park(p.sk_slots, w * 2 + (ts == it_lo / KB ? 0 : 1), acc);
+    }
+}
+
+// One workgroup per stream-K tile: a tile split over several workgroups is summed from their
+// parked slots in K order (ascending owner) and stored; a tile one workgroup covered whole
+// was stored by it already. Same block shape as the GEMM, so each thread reads back exactly
+// the accumulator pieces it will store.
+template <int BM, int BN, int WM, int WN, int OT, int SCHED>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_streamk_fixup_kernel(GemmArgs p, int grid) {
+    using Shape = StdShape<BM, BN, WM, WN, SCHED>;
+    using IO = SlotIO<BM, BN, WM, WN, SCHED>;
+    const int64_t M = p.M, N = p.N, KB = p.K / 128;
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t ts = blockIdx.x;
+    const int64_t I = (tiles - p.dp_tiles) * KB;
+    const int64_t Gs = I < grid ? I : grid;
+    const int64_t w_first = sk_owner(ts * KB, Gs, I), w_last = sk_owner(ts * KB + KB - 1, Gs, I);
+    if (w_first == w_last) return;
+    typename Shape::AccT acc[Shape::SM][Shape::SN];
+    for (int64_t ws = w_first; ws <= w_last; ++ws) {
+        const int sl = ts == (ws * I / Gs) / KB ? 0 : 1;
+        IO::add(p.sk_slots, ws * 2 + sl, ws == w_first, acc);
+    }
+    int64_t pm, pn;
+    tile_coords(p.dp_tiles + ts, tiles_m, tiles_n, p.group_m, p.raster, pm, pn);
+    std_store<OT, BM, BN, WM, WN, SCHED>(p.out, 0, M, N, pm * BM, pn * BN, acc);
+}
+
+// Whole rounds first; only the tiles of the last, partial round are split (each split tile
+// costs a parked fp32 partial per segment, written and read back once).
+int64_t streamk_dp_tiles(int64_t tiles, int grid) { return (tiles / grid) * grid; }
+
+size_t streamk_workspace_bytes(int bm, int bn, int grid) {
+    return (size_t)grid * 2 * (size_t)bm * (size_t)bn * sizeof(float);
+}
+
+// Workgroups of the stream-K grid: the device's compute units (one resident workgroup each).
+int streamk_grid() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached[dev] = cus - cus % 8;                   // keep the XCD round-robin aligned
+        if (cached[dev] <= 0) cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
+hipError_t launch_streamk(const GemmArgs& a, hipStream_t stream) {
+    constexpr int LDS_BYTES = StdShape<BM, BN, WM, WN, SCHED>::lds_bytes(STAGES);
+    const int G = streamk_grid();
+    const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    GemmArgs b = a;
+    b.dp_tiles = streamk_dp_tiles(tiles, G);
+    const int64_t I = (tiles - b.dp_tiles) * (a.K / 128);
+    const int64_t grid = b.dp_tiles > 0 ? G : (I < G ? I : G);
+    b.sk_slots = a.partials;
+    static bool attr_set = false;   // one-time opt-in to more than 64 KB of LDS
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&gemm_streamk_kernel<BM, BN, WM, WN, QT, OT, SCHED, STAGES>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((gemm_streamk_kernel<BM, BN, WM, WN, QT, OT, SCHED, STAGES>),
+                       dim3((unsigned)grid), dim3(64 * WM * WN), LDS_BYTES, stream, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || tiles == b.dp_tiles) return e;
+    hipLaunchKernelGGL((gemm_streamk_fixup_kernel<BM, BN, WM, WN, OT, SCHED>),
+                       dim3((unsigned)(tiles - b.dp_tiles)), dim3(64 * WM * WN), 0, stream, b, (int)grid);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
 hipError_t launch_std(const GemmArgs& a, hipStream_t stream) {
-    constexpr int STAGE = (BM + BN) * 128;
-    constexpr int LDS_BYTES = 2 * STAGE + (STAGES > 2 ? 256 * WM * WN : 0) + 2 * (BM + 64) * 4;
+    constexpr int LDS_BYTES = StdShape<BM, BN, WM, WN, SCHED>::lds_bytes(STAGES);
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     dim3 grid((unsigned)tiles, 1, (unsigned)a.split);
     static bool attr_set = false;   // one-time opt-in to more than 64 KB of LDS
@@ -415,6 +640,26 @@ static const KernelEntry kStdKernels[] = {
     BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 0, Q_INT8),
     BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 0, Q_INT8),
 };
+
+#define BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, OT)                                     \
+    KernelEntry{bfq_tile{2, BM, BN, 128, 1, WM, WN, ST, 8, SC, 0, 0}, QT, OT,             \
+                &launch_streamk<BM, BN, WM, WN, QT, OT, SC, ST>}
+
+#define BFQ_SK_ALL_OUT(BM, BN, WM, WN, ST, SC, QT)                                        \
+    BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_BF16),                                     \
+        BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_FP16),                                 \
+        BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_FP32)
+
+static const KernelEntry kStreamKKernels[] = {
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 0, Q_INT8),
+};
+
+const KernelEntry* streamk_kernels(int* count) {
+    *count = (int)(sizeof(kStreamKKernels) / sizeof(kStreamKKernels[0]));
+    return kStreamKKernels;
+}
 
 const KernelEntry* std_kernels(int* count) {
     *count = (int)(sizeof(kStdKernels) / sizeof(kStdKernels[0]));

@@ -123,7 +123,7 @@ def candidates(qd, M, N, K):
         t = bfq.bfq_get_tile_candidate(i, qd)
         if t.variant == 1 and M > 4 * t.bm:
             continue
-        if t.variant == 0 and M <= 16 and t.bm > 64:
+        if t.variant in (0, 2) and M <= 16 and t.bm > 64:
             continue
         if t.variant == 1:
             ctas = -(-N // t.bn) * -(-M // t.bm)
@@ -133,6 +133,8 @@ def candidates(qd, M, N, K):
             orders = [(8, 0), (2, 1)] if ctas >= 64 else [(8, 0)]
         for s in SPLITS:
             if s > KB or KB // s < 2 or (s > 1 and ctas * s > 4 * NUM_CUS):
+                continue
+            if t.variant == 2 and s > 1:        # stream-K splits K by itself
                 continue
             for g, r in orders:
                 d = t.as_dict()

@@ -72,13 +72,18 @@ typedef enum {
  *   variant 1 "swap_ab": the weight rows stream straight from HBM into the wide MFMA
  *             operand and the bm tokens ride in the narrow one; the output tile is formed
  *             transposed and stored back row-major ([HELION] kernel section).
+ *   variant 2 "stream-K": the tiles of variant 0 on a persistent grid of one workgroup per
+ *             compute unit; whole tiles in rounds, then the K blocks of the last one to two
+ *             rounds of tiles split evenly over the grid; a second kernel sums each split
+ *             tile's parked fp32 partials in K order (split_k must be 1). Its workspace holds
+ *             two partial tiles per compute unit.
  *   split_k  : K blocks split into split_k contiguous chunks (>= 1), fp32 partials reduced
  *             in a fixed order ([HELION] kernel section).
- *   stages   : LDS stages (variant 0) or weight prefetch depth in K blocks (variant 1).
- *   sched    : variant 0 instruction schedule: 0 = each sub-tile's scale FMAs right after its
+ *   stages   : LDS stages (variants 0, 2) or weight prefetch depth in K blocks (variant 1).
+ *   sched    : variants 0 and 2 instruction schedule: 0 = each sub-tile's scale FMAs right after its
  *             MFMAs, 1 = software-pipelined (FMAs one sub-tile behind the MFMAs), 2 = 32x32
  *             sub-tiles (two 32x32x64 MFMAs per K block, FMAs one pair behind; fp8 only).
- *   group_m, raster: variant 0 tile order (launch arguments, any group_m >= 1): raster 0
+ *   group_m, raster: variants 0 and 2 tile order (launch arguments, any group_m >= 1): raster 0
  *             gives each of the 8 XCDs a contiguous range of tiles, raster 1 does not.
  *   bk is always 128 (one scale block per K step). */
 typedef struct {

@@ -104,7 +104,7 @@ def test_candidates_enumerate(bfq):
         seen = set()
         for i in range(n):
             t = bfq.bfq_get_tile_candidate(i, qd)
-            assert t.split_k == 1 and t.bk == 128 and t.variant in (0, 1)
+            assert t.split_k == 1 and t.bk == 128 and t.variant in (0, 1, 2)
             seen.add(tuple(t.as_dict().values()))
         assert len(seen) == n
     with pytest.raises(bfq.BfqError):

@@ -75,6 +75,8 @@ def test_every_candidate_and_split_parity(bfq, orc, qname):
     dq = _to_dev(*host)
     for t in _candidates(bfq, qd):
         for s in (1, 2, 3):
+            if t.variant == 2 and s > 1:        # stream-K splits K by itself
+                continue
             tile = _with_split(t, s)
             what = (qname, tile.as_dict())
             print("candidate", what, flush=True)
@@ -88,6 +90,42 @@ def test_every_candidate_and_split_parity(bfq, orc, qname):
             oh = _run(bfq, dq, torch.float16, tile=tile).float().cpu().numpy()
             ref_h = torch.from_numpy(o32).half().float().numpy()
             assert np.array_equal(oh, ref_h), what
+
+
+@pytest.mark.parametrize("qname", ["fp8", "int8"])
+def test_streamk_segments_and_determinism(bfq, orc, qname):
+    """Stream-K (variant 2) with few tiles and many K blocks: at M=300, N=640, K=896 a 256x256
+    tile grid has 6 tiles of 7 blocks, so 42 one-block segments land on 42 workgroups and
+    every tile is summed from 7 parked partials; fp32 within the bar of the oracle, bf16 the
+    rounding of the same run's fp32, and two runs bit-identical (the segment sum order does
+    not depend on which workgroup arrives last)."""
+    from oracle import metrics
+    qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
+    qt = orc.FP8 if qname == "fp8" else orc.INT8
+    M, N, K = 300, 640, 896
+    host = _case(orc, M, N, K, 25, qt)
+    ref32, _ = orc.block_gemm(*host, qtype=qt)
+    dq = _to_dev(*host)
+    sk = [t for t in _candidates(bfq, qd) if t.variant == 2]
+    assert sk, "no stream-K kernel compiled for " + qname
+    for t in sk:
+        what = (qname, t.as_dict())
+        print("stream-K", what, flush=True)
+        o32a = _run(bfq, dq, torch.float32, tile=t).cpu().numpy()
+        _check_fp32(metrics, o32a, ref32, what)
+        o32b = _run(bfq, dq, torch.float32, tile=t).cpu().numpy()
+        assert np.array_equal(o32a.view(np.uint32), o32b.view(np.uint32)), what
+        o16 = _run(bfq, dq, torch.bfloat16, tile=t).view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(o16, orc.f32_to_bf16_bits_array(o32a)), what
+
+
+@pytest.mark.parametrize("M,N,K", [(2304, 7680, 1024), (5120, 7680, 512)])
+def test_streamk_large_sampled(bfq, orc, M, N, K):
+    """Stream-K at grid-filling sizes, sampled against the oracle: 270 tiles of 256x256 (all
+    split over the grid) and 600 tiles (256 taken whole, 344 split)."""
+    for t in [t for t in _candidates(bfq, bfq.BFQ_E4M3FN) if t.variant == 2]:
+        print("stream-K", M, N, K, t.as_dict(), flush=True)
+        _sampled_check(bfq, orc, M, N, K, M, "fp8", n_samples=2048, tile=t)
 
 
 @pytest.mark.parametrize("qname", ["fp8", "int8"])
@@ -114,6 +152,8 @@ def test_exact_integer_case_every_candidate(bfq, orc, qname):
     dq = _to_dev(qa, sa, qw, sw)
     for t in _candidates(bfq, qd):
         for s in (1, 4):
+            if t.variant == 2 and s > 1:
+                continue
             tile = _with_split(t, s)
             o32 = _run(bfq, dq, torch.float32, tile=tile).cpu().numpy().astype(np.float64)
             assert np.array_equal(o32, exact), (qname, tile.as_dict())
@@ -203,7 +243,7 @@ def test_deterministic_run_twice(bfq, orc):
     M, N, K = 64, 1536, 7168
     dq = _to_dev(*_case(orc, M, N, K, 71, orc.FP8))
     for t in _candidates(bfq, bfq.BFQ_E4M3FN):
-        tile = _with_split(t, 4)
+        tile = _with_split(t, 1 if t.variant == 2 else 4)
         a = _run(bfq, dq, torch.float32, tile=tile)
         b = _run(bfq, dq, torch.float32, tile=tile)
         assert torch.equal(a, b), t.as_dict()
@@ -244,13 +284,14 @@ def _full_inputs(bfq, N, K, m_max, qname):
     return _cache[key]
 
 
-def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096):
+def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096, tile=None):
     from oracle import metrics
     qt = orc.FP8 if qname == "fp8" else orc.INT8
     qa, sa, qw, sw, qa_h, sa_h, qw_h, sw_h = _full_inputs(bfq, N, K, m_max, qname)
     out32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
     out16 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-    st, tile = bfq.bfq_select_tile(M, N, K, bfq._qdtype(qa), bfq.BFQ_FP32)
+    if tile is None:
+        st, tile = bfq.bfq_select_tile(M, N, K, bfq._qdtype(qa), bfq.BFQ_FP32)
     ws_bytes = bfq.bfq_gemm_workspace_bytes(M, N, K, tile)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
     bfq.bfq_block_gemm(qa[:M], sa[:M], qw, sw, out32, tile=tile, workspace=ws, workspace_bytes=ws_bytes)
