@@ -8,7 +8,9 @@ the block GEMM benchmark page §4.1). Inputs are resident in HBM when timing sta
 
 Default workload: N=24576, K=7168 (DeepSeek-V3 wide MoE up-projection) over the 18-point M
 grid 1..4096. To keep the weight stream honest against the 256 MB Infinity Cache, launches
-rotate over R copies of the weights (default 2 -> 352 MB working set).
+rotate over R copies of the weights (default 3 -> 528 MB working set, over twice the cache).
+The weight codes sit in HBM in the packed fragment layout by default (--w-layout row for the
+row-major [N, K] form); packing, like the weight quantization, is an offline step.
 
 Prints ONE JSON line (metric, value = GEMM TFLOPS over the whole step including the
 quantization time, per-M detail, roofline of the dominant kernel, CPU-oracle baseline).
@@ -47,25 +49,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_name(t, qtype: str, out: str = "bf16") -> str:
+def kernel_name(t, qtype: str, wl: int, out: str = "bf16") -> str:
     """The demangled name of the device kernel a tile launches (as rocprofv3 prints it)."""
     q = 0 if qtype == "fp8" else 1
     o = {"bf16": 0, "fp16": 1, "fp32": 2}[out]
     d = t.as_dict()
-    if d["variant"] == 0:
-        return (f"bfq::gemm_std_kernel<{d['bm']}, {d['bn']}, {d['waves_m']}, {d['waves_n']}, "
-                f"{q}, {o}, {d['sched']}, {d['stages']}>")
+    if d["variant"] in (0, 2):
+        kern = "gemm_std_kernel" if d["variant"] == 0 else "gemm_streamk_kernel"
+        return (f"bfq::{kern}<{d['bm']}, {d['bn']}, {d['waves_m']}, {d['waves_n']}, "
+                f"{q}, {o}, {d['sched']}, {d['stages']}, {wl}>")
     nwr = d["bn"] // d["waves_n"]
-    return f"bfq::gemm_swapab_kernel<{d['bm']}, {nwr}, {d['waves_n']}, {d['stages']}, {q}, {o}>"
+    kern = "gemm_swapab_lds_kernel" if d["sched"] == 1 else "gemm_swapab_kernel"
+    return (f"bfq::{kern}<{d['bm']}, {nwr}, {d['waves_n']}, {d['waves_m']}, "
+            f"{d['stages']}, {q}, {o}, {wl}>")
 
 
 def grid_threads(t, M, N) -> int:
     d = t.as_dict()
+    if d["variant"] == 2:
+        return 256 * 64 * d["waves_m"] * d["waves_n"]
     if d["variant"] == 0:
         wg = -(-M // d["bm"]) * -(-N // d["bn"]) * d["split_k"]
         return wg * 64 * d["waves_m"] * d["waves_n"]
     wg = -(-N // d["bn"]) * -(-M // d["bm"]) * d["split_k"]
-    return wg * 64 * d["waves_n"]
+    return wg * 64 * d["waves_n"] * d["waves_m"]
 
 
 def tile_key(t) -> str:
@@ -80,6 +87,7 @@ def run_gpu(args, wl):
 
     dev = torch.device("cuda:0")
     qd = bfq.BFQ_E4M3FN if wl["qtype"] == "fp8" else bfq.BFQ_INT8
+    wlay = bfq.BFQ_W_PACKED16 if args.w_layout == "packed" else bfq.BFQ_W_ROW_MAJOR
     m_max = max(wl["M"])
     col = args.scale_layout == "col"
     shapes = []
@@ -92,6 +100,8 @@ def run_gpu(args, wl):
         copies = []
         for r in range(args.rotate):
             qw, sw = bfq.quant_weight_blocks(wd, q_dtype=qd)
+            if wlay == bfq.BFQ_W_PACKED16:        # offline layout step, like the quantization
+                qw = bfq.pack_weights(qw)
             copies.append((qw, sw))
         del wd
         xd = x.to(dev)
@@ -102,7 +112,7 @@ def run_gpu(args, wl):
         out = torch.empty((m_max, N), dtype=torch.bfloat16, device=dev)
         plans = []
         for M in wl["M"]:
-            st, tile = bfq.bfq_select_tile(M, N, K, qd, bfq.BFQ_BF16)
+            st, tile = bfq.bfq_select_tile(M, N, K, qd, bfq.BFQ_BF16, w_layout=wlay)
             ws_bytes = bfq.bfq_gemm_workspace_bytes(M, N, K, tile)
             plans.append((M, tile, ws_bytes, st))
         ws_max = max(p[2] for p in plans)
@@ -131,7 +141,7 @@ def run_gpu(args, wl):
                     e1.record()
                 bfq.bfq_block_gemm(sh["qa"][:M], sa_m, qw, sw, sh["out"][:M], a_layout=lay,
                                    a_scale_ld=sh["sa"].stride(0), tile=tile, workspace=sh["ws"],
-                                   workspace_bytes=sh["ws_max"])
+                                   workspace_bytes=sh["ws_max"], w_layout=wlay)
                 if events is not None:
                     e2.record()
                     events.append((N, K, M, tile_key(tile), e0, e1, e2))
@@ -218,7 +228,7 @@ def run_gpu(args, wl):
                 "quant_gbs": round(perf.quant_bytes(M, K) / q / 1e9, 1),
             })
             gr = groups.setdefault(r["key"], {"t": 0.0, "n": 0, "flops": 0.0, "bytes": 0.0,
-                                              "name": kernel_name(tile, wl["qtype"]),
+                                              "name": kernel_name(tile, wl["qtype"], wlay),
                                               "grids": set()})
             gr["grids"].add(grid_threads(tile, M, N))
             gr["t"] += sum(r["g"])
@@ -305,12 +315,14 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mgrid", choices=sorted(WORKLOADS))
-    ap.add_argument("--rotate", type=int, default=2, help="weight copies rotated per launch")
+    ap.add_argument("--rotate", type=int, default=3, help="weight copies rotated per launch")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--scale-layout", default="col", choices=["row", "col"],
                     help="activation-scale layout written by the quantizer and read by the GEMM")
+    ap.add_argument("--w-layout", default="packed", choices=["row", "packed"],
+                    help="weight-code layout in HBM (packed: bfq_pack_weights, done offline)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -338,7 +350,8 @@ def main():
         "config": {"workload": wl["desc"], "shapes_NK": wl["shapes"], "M": wl["M"],
                    "block_shape": [128, 128], "out_dtype": "bf16",
                    "weight_copies_rotated": args.rotate,
-                   "activation_scale_layout": args.scale_layout + "_major"},
+                   "activation_scale_layout": args.scale_layout + "_major",
+                   "weight_layout": "packed16" if args.w_layout == "packed" else "row_major"},
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "per_m": res["rows"],

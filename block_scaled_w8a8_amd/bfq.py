@@ -30,12 +30,15 @@ BFQ_BF16, BFQ_FP16, BFQ_FP32, BFQ_E4M3FN, BFQ_INT8, BFQ_INT32 = range(6)
 # scale layouts (bfq_scale_layout)
 BFQ_SCALES_ROW_MAJOR = 0
 BFQ_SCALES_COL_MAJOR = 1
+# weight-code layouts (bfq_weight_layout)
+BFQ_W_ROW_MAJOR = 0
+BFQ_W_PACKED16 = 1
 
 DEFAULT_EPS = 1e-10
 BLOCK_SHAPE = (128, 128)
 
 EXPORTED = (
-    "bfq_quant_tokens", "bfq_quant_weight_blocks", "bfq_select_tile",
+    "bfq_quant_tokens", "bfq_quant_weight_blocks", "bfq_pack_weights", "bfq_select_tile",
     "bfq_gemm_workspace_bytes", "bfq_block_gemm", "bfq_load_tile_table",
     "bfq_num_tile_candidates", "bfq_get_tile_candidate", "bfq_status_string",
     "bfq_last_error", "bfq_debug_block_partials_i32", "bfq_debug_encode",
@@ -89,13 +92,14 @@ def _load():
     sig = {
         "bfq_quant_tokens": (i32, [p, i64, i64, i32, i32, p, p, i32, i64, f32, p]),
         "bfq_quant_weight_blocks": (i32, [p, i64, i64, bs, i32, p, p, f32, p]),
-        "bfq_select_tile": (i32, [i64, i64, i64, bs, i32, i32, tp]),
+        "bfq_pack_weights": (i32, [p, i64, i64, i32, p, p]),
+        "bfq_select_tile": (i32, [i64, i64, i64, bs, i32, i32, i32, tp]),
         "bfq_gemm_workspace_bytes": (sz, [i64, i64, i64, tp]),
-        "bfq_block_gemm": (i32, [p, p, i32, i64, p, p, p, i64, i64, i64, bs, i32, i32, tp, p,
-                                 sz, p]),
+        "bfq_block_gemm": (i32, [p, p, i32, i64, p, p, i32, p, i64, i64, i64, bs, i32, i32, tp,
+                                 p, sz, p]),
         "bfq_load_tile_table": (i32, [ctypes.c_char_p]),
-        "bfq_num_tile_candidates": (i32, [i32]),
-        "bfq_get_tile_candidate": (i32, [i32, i32, tp]),
+        "bfq_num_tile_candidates": (i32, [i32, i32]),
+        "bfq_get_tile_candidate": (i32, [i32, i32, i32, tp]),
         "bfq_status_string": (ctypes.c_char_p, [i32]),
         "bfq_last_error": (ctypes.c_char_p, []),
         "bfq_debug_block_partials_i32": (i32, [p, p, p, i64, i64, i64, p]),
@@ -188,12 +192,22 @@ def bfq_quant_weight_blocks(w, q, scales, eps=DEFAULT_EPS, block_shape=BLOCK_SHA
     return _check(st, "bfq_quant_weight_blocks")
 
 
+def bfq_pack_weights(w_q, w_packed, stream=None) -> int:
+    """w_q: row-major codes [N, K]; w_packed: a separate N*K-byte buffer (any shape with that
+    many bytes, e.g. [N, K] uint8) that receives the BFQ_W_PACKED16 layout."""
+    N, K = w_q.shape
+    if w_packed.numel() * w_packed.element_size() != N * K:
+        raise ValueError("w_packed must hold exactly N*K bytes")
+    st = lib.bfq_pack_weights(_ptr(w_q), N, K, _qdtype(w_q), _ptr(w_packed), _stream(stream))
+    return _check(st, "bfq_pack_weights")
+
+
 def bfq_select_tile(M, N, K, in_dtype=BFQ_E4M3FN, out_dtype=BFQ_BF16,
-                    block_shape=BLOCK_SHAPE):
+                    block_shape=BLOCK_SHAPE, w_layout=BFQ_W_ROW_MAJOR):
     """Returns (status, bfq_tile)."""
     t = bfq_tile()
     st = lib.bfq_select_tile(M, N, K, _block_shape(block_shape), in_dtype, out_dtype,
-                             ctypes.byref(t))
+                             w_layout, ctypes.byref(t))
     if st < 0:
         raise BfqError(st, "bfq_select_tile")
     return st, t
@@ -205,8 +219,9 @@ def bfq_gemm_workspace_bytes(M, N, K, tile=None) -> int:
 
 def bfq_block_gemm(a_q, a_scales, w_q, w_scales, out, a_layout=BFQ_SCALES_ROW_MAJOR,
                    a_scale_ld=None, tile=None, workspace=None, workspace_bytes=None,
-                   block_shape=BLOCK_SHAPE, stream=None) -> int:
-    """a_q [M, K] codes, w_q [N, K] codes, a_scales per layout, w_scales [N/128, K/128],
+                   block_shape=BLOCK_SHAPE, stream=None, w_layout=BFQ_W_ROW_MAJOR) -> int:
+    """a_q [M, K] codes, w_q [N, K] codes in w_layout (row-major, or packed by
+    bfq_pack_weights and still shaped [N, K]), a_scales per layout, w_scales [N/128, K/128],
     out [M, N] (bf16 / fp16 / fp32). Returns the status (>= 0)."""
     M, K = a_q.shape
     N = w_q.shape[0]
@@ -215,7 +230,7 @@ def bfq_block_gemm(a_q, a_scales, w_q, w_scales, out, a_layout=BFQ_SCALES_ROW_MA
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.bfq_block_gemm(_ptr(a_q), _ptr(a_scales), a_layout, a_scale_ld, _ptr(w_q),
-                            _ptr(w_scales), _ptr(out), M, N, K, _block_shape(block_shape),
+                            _ptr(w_scales), w_layout, _ptr(out), M, N, K, _block_shape(block_shape),
                             _qdtype(a_q), _odtype(out), ctypes.byref(tile) if tile else None,
                             _ptr(workspace), workspace_bytes, _stream(stream))
     return _check(st, "bfq_block_gemm", warn_key=(N, K))
@@ -226,13 +241,14 @@ def bfq_load_tile_table(path=None) -> int:
     return _check(st, "bfq_load_tile_table")
 
 
-def bfq_num_tile_candidates(in_dtype=BFQ_E4M3FN) -> int:
-    return int(lib.bfq_num_tile_candidates(in_dtype))
+def bfq_num_tile_candidates(in_dtype=BFQ_E4M3FN, w_layout=BFQ_W_ROW_MAJOR) -> int:
+    return int(lib.bfq_num_tile_candidates(in_dtype, w_layout))
 
 
-def bfq_get_tile_candidate(index, in_dtype=BFQ_E4M3FN) -> bfq_tile:
+def bfq_get_tile_candidate(index, in_dtype=BFQ_E4M3FN, w_layout=BFQ_W_ROW_MAJOR) -> bfq_tile:
     t = bfq_tile()
-    _check(lib.bfq_get_tile_candidate(in_dtype, index, ctypes.byref(t)), "bfq_get_tile_candidate")
+    _check(lib.bfq_get_tile_candidate(in_dtype, w_layout, index, ctypes.byref(t)),
+           "bfq_get_tile_candidate")
     return t
 
 
@@ -284,8 +300,17 @@ def quant_weight_blocks(w, q_dtype=BFQ_E4M3FN, eps=DEFAULT_EPS, stream=None):
     return q, s
 
 
+def pack_weights(w_q, stream=None):
+    """Allocate a packed copy of row-major weight codes (same dtype and [N, K] shape) with
+    torch and run bfq_pack_weights."""
+    import torch
+    p = torch.empty_like(w_q, memory_format=torch.contiguous_format)
+    bfq_pack_weights(w_q, p, stream=stream)
+    return p
+
+
 def block_gemm(a_q, a_scales, w_q, w_scales, out_dtype=None, a_layout=BFQ_SCALES_ROW_MAJOR,
-               tile=None, stream=None):
+               tile=None, stream=None, w_layout=BFQ_W_ROW_MAJOR):
     """Allocate out (and split-K workspace) with torch and run bfq_block_gemm."""
     import torch
     out_dtype = out_dtype or torch.bfloat16
@@ -293,10 +318,10 @@ def block_gemm(a_q, a_scales, w_q, w_scales, out_dtype=None, a_layout=BFQ_SCALES
     N = w_q.shape[0]
     out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
     if tile is None:
-        st, tile = bfq_select_tile(M, N, K, _qdtype(a_q), _odtype(out))
+        st, tile = bfq_select_tile(M, N, K, _qdtype(a_q), _odtype(out), w_layout=w_layout)
         _check(st, "bfq_select_tile", warn_key=(N, K))
     ws_bytes = bfq_gemm_workspace_bytes(M, N, K, tile)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=a_q.device) if ws_bytes else None
     bfq_block_gemm(a_q, a_scales, w_q, w_scales, out, a_layout=a_layout, tile=tile,
-                   workspace=ws, workspace_bytes=ws_bytes, stream=stream)
+                   workspace=ws, workspace_bytes=ws_bytes, stream=stream, w_layout=w_layout)
     return out

@@ -60,13 +60,13 @@ bool read_file(const std::string& path, std::string& text) {
     return true;
 }
 
-const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype);
+const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype, int wlayout);
 
 // Every table tile must name a compiled kernel; otherwise the table is rejected.
 bool validate_table(const TileTable& t, std::string& err) {
     for (auto& e : t.entries)
         for (auto& b : e.second) {
-            if (!find_kernel(b.second, e.first.qtype, O_BF16)) {
+            if (!find_kernel(b.second, e.first.qtype, O_BF16, e.first.wlayout)) {
                 err = "table entry N=" + std::to_string(e.first.N) + " K=" +
                       std::to_string(e.first.K) + " M=" + std::to_string(b.first) +
                       " names a tile that is not compiled";
@@ -108,14 +108,13 @@ void ensure_table() {
 
 // ------------------------------------------------------------------ registry ----
 bool same_shape(const bfq_tile& a, const bfq_tile& b) {
-    if (a.variant != b.variant || a.bm != b.bm || a.bn != b.bn || a.waves_n != b.waves_n ||
-        a.stages != b.stages)
+    if (a.variant != b.variant || a.bm != b.bm || a.bn != b.bn || a.waves_m != b.waves_m ||
+        a.waves_n != b.waves_n || a.stages != b.stages)
         return false;
-    if (a.variant == 0 || a.variant == 2) return a.waves_m == b.waves_m && a.sched == b.sched;
-    return true;
+    return a.sched == b.sched;
 }
 
-const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype) {
+const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype, int wlayout) {
     if (t.bk != 0 && t.bk != 128) return nullptr;
     int n = 0;
     const KernelEntry* list = t.variant == 0   ? std_kernels(&n)
@@ -123,7 +122,8 @@ const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype) {
                               : t.variant == 2 ? streamk_kernels(&n)
                                                : nullptr;
     for (int i = 0; list && i < n; ++i)
-        if (list[i].qtype == qtype && list[i].otype == otype && same_shape(list[i].tile, t))
+        if (list[i].qtype == qtype && list[i].otype == otype && list[i].wlayout == wlayout &&
+            same_shape(list[i].tile, t))
             return &list[i];
     return nullptr;
 }
@@ -173,11 +173,11 @@ int qtype_of(bfq_dtype d) { return d == BFQ_E4M3FN ? Q_FP8 : Q_INT8; }
 
 int otype_of(bfq_dtype d) { return d == BFQ_BF16 ? O_BF16 : d == BFQ_FP16 ? O_FP16 : O_FP32; }
 
-bfq_status select_tile(int64_t M, int64_t N, int64_t K, int qtype, bfq_tile* out) {
+bfq_status select_tile(int64_t M, int64_t N, int64_t K, int qtype, int wlayout, bfq_tile* out) {
     ensure_table();
     {
         std::lock_guard<std::mutex> lk(g_table_mu);
-        auto it = g_table.entries.find(TableKey{N, K, qtype});
+        auto it = g_table.entries.find(TableKey{N, K, qtype, wlayout});
         if (it != g_table.entries.end()) {
             *out = it->second.at(nearest_bucket(it->second, M));
             out->bk = 128;
@@ -186,12 +186,14 @@ bfq_status select_tile(int64_t M, int64_t N, int64_t K, int qtype, bfq_tile* out
     }
     *out = default_tile(M, N, K);
     if (std::getenv("BFQ_LOG"))
-        std::fprintf(stderr, "[bfq] no tuned entry for N=%lld K=%lld; using default tile\n",
-                     (long long)N, (long long)K);
+        std::fprintf(stderr, "[bfq] no tuned entry for N=%lld K=%lld layout=%d; using default tile\n",
+                     (long long)N, (long long)K, wlayout);
     return BFQ_WARN_DEFAULT_TILE;
 }
 
 bool block_shape_ok(const int32_t* bs) { return bs && bs[0] == 128 && bs[1] == 128; }
+
+bool wlayout_ok(bfq_weight_layout w) { return w == BFQ_W_ROW_MAJOR || w == BFQ_W_PACKED16; }
 
 size_t workspace_for(int64_t M, int64_t N, const bfq_tile& t) {
     if (t.variant == 2) {
@@ -279,8 +281,29 @@ bfq_status bfq_quant_weight_blocks(const float* w, int64_t N, int64_t K,
     return BFQ_OK;
 }
 
+bfq_status bfq_pack_weights(const void* w_q, int64_t N, int64_t K, bfq_dtype q_dtype,
+                            void* w_packed, void* stream) {
+    if (!w_q || !w_packed) return fail(BFQ_ERR_NULL, "w_q and w_packed must be non-NULL");
+    if (q_dtype != BFQ_E4M3FN && q_dtype != BFQ_INT8)
+        return fail(BFQ_ERR_DTYPE, "q_dtype must be BFQ_E4M3FN or BFQ_INT8");
+    if (N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0)
+        return fail(BFQ_ERR_SHAPE, "N and K must be non-negative multiples of 128");
+    if (N > 0x7FFFFFFF || K > 0x7FFFFFFF || N * K / 4096 > 0x7FFFFFFF)
+        return fail(BFQ_ERR_SHAPE, "N * K too large (one 256-thread block per 4 KiB)");
+    if (!aligned(w_q, 16) || !aligned(w_packed, 16))
+        return fail(BFQ_ERR_ALIGN, "w_q and w_packed must be 16-byte aligned");
+    const uintptr_t a = (uintptr_t)w_q, b = (uintptr_t)w_packed, n = (uintptr_t)(N * K);
+    if (n > 0 && a < b + n && b < a + n)
+        return fail(BFQ_ERR_ARG, "w_q and w_packed must not overlap");
+    if (N == 0 || K == 0) return BFQ_OK;
+    hipError_t e = launch_pack_weights(w_q, w_packed, N, K, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
+    return BFQ_OK;
+}
+
 bfq_status bfq_select_tile(int64_t M, int64_t N, int64_t K, const int32_t block_shape[2],
-                           bfq_dtype in_dtype, bfq_dtype out_dtype, bfq_tile* tile_out) {
+                           bfq_dtype in_dtype, bfq_dtype out_dtype, bfq_weight_layout w_layout,
+                           bfq_tile* tile_out) {
     if (!tile_out || !block_shape) return fail(BFQ_ERR_NULL, "tile_out and block_shape must be non-NULL");
     if (!block_shape_ok(block_shape)) return fail(BFQ_ERR_SHAPE, "block_shape must be {128, 128}");
     if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8)
@@ -289,20 +312,22 @@ bfq_status bfq_select_tile(int64_t M, int64_t N, int64_t K, const int32_t block_
         return fail(BFQ_ERR_DTYPE, "out_dtype must be BF16, FP16 or FP32");
     if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
         return fail(BFQ_ERR_SHAPE, "need M >= 0 and N, K positive multiples of 128");
-    return select_tile(M, N, K, qtype_of(in_dtype), tile_out);
+    if (!wlayout_ok(w_layout)) return fail(BFQ_ERR_ARG, "unknown weight layout");
+    return select_tile(M, N, K, qtype_of(in_dtype), (int)w_layout, tile_out);
 }
 
 size_t bfq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const bfq_tile* tile) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
     bfq_tile t;
     if (tile) t = *tile;
-    else select_tile(M, N, K, Q_FP8, &t);
+    else select_tile(M, N, K, Q_FP8, W_ROW, &t);
     return workspace_for(M, N, t);
 }
 
 bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
-                          int64_t a_scale_ld, const void* w_q, const float* w_scales, void* out,
-                          int64_t M, int64_t N, int64_t K, const int32_t block_shape[2],
+                          int64_t a_scale_ld, const void* w_q, const float* w_scales,
+                          bfq_weight_layout w_layout, void* out, int64_t M, int64_t N, int64_t K,
+                          const int32_t block_shape[2],
                           bfq_dtype in_dtype, bfq_dtype out_dtype, const bfq_tile* tile,
                           void* workspace, size_t workspace_bytes, void* stream) {
     if (!w_q || !w_scales || !block_shape || (M != 0 && (!a_q || !a_scales || !out)))
@@ -312,6 +337,7 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
         return fail(BFQ_ERR_DTYPE, "in_dtype must be BFQ_E4M3FN or BFQ_INT8");
     if (out_dtype != BFQ_BF16 && out_dtype != BFQ_FP16 && out_dtype != BFQ_FP32)
         return fail(BFQ_ERR_DTYPE, "out_dtype must be BF16, FP16 or FP32");
+    if (!wlayout_ok(w_layout)) return fail(BFQ_ERR_ARG, "unknown weight layout");
     if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
         return fail(BFQ_ERR_SHAPE, "need M >= 0 and N, K positive multiples of 128");
     if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > (1 << 23))
@@ -335,16 +361,17 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     // blocks) with 32-bit byte offsets
     if ((255 * ssm + (KB - 1) * ssk + 1) * 4 >= (int64_t(1) << 32))
         return fail(BFQ_ERR_SHAPE, "activation scales of 256 tokens must span less than 4 GiB");
-    const int qtype = qtype_of(in_dtype), otype = otype_of(out_dtype);
+    const int qtype = qtype_of(in_dtype), otype = otype_of(out_dtype), wl = (int)w_layout;
     bfq_status status = BFQ_OK;
     bfq_tile t;
     if (tile) {
         t = *tile;
     } else {
-        status = select_tile(M, N, K, qtype, &t);
+        status = select_tile(M, N, K, qtype, wl, &t);
     }
-    const KernelEntry* ke = find_kernel(t, qtype, otype);
-    if (!ke) return fail(BFQ_ERR_TILE, "tile does not name a compiled kernel for this dtype pair");
+    const KernelEntry* ke = find_kernel(t, qtype, otype, wl);
+    if (!ke)
+        return fail(BFQ_ERR_TILE, "tile does not name a compiled kernel for this dtype pair and weight layout");
     if (t.split_k < 1 || t.split_k > 256 || t.split_k > KB)
         return fail(BFQ_ERR_TILE, "split_k must be in [1, min(256, K/128)]");
     if (t.variant == 2 && t.split_k != 1)
@@ -386,8 +413,8 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
         e = launch_splitk_reduce(ga.partials, out, M, N, t.split_k, otype, s);
     if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
     if (std::getenv("BFQ_TRACE"))
-        std::fprintf(stderr, "[bfq] gemm M=%lld N=%lld K=%lld variant=%d bm=%d bn=%d split=%d\n",
-                     (long long)M, (long long)N, (long long)K, t.variant, t.bm, t.bn, t.split_k);
+        std::fprintf(stderr, "[bfq] gemm M=%lld N=%lld K=%lld layout=%d variant=%d bm=%d bn=%d split=%d\n",
+                     (long long)M, (long long)N, (long long)K, wl, t.variant, t.bm, t.bn, t.split_k);
     return status;
 }
 
@@ -397,26 +424,31 @@ bfq_status bfq_load_tile_table(const char* json_path) {
     return load_table_locked(json_path, true);
 }
 
-int32_t bfq_num_tile_candidates(bfq_dtype in_dtype) {
+int32_t bfq_num_tile_candidates(bfq_dtype in_dtype, bfq_weight_layout w_layout) {
     if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8) return 0;
-    const int q = qtype_of(in_dtype);
+    if (!wlayout_ok(w_layout)) return 0;
+    const int q = qtype_of(in_dtype), wl = (int)w_layout;
     int ns[3] = {0, 0, 0}, count = 0;
     const KernelEntry* lists[3] = {std_kernels(&ns[0]), swapab_kernels(&ns[1]), streamk_kernels(&ns[2])};
     for (int l = 0; l < 3; ++l)
-        for (int i = 0; i < ns[l]; ++i) count += (lists[l][i].qtype == q && lists[l][i].otype == O_BF16);
+        for (int i = 0; i < ns[l]; ++i)
+            count += (lists[l][i].qtype == q && lists[l][i].otype == O_BF16 && lists[l][i].wlayout == wl);
     return count;
 }
 
-bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, int32_t index, bfq_tile* tile_out) {
+bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, bfq_weight_layout w_layout, int32_t index,
+                                  bfq_tile* tile_out) {
     if (!tile_out) return fail(BFQ_ERR_NULL, "tile_out must be non-NULL");
     if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8)
         return fail(BFQ_ERR_DTYPE, "in_dtype must be BFQ_E4M3FN or BFQ_INT8");
-    const int q = qtype_of(in_dtype);
+    if (!wlayout_ok(w_layout)) return fail(BFQ_ERR_ARG, "unknown weight layout");
+    const int q = qtype_of(in_dtype), wl = (int)w_layout;
     int ns[3] = {0, 0, 0}, count = 0;
     const KernelEntry* lists[3] = {std_kernels(&ns[0]), swapab_kernels(&ns[1]), streamk_kernels(&ns[2])};
     for (int l = 0; l < 3; ++l)
         for (int i = 0; i < ns[l]; ++i) {
-            if (lists[l][i].qtype != q || lists[l][i].otype != O_BF16) continue;
+            if (lists[l][i].qtype != q || lists[l][i].otype != O_BF16 || lists[l][i].wlayout != wl)
+                continue;
             if (count == index) { *tile_out = lists[l][i].tile; return BFQ_OK; }
             ++count;
         }

@@ -10,12 +10,16 @@ namespace bfq {
 
 enum QType { Q_FP8 = 0, Q_INT8 = 1 };
 enum OType { O_BF16 = 0, O_FP16 = 1, O_FP32 = 2 };
+enum WLayout { W_ROW = 0, W_PACKED16 = 1 };   // bfq_weight_layout
 
 hipError_t launch_quant_tokens(const void* x, void* q, float* scales, int64_t M, int64_t K,
                                int qtype, int64_t s_stride_m, int64_t s_stride_g, float eps,
                                hipStream_t stream);
 hipError_t launch_quant_weight_blocks(const float* w, void* q, float* scales, int64_t N,
                                       int64_t K, int qtype, float eps, hipStream_t stream);
+// Row-major [N][K] codes -> the packed 16-row fragment layout (BFQ_W_PACKED16).
+hipError_t launch_pack_weights(const void* w, void* packed, int64_t N, int64_t K,
+                               hipStream_t stream);
 hipError_t launch_debug_encode(const float* x, int64_t n, int qtype, void* out,
                                hipStream_t stream);
 
@@ -25,7 +29,7 @@ struct GemmArgs {
     const float* sa;        // activation scales
     int64_t sa_stride_m;    // element stride between tokens
     int64_t sa_stride_k;    // element stride between K blocks
-    const void* w;          // [N][K] codes
+    const void* w;          // N*K codes, row-major or packed (the kernel's layout)
     const float* sw;        // [N/128][K/128]
     void* out;              // [M][N]
     float* partials;        // split-K fp32 partials [split][M][N] (split > 1)
@@ -45,6 +49,7 @@ struct KernelEntry {
     bfq_tile tile;
     int qtype;              // Q_FP8 / Q_INT8
     int otype;              // O_BF16 / O_FP16 / O_FP32 (output of a split=1 launch)
+    int wlayout;            // W_ROW / W_PACKED16: the weight layout the kernel reads
     GemmLaunchFn launch;    // writes `out` (split==1) or `partials` (split>1)
 };
 

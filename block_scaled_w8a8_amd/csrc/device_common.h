@@ -115,6 +115,9 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds_base
         r, (__attribute__((address_space(3))) void*)(lds_base + lds_off), 4, voff, soff, 0, 0);
 }
 
+// Cache-policy operand of the buffer intrinsics: "nt" (non-temporal, streamed once).
+constexpr int kCachePolicyNT = 2;
+
 __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }

@@ -27,6 +27,12 @@
 //  * Workgroup ids are remapped so that each XCD (ids i, i+8, i+16, ...) owns a contiguous
 //    range of tiles, ordered in groups of group_m tile rows, keeping shared A/W panels in
 //    that XCD's L2.
+//  * Weights row-major (W_ROW) or packed (W_PACKED16, see bfq_weight_layout): packed W
+//    arrives as whole 1 KB fragment halves, lands in LDS in lane order and is read back by
+//    each lane at 16*lane (conflict-free without a swizzle). A 16x16x128 MFMA's K order is
+//    free as long as both operands share it, so with packed W the token fragment takes
+//    16-byte chunks (l/16) and (l/16)+4 of its row, the placement the packed weights carry
+//    (the int8 path uses that placement for both layouts).
 #include <type_traits>
 
 #include "bfq_internal.h"
@@ -53,7 +59,7 @@ struct StdShape {
 // K blocks [kb_begin, kb_end) of the output tile at (m0, n0) into acc (zeroed here). Every
 // wave of the workgroup calls it with the same arguments; it leaves no LDS DMA in flight and
 // ends on a barrier, so the next call may reuse the LDS at once.
-template <int BM, int BN, int WM, int WN, int QT, int SCHED, int STAGES>
+template <int BM, int BN, int WM, int WN, int QT, int SCHED, int STAGES, int WL>
 __device__ __forceinline__ void std_tile(
     const GemmArgs& p, uint8_t* lds, int64_t m0, int64_t n0, int64_t kb_begin, int64_t kb_end,
     typename StdShape<BM, BN, WM, WN, SCHED>::AccT (&acc)[StdShape<BM, BN, WM, WN, SCHED>::SM]
@@ -63,8 +69,8 @@ __device__ __forceinline__ void std_tile(
     constexpr int TM = Shape::TM, TN = Shape::TN;
     constexpr int MF = Shape::MF, SM = Shape::SM, SN = Shape::SN;
     using AccT = typename Shape::AccT;
-    static_assert(SCHED != 2 || (QT == Q_FP8 && TM % 32 == 0 && TN % 32 == 0),
-                  "the 32x32 schedule is fp8 only and needs 32-multiple wave tiles");
+    static_assert(SCHED != 2 || (QT == Q_FP8 && WL == W_ROW && TM % 32 == 0 && TN % 32 == 0),
+                  "the 32x32 schedule is fp8 only, row-major W, and needs 32-multiple wave tiles");
     constexpr int STAGE = (BM + BN) * 128;         // bytes per LDS stage
     constexpr int CHUNKS = (BM + BN) / 8;          // 1 KB load chunks per stage
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
@@ -122,6 +128,11 @@ __device__ __forceinline__ void std_tile(
     // offset serves all chunks and the chunk index goes into the scalar offset.
     const uint32_t dma_voff = (uint32_t)(((lane >> 3) + wave * 8) * K +
                                          (((lane & 7) ^ (lane >> 3) ^ (wave & 1)) << 4));
+    // packed W: lane offset within a 1 KB half, bytes between 16-row fragments
+    const uint32_t lane16 = (uint32_t)(lane * 16);
+    const uint32_t frag_stride = (uint32_t)(KB * 2048);
+    (void)lane16;
+    (void)frag_stride;
     auto issue_stage = [&](int64_t kb, int stage) {
         const uint32_t skb = (uint32_t)(kb * 128);
         // scales of block kb: waves 0 .. BM/64-1 fetch 64 activation scales each, wave 0 also
@@ -133,10 +144,17 @@ __device__ __forceinline__ void std_tile(
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const uint32_t lds_off = (uint32_t)((wave + NWAVES * i) * 1024 + stage * STAGE);
-            if (i < CPW_A)
+            if (i < CPW_A) {
                 dma16(ra, lds, lds_off, dma_voff, skb + (uint32_t)(NWAVES * i * 8 * K));
-            else
+            } else if constexpr (WL == W_ROW) {
                 dma16(rw, lds, lds_off, dma_voff, skb + (uint32_t)((NWAVES * i - BM / 8) * 8 * K));
+            } else {
+                // W chunk c of the stage is half (c & 1) of the tile's fragment c >> 1: 1 KB
+                // contiguous at (fragment * KB + kb) * 2048 + half * 1024
+                const uint32_t c = (uint32_t)(wave + NWAVES * i - BM / 8);
+                dma16(rw, lds, lds_off, lane16,
+                      (c >> 1) * frag_stride + (c & 1) * 1024u + (uint32_t)(kb * 2048));
+            }
         }
     };
 
@@ -144,6 +162,7 @@ __device__ __forceinline__ void std_tile(
     // K block kb+2 is touched one block early with a 4-byte DMA into a per-wave scratch slot
     // of LDS, so the next block's tile loads hit L2. Each lane covers one row.
     static_assert(STAGES == 2 || STAGES == 3, "two LDS stages, optionally one L2 stage");
+    static_assert(STAGES == 2 || WL == W_ROW, "the L2 stage touches row-major W lines");
     constexpr int PF_ROUNDS = (BM + BN + 64 * NWAVES - 1) / (64 * NWAVES);
     static_assert(BM % 64 == 0, "prefetch rounds split A and W rows on 64-row boundaries");
     const uint32_t lane_k = (uint32_t)(lane * K);
@@ -169,7 +188,16 @@ __device__ __forceinline__ void std_tile(
     // A sub-tile row sm adds sm*MF*128, a W sub-tile sn adds sn*MF*128 (swz depends on r & 15).
     const int fsw = swz(frow);
     const uint32_t a_row = (uint32_t)((wm * TM + frow) * 128);
-    const uint32_t w_row = (uint32_t)((BM + wn * TN + frow) * 128);
+    // W fragment base of sub-tile 0 (sub-tile sn adds sn*16*128 = sn*2048 in both layouts)
+    const uint32_t w_row = WL == W_ROW ? (uint32_t)((BM + wn * TN + frow) * 128)
+                                       : (uint32_t)((BM + wn * TN) * 128 + lane * 16);
+    // 16-byte K chunks a lane feeds to a 16x16 MFMA: fp8 row-major 2g, 2g+1 (32 contiguous
+    // bytes); fp8 packed and int8 g, g+4. Slot offsets within a row (A; W row-major) and
+    // within a fragment (W packed).
+    const int kc0 = (QT == Q_FP8 && WL == W_ROW) ? 2 * fgrp : fgrp;
+    const int kc1 = (QT == Q_FP8 && WL == W_ROW) ? 2 * fgrp + 1 : fgrp + 4;
+    const uint32_t a_s0 = (uint32_t)((kc0 ^ fsw) << 4), a_s1 = (uint32_t)((kc1 ^ fsw) << 4);
+    const uint32_t w_s0 = WL == W_ROW ? a_s0 : 0u, w_s1 = WL == W_ROW ? a_s1 : 1024u;
 
     auto lds16 = [&](uint32_t off) { return *reinterpret_cast<const v4i*>(lds + off); };
 
@@ -235,14 +263,12 @@ __device__ __forceinline__ void std_tile(
             }
             __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
         } else if constexpr (QT == Q_FP8) {
-            const uint32_t s0 = (uint32_t)(((2 * fgrp) ^ fsw) << 4);
-            const uint32_t s1 = (uint32_t)(((2 * fgrp + 1) ^ fsw) << 4);
             const uint32_t abase = sbase + a_row, wbase = sbase + w_row;
             v8i af[SM];
 #pragma unroll
             for (int sm = 0; sm < SM; ++sm) {
-                const v4i lo = lds16(abase + sm * 2048 + s0);
-                const v4i hi = lds16(abase + sm * 2048 + s1);
+                const v4i lo = lds16(abase + sm * 2048 + a_s0);
+                const v4i hi = lds16(abase + sm * 2048 + a_s1);
                 af[sm] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             }
             auto fma4 = [&](v4f& a, const v4f& q, float cc) {
@@ -252,8 +278,8 @@ __device__ __forceinline__ void std_tile(
                 a.w = __builtin_fmaf(q.w, cc, a.w);
             };
             auto read_w = [&](int sn) {
-                const v4i lo = lds16(wbase + sn * 2048 + s0);
-                const v4i hi = lds16(wbase + sn * 2048 + s1);
+                const v4i lo = lds16(wbase + sn * 2048 + w_s0);
+                const v4i hi = lds16(wbase + sn * 2048 + w_s1);
                 return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             };
             if constexpr (SCHED == 0) {
@@ -291,19 +317,17 @@ __device__ __forceinline__ void std_tile(
                 __builtin_amdgcn_sched_group_barrier(0x002, 4 * SM, 0);
             }
         } else {
-            const uint32_t s0 = (uint32_t)(((fgrp) ^ fsw) << 4);
-            const uint32_t s1 = (uint32_t)(((4 + fgrp) ^ fsw) << 4);
             const uint32_t abase = sbase + a_row, wbase = sbase + w_row;
             v4i af[SM][2];
 #pragma unroll
             for (int sm = 0; sm < SM; ++sm) {
-                af[sm][0] = lds16(abase + sm * 2048 + s0);
-                af[sm][1] = lds16(abase + sm * 2048 + s1);
+                af[sm][0] = lds16(abase + sm * 2048 + a_s0);
+                af[sm][1] = lds16(abase + sm * 2048 + a_s1);
             }
 #pragma unroll
             for (int sn = 0; sn < SN; ++sn) {
-                const v4i w0 = lds16(wbase + sn * 2048 + s0);
-                const v4i w1 = lds16(wbase + sn * 2048 + s1);
+                const v4i w0 = lds16(wbase + sn * 2048 + w_s0);
+                const v4i w1 = lds16(wbase + sn * 2048 + w_s1);
 #pragma unroll
                 for (int sm = 0; sm < SM; ++sm) {
                     v4i pi = mfma_i8_16x16x64(w0, af[sm][0], v4i{0, 0, 0, 0});
@@ -395,7 +419,7 @@ __device__ __forceinline__ void std_store(
 }
 
 // One workgroup per (tile, K split): grid = tiles x 1 x split.
-template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES, int WL>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     using Shape = StdShape<BM, BN, WM, WN, SCHED>;
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -407,7 +431,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
     const int split = p.split, z = blockIdx.z;
     const int64_t kb_begin = (int64_t)z * KB / split, kb_end = (int64_t)(z + 1) * KB / split;
     typename Shape::AccT acc[Shape::SM][Shape::SN];
-    std_tile<BM, BN, WM, WN, QT, SCHED, STAGES>(p, lds, m0, n0, kb_begin, kb_end, acc);
+    std_tile<BM, BN, WM, WN, QT, SCHED, STAGES, WL>(p, lds, m0, n0, kb_begin, kb_end, acc);
     if (split == 1) std_store<OT, BM, BN, WM, WN, SCHED>(p.out, 0, M, N, m0, n0, acc);
     else std_store<O_FP32, BM, BN, WM, WN, SCHED>(p.partials, (int64_t)z * M * N, M, N, m0, n0, acc);
 }
@@ -479,7 +503,7 @@ __device__ __forceinline__ int64_t sk_owner(int64_t x, int64_t G, int64_t I) {
     return ((x + 1) * G + I - 1) / I - 1;
 }
 
-template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES, int WL>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_streamk_kernel(GemmArgs p) {
     using Shape = StdShape<BM, BN, WM, WN, SCHED>;
     using IO = SlotIO<BM, BN, WM, WN, SCHED>;
@@ -516,7 +540,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_streamk_kernel(GemmArgs p) 
         const int64_t m0 = uniform_i64(pm * BM), n0 = uniform_i64(pn * BN);
         k0 = uniform_i64(k0);
         k1 = uniform_i64(k1);
-        std_tile<BM, BN, WM, WN, QT, SCHED, STAGES>(p, lds, m0, n0, k0, k1, acc);
+        std_tile<BM, BN, WM, WN, QT, SCHED, STAGES, WL>(p, lds, m0, n0, k0, k1, acc);
         if (k0 == 0 && k1 == KB) std_store<OT, BM, BN, WM, WN, SCHED>(p.out, 0, M, N, m0, n0, acc);
         else IO::park(p.sk_slots, w * 2 + (ts == it_lo / KB ? 0 : 1), acc);
     }
@@ -571,7 +595,7 @@ int streamk_grid() {
     return cached[dev];
 }
 
-template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES, int WL>
 hipError_t launch_streamk(const GemmArgs& a, hipStream_t stream) {
     constexpr int LDS_BYTES = StdShape<BM, BN, WM, WN, SCHED>::lds_bytes(STAGES);
     const int G = streamk_grid();
@@ -584,12 +608,12 @@ hipError_t launch_streamk(const GemmArgs& a, hipStream_t stream) {
     static bool attr_set = false;   // one-time opt-in to more than 64 KB of LDS
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&gemm_streamk_kernel<BM, BN, WM, WN, QT, OT, SCHED, STAGES>),
+            reinterpret_cast<const void*>(&gemm_streamk_kernel<BM, BN, WM, WN, QT, OT, SCHED, STAGES, WL>),
             hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((gemm_streamk_kernel<BM, BN, WM, WN, QT, OT, SCHED, STAGES>),
+    hipLaunchKernelGGL((gemm_streamk_kernel<BM, BN, WM, WN, QT, OT, SCHED, STAGES, WL>),
                        dim3((unsigned)grid), dim3(64 * WM * WN), LDS_BYTES, stream, b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || tiles == b.dp_tiles) return e;
@@ -598,7 +622,7 @@ hipError_t launch_streamk(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES>
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES, int WL>
 hipError_t launch_std(const GemmArgs& a, hipStream_t stream) {
     constexpr int LDS_BYTES = StdShape<BM, BN, WM, WN, SCHED>::lds_bytes(STAGES);
     const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
@@ -606,54 +630,65 @@ hipError_t launch_std(const GemmArgs& a, hipStream_t stream) {
     static bool attr_set = false;   // one-time opt-in to more than 64 KB of LDS
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&gemm_std_kernel<BM, BN, WM, WN, QT, OT, SCHED, STAGES>),
+            reinterpret_cast<const void*>(&gemm_std_kernel<BM, BN, WM, WN, QT, OT, SCHED, STAGES, WL>),
             hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((gemm_std_kernel<BM, BN, WM, WN, QT, OT, SCHED, STAGES>), grid,
+    hipLaunchKernelGGL((gemm_std_kernel<BM, BN, WM, WN, QT, OT, SCHED, STAGES, WL>), grid,
                        dim3(64 * WM * WN), LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 
-#define BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, OT)                                    \
-    KernelEntry{bfq_tile{0, BM, BN, 128, 1, WM, WN, ST, 8, SC, 0, 0}, QT, OT,             \
-                &launch_std<BM, BN, WM, WN, QT, OT, SC, ST>}
+#define BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, OT, WL)                                \
+    KernelEntry{bfq_tile{0, BM, BN, 128, 1, WM, WN, ST, 8, SC, 0, 0}, QT, OT, WL,         \
+                &launch_std<BM, BN, WM, WN, QT, OT, SC, ST, WL>}
 
-#define BFQ_STD_ALL_OUT(BM, BN, WM, WN, ST, SC, QT)                                       \
-    BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_BF16),                                    \
-        BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_FP16),                                \
-        BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_FP32)
+#define BFQ_STD_ALL_OUT(BM, BN, WM, WN, ST, SC, QT, WL)                                   \
+    BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_BF16, WL),                                \
+        BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_FP16, WL),                            \
+        BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_FP32, WL)
 
 static const KernelEntry kStdKernels[] = {
-    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8),
-    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8),
-    BFQ_STD_ALL_OUT(256, 256, 4, 2, 3, 1, Q_FP8),
-    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 2, Q_FP8),
-    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 2, Q_FP8),
-    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 0, Q_FP8),
-    BFQ_STD_ALL_OUT(128, 256, 2, 2, 3, 1, Q_FP8),
-    BFQ_STD_ALL_OUT(256, 128, 4, 1, 3, 1, Q_FP8),
-    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 0, Q_FP8),
-    BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 0, Q_FP8),
-    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_INT8),
-    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 0, Q_INT8),
-    BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 0, Q_INT8),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 3, 1, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 2, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 2, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 0, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 3, 1, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(256, 128, 4, 1, 3, 1, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 0, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 0, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_INT8, W_ROW),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 0, Q_INT8, W_ROW),
+    BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 0, Q_INT8, W_ROW),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 0, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 0, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 0, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_INT8, W_PACKED16),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 0, Q_INT8, W_PACKED16),
+    BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 0, Q_INT8, W_PACKED16),
 };
 
-#define BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, OT)                                     \
-    KernelEntry{bfq_tile{2, BM, BN, 128, 1, WM, WN, ST, 8, SC, 0, 0}, QT, OT,             \
-                &launch_streamk<BM, BN, WM, WN, QT, OT, SC, ST>}
+#define BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, OT, WL)                                 \
+    KernelEntry{bfq_tile{2, BM, BN, 128, 1, WM, WN, ST, 8, SC, 0, 0}, QT, OT, WL,         \
+                &launch_streamk<BM, BN, WM, WN, QT, OT, SC, ST, WL>}
 
-#define BFQ_SK_ALL_OUT(BM, BN, WM, WN, ST, SC, QT)                                        \
-    BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_BF16),                                     \
-        BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_FP16),                                 \
-        BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_FP32)
+#define BFQ_SK_ALL_OUT(BM, BN, WM, WN, ST, SC, QT, WL)                                    \
+    BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_BF16, WL),                                 \
+        BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_FP16, WL),                             \
+        BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_FP32, WL)
 
 static const KernelEntry kStreamKKernels[] = {
-    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8),
-    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8),
-    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 0, Q_INT8),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8, W_ROW),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8, W_ROW),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 0, Q_INT8, W_ROW),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8, W_PACKED16),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8, W_PACKED16),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 0, Q_INT8, W_PACKED16),
 };
 
 const KernelEntry* streamk_kernels(int* count) {

@@ -17,68 +17,100 @@
 // MFMA operand, so the result tile is W*A^T: each lane holds one token and four
 // consecutive weight rows, stored back row-major into C. Lane l loads 16-byte chunks
 // (l/16) and (l/16)+4 of its row, so each load instruction covers 64 contiguous bytes of
-// 16 rows. Split-K writes fp32 partials that a second kernel sums in a fixed order.
+// 16 rows. With packed weights (W_PACKED16) the same two fragment halves are 1 KB of
+// contiguous memory each, which is what lets the weight stream approach the HBM peak.
+// A workgroup holds NWAVES strips of NWR rows, and KW waves per strip share its K range:
+// wave wk streams the wk-th contiguous slice of the strip's K blocks, and the KW partial
+// tiles are summed through LDS in ascending wk (deterministic) before one wave stores the
+// strip. That gives a weight matrix of few strips (N / 16 = 1536 at N = 24576) enough waves
+// to keep HBM busy without a second kernel. Split-K across workgroups writes fp32 partials
+// that a second kernel sums in a fixed order.
 #include "bfq_internal.h"
 #include "device_common.h"
 
 namespace bfq {
 
-template <int MT, int NWR, int NWAVES, int D, int QT, int OT>
-__global__ __launch_bounds__(64 * NWAVES) void gemm_swapab_kernel(GemmArgs p) {
+template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL>
+__global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs p) {
     constexpr int SM = MT / 16, SN = NWR / 16;
     static_assert(MT % 16 == 0 && NWR % 16 == 0, "tiles are multiples of 16");
     static_assert(128 % NWR == 0, "a wave's rows must lie in one 128-row scale block");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int wn = wave % NWAVES, wk = wave / NWAVES;   // strip, K slice
     const int frow = lane & 15, fgrp = lane >> 4;
 
     const int64_t M = p.M, N = p.N, K = p.K, KB = K / 128;
-    const int64_t n0 = ((int64_t)blockIdx.x * NWAVES + wave) * NWR;
+    const int64_t n0 = ((int64_t)blockIdx.x * NWAVES + wn) * NWR;
     const int64_t m0 = (int64_t)blockIdx.y * MT;
     const int split = p.split, z = blockIdx.z;
-    const int64_t kb_begin = (int64_t)z * KB / split, kb_end = (int64_t)(z + 1) * KB / split;
+    const int64_t ks0 = (int64_t)z * KB / split, ks1 = (int64_t)(z + 1) * KB / split;
+    const int64_t kb_begin = ks0 + (ks1 - ks0) * wk / KW, kb_end = ks0 + (ks1 - ks0) * (wk + 1) / KW;
     const bool wave_live = n0 < N;   // whole-wave predicate (N is a multiple of 16)
 
-    const uint8_t* W = static_cast<const uint8_t*>(p.w);
-    const uint8_t* A = static_cast<const uint8_t*>(p.a);
-
-    const uint8_t* wrow[SN];
+    // Loads go through buffer resources: a scalar base per stream, a 32-bit per-lane offset
+    // fixed for the whole K loop and the K block in the scalar offset. Rows past M read as
+    // zero (past the resource), and a refill past this wave's slice uses an offset past every
+    // resource, so it returns zero without touching memory.
+    constexpr uint32_t KSTEP = WL == W_ROW ? 128u : 2048u;   // bytes between K blocks
+    constexpr uint32_t HOFF = WL == W_ROW ? 64u : 1024u;     // second half of a fragment
+    constexpr uint32_t kNoLoad = 0x80000000u;                 // past every resource here
+    const int64_t nb0 = wave_live ? n0 : 0;
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(static_cast<const uint8_t*>(p.w) + nb0 * K, (uint32_t)(NWR * K));
+    uint32_t w_voff[SN], w_sn[SN];
 #pragma unroll
     for (int sn = 0; sn < SN; ++sn) {
-        int64_t n = n0 + sn * 16 + frow;
-        n = n < N ? n : N - 1;
-        wrow[sn] = W + n * K + fgrp * 16;
+        if constexpr (WL == W_ROW) {
+            w_voff[sn] = (uint32_t)((sn * 16 + frow) * K + fgrp * 16);
+            w_sn[sn] = 0;
+        } else {
+            w_voff[sn] = (uint32_t)(lane * 16);
+            w_sn[sn] = (uint32_t)(sn * KB * 2048);
+        }
     }
-    const uint8_t* arow[SM];
-    const float* sa_ptr[SM];
+    const int64_t rows_a = (M - m0) < MT ? (M - m0) : MT;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(static_cast<const uint8_t*>(p.a) + m0 * K, (uint32_t)(rows_a * K));
+    const int64_t ssm = p.sa_stride_m, ssk = p.sa_stride_k;
+    const __amdgpu_buffer_rsrc_t rsa =
+        make_rsrc(p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + (KB - 1) * ssk + 1) * 4));
+    uint32_t a_voff[SM], sa_voff[SM];
 #pragma unroll
     for (int sm = 0; sm < SM; ++sm) {
-        int64_t m = m0 + sm * 16 + frow;
-        m = m < M ? m : M - 1;
-        arow[sm] = A + m * K + fgrp * 16;
-        sa_ptr[sm] = p.sa + m * p.sa_stride_m;
+        a_voff[sm] = (uint32_t)((sm * 16 + frow) * K + fgrp * 16);
+        sa_voff[sm] = (uint32_t)((sm * 16 + frow) * ssm * 4);
     }
-    const float* sw_row = p.sw + ((wave_live ? n0 : 0) / 128) * KB;
+    const float* sw_row = p.sw + (nb0 / 128) * KB;
+    const int64_t L = kb_end - kb_begin;
+    const int64_t kb_hi = L > 0 ? kb_end - 1 : kb_begin < KB ? kb_begin : KB - 1;
 
     v4i wbuf[D][SN][2];
     v4i abuf[D][SM][2];
     float sab[D][SM];
     float swb[D];
 
-    auto fetch = [&](int slot, int64_t kb) {
+    // the loads of step i (K block kb_begin + i) into ring slot `slot`
+    auto fetch = [&](int slot, int64_t i) {
+        const bool live = i < L;
+        const int64_t kb = live ? kb_begin + i : kb_hi;
+        const uint32_t ws = live ? (uint32_t)kb * KSTEP : kNoLoad;
+        const uint32_t as = live ? (uint32_t)kb * 128u : kNoLoad;
+        const uint32_t ss = live ? (uint32_t)(kb * ssk * 4) : kNoLoad;
         swb[slot] = sw_row[kb];
 #pragma unroll
-        for (int sm = 0; sm < SM; ++sm) sab[slot][sm] = sa_ptr[sm][kb * p.sa_stride_k];
+        for (int sm = 0; sm < SM; ++sm) sab[slot][sm] = buf_f32(rsa, sa_voff[sm], ss);
 #pragma unroll
         for (int sn = 0; sn < SN; ++sn) {
-            wbuf[slot][sn][0] = *reinterpret_cast<const v4i*>(wrow[sn] + kb * 128);
-            wbuf[slot][sn][1] = *reinterpret_cast<const v4i*>(wrow[sn] + kb * 128 + 64);
+            // streamed once: non-temporal, so the weight stream does not evict the tokens
+            wbuf[slot][sn][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff[sn], w_sn[sn] + ws, kCachePolicyNT);
+            wbuf[slot][sn][1] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff[sn], w_sn[sn] + ws + HOFF, kCachePolicyNT);
         }
 #pragma unroll
         for (int sm = 0; sm < SM; ++sm) {
-            abuf[slot][sm][0] = *reinterpret_cast<const v4i*>(arow[sm] + kb * 128);
-            abuf[slot][sm][1] = *reinterpret_cast<const v4i*>(arow[sm] + kb * 128 + 64);
+            abuf[slot][sm][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_voff[sm], as, 0);
+            abuf[slot][sm][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_voff[sm], as + 64u, 0);
         }
     };
 
@@ -116,33 +148,51 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_swapab_kernel(GemmArgs p) {
         }
     };
 
-    if (wave_live && kb_begin < kb_end) {
-        // Ring of D K-blocks in flight. The steady-state loop is branch-free: a refill past
-        // the end of this split re-reads its last block (never used), so the compiler can
-        // count outstanding loads exactly instead of draining the queue at every join.
-        const int64_t kb_last = kb_end - 1;
+    if (wave_live && L > 0) {
+        // Ring of D K blocks in flight. The steady-state loop is branch-free: a refill past the
+        // end of the slice re-reads its last block (never used). (Measured: a single loop with
+        // predicated steps instead is ~5 % slower on the short slices of an in-workgroup split.)
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
-            const int64_t kb = kb_begin + i;
-            fetch(i, kb < kb_last ? kb : kb_last);
-        }
-        int64_t kb0 = kb_begin;
-        for (; kb0 + D <= kb_end; kb0 += D) {
+        for (int i = 0; i < D; ++i) fetch(i, i < L ? i : L - 1);
+        int64_t i0 = 0;
+        for (; i0 + D <= L; i0 += D) {
 #pragma unroll
-            for (int i = 0; i < D; ++i) {
+            for (int r = 0; r < D; ++r) {
                 // keep each slot's work in its own stage: the scheduler must not hoist the
                 // scale products of later slots (that would wait for every load in flight)
                 __builtin_amdgcn_sched_barrier(0);
-                consume(i);
-                const int64_t nk = kb0 + i + D;
-                fetch(i, nk < kb_last ? nk : kb_last);
+                consume(r);
+                const int64_t ni = i0 + r + D;
+                fetch(r, ni < L ? ni : L - 1);
             }
         }
-        const int rem = (int)(kb_end - kb0);
+        const int rem = (int)(L - i0);
 #pragma unroll
-        for (int i = 0; i < D; ++i)
-            if (i < rem) consume(i);
+        for (int r = 0; r < D; ++r)
+            if (r < rem) consume(r);
+    }
 
+    if constexpr (KW > 1) {
+        // strip partials of K slices 1..KW-1 go through LDS; slice 0's wave adds them in order
+        __shared__ v4f red[KW - 1][NWAVES][SM * SN][64];
+        if (wk > 0) {
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+                for (int sn = 0; sn < SN; ++sn) red[wk - 1][wn][sm * SN + sn][lane] = acc[sm][sn];
+        }
+        __syncthreads();
+        if (wk == 0) {
+#pragma unroll
+            for (int j = 0; j < KW - 1; ++j)
+#pragma unroll
+                for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+                    for (int sn = 0; sn < SN; ++sn) acc[sm][sn] += red[j][wn][sm * SN + sn][lane];
+        }
+    }
+
+    if (wk == 0 && wave_live) {
 #pragma unroll
         for (int sm = 0; sm < SM; ++sm) {
             const int64_t m = m0 + sm * 16 + frow;
@@ -157,34 +207,307 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_swapab_kernel(GemmArgs p) {
     }
 }
 
-template <int MT, int NWR, int NWAVES, int D, int QT, int OT>
+// Swap-AB with the token fragments shared through LDS (sched 1). The waves of a workgroup
+// that work on the same K slice (the NWAVES strips of one wk group) need the same token
+// fragments, so instead of every wave fetching them from L2 (MT/NWR times the bytes of its
+// weight stream), each K block's MT x 128 token bytes are fetched once per wk group: the 2*SM
+// fragment halves of 1 KB are dealt over the group's waves, and the token scales go to the
+// group's last wave. Those loads travel in the same D-deep register ring as the weights (so
+// the in-order completion of vector loads never shortens the weight prefetch distance); at
+// step i they are written to LDS buffer i & 1, one barrier later every wave reads them back
+// in lane order (conflict-free) for its MFMAs. Buffer i & 1 was last read at step i - 2, before
+// the previous step's barrier. Every wave runs the same number of steps (the longest K slice
+// of the workgroup) so the barriers match; a wave with a shorter slice idles on its last one.
+template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL>
+__global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmArgs p) {
+    constexpr int SM = MT / 16, SN = NWR / 16;
+    constexpr int AI = 2 * SM;                              // 1 KB token halves per K block
+    constexpr int API = (AI + NWAVES - 1) / NWAVES;         // at most this many per wave
+    constexpr int SLOT = MT * 128 + MT * 4;                 // token codes + token scales
+    constexpr int SCW = (MT + 63) / 64;                     // token scales per lane of the scale wave
+    static_assert(MT % 16 == 0 && NWR % 16 == 0 && MT <= 128, "tiles are multiples of 16, MT <= 128");
+    static_assert(128 % NWR == 0, "a wave's rows must lie in one 128-row scale block");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave % NWAVES, wk = wave / NWAVES;
+    const int frow = lane & 15, fgrp = lane >> 4;
+
+    const int64_t M = p.M, N = p.N, K = p.K, KB = K / 128;
+    const int64_t n0 = ((int64_t)blockIdx.x * NWAVES + wn) * NWR;
+    const int64_t m0 = (int64_t)blockIdx.y * MT;
+    const int split = p.split, z = blockIdx.z;
+    const int64_t ks0 = (int64_t)z * KB / split, ks1 = (int64_t)(z + 1) * KB / split;
+    const int64_t len = ks1 - ks0;                          // >= 1 (split <= K/128)
+    const int64_t kb_begin = ks0 + len * wk / KW, kb_end = ks0 + len * (wk + 1) / KW;
+    const int64_t L = kb_end - kb_begin, Lmax = (len + KW - 1) / KW;
+    const int64_t kb_hi = L > 0 ? kb_end - 1 : ks0;        // weight-scale index past the slice
+    const bool wave_live = n0 < N;
+
+    // Loads go through buffer resources: one scalar base per stream, a 32-bit per-lane offset
+    // that is the same for every K block, and the K block in the scalar offset, so the ring
+    // costs only its data registers. Rows past M (N) lie past the resource and read as zero.
+    constexpr uint32_t KSTEP = WL == W_ROW ? 128u : 2048u;   // bytes between K blocks
+    constexpr uint32_t HOFF = WL == W_ROW ? 64u : 1024u;     // second half of a fragment
+    const int64_t nb0 = wave_live ? n0 : 0;
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(static_cast<const uint8_t*>(p.w) + nb0 * K, (uint32_t)(NWR * K));
+    // weight sub-tile sn: per-lane offset and the scalar offset of K block 0
+    uint32_t w_voff[SN];
+    uint32_t w_sn[SN];
+#pragma unroll
+    for (int sn = 0; sn < SN; ++sn) {
+        if constexpr (WL == W_ROW) {
+            w_voff[sn] = (uint32_t)((sn * 16 + frow) * K + fgrp * 16);
+            w_sn[sn] = 0;
+        } else {
+            w_voff[sn] = (uint32_t)(lane * 16);
+            w_sn[sn] = (uint32_t)(sn * KB * 2048);
+        }
+    }
+    const int64_t rows_a = (M - m0) < MT ? (M - m0) : MT;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(static_cast<const uint8_t*>(p.a) + m0 * K, (uint32_t)(rows_a * K));
+    // Every wave issues the same loads every step, so the compiler's count of loads in flight
+    // is exact and each wait lets the whole ring stay outstanding; loads a wave does not need
+    // use an offset past the resource (they return zero without a memory access).
+    constexpr uint32_t kNoLoad = 0x80000000u;   // past every resource here (all < 2^31 bytes)
+    // token halves this wave fetches: j = wn + NWAVES * t (sub-tile j >> 1, K half j & 1)
+    uint32_t a_voff[API];
+#pragma unroll
+    for (int t = 0; t < API; ++t) {
+        const int j = wn + NWAVES * t;
+        a_voff[t] = j < AI ? (uint32_t)((((j >> 1) * 16 + frow) * K) + 64 * (j & 1) + 16 * fgrp)
+                           : kNoLoad;
+    }
+    // token scales (last wave of the group): scale slot x = r * SM + s holds token s * 16 + r,
+    // so each lane later reads its SM scales as one contiguous run; lane l fills slots l + 64q
+    const bool scale_wave = wn == NWAVES - 1;
+    const int64_t ssm = p.sa_stride_m, ssk = p.sa_stride_k;
+    const __amdgpu_buffer_rsrc_t rsa =
+        make_rsrc(p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + (KB - 1) * ssk + 1) * 4));
+    uint32_t sa_voff[SCW];
+#pragma unroll
+    for (int q = 0; q < SCW; ++q) {
+        const int x = lane + 64 * q;
+        sa_voff[q] = scale_wave ? (uint32_t)(((x % SM) * 16 + x / SM) * ssm * 4) : kNoLoad;
+    }
+    const float* sw_row = p.sw + (nb0 / 128) * KB;
+
+    __shared__ __attribute__((aligned(16))) uint8_t tok[KW][2][SLOT];
+
+    v4i wbuf[D][SN][2];
+    v4i abuf[D][API];
+    float sab[D][SCW];
+    float swb[D];
+
+    // the loads of step i (K block kb_begin + i) into ring slot `slot`; a step past this
+    // wave's slice loads nothing (offsets past the resources)
+    auto fetch = [&](int slot, int64_t i) {
+        const bool live = i < L;
+        const int64_t kb = live ? kb_begin + i : kb_hi;
+        const uint32_t ws = live ? (uint32_t)kb * KSTEP : kNoLoad;
+        const uint32_t as = live ? (uint32_t)kb * 128u : kNoLoad;
+        const uint32_t ss = live ? (uint32_t)(kb * ssk * 4) : kNoLoad;
+        swb[slot] = sw_row[kb];
+#pragma unroll
+        for (int q = 0; q < SCW; ++q) sab[slot][q] = buf_f32(rsa, sa_voff[q], ss);
+#pragma unroll
+        for (int sn = 0; sn < SN; ++sn) {
+            // streamed once: non-temporal, so the weight stream does not evict the tokens
+            wbuf[slot][sn][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff[sn], w_sn[sn] + ws, kCachePolicyNT);
+            wbuf[slot][sn][1] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff[sn], w_sn[sn] + ws + HOFF, kCachePolicyNT);
+        }
+#pragma unroll
+        for (int t = 0; t < API; ++t)
+            abuf[slot][t] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_voff[t], as, 0);
+    };
+
+    v4f acc[SM][SN];
+#pragma unroll
+    for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+        for (int sn = 0; sn < SN; ++sn) acc[sm][sn] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // step i: publish ring slot r's token data in buffer i & 1, barrier, then (if this wave's
+    // slice has a block i) the MFMAs and scale FMAs of block kb_begin + i
+    auto step = [&](int r, int64_t i) {
+        uint8_t* buf = tok[wk][i & 1];
+#pragma unroll
+        for (int t = 0; t < API; ++t) {
+            const int j = wn + NWAVES * t;
+            if (j < AI) *reinterpret_cast<v4i*>(buf + j * 1024 + lane * 16) = abuf[r][t];
+        }
+        if (scale_wave) {
+#pragma unroll
+            for (int q = 0; q < SCW; ++q)
+                if (lane + 64 * q < MT)
+                    *reinterpret_cast<float*>(buf + MT * 128 + (lane + 64 * q) * 4) = sab[r][q];
+        }
+        __syncthreads();
+        if (i < L && wave_live) {
+            float c[SM];
+            const float* sp = reinterpret_cast<const float*>(buf + MT * 128) + frow * SM;
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm) c[sm] = sp[sm] * swb[r];
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm) {
+                const v4i a0 = *reinterpret_cast<const v4i*>(buf + (2 * sm) * 1024 + lane * 16);
+                const v4i a1 = *reinterpret_cast<const v4i*>(buf + (2 * sm + 1) * 1024 + lane * 16);
+#pragma unroll
+                for (int sn = 0; sn < SN; ++sn) {
+                    v4f pb;
+                    if constexpr (QT == Q_FP8) {
+                        const v4i* w2 = wbuf[r][sn];
+                        const v8i wf = v8i{w2[0].x, w2[0].y, w2[0].z, w2[0].w,
+                                           w2[1].x, w2[1].y, w2[1].z, w2[1].w};
+                        const v8i af = v8i{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                        pb = mfma_fp8_16x16x128(wf, af);
+                    } else {
+                        v4i pi = mfma_i8_16x16x64(wbuf[r][sn][0], a0, v4i{0, 0, 0, 0});
+                        pi = mfma_i8_16x16x64(wbuf[r][sn][1], a1, pi);
+                        pb = v4f{(float)pi.x, (float)pi.y, (float)pi.z, (float)pi.w};
+                    }
+                    acc[sm][sn].x = __builtin_fmaf(pb.x, c[sm], acc[sm][sn].x);
+                    acc[sm][sn].y = __builtin_fmaf(pb.y, c[sm], acc[sm][sn].y);
+                    acc[sm][sn].z = __builtin_fmaf(pb.z, c[sm], acc[sm][sn].z);
+                    acc[sm][sn].w = __builtin_fmaf(pb.w, c[sm], acc[sm][sn].w);
+                }
+            }
+        }
+    };
+
+    // the ring: steps 0 .. D-1 in flight before the loop; step i refills its slot for i + D.
+    // One loop for every step (Lmax >= 1): the prologue's loads flow into it on its only
+    // entry path, so no register copies wait for them.
+#pragma unroll
+    for (int i = 0; i < D; ++i) fetch(i, i);
+    int64_t i0 = 0;
+    do {
+#pragma unroll
+        for (int r = 0; r < D; ++r) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (i0 + r < Lmax) step(r, i0 + r);      // uniform over the workgroup
+            fetch(r, i0 + r + D);
+        }
+        i0 += D;
+    } while (i0 < Lmax);
+
+    if constexpr (KW > 1) {
+        __shared__ v4f red[KW - 1][NWAVES][SM * SN][64];
+        if (wk > 0) {
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+                for (int sn = 0; sn < SN; ++sn) red[wk - 1][wn][sm * SN + sn][lane] = acc[sm][sn];
+        }
+        __syncthreads();
+        if (wk == 0) {
+#pragma unroll
+            for (int j = 0; j < KW - 1; ++j)
+#pragma unroll
+                for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+                    for (int sn = 0; sn < SN; ++sn) acc[sm][sn] += red[j][wn][sm * SN + sn][lane];
+        }
+    }
+
+    if (wk == 0 && wave_live) {
+#pragma unroll
+        for (int sm = 0; sm < SM; ++sm) {
+            const int64_t m = m0 + sm * 16 + frow;
+            if (m >= M) continue;
+#pragma unroll
+            for (int sn = 0; sn < SN; ++sn) {
+                const int64_t n = n0 + sn * 16 + 4 * fgrp;
+                if (split == 1) store4<OT>(p.out, m * N + n, acc[sm][sn]);
+                else store4<O_FP32>(p.partials, ((int64_t)z * M + m) * N + n, acc[sm][sn]);
+            }
+        }
+    }
+}
+
+template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL>
 hipError_t launch_swapab(const GemmArgs& a, hipStream_t stream) {
     const int64_t strips = (a.N + NWR * NWAVES - 1) / (NWR * NWAVES);
     dim3 grid((unsigned)strips, (unsigned)((a.M + MT - 1) / MT), (unsigned)a.split);
-    hipLaunchKernelGGL((gemm_swapab_kernel<MT, NWR, NWAVES, D, QT, OT>), grid,
-                       dim3(64 * NWAVES), 0, stream, a);
+    hipLaunchKernelGGL((gemm_swapab_kernel<MT, NWR, NWAVES, KW, D, QT, OT, WL>), grid,
+                       dim3(64 * NWAVES * KW), 0, stream, a);
     return hipGetLastError();
 }
 
-#define BFQ_SAB_ENTRY(MT, NWR, NW, D, QT, OT)                                              \
-    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, 1, NW, D, 1, 0, 0, 0}, QT, OT,          \
-                &launch_swapab<MT, NWR, NW, D, QT, OT>}
-#define BFQ_SAB_ALL_OUT(MT, NWR, NW, D, QT)                                                \
-    BFQ_SAB_ENTRY(MT, NWR, NW, D, QT, O_BF16), BFQ_SAB_ENTRY(MT, NWR, NW, D, QT, O_FP16),   \
-        BFQ_SAB_ENTRY(MT, NWR, NW, D, QT, O_FP32)
+template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL>
+hipError_t launch_swapab_lds(const GemmArgs& a, hipStream_t stream) {
+    const int64_t strips = (a.N + NWR * NWAVES - 1) / (NWR * NWAVES);
+    dim3 grid((unsigned)strips, (unsigned)((a.M + MT - 1) / MT), (unsigned)a.split);
+    hipLaunchKernelGGL((gemm_swapab_lds_kernel<MT, NWR, NWAVES, KW, D, QT, OT, WL>), grid,
+                       dim3(64 * NWAVES * KW), 0, stream, a);
+    return hipGetLastError();
+}
+
+// bfq_tile for variant 1: bm = MT tokens, bn = NWR * NW rows per workgroup, waves_m = KW
+// waves sharing each strip's K range, waves_n = NW strips, stages = D K blocks in flight,
+// sched 0 = tokens per wave from L2, sched 1 = tokens shared through LDS.
+#define BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, OT, WL)                                      \
+    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 0, 0, 0}, QT, OT, WL,     \
+                &launch_swapab<MT, NWR, NW, KW, D, QT, OT, WL>}
+#define BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, WL)                                        \
+    BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, O_BF16, WL),                                     \
+        BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, O_FP16, WL),                                 \
+        BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, O_FP32, WL)
+#define BFQ_SAB_BOTH(MT, NWR, NW, KW, D, QT)                                                \
+    BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW), BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16)
+
+#define BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, OT, WL)                                     \
+    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 1, 0, 0}, QT, OT, WL,     \
+                &launch_swapab_lds<MT, NWR, NW, KW, D, QT, OT, WL>}
+#define BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, WL)                                       \
+    BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, O_BF16, WL),                                    \
+        BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, O_FP16, WL),                                \
+        BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, O_FP32, WL)
+#define BFQ_SABL_BOTH(MT, NWR, NW, KW, D, QT)                                               \
+    BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW), BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16)
 
 static const KernelEntry kSwapabKernels[] = {
-    BFQ_SAB_ALL_OUT(16, 32, 4, 4, Q_FP8),
-    BFQ_SAB_ALL_OUT(16, 16, 4, 8, Q_FP8),
-    BFQ_SAB_ALL_OUT(16, 16, 8, 8, Q_FP8),
-    BFQ_SAB_ALL_OUT(16, 32, 8, 4, Q_FP8),
-    BFQ_SAB_ALL_OUT(16, 64, 4, 2, Q_FP8),
-    BFQ_SAB_ALL_OUT(16, 32, 4, 8, Q_FP8),
-    BFQ_SAB_ALL_OUT(32, 32, 4, 4, Q_FP8),
-    BFQ_SAB_ALL_OUT(64, 32, 4, 2, Q_FP8),
-    BFQ_SAB_ALL_OUT(16, 32, 4, 4, Q_INT8),
-    BFQ_SAB_ALL_OUT(32, 32, 4, 4, Q_INT8),
-    BFQ_SAB_ALL_OUT(64, 32, 4, 2, Q_INT8),
+    BFQ_SABL_BOTH(16, 16, 8, 1, 8, Q_FP8),
+    BFQ_SABL_BOTH(16, 16, 4, 2, 8, Q_FP8),
+    BFQ_SABL_BOTH(32, 16, 8, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(32, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(32, 16, 4, 2, 4, Q_FP8),
+    BFQ_SABL_BOTH(64, 16, 8, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(64, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(64, 16, 4, 2, 4, Q_FP8),
+    BFQ_SABL_BOTH(64, 32, 4, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(96, 16, 8, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(96, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(128, 16, 8, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(128, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(16, 16, 8, 1, 8, Q_INT8),
+    BFQ_SABL_BOTH(32, 16, 8, 1, 4, Q_INT8),
+    BFQ_SABL_BOTH(64, 16, 8, 1, 4, Q_INT8),
+    BFQ_SABL_BOTH(128, 16, 8, 1, 4, Q_INT8),
+    BFQ_SAB_BOTH(16, 32, 4, 1, 4, Q_FP8),
+    BFQ_SAB_BOTH(16, 16, 4, 1, 8, Q_FP8),
+    BFQ_SAB_BOTH(16, 16, 8, 1, 8, Q_FP8),
+    BFQ_SAB_BOTH(16, 32, 8, 1, 4, Q_FP8),
+    BFQ_SAB_BOTH(16, 64, 4, 1, 2, Q_FP8),
+    BFQ_SAB_BOTH(16, 32, 4, 1, 8, Q_FP8),
+    BFQ_SAB_BOTH(32, 32, 4, 1, 4, Q_FP8),
+    BFQ_SAB_BOTH(64, 32, 4, 1, 2, Q_FP8),
+    BFQ_SAB_BOTH(16, 16, 1, 4, 4, Q_FP8),
+    BFQ_SAB_BOTH(16, 16, 1, 4, 8, Q_FP8),
+    BFQ_SAB_BOTH(16, 16, 2, 2, 8, Q_FP8),
+    BFQ_SAB_BOTH(16, 16, 1, 8, 4, Q_FP8),
+    BFQ_SAB_BOTH(16, 32, 1, 4, 4, Q_FP8),
+    BFQ_SAB_BOTH(32, 16, 1, 4, 4, Q_FP8),
+    BFQ_SAB_BOTH(64, 16, 1, 4, 2, Q_FP8),
+    BFQ_SAB_BOTH(32, 32, 1, 4, 4, Q_FP8),
+    BFQ_SAB_BOTH(16, 32, 4, 1, 4, Q_INT8),
+    BFQ_SAB_BOTH(32, 32, 4, 1, 4, Q_INT8),
+    BFQ_SAB_BOTH(64, 32, 4, 1, 2, Q_INT8),
+    BFQ_SAB_BOTH(16, 16, 1, 4, 4, Q_INT8),
+    BFQ_SAB_BOTH(32, 16, 1, 4, 4, Q_INT8),
+    BFQ_SAB_BOTH(64, 16, 1, 4, 2, Q_INT8),
 };
 
 const KernelEntry* swapab_kernels(int* count) {

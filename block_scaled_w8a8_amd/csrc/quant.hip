@@ -1,6 +1,7 @@
 // Quantization kernels for gfx950: per-token-group activation quantization (bf16 -> e4m3fn
 // or int8 codes + one fp32 scale per 1x128 group), per-128x128-block weight quantization
-// (fp32 -> codes + one fp32 scale per block), and the element-encoder probe used by tests.
+// (fp32 -> codes + one fp32 scale per block), the weight-code packing into the 16-row
+// fragment layout, and the element-encoder probe used by tests.
 //
 // Pages cited by title and section:
 //   [BENCH] "vLLM DeepGEMM FP8 Block GEMM 基准测试 ..." §4.1 (per_token_group_quant_fp8,
@@ -189,6 +190,21 @@ __global__ __launch_bounds__(256) void debug_encode_kernel(const float* __restri
 
 // ---------------------------------------------------------------- launchers ----
 
+// Row-major [N][K] codes -> BFQ_W_PACKED16. Thread c writes 16-byte chunk c of the packed
+// matrix (coalesced): fragment F = c / 128 = f*KB + kb, half h, lane l; it reads the 16 bytes
+// of row 16f + l%16 at column 128kb + 64h + 16*(l/16).
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __restrict__ w,
+                                                           uint8_t* __restrict__ packed,
+                                                           int64_t chunks, int64_t K) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= chunks) return;
+    const int64_t KB = K / 128;
+    const int64_t F = c >> 7, f = F / KB, kb = F - f * KB;
+    const int h = (int)(c >> 6) & 1, l = (int)c & 63;
+    const int64_t row = 16 * f + (l & 15), col = 128 * kb + 64 * h + 16 * (l >> 4);
+    *reinterpret_cast<v4u*>(packed + c * 16) = *reinterpret_cast<const v4u*>(w + row * K + col);
+}
+
 hipError_t launch_quant_tokens(const void* x, void* q, float* scales, int64_t M, int64_t K,
                                int qtype, int64_t s_stride_m, int64_t s_stride_g, float eps,
                                hipStream_t stream) {
@@ -226,6 +242,15 @@ hipError_t launch_debug_encode(const float* x, int64_t n, int qtype, void* out,
     else
         hipLaunchKernelGGL(debug_encode_kernel<Q_INT8>, grid, dim3(256), 0, stream, x,
                            (uint8_t*)out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_weights(const void* w, void* packed, int64_t N, int64_t K,
+                               hipStream_t stream) {
+    const int64_t chunks = N * K / 16;
+    hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                       stream, static_cast<const uint8_t*>(w), static_cast<uint8_t*>(packed),
+                       chunks, K);
     return hipGetLastError();
 }
 

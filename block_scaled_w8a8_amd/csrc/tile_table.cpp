@@ -6,6 +6,7 @@
 //   "device": "gfx950",
 //   "entries": [
 //     { "N": 24576, "K": 7168, "dtype": "fp8_w8a8", "block_shape": [128, 128],
+//       "w_layout": "packed16",            (optional; "row_major" when absent)
 //       "configs": { "1": {"variant": 1, "bm": 16, "bn": 128, "split_k": 2, "waves_m": 1,
 //                          "waves_n": 4, "stages": 4, "group_m": 1}, ... } } ] }
 #include "tile_table.h"
@@ -160,6 +161,13 @@ bool parse_tile_table(const std::string& text, TileTable& out, std::string& err)
         if (dt->str == "fp8_w8a8") qtype = 0;
         else if (dt->str == "int8_w8a8") qtype = 1;
         else { err = "unknown dtype '" + dt->str + "'"; return false; }
+        int wlayout = 0;
+        if (const JVal* wl = e.get("w_layout")) {
+            if (wl->kind != JVal::STR) { err = "'w_layout' is not a string"; return false; }
+            if (wl->str == "row_major") wlayout = 0;
+            else if (wl->str == "packed16") wlayout = 1;
+            else { err = "unknown w_layout '" + wl->str + "'"; return false; }
+        }
         const JVal* bs = e.get("block_shape");
         if (bs) {
             if (bs->kind != JVal::ARR || bs->arr.size() != 2 || bs->arr[0].num != 128 ||
@@ -201,7 +209,7 @@ bool parse_tile_table(const std::string& text, TileTable& out, std::string& err)
             buckets[(int64_t)m] = tl;
         }
         if (buckets.empty()) { err = "entry has no configs"; return false; }
-        t.entries[TableKey{N, K, qtype}] = std::move(buckets);
+        t.entries[TableKey{N, K, qtype, wlayout}] = std::move(buckets);
     }
     out = std::move(t);
     return true;

@@ -20,10 +20,12 @@ namespace bfq {
 struct TableKey {
     int64_t N, K;
     int qtype;
+    int wlayout;   // weight layout the tuned kernels read (W_ROW / W_PACKED16)
     bool operator<(const TableKey& o) const {
         if (N != o.N) return N < o.N;
         if (K != o.K) return K < o.K;
-        return qtype < o.qtype;
+        if (qtype != o.qtype) return qtype < o.qtype;
+        return wlayout < o.wlayout;
     }
 };
 

@@ -1,7 +1,9 @@
 """On-device tile sweep that fills the tile table, and a single-shape runner for profiling.
 
-  python -m block_scaled_w8a8_amd.sweep tune  [--shapes N,K ...] [--dtype fp8|int8] [--out PATH]
+  python -m block_scaled_w8a8_amd.sweep tune  [--shapes N,K ...] [--dtype fp8|int8]
+                                             [--w-layout row|packed] [--out PATH]
   python -m block_scaled_w8a8_amd.sweep run   --M 4096 --N 24576 --K 7168 [--tile JSON] [--iters 50]
+                                             [--w-layout row|packed]
   python -m block_scaled_w8a8_amd.sweep copy  [--bytes N]   (byte-counter calibration)
 
 `tune` follows the tuning flow of the config-mechanism page ("vLLM 量化 Kernel 配置机制 ...",
@@ -10,7 +12,8 @@
 one whose output agrees with a reference configuration is kept. Configurations the library
 rejects (grid or workspace limits) are skipped, like the page's OutOfResources candidates.
 Results are written to a JSON tile table after every shape, and shapes already present in the
-output file are skipped, so an interrupted sweep resumes where it stopped.
+output file are skipped, so an interrupted sweep resumes where it stopped. Each weight layout
+(row-major or packed) has entries of its own.
 
 Timing rotates over enough copies of the weights and activations to exceed the 256 MB
 Infinity Cache, so the weight stream is measured from HBM.
@@ -41,7 +44,7 @@ def log(*a):
 class Problem:
     """Device buffers for one (N, K) and the largest M, with rotation copies."""
 
-    def __init__(self, N, K, m_max, qname, rotate=None, layout="col"):
+    def __init__(self, N, K, m_max, qname, rotate=None, layout="col", w_layout="row"):
         import torch
 
         from . import bfq, synth
@@ -51,6 +54,9 @@ class Problem:
         x = synth.activations(m_max, K, seed=0).to(dev)
         w = synth.weights(N, K, seed=0).to(dev)
         qw, sw = bfq.quant_weight_blocks(w, q_dtype=self.qd)
+        self.wl = bfq.BFQ_W_PACKED16 if w_layout == "packed" else bfq.BFQ_W_ROW_MAJOR
+        if self.wl == bfq.BFQ_W_PACKED16:
+            qw = bfq.pack_weights(qw)
         self.layout = bfq.BFQ_SCALES_COL_MAJOR if layout == "col" else bfq.BFQ_SCALES_ROW_MAJOR
         qa, sa = bfq.quant_tokens(x, q_dtype=self.qd, layout=self.layout)
         del w, x
@@ -82,7 +88,7 @@ class Problem:
         sa_m = sa if self.layout == bfq.BFQ_SCALES_COL_MAJOR else sa[:M]
         return bfq.bfq_block_gemm(qa[:M], sa_m, qw, sw, out[:M], a_layout=self.layout,
                                   a_scale_ld=sa.stride(0), tile=tile, workspace=ws,
-                                  workspace_bytes=need)
+                                  workspace_bytes=need, w_layout=self.wl)
 
     def time_us(self, M, tile, warmup=3, iters=20, reps=3):
         """Median over reps of the mean time of `iters` back-to-back launches, replayed from a
@@ -112,15 +118,15 @@ class Problem:
         return res[len(res) // 2]
 
 
-def candidates(qd, M, N, K):
+def candidates(qd, M, N, K, wl=0):
     """Compiled kernels x split-K factors x tile orders worth timing at this shape: the
     streaming kernel only while it re-reads the weights at most 4 times, split-K only while
     the grid is short of 4 workgroups per CU, tile orders only for multi-tile grids."""
     from . import bfq
     out = []
     KB = K // 128
-    for i in range(bfq.bfq_num_tile_candidates(qd)):
-        t = bfq.bfq_get_tile_candidate(i, qd)
+    for i in range(bfq.bfq_num_tile_candidates(qd, wl)):
+        t = bfq.bfq_get_tile_candidate(i, qd, wl)
         if t.variant == 1 and M > 4 * t.bm:
             continue
         if t.variant in (0, 2) and M <= 16 and t.bm > 64:
@@ -156,21 +162,21 @@ def agrees(a, b) -> bool:
     return rf <= 1e-3 and md <= 2.0 ** -7 * rms + 1e-3
 
 
-def tune_shape(N, K, qname, grid, budget_s):
+def tune_shape(N, K, qname, grid, budget_s, w_layout="row"):
     import torch
 
     from . import bfq
-    prob = Problem(N, K, max(grid), qname)
+    prob = Problem(N, K, max(grid), qname, w_layout=w_layout)
     results = {}
     for M in grid:
         t0 = time.time()
-        _, ref_tile = bfq.bfq_select_tile(M, N, K, prob.qd, bfq.BFQ_FP32)
+        _, ref_tile = bfq.bfq_select_tile(M, N, K, prob.qd, bfq.BFQ_FP32, w_layout=prob.wl)
         prob.launch(M, ref_tile, out32=True)
         torch.cuda.synchronize()
         ref = prob.out32[:M].clone()
         best = None
         trials = []
-        for tile in candidates(prob.qd, M, N, K):
+        for tile in candidates(prob.qd, M, N, K, prob.wl):
             if time.time() - t0 > budget_s:
                 break
             try:
@@ -218,19 +224,26 @@ def cmd_tune(args):
         else DEFAULT_SHAPES[qname]
     table = load_table(args.out)
     dname = "fp8_w8a8" if qname == "fp8" else "int8_w8a8"
-    done = {(e["N"], e["K"], e["dtype"]) for e in table["entries"]}
+    wname = "packed16" if args.w_layout == "packed" else "row_major"
+
+    def key(e):
+        return (e["N"], e["K"], e["dtype"], e.get("w_layout", "row_major"))
+
+    done = {key(e) for e in table["entries"]}
     for (N, K) in shapes:
-        if (N, K, dname) in done and not args.force:
-            log(f"[sweep] N={N} K={K} {dname}: already in {args.out}, skipped")
+        if (N, K, dname, wname) in done and not args.force:
+            log(f"[sweep] N={N} K={K} {dname} {wname}: already in {args.out}, skipped")
             continue
-        log(f"[sweep] N={N} K={K} {dname}")
-        res = tune_shape(N, K, qname, args.grid or M_GRID, args.budget)
+        log(f"[sweep] N={N} K={K} {dname} {wname}")
+        res = tune_shape(N, K, qname, args.grid or M_GRID, args.budget, args.w_layout)
         entry = {"N": N, "K": K, "dtype": dname, "block_shape": [128, 128],
                  "configs": {str(M): {k: v for k, v in t.items() if k != "bk"}
                              for M, (us, t) in res.items()},
                  "us": {str(M): round(us, 3) for M, (us, t) in res.items()}}
+        if wname != "row_major":
+            entry["w_layout"] = wname
         table["entries"] = [e for e in table["entries"]
-                            if (e["N"], e["K"], e["dtype"]) != (N, K, dname)] + [entry]
+                            if key(e) != (N, K, dname, wname)] + [entry]
         save_table(args.out, table)
     print(json.dumps({"table": args.out, "entries": len(table["entries"])}))
 
@@ -239,11 +252,13 @@ def cmd_run(args):
     import torch
 
     from . import bfq
-    prob = Problem(args.N, args.K, args.M, args.dtype, rotate=args.rotate, layout=args.layout)
+    prob = Problem(args.N, args.K, args.M, args.dtype, rotate=args.rotate, layout=args.layout,
+                   w_layout=args.w_layout)
     if args.tile:
         tile = bfq.bfq_tile.from_dict(json.loads(args.tile))
     else:
-        _, tile = bfq.bfq_select_tile(args.M, args.N, args.K, prob.qd, bfq.BFQ_BF16)
+        _, tile = bfq.bfq_select_tile(args.M, args.N, args.K, prob.qd, bfq.BFQ_BF16,
+                                      w_layout=prob.wl)
     if args.eager:
         # plain launches, no graph: for counter collection, which wants one dispatch per call
         for i in range(args.eager):
@@ -285,6 +300,7 @@ def main():
     t.add_argument("--out", default=DEFAULT_TABLE)
     t.add_argument("--budget", type=float, default=20.0, help="seconds per (shape, M)")
     t.add_argument("--force", action="store_true")
+    t.add_argument("--w-layout", default="row", choices=["row", "packed"])
     r = sub.add_parser("run")
     r.add_argument("--M", type=int, required=True)
     r.add_argument("--N", type=int, required=True)
@@ -295,6 +311,7 @@ def main():
     r.add_argument("--rotate", type=int, default=None)
     r.add_argument("--eager", type=int, default=0, help="launch this many times without timing")
     r.add_argument("--layout", default="col", choices=["row", "col"], help="activation scales")
+    r.add_argument("--w-layout", default="row", choices=["row", "packed"])
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=1 << 30)
     c.add_argument("--iters", type=int, default=3)

@@ -66,12 +66,30 @@ typedef enum {
     BFQ_SCALES_COL_MAJOR = 1   /* s[g * ld + m], ld >= M     */
 } bfq_scale_layout;
 
+/* Layout of the weight codes in memory. The values are the same bytes either way; the packed
+ * layout puts each MFMA fragment's bytes together so that every wave-wide 16-byte-per-lane
+ * load reads 1 KB of contiguous memory (a row-major [N][K] matrix can only give each load
+ * 16 rows x 64 bytes, which caps the weight stream well below the HBM peak).
+ *   BFQ_W_ROW_MAJOR: w[n][k] at byte n*K + k.
+ *   BFQ_W_PACKED16 : for every 16-row group f = n/16 and K block kb, 2048 bytes at
+ *                    (f*(K/128) + kb)*2048; inside them byte h*1024 + 16*l + b (h in {0,1},
+ *                    lane l in [0,64), b in [0,16)) holds w[16f + l%16][128kb + 64h + 16*(l/16) + b].
+ *                    The whole matrix still spans N*K bytes, rows in blocks of 16. */
+typedef enum {
+    BFQ_W_ROW_MAJOR = 0,
+    BFQ_W_PACKED16 = 1
+} bfq_weight_layout;
+
 /* One launch configuration of the block GEMM ([CONFIG] §2: per-M launch parameters).
  *   variant 0 "standard": bm x bn output tile per workgroup, A and W tiles staged through
  *             LDS (double-buffered), waves_m x waves_n waves, group_m = grouped tile order.
  *   variant 1 "swap_ab": the weight rows stream straight from HBM into the wide MFMA
  *             operand and the bm tokens ride in the narrow one; the output tile is formed
- *             transposed and stored back row-major ([HELION] kernel section).
+ *             transposed and stored back row-major ([HELION] kernel section). A workgroup
+ *             holds waves_n strips of bn/waves_n weight rows; the waves_m waves of a strip
+ *             split its K range and are summed in the workgroup, in a fixed order. sched 0:
+ *             each wave fetches its token fragments; sched 1: each K block's token fragments
+ *             are fetched once per workgroup and shared through LDS.
  *   variant 2 "stream-K": the tiles of variant 0 on a persistent grid of one workgroup per
  *             compute unit; whole tiles in rounds, then the K blocks of the last one to two
  *             rounds of tiles split evenly over the grid; a second kernel sums each split
@@ -80,7 +98,7 @@ typedef enum {
  *   split_k  : K blocks split into split_k contiguous chunks (>= 1), fp32 partials reduced
  *             in a fixed order ([HELION] kernel section).
  *   stages   : LDS stages (variants 0, 2) or weight prefetch depth in K blocks (variant 1).
- *   sched    : variants 0 and 2 instruction schedule: 0 = each sub-tile's scale FMAs right after its
+ *   sched    : variants 0 and 2 instruction schedule (variant 1: see above): 0 = each sub-tile's scale FMAs right after its
  *             MFMAs, 1 = software-pipelined (FMAs one sub-tile behind the MFMAs), 2 = 32x32
  *             sub-tiles (two 32x32x64 MFMAs per K block, FMAs one pair behind; fp8 only).
  *   group_m, raster: variants 0 and 2 tile order (launch arguments, any group_m >= 1): raster 0
@@ -112,28 +130,39 @@ bfq_status bfq_quant_weight_blocks(const float* w, int64_t N, int64_t K,
                                    const int32_t block_shape[2] /* host */, bfq_dtype q_dtype,
                                    void* q, float* scales, float eps, void* stream);
 
-/* Tile selection ([CONFIG] §4.1-§4.2): exact (N, K, dtype) entry of the loaded tile table,
- * then the bucket nearest to M (ties to the smaller bucket; M past the grid -> last bucket).
- * No entry -> the compiled-in default rule and BFQ_WARN_DEFAULT_TILE ([CONFIG] §4.1 warns
- * and falls back to a default config). tile_out is a host pointer. */
+/* Rearrange weight codes from row-major [N][K] into BFQ_W_PACKED16 (a byte permutation, part
+ * of the offline weight preparation like bfq_quant_weight_blocks). w_q and w_packed are
+ * separate N*K-byte device buffers (16-byte aligned, not overlapping); q_dtype E4M3FN or
+ * INT8 (the permutation does not depend on it). N, K multiples of 128. */
+bfq_status bfq_pack_weights(const void* w_q, int64_t N, int64_t K, bfq_dtype q_dtype,
+                            void* w_packed, void* stream);
+
+/* Tile selection ([CONFIG] §4.1-§4.2): exact (N, K, dtype, weight layout) entry of the loaded
+ * tile table, then the bucket nearest to M (ties to the smaller bucket; M past the grid ->
+ * last bucket). No entry -> the compiled-in default rule and BFQ_WARN_DEFAULT_TILE ([CONFIG]
+ * §4.1 warns and falls back to a default config). tile_out is a host pointer. */
 bfq_status bfq_select_tile(int64_t M, int64_t N, int64_t K, const int32_t block_shape[2],
-                           bfq_dtype in_dtype, bfq_dtype out_dtype, bfq_tile* tile_out);
+                           bfq_dtype in_dtype, bfq_dtype out_dtype, bfq_weight_layout w_layout,
+                           bfq_tile* tile_out);
 
 /* Bytes of device workspace bfq_block_gemm needs for this shape and tile (split-K fp32
- * partials: split_k * M * N * 4 when split_k > 1, else 0). tile NULL -> selected tile. */
+ * partials: split_k * M * N * 4 when split_k > 1; stream-K: two partial tiles per compute
+ * unit; else 0). tile NULL -> the tile selected for e4m3fn codes in the row-major layout. */
 size_t bfq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const bfq_tile* tile);
 
 /* Block-scaled GEMM ([BENCH] §4.2, w8a8 block-scaled matmul):
  *   out[m][n] = sum_kb ( sum_{k in kb} a_q[m][k] * w_q[n][k] ) * a_scales[m, kb] * w_scales[n/128][kb]
  * with exact per-block products, an fp32 accumulator and one rounding to out_dtype.
- *   a_q [M][K] codes, w_q [N][K] codes (both K-contiguous, "NT");
+ *   a_q [M][K] codes (K-contiguous); w_q N*K codes in w_layout (row-major [N][K] is the
+ *   "NT" form of the page; BFQ_W_PACKED16 from bfq_pack_weights);
  *   a_scales per a_layout/a_scale_ld; w_scales [N/128][K/128] row-major;
  *   out [M][N] row-major, out_dtype BF16 | FP16 | FP32.
- *   tile NULL -> bfq_select_tile; workspace may be NULL when the tile needs none.
+ *   tile NULL -> bfq_select_tile for w_layout; an explicit tile must name a kernel compiled
+ *   for w_layout (else BFQ_ERR_TILE); workspace may be NULL when the tile needs none.
  * Returns BFQ_WARN_DEFAULT_TILE when tile was NULL and the default rule was used. */
 bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
                           int64_t a_scale_ld, const void* w_q, const float* w_scales,
-                          void* out, int64_t M, int64_t N, int64_t K,
+                          bfq_weight_layout w_layout, void* out, int64_t M, int64_t N, int64_t K,
                           const int32_t block_shape[2] /* host */, bfq_dtype in_dtype,
                           bfq_dtype out_dtype, const bfq_tile* tile /* host */,
                           void* workspace, size_t workspace_bytes, void* stream);
@@ -143,10 +172,11 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
  * concurrently with other calls. NULL reloads the default location. */
 bfq_status bfq_load_tile_table(const char* json_path);
 
-/* Number of compiled kernel configurations for in_dtype, and the i-th one (split_k = 1;
- * any split_k >= 1 may be combined with it). Used by the on-device sweep. */
-int32_t bfq_num_tile_candidates(bfq_dtype in_dtype);
-bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, int32_t index, bfq_tile* tile_out);
+/* Number of compiled kernel configurations for (in_dtype, w_layout), and the i-th one
+ * (split_k = 1; any split_k >= 1 may be combined with it). Used by the on-device sweep. */
+int32_t bfq_num_tile_candidates(bfq_dtype in_dtype, bfq_weight_layout w_layout);
+bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, bfq_weight_layout w_layout, int32_t index,
+                                  bfq_tile* tile_out);
 
 const char* bfq_status_string(bfq_status s);
 const char* bfq_last_error(void);

@@ -162,6 +162,21 @@ def quant_blocks(w: np.ndarray, block=(128, 128), qtype: int = FP8, eps: float =
 
 # ------------------------------------------------------------------ GEMM
 
+def pack16(w: np.ndarray) -> np.ndarray:
+    """The packed 16-row fragment layout of weight codes (a byte permutation; the layout is
+    this library's own HBM format for the weights, not something the pages define, so the
+    definition written out is the oracle). For every 16-row group f and 128-wide K block kb
+    there are 2048 consecutive bytes at (f*(K/128) + kb)*2048; byte h*1024 + 16*l + b of
+    them (h in {0,1}, l in [0,64), b in [0,16)) is w[16f + l%16, 128kb + 64h + 16*(l//16) + b].
+    Works on any dtype (tests pack index arrays to check it is a permutation)."""
+    N, K = w.shape
+    assert N % 16 == 0 and K % 128 == 0
+    # axes (f, r, kb, h, g, b): row 16f + r, column 128kb + 64h + 16g + b
+    x = np.asarray(w).reshape(N // 16, 16, K // 128, 2, 4, 16)
+    # fragment-major, then half, then lane l = 16g + r, then byte
+    return np.ascontiguousarray(x.transpose(0, 2, 3, 4, 1, 5)).reshape(N, K)
+
+
 def _gemm_args(qa, sa, qw, sw, qtype):
     qa = np.ascontiguousarray(qa, dtype=_code_dtype(qtype))
     qw = np.ascontiguousarray(qw, dtype=_code_dtype(qtype))

@@ -37,7 +37,7 @@ FAKE = 1 << 20          # a 16-byte aligned non-NULL address; never dereferenced
 
 def _gemm(bfq, **kw):
     a = dict(a_q=FAKE, a_scales=FAKE, a_layout=0, a_scale_ld=56, w_q=FAKE, w_scales=FAKE,
-             out=FAKE, M=0, N=1536, K=7168, block_shape=BS, in_dtype=bfq.BFQ_E4M3FN,
+             w_layout=0, out=FAKE, M=0, N=1536, K=7168, block_shape=BS, in_dtype=bfq.BFQ_E4M3FN,
              out_dtype=bfq.BFQ_BF16, tile=None, workspace=None, workspace_bytes=0, stream=None)
     a.update(kw)
     return bfq.lib.bfq_block_gemm(*a.values())
@@ -57,6 +57,14 @@ def test_gemm_validation_errors_without_launch(bfq):
     assert _gemm(bfq, a_scale_ld=10) == bfq.BFQ_ERR_SHAPE
     assert _gemm(bfq, M=64, a_layout=1, a_scale_ld=63) == bfq.BFQ_ERR_SHAPE
     assert _gemm(bfq, a_layout=7) == bfq.BFQ_ERR_ARG
+    assert _gemm(bfq, w_layout=2) == bfq.BFQ_ERR_ARG
+    # a tile compiled only for row-major weights is rejected for packed ones
+    row_only = [bfq.bfq_get_tile_candidate(i) for i in range(bfq.bfq_num_tile_candidates())]
+    packed = {tuple(bfq.bfq_get_tile_candidate(i, bfq.BFQ_E4M3FN, bfq.BFQ_W_PACKED16).as_dict().values())
+              for i in range(bfq.bfq_num_tile_candidates(bfq.BFQ_E4M3FN, bfq.BFQ_W_PACKED16))}
+    t32 = next(t for t in row_only if tuple(t.as_dict().values()) not in packed)
+    assert _gemm(bfq, M=64, w_layout=1, tile=ctypes.pointer(t32)) == bfq.BFQ_ERR_TILE
+    assert "weight layout" in bfq.last_error()
     bad = bfq.bfq_tile.from_dict({"variant": 0, "bm": 96, "bn": 96, "waves_m": 2, "waves_n": 2})
     assert _gemm(bfq, tile=ctypes.pointer(bad)) == bfq.BFQ_ERR_TILE
     t = bfq.bfq_get_tile_candidate(0)
@@ -97,18 +105,37 @@ def test_quant_validation_errors_without_launch(bfq):
     assert w(FAKE, 0, 256, BS, bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, None) == bfq.BFQ_OK
 
 
-def test_candidates_enumerate(bfq):
+def test_pack_validation_errors_without_launch(bfq):
+    pk = bfq.lib.bfq_pack_weights
+    other = FAKE + (1 << 24)
+    assert pk(None, 256, 256, bfq.BFQ_E4M3FN, other, None) == bfq.BFQ_ERR_NULL
+    assert pk(FAKE, 256, 256, bfq.BFQ_E4M3FN, None, None) == bfq.BFQ_ERR_NULL
+    assert pk(FAKE, 250, 256, bfq.BFQ_E4M3FN, other, None) == bfq.BFQ_ERR_SHAPE
+    assert pk(FAKE, 256, 200, bfq.BFQ_E4M3FN, other, None) == bfq.BFQ_ERR_SHAPE
+    assert pk(FAKE, 256, 256, bfq.BFQ_BF16, other, None) == bfq.BFQ_ERR_DTYPE
+    assert pk(FAKE + 4, 256, 256, bfq.BFQ_E4M3FN, other, None) == bfq.BFQ_ERR_ALIGN
+    # the buffers overlap (in place, or offset by less than N*K bytes)
+    assert pk(FAKE, 256, 256, bfq.BFQ_E4M3FN, FAKE, None) == bfq.BFQ_ERR_ARG
+    assert pk(FAKE, 256, 256, bfq.BFQ_E4M3FN, FAKE + 65520, None) == bfq.BFQ_ERR_ARG
+    assert pk(FAKE, 0, 256, bfq.BFQ_INT8, other, None) == bfq.BFQ_OK
+
+
+@pytest.mark.parametrize("wl", [0, 1])
+def test_candidates_enumerate(bfq, wl):
     for qd in (bfq.BFQ_E4M3FN, bfq.BFQ_INT8):
-        n = bfq.bfq_num_tile_candidates(qd)
+        n = bfq.bfq_num_tile_candidates(qd, wl)
         assert n >= 4
         seen = set()
         for i in range(n):
-            t = bfq.bfq_get_tile_candidate(i, qd)
+            t = bfq.bfq_get_tile_candidate(i, qd, wl)
             assert t.split_k == 1 and t.bk == 128 and t.variant in (0, 1, 2)
             seen.add(tuple(t.as_dict().values()))
         assert len(seen) == n
+        # every kernel variant is compiled for both layouts
+        assert {t[0] for t in seen} == {0, 1, 2}
     with pytest.raises(bfq.BfqError):
         bfq.bfq_get_tile_candidate(10_000)
+    assert bfq.bfq_num_tile_candidates(bfq.BFQ_E4M3FN, 5) == 0
 
 
 def _table(entries):
@@ -135,8 +162,34 @@ def test_table_nearest_m_and_fallback(bfq, tmp_path):
         assert st == bfq.BFQ_WARN_DEFAULT_TILE
         st, t = bfq.bfq_select_tile(64, 1536, 7168, in_dtype=bfq.BFQ_INT8)   # dtype is part of the key
         assert st == bfq.BFQ_WARN_DEFAULT_TILE
+        st, t = bfq.bfq_select_tile(64, 1536, 7168, w_layout=bfq.BFQ_W_PACKED16)   # so is the layout
+        assert st == bfq.BFQ_WARN_DEFAULT_TILE
     finally:
         bfq.bfq_load_tile_table(None)
+
+
+def test_table_weight_layout_key(bfq, tmp_path):
+    """An entry marked "w_layout": "packed16" serves packed weights only, and its tiles must
+    name kernels compiled for that layout."""
+    wl = bfq.BFQ_W_PACKED16
+    cand = bfq.bfq_get_tile_candidate(0, bfq.BFQ_E4M3FN, wl).as_dict()
+    p = tmp_path / "t.json"
+    p.write_text(_table([{"N": 1536, "K": 7168, "dtype": "fp8_w8a8", "w_layout": "packed16",
+                          "configs": {"16": dict(cand, split_k=2)}}]))
+    try:
+        assert bfq.bfq_load_tile_table(str(p)) == bfq.BFQ_OK
+        st, t = bfq.bfq_select_tile(16, 1536, 7168, w_layout=wl)
+        assert st == bfq.BFQ_OK and t.as_dict() == dict(cand, split_k=2, bk=128)
+        st, t = bfq.bfq_select_tile(16, 1536, 7168)
+        assert st == bfq.BFQ_WARN_DEFAULT_TILE
+    finally:
+        bfq.bfq_load_tile_table(None)
+    bad = tmp_path / "bad.json"
+    bad.write_text(_table([{"N": 1536, "K": 7168, "dtype": "fp8_w8a8", "w_layout": "tiled",
+                            "configs": {"16": cand}}]))
+    with pytest.raises(bfq.BfqError):
+        bfq.bfq_load_tile_table(str(bad))
+    bfq.bfq_load_tile_table(None)
 
 
 @pytest.mark.parametrize("text,why", [
@@ -170,6 +223,12 @@ def test_default_rule(bfq, tmp_path):
         for M in (1, 8, 16, 31):
             st, t = bfq.bfq_select_tile(M, 24576, 7168)
             assert st == bfq.BFQ_WARN_DEFAULT_TILE and t.variant == 1
+        # the default tiles exist for both weight layouts
+        for wl in (bfq.BFQ_W_ROW_MAJOR, bfq.BFQ_W_PACKED16):
+            for M in (1, 31, 64, 200, 4096):
+                st, t = bfq.bfq_select_tile(M, 24576, 7168, w_layout=wl)
+                assert st == bfq.BFQ_WARN_DEFAULT_TILE
+                assert _gemm(bfq, M=0, N=24576, w_layout=wl, tile=ctypes.pointer(t)) >= 0
         for M in (32, 64, 4096):
             st, t = bfq.bfq_select_tile(M, 24576, 7168)
             assert t.variant == 0

@@ -6,6 +6,8 @@ Bar (see oracle/metrics.py):
   bf16 output: bit-exact bf16 rounding of the GPU's own fp32 output for the same tile,
   plus the straddle reading against the oracle's bf16 output;
   exact-integer inputs: fp32 output bit-exact; int8 block partials bit-exact.
+Kernels are checked with the weights row-major and packed (the packing done on the device
+by bfq_pack_weights, itself checked byte for byte against the oracle's pack16).
 """
 import numpy as np
 import pytest
@@ -15,6 +17,7 @@ from block_scaled_w8a8_amd import synth
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+LAYOUTS = ["row", "packed"]
 
 
 def _case(orc, M, N, K, seed, qtype):
@@ -25,30 +28,54 @@ def _case(orc, M, N, K, seed, qtype):
     return qa, sa, qw, sw
 
 
-def _to_dev(qa, sa, qw, sw):
-    return (torch.from_numpy(qa).to(DEV), torch.from_numpy(sa).to(DEV),
-            torch.from_numpy(qw).to(DEV), torch.from_numpy(sw).to(DEV))
+def _to_dev(qa, sa, qw, sw, layout="row"):
+    """Device copies; with layout "packed" the weight codes are packed on the device."""
+    from block_scaled_w8a8_amd import bfq
+    qw_d = torch.from_numpy(qw).to(DEV)
+    if layout == "packed":
+        qw_d = bfq.pack_weights(qw_d)
+    return (torch.from_numpy(qa).to(DEV), torch.from_numpy(sa).to(DEV), qw_d,
+            torch.from_numpy(sw).to(DEV), layout)
+
+
+def _wl(bfq, layout):
+    return bfq.BFQ_W_PACKED16 if layout == "packed" else bfq.BFQ_W_ROW_MAJOR
 
 
 def _run(bfq, dq, out_dtype, tile=None, a_layout=None, sa_override=None):
-    qa, sa, qw, sw = dq
+    qa, sa, qw, sw, wlay = dq
+    wl = _wl(bfq, wlay)
     M, N = qa.shape[0], qw.shape[0]
     out = torch.full((M, N), float("nan"), dtype=out_dtype, device=DEV)
     layout = bfq.BFQ_SCALES_ROW_MAJOR if a_layout is None else a_layout
     sa_arg = sa if sa_override is None else sa_override
     ws_bytes = bfq.bfq_gemm_workspace_bytes(M, N, qa.shape[1], tile) if tile is not None else 0
     if tile is None:
-        st, t = bfq.bfq_select_tile(M, N, qa.shape[1], bfq._qdtype(qa), bfq._odtype(out))
+        st, t = bfq.bfq_select_tile(M, N, qa.shape[1], bfq._qdtype(qa), bfq._odtype(out),
+                                    w_layout=wl)
         ws_bytes = bfq.bfq_gemm_workspace_bytes(M, N, qa.shape[1], t)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
     bfq.bfq_block_gemm(qa, sa_arg, qw, sw, out, a_layout=layout, a_scale_ld=sa_arg.stride(0),
-                       tile=tile, workspace=ws, workspace_bytes=ws_bytes)
+                       tile=tile, workspace=ws, workspace_bytes=ws_bytes, w_layout=wl)
     torch.cuda.synchronize()
     return out
 
 
-def _candidates(bfq, qd):
-    return [bfq.bfq_get_tile_candidate(i, qd) for i in range(bfq.bfq_num_tile_candidates(qd))]
+def _candidates(bfq, qd, layout="row"):
+    wl = _wl(bfq, layout)
+    return [bfq.bfq_get_tile_candidate(i, qd, wl)
+            for i in range(bfq.bfq_num_tile_candidates(qd, wl))]
+
+
+@pytest.mark.parametrize("N,K", [(128, 128), (640, 768), (1536, 7168), (24576, 7168)])
+def test_pack_weights_bit_exact(bfq, orc, N, K):
+    """bfq_pack_weights equals the oracle's pack16 byte for byte (the full-size shape is the
+    wide up-projection's weight matrix)."""
+    g = torch.Generator().manual_seed(N + K)
+    w = torch.randint(0, 256, (N, K), dtype=torch.uint8, generator=g)
+    got = bfq.pack_weights(w.to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), orc.pack16(w.numpy()))
 
 
 def _with_split(t, s):
@@ -62,8 +89,9 @@ def _check_fp32(orc_metrics, out, ref, what):
     assert r["ok"], (what, r)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("qname", ["fp8", "int8"])
-def test_every_candidate_and_split_parity(bfq, orc, qname):
+def test_every_candidate_and_split_parity(bfq, orc, qname, layout):
     """Every compiled kernel x split_k {1, 2, 3} x out dtype on a shape spanning several
     tiles with ragged M (multiple tiles in N, K = 6 blocks so 3 splits are uneven-free)."""
     from oracle import metrics
@@ -72,13 +100,15 @@ def test_every_candidate_and_split_parity(bfq, orc, qname):
     M, N, K = 83, 640, 768
     host = _case(orc, M, N, K, 21, qt)
     ref32, ref16 = orc.block_gemm(*host, qtype=qt)
-    dq = _to_dev(*host)
-    for t in _candidates(bfq, qd):
+    dq = _to_dev(*host, layout=layout)
+    cands = _candidates(bfq, qd, layout)
+    assert cands, (qname, layout)
+    for t in cands:
         for s in (1, 2, 3):
             if t.variant == 2 and s > 1:        # stream-K splits K by itself
                 continue
             tile = _with_split(t, s)
-            what = (qname, tile.as_dict())
+            what = (qname, layout, tile.as_dict())
             print("candidate", what, flush=True)
             o32 = _run(bfq, dq, torch.float32, tile=tile).cpu().numpy()
             _check_fp32(metrics, o32, ref32, what)
@@ -92,8 +122,9 @@ def test_every_candidate_and_split_parity(bfq, orc, qname):
             assert np.array_equal(oh, ref_h), what
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("qname", ["fp8", "int8"])
-def test_streamk_segments_and_determinism(bfq, orc, qname):
+def test_streamk_segments_and_determinism(bfq, orc, qname, layout):
     """Stream-K (variant 2) with few tiles and many K blocks: at M=300, N=640, K=896 a 256x256
     tile grid has 6 tiles of 7 blocks, so 42 one-block segments land on 42 workgroups and
     every tile is summed from 7 parked partials; fp32 within the bar of the oracle, bf16 the
@@ -105,11 +136,11 @@ def test_streamk_segments_and_determinism(bfq, orc, qname):
     M, N, K = 300, 640, 896
     host = _case(orc, M, N, K, 25, qt)
     ref32, _ = orc.block_gemm(*host, qtype=qt)
-    dq = _to_dev(*host)
-    sk = [t for t in _candidates(bfq, qd) if t.variant == 2]
+    dq = _to_dev(*host, layout=layout)
+    sk = [t for t in _candidates(bfq, qd, layout) if t.variant == 2]
     assert sk, "no stream-K kernel compiled for " + qname
     for t in sk:
-        what = (qname, t.as_dict())
+        what = (qname, layout, t.as_dict())
         print("stream-K", what, flush=True)
         o32a = _run(bfq, dq, torch.float32, tile=t).cpu().numpy()
         _check_fp32(metrics, o32a, ref32, what)
@@ -119,17 +150,19 @@ def test_streamk_segments_and_determinism(bfq, orc, qname):
         assert np.array_equal(o16, orc.f32_to_bf16_bits_array(o32a)), what
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", [(2304, 7680, 1024), (5120, 7680, 512)])
-def test_streamk_large_sampled(bfq, orc, M, N, K):
+def test_streamk_large_sampled(bfq, orc, M, N, K, layout):
     """Stream-K at grid-filling sizes, sampled against the oracle: 270 tiles of 256x256 (all
     split over the grid) and 600 tiles (256 taken whole, 344 split)."""
-    for t in [t for t in _candidates(bfq, bfq.BFQ_E4M3FN) if t.variant == 2]:
-        print("stream-K", M, N, K, t.as_dict(), flush=True)
-        _sampled_check(bfq, orc, M, N, K, M, "fp8", n_samples=2048, tile=t)
+    for t in [t for t in _candidates(bfq, bfq.BFQ_E4M3FN, layout) if t.variant == 2]:
+        print("stream-K", M, N, K, layout, t.as_dict(), flush=True)
+        _sampled_check(bfq, orc, M, N, K, M, "fp8", n_samples=2048, tile=t, layout=layout)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("qname", ["fp8", "int8"])
-def test_exact_integer_case_every_candidate(bfq, orc, qname):
+def test_exact_integer_case_every_candidate(bfq, orc, qname, layout):
     """P6 on the device: integer-valued codes with |v| <= 8 and power-of-two scales make
     every partial exact, so the fp32 output must equal the integer matmul bit for bit for
     every kernel and split."""
@@ -149,17 +182,18 @@ def test_exact_integer_case_every_candidate(bfq, orc, qname):
     sa = np.full((M, K // 128), 2.0 ** -3, dtype=np.float32)
     sw = np.full((N // 128, K // 128), 2.0 ** -5, dtype=np.float32)
     exact = (ia.astype(np.int64) @ iw.T.astype(np.int64)).astype(np.float64) * 2.0 ** -8
-    dq = _to_dev(qa, sa, qw, sw)
-    for t in _candidates(bfq, qd):
+    dq = _to_dev(qa, sa, qw, sw, layout=layout)
+    for t in _candidates(bfq, qd, layout):
         for s in (1, 4):
             if t.variant == 2 and s > 1:
                 continue
             tile = _with_split(t, s)
             o32 = _run(bfq, dq, torch.float32, tile=tile).cpu().numpy().astype(np.float64)
-            assert np.array_equal(o32, exact), (qname, tile.as_dict())
+            assert np.array_equal(o32, exact), (qname, layout, tile.as_dict())
 
 
-def test_one_hot_rows_pin_layout(bfq, orc):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_one_hot_rows_pin_layout(bfq, orc, layout):
     """A token row holding code 1.0 at one column reproduces that weight column times its
     block scale (fp32 product) on every kernel: pins the row/column/K index mapping."""
     M, N, K = 20, 256, 512
@@ -172,10 +206,10 @@ def test_one_hot_rows_pin_layout(bfq, orc):
     sa = np.ones((M, K // 128), dtype=np.float32)
     deq = torch.from_numpy(qw).view(torch.float8_e4m3fn).float().numpy()
     want = np.stack([deq[:, k] * np.repeat(sw[:, k // 128], 128) for k in ks]).astype(np.float32)
-    dq = _to_dev(qa, sa, qw, sw)
-    for t in _candidates(bfq, bfq.BFQ_E4M3FN):
+    dq = _to_dev(qa, sa, qw, sw, layout=layout)
+    for t in _candidates(bfq, bfq.BFQ_E4M3FN, layout):
         o32 = _run(bfq, dq, torch.float32, tile=t).cpu().numpy()
-        assert np.array_equal(o32, want), t.as_dict()
+        assert np.array_equal(o32, want), (layout, t.as_dict())
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (16, 1536, 7168), (130, 1536, 7168),
@@ -193,25 +227,28 @@ def test_int8_block_partials_bit_exact(bfq, orc, M, N, K):
     assert np.array_equal(part.cpu().numpy(), orc.block_partials_i32(qa, qw))
 
 
-def test_column_major_scales_and_padded_ld(bfq, orc):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_column_major_scales_and_padded_ld(bfq, orc, layout):
     from oracle import metrics
     M, N, K = 50, 512, 1024
     host = _case(orc, M, N, K, 51, orc.FP8)
     ref32, _ = orc.block_gemm(*host)
-    qa, sa, qw, sw = _to_dev(*host)
+    dq = _to_dev(*host, layout=layout)
+    sa = dq[1]
     sa_col = torch.full((K // 128, M + 3), float("nan"), device=DEV)
     sa_col[:, :M] = sa.t()
-    for t in _candidates(bfq, bfq.BFQ_E4M3FN):
-        o = _run(bfq, (qa, sa, qw, sw), torch.float32, tile=t, a_layout=bfq.BFQ_SCALES_COL_MAJOR,
+    for t in _candidates(bfq, bfq.BFQ_E4M3FN, layout):
+        o = _run(bfq, dq, torch.float32, tile=t, a_layout=bfq.BFQ_SCALES_COL_MAJOR,
                  sa_override=sa_col)
-        _check_fp32(metrics, o.cpu().numpy(), ref32, t.as_dict())
+        _check_fp32(metrics, o.cpu().numpy(), ref32, (layout, t.as_dict()))
     sa_pad = torch.full((M, K // 128 + 4), float("nan"), device=DEV)
     sa_pad[:, :K // 128] = sa
-    o = _run(bfq, (qa, sa, qw, sw), torch.float32, sa_override=sa_pad)
+    o = _run(bfq, dq, torch.float32, sa_override=sa_pad)
     _check_fp32(metrics, o.cpu().numpy(), ref32, "padded ld")
 
 
-def test_nan_input_propagates_to_its_row(bfq, orc):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_nan_input_propagates_to_its_row(bfq, orc, layout):
     """A NaN activation gives its group a NaN scale; the whole output row is NaN, other
     rows are unaffected (oracle and GPU agree on which outputs are NaN)."""
     M, N, K = 8, 256, 512
@@ -221,10 +258,10 @@ def test_nan_input_propagates_to_its_row(bfq, orc):
     qa, sa = orc.quant_groups(bits)
     qw, sw = orc.quant_blocks(synth.weights(N, K, seed=62).numpy())
     ref32, _ = orc.block_gemm(qa, sa, qw, sw)
-    dq = _to_dev(qa, sa, qw, sw)
-    for t in [None] + _candidates(bfq, bfq.BFQ_E4M3FN):
+    dq = _to_dev(qa, sa, qw, sw, layout=layout)
+    for t in [None] + _candidates(bfq, bfq.BFQ_E4M3FN, layout):
         o = _run(bfq, dq, torch.float32, tile=t).cpu().numpy()
-        what = None if t is None else t.as_dict()
+        what = (layout, None if t is None else t.as_dict())
         assert np.array_equal(np.isnan(o), np.isnan(ref32)), what
         assert np.isnan(o[3]).all() and not np.isnan(np.delete(o, 3, 0)).any(), what
 
@@ -239,10 +276,11 @@ def test_m0_no_launch(bfq):
     assert st >= 0
 
 
-def test_deterministic_run_twice(bfq, orc):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_deterministic_run_twice(bfq, orc, layout):
     M, N, K = 64, 1536, 7168
-    dq = _to_dev(*_case(orc, M, N, K, 71, orc.FP8))
-    for t in _candidates(bfq, bfq.BFQ_E4M3FN):
+    dq = _to_dev(*_case(orc, M, N, K, 71, orc.FP8), layout=layout)
+    for t in _candidates(bfq, bfq.BFQ_E4M3FN, layout):
         tile = _with_split(t, 1 if t.variant == 2 else 4)
         a = _run(bfq, dq, torch.float32, tile=tile)
         b = _run(bfq, dq, torch.float32, tile=tile)
@@ -277,25 +315,30 @@ def _full_inputs(bfq, N, K, m_max, qname):
         xd, wd = x.to(DEV), w.to(DEV)
         qw, sw = bfq.quant_weight_blocks(wd, q_dtype=qd)
         qa, sa = bfq.quant_tokens(xd, q_dtype=qd)
+        qwp = bfq.pack_weights(qw)
         torch.cuda.synchronize()
         del wd
         _cache[key] = (qa, sa, qw, sw, qa.cpu().numpy(), sa.cpu().numpy(), qw.cpu().numpy(),
-                       sw.cpu().numpy())
+                       sw.cpu().numpy(), qwp)
     return _cache[key]
 
 
-def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096, tile=None):
+def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096, tile=None, layout="row"):
     from oracle import metrics
     qt = orc.FP8 if qname == "fp8" else orc.INT8
-    qa, sa, qw, sw, qa_h, sa_h, qw_h, sw_h = _full_inputs(bfq, N, K, m_max, qname)
+    qa, sa, qw, sw, qa_h, sa_h, qw_h, sw_h, qwp = _full_inputs(bfq, N, K, m_max, qname)
+    wl = _wl(bfq, layout)
+    qw_arg = qwp if layout == "packed" else qw
     out32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
     out16 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     if tile is None:
-        st, tile = bfq.bfq_select_tile(M, N, K, bfq._qdtype(qa), bfq.BFQ_FP32)
+        st, tile = bfq.bfq_select_tile(M, N, K, bfq._qdtype(qa), bfq.BFQ_FP32, w_layout=wl)
     ws_bytes = bfq.bfq_gemm_workspace_bytes(M, N, K, tile)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
-    bfq.bfq_block_gemm(qa[:M], sa[:M], qw, sw, out32, tile=tile, workspace=ws, workspace_bytes=ws_bytes)
-    bfq.bfq_block_gemm(qa[:M], sa[:M], qw, sw, out16, tile=tile, workspace=ws, workspace_bytes=ws_bytes)
+    bfq.bfq_block_gemm(qa[:M], sa[:M], qw_arg, sw, out32, tile=tile, workspace=ws,
+                       workspace_bytes=ws_bytes, w_layout=wl)
+    bfq.bfq_block_gemm(qa[:M], sa[:M], qw_arg, sw, out16, tile=tile, workspace=ws,
+                       workspace_bytes=ws_bytes, w_layout=wl)
     torch.cuda.synchronize()
     rng = np.random.default_rng(M * 7 + N)
     ms = np.concatenate([rng.integers(0, M, n_samples), [0, M - 1, M - 1]])
@@ -304,7 +347,7 @@ def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096, tile=None):
     o32 = out32.cpu().numpy()
     got = o32[ms, ns]
     r = metrics.gemm_fp32_report(got, ref)
-    assert r["ok"], (M, N, K, tile.as_dict(), r)
+    assert r["ok"], (M, N, K, layout, tile.as_dict(), r)
     o16 = out16.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(o16, orc.f32_to_bf16_bits_array(o32)), (M, N, K)
     # quantized inputs were produced on the device: they must equal the oracle's
@@ -315,25 +358,30 @@ def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096, tile=None):
         assert np.array_equal(sa_h.view(np.uint32), so.view(np.uint32))
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", CONFIGS["tiny"] + CONFIGS["decode"])
-def test_config_tiny_and_decode(bfq, orc, M, N, K):
-    print(f"config M={M} N={N} K={K}", flush=True)
-    _sampled_check(bfq, orc, M, N, K, 128 if M > 8 or N != 1536 or K != 1536 else 8, "fp8")
+def test_config_tiny_and_decode(bfq, orc, M, N, K, layout):
+    print(f"config M={M} N={N} K={K} {layout}", flush=True)
+    _sampled_check(bfq, orc, M, N, K, 128 if M > 8 or N != 1536 or K != 1536 else 8, "fp8",
+                   layout=layout)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", CONFIGS["mgrid"])
-def test_config_mgrid(bfq, orc, M, N, K):
-    print(f"config M={M} N={N} K={K}", flush=True)
-    _sampled_check(bfq, orc, M, N, K, 4096, "fp8")
+def test_config_mgrid(bfq, orc, M, N, K, layout):
+    print(f"config M={M} N={N} K={K} {layout}", flush=True)
+    _sampled_check(bfq, orc, M, N, K, 4096, "fp8", layout=layout)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", CONFIGS["dense"])
-def test_config_dense(bfq, orc, M, N, K):
-    print(f"config M={M} N={N} K={K}", flush=True)
-    _sampled_check(bfq, orc, M, N, K, 4096, "fp8")
+def test_config_dense(bfq, orc, M, N, K, layout):
+    print(f"config M={M} N={N} K={K} {layout}", flush=True)
+    _sampled_check(bfq, orc, M, N, K, 4096, "fp8", layout=layout)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("M", [1, 16, 128, 1024, 4096])
-def test_config_int8(bfq, orc, M):
-    print(f"config int8 M={M}", flush=True)
-    _sampled_check(bfq, orc, M, 1536, 7168, 4096, "int8")
+def test_config_int8(bfq, orc, M, layout):
+    print(f"config int8 M={M} {layout}", flush=True)
+    _sampled_check(bfq, orc, M, 1536, 7168, 4096, "int8", layout=layout)

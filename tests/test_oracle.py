@@ -330,3 +330,44 @@ def test_nearest_m_rule_pages_examples():
     g = json.load(open(os.path.join(GOLDEN, "nearest_m.json")))
     for m, want in g["examples"] + g["ties"] + g["ends"]:
         assert nearest_bucket(m, g["grid"]) == want, (m, want)
+
+
+# ------------------------------------------------------------------ packed weight layout
+
+def test_pack16_is_the_stated_byte_map(orc):
+    """The packed 16-row fragment layout, read back byte by byte with a plain loop that
+    decodes each destination offset (fragment, half, lane, byte) into a source row and
+    column, agrees with the vectorized oracle on a shape with several fragments per row
+    group and several row groups."""
+    N, K = 48, 384
+    rng = np.random.default_rng(7)
+    w = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    p = orc.pack16(w).ravel()
+    KB = K // 128
+    for d in range(N * K):
+        frag, within = divmod(d, 2048)
+        f, kb = divmod(frag, KB)
+        h, rest = divmod(within, 1024)
+        lane, b = divmod(rest, 16)
+        assert p[d] == w[16 * f + lane % 16, 128 * kb + 64 * h + 16 * (lane // 16) + b], d
+
+
+def test_pack16_permutation_and_fragment_contents(orc):
+    """pack16 applied to an array of source positions is a permutation of them; every 2 KB
+    fragment holds exactly one 16-row x 128-column block; and each lane's two 16-byte slots
+    (one per half) come from a single row — the row the lane feeds to a 16-row MFMA."""
+    N, K = 64, 512
+    KB = K // 128
+    pos = np.arange(N * K, dtype=np.int64).reshape(N, K)
+    p = orc.pack16(pos).ravel()
+    assert np.array_equal(np.sort(p), np.arange(N * K))
+    rows, cols = p // K, p % K
+    for frag in range(N * K // 2048):
+        f, kb = divmod(frag, KB)
+        sl = slice(frag * 2048, (frag + 1) * 2048)
+        assert set(rows[sl]) == set(range(16 * f, 16 * f + 16))
+        assert set(cols[sl]) == set(range(128 * kb, 128 * kb + 128))
+        for lane in range(64):
+            a = frag * 2048 + 16 * lane
+            lane_rows = np.concatenate([rows[a:a + 16], rows[a + 1024:a + 1040]])
+            assert np.all(lane_rows == 16 * f + lane % 16)
