@@ -124,27 +124,18 @@ def run_gpu(args, wl):
 
     launch_counter = [0]
 
-    def one_step(events=None):
+    def one_step():
         for sh in shapes:
-            N, K = sh["N"], sh["K"]
             for (M, tile, ws_bytes, _st) in sh["plans"]:
                 qw, sw = sh["copies"][launch_counter[0] % len(sh["copies"])]
                 launch_counter[0] += 1
-                if events is not None:
-                    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-                    e0.record()
                 lay = bfq.BFQ_SCALES_COL_MAJOR if col else bfq.BFQ_SCALES_ROW_MAJOR
                 sa_m = sh["sa"] if col else sh["sa"][:M]
                 bfq.bfq_quant_tokens(sh["xd"][:M], sh["qa"][:M], sa_m, layout=lay,
                                      scale_ld=sh["sa"].stride(0))
-                if events is not None:
-                    e1.record()
                 bfq.bfq_block_gemm(sh["qa"][:M], sa_m, qw, sw, sh["out"][:M], a_layout=lay,
                                    a_scale_ld=sh["sa"].stride(0), tile=tile, workspace=sh["ws"],
                                    workspace_bytes=sh["ws_max"], w_layout=wlay)
-                if events is not None:
-                    e2.record()
-                    events.append((N, K, M, tile_key(tile), e0, e1, e2))
 
     for _ in range(args.warmup):
         one_step()
@@ -178,33 +169,52 @@ def run_gpu(args, wl):
         if not torch.equal(sh["out"], ref):
             raise RuntimeError("graph replay output differs from the eager step")
 
-    # Per-launch durations: HIP events around every launch on the launch stream. A spin
-    # kernel holds the stream while the host enqueues the step, so the events time the
-    # kernels back to back rather than the host's launch cadence.
-    spin_ratio = None
-    if hasattr(torch.cuda, "_sleep"):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        torch.cuda._sleep(1_000_000)
-        b.record()
-        torch.cuda.synchronize()
-        spin_ratio = a.elapsed_time(b) * 1e-3 / 1_000_000      # seconds per spin cycle
-    events = []
-    enqueue_s = 0.002
-    for _ in range(args.steps):
-        torch.cuda.synchronize()
-        if spin_ratio:
-            torch.cuda._sleep(int(2.0 * enqueue_s / spin_ratio))
-        h0 = time.perf_counter()
-        one_step(events)
-        enqueue_s = max(enqueue_s, time.perf_counter() - h0)
-    torch.cuda.synchronize()
-
+    # Per-launch durations, per M: R back-to-back launches of the quantizer, then of the GEMM
+    # (rotating the weight copies as the step does), each captured in a graph and replayed
+    # between two HIP events on the stream the kernels run on; duration = elapsed / R. A
+    # single launch bracketed by events would add the event overhead (several us) to
+    # kernels of ~30 us.
+    stream = torch.cuda.current_stream()
+    lay = bfq.BFQ_SCALES_COL_MAJOR if col else bfq.BFQ_SCALES_ROW_MAJOR
+    R = args.launch_reps
     per = {}
-    for (N, K, M, key, e0, e1, e2) in events:
-        r = per.setdefault((N, K, M), {"key": key, "q": [], "g": []})
-        r["q"].append(e0.elapsed_time(e1) * 1e-3)
-        r["g"].append(e1.elapsed_time(e2) * 1e-3)
+    for sh in shapes:
+        N, K = sh["N"], sh["K"]
+        sa_all = sh["sa"]
+        for (M, tile, ws_bytes, _st) in sh["plans"]:
+            sa_m = sa_all if col else sa_all[:M]
+
+            def q_once():
+                bfq.bfq_quant_tokens(sh["xd"][:M], sh["qa"][:M], sa_m, layout=lay,
+                                     scale_ld=sa_all.stride(0))
+
+            def g_once(i):
+                qw, sw = sh["copies"][i % len(sh["copies"])]
+                bfq.bfq_block_gemm(sh["qa"][:M], sa_m, qw, sw, sh["out"][:M], a_layout=lay,
+                                   a_scale_ld=sa_all.stride(0), tile=tile, workspace=sh["ws"],
+                                   workspace_bytes=sh["ws_max"], w_layout=wlay)
+
+            res = {}
+            for name, fn in (("q", lambda i: q_once()), ("g", g_once)):
+                fn(0)
+                torch.cuda.synchronize()
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    for i in range(R):
+                        fn(i)
+                gr.replay()                          # warm
+                torch.cuda.synchronize()
+                vals = []
+                for _ in range(args.launch_rounds):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    gr.replay()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    vals.append(e0.elapsed_time(e1) * 1e-3 / R)
+                del gr
+                res[name] = vals
+            per[(N, K, M)] = {"key": tile_key(tile), "q": res["q"], "g": res["g"]}
 
     flops_step = sum(perf.gemm_flops(M, sh["N"], sh["K"]) for sh in shapes
                      for (M, *_r) in sh["plans"])
@@ -231,10 +241,10 @@ def run_gpu(args, wl):
                                               "name": kernel_name(tile, wl["qtype"], wlay),
                                               "grids": set()})
             gr["grids"].add(grid_threads(tile, M, N))
-            gr["t"] += sum(r["g"])
-            gr["n"] += len(r["g"])
-            gr["flops"] += perf.gemm_flops(M, N, K) * len(r["g"])
-            gr["bytes"] += perf.gemm_bytes_all(M, N, K) * len(r["g"])
+            gr["t"] += sum(r["g"]) * R
+            gr["n"] += len(r["g"]) * R
+            gr["flops"] += perf.gemm_flops(M, N, K) * len(r["g"]) * R
+            gr["bytes"] += perf.gemm_bytes_all(M, N, K) * len(r["g"]) * R
     dom_key = max(groups, key=lambda k: groups[k]["t"])
     dom = groups[dom_key]
     t_flop = dom["flops"] / (perf.FP8_PEAK_TFLOPS * 1e12)
@@ -317,6 +327,9 @@ def main():
     ap.add_argument("--workload", default="mgrid", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=3, help="weight copies rotated per launch")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--launch-reps", type=int, default=20,
+                    help="back-to-back launches per graph when timing one kernel")
+    ap.add_argument("--launch-rounds", type=int, default=3, help="graph replays per kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--scale-layout", default="col", choices=["row", "col"],
