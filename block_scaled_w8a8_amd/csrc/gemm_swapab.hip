@@ -482,6 +482,12 @@ static const KernelEntry kSwapabKernels[] = {
     BFQ_SABL_BOTH(96, 16, 6, 1, 4, Q_FP8),
     BFQ_SABL_BOTH(128, 16, 8, 1, 4, Q_FP8),
     BFQ_SABL_BOTH(128, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(32, 16, 6, 1, 8, Q_FP8),
+    BFQ_SABL_BOTH(32, 16, 6, 2, 4, Q_FP8),
+    BFQ_SABL_BOTH(64, 16, 6, 1, 8, Q_FP8),
+    BFQ_SABL_BOTH(64, 16, 6, 2, 4, Q_FP8),
+    BFQ_SABL_BOTH(96, 16, 6, 2, 4, Q_FP8),
+    BFQ_SABL_BOTH(128, 16, 6, 2, 4, Q_FP8),
     BFQ_SABL_BOTH(16, 16, 8, 1, 8, Q_INT8),
     BFQ_SABL_BOTH(32, 16, 8, 1, 4, Q_INT8),
     BFQ_SABL_BOTH(64, 16, 8, 1, 4, Q_INT8),
