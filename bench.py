@@ -88,6 +88,7 @@ def run_gpu(args, wl):
     dev = torch.device("cuda:0")
     qd = bfq.BFQ_E4M3FN if wl["qtype"] == "fp8" else bfq.BFQ_INT8
     wlay = bfq.BFQ_W_PACKED16 if args.w_layout == "packed" else bfq.BFQ_W_ROW_MAJOR
+    sfmt = bfq.BFQ_SCALE_UE8M0 if args.scales == "ue8m0" else bfq.BFQ_SCALE_FP32
     m_max = max(wl["M"])
     col = args.scale_layout == "col"
     shapes = []
@@ -99,7 +100,7 @@ def run_gpu(args, wl):
         wd = w.to(dev)
         copies = []
         for r in range(args.rotate):
-            qw, sw = bfq.quant_weight_blocks(wd, q_dtype=qd)
+            qw, sw = bfq.quant_weight_blocks(wd, q_dtype=qd, scale_fmt=sfmt)
             if wlay == bfq.BFQ_W_PACKED16:        # offline layout step, like the quantization
                 qw = bfq.pack_weights(qw)
             copies.append((qw, sw))
@@ -112,7 +113,8 @@ def run_gpu(args, wl):
         out = torch.empty((m_max, N), dtype=torch.bfloat16, device=dev)
         plans = []
         for M in wl["M"]:
-            st, tile = bfq.bfq_select_tile(M, N, K, qd, bfq.BFQ_BF16, w_layout=wlay)
+            st, tile = bfq.bfq_select_tile(M, N, K, qd, bfq.BFQ_BF16, w_layout=wlay,
+                                           scale_fmt=sfmt)
             ws_bytes = bfq.bfq_gemm_workspace_bytes(M, N, K, tile)
             plans.append((M, tile, ws_bytes, st))
         ws_max = max(p[2] for p in plans)
@@ -132,10 +134,10 @@ def run_gpu(args, wl):
                 lay = bfq.BFQ_SCALES_COL_MAJOR if col else bfq.BFQ_SCALES_ROW_MAJOR
                 sa_m = sh["sa"] if col else sh["sa"][:M]
                 bfq.bfq_quant_tokens(sh["xd"][:M], sh["qa"][:M], sa_m, layout=lay,
-                                     scale_ld=sh["sa"].stride(0))
+                                     scale_ld=sh["sa"].stride(0), scale_fmt=sfmt)
                 bfq.bfq_block_gemm(sh["qa"][:M], sa_m, qw, sw, sh["out"][:M], a_layout=lay,
                                    a_scale_ld=sh["sa"].stride(0), tile=tile, workspace=sh["ws"],
-                                   workspace_bytes=sh["ws_max"], w_layout=wlay)
+                                   workspace_bytes=sh["ws_max"], w_layout=wlay, scale_fmt=sfmt)
 
     for _ in range(args.warmup):
         one_step()
@@ -186,13 +188,13 @@ def run_gpu(args, wl):
 
             def q_once():
                 bfq.bfq_quant_tokens(sh["xd"][:M], sh["qa"][:M], sa_m, layout=lay,
-                                     scale_ld=sa_all.stride(0))
+                                     scale_ld=sa_all.stride(0), scale_fmt=sfmt)
 
             def g_once(i):
                 qw, sw = sh["copies"][i % len(sh["copies"])]
                 bfq.bfq_block_gemm(sh["qa"][:M], sa_m, qw, sw, sh["out"][:M], a_layout=lay,
                                    a_scale_ld=sa_all.stride(0), tile=tile, workspace=sh["ws"],
-                                   workspace_bytes=sh["ws_max"], w_layout=wlay)
+                                   workspace_bytes=sh["ws_max"], w_layout=wlay, scale_fmt=sfmt)
 
             res = {}
             for name, fn in (("q", lambda i: q_once()), ("g", g_once)):
@@ -288,7 +290,7 @@ def traffic_for(args, dom, wl):
     return float(t["hbm_bytes_per_dispatch"])
 
 
-def cpu_baseline(wl, host, target_s: float):
+def cpu_baseline(wl, host, target_s: float, scales: str = "fp32"):
     """The CPU oracle, as it stands, on a bounded sample of the same workload: the
     quantization and GEMM of a few token rows of the largest M against the full weights."""
     import numpy as np
@@ -299,13 +301,14 @@ def cpu_baseline(wl, host, target_s: float):
     qt = oracle.FP8 if wl["qtype"] == "fp8" else oracle.INT8
     (N, K) = wl["shapes"][0]
     w, x = host[(N, K)]
+    sf = oracle.SCALE_UE8M0 if scales == "ue8m0" else oracle.SCALE_FP32
     log(f"[bench] cpu baseline: oracle weight quantization N={N} K={K} (untimed)")
-    qw, sw = oracle.quant_blocks(w.numpy(), qtype=qt)
+    qw, sw = oracle.quant_blocks(w.numpy(), qtype=qt, scale_fmt=sf)
     xb = synth.bf16_bits(x)
 
     def run(rows):
         t0 = time.perf_counter()
-        qa, sa = oracle.quant_groups(np.ascontiguousarray(xb[:rows]), qtype=qt)
+        qa, sa = oracle.quant_groups(np.ascontiguousarray(xb[:rows]), qtype=qt, scale_fmt=sf)
         oracle.block_gemm(qa, sa, qw, sw, qtype=qt)
         return time.perf_counter() - t0
 
@@ -334,6 +337,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--scale-layout", default="col", choices=["row", "col"],
                     help="activation-scale layout written by the quantizer and read by the GEMM")
+    ap.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0"],
+                    help="block scale format: fp32 amax/Qmax (default), or rounded up to a "
+                         "power of two (UE8M0)")
     ap.add_argument("--w-layout", default="packed", choices=["row", "packed"],
                     help="weight-code layout in HBM (packed: bfq_pack_weights, done offline)")
     args = ap.parse_args()
@@ -346,7 +352,7 @@ def main():
     res = run_gpu(args, wl)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, res["host"], args.cpu_seconds)
+        cpu = cpu_baseline(wl, res["host"], args.cpu_seconds, args.scales)
     line = {
         "metric": METRIC,
         "value": round(res["value"], 3),
@@ -364,7 +370,8 @@ def main():
                    "block_shape": [128, 128], "out_dtype": "bf16",
                    "weight_copies_rotated": args.rotate,
                    "activation_scale_layout": args.scale_layout + "_major",
-                   "weight_layout": "packed16" if args.w_layout == "packed" else "row_major"},
+                   "weight_layout": "packed16" if args.w_layout == "packed" else "row_major",
+                   "scales": args.scales},
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "per_m": res["rows"],

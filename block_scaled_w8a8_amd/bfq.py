@@ -33,6 +33,9 @@ BFQ_SCALES_COL_MAJOR = 1
 # weight-code layouts (bfq_weight_layout)
 BFQ_W_ROW_MAJOR = 0
 BFQ_W_PACKED16 = 1
+# scale formats (bfq_scale_format)
+BFQ_SCALE_FP32 = 0
+BFQ_SCALE_UE8M0 = 1
 
 DEFAULT_EPS = 1e-10
 BLOCK_SHAPE = (128, 128)
@@ -90,16 +93,16 @@ def _load():
     tp = ctypes.POINTER(bfq_tile)
     bs = ctypes.POINTER(ctypes.c_int32)
     sig = {
-        "bfq_quant_tokens": (i32, [p, i64, i64, i32, i32, p, p, i32, i64, f32, p]),
-        "bfq_quant_weight_blocks": (i32, [p, i64, i64, bs, i32, p, p, f32, p]),
+        "bfq_quant_tokens": (i32, [p, i64, i64, i32, i32, p, p, i32, i64, f32, i32, p]),
+        "bfq_quant_weight_blocks": (i32, [p, i64, i64, bs, i32, p, p, f32, i32, p]),
         "bfq_pack_weights": (i32, [p, i64, i64, i32, p, p]),
-        "bfq_select_tile": (i32, [i64, i64, i64, bs, i32, i32, i32, tp]),
+        "bfq_select_tile": (i32, [i64, i64, i64, bs, i32, i32, i32, i32, tp]),
         "bfq_gemm_workspace_bytes": (sz, [i64, i64, i64, tp]),
-        "bfq_block_gemm": (i32, [p, p, i32, i64, p, p, i32, p, i64, i64, i64, bs, i32, i32, tp,
-                                 p, sz, p]),
+        "bfq_block_gemm": (i32, [p, p, i32, i64, p, p, i32, i32, p, i64, i64, i64, bs, i32, i32,
+                                 tp, p, sz, p]),
         "bfq_load_tile_table": (i32, [ctypes.c_char_p]),
-        "bfq_num_tile_candidates": (i32, [i32, i32]),
-        "bfq_get_tile_candidate": (i32, [i32, i32, i32, tp]),
+        "bfq_num_tile_candidates": (i32, [i32, i32, i32]),
+        "bfq_get_tile_candidate": (i32, [i32, i32, i32, i32, tp]),
         "bfq_status_string": (ctypes.c_char_p, [i32]),
         "bfq_last_error": (ctypes.c_char_p, []),
         "bfq_debug_block_partials_i32": (i32, [p, p, p, i64, i64, i64, p]),
@@ -172,23 +175,24 @@ def _odtype(t) -> int:
 # ----------------------------------------------------------------------- entry points
 
 def bfq_quant_tokens(x, q, scales, layout=BFQ_SCALES_ROW_MAJOR, scale_ld=None,
-                     eps=DEFAULT_EPS, group_size=128, stream=None) -> int:
+                     eps=DEFAULT_EPS, group_size=128, stream=None,
+                     scale_fmt=BFQ_SCALE_FP32) -> int:
     """x: bf16 [M, K]; q: uint8/float8_e4m3fn (e4m3fn codes) or int8 [M, K];
     scales: fp32, [M, ld] (row-major) or [K/128, ld] (column-major)."""
     M, K = x.shape
     if scale_ld is None:
         scale_ld = scales.stride(0)
     st = lib.bfq_quant_tokens(_ptr(x), M, K, group_size, _qdtype(q), _ptr(q), _ptr(scales),
-                              layout, scale_ld, eps, _stream(stream))
+                              layout, scale_ld, eps, scale_fmt, _stream(stream))
     return _check(st, "bfq_quant_tokens")
 
 
 def bfq_quant_weight_blocks(w, q, scales, eps=DEFAULT_EPS, block_shape=BLOCK_SHAPE,
-                            stream=None) -> int:
+                            stream=None, scale_fmt=BFQ_SCALE_FP32) -> int:
     """w: fp32 [N, K]; q: codes [N, K]; scales: fp32 [N/128, K/128]."""
     N, K = w.shape
     st = lib.bfq_quant_weight_blocks(_ptr(w), N, K, _block_shape(block_shape), _qdtype(q),
-                                     _ptr(q), _ptr(scales), eps, _stream(stream))
+                                     _ptr(q), _ptr(scales), eps, scale_fmt, _stream(stream))
     return _check(st, "bfq_quant_weight_blocks")
 
 
@@ -203,11 +207,11 @@ def bfq_pack_weights(w_q, w_packed, stream=None) -> int:
 
 
 def bfq_select_tile(M, N, K, in_dtype=BFQ_E4M3FN, out_dtype=BFQ_BF16,
-                    block_shape=BLOCK_SHAPE, w_layout=BFQ_W_ROW_MAJOR):
+                    block_shape=BLOCK_SHAPE, w_layout=BFQ_W_ROW_MAJOR, scale_fmt=BFQ_SCALE_FP32):
     """Returns (status, bfq_tile)."""
     t = bfq_tile()
     st = lib.bfq_select_tile(M, N, K, _block_shape(block_shape), in_dtype, out_dtype,
-                             w_layout, ctypes.byref(t))
+                             w_layout, scale_fmt, ctypes.byref(t))
     if st < 0:
         raise BfqError(st, "bfq_select_tile")
     return st, t
@@ -219,10 +223,12 @@ def bfq_gemm_workspace_bytes(M, N, K, tile=None) -> int:
 
 def bfq_block_gemm(a_q, a_scales, w_q, w_scales, out, a_layout=BFQ_SCALES_ROW_MAJOR,
                    a_scale_ld=None, tile=None, workspace=None, workspace_bytes=None,
-                   block_shape=BLOCK_SHAPE, stream=None, w_layout=BFQ_W_ROW_MAJOR) -> int:
+                   block_shape=BLOCK_SHAPE, stream=None, w_layout=BFQ_W_ROW_MAJOR,
+                   scale_fmt=BFQ_SCALE_FP32) -> int:
     """a_q [M, K] codes, w_q [N, K] codes in w_layout (row-major, or packed by
     bfq_pack_weights and still shaped [N, K]), a_scales per layout, w_scales [N/128, K/128],
-    out [M, N] (bf16 / fp16 / fp32). Returns the status (>= 0)."""
+    out [M, N] (bf16 / fp16 / fp32). scale_fmt BFQ_SCALE_UE8M0 declares every scale a power
+    of two. Returns the status (>= 0)."""
     M, K = a_q.shape
     N = w_q.shape[0]
     if a_scale_ld is None:
@@ -230,7 +236,8 @@ def bfq_block_gemm(a_q, a_scales, w_q, w_scales, out, a_layout=BFQ_SCALES_ROW_MA
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.bfq_block_gemm(_ptr(a_q), _ptr(a_scales), a_layout, a_scale_ld, _ptr(w_q),
-                            _ptr(w_scales), w_layout, _ptr(out), M, N, K, _block_shape(block_shape),
+                            _ptr(w_scales), w_layout, scale_fmt, _ptr(out), M, N, K,
+                            _block_shape(block_shape),
                             _qdtype(a_q), _odtype(out), ctypes.byref(tile) if tile else None,
                             _ptr(workspace), workspace_bytes, _stream(stream))
     return _check(st, "bfq_block_gemm", warn_key=(N, K))
@@ -241,13 +248,15 @@ def bfq_load_tile_table(path=None) -> int:
     return _check(st, "bfq_load_tile_table")
 
 
-def bfq_num_tile_candidates(in_dtype=BFQ_E4M3FN, w_layout=BFQ_W_ROW_MAJOR) -> int:
-    return int(lib.bfq_num_tile_candidates(in_dtype, w_layout))
+def bfq_num_tile_candidates(in_dtype=BFQ_E4M3FN, w_layout=BFQ_W_ROW_MAJOR,
+                            scale_fmt=BFQ_SCALE_FP32) -> int:
+    return int(lib.bfq_num_tile_candidates(in_dtype, w_layout, scale_fmt))
 
 
-def bfq_get_tile_candidate(index, in_dtype=BFQ_E4M3FN, w_layout=BFQ_W_ROW_MAJOR) -> bfq_tile:
+def bfq_get_tile_candidate(index, in_dtype=BFQ_E4M3FN, w_layout=BFQ_W_ROW_MAJOR,
+                           scale_fmt=BFQ_SCALE_FP32) -> bfq_tile:
     t = bfq_tile()
-    _check(lib.bfq_get_tile_candidate(in_dtype, w_layout, index, ctypes.byref(t)),
+    _check(lib.bfq_get_tile_candidate(in_dtype, w_layout, scale_fmt, index, ctypes.byref(t)),
            "bfq_get_tile_candidate")
     return t
 
@@ -276,7 +285,7 @@ def bfq_debug_encode(x, codes, q_dtype=BFQ_E4M3FN, stream=None) -> int:
 # ------------------------------------------------------------ allocating conveniences
 
 def quant_tokens(x, q_dtype=BFQ_E4M3FN, layout=BFQ_SCALES_ROW_MAJOR, eps=DEFAULT_EPS,
-                 stream=None):
+                 stream=None, scale_fmt=BFQ_SCALE_FP32):
     """Allocate (q, scales) with torch and run bfq_quant_tokens. Returns (q, scales)."""
     import torch
     M, K = x.shape
@@ -286,17 +295,19 @@ def quant_tokens(x, q_dtype=BFQ_E4M3FN, layout=BFQ_SCALES_ROW_MAJOR, eps=DEFAULT
         s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
     else:
         s = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
-    bfq_quant_tokens(x, q, s, layout=layout, scale_ld=s.stride(0), eps=eps, stream=stream)
+    bfq_quant_tokens(x, q, s, layout=layout, scale_ld=s.stride(0), eps=eps, stream=stream,
+                     scale_fmt=scale_fmt)
     return q, s
 
 
-def quant_weight_blocks(w, q_dtype=BFQ_E4M3FN, eps=DEFAULT_EPS, stream=None):
+def quant_weight_blocks(w, q_dtype=BFQ_E4M3FN, eps=DEFAULT_EPS, stream=None,
+                        scale_fmt=BFQ_SCALE_FP32):
     import torch
     N, K = w.shape
     q = torch.empty((N, K), dtype=torch.uint8 if q_dtype == BFQ_E4M3FN else torch.int8,
                     device=w.device)
     s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
-    bfq_quant_weight_blocks(w, q, s, eps=eps, stream=stream)
+    bfq_quant_weight_blocks(w, q, s, eps=eps, stream=stream, scale_fmt=scale_fmt)
     return q, s
 
 
@@ -310,7 +321,7 @@ def pack_weights(w_q, stream=None):
 
 
 def block_gemm(a_q, a_scales, w_q, w_scales, out_dtype=None, a_layout=BFQ_SCALES_ROW_MAJOR,
-               tile=None, stream=None, w_layout=BFQ_W_ROW_MAJOR):
+               tile=None, stream=None, w_layout=BFQ_W_ROW_MAJOR, scale_fmt=BFQ_SCALE_FP32):
     """Allocate out (and split-K workspace) with torch and run bfq_block_gemm."""
     import torch
     out_dtype = out_dtype or torch.bfloat16
@@ -318,10 +329,12 @@ def block_gemm(a_q, a_scales, w_q, w_scales, out_dtype=None, a_layout=BFQ_SCALES
     N = w_q.shape[0]
     out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
     if tile is None:
-        st, tile = bfq_select_tile(M, N, K, _qdtype(a_q), _odtype(out), w_layout=w_layout)
+        st, tile = bfq_select_tile(M, N, K, _qdtype(a_q), _odtype(out), w_layout=w_layout,
+                                   scale_fmt=scale_fmt)
         _check(st, "bfq_select_tile", warn_key=(N, K))
     ws_bytes = bfq_gemm_workspace_bytes(M, N, K, tile)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=a_q.device) if ws_bytes else None
     bfq_block_gemm(a_q, a_scales, w_q, w_scales, out, a_layout=a_layout, tile=tile,
-                   workspace=ws, workspace_bytes=ws_bytes, stream=stream, w_layout=w_layout)
+                   workspace=ws, workspace_bytes=ws_bytes, stream=stream, w_layout=w_layout,
+                   scale_fmt=scale_fmt)
     return out

@@ -60,13 +60,13 @@ bool read_file(const std::string& path, std::string& text) {
     return true;
 }
 
-const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype, int wlayout);
+const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype, int wlayout, int sfmt);
 
 // Every table tile must name a compiled kernel; otherwise the table is rejected.
 bool validate_table(const TileTable& t, std::string& err) {
     for (auto& e : t.entries)
         for (auto& b : e.second) {
-            if (!find_kernel(b.second, e.first.qtype, O_BF16, e.first.wlayout)) {
+            if (!find_kernel(b.second, e.first.qtype, O_BF16, e.first.wlayout, e.first.sfmt)) {
                 err = "table entry N=" + std::to_string(e.first.N) + " K=" +
                       std::to_string(e.first.K) + " M=" + std::to_string(b.first) +
                       " names a tile that is not compiled";
@@ -114,7 +114,11 @@ bool same_shape(const bfq_tile& a, const bfq_tile& b) {
     return a.sched == b.sched;
 }
 
-const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype, int wlayout) {
+// A kernel serves scale format sfmt if it takes any fp32 scales (S_FP32) or if the scales are
+// declared powers of two (a S_UE8M0 kernel applies them inside the MFMA).
+bool serves(const KernelEntry& k, int sfmt) { return k.sfmt == S_FP32 || sfmt == S_UE8M0; }
+
+const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype, int wlayout, int sfmt) {
     if (t.bk != 0 && t.bk != 128) return nullptr;
     int n = 0;
     const KernelEntry* list = t.variant == 0   ? std_kernels(&n)
@@ -123,7 +127,7 @@ const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype, int wlay
                                                : nullptr;
     for (int i = 0; list && i < n; ++i)
         if (list[i].qtype == qtype && list[i].otype == otype && list[i].wlayout == wlayout &&
-            same_shape(list[i].tile, t))
+            serves(list[i], sfmt) && same_shape(list[i].tile, t))
             return &list[i];
     return nullptr;
 }
@@ -136,7 +140,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // tokens the swap-AB streaming kernel ([HELION]: the Hopper rule dispatches swap-AB for
 // M < 32), else the standard kernel with the largest tile that still yields one workgroup
 // per CU. Split-K is added until the grid covers the CUs, keeping >= 4 K blocks per split.
-bfq_tile default_tile(int64_t M, int64_t N, int64_t K) {
+bfq_tile default_tile(int64_t M, int64_t N, int64_t K, int qtype, int sfmt) {
     const int64_t KB = K / 128;
     bfq_tile t{};
     t.bk = 128;
@@ -163,6 +167,8 @@ bfq_tile default_tile(int64_t M, int64_t N, int64_t K) {
         t.waves_n = shapes[pick][3];
         t.stages = 2;
         t.group_m = 8;
+        // power-of-two fp8 scales: the block-scaled MFMA schedule where it is compiled
+        t.sched = (qtype == Q_FP8 && sfmt == S_UE8M0 && pick < 3) ? 3 : 0;
         ctas = ceil_div(M, t.bm) * ceil_div(N, t.bn);
     }
     while (ctas * t.split_k < kNumCUs && KB / (t.split_k * 2) >= 4) t.split_k *= 2;
@@ -173,27 +179,30 @@ int qtype_of(bfq_dtype d) { return d == BFQ_E4M3FN ? Q_FP8 : Q_INT8; }
 
 int otype_of(bfq_dtype d) { return d == BFQ_BF16 ? O_BF16 : d == BFQ_FP16 ? O_FP16 : O_FP32; }
 
-bfq_status select_tile(int64_t M, int64_t N, int64_t K, int qtype, int wlayout, bfq_tile* out) {
+bfq_status select_tile(int64_t M, int64_t N, int64_t K, int qtype, int wlayout, int sfmt,
+                       bfq_tile* out) {
     ensure_table();
     {
         std::lock_guard<std::mutex> lk(g_table_mu);
-        auto it = g_table.entries.find(TableKey{N, K, qtype, wlayout});
+        auto it = g_table.entries.find(TableKey{N, K, qtype, wlayout, sfmt});
         if (it != g_table.entries.end()) {
             *out = it->second.at(nearest_bucket(it->second, M));
             out->bk = 128;
             return BFQ_OK;
         }
     }
-    *out = default_tile(M, N, K);
+    *out = default_tile(M, N, K, qtype, sfmt);
     if (std::getenv("BFQ_LOG"))
-        std::fprintf(stderr, "[bfq] no tuned entry for N=%lld K=%lld layout=%d; using default tile\n",
-                     (long long)N, (long long)K, wlayout);
+        std::fprintf(stderr, "[bfq] no tuned entry for N=%lld K=%lld layout=%d scales=%d; using default tile\n",
+                     (long long)N, (long long)K, wlayout, sfmt);
     return BFQ_WARN_DEFAULT_TILE;
 }
 
 bool block_shape_ok(const int32_t* bs) { return bs && bs[0] == 128 && bs[1] == 128; }
 
 bool wlayout_ok(bfq_weight_layout w) { return w == BFQ_W_ROW_MAJOR || w == BFQ_W_PACKED16; }
+
+bool sfmt_ok(bfq_scale_format f) { return f == BFQ_SCALE_FP32 || f == BFQ_SCALE_UE8M0; }
 
 size_t workspace_for(int64_t M, int64_t N, const bfq_tile& t) {
     if (t.variant == 2) {
@@ -230,7 +239,8 @@ const char* bfq_last_error(void) { return g_last_error.c_str(); }
 
 bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t group_size,
                             bfq_dtype q_dtype, void* q, float* scales, bfq_scale_layout layout,
-                            int64_t scale_ld, float eps, void* stream) {
+                            int64_t scale_ld, float eps, bfq_scale_format scale_fmt,
+                            void* stream) {
     if (M != 0 && (!x_bf16 || !q || !scales))
         return fail(BFQ_ERR_NULL, "x, q and scales must be non-NULL");
     if (q_dtype != BFQ_E4M3FN && q_dtype != BFQ_INT8)
@@ -242,6 +252,7 @@ bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t gr
     if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(scales, 4))
         return fail(BFQ_ERR_ALIGN, "x and q must be 16-byte aligned, scales 4-byte aligned");
     if (!(eps > 0.0f) || eps > 3.0e38f) return fail(BFQ_ERR_ARG, "eps must be positive and finite");
+    if (!sfmt_ok(scale_fmt)) return fail(BFQ_ERR_ARG, "unknown scale format");
     const int64_t G = K / 128;
     int64_t sm, sg;
     if (layout == BFQ_SCALES_ROW_MAJOR) {
@@ -255,14 +266,15 @@ bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t gr
     }
     if (M == 0) return BFQ_OK;
     hipError_t e = launch_quant_tokens(x_bf16, q, scales, M, K, qtype_of(q_dtype), sm, sg, eps,
-                                       (hipStream_t)stream);
+                                       (int)scale_fmt, (hipStream_t)stream);
     if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
     return BFQ_OK;
 }
 
 bfq_status bfq_quant_weight_blocks(const float* w, int64_t N, int64_t K,
                                    const int32_t block_shape[2], bfq_dtype q_dtype, void* q,
-                                   float* scales, float eps, void* stream) {
+                                   float* scales, float eps, bfq_scale_format scale_fmt,
+                                   void* stream) {
     if (!w || !q || !scales || !block_shape)
         return fail(BFQ_ERR_NULL, "w, q, scales and block_shape must be non-NULL");
     if (q_dtype != BFQ_E4M3FN && q_dtype != BFQ_INT8)
@@ -274,9 +286,10 @@ bfq_status bfq_quant_weight_blocks(const float* w, int64_t N, int64_t K,
     if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scales, 4))
         return fail(BFQ_ERR_ALIGN, "w and q must be 16-byte aligned, scales 4-byte aligned");
     if (!(eps > 0.0f) || eps > 3.0e38f) return fail(BFQ_ERR_ARG, "eps must be positive and finite");
+    if (!sfmt_ok(scale_fmt)) return fail(BFQ_ERR_ARG, "unknown scale format");
     if (N == 0 || K == 0) return BFQ_OK;
     hipError_t e = launch_quant_weight_blocks(w, q, scales, N, K, qtype_of(q_dtype), eps,
-                                              (hipStream_t)stream);
+                                              (int)scale_fmt, (hipStream_t)stream);
     if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
     return BFQ_OK;
 }
@@ -303,7 +316,7 @@ bfq_status bfq_pack_weights(const void* w_q, int64_t N, int64_t K, bfq_dtype q_d
 
 bfq_status bfq_select_tile(int64_t M, int64_t N, int64_t K, const int32_t block_shape[2],
                            bfq_dtype in_dtype, bfq_dtype out_dtype, bfq_weight_layout w_layout,
-                           bfq_tile* tile_out) {
+                           bfq_scale_format scale_fmt, bfq_tile* tile_out) {
     if (!tile_out || !block_shape) return fail(BFQ_ERR_NULL, "tile_out and block_shape must be non-NULL");
     if (!block_shape_ok(block_shape)) return fail(BFQ_ERR_SHAPE, "block_shape must be {128, 128}");
     if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8)
@@ -313,21 +326,22 @@ bfq_status bfq_select_tile(int64_t M, int64_t N, int64_t K, const int32_t block_
     if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
         return fail(BFQ_ERR_SHAPE, "need M >= 0 and N, K positive multiples of 128");
     if (!wlayout_ok(w_layout)) return fail(BFQ_ERR_ARG, "unknown weight layout");
-    return select_tile(M, N, K, qtype_of(in_dtype), (int)w_layout, tile_out);
+    if (!sfmt_ok(scale_fmt)) return fail(BFQ_ERR_ARG, "unknown scale format");
+    return select_tile(M, N, K, qtype_of(in_dtype), (int)w_layout, (int)scale_fmt, tile_out);
 }
 
 size_t bfq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const bfq_tile* tile) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
     bfq_tile t;
     if (tile) t = *tile;
-    else select_tile(M, N, K, Q_FP8, W_ROW, &t);
+    else select_tile(M, N, K, Q_FP8, W_ROW, S_FP32, &t);
     return workspace_for(M, N, t);
 }
 
 bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
                           int64_t a_scale_ld, const void* w_q, const float* w_scales,
-                          bfq_weight_layout w_layout, void* out, int64_t M, int64_t N, int64_t K,
-                          const int32_t block_shape[2],
+                          bfq_weight_layout w_layout, bfq_scale_format scale_fmt, void* out,
+                          int64_t M, int64_t N, int64_t K, const int32_t block_shape[2],
                           bfq_dtype in_dtype, bfq_dtype out_dtype, const bfq_tile* tile,
                           void* workspace, size_t workspace_bytes, void* stream) {
     if (!w_q || !w_scales || !block_shape || (M != 0 && (!a_q || !a_scales || !out)))
@@ -338,6 +352,7 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     if (out_dtype != BFQ_BF16 && out_dtype != BFQ_FP16 && out_dtype != BFQ_FP32)
         return fail(BFQ_ERR_DTYPE, "out_dtype must be BF16, FP16 or FP32");
     if (!wlayout_ok(w_layout)) return fail(BFQ_ERR_ARG, "unknown weight layout");
+    if (!sfmt_ok(scale_fmt)) return fail(BFQ_ERR_ARG, "unknown scale format");
     if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0)
         return fail(BFQ_ERR_SHAPE, "need M >= 0 and N, K positive multiples of 128");
     if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > (1 << 23))
@@ -362,16 +377,18 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     if ((255 * ssm + (KB - 1) * ssk + 1) * 4 >= (int64_t(1) << 32))
         return fail(BFQ_ERR_SHAPE, "activation scales of 256 tokens must span less than 4 GiB");
     const int qtype = qtype_of(in_dtype), otype = otype_of(out_dtype), wl = (int)w_layout;
+    const int sf = (int)scale_fmt;
     bfq_status status = BFQ_OK;
     bfq_tile t;
     if (tile) {
         t = *tile;
     } else {
-        status = select_tile(M, N, K, qtype, wl, &t);
+        status = select_tile(M, N, K, qtype, wl, sf, &t);
     }
-    const KernelEntry* ke = find_kernel(t, qtype, otype, wl);
+    const KernelEntry* ke = find_kernel(t, qtype, otype, wl, sf);
     if (!ke)
-        return fail(BFQ_ERR_TILE, "tile does not name a compiled kernel for this dtype pair and weight layout");
+        return fail(BFQ_ERR_TILE, "tile does not name a compiled kernel for this dtype pair, weight "
+                                  "layout and scale format");
     if (t.split_k < 1 || t.split_k > 256 || t.split_k > KB)
         return fail(BFQ_ERR_TILE, "split_k must be in [1, min(256, K/128)]");
     if (t.variant == 2 && t.split_k != 1)
@@ -424,30 +441,34 @@ bfq_status bfq_load_tile_table(const char* json_path) {
     return load_table_locked(json_path, true);
 }
 
-int32_t bfq_num_tile_candidates(bfq_dtype in_dtype, bfq_weight_layout w_layout) {
+int32_t bfq_num_tile_candidates(bfq_dtype in_dtype, bfq_weight_layout w_layout,
+                                bfq_scale_format scale_fmt) {
     if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8) return 0;
-    if (!wlayout_ok(w_layout)) return 0;
+    if (!wlayout_ok(w_layout) || !sfmt_ok(scale_fmt)) return 0;
     const int q = qtype_of(in_dtype), wl = (int)w_layout;
     int ns[3] = {0, 0, 0}, count = 0;
     const KernelEntry* lists[3] = {std_kernels(&ns[0]), swapab_kernels(&ns[1]), streamk_kernels(&ns[2])};
     for (int l = 0; l < 3; ++l)
         for (int i = 0; i < ns[l]; ++i)
-            count += (lists[l][i].qtype == q && lists[l][i].otype == O_BF16 && lists[l][i].wlayout == wl);
+            count += (lists[l][i].qtype == q && lists[l][i].otype == O_BF16 && lists[l][i].wlayout == wl &&
+                      serves(lists[l][i], (int)scale_fmt));
     return count;
 }
 
-bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, bfq_weight_layout w_layout, int32_t index,
-                                  bfq_tile* tile_out) {
+bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, bfq_weight_layout w_layout,
+                                  bfq_scale_format scale_fmt, int32_t index, bfq_tile* tile_out) {
     if (!tile_out) return fail(BFQ_ERR_NULL, "tile_out must be non-NULL");
     if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8)
         return fail(BFQ_ERR_DTYPE, "in_dtype must be BFQ_E4M3FN or BFQ_INT8");
     if (!wlayout_ok(w_layout)) return fail(BFQ_ERR_ARG, "unknown weight layout");
+    if (!sfmt_ok(scale_fmt)) return fail(BFQ_ERR_ARG, "unknown scale format");
     const int q = qtype_of(in_dtype), wl = (int)w_layout;
     int ns[3] = {0, 0, 0}, count = 0;
     const KernelEntry* lists[3] = {std_kernels(&ns[0]), swapab_kernels(&ns[1]), streamk_kernels(&ns[2])};
     for (int l = 0; l < 3; ++l)
         for (int i = 0; i < ns[l]; ++i) {
-            if (lists[l][i].qtype != q || lists[l][i].otype != O_BF16 || lists[l][i].wlayout != wl)
+            if (lists[l][i].qtype != q || lists[l][i].otype != O_BF16 || lists[l][i].wlayout != wl ||
+                !serves(lists[l][i], (int)scale_fmt))
                 continue;
             if (count == index) { *tile_out = lists[l][i].tile; return BFQ_OK; }
             ++count;

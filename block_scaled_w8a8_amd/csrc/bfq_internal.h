@@ -11,12 +11,14 @@ namespace bfq {
 enum QType { Q_FP8 = 0, Q_INT8 = 1 };
 enum OType { O_BF16 = 0, O_FP16 = 1, O_FP32 = 2 };
 enum WLayout { W_ROW = 0, W_PACKED16 = 1 };   // bfq_weight_layout
+enum ScaleFmt { S_FP32 = 0, S_UE8M0 = 1 };    // bfq_scale_format
 
 hipError_t launch_quant_tokens(const void* x, void* q, float* scales, int64_t M, int64_t K,
                                int qtype, int64_t s_stride_m, int64_t s_stride_g, float eps,
-                               hipStream_t stream);
+                               int sfmt, hipStream_t stream);
 hipError_t launch_quant_weight_blocks(const float* w, void* q, float* scales, int64_t N,
-                                      int64_t K, int qtype, float eps, hipStream_t stream);
+                                      int64_t K, int qtype, float eps, int sfmt,
+                                      hipStream_t stream);
 // Row-major [N][K] codes -> the packed 16-row fragment layout (BFQ_W_PACKED16).
 hipError_t launch_pack_weights(const void* w, void* packed, int64_t N, int64_t K,
                                hipStream_t stream);
@@ -50,6 +52,7 @@ struct KernelEntry {
     int qtype;              // Q_FP8 / Q_INT8
     int otype;              // O_BF16 / O_FP16 / O_FP32 (output of a split=1 launch)
     int wlayout;            // W_ROW / W_PACKED16: the weight layout the kernel reads
+    int sfmt;               // S_FP32: any fp32 scales; S_UE8M0: power-of-two scales only
     GemmLaunchFn launch;    // writes `out` (split==1) or `partials` (split>1)
 };
 

@@ -86,6 +86,18 @@ __device__ __forceinline__ v16f mfma_fp8_32x32x64(const v8i& a, const v8i& b, co
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The same 16x16x128 product with block scales applied and accumulated by the MFMA:
+// D = C + sum_k (A[i][k] * 2^(ea - 127)) * (B[k][j] * 2^(eb - 127)), where ea is the E8M0
+// exponent of row i's scale and eb that of column j's (each lane passes the scale of the row
+// / column it supplies; all of a row's 128 K share one scale here).
+__device__ __forceinline__ v4f mfma_fp8_16x16x128_e8(const v8i& a, const v8i& b, const v4f& c,
+                                                     int ea, int eb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+}
+
+// E8M0 exponent byte of a positive power-of-two fp32 value (its biased exponent field).
+__device__ __forceinline__ uint32_t e8m0_of(float pow2) { return (__float_as_uint(pow2) >> 23) & 0xFFu; }
+
 // int8: D(16x16, int32) += A(16x64) * B(64x16); 16 bytes of K per lane.
 __device__ __forceinline__ v4i mfma_i8_16x16x64(const v4i& a, const v4i& b, const v4i& c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);

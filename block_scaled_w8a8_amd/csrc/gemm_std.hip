@@ -19,6 +19,11 @@
 //    sched 2 instead uses 32x32 sub-tiles: two v_mfma_f32_32x32x64_f8f6f4 per K block
 //    (each weight fragment feeds twice the MFMA work per LDS read; a lane owns one token and
 //    four groups of four output columns).
+//  * sched 3 (power-of-two scales only): the scales are applied inside the block-scaled MFMA
+//    as E8M0 exponents — the weight scale (one per 128-row block, uniform over a wave) for
+//    the first operand, each lane's token scale for the second — and the MFMA accumulates
+//    across K blocks itself: no block partial, no FMA. A power-of-two fp32 scale's E8M0
+//    byte is its exponent field.
 //  * The weight fragment sits in the MFMA's first operand and the token fragment in the
 //    second, so each lane ends up owning one token row and four consecutive output columns:
 //    one scale product per lane and sub-tile row, and 8-byte (bf16) row-contiguous stores.
@@ -71,6 +76,7 @@ __device__ __forceinline__ void std_tile(
     using AccT = typename Shape::AccT;
     static_assert(SCHED != 2 || (QT == Q_FP8 && WL == W_ROW && TM % 32 == 0 && TN % 32 == 0),
                   "the 32x32 schedule is fp8 only, row-major W, and needs 32-multiple wave tiles");
+    static_assert(SCHED != 3 || QT == Q_FP8, "the block-scaled MFMA schedule is fp8 only");
     constexpr int STAGE = (BM + BN) * 128;         // bytes per LDS stage
     constexpr int CHUNKS = (BM + BN) / 8;          // 1 KB load chunks per stage
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
@@ -201,9 +207,29 @@ __device__ __forceinline__ void std_tile(
 
     auto lds16 = [&](uint32_t off) { return *reinterpret_cast<const v4i*>(lds + off); };
 
-    // One K block on LDS stage `stage`: fragments from LDS, MFMA, scale fusion.
-    auto compute = [&](uint32_t sbase, const float (&c)[SM]) {
-        if constexpr (MF == 32) {
+    // One K block on LDS stage `stage`: fragments from LDS, MFMA, scale fusion. c[sm] is the
+    // scale product of sub-tile row sm (sched 0-2); ea[sm] and ew the E8M0 exponents of the
+    // token and weight scales (sched 3).
+    auto compute = [&](uint32_t sbase, const float (&c)[SM], const int (&ea)[SM], int ew) {
+        if constexpr (SCHED == 3) {
+            const uint32_t abase = sbase + a_row, wbase = sbase + w_row;
+            v8i af[SM];
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm) {
+                const v4i lo = lds16(abase + sm * 2048 + a_s0);
+                const v4i hi = lds16(abase + sm * 2048 + a_s1);
+                af[sm] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            }
+#pragma unroll
+            for (int sn = 0; sn < SN; ++sn) {
+                const v4i lo = lds16(wbase + sn * 2048 + w_s0);
+                const v4i hi = lds16(wbase + sn * 2048 + w_s1);
+                const v8i wf = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+                for (int sm = 0; sm < SM; ++sm)
+                    acc[sm][sn] = mfma_fp8_16x16x128_e8(wf, af[sm], acc[sm][sn], ew, ea[sm]);
+            }
+        } else if constexpr (MF == 32) {
             // Lane l covers row l % 32 of each 32-row sub-tile and, in K half h, the 16-byte
             // chunks 4h + 2*(l/32) and 4h + 2*(l/32) + 1. Each W fragment feeds SM pairs of
             // MFMAs (64 K each) whose sum is the block partial of a 32x32 sub-tile.
@@ -344,9 +370,20 @@ __device__ __forceinline__ void std_tile(
 
     auto kblock = [&](int64_t kb, int stage) {
         float c[SM];
-        {
+        int ea[SM], ew = 0;
+        if constexpr (SCHED == 3) {
+            const uint32_t sc = (uint32_t)(SC_BASE + stage * SC_STAGE);
+            ew = (int)e8m0_of(*reinterpret_cast<const float*>(lds + sc + sw_lds));
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm) {
+                ea[sm] = (int)e8m0_of(*reinterpret_cast<const float*>(lds + sc + sa_lds + sm * 4));
+                c[sm] = 0.f;
+            }
+        } else {
             const uint32_t sc = (uint32_t)(SC_BASE + stage * SC_STAGE);
             const float swv = *reinterpret_cast<const float*>(lds + sc + sw_lds);
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm) ea[sm] = 0;
             if constexpr (SM == 4) {
                 const v4f sa4 = *reinterpret_cast<const v4f*>(lds + sc + sa_lds);
                 c[0] = sa4.x * swv; c[1] = sa4.y * swv; c[2] = sa4.z * swv; c[3] = sa4.w * swv;
@@ -363,7 +400,7 @@ __device__ __forceinline__ void std_tile(
             prefetch_l2(kb + 2 < kb_end ? kb + 2 : kb_end - 1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        compute((uint32_t)(stage * STAGE), c);
+        compute((uint32_t)(stage * STAGE), c, ea, ew);
         // the L2 touches (issued last) may stay in flight; everything before them must land
         if constexpr (STAGES == 3) wait_vmem_keep(PF_ROUNDS);
         else wait_vmem_all();
@@ -642,7 +679,7 @@ hipError_t launch_std(const GemmArgs& a, hipStream_t stream) {
 
 #define BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, OT, WL)                                \
     KernelEntry{bfq_tile{0, BM, BN, 128, 1, WM, WN, ST, 8, SC, 0, 0}, QT, OT, WL,         \
-                &launch_std<BM, BN, WM, WN, QT, OT, SC, ST, WL>}
+                (SC) == 3 ? S_UE8M0 : S_FP32, &launch_std<BM, BN, WM, WN, QT, OT, SC, ST, WL>}
 
 #define BFQ_STD_ALL_OUT(BM, BN, WM, WN, ST, SC, QT, WL)                                   \
     BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_BF16, WL),                                \
@@ -671,11 +708,17 @@ static const KernelEntry kStdKernels[] = {
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_INT8, W_PACKED16),
     BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 0, Q_INT8, W_PACKED16),
     BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 0, Q_INT8, W_PACKED16),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 3, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 3, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 3, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 3, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 3, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 3, Q_FP8, W_PACKED16),
 };
 
 #define BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, OT, WL)                                 \
     KernelEntry{bfq_tile{2, BM, BN, 128, 1, WM, WN, ST, 8, SC, 0, 0}, QT, OT, WL,         \
-                &launch_streamk<BM, BN, WM, WN, QT, OT, SC, ST, WL>}
+                (SC) == 3 ? S_UE8M0 : S_FP32, &launch_streamk<BM, BN, WM, WN, QT, OT, SC, ST, WL>}
 
 #define BFQ_SK_ALL_OUT(BM, BN, WM, WN, ST, SC, QT, WL)                                    \
     BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_BF16, WL),                                 \
@@ -689,6 +732,8 @@ static const KernelEntry kStreamKKernels[] = {
     BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8, W_PACKED16),
     BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8, W_PACKED16),
     BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 0, Q_INT8, W_PACKED16),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 3, Q_FP8, W_ROW),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 3, Q_FP8, W_PACKED16),
 };
 
 const KernelEntry* streamk_kernels(int* count) {

@@ -449,7 +449,7 @@ hipError_t launch_swapab_lds(const GemmArgs& a, hipStream_t stream) {
 // waves sharing each strip's K range, waves_n = NW strips, stages = D K blocks in flight,
 // sched 0 = tokens per wave from L2, sched 1 = tokens shared through LDS.
 #define BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, OT, WL)                                      \
-    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 0, 0, 0}, QT, OT, WL,     \
+    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 0, 0, 0}, QT, OT, WL, S_FP32, \
                 &launch_swapab<MT, NWR, NW, KW, D, QT, OT, WL>}
 #define BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, WL)                                        \
     BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, O_BF16, WL),                                     \
@@ -459,7 +459,7 @@ hipError_t launch_swapab_lds(const GemmArgs& a, hipStream_t stream) {
     BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW), BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16)
 
 #define BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, OT, WL)                                     \
-    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 1, 0, 0}, QT, OT, WL,     \
+    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 1, 0, 0}, QT, OT, WL, S_FP32, \
                 &launch_swapab_lds<MT, NWR, NW, KW, D, QT, OT, WL>}
 #define BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, WL)                                       \
     BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, O_BF16, WL),                                    \

@@ -1,5 +1,6 @@
 // Quantization kernels for gfx950: per-token-group activation quantization (bf16 -> e4m3fn
-// or int8 codes + one fp32 scale per 1x128 group), per-128x128-block weight quantization
+// or int8 codes + one fp32 scale per 1x128 group, optionally rounded up to a power of two),
+// per-128x128-block weight quantization
 // (fp32 -> codes + one fp32 scale per block), the weight-code packing into the 16-row
 // fragment layout, and the element-encoder probe used by tests.
 //
@@ -66,10 +67,20 @@ __device__ __forceinline__ uint2 encode8_special(const float* x, bool nan_group)
     return r;
 }
 
+// UE8M0 scale format ([BENCH] §4.1, use_ue8m0): the smallest power of two >= s, for a
+// positive normal fp32 s (s >= eps / Qmax keeps it normal; s <= FLT_MAX / 127 keeps the
+// next power finite). A power of two stays; otherwise the mantissa is cleared and the
+// exponent stepped up by one.
+__device__ __forceinline__ float pow2_ceil(float s) {
+    const uint32_t u = __float_as_uint(s);
+    return (u & 0x007FFFFFu) ? __uint_as_float((u & 0xFF800000u) + 0x00800000u) : s;
+}
+
 template <int QT>
 __global__ __launch_bounds__(64 * kQuantWaves) void quant_tokens_kernel(
     const uint4* __restrict__ x, uint2* __restrict__ q, float* __restrict__ scales,
-    int64_t M, int64_t K, int64_t G, int64_t s_stride_m, int64_t s_stride_g, float eps) {
+    int64_t M, int64_t K, int64_t G, int64_t s_stride_m, int64_t s_stride_g, float eps,
+    int ue8m0) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t m = blockIdx.x;
@@ -103,6 +114,7 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quant_tokens_kernel(
         if (mx < 0x7F80u) {                              // finite amax
             float amax = __uint_as_float(mx << 16);
             s = (amax > eps ? amax : eps) / qmax<QT>();
+            if (ue8m0) s = pow2_ceil(s);
             codes = encode8<QT>(xv, s);
         } else {
             bool nan_group = mx > 0x7F80u;
@@ -118,7 +130,7 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quant_tokens_kernel(
 template <int QT>
 __global__ __launch_bounds__(256) void quant_weight_blocks_kernel(
     const float* __restrict__ w, uint8_t* __restrict__ q, float* __restrict__ scales,
-    int64_t N, int64_t K, float eps) {
+    int64_t N, int64_t K, float eps, int ue8m0) {
     const int64_t nb = blockIdx.y, kb = blockIdx.x, KB = K / 128;
     const int t = threadIdx.x;
     const int col4 = t & 31;          // float4 column within the 128-wide block row
@@ -149,6 +161,7 @@ __global__ __launch_bounds__(256) void quant_weight_blocks_kernel(
     if (finite) {
         float amax = __uint_as_float(mx);
         s = (amax > eps ? amax : eps) / qmax<QT>();
+        if (ue8m0) s = pow2_ceil(s);
     } else {
         s = nan_block ? __uint_as_float(0x7FC00000u) : __uint_as_float(0x7F800000u);
     }
@@ -207,28 +220,31 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __rest
 
 hipError_t launch_quant_tokens(const void* x, void* q, float* scales, int64_t M, int64_t K,
                                int qtype, int64_t s_stride_m, int64_t s_stride_g, float eps,
-                               hipStream_t stream) {
+                               int sfmt, hipStream_t stream) {
     const int64_t G = K / 128;
     dim3 grid((unsigned)M, (unsigned)((G + kGroupsPerBlock - 1) / kGroupsPerBlock));
     dim3 block(64 * kQuantWaves);
+    const int ue = sfmt == S_UE8M0;
     if (qtype == Q_FP8)
         hipLaunchKernelGGL(quant_tokens_kernel<Q_FP8>, grid, block, 0, stream,
-                           (const uint4*)x, (uint2*)q, scales, M, K, G, s_stride_m, s_stride_g, eps);
+                           (const uint4*)x, (uint2*)q, scales, M, K, G, s_stride_m, s_stride_g, eps, ue);
     else
         hipLaunchKernelGGL(quant_tokens_kernel<Q_INT8>, grid, block, 0, stream,
-                           (const uint4*)x, (uint2*)q, scales, M, K, G, s_stride_m, s_stride_g, eps);
+                           (const uint4*)x, (uint2*)q, scales, M, K, G, s_stride_m, s_stride_g, eps, ue);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_weight_blocks(const float* w, void* q, float* scales, int64_t N,
-                                      int64_t K, int qtype, float eps, hipStream_t stream) {
+                                      int64_t K, int qtype, float eps, int sfmt,
+                                      hipStream_t stream) {
     dim3 grid((unsigned)(K / 128), (unsigned)(N / 128));
+    const int ue = sfmt == S_UE8M0;
     if (qtype == Q_FP8)
         hipLaunchKernelGGL(quant_weight_blocks_kernel<Q_FP8>, grid, dim3(256), 0, stream, w,
-                           (uint8_t*)q, scales, N, K, eps);
+                           (uint8_t*)q, scales, N, K, eps, ue);
     else
         hipLaunchKernelGGL(quant_weight_blocks_kernel<Q_INT8>, grid, dim3(256), 0, stream, w,
-                           (uint8_t*)q, scales, N, K, eps);
+                           (uint8_t*)q, scales, N, K, eps, ue);
     return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@
 //   "entries": [
 //     { "N": 24576, "K": 7168, "dtype": "fp8_w8a8", "block_shape": [128, 128],
 //       "w_layout": "packed16",            (optional; "row_major" when absent)
+//       "scales": "ue8m0",                 (optional; "fp32" when absent)
 //       "configs": { "1": {"variant": 1, "bm": 16, "bn": 128, "split_k": 2, "waves_m": 1,
 //                          "waves_n": 4, "stages": 4, "group_m": 1}, ... } } ] }
 #include "tile_table.h"
@@ -168,6 +169,13 @@ bool parse_tile_table(const std::string& text, TileTable& out, std::string& err)
             else if (wl->str == "packed16") wlayout = 1;
             else { err = "unknown w_layout '" + wl->str + "'"; return false; }
         }
+        int sfmt = 0;
+        if (const JVal* sf = e.get("scales")) {
+            if (sf->kind != JVal::STR) { err = "'scales' is not a string"; return false; }
+            if (sf->str == "fp32") sfmt = 0;
+            else if (sf->str == "ue8m0") sfmt = 1;
+            else { err = "unknown scales '" + sf->str + "'"; return false; }
+        }
         const JVal* bs = e.get("block_shape");
         if (bs) {
             if (bs->kind != JVal::ARR || bs->arr.size() != 2 || bs->arr[0].num != 128 ||
@@ -209,7 +217,7 @@ bool parse_tile_table(const std::string& text, TileTable& out, std::string& err)
             buckets[(int64_t)m] = tl;
         }
         if (buckets.empty()) { err = "entry has no configs"; return false; }
-        t.entries[TableKey{N, K, qtype, wlayout}] = std::move(buckets);
+        t.entries[TableKey{N, K, qtype, wlayout, sfmt}] = std::move(buckets);
     }
     out = std::move(t);
     return true;

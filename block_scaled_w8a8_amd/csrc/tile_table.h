@@ -21,11 +21,13 @@ struct TableKey {
     int64_t N, K;
     int qtype;
     int wlayout;   // weight layout the tuned kernels read (W_ROW / W_PACKED16)
+    int sfmt;      // scale format the entry was tuned for (S_FP32 / S_UE8M0)
     bool operator<(const TableKey& o) const {
         if (N != o.N) return N < o.N;
         if (K != o.K) return K < o.K;
         if (qtype != o.qtype) return qtype < o.qtype;
-        return wlayout < o.wlayout;
+        if (wlayout != o.wlayout) return wlayout < o.wlayout;
+        return sfmt < o.sfmt;
     }
 };
 

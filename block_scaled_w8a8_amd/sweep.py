@@ -1,6 +1,6 @@
 """On-device tile sweep that fills the tile table, and a single-shape runner for profiling.
 
-  python -m block_scaled_w8a8_amd.sweep tune  [--shapes N,K ...] [--dtype fp8|int8]
+  python -m block_scaled_w8a8_amd.sweep tune  [--shapes N,K ...] [--dtype fp8|int8] [--scales fp32|ue8m0]
                                              [--w-layout row|packed] [--out PATH]
   python -m block_scaled_w8a8_amd.sweep run   --M 4096 --N 24576 --K 7168 [--tile JSON] [--iters 50]
                                              [--w-layout row|packed]
@@ -44,7 +44,8 @@ def log(*a):
 class Problem:
     """Device buffers for one (N, K) and the largest M, with rotation copies."""
 
-    def __init__(self, N, K, m_max, qname, rotate=None, layout="col", w_layout="row"):
+    def __init__(self, N, K, m_max, qname, rotate=None, layout="col", w_layout="row",
+                 scales="fp32"):
         import torch
 
         from . import bfq, synth
@@ -53,12 +54,13 @@ class Problem:
         dev = torch.device("cuda:0")
         x = synth.activations(m_max, K, seed=0).to(dev)
         w = synth.weights(N, K, seed=0).to(dev)
-        qw, sw = bfq.quant_weight_blocks(w, q_dtype=self.qd)
+        self.sf = bfq.BFQ_SCALE_UE8M0 if scales == "ue8m0" else bfq.BFQ_SCALE_FP32
+        qw, sw = bfq.quant_weight_blocks(w, q_dtype=self.qd, scale_fmt=self.sf)
         self.wl = bfq.BFQ_W_PACKED16 if w_layout == "packed" else bfq.BFQ_W_ROW_MAJOR
         if self.wl == bfq.BFQ_W_PACKED16:
             qw = bfq.pack_weights(qw)
         self.layout = bfq.BFQ_SCALES_COL_MAJOR if layout == "col" else bfq.BFQ_SCALES_ROW_MAJOR
-        qa, sa = bfq.quant_tokens(x, q_dtype=self.qd, layout=self.layout)
+        qa, sa = bfq.quant_tokens(x, q_dtype=self.qd, layout=self.layout, scale_fmt=self.sf)
         del w, x
         foot = N * K + m_max * K
         if rotate is None:
@@ -88,7 +90,7 @@ class Problem:
         sa_m = sa if self.layout == bfq.BFQ_SCALES_COL_MAJOR else sa[:M]
         return bfq.bfq_block_gemm(qa[:M], sa_m, qw, sw, out[:M], a_layout=self.layout,
                                   a_scale_ld=sa.stride(0), tile=tile, workspace=ws,
-                                  workspace_bytes=need, w_layout=self.wl)
+                                  workspace_bytes=need, w_layout=self.wl, scale_fmt=self.sf)
 
     def time_us(self, M, tile, warmup=3, iters=20, reps=3):
         """Median over reps of the mean time of `iters` back-to-back launches, replayed from a
@@ -118,15 +120,15 @@ class Problem:
         return res[len(res) // 2]
 
 
-def candidates(qd, M, N, K, wl=0):
+def candidates(qd, M, N, K, wl=0, sf=0):
     """Compiled kernels x split-K factors x tile orders worth timing at this shape: the
     streaming kernel only while it re-reads the weights at most 4 times, split-K only while
     the grid is short of 4 workgroups per CU, tile orders only for multi-tile grids."""
     from . import bfq
     out = []
     KB = K // 128
-    for i in range(bfq.bfq_num_tile_candidates(qd, wl)):
-        t = bfq.bfq_get_tile_candidate(i, qd, wl)
+    for i in range(bfq.bfq_num_tile_candidates(qd, wl, sf)):
+        t = bfq.bfq_get_tile_candidate(i, qd, wl, sf)
         if t.variant == 1 and M > 4 * t.bm:
             continue
         if t.variant in (0, 2) and M <= 16 and t.bm > 64:
@@ -162,21 +164,22 @@ def agrees(a, b) -> bool:
     return rf <= 1e-3 and md <= 2.0 ** -7 * rms + 1e-3
 
 
-def tune_shape(N, K, qname, grid, budget_s, w_layout="row"):
+def tune_shape(N, K, qname, grid, budget_s, w_layout="row", scales="fp32"):
     import torch
 
     from . import bfq
-    prob = Problem(N, K, max(grid), qname, w_layout=w_layout)
+    prob = Problem(N, K, max(grid), qname, w_layout=w_layout, scales=scales)
     results = {}
     for M in grid:
         t0 = time.time()
-        _, ref_tile = bfq.bfq_select_tile(M, N, K, prob.qd, bfq.BFQ_FP32, w_layout=prob.wl)
+        _, ref_tile = bfq.bfq_select_tile(M, N, K, prob.qd, bfq.BFQ_FP32, w_layout=prob.wl,
+                                          scale_fmt=prob.sf)
         prob.launch(M, ref_tile, out32=True)
         torch.cuda.synchronize()
         ref = prob.out32[:M].clone()
         best = None
         trials = []
-        for tile in candidates(prob.qd, M, N, K, prob.wl):
+        for tile in candidates(prob.qd, M, N, K, prob.wl, prob.sf):
             if time.time() - t0 > budget_s:
                 break
             try:
@@ -227,23 +230,25 @@ def cmd_tune(args):
     wname = "packed16" if args.w_layout == "packed" else "row_major"
 
     def key(e):
-        return (e["N"], e["K"], e["dtype"], e.get("w_layout", "row_major"))
+        return (e["N"], e["K"], e["dtype"], e.get("w_layout", "row_major"), e.get("scales", "fp32"))
 
     done = {key(e) for e in table["entries"]}
     for (N, K) in shapes:
-        if (N, K, dname, wname) in done and not args.force:
-            log(f"[sweep] N={N} K={K} {dname} {wname}: already in {args.out}, skipped")
+        if (N, K, dname, wname, args.scales) in done and not args.force:
+            log(f"[sweep] N={N} K={K} {dname} {wname} {args.scales}: already in {args.out}, skipped")
             continue
-        log(f"[sweep] N={N} K={K} {dname} {wname}")
-        res = tune_shape(N, K, qname, args.grid or M_GRID, args.budget, args.w_layout)
+        log(f"[sweep] N={N} K={K} {dname} {wname} {args.scales}")
+        res = tune_shape(N, K, qname, args.grid or M_GRID, args.budget, args.w_layout, args.scales)
         entry = {"N": N, "K": K, "dtype": dname, "block_shape": [128, 128],
                  "configs": {str(M): {k: v for k, v in t.items() if k != "bk"}
                              for M, (us, t) in res.items()},
                  "us": {str(M): round(us, 3) for M, (us, t) in res.items()}}
         if wname != "row_major":
             entry["w_layout"] = wname
+        if args.scales != "fp32":
+            entry["scales"] = args.scales
         table["entries"] = [e for e in table["entries"]
-                            if key(e) != (N, K, dname, wname)] + [entry]
+                            if key(e) != (N, K, dname, wname, args.scales)] + [entry]
         save_table(args.out, table)
     print(json.dumps({"table": args.out, "entries": len(table["entries"])}))
 
@@ -253,12 +258,12 @@ def cmd_run(args):
 
     from . import bfq
     prob = Problem(args.N, args.K, args.M, args.dtype, rotate=args.rotate, layout=args.layout,
-                   w_layout=args.w_layout)
+                   w_layout=args.w_layout, scales=args.scales)
     if args.tile:
         tile = bfq.bfq_tile.from_dict(json.loads(args.tile))
     else:
         _, tile = bfq.bfq_select_tile(args.M, args.N, args.K, prob.qd, bfq.BFQ_BF16,
-                                      w_layout=prob.wl)
+                                      w_layout=prob.wl, scale_fmt=prob.sf)
     if args.eager:
         # plain launches, no graph: for counter collection, which wants one dispatch per call
         for i in range(args.eager):
@@ -301,6 +306,7 @@ def main():
     t.add_argument("--budget", type=float, default=20.0, help="seconds per (shape, M)")
     t.add_argument("--force", action="store_true")
     t.add_argument("--w-layout", default="row", choices=["row", "packed"])
+    t.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0"])
     r = sub.add_parser("run")
     r.add_argument("--M", type=int, required=True)
     r.add_argument("--N", type=int, required=True)
@@ -312,6 +318,7 @@ def main():
     r.add_argument("--eager", type=int, default=0, help="launch this many times without timing")
     r.add_argument("--layout", default="col", choices=["row", "col"], help="activation scales")
     r.add_argument("--w-layout", default="row", choices=["row", "packed"])
+    r.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0"])
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=1 << 30)
     c.add_argument("--iters", type=int, default=3)

@@ -80,6 +80,17 @@ typedef enum {
     BFQ_W_PACKED16 = 1
 } bfq_weight_layout;
 
+/* Format of the fp32 scales. UE8M0: every scale is a power of two — the block's
+ * max(amax, eps)/Qmax rounded up to the next power of two ([BENCH] §4.1: with use_ue8m0 the
+ * scale is first rounded up to a power of two, the format DeepGEMM's hardware scaling path
+ * requires). The scales are still stored as fp32 (exact); the codes are encode(x / scale).
+ * A GEMM told that both scale arrays are UE8M0 may apply them inside gfx950's
+ * block-scaled MFMA instead of with one fp32 FMA per output and K block. */
+typedef enum {
+    BFQ_SCALE_FP32 = 0,
+    BFQ_SCALE_UE8M0 = 1
+} bfq_scale_format;
+
 /* One launch configuration of the block GEMM ([CONFIG] §2: per-M launch parameters).
  *   variant 0 "standard": bm x bn output tile per workgroup, A and W tiles staged through
  *             LDS (double-buffered), waves_m x waves_n waves, group_m = grouped tile order.
@@ -98,7 +109,9 @@ typedef enum {
  *   split_k  : K blocks split into split_k contiguous chunks (>= 1), fp32 partials reduced
  *             in a fixed order ([HELION] kernel section).
  *   stages   : LDS stages (variants 0, 2) or weight prefetch depth in K blocks (variant 1).
- *   sched    : variants 0 and 2 instruction schedule (variant 1: see above): 0 = each sub-tile's scale FMAs right after its
+ *   sched    : variants 0 and 2 instruction schedule (variant 1: see above): 3 = the scales
+ *             applied by the block-scaled MFMA, which accumulates across K blocks (fp8 and
+ *             BFQ_SCALE_UE8M0 scales only); 0 = each sub-tile's scale FMAs right after its
  *             MFMAs, 1 = software-pipelined (FMAs one sub-tile behind the MFMAs), 2 = 32x32
  *             sub-tiles (two 32x32x64 MFMAs per K block, FMAs one pair behind; fp8 only).
  *   group_m, raster: variants 0 and 2 tile order (launch arguments, any group_m >= 1): raster 0
@@ -114,13 +127,15 @@ typedef struct {
  *   scale = max(amax, eps) / Qmax   (Qmax = 448 for E4M3FN, 127 for INT8; IEEE division)
  *   q     = encode(x / scale)       (IEEE division; e4m3fn: RNE, saturating; int8: RNE,
  *                                    clamp [-127, 127])
+ * scale_fmt BFQ_SCALE_UE8M0 rounds each scale up to a power of two before encoding.
  * A group containing NaN gets a NaN scale and codes 0x7F (e4m3fn) or 0 (int8).
  *   x_bf16 [M][K] row-major bf16; q [M][K] row-major codes (1 byte);
  *   scales: fp32, layout per `layout` with leading dimension scale_ld.
  * group_size must be 128; q_dtype must be BFQ_E4M3FN or BFQ_INT8. */
 bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t group_size,
                             bfq_dtype q_dtype, void* q, float* scales, bfq_scale_layout layout,
-                            int64_t scale_ld, float eps, void* stream);
+                            int64_t scale_ld, float eps, bfq_scale_format scale_fmt,
+                            void* stream);
 
 /* Per-block weight quantization, the offline step before the GEMM ([BENCH] §4.1
  * per_block_cast_to_fp8 with fp32 scales): for each block_shape[0] x block_shape[1] block of
@@ -128,7 +143,8 @@ bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t gr
  *   q [N][K] codes; scales [N/128][K/128] row-major fp32. block_shape must be {128,128}. */
 bfq_status bfq_quant_weight_blocks(const float* w, int64_t N, int64_t K,
                                    const int32_t block_shape[2] /* host */, bfq_dtype q_dtype,
-                                   void* q, float* scales, float eps, void* stream);
+                                   void* q, float* scales, float eps,
+                                   bfq_scale_format scale_fmt, void* stream);
 
 /* Rearrange weight codes from row-major [N][K] into BFQ_W_PACKED16 (a byte permutation, part
  * of the offline weight preparation like bfq_quant_weight_blocks). w_q and w_packed are
@@ -137,13 +153,13 @@ bfq_status bfq_quant_weight_blocks(const float* w, int64_t N, int64_t K,
 bfq_status bfq_pack_weights(const void* w_q, int64_t N, int64_t K, bfq_dtype q_dtype,
                             void* w_packed, void* stream);
 
-/* Tile selection ([CONFIG] §4.1-§4.2): exact (N, K, dtype, weight layout) entry of the loaded
+/* Tile selection ([CONFIG] §4.1-§4.2): exact (N, K, dtype, weight layout, scale format) entry of the loaded
  * tile table, then the bucket nearest to M (ties to the smaller bucket; M past the grid ->
  * last bucket). No entry -> the compiled-in default rule and BFQ_WARN_DEFAULT_TILE ([CONFIG]
  * §4.1 warns and falls back to a default config). tile_out is a host pointer. */
 bfq_status bfq_select_tile(int64_t M, int64_t N, int64_t K, const int32_t block_shape[2],
                            bfq_dtype in_dtype, bfq_dtype out_dtype, bfq_weight_layout w_layout,
-                           bfq_tile* tile_out);
+                           bfq_scale_format scale_fmt, bfq_tile* tile_out);
 
 /* Bytes of device workspace bfq_block_gemm needs for this shape and tile (split-K fp32
  * partials: split_k * M * N * 4 when split_k > 1; stream-K: two partial tiles per compute
@@ -156,13 +172,17 @@ size_t bfq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const bfq_tile*
  *   a_q [M][K] codes (K-contiguous); w_q N*K codes in w_layout (row-major [N][K] is the
  *   "NT" form of the page; BFQ_W_PACKED16 from bfq_pack_weights);
  *   a_scales per a_layout/a_scale_ld; w_scales [N/128][K/128] row-major;
+ *   scale_fmt BFQ_SCALE_UE8M0 states that every a_scales and w_scales value is a power of
+ *   two (as the quantizers write in that format); results are then undefined otherwise.
  *   out [M][N] row-major, out_dtype BF16 | FP16 | FP32.
- *   tile NULL -> bfq_select_tile for w_layout; an explicit tile must name a kernel compiled
- *   for w_layout (else BFQ_ERR_TILE); workspace may be NULL when the tile needs none.
+ *   tile NULL -> bfq_select_tile for (w_layout, scale_fmt); an explicit tile must name a
+ *   kernel compiled for w_layout whose scale handling allows scale_fmt (else BFQ_ERR_TILE);
+ *   workspace may be NULL when the tile needs none.
  * Returns BFQ_WARN_DEFAULT_TILE when tile was NULL and the default rule was used. */
 bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
                           int64_t a_scale_ld, const void* w_q, const float* w_scales,
-                          bfq_weight_layout w_layout, void* out, int64_t M, int64_t N, int64_t K,
+                          bfq_weight_layout w_layout, bfq_scale_format scale_fmt, void* out,
+                          int64_t M, int64_t N, int64_t K,
                           const int32_t block_shape[2] /* host */, bfq_dtype in_dtype,
                           bfq_dtype out_dtype, const bfq_tile* tile /* host */,
                           void* workspace, size_t workspace_bytes, void* stream);
@@ -172,11 +192,13 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
  * concurrently with other calls. NULL reloads the default location. */
 bfq_status bfq_load_tile_table(const char* json_path);
 
-/* Number of compiled kernel configurations for (in_dtype, w_layout), and the i-th one
- * (split_k = 1; any split_k >= 1 may be combined with it). Used by the on-device sweep. */
-int32_t bfq_num_tile_candidates(bfq_dtype in_dtype, bfq_weight_layout w_layout);
-bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, bfq_weight_layout w_layout, int32_t index,
-                                  bfq_tile* tile_out);
+/* Number of compiled kernel configurations usable for (in_dtype, w_layout, scale_fmt), and
+ * the i-th one (split_k = 1; any split_k >= 1 may be combined with it). Used by the
+ * on-device sweep. */
+int32_t bfq_num_tile_candidates(bfq_dtype in_dtype, bfq_weight_layout w_layout,
+                                bfq_scale_format scale_fmt);
+bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, bfq_weight_layout w_layout,
+                                  bfq_scale_format scale_fmt, int32_t index, bfq_tile* tile_out);
 
 const char* bfq_status_string(bfq_status s);
 const char* bfq_last_error(void);

@@ -23,6 +23,8 @@ LIB_PATH = os.path.join(BUILD_DIR, "liboracle.so")
 
 FP8 = 0
 INT8 = 1
+SCALE_FP32 = 0
+SCALE_UE8M0 = 1
 DEFAULT_EPS = np.float32(1e-10)
 
 
@@ -64,9 +66,9 @@ def lib() -> ctypes.CDLL:
             getattr(L, nm).restype = None
             getattr(L, nm).argtypes = [p, i64, p]
         L.orc_quant_groups.restype = None
-        L.orc_quant_groups.argtypes = [p, i64, i64, i64, i32, p, p, f32]
+        L.orc_quant_groups.argtypes = [p, i64, i64, i64, i32, p, p, f32, i32]
         L.orc_quant_blocks.restype = None
-        L.orc_quant_blocks.argtypes = [p, i64, i64, i64, i64, i32, p, p, f32]
+        L.orc_quant_blocks.argtypes = [p, i64, i64, i64, i64, i32, p, p, f32, i32]
         L.orc_block_gemm.restype = None
         L.orc_block_gemm.argtypes = [p, p, p, p, i64, i64, i64, i32, p, p]
         L.orc_block_gemm_sampled.restype = None
@@ -137,26 +139,31 @@ def int8_encode_array(x: np.ndarray) -> np.ndarray:
 # ------------------------------------------------------------------ quantizers
 
 def quant_groups(x_bf16_bits: np.ndarray, group: int = 128, qtype: int = FP8,
-                 eps: float = DEFAULT_EPS):
-    """bf16 activations (uint16 bit patterns, [M, K]) -> (codes [M, K], scales [M, K/group])."""
+                 eps: float = DEFAULT_EPS, scale_fmt: int = SCALE_FP32):
+    """bf16 activations (uint16 bit patterns, [M, K]) -> (codes [M, K], scales [M, K/group]).
+    scale_fmt SCALE_UE8M0: scales rounded up to a power of two (block GEMM benchmark page
+    §4.1, use_ue8m0)."""
     x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16)
     M, K = x.shape
     assert K % group == 0
     q = np.empty((M, K), dtype=_code_dtype(qtype))
     s = np.empty((M, K // group), dtype=np.float32)
-    lib().orc_quant_groups(_ptr(x), M, K, group, qtype, _ptr(q), _ptr(s), float(eps))
+    lib().orc_quant_groups(_ptr(x), M, K, group, qtype, _ptr(q), _ptr(s), float(eps),
+                           int(scale_fmt))
     return q, s
 
 
-def quant_blocks(w: np.ndarray, block=(128, 128), qtype: int = FP8, eps: float = DEFAULT_EPS):
-    """fp32 weights [N, K] -> (codes [N, K], scales [N/bn, K/bk])."""
+def quant_blocks(w: np.ndarray, block=(128, 128), qtype: int = FP8, eps: float = DEFAULT_EPS,
+                 scale_fmt: int = SCALE_FP32):
+    """fp32 weights [N, K] -> (codes [N, K], scales [N/bn, K/bk]); scale_fmt as above."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     N, K = w.shape
     bn, bk = block
     assert N % bn == 0 and K % bk == 0
     q = np.empty((N, K), dtype=_code_dtype(qtype))
     s = np.empty((N // bn, K // bk), dtype=np.float32)
-    lib().orc_quant_blocks(_ptr(w), N, K, bn, bk, qtype, _ptr(q), _ptr(s), float(eps))
+    lib().orc_quant_blocks(_ptr(w), N, K, bn, bk, qtype, _ptr(q), _ptr(s), float(eps),
+                           int(scale_fmt))
     return q, s
 
 

@@ -109,11 +109,18 @@ void orc_f32_to_bf16_array(const float* x, int64_t n, uint16_t* out) {
 static float qmax_of(int qtype) { return qtype == ORC_FP8 ? 448.0f : 127.0f; }
 
 /* scale = max(amax, eps) / Qmax as one correctly rounded fp32 division.
- * Reading: a NaN amax propagates into the scale. */
-static float scale_of(float amax, float eps, int qtype) {
+ * UE8M0 format ([BENCH] §4.1, use_ue8m0=True): that quotient is rounded up to a power of
+ * two. Reading: "rounded up" is the smallest power of two that is >= the fp32 quotient (a
+ * quotient that already is a power of two stays); the codes are then encode(x / scale).
+ * Reading: a NaN amax propagates into the scale, an infinite one stays infinite. */
+static float scale_of(float amax, float eps, int qtype, int scale_fmt) {
     if (isnan(amax)) return NAN;
     float a = amax > eps ? amax : eps;
-    return a / qmax_of(qtype);
+    float t = a / qmax_of(qtype);
+    if (scale_fmt != ORC_SCALE_UE8M0 || isinf(t)) return t;
+    int e;
+    double f = frexp((double)t, &e);            /* t = f * 2^e, f in [0.5, 1) */
+    return f == 0.5 ? t : (float)ldexp(1.0, e);  /* 2^(e-1) < t < 2^e otherwise */
 }
 
 static void store_code(void* q, int64_t i, float y, int qtype) {
@@ -122,7 +129,7 @@ static void store_code(void* q, int64_t i, float y, int qtype) {
 }
 
 void orc_quant_groups(const uint16_t* x, int64_t M, int64_t K, int64_t group,
-                      int qtype, void* q, float* s, float eps) {
+                      int qtype, void* q, float* s, float eps, int scale_fmt) {
     int64_t G = K / group;
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
@@ -136,7 +143,7 @@ void orc_quant_groups(const uint16_t* x, int64_t M, int64_t K, int64_t group,
                 else if (fabsf(v) > amax) amax = fabsf(v);
             }
             if (nan_seen) amax = NAN;
-            float sc = scale_of(amax, eps, qtype);
+            float sc = scale_of(amax, eps, qtype, scale_fmt);
             s[m * G + g] = sc;
             for (int64_t k = 0; k < group; ++k) {
                 float y = orc_bf16_to_f32(row[k]) / sc;     /* IEEE division (reading) */
@@ -147,7 +154,7 @@ void orc_quant_groups(const uint16_t* x, int64_t M, int64_t K, int64_t group,
 }
 
 void orc_quant_blocks(const float* w, int64_t N, int64_t K, int64_t bn, int64_t bk,
-                      int qtype, void* q, float* s, float eps) {
+                      int qtype, void* q, float* s, float eps, int scale_fmt) {
     int64_t NB = N / bn, KB = K / bk;
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t nb = 0; nb < NB; ++nb) {
@@ -161,7 +168,7 @@ void orc_quant_blocks(const float* w, int64_t N, int64_t K, int64_t bn, int64_t 
                     else if (fabsf(v) > amax) amax = fabsf(v);
                 }
             if (nan_seen) amax = NAN;
-            float sc = scale_of(amax, eps, qtype);
+            float sc = scale_of(amax, eps, qtype, scale_fmt);
             s[nb * KB + kb] = sc;
             for (int64_t i = 0; i < bn; ++i)
                 for (int64_t j = 0; j < bk; ++j) {

@@ -26,6 +26,8 @@ extern "C" {
 #endif
 
 enum { ORC_FP8 = 0, ORC_INT8 = 1 };
+/* Scale formats: fp32 quotient, or that quotient rounded up to a power of two (UE8M0). */
+enum { ORC_SCALE_FP32 = 0, ORC_SCALE_UE8M0 = 1 };
 
 /* OCP FP8 e4m3fn codec. decode: 0x7F/0xFF -> NaN; exact value otherwise (as double). */
 double  orc_e4m3_decode(uint8_t code);
@@ -46,14 +48,15 @@ uint16_t orc_f32_to_bf16(float f);   /* RNE; NaN -> 0x7FC0 */
 /* Per-token-group quantization of bf16 activations x[M][K] (row-major).
  * q[M][K] codes (1 byte each); s[M][K/group] row-major fp32 scales.
  * scale = max(amax, eps) / Qmax with Qmax = 448 (fp8) or 127 (int8); code = enc(x / scale).
+ * scale_fmt ORC_SCALE_UE8M0 rounds the scale up to a power of two first.
  * A group containing NaN gets a NaN scale. */
 void orc_quant_groups(const uint16_t* x, int64_t M, int64_t K, int64_t group,
-                      int qtype, void* q, float* s, float eps);
+                      int qtype, void* q, float* s, float eps, int scale_fmt);
 
 /* Per-block quantization of fp32 weights W[N][K] over bn x bk blocks.
  * q[N][K] codes; s[N/bn][K/bk] row-major fp32 scales. Same rule as the groups. */
 void orc_quant_blocks(const float* w, int64_t N, int64_t K, int64_t bn, int64_t bk,
-                      int qtype, void* q, float* s, float eps);
+                      int qtype, void* q, float* s, float eps, int scale_fmt);
 
 /* Block-scaled GEMM C[M][N] = sum_kb (sum_{k in kb} A[m,k] W[n,k]) * sa[m,kb] * sw[n/128,kb].
  * qa[M][K], qw[N][K] codes; sa[M][K/128]; sw[N/128][K/128]. Per-block sums are exact

@@ -37,7 +37,8 @@ FAKE = 1 << 20          # a 16-byte aligned non-NULL address; never dereferenced
 
 def _gemm(bfq, **kw):
     a = dict(a_q=FAKE, a_scales=FAKE, a_layout=0, a_scale_ld=56, w_q=FAKE, w_scales=FAKE,
-             w_layout=0, out=FAKE, M=0, N=1536, K=7168, block_shape=BS, in_dtype=bfq.BFQ_E4M3FN,
+             w_layout=0, scale_fmt=0, out=FAKE, M=0, N=1536, K=7168, block_shape=BS,
+             in_dtype=bfq.BFQ_E4M3FN,
              out_dtype=bfq.BFQ_BF16, tile=None, workspace=None, workspace_bytes=0, stream=None)
     a.update(kw)
     return bfq.lib.bfq_block_gemm(*a.values())
@@ -58,6 +59,14 @@ def test_gemm_validation_errors_without_launch(bfq):
     assert _gemm(bfq, M=64, a_layout=1, a_scale_ld=63) == bfq.BFQ_ERR_SHAPE
     assert _gemm(bfq, a_layout=7) == bfq.BFQ_ERR_ARG
     assert _gemm(bfq, w_layout=2) == bfq.BFQ_ERR_ARG
+    assert _gemm(bfq, scale_fmt=2) == bfq.BFQ_ERR_ARG
+    # a block-scaled-MFMA tile (sched 3) needs scales declared as powers of two
+    ue = [bfq.bfq_get_tile_candidate(i, bfq.BFQ_E4M3FN, 0, bfq.BFQ_SCALE_UE8M0)
+          for i in range(bfq.bfq_num_tile_candidates(bfq.BFQ_E4M3FN, 0, bfq.BFQ_SCALE_UE8M0))]
+    t3 = next(t for t in ue if t.sched == 3 and t.variant == 0)
+    assert _gemm(bfq, M=64, tile=ctypes.pointer(t3)) == bfq.BFQ_ERR_TILE
+    assert "scale format" in bfq.last_error()
+    assert _gemm(bfq, M=0, scale_fmt=1, tile=ctypes.pointer(t3)) >= 0
     # a tile compiled only for row-major weights is rejected for packed ones
     row_only = [bfq.bfq_get_tile_candidate(i) for i in range(bfq.bfq_num_tile_candidates())]
     packed = {tuple(bfq.bfq_get_tile_candidate(i, bfq.BFQ_E4M3FN, bfq.BFQ_W_PACKED16).as_dict().values())
@@ -79,11 +88,11 @@ def test_gemm_validation_errors_without_launch(bfq):
 
 def test_quant_validation_errors_without_launch(bfq):
     q = bfq.lib.bfq_quant_tokens
-    args = [FAKE, 4, 7168, 128, bfq.BFQ_E4M3FN, FAKE, FAKE, 0, 56, 1e-10, None]
+    args = [FAKE, 4, 7168, 128, bfq.BFQ_E4M3FN, FAKE, FAKE, 0, 56, 1e-10, 0, None]
 
     def call(**kw):
         a = list(args)
-        names = ["x", "M", "K", "group", "qd", "q", "s", "layout", "ld", "eps", "stream"]
+        names = ["x", "M", "K", "group", "qd", "q", "s", "layout", "ld", "eps", "sfmt", "stream"]
         for k, v in kw.items():
             a[names.index(k)] = v
         return q(*a)
@@ -97,12 +106,14 @@ def test_quant_validation_errors_without_launch(bfq):
     assert call(layout=1, ld=3) == bfq.BFQ_ERR_SHAPE
     assert call(eps=0.0) == bfq.BFQ_ERR_ARG
     assert call(eps=float("nan")) == bfq.BFQ_ERR_ARG
+    assert call(sfmt=5) == bfq.BFQ_ERR_ARG
     assert call(M=0, x=None, q=None, s=None) == bfq.BFQ_OK
     w = bfq.lib.bfq_quant_weight_blocks
-    assert w(FAKE, 256, 256, (ctypes.c_int32 * 2)(64, 128), bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, None) == bfq.BFQ_ERR_SHAPE
-    assert w(FAKE, 250, 256, BS, bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, None) == bfq.BFQ_ERR_SHAPE
-    assert w(None, 256, 256, BS, bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, None) == bfq.BFQ_ERR_NULL
-    assert w(FAKE, 0, 256, BS, bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, None) == bfq.BFQ_OK
+    assert w(FAKE, 256, 256, (ctypes.c_int32 * 2)(64, 128), bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, 0, None) == bfq.BFQ_ERR_SHAPE
+    assert w(FAKE, 250, 256, BS, bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, 0, None) == bfq.BFQ_ERR_SHAPE
+    assert w(None, 256, 256, BS, bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, 0, None) == bfq.BFQ_ERR_NULL
+    assert w(FAKE, 256, 256, BS, bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, 3, None) == bfq.BFQ_ERR_ARG
+    assert w(FAKE, 0, 256, BS, bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, 1, None) == bfq.BFQ_OK
 
 
 def test_pack_validation_errors_without_launch(bfq):
@@ -120,22 +131,32 @@ def test_pack_validation_errors_without_launch(bfq):
     assert pk(FAKE, 0, 256, bfq.BFQ_INT8, other, None) == bfq.BFQ_OK
 
 
+@pytest.mark.parametrize("sf", [0, 1])
 @pytest.mark.parametrize("wl", [0, 1])
-def test_candidates_enumerate(bfq, wl):
+def test_candidates_enumerate(bfq, wl, sf):
     for qd in (bfq.BFQ_E4M3FN, bfq.BFQ_INT8):
-        n = bfq.bfq_num_tile_candidates(qd, wl)
+        n = bfq.bfq_num_tile_candidates(qd, wl, sf)
         assert n >= 4
         seen = set()
         for i in range(n):
-            t = bfq.bfq_get_tile_candidate(i, qd, wl)
+            t = bfq.bfq_get_tile_candidate(i, qd, wl, sf)
             assert t.split_k == 1 and t.bk == 128 and t.variant in (0, 1, 2)
             seen.add(tuple(t.as_dict().values()))
         assert len(seen) == n
         # every kernel variant is compiled for both layouts
         assert {t[0] for t in seen} == {0, 1, 2}
+        # block-scaled MFMA tiles (sched 3, variants 0 and 2) exactly for fp8 with UE8M0 scales
+        has3 = any(t[0] in (0, 2) and t[9] == 3 for t in seen)
+        assert has3 == (qd == bfq.BFQ_E4M3FN and sf == 1)
+        # UE8M0 scales can use every kernel the fp32 format can
+        if sf == 1:
+            fp32 = {tuple(bfq.bfq_get_tile_candidate(i, qd, wl, 0).as_dict().values())
+                    for i in range(bfq.bfq_num_tile_candidates(qd, wl, 0))}
+            assert fp32 <= seen
     with pytest.raises(bfq.BfqError):
         bfq.bfq_get_tile_candidate(10_000)
     assert bfq.bfq_num_tile_candidates(bfq.BFQ_E4M3FN, 5) == 0
+    assert bfq.bfq_num_tile_candidates(bfq.BFQ_E4M3FN, 0, 7) == 0
 
 
 def _table(entries):
@@ -164,6 +185,8 @@ def test_table_nearest_m_and_fallback(bfq, tmp_path):
         assert st == bfq.BFQ_WARN_DEFAULT_TILE
         st, t = bfq.bfq_select_tile(64, 1536, 7168, w_layout=bfq.BFQ_W_PACKED16)   # so is the layout
         assert st == bfq.BFQ_WARN_DEFAULT_TILE
+        st, t = bfq.bfq_select_tile(64, 1536, 7168, scale_fmt=bfq.BFQ_SCALE_UE8M0)   # and the scales
+        assert st == bfq.BFQ_WARN_DEFAULT_TILE
     finally:
         bfq.bfq_load_tile_table(None)
 
@@ -187,6 +210,35 @@ def test_table_weight_layout_key(bfq, tmp_path):
     bad = tmp_path / "bad.json"
     bad.write_text(_table([{"N": 1536, "K": 7168, "dtype": "fp8_w8a8", "w_layout": "tiled",
                             "configs": {"16": cand}}]))
+    with pytest.raises(bfq.BfqError):
+        bfq.bfq_load_tile_table(str(bad))
+    bfq.bfq_load_tile_table(None)
+
+
+def test_table_scale_format_key(bfq, tmp_path):
+    """An entry marked "scales": "ue8m0" serves power-of-two scales only and may name
+    block-scaled-MFMA tiles; the same tile in an fp32 entry is rejected."""
+    sf = bfq.BFQ_SCALE_UE8M0
+    ue = [bfq.bfq_get_tile_candidate(i, bfq.BFQ_E4M3FN, 0, sf).as_dict()
+          for i in range(bfq.bfq_num_tile_candidates(bfq.BFQ_E4M3FN, 0, sf))]
+    t3 = next(d for d in ue if d["sched"] == 3)
+    p = tmp_path / "t.json"
+    p.write_text(_table([{"N": 1536, "K": 7168, "dtype": "fp8_w8a8", "scales": "ue8m0",
+                          "configs": {"4096": t3}}]))
+    try:
+        assert bfq.bfq_load_tile_table(str(p)) == bfq.BFQ_OK
+        st, t = bfq.bfq_select_tile(4096, 1536, 7168, scale_fmt=sf)
+        assert st == bfq.BFQ_OK and t.as_dict() == dict(t3, bk=128)
+        st, t = bfq.bfq_select_tile(4096, 1536, 7168)
+        assert st == bfq.BFQ_WARN_DEFAULT_TILE and t.sched != 3
+    finally:
+        bfq.bfq_load_tile_table(None)
+    bad = tmp_path / "bad.json"
+    bad.write_text(_table([{"N": 1536, "K": 7168, "dtype": "fp8_w8a8", "configs": {"4096": t3}}]))
+    with pytest.raises(bfq.BfqError):
+        bfq.bfq_load_tile_table(str(bad))
+    bad.write_text(_table([{"N": 1536, "K": 7168, "dtype": "fp8_w8a8", "scales": "e5m2",
+                            "configs": {"4096": t3}}]))
     with pytest.raises(bfq.BfqError):
         bfq.bfq_load_tile_table(str(bad))
     bfq.bfq_load_tile_table(None)
@@ -223,12 +275,16 @@ def test_default_rule(bfq, tmp_path):
         for M in (1, 8, 16, 31):
             st, t = bfq.bfq_select_tile(M, 24576, 7168)
             assert st == bfq.BFQ_WARN_DEFAULT_TILE and t.variant == 1
-        # the default tiles exist for both weight layouts
+        # the default tiles exist for both weight layouts and scale formats
         for wl in (bfq.BFQ_W_ROW_MAJOR, bfq.BFQ_W_PACKED16):
-            for M in (1, 31, 64, 200, 4096):
-                st, t = bfq.bfq_select_tile(M, 24576, 7168, w_layout=wl)
-                assert st == bfq.BFQ_WARN_DEFAULT_TILE
-                assert _gemm(bfq, M=0, N=24576, w_layout=wl, tile=ctypes.pointer(t)) >= 0
+            for sf in (bfq.BFQ_SCALE_FP32, bfq.BFQ_SCALE_UE8M0):
+                for M in (1, 31, 64, 200, 4096):
+                    st, t = bfq.bfq_select_tile(M, 24576, 7168, w_layout=wl, scale_fmt=sf)
+                    assert st == bfq.BFQ_WARN_DEFAULT_TILE
+                    assert _gemm(bfq, M=0, N=24576, w_layout=wl, scale_fmt=sf,
+                                 tile=ctypes.pointer(t)) >= 0
+        st, t = bfq.bfq_select_tile(4096, 24576, 7168, scale_fmt=bfq.BFQ_SCALE_UE8M0)
+        assert t.sched == 3
         for M in (32, 64, 4096):
             st, t = bfq.bfq_select_tile(M, 24576, 7168)
             assert t.variant == 0

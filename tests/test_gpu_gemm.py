@@ -7,7 +7,8 @@ Bar (see oracle/metrics.py):
   plus the straddle reading against the oracle's bf16 output;
   exact-integer inputs: fp32 output bit-exact; int8 block partials bit-exact.
 Kernels are checked with the weights row-major and packed (the packing done on the device
-by bfq_pack_weights, itself checked byte for byte against the oracle's pack16).
+by bfq_pack_weights, itself checked byte for byte against the oracle's pack16), and with
+UE8M0 (power-of-two) scales, where the block-scaled-MFMA tiles (sched 3) also run.
 """
 import numpy as np
 import pytest
@@ -20,22 +21,23 @@ DEV = "cuda:0"
 LAYOUTS = ["row", "packed"]
 
 
-def _case(orc, M, N, K, seed, qtype):
+def _case(orc, M, N, K, seed, qtype, sfmt=0):
     x = synth.activations(M, K, seed=seed)
     w = synth.weights(N, K, seed=seed + 1).numpy()
-    qa, sa = orc.quant_groups(synth.bf16_bits(x), qtype=qtype)
-    qw, sw = orc.quant_blocks(w, qtype=qtype)
+    qa, sa = orc.quant_groups(synth.bf16_bits(x), qtype=qtype, scale_fmt=sfmt)
+    qw, sw = orc.quant_blocks(w, qtype=qtype, scale_fmt=sfmt)
     return qa, sa, qw, sw
 
 
-def _to_dev(qa, sa, qw, sw, layout="row"):
-    """Device copies; with layout "packed" the weight codes are packed on the device."""
+def _to_dev(qa, sa, qw, sw, layout="row", sfmt=0):
+    """Device copies; with layout "packed" the weight codes are packed on the device. sfmt is
+    the scale format the GEMM is told (1: every scale a power of two)."""
     from block_scaled_w8a8_amd import bfq
     qw_d = torch.from_numpy(qw).to(DEV)
     if layout == "packed":
         qw_d = bfq.pack_weights(qw_d)
     return (torch.from_numpy(qa).to(DEV), torch.from_numpy(sa).to(DEV), qw_d,
-            torch.from_numpy(sw).to(DEV), layout)
+            torch.from_numpy(sw).to(DEV), layout, sfmt)
 
 
 def _wl(bfq, layout):
@@ -43,7 +45,7 @@ def _wl(bfq, layout):
 
 
 def _run(bfq, dq, out_dtype, tile=None, a_layout=None, sa_override=None):
-    qa, sa, qw, sw, wlay = dq
+    qa, sa, qw, sw, wlay, sf = dq
     wl = _wl(bfq, wlay)
     M, N = qa.shape[0], qw.shape[0]
     out = torch.full((M, N), float("nan"), dtype=out_dtype, device=DEV)
@@ -52,19 +54,20 @@ def _run(bfq, dq, out_dtype, tile=None, a_layout=None, sa_override=None):
     ws_bytes = bfq.bfq_gemm_workspace_bytes(M, N, qa.shape[1], tile) if tile is not None else 0
     if tile is None:
         st, t = bfq.bfq_select_tile(M, N, qa.shape[1], bfq._qdtype(qa), bfq._odtype(out),
-                                    w_layout=wl)
+                                    w_layout=wl, scale_fmt=sf)
         ws_bytes = bfq.bfq_gemm_workspace_bytes(M, N, qa.shape[1], t)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
     bfq.bfq_block_gemm(qa, sa_arg, qw, sw, out, a_layout=layout, a_scale_ld=sa_arg.stride(0),
-                       tile=tile, workspace=ws, workspace_bytes=ws_bytes, w_layout=wl)
+                       tile=tile, workspace=ws, workspace_bytes=ws_bytes, w_layout=wl,
+                       scale_fmt=sf)
     torch.cuda.synchronize()
     return out
 
 
-def _candidates(bfq, qd, layout="row"):
+def _candidates(bfq, qd, layout="row", sfmt=0):
     wl = _wl(bfq, layout)
-    return [bfq.bfq_get_tile_candidate(i, qd, wl)
-            for i in range(bfq.bfq_num_tile_candidates(qd, wl))]
+    return [bfq.bfq_get_tile_candidate(i, qd, wl, sfmt)
+            for i in range(bfq.bfq_num_tile_candidates(qd, wl, sfmt))]
 
 
 @pytest.mark.parametrize("N,K", [(128, 128), (640, 768), (1536, 7168), (24576, 7168)])
@@ -89,26 +92,28 @@ def _check_fp32(orc_metrics, out, ref, what):
     assert r["ok"], (what, r)
 
 
+@pytest.mark.parametrize("sfmt", [0, 1])
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("qname", ["fp8", "int8"])
-def test_every_candidate_and_split_parity(bfq, orc, qname, layout):
+def test_every_candidate_and_split_parity(bfq, orc, qname, layout, sfmt):
     """Every compiled kernel x split_k {1, 2, 3} x out dtype on a shape spanning several
-    tiles with ragged M (multiple tiles in N, K = 6 blocks so 3 splits are uneven-free)."""
+    tiles with ragged M (multiple tiles in N, K = 6 blocks so 3 splits are uneven-free),
+    for plain fp32 scales and for UE8M0 scales (every kernel that serves them)."""
     from oracle import metrics
     qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
     qt = orc.FP8 if qname == "fp8" else orc.INT8
     M, N, K = 83, 640, 768
-    host = _case(orc, M, N, K, 21, qt)
+    host = _case(orc, M, N, K, 21, qt, sfmt)
     ref32, ref16 = orc.block_gemm(*host, qtype=qt)
-    dq = _to_dev(*host, layout=layout)
-    cands = _candidates(bfq, qd, layout)
+    dq = _to_dev(*host, layout=layout, sfmt=sfmt)
+    cands = _candidates(bfq, qd, layout, sfmt)
     assert cands, (qname, layout)
     for t in cands:
         for s in (1, 2, 3):
             if t.variant == 2 and s > 1:        # stream-K splits K by itself
                 continue
             tile = _with_split(t, s)
-            what = (qname, layout, tile.as_dict())
+            what = (qname, layout, sfmt, tile.as_dict())
             print("candidate", what, flush=True)
             o32 = _run(bfq, dq, torch.float32, tile=tile).cpu().numpy()
             _check_fp32(metrics, o32, ref32, what)
@@ -122,9 +127,10 @@ def test_every_candidate_and_split_parity(bfq, orc, qname, layout):
             assert np.array_equal(oh, ref_h), what
 
 
+@pytest.mark.parametrize("sfmt", [0, 1])
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("qname", ["fp8", "int8"])
-def test_streamk_segments_and_determinism(bfq, orc, qname, layout):
+def test_streamk_segments_and_determinism(bfq, orc, qname, layout, sfmt):
     """Stream-K (variant 2) with few tiles and many K blocks: at M=300, N=640, K=896 a 256x256
     tile grid has 6 tiles of 7 blocks, so 42 one-block segments land on 42 workgroups and
     every tile is summed from 7 parked partials; fp32 within the bar of the oracle, bf16 the
@@ -134,10 +140,10 @@ def test_streamk_segments_and_determinism(bfq, orc, qname, layout):
     qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
     qt = orc.FP8 if qname == "fp8" else orc.INT8
     M, N, K = 300, 640, 896
-    host = _case(orc, M, N, K, 25, qt)
+    host = _case(orc, M, N, K, 25, qt, sfmt)
     ref32, _ = orc.block_gemm(*host, qtype=qt)
-    dq = _to_dev(*host, layout=layout)
-    sk = [t for t in _candidates(bfq, qd, layout) if t.variant == 2]
+    dq = _to_dev(*host, layout=layout, sfmt=sfmt)
+    sk = [t for t in _candidates(bfq, qd, layout, sfmt) if t.variant == 2]
     assert sk, "no stream-K kernel compiled for " + qname
     for t in sk:
         what = (qname, layout, t.as_dict())
@@ -160,9 +166,10 @@ def test_streamk_large_sampled(bfq, orc, M, N, K, layout):
         _sampled_check(bfq, orc, M, N, K, M, "fp8", n_samples=2048, tile=t, layout=layout)
 
 
+@pytest.mark.parametrize("sfmt", [0, 1])
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("qname", ["fp8", "int8"])
-def test_exact_integer_case_every_candidate(bfq, orc, qname, layout):
+def test_exact_integer_case_every_candidate(bfq, orc, qname, layout, sfmt):
     """P6 on the device: integer-valued codes with |v| <= 8 and power-of-two scales make
     every partial exact, so the fp32 output must equal the integer matmul bit for bit for
     every kernel and split."""
@@ -182,22 +189,23 @@ def test_exact_integer_case_every_candidate(bfq, orc, qname, layout):
     sa = np.full((M, K // 128), 2.0 ** -3, dtype=np.float32)
     sw = np.full((N // 128, K // 128), 2.0 ** -5, dtype=np.float32)
     exact = (ia.astype(np.int64) @ iw.T.astype(np.int64)).astype(np.float64) * 2.0 ** -8
-    dq = _to_dev(qa, sa, qw, sw, layout=layout)
-    for t in _candidates(bfq, qd, layout):
+    dq = _to_dev(qa, sa, qw, sw, layout=layout, sfmt=sfmt)   # the scales are powers of two
+    for t in _candidates(bfq, qd, layout, sfmt):
         for s in (1, 4):
             if t.variant == 2 and s > 1:
                 continue
             tile = _with_split(t, s)
             o32 = _run(bfq, dq, torch.float32, tile=tile).cpu().numpy().astype(np.float64)
-            assert np.array_equal(o32, exact), (qname, layout, tile.as_dict())
+            assert np.array_equal(o32, exact), (qname, layout, sfmt, tile.as_dict())
 
 
+@pytest.mark.parametrize("sfmt", [0, 1])
 @pytest.mark.parametrize("layout", LAYOUTS)
-def test_one_hot_rows_pin_layout(bfq, orc, layout):
+def test_one_hot_rows_pin_layout(bfq, orc, layout, sfmt):
     """A token row holding code 1.0 at one column reproduces that weight column times its
     block scale (fp32 product) on every kernel: pins the row/column/K index mapping."""
     M, N, K = 20, 256, 512
-    host = _case(orc, 1, N, K, 31, orc.FP8)
+    host = _case(orc, 1, N, K, 31, orc.FP8, sfmt)
     qw, sw = host[2], host[3]
     ks = [(m * 37 + 5) % K for m in range(M)]
     qa = np.zeros((M, K), dtype=np.uint8)
@@ -206,10 +214,10 @@ def test_one_hot_rows_pin_layout(bfq, orc, layout):
     sa = np.ones((M, K // 128), dtype=np.float32)
     deq = torch.from_numpy(qw).view(torch.float8_e4m3fn).float().numpy()
     want = np.stack([deq[:, k] * np.repeat(sw[:, k // 128], 128) for k in ks]).astype(np.float32)
-    dq = _to_dev(qa, sa, qw, sw, layout=layout)
-    for t in _candidates(bfq, bfq.BFQ_E4M3FN, layout):
+    dq = _to_dev(qa, sa, qw, sw, layout=layout, sfmt=sfmt)
+    for t in _candidates(bfq, bfq.BFQ_E4M3FN, layout, sfmt):
         o32 = _run(bfq, dq, torch.float32, tile=t).cpu().numpy()
-        assert np.array_equal(o32, want), (layout, t.as_dict())
+        assert np.array_equal(o32, want), (layout, sfmt, t.as_dict())
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (16, 1536, 7168), (130, 1536, 7168),
@@ -227,17 +235,18 @@ def test_int8_block_partials_bit_exact(bfq, orc, M, N, K):
     assert np.array_equal(part.cpu().numpy(), orc.block_partials_i32(qa, qw))
 
 
+@pytest.mark.parametrize("sfmt", [0, 1])
 @pytest.mark.parametrize("layout", LAYOUTS)
-def test_column_major_scales_and_padded_ld(bfq, orc, layout):
+def test_column_major_scales_and_padded_ld(bfq, orc, layout, sfmt):
     from oracle import metrics
     M, N, K = 50, 512, 1024
-    host = _case(orc, M, N, K, 51, orc.FP8)
+    host = _case(orc, M, N, K, 51, orc.FP8, sfmt)
     ref32, _ = orc.block_gemm(*host)
-    dq = _to_dev(*host, layout=layout)
+    dq = _to_dev(*host, layout=layout, sfmt=sfmt)
     sa = dq[1]
     sa_col = torch.full((K // 128, M + 3), float("nan"), device=DEV)
     sa_col[:, :M] = sa.t()
-    for t in _candidates(bfq, bfq.BFQ_E4M3FN, layout):
+    for t in _candidates(bfq, bfq.BFQ_E4M3FN, layout, sfmt):
         o = _run(bfq, dq, torch.float32, tile=t, a_layout=bfq.BFQ_SCALES_COL_MAJOR,
                  sa_override=sa_col)
         _check_fp32(metrics, o.cpu().numpy(), ref32, (layout, t.as_dict()))
@@ -304,8 +313,8 @@ CONFIGS = {
 _cache = {}
 
 
-def _full_inputs(bfq, N, K, m_max, qname):
-    key = (N, K, m_max, qname)
+def _full_inputs(bfq, N, K, m_max, qname, sfmt=0):
+    key = (N, K, m_max, qname, sfmt)
     if key not in _cache:
         _cache.clear()
         torch.cuda.empty_cache()
@@ -313,8 +322,8 @@ def _full_inputs(bfq, N, K, m_max, qname):
         x = synth.activations(m_max, K, seed=0)
         w = synth.weights(N, K, seed=0)
         xd, wd = x.to(DEV), w.to(DEV)
-        qw, sw = bfq.quant_weight_blocks(wd, q_dtype=qd)
-        qa, sa = bfq.quant_tokens(xd, q_dtype=qd)
+        qw, sw = bfq.quant_weight_blocks(wd, q_dtype=qd, scale_fmt=sfmt)
+        qa, sa = bfq.quant_tokens(xd, q_dtype=qd, scale_fmt=sfmt)
         qwp = bfq.pack_weights(qw)
         torch.cuda.synchronize()
         del wd
@@ -323,22 +332,24 @@ def _full_inputs(bfq, N, K, m_max, qname):
     return _cache[key]
 
 
-def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096, tile=None, layout="row"):
+def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096, tile=None, layout="row",
+                   sfmt=0):
     from oracle import metrics
     qt = orc.FP8 if qname == "fp8" else orc.INT8
-    qa, sa, qw, sw, qa_h, sa_h, qw_h, sw_h, qwp = _full_inputs(bfq, N, K, m_max, qname)
+    qa, sa, qw, sw, qa_h, sa_h, qw_h, sw_h, qwp = _full_inputs(bfq, N, K, m_max, qname, sfmt)
     wl = _wl(bfq, layout)
     qw_arg = qwp if layout == "packed" else qw
     out32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
     out16 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     if tile is None:
-        st, tile = bfq.bfq_select_tile(M, N, K, bfq._qdtype(qa), bfq.BFQ_FP32, w_layout=wl)
+        st, tile = bfq.bfq_select_tile(M, N, K, bfq._qdtype(qa), bfq.BFQ_FP32, w_layout=wl,
+                                       scale_fmt=sfmt)
     ws_bytes = bfq.bfq_gemm_workspace_bytes(M, N, K, tile)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
     bfq.bfq_block_gemm(qa[:M], sa[:M], qw_arg, sw, out32, tile=tile, workspace=ws,
-                       workspace_bytes=ws_bytes, w_layout=wl)
+                       workspace_bytes=ws_bytes, w_layout=wl, scale_fmt=sfmt)
     bfq.bfq_block_gemm(qa[:M], sa[:M], qw_arg, sw, out16, tile=tile, workspace=ws,
-                       workspace_bytes=ws_bytes, w_layout=wl)
+                       workspace_bytes=ws_bytes, w_layout=wl, scale_fmt=sfmt)
     torch.cuda.synchronize()
     rng = np.random.default_rng(M * 7 + N)
     ms = np.concatenate([rng.integers(0, M, n_samples), [0, M - 1, M - 1]])
@@ -347,13 +358,13 @@ def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096, tile=None, l
     o32 = out32.cpu().numpy()
     got = o32[ms, ns]
     r = metrics.gemm_fp32_report(got, ref)
-    assert r["ok"], (M, N, K, layout, tile.as_dict(), r)
+    assert r["ok"], (M, N, K, layout, sfmt, tile.as_dict(), r)
     o16 = out16.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(o16, orc.f32_to_bf16_bits_array(o32)), (M, N, K)
     # quantized inputs were produced on the device: they must equal the oracle's
     if M == m_max:
         x = synth.activations(m_max, K, seed=0)
-        qo, so = orc.quant_groups(synth.bf16_bits(x), qtype=qt)
+        qo, so = orc.quant_groups(synth.bf16_bits(x), qtype=qt, scale_fmt=sfmt)
         assert np.array_equal(qa_h.view(np.uint8), qo.view(np.uint8))
         assert np.array_equal(sa_h.view(np.uint32), so.view(np.uint32))
 
@@ -385,3 +396,13 @@ def test_config_dense(bfq, orc, M, N, K, layout):
 def test_config_int8(bfq, orc, M, layout):
     print(f"config int8 M={M} {layout}", flush=True)
     _sampled_check(bfq, orc, M, 1536, 7168, 4096, "int8", layout=layout)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(m, 24576, 7168) for m in (1, 64, 256, 1024, 2048, 4096)]
+                         + [(4096, 7168, 18432), (4096, 18432, 7168), (8, 1536, 1536)])
+def test_config_ue8m0(bfq, orc, M, N, K, layout):
+    """The workloads with UE8M0 scales (quantized on the device in that format, the GEMM told
+    so), through the tile the library selects: block-scaled-MFMA tiles at large M."""
+    print(f"config ue8m0 M={M} N={N} K={K} {layout}", flush=True)
+    _sampled_check(bfq, orc, M, N, K, 4096 if M > 8 else 8, "fp8", layout=layout, sfmt=1)

@@ -1,5 +1,5 @@
 """GPU parity of the quantizers (through the C-ABI) against the CPU oracle: codes and fp32
-scales must be bit-exact."""
+scales must be bit-exact, with plain fp32 scales and with UE8M0 (power-of-two) scales."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +13,7 @@ def _codes_np(t):
     return t.cpu().numpy()
 
 
-def _gpu_quant_tokens(bfq, x_cpu, qdtype, layout, ld_pad=0):
+def _gpu_quant_tokens(bfq, x_cpu, qdtype, layout, ld_pad=0, sfmt=0):
     dev = torch.device("cuda:0")
     x = x_cpu.to(dev)
     M, K = x.shape
@@ -26,7 +26,7 @@ def _gpu_quant_tokens(bfq, x_cpu, qdtype, layout, ld_pad=0):
         s = torch.full((M, G + ld_pad), float("nan"), dtype=torch.float32, device=dev)
     else:
         s = torch.full((G, M + ld_pad), float("nan"), dtype=torch.float32, device=dev)
-    bfq.bfq_quant_tokens(x, q, s, layout=layout, scale_ld=s.stride(0))
+    bfq.bfq_quant_tokens(x, q, s, layout=layout, scale_ld=s.stride(0), scale_fmt=sfmt)
     torch.cuda.synchronize()
     s = s.cpu().numpy()
     s = s[:, :G] if layout == bfq.BFQ_SCALES_ROW_MAJOR else s[:, :M].T.copy()
@@ -37,15 +37,17 @@ SHAPES = [(8, 1536), (1, 7168), (24, 1536), (37, 7168), (128, 7168), (64, 18432)
           (4096, 7168), (4096, 18432), (3, 128), (5, 640)]
 
 
+@pytest.mark.parametrize("sfmt", ["fp32", "ue8m0"])
 @pytest.mark.parametrize("M,K", SHAPES)
 @pytest.mark.parametrize("qname", ["fp8", "int8"])
-def test_quant_tokens_bit_exact(bfq, orc, M, K, qname):
-    print(f"quant_tokens M={M} K={K} {qname}", flush=True)
+def test_quant_tokens_bit_exact(bfq, orc, M, K, qname, sfmt):
+    print(f"quant_tokens M={M} K={K} {qname} {sfmt}", flush=True)
     qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
     ot = orc.FP8 if qname == "fp8" else orc.INT8
+    sf = 1 if sfmt == "ue8m0" else 0
     x = synth.activations(M, K, seed=M + K)
-    qg, sg = _gpu_quant_tokens(bfq, x, qd, bfq.BFQ_SCALES_ROW_MAJOR)
-    qo, so = orc.quant_groups(synth.bf16_bits(x), qtype=ot)
+    qg, sg = _gpu_quant_tokens(bfq, x, qd, bfq.BFQ_SCALES_ROW_MAJOR, sfmt=sf)
+    qo, so = orc.quant_groups(synth.bf16_bits(x), qtype=ot, scale_fmt=sf)
     assert np.array_equal(qg.view(np.uint8), qo.view(np.uint8))
     assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
 
@@ -83,41 +85,44 @@ def _special_input():
     return bits
 
 
+@pytest.mark.parametrize("sfmt", [0, 1])
 @pytest.mark.parametrize("qname", ["fp8", "int8"])
-def test_quant_tokens_special_values(bfq, orc, qname):
+def test_quant_tokens_special_values(bfq, orc, qname, sfmt):
     bits = _special_input()
     x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
     qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
     ot = orc.FP8 if qname == "fp8" else orc.INT8
-    qg, sg = _gpu_quant_tokens(bfq, x, qd, bfq.BFQ_SCALES_ROW_MAJOR)
-    qo, so = orc.quant_groups(bits, qtype=ot)
+    qg, sg = _gpu_quant_tokens(bfq, x, qd, bfq.BFQ_SCALES_ROW_MAJOR, sfmt=sfmt)
+    qo, so = orc.quant_groups(bits, qtype=ot, scale_fmt=sfmt)
     assert np.array_equal(qg.view(np.uint8), qo.view(np.uint8))
     nan_g, nan_o = np.isnan(sg), np.isnan(so)
     assert np.array_equal(nan_g, nan_o)
     assert np.array_equal(sg[~nan_g].view(np.uint32), so[~nan_o].view(np.uint32))
 
 
+@pytest.mark.parametrize("sfmt", [0, 1])
 @pytest.mark.parametrize("N,K", [(1536, 1536), (7168, 1536), (1536, 7168), (4096, 7168),
                                  (24576, 7168), (256, 384)])
 @pytest.mark.parametrize("qname", ["fp8", "int8"])
-def test_quant_weight_blocks_bit_exact(bfq, orc, N, K, qname):
+def test_quant_weight_blocks_bit_exact(bfq, orc, N, K, qname, sfmt):
     if N * K > 50_000_000 and qname == "int8":
         pytest.skip("the large shape is covered by the fp8 case")
-    print(f"quant_weight_blocks N={N} K={K} {qname}", flush=True)
+    print(f"quant_weight_blocks N={N} K={K} {qname} sfmt={sfmt}", flush=True)
     qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
     ot = orc.FP8 if qname == "fp8" else orc.INT8
     w = synth.weights(N, K, seed=N ^ K)
     wg = w.to("cuda:0")
     q = torch.empty((N, K), dtype=torch.uint8 if qname == "fp8" else torch.int8, device="cuda:0")
     s = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda:0")
-    bfq.bfq_quant_weight_blocks(wg, q, s)
+    bfq.bfq_quant_weight_blocks(wg, q, s, scale_fmt=sfmt)
     torch.cuda.synchronize()
-    qo, so = orc.quant_blocks(w.numpy(), qtype=ot)
+    qo, so = orc.quant_blocks(w.numpy(), qtype=ot, scale_fmt=sfmt)
     assert np.array_equal(q.cpu().numpy().view(np.uint8), qo.view(np.uint8))
     assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
 
 
-def test_weight_blocks_special_values(bfq, orc):
+@pytest.mark.parametrize("sfmt", [0, 1])
+def test_weight_blocks_special_values(bfq, orc, sfmt):
     w = synth.weights(256, 256, seed=1).numpy().copy()
     w[0:128, 0:128] = 0.0
     w[5, 130] = np.nan
@@ -127,9 +132,9 @@ def test_weight_blocks_special_values(bfq, orc):
     wg = torch.from_numpy(w).to("cuda:0")
     q = torch.empty((256, 256), dtype=torch.uint8, device="cuda:0")
     s = torch.empty((2, 2), dtype=torch.float32, device="cuda:0")
-    bfq.bfq_quant_weight_blocks(wg, q, s)
+    bfq.bfq_quant_weight_blocks(wg, q, s, scale_fmt=sfmt)
     torch.cuda.synchronize()
-    qo, so = orc.quant_blocks(w)
+    qo, so = orc.quant_blocks(w, scale_fmt=sfmt)
     assert np.array_equal(q.cpu().numpy(), qo)
     sg = s.cpu().numpy()
     assert np.array_equal(np.isnan(sg), np.isnan(so))
