@@ -45,6 +45,7 @@ EXPORTED = (
     "bfq_gemm_workspace_bytes", "bfq_block_gemm", "bfq_load_tile_table",
     "bfq_num_tile_candidates", "bfq_get_tile_candidate", "bfq_status_string",
     "bfq_last_error", "bfq_debug_block_partials_i32", "bfq_debug_encode",
+    "bfq_set_batch_invariant", "bfq_get_batch_invariant",
 )
 
 
@@ -107,6 +108,8 @@ def _load():
         "bfq_last_error": (ctypes.c_char_p, []),
         "bfq_debug_block_partials_i32": (i32, [p, p, p, i64, i64, i64, p]),
         "bfq_debug_encode": (i32, [p, i64, i32, p, p]),
+        "bfq_set_batch_invariant": (None, [i32]),
+        "bfq_get_batch_invariant": (i32, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -263,6 +266,14 @@ def bfq_get_tile_candidate(index, in_dtype=BFQ_E4M3FN, w_layout=BFQ_W_ROW_MAJOR,
 
 def bfq_status_string(s: int) -> str:
     return status_string(s)
+
+
+def bfq_set_batch_invariant(enable: bool) -> None:
+    lib.bfq_set_batch_invariant(1 if enable else 0)
+
+
+def bfq_get_batch_invariant() -> bool:
+    return bool(lib.bfq_get_batch_invariant())
 
 
 def bfq_last_error() -> str:

@@ -175,12 +175,57 @@ bfq_tile default_tile(int64_t M, int64_t N, int64_t K, int qtype, int sfmt) {
     return t;
 }
 
+// Batch-invariant tiles ([CONFIG] §5): every output element is computed by one 16x16x128
+// MFMA per K block (int8: two chained, exact) and fma(P, sa*sw, acc) in ascending block
+// order, whatever the tile. Excluded: split-K, in-workgroup K splits and stream-K (they sum
+// partial K ranges) and, with row-major weights, the swap-AB kernels (their token/weight
+// fragments take a different K order inside the MFMA than the standard kernel's).
+bfq_tile invariant_tile(int64_t M, int wlayout) {
+    bfq_tile t{};
+    t.bk = 128;
+    t.split_k = 1;
+    t.group_m = 8;
+    t.stages = 2;
+    t.waves_m = 1;
+    if (wlayout == W_PACKED16 && M <= 128) {
+        t.variant = 1;
+        if (M <= 16) {              // per-wave tokens, 4 strips of 32 rows
+            t.bm = 16; t.bn = 128; t.waves_n = 4; t.stages = 4; t.sched = 0;
+        } else {                    // tokens shared through LDS, 8 strips of 16 rows
+            t.bm = M <= 32 ? 32 : M <= 64 ? 64 : 128; t.bn = 128; t.waves_n = 8; t.stages = 4;
+            t.sched = 1;
+        }
+        t.group_m = 1;
+        return t;
+    }
+    t.variant = 0;
+    t.sched = 0;
+    if (M <= 64) { t.bm = 64; t.bn = 128; t.waves_m = 1; t.waves_n = 2; }
+    else if (M <= 512) { t.bm = 128; t.bn = 128; t.waves_m = 2; t.waves_n = 2; }
+    else { t.bm = 256; t.bn = 256; t.waves_m = 4; t.waves_n = 2; }
+    return t;
+}
+
+int g_batch_invariant = -1;   // -1: not yet read from the environment
+
+bool batch_invariant() {
+    if (g_batch_invariant < 0) {
+        const char* e = std::getenv("BFQ_BATCH_INVARIANT");
+        g_batch_invariant = (e && e[0] == '1') ? 1 : 0;
+    }
+    return g_batch_invariant == 1;
+}
+
 int qtype_of(bfq_dtype d) { return d == BFQ_E4M3FN ? Q_FP8 : Q_INT8; }
 
 int otype_of(bfq_dtype d) { return d == BFQ_BF16 ? O_BF16 : d == BFQ_FP16 ? O_FP16 : O_FP32; }
 
 bfq_status select_tile(int64_t M, int64_t N, int64_t K, int qtype, int wlayout, int sfmt,
                        bfq_tile* out) {
+    if (batch_invariant()) {
+        *out = invariant_tile(M, wlayout);
+        return BFQ_OK;
+    }
     ensure_table();
     {
         std::lock_guard<std::mutex> lk(g_table_mu);
@@ -236,6 +281,10 @@ const char* bfq_status_string(bfq_status s) {
 }
 
 const char* bfq_last_error(void) { return g_last_error.c_str(); }
+
+void bfq_set_batch_invariant(int32_t enable) { g_batch_invariant = enable ? 1 : 0; }
+
+int32_t bfq_get_batch_invariant(void) { return batch_invariant() ? 1 : 0; }
 
 bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t group_size,
                             bfq_dtype q_dtype, void* q, float* scales, bfq_scale_layout layout,

@@ -161,6 +161,19 @@ bfq_status bfq_select_tile(int64_t M, int64_t N, int64_t K, const int32_t block_
                            bfq_dtype in_dtype, bfq_dtype out_dtype, bfq_weight_layout w_layout,
                            bfq_scale_format scale_fmt, bfq_tile* tile_out);
 
+/* Batch-invariant mode ([CONFIG] §5: with the batch-invariant switch set, tuned configs are
+ * not used, so that the output of a token does not depend on how many tokens are in the
+ * batch). When enabled, bfq_select_tile ignores the tile table and returns tiles that
+ * compute every output element with the same operations in the same order for any M: no
+ * split-K, no K split inside a workgroup, no stream-K; with row-major weights only standard
+ * tiles (the swap-AB kernels feed the MFMA a different K order there); scales always applied
+ * by the fp32 FMA. Rows of the output are then bitwise independent of M. Process-wide;
+ * initialized from the environment variable BFQ_BATCH_INVARIANT (1 = on) at first use; must
+ * not be changed concurrently with other calls. Explicit tiles passed to bfq_block_gemm are
+ * not affected. */
+void    bfq_set_batch_invariant(int32_t enable);
+int32_t bfq_get_batch_invariant(void);
+
 /* Bytes of device workspace bfq_block_gemm needs for this shape and tile (split-K fp32
  * partials: split_k * M * N * 4 when split_k > 1; stream-K: two partial tiles per compute
  * unit; else 0). tile NULL -> the tile selected for e4m3fn codes in the row-major layout. */

@@ -313,3 +313,27 @@ def test_metric_formulas_reproduce_pages_table():
         sel = [r for r in rows if r[0] == impl]
         assert sum(float(r[5]) for r in sel) / 16 == pytest.approx(avg_tf, abs=0.01)
         assert sum(float(r[6]) for r in sel) / 16 == pytest.approx(avg_gbs, abs=0.01)
+
+
+def test_batch_invariant_selection(bfq):
+    """Batch-invariant mode (config page §5): tuned entries are ignored; every selected tile
+    is a compiled kernel with no split-K, no in-workgroup K split, no stream-K and the fp32
+    FMA scale step, and with row-major weights a standard tile."""
+    assert bfq.bfq_get_batch_invariant() in (False, True)
+    bfq.bfq_set_batch_invariant(True)
+    try:
+        assert bfq.bfq_get_batch_invariant()
+        for qd in (bfq.BFQ_E4M3FN, bfq.BFQ_INT8):
+            for wl in (bfq.BFQ_W_ROW_MAJOR, bfq.BFQ_W_PACKED16):
+                for sf in (bfq.BFQ_SCALE_FP32, bfq.BFQ_SCALE_UE8M0):
+                    for M in (1, 7, 16, 17, 33, 64, 65, 128, 129, 512, 513, 4096):
+                        st, t = bfq.bfq_select_tile(M, 24576, 7168, in_dtype=qd, w_layout=wl,
+                                                    scale_fmt=sf)
+                        assert st == bfq.BFQ_OK
+                        assert t.split_k == 1 and t.variant in (0, 1) and t.sched in (0, 1)
+                        assert t.variant == 0 or (t.waves_m == 1 and wl == bfq.BFQ_W_PACKED16)
+                        assert _gemm(bfq, M=0, N=24576, in_dtype=qd, w_layout=wl, scale_fmt=sf,
+                                     tile=ctypes.pointer(t)) >= 0, (qd, wl, sf, M, t.as_dict())
+    finally:
+        bfq.bfq_set_batch_invariant(False)
+    assert not bfq.bfq_get_batch_invariant()

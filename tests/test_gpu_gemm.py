@@ -406,3 +406,35 @@ def test_config_ue8m0(bfq, orc, M, N, K, layout):
     so), through the tile the library selects: block-scaled-MFMA tiles at large M."""
     print(f"config ue8m0 M={M} N={N} K={K} {layout}", flush=True)
     _sampled_check(bfq, orc, M, N, K, 4096 if M > 8 else 8, "fp8", layout=layout, sfmt=1)
+
+
+@pytest.mark.parametrize("sfmt", [0, 1])
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("qname", ["fp8", "int8"])
+def test_batch_invariant_mode_rows_bitwise(bfq, orc, qname, layout, sfmt):
+    """Batch-invariant mode (config page §5): the output rows of the first M tokens are
+    bitwise the same whatever M is — across every tile bracket the mode selects (swap-AB,
+    LDS-shared tokens, 64x128, 128x128, 256x256) — and within the parity bar of the oracle."""
+    from oracle import metrics
+    qt = orc.FP8 if qname == "fp8" else orc.INT8
+    qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
+    M_all, N, K = 600, 1536, 3072
+    host = _case(orc, M_all, N, K, 91, qt, sfmt)
+    ref32, _ = orc.block_gemm(*host, qtype=qt)
+    qa, sa, qw, sw, wlay, sf = _to_dev(*host, layout=layout, sfmt=sfmt)
+    bfq.bfq_set_batch_invariant(True)
+    try:
+        full = _run(bfq, (qa, sa, qw, sw, wlay, sf), torch.float32).cpu().numpy()
+        _check_fp32(metrics, full, ref32, (qname, layout, sfmt, "M=600"))
+        full16 = _run(bfq, (qa, sa, qw, sw, wlay, sf), torch.bfloat16).view(torch.int16).cpu().numpy()
+        for M in (1, 9, 16, 17, 40, 64, 65, 100, 128, 129, 300, 512, 513):
+            st, t = bfq.bfq_select_tile(M, N, K, qd, bfq.BFQ_FP32, w_layout=_wl(bfq, layout),
+                                        scale_fmt=sfmt)
+            print("batch-invariant", qname, layout, sfmt, M, t.as_dict(), flush=True)
+            dq = (qa[:M], sa[:M], qw, sw, wlay, sf)
+            o = _run(bfq, dq, torch.float32).cpu().numpy()
+            assert np.array_equal(o.view(np.uint32), full[:M].view(np.uint32)), (M, t.as_dict())
+            o16 = _run(bfq, dq, torch.bfloat16).view(torch.int16).cpu().numpy()
+            assert np.array_equal(o16, full16[:M]), (M, t.as_dict())
+    finally:
+        bfq.bfq_set_batch_invariant(False)
