@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.orc_block_gemm.argtypes = [p, p, p, p, i64, i64, i64, i32, p, p]
         L.orc_block_gemm_sampled.restype = None
         L.orc_block_gemm_sampled.argtypes = [p, p, p, p, i64, i64, i64, i32, p, p, i64, p]
+        L.orc_channel_gemm.restype = None
+        L.orc_channel_gemm.argtypes = [p, p, p, p, i64, i64, i64, i32, p, p]
+        L.orc_channel_gemm_sampled.restype = None
+        L.orc_channel_gemm_sampled.argtypes = [p, p, p, p, i64, i64, i64, i32, p, p, i64, p]
         L.orc_block_partials_i32.restype = None
         L.orc_block_partials_i32.argtypes = [p, p, i64, i64, i64, p]
         L.orc_dequant_gemm_f64.restype = None
@@ -215,6 +219,40 @@ def block_gemm_sampled(qa, sa, qw, sw, ms, ns, qtype: int = FP8):
     out = np.empty(ms.shape, dtype=np.float32)
     lib().orc_block_gemm_sampled(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, qtype,
                                  _ptr(ms), _ptr(ns), ms.size, _ptr(out))
+    return out
+
+
+def _channel_args(qa, sa, qw, sw, qtype):
+    qa = np.ascontiguousarray(qa, dtype=_code_dtype(qtype))
+    qw = np.ascontiguousarray(qw, dtype=_code_dtype(qtype))
+    sa = np.ascontiguousarray(np.asarray(sa, dtype=np.float32).reshape(-1))
+    sw = np.ascontiguousarray(np.asarray(sw, dtype=np.float32).reshape(-1))
+    M, K = qa.shape
+    N, K2 = qw.shape
+    assert K == K2 and sa.shape == (M,) and sw.shape == (N,)
+    return qa, sa, qw, sw, M, N, K
+
+
+def channel_gemm(qa, sa, qw, sw, qtype: int = FP8):
+    """Per-token x per-channel GEMM: sa [M] (or [M, 1]), sw [N] (or [N, 1]).
+    Returns (c32 [M, N] float32, c16 [M, N] uint16 bf16 bits)."""
+    qa, sa, qw, sw, M, N, K = _channel_args(qa, sa, qw, sw, qtype)
+    c32 = np.empty((M, N), dtype=np.float32)
+    c16 = np.empty((M, N), dtype=np.uint16)
+    lib().orc_channel_gemm(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, qtype,
+                           _ptr(c32), _ptr(c16))
+    return c32, c16
+
+
+def channel_gemm_sampled(qa, sa, qw, sw, ms, ns, qtype: int = FP8):
+    qa, sa, qw, sw, M, N, K = _channel_args(qa, sa, qw, sw, qtype)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    assert ms.shape == ns.shape and ms.ndim == 1
+    assert (ms >= 0).all() and (ms < M).all() and (ns >= 0).all() and (ns < N).all()
+    out = np.empty(ms.shape, dtype=np.float32)
+    lib().orc_channel_gemm_sampled(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, qtype,
+                                   _ptr(ms), _ptr(ns), ms.size, _ptr(out))
     return out
 
 

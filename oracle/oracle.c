@@ -243,6 +243,58 @@ void orc_block_gemm_sampled(const void* qa, const float* sa, const void* qw, con
         c32[i] = gemm_element(qa, sa, qw, sw, ms[i], ns[i], K, qtype);
 }
 
+/* ----------------------------------------------- per-token x per-channel GEMM ---- */
+
+/* [HELION] scope section: in the FP8_Dynamic and W8A8_INT8 formats every token row of the
+ * activations has one scale and every output channel (weight row) has one. Reading: the dot
+ * product of the codes over the whole of K is taken exactly, rounded once to fp32, then
+ * multiplied by the token scale and then by the channel scale (the left-to-right order the
+ * block path uses within a block). Exactness: e4m3 products are multiples of 2^-18 below
+ * 2^18 in magnitude, so a sum of K of them needs fewer than 53 bits while K < 2^17; int8
+ * sums are exact in int64. */
+static float channel_element(const void* qa, const float* sa, const void* qw, const float* sw,
+                             int64_t m, int64_t n, int64_t K, int qtype) {
+    float p;
+    if (qtype == ORC_FP8) {
+        const uint8_t* a = (const uint8_t*)qa + m * K;
+        const uint8_t* w = (const uint8_t*)qw + n * K;
+        double sum = 0.0;
+        for (int64_t k = 0; k < K; ++k) sum += g_dec[a[k]] * g_dec[w[k]];
+        p = (float)sum;
+    } else {
+        const int8_t* a = (const int8_t*)qa + m * K;
+        const int8_t* w = (const int8_t*)qw + n * K;
+        int64_t sum = 0;
+        for (int64_t k = 0; k < K; ++k) sum += (int64_t)a[k] * (int64_t)w[k];
+        p = (float)sum;
+    }
+    float t = p * sa[m];
+    t = t * sw[n];
+    return t;
+}
+
+void orc_channel_gemm(const void* qa, const float* sa, const void* qw, const float* sw,
+                      int64_t M, int64_t N, int64_t K, int qtype, float* c32, uint16_t* c16) {
+    init_decode_table();
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float v = channel_element(qa, sa, qw, sw, m, n, K, qtype);
+            if (c32) c32[m * N + n] = v;
+            if (c16) c16[m * N + n] = orc_f32_to_bf16(v);
+        }
+}
+
+void orc_channel_gemm_sampled(const void* qa, const float* sa, const void* qw, const float* sw,
+                              int64_t M, int64_t N, int64_t K, int qtype,
+                              const int64_t* ms, const int64_t* ns, int64_t count, float* c32) {
+    (void)M; (void)N;
+    init_decode_table();
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < count; ++i)
+        c32[i] = channel_element(qa, sa, qw, sw, ms[i], ns[i], K, qtype);
+}
+
 void orc_block_partials_i32(const int8_t* qa, const int8_t* qw, int64_t M, int64_t N,
                             int64_t K, int32_t* out) {
     int64_t KB = K / 128;

@@ -70,6 +70,15 @@ void orc_block_gemm_sampled(const void* qa, const float* sa, const void* qw, con
                             int64_t M, int64_t N, int64_t K, int qtype,
                             const int64_t* ms, const int64_t* ns, int64_t count, float* c32);
 
+/* Per-token x per-channel GEMM (FP8_Dynamic / W8A8_INT8):
+ * C[m][n] = ((float)(sum_k A[m,k] W[n,k]) * sa[m]) * sw[n], the code dot product over the
+ * whole K exact (fp64 for fp8 while K < 2^17, int64 for int8). sa[M], sw[N]. */
+void orc_channel_gemm(const void* qa, const float* sa, const void* qw, const float* sw,
+                      int64_t M, int64_t N, int64_t K, int qtype, float* c32, uint16_t* c16);
+void orc_channel_gemm_sampled(const void* qa, const float* sa, const void* qw, const float* sw,
+                              int64_t M, int64_t N, int64_t K, int qtype,
+                              const int64_t* ms, const int64_t* ns, int64_t count, float* c32);
+
 /* int8 only: exact per-128-K-block integer partials, layout [K/128][M][N]. */
 void orc_block_partials_i32(const int8_t* qa, const int8_t* qw, int64_t M, int64_t N,
                             int64_t K, int32_t* out);

@@ -452,3 +452,168 @@ def test_ue8m0_calc_diff_matches_pages_accuracy(orc):
         _, c16 = orc.block_gemm(qa, sa, qw, sw)
         d = calc_diff(bf16_bits_to_f32(c16), c_ref)
         assert 6.0e-4 <= d <= 7.7e-4, (a_fmt, d)
+
+
+# ------------------------------------------- per-token x per-channel formats
+# Helion linear-backend page, scope section: FP8_Dynamic and W8A8_INT8 scale activations per
+# token and weights per output channel. The oracle reaches them through group = K (tokens)
+# and block = (1, K) (channels) of the same quantizers, and through channel_gemm.
+
+@pytest.mark.parametrize("qname", ["fp8", "int8"])
+def test_token_quant_invariants(orc, qname):
+    """Per token: scale = row amax / Qmax (amax from numpy), the largest |code| of each row
+    is the top code (0x7E / 127), codes within half a step of x / scale, and an all-zero row
+    gets codes 0 and scale eps / Qmax."""
+    qt = orc.FP8 if qname == "fp8" else orc.INT8
+    Q = np.float32(448 if qname == "fp8" else 127)
+    M, K = 6, 1536
+    x = synth.activations(M, K, seed=21)
+    bits = synth.bf16_bits(x).copy()
+    bits[5] = 0
+    q, s = orc.quant_groups(bits, group=K, qtype=qt)
+    assert s.shape == (M, 1)
+    xf = x.float().numpy()
+    xf[5] = 0
+    amax = np.abs(xf).max(axis=1)
+    assert np.array_equal(s[:5, 0], (amax[:5] / Q).astype(np.float32))
+    assert s[5, 0] == np.float32(np.float32(1e-10) / Q) and (q[5] == 0).all()
+    if qt == orc.FP8:
+        assert ((q[:5] & 0x7F).max(axis=1) == 0x7E).all()
+        deq = _dequant_fp8(q)
+        bound = np.maximum(2.0 ** -4 * np.abs(xf), 2.0 ** -10 * s.astype(np.float64))
+    else:
+        assert (np.abs(q[:5].astype(np.int32)).max(axis=1) == 127).all()
+        deq = q.astype(np.float64)
+        bound = 0.5 * s.astype(np.float64) * np.ones_like(xf, dtype=np.float64)
+    err = np.abs(deq * s.astype(np.float64) - xf)
+    assert (err <= bound * (1 + 1e-6)).all()
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+def test_token_scale_is_max_of_group_scales(orc, fmt):
+    """max(amax, eps) / Qmax and the rounding up to a power of two are monotonic, so a token's
+    scale is the largest of its 1x128 group scales, and every group whose scale equals it
+    gets the same codes in both granularities."""
+    sf = orc.SCALE_FP32 if fmt == "fp32" else orc.SCALE_UE8M0
+    M, K = 8, 7168
+    bits = synth.bf16_bits(synth.activations(M, K, seed=22))
+    qg, sg = orc.quant_groups(bits, qtype=orc.FP8, scale_fmt=sf)
+    qt, st = orc.quant_groups(bits, group=K, qtype=orc.FP8, scale_fmt=sf)
+    assert np.array_equal(st[:, 0], sg.max(axis=1))
+    hits = 0
+    for m in range(M):
+        for g in np.nonzero(sg[m] == st[m, 0])[0]:
+            assert np.array_equal(qt[m, g * 128:(g + 1) * 128], qg[m, g * 128:(g + 1) * 128])
+            hits += 1
+    assert hits >= M
+
+
+def test_token_quant_worked_values(orc):
+    """Worked from the definition: a row whose largest magnitude is 896 has scale 2 (fp8),
+    so 1.0 encodes as 0.5 (0x30) and 896 as 448 (0x7E); int8 with amax 254 has scale 2,
+    3.0 -> 1.5 -> 2 (ties to even) and 5.0 -> 2.5 -> 2."""
+    x = np.ones((2, 256), dtype=np.float32)
+    x[0, 17] = -896.0
+    x[1, :] = 0.0
+    x[1, 3], x[1, 4], x[1, 200] = 3.0, 5.0, 254.0
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q, s = orc.quant_groups(bits.copy(), group=256, qtype=orc.FP8)
+    assert s[0, 0] == 2.0 and q[0, 17] == 0xFE and q[0, 0] == 0x30
+    qi, si = orc.quant_groups(bits.copy(), group=256, qtype=orc.INT8)
+    assert si[1, 0] == 2.0 and qi[1, 3] == 2 and qi[1, 4] == 2 and qi[1, 200] == 127
+
+
+def test_channel_quant_invariants(orc):
+    """Per output channel (block 1 x K): scale = row amax / 448, top code in every row, codes
+    within half a step; int8 max |q| = 127 per row."""
+    N, K = 256, 1536
+    w = synth.weights(N, K, seed=23).numpy()
+    q, s = orc.quant_blocks(w, block=(1, K))
+    assert s.shape == (N, 1)
+    assert np.array_equal(s[:, 0], (np.abs(w).max(axis=1) / np.float32(448)).astype(np.float32))
+    assert ((q & 0x7F).max(axis=1) == 0x7E).all()
+    err = np.abs(_dequant_fp8(q) * s.astype(np.float64) - w)
+    assert (err <= np.maximum(2.0 ** -4 * np.abs(w), 2.0 ** -10 * s.astype(np.float64)) * (1 + 1e-6)).all()
+    qi, si = orc.quant_blocks(w, block=(1, K), qtype=orc.INT8)
+    assert (np.abs(qi.astype(np.int32)).max(axis=1) == 127).all()
+
+
+def _channel_case(M, N, K, seed, qtype):
+    import oracle as orc
+    x = synth.activations(M, K, seed=seed)
+    w = synth.weights(N, K, seed=seed).numpy()
+    qa, sa = orc.quant_groups(synth.bf16_bits(x), group=K, qtype=qtype)
+    qw, sw = orc.quant_blocks(w, block=(1, K), qtype=qtype)
+    return qa, sa[:, 0].copy(), qw, sw[:, 0].copy()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (3, 256, 384), (8, 128, 1536)])
+def test_channel_gemm_vs_fp64_dequant_matmul(orc, M, N, K):
+    """Against an fp64 dequantize-then-matmul from library routines (torch's e4m3fn decode,
+    numpy fp64 matmul): |C32 - D| <= 1e-5 * rms(D)."""
+    qa, sa, qw, sw = _channel_case(M, N, K, 24, orc.FP8)
+    c32, c16 = orc.channel_gemm(qa, sa, qw, sw)
+    d = (_dequant_fp8(qa) * sa.astype(np.float64)[:, None]) @ \
+        (_dequant_fp8(qw) * sw.astype(np.float64)[:, None]).T
+    assert np.abs(c32 - d).max() <= 1e-5 * np.sqrt((d * d).mean())
+    ref16 = torch.from_numpy(c32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(c16, ref16)
+
+
+def test_channel_gemm_exact_integer_case(orc):
+    """Codes restricted to e4m3 integers |v| <= 8, token scales 2^-(m mod 3) and channel
+    scales 2^-(n mod 4): every step is exact in fp32, so the result is the numpy int64 matmul
+    times the two powers of two exactly. Scales that differ per row and per column catch a
+    transposed or mis-indexed scale."""
+    rng = np.random.default_rng(25)
+    enc = {int(v): torch.tensor([float(v)]).to(torch.float8_e4m3fn).view(torch.uint8).item()
+           for v in range(-8, 9)}
+    M, N, K = 6, 256, 1024
+    ia = rng.integers(-8, 9, size=(M, K))
+    iw = rng.integers(-8, 9, size=(N, K))
+    qa = np.vectorize(enc.get)(ia).astype(np.uint8)
+    qw = np.vectorize(enc.get)(iw).astype(np.uint8)
+    ea = -(np.arange(M) % 3)
+    ew = -(np.arange(N) % 4)
+    sa = (2.0 ** ea).astype(np.float32)
+    sw = (2.0 ** ew).astype(np.float32)
+    c32, _ = orc.channel_gemm(qa, sa, qw, sw)
+    exact = (ia.astype(np.int64) @ iw.T.astype(np.int64)).astype(np.float64)
+    exact *= (2.0 ** ea)[:, None] * (2.0 ** ew)[None, :]
+    assert np.array_equal(c32.astype(np.float64), exact)
+
+
+def test_channel_gemm_int8_is_rounded_exact_dot(orc):
+    """int8: the dot product over the whole K is the numpy int64 matmul, rounded once to
+    fp32 and scaled token-then-channel; sums beyond 2^24 exercise that single rounding."""
+    qa, sa, qw, sw = _channel_case(4, 128, 7168, 26, orc.INT8)
+    rng = np.random.default_rng(26)
+    qa[2:] = rng.integers(60, 128, size=(2, 7168)).astype(np.int8)   # same-sign rows:
+    qw[64:] = rng.integers(60, 128, size=(64, 7168)).astype(np.int8)  # sums near 6e7
+    c32, _ = orc.channel_gemm(qa, sa, qw, sw, qtype=orc.INT8)
+    p = qa.astype(np.int64) @ qw.astype(np.int64).T
+    assert np.abs(p).max() > 2 ** 24 and (p.astype(np.float32).astype(np.int64) != p).any()
+    ref = (p.astype(np.float32) * sa[:, None]).astype(np.float32) * sw[None, :]
+    assert np.array_equal(c32, ref.astype(np.float32))
+
+
+def test_channel_gemm_agrees_with_block_gemm(orc):
+    """With every group of a token sharing its scale and every 128 channels sharing one
+    scale, the block-scaled GEMM computes the same quantity by another summation order."""
+    qa, sa, qw, sw = _channel_case(5, 256, 768, 27, orc.FP8)
+    sw = np.repeat(sw.reshape(2, 128)[:, :1], 128, axis=1).reshape(-1).copy()
+    c_ch, _ = orc.channel_gemm(qa, sa, qw, sw)
+    sa_b = np.repeat(sa[:, None], 768 // 128, axis=1)
+    sw_b = np.repeat(sw.reshape(2, 128)[:, :1], 768 // 128, axis=1)
+    c_bl, _ = orc.block_gemm(qa, sa_b, qw, sw_b)
+    rms = np.sqrt((c_bl.astype(np.float64) ** 2).mean())
+    assert np.abs(c_ch.astype(np.float64) - c_bl).max() <= 1e-5 * rms
+
+
+def test_channel_gemm_sampled_matches_full(orc):
+    qa, sa, qw, sw = _channel_case(9, 384, 256, 28, orc.INT8)
+    c32, _ = orc.channel_gemm(qa, sa, qw, sw, qtype=orc.INT8)
+    rng = np.random.default_rng(1)
+    ms = rng.integers(0, 9, 100)
+    ns = rng.integers(0, 384, 100)
+    assert np.array_equal(orc.channel_gemm_sampled(qa, sa, qw, sw, ms, ns, qtype=orc.INT8), c32[ms, ns])
