@@ -39,6 +39,14 @@ BFQ_SCALE_UE8M0 = 1
 
 DEFAULT_EPS = 1e-10
 BLOCK_SHAPE = (128, 128)
+# Maximum K of the per-token x per-channel format (block_shape (1, K)).
+CHANNEL_MAX_K = 32768
+
+
+def channel_block_shape(K: int):
+    """block_shape of the per-token x per-channel format (one scale per token and per output
+    channel; Helion linear-backend page, scope section)."""
+    return (1, int(K))
 
 EXPORTED = (
     "bfq_quant_tokens", "bfq_quant_weight_blocks", "bfq_pack_weights", "bfq_select_tile",
@@ -102,8 +110,8 @@ def _load():
         "bfq_block_gemm": (i32, [p, p, i32, i64, p, p, i32, i32, p, i64, i64, i64, bs, i32, i32,
                                  tp, p, sz, p]),
         "bfq_load_tile_table": (i32, [ctypes.c_char_p]),
-        "bfq_num_tile_candidates": (i32, [i32, i32, i32]),
-        "bfq_get_tile_candidate": (i32, [i32, i32, i32, i32, tp]),
+        "bfq_num_tile_candidates": (i32, [bs, i32, i32, i32]),
+        "bfq_get_tile_candidate": (i32, [bs, i32, i32, i32, i32, tp]),
         "bfq_status_string": (ctypes.c_char_p, [i32]),
         "bfq_last_error": (ctypes.c_char_p, []),
         "bfq_debug_block_partials_i32": (i32, [p, p, p, i64, i64, i64, p]),
@@ -181,7 +189,8 @@ def bfq_quant_tokens(x, q, scales, layout=BFQ_SCALES_ROW_MAJOR, scale_ld=None,
                      eps=DEFAULT_EPS, group_size=128, stream=None,
                      scale_fmt=BFQ_SCALE_FP32) -> int:
     """x: bf16 [M, K]; q: uint8/float8_e4m3fn (e4m3fn codes) or int8 [M, K];
-    scales: fp32, [M, ld] (row-major) or [K/128, ld] (column-major)."""
+    scales: fp32, [M, ld] (row-major) or [K/group_size, ld] (column-major). group_size 128,
+    or K for one scale per token."""
     M, K = x.shape
     if scale_ld is None:
         scale_ld = scales.stride(0)
@@ -192,7 +201,8 @@ def bfq_quant_tokens(x, q, scales, layout=BFQ_SCALES_ROW_MAJOR, scale_ld=None,
 
 def bfq_quant_weight_blocks(w, q, scales, eps=DEFAULT_EPS, block_shape=BLOCK_SHAPE,
                             stream=None, scale_fmt=BFQ_SCALE_FP32) -> int:
-    """w: fp32 [N, K]; q: codes [N, K]; scales: fp32 [N/128, K/128]."""
+    """w: fp32 [N, K]; q: codes [N, K]; scales: fp32 [N/128, K/128], or [N] (any shape of N
+    contiguous floats) with block_shape (1, K)."""
     N, K = w.shape
     st = lib.bfq_quant_weight_blocks(_ptr(w), N, K, _block_shape(block_shape), _qdtype(q),
                                      _ptr(q), _ptr(scales), eps, scale_fmt, _stream(stream))
@@ -231,7 +241,8 @@ def bfq_block_gemm(a_q, a_scales, w_q, w_scales, out, a_layout=BFQ_SCALES_ROW_MA
     """a_q [M, K] codes, w_q [N, K] codes in w_layout (row-major, or packed by
     bfq_pack_weights and still shaped [N, K]), a_scales per layout, w_scales [N/128, K/128],
     out [M, N] (bf16 / fp16 / fp32). scale_fmt BFQ_SCALE_UE8M0 declares every scale a power
-    of two. Returns the status (>= 0)."""
+    of two. block_shape (1, K): per-token a_scales ([M, 1] or [1, M]) and per-channel
+    w_scales [N]. Returns the status (>= 0)."""
     M, K = a_q.shape
     N = w_q.shape[0]
     if a_scale_ld is None:
@@ -252,14 +263,16 @@ def bfq_load_tile_table(path=None) -> int:
 
 
 def bfq_num_tile_candidates(in_dtype=BFQ_E4M3FN, w_layout=BFQ_W_ROW_MAJOR,
-                            scale_fmt=BFQ_SCALE_FP32) -> int:
-    return int(lib.bfq_num_tile_candidates(in_dtype, w_layout, scale_fmt))
+                            scale_fmt=BFQ_SCALE_FP32, block_shape=BLOCK_SHAPE) -> int:
+    return int(lib.bfq_num_tile_candidates(_block_shape(block_shape), in_dtype, w_layout,
+                                           scale_fmt))
 
 
 def bfq_get_tile_candidate(index, in_dtype=BFQ_E4M3FN, w_layout=BFQ_W_ROW_MAJOR,
-                           scale_fmt=BFQ_SCALE_FP32) -> bfq_tile:
+                           scale_fmt=BFQ_SCALE_FP32, block_shape=BLOCK_SHAPE) -> bfq_tile:
     t = bfq_tile()
-    _check(lib.bfq_get_tile_candidate(in_dtype, w_layout, scale_fmt, index, ctypes.byref(t)),
+    _check(lib.bfq_get_tile_candidate(_block_shape(block_shape), in_dtype, w_layout, scale_fmt,
+                                      index, ctypes.byref(t)),
            "bfq_get_tile_candidate")
     return t
 
@@ -296,29 +309,38 @@ def bfq_debug_encode(x, codes, q_dtype=BFQ_E4M3FN, stream=None) -> int:
 # ------------------------------------------------------------ allocating conveniences
 
 def quant_tokens(x, q_dtype=BFQ_E4M3FN, layout=BFQ_SCALES_ROW_MAJOR, eps=DEFAULT_EPS,
-                 stream=None, scale_fmt=BFQ_SCALE_FP32):
-    """Allocate (q, scales) with torch and run bfq_quant_tokens. Returns (q, scales)."""
+                 stream=None, scale_fmt=BFQ_SCALE_FP32, per_token=False):
+    """Allocate (q, scales) with torch and run bfq_quant_tokens. Returns (q, scales); with
+    per_token the scales are [M, 1] (row-major) or [1, M] (column-major)."""
     import torch
     M, K = x.shape
+    group = K if per_token else 128
     q = torch.empty((M, K), dtype=torch.uint8 if q_dtype == BFQ_E4M3FN else torch.int8,
                     device=x.device)
     if layout == BFQ_SCALES_ROW_MAJOR:
-        s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+        s = torch.empty((M, K // group), dtype=torch.float32, device=x.device)
     else:
-        s = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
+        s = torch.empty((K // group, M), dtype=torch.float32, device=x.device)
     bfq_quant_tokens(x, q, s, layout=layout, scale_ld=s.stride(0), eps=eps, stream=stream,
-                     scale_fmt=scale_fmt)
+                     scale_fmt=scale_fmt, group_size=group)
     return q, s
 
 
 def quant_weight_blocks(w, q_dtype=BFQ_E4M3FN, eps=DEFAULT_EPS, stream=None,
-                        scale_fmt=BFQ_SCALE_FP32):
+                        scale_fmt=BFQ_SCALE_FP32, per_channel=False):
+    """Allocate (q, scales) with torch and run bfq_quant_weight_blocks; per_channel gives one
+    scale per output channel (scales [N])."""
     import torch
     N, K = w.shape
     q = torch.empty((N, K), dtype=torch.uint8 if q_dtype == BFQ_E4M3FN else torch.int8,
                     device=w.device)
-    s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
-    bfq_quant_weight_blocks(w, q, s, eps=eps, stream=stream, scale_fmt=scale_fmt)
+    if per_channel:
+        s = torch.empty((N,), dtype=torch.float32, device=w.device)
+        bs = channel_block_shape(K)
+    else:
+        s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+        bs = BLOCK_SHAPE
+    bfq_quant_weight_blocks(w, q, s, eps=eps, stream=stream, scale_fmt=scale_fmt, block_shape=bs)
     return q, s
 
 
@@ -332,20 +354,23 @@ def pack_weights(w_q, stream=None):
 
 
 def block_gemm(a_q, a_scales, w_q, w_scales, out_dtype=None, a_layout=BFQ_SCALES_ROW_MAJOR,
-               tile=None, stream=None, w_layout=BFQ_W_ROW_MAJOR, scale_fmt=BFQ_SCALE_FP32):
-    """Allocate out (and split-K workspace) with torch and run bfq_block_gemm."""
+               tile=None, stream=None, w_layout=BFQ_W_ROW_MAJOR, scale_fmt=BFQ_SCALE_FP32,
+               per_channel=False):
+    """Allocate out (and split-K workspace) with torch and run bfq_block_gemm; per_channel
+    selects the per-token x per-channel format (block_shape (1, K))."""
     import torch
     out_dtype = out_dtype or torch.bfloat16
     M, K = a_q.shape
     N = w_q.shape[0]
+    bs = channel_block_shape(K) if per_channel else BLOCK_SHAPE
     out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
     if tile is None:
         st, tile = bfq_select_tile(M, N, K, _qdtype(a_q), _odtype(out), w_layout=w_layout,
-                                   scale_fmt=scale_fmt)
+                                   scale_fmt=scale_fmt, block_shape=bs)
         _check(st, "bfq_select_tile", warn_key=(N, K))
     ws_bytes = bfq_gemm_workspace_bytes(M, N, K, tile)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=a_q.device) if ws_bytes else None
     bfq_block_gemm(a_q, a_scales, w_q, w_scales, out, a_layout=a_layout, tile=tile,
                    workspace=ws, workspace_bytes=ws_bytes, stream=stream, w_layout=w_layout,
-                   scale_fmt=scale_fmt)
+                   scale_fmt=scale_fmt, block_shape=bs)
     return out

@@ -7,7 +7,8 @@
 //            64 and K a multiple of 128)
 //   [CONFIG] "vLLM 量化 Kernel 配置机制 ..." §4.1-§4.2 (lookup, nearest M, warning + default)
 //   [HELION] "Building a High-Performance and Portable vLLM Linear Backend with Helion",
-//            kernel section (swap-AB below 32 tokens on Hopper; split-K for small M/N)
+//            scope section (per-token x per-channel scale formats), kernel section (swap-AB
+//            below 32 tokens on Hopper; split-K for small M/N)
 #include <dlfcn.h>
 
 #include <cstdio>
@@ -114,9 +115,13 @@ bool same_shape(const bfq_tile& a, const bfq_tile& b) {
     return a.sched == b.sched;
 }
 
-// A kernel serves scale format sfmt if it takes any fp32 scales (S_FP32) or if the scales are
-// declared powers of two (a S_UE8M0 kernel applies them inside the MFMA).
-bool serves(const KernelEntry& k, int sfmt) { return k.sfmt == S_FP32 || sfmt == S_UE8M0; }
+// A kernel serves scale format sfmt if it takes any fp32 block scales (S_FP32) or if the block
+// scales are declared powers of two (a S_UE8M0 kernel applies them inside the MFMA);
+// per-token x per-channel scales (S_CHANNEL) need a kernel built for them.
+bool serves(const KernelEntry& k, int sfmt) {
+    if (sfmt == S_CHANNEL || k.sfmt == S_CHANNEL) return k.sfmt == sfmt;
+    return k.sfmt == S_FP32 || sfmt == S_UE8M0;
+}
 
 const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype, int wlayout, int sfmt) {
     if (t.bk != 0 && t.bk != 128) return nullptr;
@@ -167,8 +172,9 @@ bfq_tile default_tile(int64_t M, int64_t N, int64_t K, int qtype, int sfmt) {
         t.waves_n = shapes[pick][3];
         t.stages = 2;
         t.group_m = 8;
-        // power-of-two fp8 scales: the block-scaled MFMA schedule where it is compiled
-        t.sched = (qtype == Q_FP8 && sfmt == S_UE8M0 && pick < 3) ? 3 : 0;
+        // power-of-two fp8 scales: the block-scaled MFMA schedule where it is compiled;
+        // per-token x per-channel scales: the whole-K accumulation schedule
+        t.sched = sfmt == S_CHANNEL ? 4 : (qtype == Q_FP8 && sfmt == S_UE8M0 && pick < 3) ? 3 : 0;
         ctas = ceil_div(M, t.bm) * ceil_div(N, t.bn);
     }
     while (ctas * t.split_k < kNumCUs && KB / (t.split_k * 2) >= 4) t.split_k *= 2;
@@ -180,7 +186,7 @@ bfq_tile default_tile(int64_t M, int64_t N, int64_t K, int qtype, int sfmt) {
 // order, whatever the tile. Excluded: split-K, in-workgroup K splits and stream-K (they sum
 // partial K ranges) and, with row-major weights, the swap-AB kernels (their token/weight
 // fragments take a different K order inside the MFMA than the standard kernel's).
-bfq_tile invariant_tile(int64_t M, int wlayout) {
+bfq_tile invariant_tile(int64_t M, int wlayout, int sfmt) {
     bfq_tile t{};
     t.bk = 128;
     t.split_k = 1;
@@ -199,7 +205,7 @@ bfq_tile invariant_tile(int64_t M, int wlayout) {
         return t;
     }
     t.variant = 0;
-    t.sched = 0;
+    t.sched = sfmt == S_CHANNEL ? 4 : 0;
     if (M <= 64) { t.bm = 64; t.bn = 128; t.waves_m = 1; t.waves_n = 2; }
     else if (M <= 512) { t.bm = 128; t.bn = 128; t.waves_m = 2; t.waves_n = 2; }
     else { t.bm = 256; t.bn = 256; t.waves_m = 4; t.waves_n = 2; }
@@ -223,7 +229,7 @@ int otype_of(bfq_dtype d) { return d == BFQ_BF16 ? O_BF16 : d == BFQ_FP16 ? O_FP
 bfq_status select_tile(int64_t M, int64_t N, int64_t K, int qtype, int wlayout, int sfmt,
                        bfq_tile* out) {
     if (batch_invariant()) {
-        *out = invariant_tile(M, wlayout);
+        *out = invariant_tile(M, wlayout, sfmt);
         return BFQ_OK;
     }
     ensure_table();
@@ -243,7 +249,21 @@ bfq_status select_tile(int64_t M, int64_t N, int64_t K, int qtype, int wlayout, 
     return BFQ_WARN_DEFAULT_TILE;
 }
 
-bool block_shape_ok(const int32_t* bs) { return bs && bs[0] == 128 && bs[1] == 128; }
+// Scale granularity from block_shape ([BENCH] §4.2 block_size; [HELION] scope section):
+// {128, 128} = 1x128 token groups and 128x128 weight blocks; {1, K} = one scale per token and
+// one per output channel (K <= kChannelMaxK). Sets *sfmt to S_CHANNEL for the latter.
+bool scale_mode(const int32_t* bs, int64_t K, int* sfmt) {
+    if (!bs) return false;
+    if (bs[0] == 128 && bs[1] == 128) return true;
+    if (bs[0] == 1 && bs[1] > 0 && bs[1] == K && K <= kChannelMaxK) {
+        *sfmt = S_CHANNEL;
+        return true;
+    }
+    return false;
+}
+
+const char* kBlockShapeMsg =
+    "block_shape must be {128, 128} or {1, K} (per-channel, K a multiple of 128 up to 32768)";
 
 bool wlayout_ok(bfq_weight_layout w) { return w == BFQ_W_ROW_MAJOR || w == BFQ_W_PACKED16; }
 
@@ -294,18 +314,20 @@ bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t gr
         return fail(BFQ_ERR_NULL, "x, q and scales must be non-NULL");
     if (q_dtype != BFQ_E4M3FN && q_dtype != BFQ_INT8)
         return fail(BFQ_ERR_DTYPE, "q_dtype must be BFQ_E4M3FN or BFQ_INT8");
-    if (group_size != 128) return fail(BFQ_ERR_SHAPE, "group_size must be 128");
     if (M < 0 || K <= 0 || K % 128 != 0)
         return fail(BFQ_ERR_SHAPE, "need M >= 0 and K a positive multiple of 128");
+    const bool per_token = group_size == K && K != 128;
+    if (group_size != 128 && !(per_token && K <= kChannelMaxK))
+        return fail(BFQ_ERR_SHAPE, "group_size must be 128 or K (per token, K <= 32768)");
     if (M > 0x7FFFFFFF) return fail(BFQ_ERR_SHAPE, "M exceeds 2^31 - 1");
     if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(scales, 4))
         return fail(BFQ_ERR_ALIGN, "x and q must be 16-byte aligned, scales 4-byte aligned");
     if (!(eps > 0.0f) || eps > 3.0e38f) return fail(BFQ_ERR_ARG, "eps must be positive and finite");
     if (!sfmt_ok(scale_fmt)) return fail(BFQ_ERR_ARG, "unknown scale format");
-    const int64_t G = K / 128;
+    const int64_t G = K / group_size;
     int64_t sm, sg;
     if (layout == BFQ_SCALES_ROW_MAJOR) {
-        if (scale_ld < G) return fail(BFQ_ERR_SHAPE, "row-major scale_ld must be >= K/128");
+        if (scale_ld < G) return fail(BFQ_ERR_SHAPE, "row-major scale_ld must be >= K/group_size");
         sm = scale_ld; sg = 1;
     } else if (layout == BFQ_SCALES_COL_MAJOR) {
         if (scale_ld < M) return fail(BFQ_ERR_SHAPE, "column-major scale_ld must be >= M");
@@ -314,8 +336,11 @@ bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t gr
         return fail(BFQ_ERR_ARG, "unknown scale layout");
     }
     if (M == 0) return BFQ_OK;
-    hipError_t e = launch_quant_tokens(x_bf16, q, scales, M, K, qtype_of(q_dtype), sm, sg, eps,
-                                       (int)scale_fmt, (hipStream_t)stream);
+    hipError_t e = per_token
+                       ? launch_quant_rows(x_bf16, 0, q, scales, M, K, qtype_of(q_dtype), sm, eps,
+                                           (int)scale_fmt, (hipStream_t)stream)
+                       : launch_quant_tokens(x_bf16, q, scales, M, K, qtype_of(q_dtype), sm, sg,
+                                             eps, (int)scale_fmt, (hipStream_t)stream);
     if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
     return BFQ_OK;
 }
@@ -328,7 +353,8 @@ bfq_status bfq_quant_weight_blocks(const float* w, int64_t N, int64_t K,
         return fail(BFQ_ERR_NULL, "w, q, scales and block_shape must be non-NULL");
     if (q_dtype != BFQ_E4M3FN && q_dtype != BFQ_INT8)
         return fail(BFQ_ERR_DTYPE, "q_dtype must be BFQ_E4M3FN or BFQ_INT8");
-    if (!block_shape_ok(block_shape)) return fail(BFQ_ERR_SHAPE, "block_shape must be {128, 128}");
+    int wsf = S_FP32;
+    if (!scale_mode(block_shape, K, &wsf)) return fail(BFQ_ERR_SHAPE, kBlockShapeMsg);
     if (N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0)
         return fail(BFQ_ERR_SHAPE, "N and K must be non-negative multiples of 128");
     if (N / 128 > 65535 || K / 128 > 0x7FFFFFFF) return fail(BFQ_ERR_SHAPE, "N or K too large");
@@ -337,8 +363,11 @@ bfq_status bfq_quant_weight_blocks(const float* w, int64_t N, int64_t K,
     if (!(eps > 0.0f) || eps > 3.0e38f) return fail(BFQ_ERR_ARG, "eps must be positive and finite");
     if (!sfmt_ok(scale_fmt)) return fail(BFQ_ERR_ARG, "unknown scale format");
     if (N == 0 || K == 0) return BFQ_OK;
-    hipError_t e = launch_quant_weight_blocks(w, q, scales, N, K, qtype_of(q_dtype), eps,
-                                              (int)scale_fmt, (hipStream_t)stream);
+    hipError_t e = wsf == S_CHANNEL
+                       ? launch_quant_rows(w, 1, q, scales, N, K, qtype_of(q_dtype), 1, eps,
+                                           (int)scale_fmt, (hipStream_t)stream)
+                       : launch_quant_weight_blocks(w, q, scales, N, K, qtype_of(q_dtype), eps,
+                                                    (int)scale_fmt, (hipStream_t)stream);
     if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
     return BFQ_OK;
 }
@@ -367,7 +396,8 @@ bfq_status bfq_select_tile(int64_t M, int64_t N, int64_t K, const int32_t block_
                            bfq_dtype in_dtype, bfq_dtype out_dtype, bfq_weight_layout w_layout,
                            bfq_scale_format scale_fmt, bfq_tile* tile_out) {
     if (!tile_out || !block_shape) return fail(BFQ_ERR_NULL, "tile_out and block_shape must be non-NULL");
-    if (!block_shape_ok(block_shape)) return fail(BFQ_ERR_SHAPE, "block_shape must be {128, 128}");
+    int sf = (int)scale_fmt;
+    if (!scale_mode(block_shape, K, &sf)) return fail(BFQ_ERR_SHAPE, kBlockShapeMsg);
     if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8)
         return fail(BFQ_ERR_DTYPE, "in_dtype must be BFQ_E4M3FN or BFQ_INT8");
     if (out_dtype != BFQ_BF16 && out_dtype != BFQ_FP16 && out_dtype != BFQ_FP32)
@@ -376,7 +406,7 @@ bfq_status bfq_select_tile(int64_t M, int64_t N, int64_t K, const int32_t block_
         return fail(BFQ_ERR_SHAPE, "need M >= 0 and N, K positive multiples of 128");
     if (!wlayout_ok(w_layout)) return fail(BFQ_ERR_ARG, "unknown weight layout");
     if (!sfmt_ok(scale_fmt)) return fail(BFQ_ERR_ARG, "unknown scale format");
-    return select_tile(M, N, K, qtype_of(in_dtype), (int)w_layout, (int)scale_fmt, tile_out);
+    return select_tile(M, N, K, qtype_of(in_dtype), (int)w_layout, sf, tile_out);
 }
 
 size_t bfq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const bfq_tile* tile) {
@@ -395,7 +425,9 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
                           void* workspace, size_t workspace_bytes, void* stream) {
     if (!w_q || !w_scales || !block_shape || (M != 0 && (!a_q || !a_scales || !out)))
         return fail(BFQ_ERR_NULL, "a_q, a_scales, w_q, w_scales, out and block_shape must be non-NULL");
-    if (!block_shape_ok(block_shape)) return fail(BFQ_ERR_SHAPE, "block_shape must be {128, 128}");
+    int sf = (int)scale_fmt;
+    if (!scale_mode(block_shape, K, &sf)) return fail(BFQ_ERR_SHAPE, kBlockShapeMsg);
+    const bool channel = sf == S_CHANNEL;
     if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8)
         return fail(BFQ_ERR_DTYPE, "in_dtype must be BFQ_E4M3FN or BFQ_INT8");
     if (out_dtype != BFQ_BF16 && out_dtype != BFQ_FP16 && out_dtype != BFQ_FP32)
@@ -411,13 +443,15 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
         !aligned(w_scales, 4) || !aligned(workspace, 16))
         return fail(BFQ_ERR_ALIGN, "codes, out and workspace must be 16-byte aligned, scales 4-byte");
     const int64_t KB = K / 128;
+    const int64_t G = channel ? 1 : KB;   // activation scales per token
     int64_t ssm, ssk;
     if (a_layout == BFQ_SCALES_ROW_MAJOR) {
-        if (a_scale_ld < KB) return fail(BFQ_ERR_SHAPE, "row-major a_scale_ld must be >= K/128");
-        ssm = a_scale_ld; ssk = 1;
+        if (a_scale_ld < G)
+            return fail(BFQ_ERR_SHAPE, "row-major a_scale_ld must be >= K/128 (per token: >= 1)");
+        ssm = a_scale_ld; ssk = channel ? 0 : 1;
     } else if (a_layout == BFQ_SCALES_COL_MAJOR) {
         if (a_scale_ld < M) return fail(BFQ_ERR_SHAPE, "column-major a_scale_ld must be >= M");
-        ssm = 1; ssk = a_scale_ld;
+        ssm = 1; ssk = channel ? 0 : a_scale_ld;
     } else {
         return fail(BFQ_ERR_ARG, "unknown scale layout");
     }
@@ -426,7 +460,6 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     if ((255 * ssm + (KB - 1) * ssk + 1) * 4 >= (int64_t(1) << 32))
         return fail(BFQ_ERR_SHAPE, "activation scales of 256 tokens must span less than 4 GiB");
     const int qtype = qtype_of(in_dtype), otype = otype_of(out_dtype), wl = (int)w_layout;
-    const int sf = (int)scale_fmt;
     bfq_status status = BFQ_OK;
     bfq_tile t;
     if (tile) {
@@ -437,7 +470,7 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     const KernelEntry* ke = find_kernel(t, qtype, otype, wl, sf);
     if (!ke)
         return fail(BFQ_ERR_TILE, "tile does not name a compiled kernel for this dtype pair, weight "
-                                  "layout and scale format");
+                                  "layout and scale format / granularity");
     if (t.split_k < 1 || t.split_k > 256 || t.split_k > KB)
         return fail(BFQ_ERR_TILE, "split_k must be in [1, min(256, K/128)]");
     if (t.variant == 2 && t.split_k != 1)
@@ -479,8 +512,8 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
         e = launch_splitk_reduce(ga.partials, out, M, N, t.split_k, otype, s);
     if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
     if (std::getenv("BFQ_TRACE"))
-        std::fprintf(stderr, "[bfq] gemm M=%lld N=%lld K=%lld layout=%d variant=%d bm=%d bn=%d split=%d\n",
-                     (long long)M, (long long)N, (long long)K, wl, t.variant, t.bm, t.bn, t.split_k);
+        std::fprintf(stderr, "[bfq] gemm M=%lld N=%lld K=%lld layout=%d scales=%d variant=%d bm=%d bn=%d split=%d\n",
+                     (long long)M, (long long)N, (long long)K, wl, sf, t.variant, t.bm, t.bn, t.split_k);
     return status;
 }
 
@@ -490,23 +523,36 @@ bfq_status bfq_load_tile_table(const char* json_path) {
     return load_table_locked(json_path, true);
 }
 
-int32_t bfq_num_tile_candidates(bfq_dtype in_dtype, bfq_weight_layout w_layout,
-                                bfq_scale_format scale_fmt) {
+// block_shape {1, k} (any k > 0) selects the per-token x per-channel kernels here
+static int candidate_sfmt(const int32_t* bs, bfq_scale_format f) {
+    if (!bs) return -1;
+    if (bs[0] == 128 && bs[1] == 128) return (int)f;
+    if (bs[0] == 1 && bs[1] > 0) return S_CHANNEL;
+    return -1;
+}
+
+int32_t bfq_num_tile_candidates(const int32_t block_shape[2], bfq_dtype in_dtype,
+                                bfq_weight_layout w_layout, bfq_scale_format scale_fmt) {
     if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8) return 0;
     if (!wlayout_ok(w_layout) || !sfmt_ok(scale_fmt)) return 0;
+    const int sf = candidate_sfmt(block_shape, scale_fmt);
+    if (sf < 0) return 0;
     const int q = qtype_of(in_dtype), wl = (int)w_layout;
     int ns[3] = {0, 0, 0}, count = 0;
     const KernelEntry* lists[3] = {std_kernels(&ns[0]), swapab_kernels(&ns[1]), streamk_kernels(&ns[2])};
     for (int l = 0; l < 3; ++l)
         for (int i = 0; i < ns[l]; ++i)
             count += (lists[l][i].qtype == q && lists[l][i].otype == O_BF16 && lists[l][i].wlayout == wl &&
-                      serves(lists[l][i], (int)scale_fmt));
+                      serves(lists[l][i], sf));
     return count;
 }
 
-bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, bfq_weight_layout w_layout,
-                                  bfq_scale_format scale_fmt, int32_t index, bfq_tile* tile_out) {
-    if (!tile_out) return fail(BFQ_ERR_NULL, "tile_out must be non-NULL");
+bfq_status bfq_get_tile_candidate(const int32_t block_shape[2], bfq_dtype in_dtype,
+                                  bfq_weight_layout w_layout, bfq_scale_format scale_fmt,
+                                  int32_t index, bfq_tile* tile_out) {
+    if (!tile_out || !block_shape) return fail(BFQ_ERR_NULL, "tile_out and block_shape must be non-NULL");
+    const int sf = candidate_sfmt(block_shape, scale_fmt);
+    if (sf < 0) return fail(BFQ_ERR_SHAPE, "block_shape must be {128, 128} or {1, k}");
     if (in_dtype != BFQ_E4M3FN && in_dtype != BFQ_INT8)
         return fail(BFQ_ERR_DTYPE, "in_dtype must be BFQ_E4M3FN or BFQ_INT8");
     if (!wlayout_ok(w_layout)) return fail(BFQ_ERR_ARG, "unknown weight layout");
@@ -517,7 +563,7 @@ bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, bfq_weight_layout w_layout
     for (int l = 0; l < 3; ++l)
         for (int i = 0; i < ns[l]; ++i) {
             if (lists[l][i].qtype != q || lists[l][i].otype != O_BF16 || lists[l][i].wlayout != wl ||
-                !serves(lists[l][i], (int)scale_fmt))
+                !serves(lists[l][i], sf))
                 continue;
             if (count == index) { *tile_out = lists[l][i].tile; return BFQ_OK; }
             ++count;

@@ -11,7 +11,13 @@ namespace bfq {
 enum QType { Q_FP8 = 0, Q_INT8 = 1 };
 enum OType { O_BF16 = 0, O_FP16 = 1, O_FP32 = 2 };
 enum WLayout { W_ROW = 0, W_PACKED16 = 1 };   // bfq_weight_layout
-enum ScaleFmt { S_FP32 = 0, S_UE8M0 = 1 };    // bfq_scale_format
+// How a kernel applies scales: per 128-wide K block, any fp32 values (S_FP32) or powers of two
+// only (S_UE8M0, bfq_scale_format); or one scale per token and per output channel after the
+// whole-K product (S_CHANNEL, block_shape {1, K}).
+enum ScaleFmt { S_FP32 = 0, S_UE8M0 = 1, S_CHANNEL = 2 };
+
+// Largest K of the per-token / per-channel format (the row quantizer keeps a row in registers).
+constexpr int64_t kChannelMaxK = 32768;
 
 hipError_t launch_quant_tokens(const void* x, void* q, float* scales, int64_t M, int64_t K,
                                int qtype, int64_t s_stride_m, int64_t s_stride_g, float eps,
@@ -19,6 +25,11 @@ hipError_t launch_quant_tokens(const void* x, void* q, float* scales, int64_t M,
 hipError_t launch_quant_weight_blocks(const float* w, void* q, float* scales, int64_t N,
                                       int64_t K, int qtype, float eps, int sfmt,
                                       hipStream_t stream);
+// One scale per row: bf16 token rows (is_f32 = 0) or fp32 weight rows (is_f32 = 1) of length
+// K <= kChannelMaxK; row r's scale goes to scales[r * s_stride].
+hipError_t launch_quant_rows(const void* x, int is_f32, void* q, float* scales, int64_t rows,
+                             int64_t K, int qtype, int64_t s_stride, float eps, int sfmt,
+                             hipStream_t stream);
 // Row-major [N][K] codes -> the packed 16-row fragment layout (BFQ_W_PACKED16).
 hipError_t launch_pack_weights(const void* w, void* packed, int64_t N, int64_t K,
                                hipStream_t stream);
@@ -32,7 +43,7 @@ struct GemmArgs {
     int64_t sa_stride_m;    // element stride between tokens
     int64_t sa_stride_k;    // element stride between K blocks
     const void* w;          // N*K codes, row-major or packed (the kernel's layout)
-    const float* sw;        // [N/128][K/128]
+    const float* sw;        // [N/128][K/128] (S_CHANNEL: [N])
     void* out;              // [M][N]
     float* partials;        // split-K fp32 partials [split][M][N] (split > 1)
     int64_t M, N, K;
@@ -52,7 +63,8 @@ struct KernelEntry {
     int qtype;              // Q_FP8 / Q_INT8
     int otype;              // O_BF16 / O_FP16 / O_FP32 (output of a split=1 launch)
     int wlayout;            // W_ROW / W_PACKED16: the weight layout the kernel reads
-    int sfmt;               // S_FP32: any fp32 scales; S_UE8M0: power-of-two scales only
+    int sfmt;               // S_FP32: any fp32 block scales; S_UE8M0: power-of-two block
+                            // scales only; S_CHANNEL: per-token x per-channel scales
     GemmLaunchFn launch;    // writes `out` (split==1) or `partials` (split>1)
 };
 

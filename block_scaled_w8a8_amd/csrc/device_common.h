@@ -79,6 +79,12 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
 }
 
+// The same product added to an accumulator: D = C + A * B (per-token x per-channel scales,
+// where the MFMA accumulates over the whole K and the scales come after).
+__device__ __forceinline__ v4f mfma_fp8_16x16x128_acc(const v8i& a, const v8i& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // D(32x32, fp32) = A(32x64 e4m3) * B(64x32 e4m3) + C. Lane l supplies row (l % 32) of A and
 // column (l % 32) of B, 32 bytes of the 64-long K slice each (same placement for both).
 // Output: lane l holds D[8*j + 4*(l/32) + i][l % 32] in element 4*j + i (i, j = 0..3).

@@ -24,6 +24,10 @@
 //    the first operand, each lane's token scale for the second — and the MFMA accumulates
 //    across K blocks itself: no block partial, no FMA. A power-of-two fp32 scale's E8M0
 //    byte is its exponent field.
+//  * sched 4 (per-token x per-channel scales, [HELION] scope section): no per-block scale at
+//    all; the MFMA accumulates the whole K range (fp8 in fp32; int8 in int32, exact, kept in
+//    the accumulator registers' bits) and the tile routine multiplies each element by its
+//    token and channel scale once at the end.
 //  * The weight fragment sits in the MFMA's first operand and the token fragment in the
 //    second, so each lane ends up owning one token row and four consecutive output columns:
 //    one scale product per lane and sub-tile row, and 8-byte (bf16) row-contiguous stores.
@@ -77,6 +81,7 @@ __device__ __forceinline__ void std_tile(
     static_assert(SCHED != 2 || (QT == Q_FP8 && WL == W_ROW && TM % 32 == 0 && TN % 32 == 0),
                   "the 32x32 schedule is fp8 only, row-major W, and needs 32-multiple wave tiles");
     static_assert(SCHED != 3 || QT == Q_FP8, "the block-scaled MFMA schedule is fp8 only");
+    static_assert(SCHED <= 4, "schedules 0-4");
     constexpr int STAGE = (BM + BN) * 128;         // bytes per LDS stage
     constexpr int CHUNKS = (BM + BN) / 8;          // 1 KB load chunks per stage
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
@@ -144,9 +149,11 @@ __device__ __forceinline__ void std_tile(
         // scales of block kb: waves 0 .. BM/64-1 fetch 64 activation scales each, wave 0 also
         // the weight scales of the tile's 128-row blocks
         const uint32_t sc = (uint32_t)(SC_BASE + stage * SC_STAGE);
-        if (wave < BM / 64)
-            dma4(rsa, lds, sc + wave * 256, sa_dma_voff, (uint32_t)(kb * ssk * 4));
-        if (wave == 0) dma4(rsw, lds, sc + BM * 4, sw_dma_voff, (uint32_t)(kb * 4));
+        if constexpr (SCHED != 4) {   // sched 4 has no per-block scales
+            if (wave < BM / 64)
+                dma4(rsa, lds, sc + wave * 256, sa_dma_voff, (uint32_t)(kb * ssk * 4));
+            if (wave == 0) dma4(rsw, lds, sc + BM * 4, sw_dma_voff, (uint32_t)(kb * 4));
+        }
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const uint32_t lds_off = (uint32_t)((wave + NWAVES * i) * 1024 + stage * STAGE);
@@ -211,7 +218,50 @@ __device__ __forceinline__ void std_tile(
     // scale product of sub-tile row sm (sched 0-2); ea[sm] and ew the E8M0 exponents of the
     // token and weight scales (sched 3).
     auto compute = [&](uint32_t sbase, const float (&c)[SM], const int (&ea)[SM], int ew) {
-        if constexpr (SCHED == 3) {
+        if constexpr (SCHED == 4) {
+            // accumulate the raw products; int8 keeps its exact int32 sum in acc's bits
+            const uint32_t abase = sbase + a_row, wbase = sbase + w_row;
+            if constexpr (QT == Q_FP8) {
+                v8i af[SM];
+#pragma unroll
+                for (int sm = 0; sm < SM; ++sm) {
+                    const v4i lo = lds16(abase + sm * 2048 + a_s0);
+                    const v4i hi = lds16(abase + sm * 2048 + a_s1);
+                    af[sm] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                }
+#pragma unroll
+                for (int sn = 0; sn < SN; ++sn) {
+                    const v4i lo = lds16(wbase + sn * 2048 + w_s0);
+                    const v4i hi = lds16(wbase + sn * 2048 + w_s1);
+                    const v8i wf = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+                    for (int sm = 0; sm < SM; ++sm)
+                        acc[sm][sn] = mfma_fp8_16x16x128_acc(wf, af[sm], acc[sm][sn]);
+                }
+            } else {
+                v4i af[SM][2];
+#pragma unroll
+                for (int sm = 0; sm < SM; ++sm) {
+                    af[sm][0] = lds16(abase + sm * 2048 + a_s0);
+                    af[sm][1] = lds16(abase + sm * 2048 + a_s1);
+                }
+#pragma unroll
+                for (int sn = 0; sn < SN; ++sn) {
+                    const v4i w0 = lds16(wbase + sn * 2048 + w_s0);
+                    const v4i w1 = lds16(wbase + sn * 2048 + w_s1);
+#pragma unroll
+                    for (int sm = 0; sm < SM; ++sm) {
+                        v4i pi = __builtin_bit_cast(v4i, acc[sm][sn]);
+                        pi = mfma_i8_16x16x64(w0, af[sm][0], pi);
+                        pi = mfma_i8_16x16x64(w1, af[sm][1], pi);
+                        acc[sm][sn] = __builtin_bit_cast(v4f, pi);
+                    }
+                }
+            }
+            (void)c;
+            (void)ea;
+            (void)ew;
+        } else if constexpr (SCHED == 3) {
             const uint32_t abase = sbase + a_row, wbase = sbase + w_row;
             v8i af[SM];
 #pragma unroll
@@ -371,7 +421,10 @@ __device__ __forceinline__ void std_tile(
     auto kblock = [&](int64_t kb, int stage) {
         float c[SM];
         int ea[SM], ew = 0;
-        if constexpr (SCHED == 3) {
+        if constexpr (SCHED == 4) {
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm) { c[sm] = 0.f; ea[sm] = 0; }
+        } else if constexpr (SCHED == 3) {
             const uint32_t sc = (uint32_t)(SC_BASE + stage * SC_STAGE);
             ew = (int)e8m0_of(*reinterpret_cast<const float*>(lds + sc + sw_lds));
 #pragma unroll
@@ -414,6 +467,36 @@ __device__ __forceinline__ void std_tile(
         __syncthreads();
         for (int64_t kb = kb_begin; kb < kb_end; ++kb) kblock(kb, (int)((kb - kb_begin) & 1));
         wait_vmem_all();      // no LDS DMA may still be in flight when the wave ends
+    }
+
+    if constexpr (SCHED == 4) {
+        // acc[m][n] = ((float)P * sa[m]) * sw[n] for the lane's token m (one per sub-tile row)
+        // and columns n..n+3; rows past M and columns past N take scale 0 (never stored)
+        float swv[SN][4];
+#pragma unroll
+        for (int sn = 0; sn < SN; ++sn) {
+            const int64_t n = n0 + wn * TN + sn * 16 + 4 * fgrp;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) swv[sn][j] = n + j < N ? p.sw[n + j] : 0.f;
+        }
+#pragma unroll
+        for (int sm = 0; sm < SM; ++sm) {
+            const int64_t m = m0 + wm * TM + sm * 16 + frow;
+            const float sav = m < M ? p.sa[m * ssm] : 0.f;
+#pragma unroll
+            for (int sn = 0; sn < SN; ++sn) {
+                v4f a = acc[sm][sn];
+                if constexpr (QT == Q_INT8) {
+                    const v4i pi = __builtin_bit_cast(v4i, a);
+                    a = v4f{(float)pi.x, (float)pi.y, (float)pi.z, (float)pi.w};
+                }
+                a.x = (a.x * sav) * swv[sn][0];
+                a.y = (a.y * sav) * swv[sn][1];
+                a.z = (a.z * sav) * swv[sn][2];
+                a.w = (a.w * sav) * swv[sn][3];
+                acc[sm][sn] = a;
+            }
+        }
     }
 }
 
@@ -679,7 +762,8 @@ hipError_t launch_std(const GemmArgs& a, hipStream_t stream) {
 
 #define BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, OT, WL)                                \
     KernelEntry{bfq_tile{0, BM, BN, 128, 1, WM, WN, ST, 8, SC, 0, 0}, QT, OT, WL,         \
-                (SC) == 3 ? S_UE8M0 : S_FP32, &launch_std<BM, BN, WM, WN, QT, OT, SC, ST, WL>}
+                (SC) == 3 ? S_UE8M0 : (SC) == 4 ? S_CHANNEL : S_FP32,                      \
+                &launch_std<BM, BN, WM, WN, QT, OT, SC, ST, WL>}
 
 #define BFQ_STD_ALL_OUT(BM, BN, WM, WN, ST, SC, QT, WL)                                   \
     BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_BF16, WL),                                \
@@ -714,11 +798,29 @@ static const KernelEntry kStdKernels[] = {
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 3, Q_FP8, W_PACKED16),
     BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 3, Q_FP8, W_PACKED16),
     BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 3, Q_FP8, W_PACKED16),
+    // per-token x per-channel scales
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 4, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 4, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 4, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 4, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 4, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 4, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 4, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 4, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 4, Q_INT8, W_ROW),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 4, Q_INT8, W_ROW),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 4, Q_INT8, W_ROW),
+    BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 4, Q_INT8, W_ROW),
+    BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 4, Q_INT8, W_PACKED16),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 4, Q_INT8, W_PACKED16),
+    BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 4, Q_INT8, W_PACKED16),
+    BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 4, Q_INT8, W_PACKED16),
 };
 
 #define BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, OT, WL)                                 \
     KernelEntry{bfq_tile{2, BM, BN, 128, 1, WM, WN, ST, 8, SC, 0, 0}, QT, OT, WL,         \
-                (SC) == 3 ? S_UE8M0 : S_FP32, &launch_streamk<BM, BN, WM, WN, QT, OT, SC, ST, WL>}
+                (SC) == 3 ? S_UE8M0 : (SC) == 4 ? S_CHANNEL : S_FP32,                      \
+                &launch_streamk<BM, BN, WM, WN, QT, OT, SC, ST, WL>}
 
 #define BFQ_SK_ALL_OUT(BM, BN, WM, WN, ST, SC, QT, WL)                                    \
     BFQ_SK_ENTRY(BM, BN, WM, WN, ST, SC, QT, O_BF16, WL),                                 \
@@ -734,6 +836,9 @@ static const KernelEntry kStreamKKernels[] = {
     BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 0, Q_INT8, W_PACKED16),
     BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 3, Q_FP8, W_ROW),
     BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 3, Q_FP8, W_PACKED16),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 4, Q_FP8, W_ROW),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 4, Q_FP8, W_PACKED16),
+    BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 4, Q_INT8, W_PACKED16),
 };
 
 const KernelEntry* streamk_kernels(int* count) {

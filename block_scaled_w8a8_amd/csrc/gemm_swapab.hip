@@ -25,12 +25,62 @@
 // strip. That gives a weight matrix of few strips (N / 16 = 1536 at N = 24576) enough waves
 // to keep HBM busy without a second kernel. Split-K across workgroups writes fp32 partials
 // that a second kernel sums in a fixed order.
+// CH = 1 (per-token x per-channel scales, [HELION] scope section): no scale loads in the K
+// loop; the MFMA accumulates the wave's K range (int8: exact int32 in the accumulator's
+// bits) and each wave scales its partial tile by token and channel scale before the
+// in-workgroup sum.
 #include "bfq_internal.h"
 #include "device_common.h"
 
 namespace bfq {
 
-template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL>
+// Scale a wave's partial tile by its tokens' and channels' scales (CH = 1): lane holds token
+// m0 + 16*sm + frow and channels n0 + 16*sn + 4*fgrp .. +3; tokens past M take scale 0.
+template <int QT, int SM, int SN>
+__device__ __forceinline__ void channel_scale(v4f (&acc)[SM][SN], const GemmArgs& p, int64_t m0,
+                                              int64_t n0, int frow, int fgrp) {
+    float swv[SN][4];
+#pragma unroll
+    for (int sn = 0; sn < SN; ++sn)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) swv[sn][j] = p.sw[n0 + sn * 16 + 4 * fgrp + j];
+#pragma unroll
+    for (int sm = 0; sm < SM; ++sm) {
+        const int64_t m = m0 + sm * 16 + frow;
+        const float sav = m < p.M ? p.sa[m * p.sa_stride_m] : 0.f;
+#pragma unroll
+        for (int sn = 0; sn < SN; ++sn) {
+            v4f a = acc[sm][sn];
+            if constexpr (QT == Q_INT8) {
+                const v4i pi = __builtin_bit_cast(v4i, a);
+                a = v4f{(float)pi.x, (float)pi.y, (float)pi.z, (float)pi.w};
+            }
+            a.x = (a.x * sav) * swv[sn][0];
+            a.y = (a.y * sav) * swv[sn][1];
+            a.z = (a.z * sav) * swv[sn][2];
+            a.w = (a.w * sav) * swv[sn][3];
+            acc[sm][sn] = a;
+        }
+    }
+}
+
+// One MFMA step of the CH = 1 kernels: acc += W fragment x token fragment, no scaling.
+template <int QT>
+__device__ __forceinline__ void mfma_accumulate(v4f& acc, const v4i (&w)[2], const v4i& a0,
+                                                const v4i& a1) {
+    if constexpr (QT == Q_FP8) {
+        const v8i wf = v8i{w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+        const v8i af = v8i{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        acc = mfma_fp8_16x16x128_acc(wf, af, acc);
+    } else {
+        v4i pi = __builtin_bit_cast(v4i, acc);
+        pi = mfma_i8_16x16x64(w[0], a0, pi);
+        pi = mfma_i8_16x16x64(w[1], a1, pi);
+        acc = __builtin_bit_cast(v4f, pi);
+    }
+}
+
+template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL, int CH>
 __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs p) {
     constexpr int SM = MT / 16, SN = NWR / 16;
     static_assert(MT % 16 == 0 && NWR % 16 == 0, "tiles are multiples of 16");
@@ -98,9 +148,11 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
         const uint32_t ws = live ? (uint32_t)kb * KSTEP : kNoLoad;
         const uint32_t as = live ? (uint32_t)kb * 128u : kNoLoad;
         const uint32_t ss = live ? (uint32_t)(kb * ssk * 4) : kNoLoad;
-        swb[slot] = sw_row[kb];
+        if constexpr (!CH) {
+            swb[slot] = sw_row[kb];
 #pragma unroll
-        for (int sm = 0; sm < SM; ++sm) sab[slot][sm] = buf_f32(rsa, sa_voff[sm], ss);
+            for (int sm = 0; sm < SM; ++sm) sab[slot][sm] = buf_f32(rsa, sa_voff[sm], ss);
+        }
 #pragma unroll
         for (int sn = 0; sn < SN; ++sn) {
             // streamed once: non-temporal, so the weight stream does not evict the tokens
@@ -121,6 +173,14 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
         for (int sn = 0; sn < SN; ++sn) acc[sm][sn] = v4f{0.f, 0.f, 0.f, 0.f};
 
     auto consume = [&](int i) {
+        if constexpr (CH) {
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+                for (int sn = 0; sn < SN; ++sn)
+                    mfma_accumulate<QT>(acc[sm][sn], wbuf[i][sn], abuf[i][sm][0], abuf[i][sm][1]);
+            return;
+        }
 #pragma unroll
         for (int sm = 0; sm < SM; ++sm) {
             const float c = sab[i][sm] * swb[i];
@@ -171,6 +231,9 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
         for (int r = 0; r < D; ++r)
             if (r < rem) consume(r);
     }
+    if constexpr (CH) {
+        if (wave_live) channel_scale<QT, SM, SN>(acc, p, m0, n0, frow, fgrp);
+    }
 
     if constexpr (KW > 1) {
         // strip partials of K slices 1..KW-1 go through LDS; slice 0's wave adds them in order
@@ -218,7 +281,7 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
 // in lane order (conflict-free) for its MFMAs. Buffer i & 1 was last read at step i - 2, before
 // the previous step's barrier. Every wave runs the same number of steps (the longest K slice
 // of the workgroup) so the barriers match; a wave with a shorter slice idles on its last one.
-template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL>
+template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL, int CH>
 __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmArgs p) {
     constexpr int SM = MT / 16, SN = NWR / 16;
     constexpr int AI = 2 * SM;                              // 1 KB token halves per K block
@@ -309,9 +372,11 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
         const uint32_t ws = live ? (uint32_t)kb * KSTEP : kNoLoad;
         const uint32_t as = live ? (uint32_t)kb * 128u : kNoLoad;
         const uint32_t ss = live ? (uint32_t)(kb * ssk * 4) : kNoLoad;
-        swb[slot] = sw_row[kb];
+        if constexpr (!CH) {
+            swb[slot] = sw_row[kb];
 #pragma unroll
-        for (int q = 0; q < SCW; ++q) sab[slot][q] = buf_f32(rsa, sa_voff[q], ss);
+            for (int q = 0; q < SCW; ++q) sab[slot][q] = buf_f32(rsa, sa_voff[q], ss);
+        }
 #pragma unroll
         for (int sn = 0; sn < SN; ++sn) {
             // streamed once: non-temporal, so the weight stream does not evict the tokens
@@ -338,14 +403,22 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
             const int j = wn + NWAVES * t;
             if (j < AI) *reinterpret_cast<v4i*>(buf + j * 1024 + lane * 16) = abuf[r][t];
         }
-        if (scale_wave) {
+        if (!CH && scale_wave) {
 #pragma unroll
             for (int q = 0; q < SCW; ++q)
                 if (lane + 64 * q < MT)
                     *reinterpret_cast<float*>(buf + MT * 128 + (lane + 64 * q) * 4) = sab[r][q];
         }
         __syncthreads();
-        if (i < L && wave_live) {
+        if (CH && i < L && wave_live) {
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm) {
+                const v4i a0 = *reinterpret_cast<const v4i*>(buf + (2 * sm) * 1024 + lane * 16);
+                const v4i a1 = *reinterpret_cast<const v4i*>(buf + (2 * sm + 1) * 1024 + lane * 16);
+#pragma unroll
+                for (int sn = 0; sn < SN; ++sn) mfma_accumulate<QT>(acc[sm][sn], wbuf[r][sn], a0, a1);
+            }
+        } else if (!CH && i < L && wave_live) {
             float c[SM];
             const float* sp = reinterpret_cast<const float*>(buf + MT * 128) + frow * SM;
 #pragma unroll
@@ -392,6 +465,9 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
         }
         i0 += D;
     } while (i0 < Lmax);
+    if constexpr (CH) {
+        if (wave_live) channel_scale<QT, SM, SN>(acc, p, m0, n0, frow, fgrp);
+    }
 
     if constexpr (KW > 1) {
         __shared__ v4f red[KW - 1][NWAVES][SM * SN][64];
@@ -427,20 +503,20 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
     }
 }
 
-template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL>
+template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL, int CH>
 hipError_t launch_swapab(const GemmArgs& a, hipStream_t stream) {
     const int64_t strips = (a.N + NWR * NWAVES - 1) / (NWR * NWAVES);
     dim3 grid((unsigned)strips, (unsigned)((a.M + MT - 1) / MT), (unsigned)a.split);
-    hipLaunchKernelGGL((gemm_swapab_kernel<MT, NWR, NWAVES, KW, D, QT, OT, WL>), grid,
+    hipLaunchKernelGGL((gemm_swapab_kernel<MT, NWR, NWAVES, KW, D, QT, OT, WL, CH>), grid,
                        dim3(64 * NWAVES * KW), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL>
+template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL, int CH>
 hipError_t launch_swapab_lds(const GemmArgs& a, hipStream_t stream) {
     const int64_t strips = (a.N + NWR * NWAVES - 1) / (NWR * NWAVES);
     dim3 grid((unsigned)strips, (unsigned)((a.M + MT - 1) / MT), (unsigned)a.split);
-    hipLaunchKernelGGL((gemm_swapab_lds_kernel<MT, NWR, NWAVES, KW, D, QT, OT, WL>), grid,
+    hipLaunchKernelGGL((gemm_swapab_lds_kernel<MT, NWR, NWAVES, KW, D, QT, OT, WL, CH>), grid,
                        dim3(64 * NWAVES * KW), 0, stream, a);
     return hipGetLastError();
 }
@@ -448,25 +524,30 @@ hipError_t launch_swapab_lds(const GemmArgs& a, hipStream_t stream) {
 // bfq_tile for variant 1: bm = MT tokens, bn = NWR * NW rows per workgroup, waves_m = KW
 // waves sharing each strip's K range, waves_n = NW strips, stages = D K blocks in flight,
 // sched 0 = tokens per wave from L2, sched 1 = tokens shared through LDS.
-#define BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, OT, WL)                                      \
-    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 0, 0, 0}, QT, OT, WL, S_FP32, \
-                &launch_swapab<MT, NWR, NW, KW, D, QT, OT, WL>}
-#define BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, WL)                                        \
-    BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, O_BF16, WL),                                     \
-        BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, O_FP16, WL),                                 \
-        BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, O_FP32, WL)
+#define BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, OT, WL, CH)                                  \
+    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 0, 0, 0}, QT, OT, WL,         \
+                (CH) ? S_CHANNEL : S_FP32, &launch_swapab<MT, NWR, NW, KW, D, QT, OT, WL, CH>}
+#define BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, WL, CH)                                    \
+    BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, O_BF16, WL, CH),                                 \
+        BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, O_FP16, WL, CH),                             \
+        BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, O_FP32, WL, CH)
 #define BFQ_SAB_BOTH(MT, NWR, NW, KW, D, QT)                                                \
-    BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW), BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16)
+    BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW, 0), BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16, 0)
+// per-token x per-channel scales
+#define BFQ_SAB_CH(MT, NWR, NW, KW, D, QT)                                                  \
+    BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW, 1), BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16, 1)
 
-#define BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, OT, WL)                                     \
-    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 1, 0, 0}, QT, OT, WL, S_FP32, \
-                &launch_swapab_lds<MT, NWR, NW, KW, D, QT, OT, WL>}
-#define BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, WL)                                       \
-    BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, O_BF16, WL),                                    \
-        BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, O_FP16, WL),                                \
-        BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, O_FP32, WL)
+#define BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, OT, WL, CH)                                 \
+    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 1, 0, 0}, QT, OT, WL,         \
+                (CH) ? S_CHANNEL : S_FP32, &launch_swapab_lds<MT, NWR, NW, KW, D, QT, OT, WL, CH>}
+#define BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, WL, CH)                                   \
+    BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, O_BF16, WL, CH),                                \
+        BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, O_FP16, WL, CH),                            \
+        BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, O_FP32, WL, CH)
 #define BFQ_SABL_BOTH(MT, NWR, NW, KW, D, QT)                                               \
-    BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW), BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16)
+    BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW, 0), BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16, 0)
+#define BFQ_SABL_CH(MT, NWR, NW, KW, D, QT)                                                 \
+    BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW, 1), BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16, 1)
 
 static const KernelEntry kSwapabKernels[] = {
     BFQ_SABL_BOTH(16, 16, 8, 1, 8, Q_FP8),
@@ -514,6 +595,33 @@ static const KernelEntry kSwapabKernels[] = {
     BFQ_SAB_BOTH(16, 16, 1, 4, 4, Q_INT8),
     BFQ_SAB_BOTH(32, 16, 1, 4, 4, Q_INT8),
     BFQ_SAB_BOTH(64, 16, 1, 4, 2, Q_INT8),
+    BFQ_SABL_CH(16, 16, 8, 1, 8, Q_FP8),
+    BFQ_SABL_CH(32, 16, 8, 1, 4, Q_FP8),
+    BFQ_SABL_CH(32, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_CH(32, 16, 4, 2, 4, Q_FP8),
+    BFQ_SABL_CH(64, 16, 8, 1, 4, Q_FP8),
+    BFQ_SABL_CH(64, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_CH(64, 16, 4, 2, 4, Q_FP8),
+    BFQ_SABL_CH(96, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_CH(128, 16, 8, 1, 4, Q_FP8),
+    BFQ_SABL_CH(128, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_CH(16, 16, 8, 1, 8, Q_INT8),
+    BFQ_SABL_CH(32, 16, 8, 1, 4, Q_INT8),
+    BFQ_SABL_CH(64, 16, 8, 1, 4, Q_INT8),
+    BFQ_SABL_CH(128, 16, 8, 1, 4, Q_INT8),
+    BFQ_SAB_CH(16, 32, 4, 1, 4, Q_FP8),
+    BFQ_SAB_CH(16, 16, 4, 1, 8, Q_FP8),
+    BFQ_SAB_CH(16, 16, 8, 1, 8, Q_FP8),
+    BFQ_SAB_CH(32, 32, 4, 1, 4, Q_FP8),
+    BFQ_SAB_CH(16, 16, 1, 4, 4, Q_FP8),
+    BFQ_SAB_CH(16, 16, 1, 4, 8, Q_FP8),
+    BFQ_SAB_CH(16, 32, 1, 4, 4, Q_FP8),
+    BFQ_SAB_CH(32, 16, 1, 4, 4, Q_FP8),
+    BFQ_SAB_CH(64, 16, 1, 4, 2, Q_FP8),
+    BFQ_SAB_CH(16, 32, 4, 1, 4, Q_INT8),
+    BFQ_SAB_CH(32, 32, 4, 1, 4, Q_INT8),
+    BFQ_SAB_CH(16, 16, 1, 4, 4, Q_INT8),
+    BFQ_SAB_CH(32, 16, 1, 4, 4, Q_INT8),
 };
 
 const KernelEntry* swapab_kernels(int* count) {

@@ -1,8 +1,9 @@
 // Quantization kernels for gfx950: per-token-group activation quantization (bf16 -> e4m3fn
 // or int8 codes + one fp32 scale per 1x128 group, optionally rounded up to a power of two),
 // per-128x128-block weight quantization
-// (fp32 -> codes + one fp32 scale per block), the weight-code packing into the 16-row
-// fragment layout, and the element-encoder probe used by tests.
+// (fp32 -> codes + one fp32 scale per block), one-scale-per-row quantization (per token or
+// per output channel), the weight-code packing into the 16-row fragment layout, and the
+// element-encoder probe used by tests.
 //
 // Pages cited by title and section:
 //   [BENCH] "vLLM DeepGEMM FP8 Block GEMM 基准测试 ..." §4.1 (per_token_group_quant_fp8,
@@ -10,6 +11,8 @@
 //   [PR]    vLLM pull request 42153 — what the group kernel is parameterised by (group size,
 //           eps, min/max code) and its point that index arithmetic should be compile-time
 //           constants rather than runtime divisions.
+//   [HELION] "Building a High-Performance and Portable vLLM Linear Backend with Helion",
+//           scope section (per-token activation and per-channel weight scales).
 //
 // Group kernel layout (wave64): 16 lanes own one 128-element group, 8 bf16 (16 bytes) per
 // lane, so one wave covers 4 groups of one token row per pass and each 16-byte load is
@@ -201,7 +204,124 @@ __global__ __launch_bounds__(256) void debug_encode_kernel(const float* __restri
     }
 }
 
+// One scale per row ([HELION] scope section: FP8_Dynamic / W8A8_INT8 quantize activations per
+// token and weights per output channel): one 256-thread workgroup per row, which it reads
+// once into registers as 16-byte chunks (8 bf16 or 4 fp32 values; chunk c of the row is
+// held by thread c % 256 in slot c / 256), reduces the row's absolute maximum on the raw
+// bits (NaN > Inf > finite, as in the group kernel) over the workgroup, and encodes from
+// registers. P slots per thread bound K: P * 256 * (8 or 4) elements.
+template <int IS_F32, int QT, int P>
+__global__ __launch_bounds__(256) void quant_rows_kernel(
+    const uint4* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ scales, int64_t K,
+    int64_t s_stride, float eps, int ue8m0) {
+    constexpr int E = IS_F32 ? 4 : 8;                  // values per 16-byte chunk
+    const int t = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    const int64_t chunks = K / E;
+    __shared__ uint32_t red[4];
+
+    uint4 raw[P];
+    uint32_t mx = 0;
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+        const int64_t c = (int64_t)u * 256 + t;
+        raw[u] = c < chunks ? x[r * chunks + c] : make_uint4(0, 0, 0, 0);
+        if constexpr (IS_F32) {
+            mx = max(mx, max(max(raw[u].x & 0x7FFFFFFFu, raw[u].y & 0x7FFFFFFFu),
+                             max(raw[u].z & 0x7FFFFFFFu, raw[u].w & 0x7FFFFFFFu)));
+        } else {
+            const uint32_t m2 = max_u16x2(max_u16x2(raw[u].x & 0x7FFF7FFFu, raw[u].y & 0x7FFF7FFFu),
+                                          max_u16x2(raw[u].z & 0x7FFF7FFFu, raw[u].w & 0x7FFF7FFFu));
+            mx = max(mx, max(m2 & 0xFFFFu, m2 >> 16));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    if ((t & 63) == 0) red[t >> 6] = mx;
+    __syncthreads();
+    mx = max(max(red[0], red[1]), max(red[2], red[3]));
+
+    // bf16 magnitudes widen to fp32 bit patterns by a 16-bit shift
+    const uint32_t mxf = IS_F32 ? mx : mx << 16;
+    const bool finite = mxf < 0x7F800000u, nan_row = mxf > 0x7F800000u;
+    float s;
+    if (finite) {
+        const float amax = __uint_as_float(mxf);
+        s = (amax > eps ? amax : eps) / qmax<QT>();
+        if (ue8m0) s = pow2_ceil(s);
+    } else {
+        s = nan_row ? __uint_as_float(0x7FC00000u) : __uint_as_float(0x7F800000u);
+    }
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+        const int64_t c = (int64_t)u * 256 + t;
+        if (c >= chunks) continue;
+        if constexpr (IS_F32) {
+            const float e[4] = {__uint_as_float(raw[u].x), __uint_as_float(raw[u].y),
+                                __uint_as_float(raw[u].z), __uint_as_float(raw[u].w)};
+            uint32_t word = 0;
+            if (finite) {
+                const float y0 = e[0] / s, y1 = e[1] / s, y2 = e[2] / s, y3 = e[3] / s;
+                word = (QT == Q_FP8) ? enc_fp8x4(y0, y1, y2, y3) : enc_i8x4(y0, y1, y2, y3);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t code;
+                    if (nan_row || __builtin_isinf(e[j])) code = (QT == Q_FP8) ? 0x7Fu : 0u;
+                    else code = (QT == Q_FP8) ? ((__float_as_uint(e[j]) >> 24) & 0x80u) : 0u;
+                    word |= code << (8 * j);
+                }
+            }
+            *reinterpret_cast<uint32_t*>(q + r * K + c * 4) = word;
+        } else {
+            const float xv[8] = {bf16_lo(raw[u].x), bf16_hi(raw[u].x), bf16_lo(raw[u].y),
+                                 bf16_hi(raw[u].y), bf16_lo(raw[u].z), bf16_hi(raw[u].z),
+                                 bf16_lo(raw[u].w), bf16_hi(raw[u].w)};
+            const uint2 codes = finite ? encode8<QT>(xv, s) : encode8_special<QT>(xv, nan_row);
+            *reinterpret_cast<uint2*>(q + r * K + c * 8) = codes;
+        }
+    }
+    if (t == 0) scales[r * s_stride] = s;
+}
+
 // ---------------------------------------------------------------- launchers ----
+
+template <int IS_F32, int QT>
+static hipError_t launch_rows_p(const void* x, void* q, float* scales, int64_t rows, int64_t K,
+                                int64_t s_stride, float eps, int ue, hipStream_t stream) {
+    constexpr int E = IS_F32 ? 4 : 8;
+    const int64_t slots = (K / E + 255) / 256;
+    const dim3 grid((unsigned)rows);
+    const uint4* xp = static_cast<const uint4*>(x);
+    uint8_t* qp = static_cast<uint8_t*>(q);
+#define BFQ_ROWS_CASE(PP)                                                                   \
+    if (slots <= PP) {                                                                      \
+        hipLaunchKernelGGL((quant_rows_kernel<IS_F32, QT, PP>), grid, dim3(256), 0, stream,  \
+                           xp, qp, scales, K, s_stride, eps, ue);                           \
+        return hipGetLastError();                                                           \
+    }
+    BFQ_ROWS_CASE(1)
+    BFQ_ROWS_CASE(2)
+    BFQ_ROWS_CASE(4)
+    BFQ_ROWS_CASE(8)
+    BFQ_ROWS_CASE(16)
+    BFQ_ROWS_CASE(32)
+#undef BFQ_ROWS_CASE
+    return hipErrorInvalidValue;   // K beyond kChannelMaxK (rejected by the caller)
+}
+
+hipError_t launch_quant_rows(const void* x, int is_f32, void* q, float* scales, int64_t rows,
+                             int64_t K, int qtype, int64_t s_stride, float eps, int sfmt,
+                             hipStream_t stream) {
+    const int ue = sfmt == S_UE8M0;
+    if (is_f32)
+        return qtype == Q_FP8
+                   ? launch_rows_p<1, Q_FP8>(x, q, scales, rows, K, s_stride, eps, ue, stream)
+                   : launch_rows_p<1, Q_INT8>(x, q, scales, rows, K, s_stride, eps, ue, stream);
+    return qtype == Q_FP8
+               ? launch_rows_p<0, Q_FP8>(x, q, scales, rows, K, s_stride, eps, ue, stream)
+               : launch_rows_p<0, Q_INT8>(x, q, scales, rows, K, s_stride, eps, ue, stream);
+}
 
 // Row-major [N][K] codes -> BFQ_W_PACKED16. Thread c writes 16-byte chunk c of the packed
 // matrix (coalesced): fragment F = c / 128 = f*KB + kb, half h, lane l; it reads the 16 bytes

@@ -7,7 +7,7 @@
 //   "entries": [
 //     { "N": 24576, "K": 7168, "dtype": "fp8_w8a8", "block_shape": [128, 128],
 //       "w_layout": "packed16",            (optional; "row_major" when absent)
-//       "scales": "ue8m0",                 (optional; "fp32" when absent)
+//       "scales": "ue8m0",                 (optional; "fp32" when absent; not with [1, K])
 //       "configs": { "1": {"variant": 1, "bm": 16, "bn": 128, "split_k": 2, "waves_m": 1,
 //                          "waves_n": 4, "stages": 4, "group_m": 1}, ... } } ] }
 #include "tile_table.h"
@@ -178,10 +178,17 @@ bool parse_tile_table(const std::string& text, TileTable& out, std::string& err)
         }
         const JVal* bs = e.get("block_shape");
         if (bs) {
-            if (bs->kind != JVal::ARR || bs->arr.size() != 2 || bs->arr[0].num != 128 ||
-                bs->arr[1].num != 128) {
-                err = "block_shape must be [128, 128]";
+            const bool two = bs->kind == JVal::ARR && bs->arr.size() == 2;
+            const bool block = two && bs->arr[0].num == 128 && bs->arr[1].num == 128;
+            // [1, K]: per-token x per-channel scales (a kernel family of its own)
+            const bool channel = two && bs->arr[0].num == 1 && bs->arr[1].num == (double)K;
+            if (!block && !channel) {
+                err = "block_shape must be [128, 128] or [1, K]";
                 return false;
+            }
+            if (channel) {
+                if (sfmt != 0) { err = "'scales' does not apply to block_shape [1, K]"; return false; }
+                sfmt = 2;
             }
         }
         const JVal* cfgs = e.get("configs");

@@ -21,7 +21,7 @@ struct TableKey {
     int64_t N, K;
     int qtype;
     int wlayout;   // weight layout the tuned kernels read (W_ROW / W_PACKED16)
-    int sfmt;      // scale format the entry was tuned for (S_FP32 / S_UE8M0)
+    int sfmt;      // scale handling the entry was tuned for (S_FP32 / S_UE8M0 / S_CHANNEL)
     bool operator<(const TableKey& o) const {
         if (N != o.N) return N < o.N;
         if (K != o.K) return K < o.K;

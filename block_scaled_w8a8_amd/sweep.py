@@ -1,6 +1,7 @@
 """On-device tile sweep that fills the tile table, and a single-shape runner for profiling.
 
-  python -m block_scaled_w8a8_amd.sweep tune  [--shapes N,K ...] [--dtype fp8|int8] [--scales fp32|ue8m0]
+  python -m block_scaled_w8a8_amd.sweep tune  [--shapes N,K ...] [--dtype fp8|int8]
+                                             [--scales fp32|ue8m0|channel]
                                              [--w-layout row|packed] [--out PATH]
   python -m block_scaled_w8a8_amd.sweep run   --M 4096 --N 24576 --K 7168 [--tile JSON] [--iters 50]
                                              [--w-layout row|packed]
@@ -13,7 +14,8 @@ one whose output agrees with a reference configuration is kept. Configurations t
 rejects (grid or workspace limits) are skipped, like the page's OutOfResources candidates.
 Results are written to a JSON tile table after every shape, and shapes already present in the
 output file are skipped, so an interrupted sweep resumes where it stopped. Each weight layout
-(row-major or packed) has entries of its own.
+(row-major or packed) and scale format has entries of its own; "channel" is the per-token x
+per-channel format (block_shape [1, K]).
 
 Timing rotates over enough copies of the weights and activations to exceed the 256 MB
 Infinity Cache, so the weight stream is measured from HBM.
@@ -55,12 +57,16 @@ class Problem:
         x = synth.activations(m_max, K, seed=0).to(dev)
         w = synth.weights(N, K, seed=0).to(dev)
         self.sf = bfq.BFQ_SCALE_UE8M0 if scales == "ue8m0" else bfq.BFQ_SCALE_FP32
-        qw, sw = bfq.quant_weight_blocks(w, q_dtype=self.qd, scale_fmt=self.sf)
+        self.channel = scales == "channel"
+        self.bs = bfq.channel_block_shape(K) if self.channel else bfq.BLOCK_SHAPE
+        qw, sw = bfq.quant_weight_blocks(w, q_dtype=self.qd, scale_fmt=self.sf,
+                                         per_channel=self.channel)
         self.wl = bfq.BFQ_W_PACKED16 if w_layout == "packed" else bfq.BFQ_W_ROW_MAJOR
         if self.wl == bfq.BFQ_W_PACKED16:
             qw = bfq.pack_weights(qw)
         self.layout = bfq.BFQ_SCALES_COL_MAJOR if layout == "col" else bfq.BFQ_SCALES_ROW_MAJOR
-        qa, sa = bfq.quant_tokens(x, q_dtype=self.qd, layout=self.layout, scale_fmt=self.sf)
+        qa, sa = bfq.quant_tokens(x, q_dtype=self.qd, layout=self.layout, scale_fmt=self.sf,
+                                  per_token=self.channel)
         del w, x
         foot = N * K + m_max * K
         if rotate is None:
@@ -90,7 +96,8 @@ class Problem:
         sa_m = sa if self.layout == bfq.BFQ_SCALES_COL_MAJOR else sa[:M]
         return bfq.bfq_block_gemm(qa[:M], sa_m, qw, sw, out[:M], a_layout=self.layout,
                                   a_scale_ld=sa.stride(0), tile=tile, workspace=ws,
-                                  workspace_bytes=need, w_layout=self.wl, scale_fmt=self.sf)
+                                  workspace_bytes=need, w_layout=self.wl, scale_fmt=self.sf,
+                                  block_shape=self.bs)
 
     def time_us(self, M, tile, warmup=3, iters=20, reps=3):
         """Median over reps of the mean time of `iters` back-to-back launches, replayed from a
@@ -120,15 +127,15 @@ class Problem:
         return res[len(res) // 2]
 
 
-def candidates(qd, M, N, K, wl=0, sf=0):
+def candidates(qd, M, N, K, wl=0, sf=0, block_shape=(128, 128)):
     """Compiled kernels x split-K factors x tile orders worth timing at this shape: the
     streaming kernel only while it re-reads the weights at most 4 times, split-K only while
     the grid is short of 4 workgroups per CU, tile orders only for multi-tile grids."""
     from . import bfq
     out = []
     KB = K // 128
-    for i in range(bfq.bfq_num_tile_candidates(qd, wl, sf)):
-        t = bfq.bfq_get_tile_candidate(i, qd, wl, sf)
+    for i in range(bfq.bfq_num_tile_candidates(qd, wl, sf, block_shape=block_shape)):
+        t = bfq.bfq_get_tile_candidate(i, qd, wl, sf, block_shape=block_shape)
         if t.variant == 1 and M > 4 * t.bm:
             continue
         if t.variant in (0, 2) and M <= 16 and t.bm > 64:
@@ -173,13 +180,13 @@ def tune_shape(N, K, qname, grid, budget_s, w_layout="row", scales="fp32"):
     for M in grid:
         t0 = time.time()
         _, ref_tile = bfq.bfq_select_tile(M, N, K, prob.qd, bfq.BFQ_FP32, w_layout=prob.wl,
-                                          scale_fmt=prob.sf)
+                                          scale_fmt=prob.sf, block_shape=prob.bs)
         prob.launch(M, ref_tile, out32=True)
         torch.cuda.synchronize()
         ref = prob.out32[:M].clone()
         best = None
         trials = []
-        for tile in candidates(prob.qd, M, N, K, prob.wl, prob.sf):
+        for tile in candidates(prob.qd, M, N, K, prob.wl, prob.sf, prob.bs):
             if time.time() - t0 > budget_s:
                 break
             try:
@@ -230,7 +237,8 @@ def cmd_tune(args):
     wname = "packed16" if args.w_layout == "packed" else "row_major"
 
     def key(e):
-        return (e["N"], e["K"], e["dtype"], e.get("w_layout", "row_major"), e.get("scales", "fp32"))
+        sc = "channel" if e.get("block_shape", [128, 128])[0] == 1 else e.get("scales", "fp32")
+        return (e["N"], e["K"], e["dtype"], e.get("w_layout", "row_major"), sc)
 
     done = {key(e) for e in table["entries"]}
     for (N, K) in shapes:
@@ -239,13 +247,14 @@ def cmd_tune(args):
             continue
         log(f"[sweep] N={N} K={K} {dname} {wname} {args.scales}")
         res = tune_shape(N, K, qname, args.grid or M_GRID, args.budget, args.w_layout, args.scales)
-        entry = {"N": N, "K": K, "dtype": dname, "block_shape": [128, 128],
+        entry = {"N": N, "K": K, "dtype": dname,
+                 "block_shape": [1, K] if args.scales == "channel" else [128, 128],
                  "configs": {str(M): {k: v for k, v in t.items() if k != "bk"}
                              for M, (us, t) in res.items()},
                  "us": {str(M): round(us, 3) for M, (us, t) in res.items()}}
         if wname != "row_major":
             entry["w_layout"] = wname
-        if args.scales != "fp32":
+        if args.scales == "ue8m0":
             entry["scales"] = args.scales
         table["entries"] = [e for e in table["entries"]
                             if key(e) != (N, K, dname, wname, args.scales)] + [entry]
@@ -263,7 +272,7 @@ def cmd_run(args):
         tile = bfq.bfq_tile.from_dict(json.loads(args.tile))
     else:
         _, tile = bfq.bfq_select_tile(args.M, args.N, args.K, prob.qd, bfq.BFQ_BF16,
-                                      w_layout=prob.wl, scale_fmt=prob.sf)
+                                      w_layout=prob.wl, scale_fmt=prob.sf, block_shape=prob.bs)
     if args.eager:
         # plain launches, no graph: for counter collection, which wants one dispatch per call
         for i in range(args.eager):
@@ -306,7 +315,7 @@ def main():
     t.add_argument("--budget", type=float, default=20.0, help="seconds per (shape, M)")
     t.add_argument("--force", action="store_true")
     t.add_argument("--w-layout", default="row", choices=["row", "packed"])
-    t.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0"])
+    t.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0", "channel"])
     r = sub.add_parser("run")
     r.add_argument("--M", type=int, required=True)
     r.add_argument("--N", type=int, required=True)
@@ -318,7 +327,7 @@ def main():
     r.add_argument("--eager", type=int, default=0, help="launch this many times without timing")
     r.add_argument("--layout", default="col", choices=["row", "col"], help="activation scales")
     r.add_argument("--w-layout", default="row", choices=["row", "packed"])
-    r.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0"])
+    r.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0", "channel"])
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=1 << 30)
     c.add_argument("--iters", type=int, default=3)

@@ -109,7 +109,8 @@ typedef enum {
  *   split_k  : K blocks split into split_k contiguous chunks (>= 1), fp32 partials reduced
  *             in a fixed order ([HELION] kernel section).
  *   stages   : LDS stages (variants 0, 2) or weight prefetch depth in K blocks (variant 1).
- *   sched    : variants 0 and 2 instruction schedule (variant 1: see above): 3 = the scales
+ *   sched    : variants 0 and 2 instruction schedule (variant 1: see above): 4 = per-token x
+ *             per-channel scales (block_shape {1, K}), the MFMA accumulating the whole K; 3 = the scales
  *             applied by the block-scaled MFMA, which accumulates across K blocks (fp8 and
  *             BFQ_SCALE_UE8M0 scales only); 0 = each sub-tile's scale FMAs right after its
  *             MFMAs, 1 = software-pipelined (FMAs one sub-tile behind the MFMAs), 2 = 32x32
@@ -131,7 +132,10 @@ typedef struct {
  * A group containing NaN gets a NaN scale and codes 0x7F (e4m3fn) or 0 (int8).
  *   x_bf16 [M][K] row-major bf16; q [M][K] row-major codes (1 byte);
  *   scales: fp32, layout per `layout` with leading dimension scale_ld.
- * group_size must be 128; q_dtype must be BFQ_E4M3FN or BFQ_INT8. */
+ * group_size 128, or group_size == K for one scale per token (the per-token activation scales
+ * of the FP8_Dynamic / W8A8_INT8 formats, [HELION] scope section; K <= 32768): scales then
+ * hold one value per row, at scales[m * scale_ld] (row-major, scale_ld >= 1) or scales[m]
+ * (column-major, scale_ld >= M). q_dtype must be BFQ_E4M3FN or BFQ_INT8. */
 bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t group_size,
                             bfq_dtype q_dtype, void* q, float* scales, bfq_scale_layout layout,
                             int64_t scale_ld, float eps, bfq_scale_format scale_fmt,
@@ -140,7 +144,9 @@ bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t gr
 /* Per-block weight quantization, the offline step before the GEMM ([BENCH] §4.1
  * per_block_cast_to_fp8 with fp32 scales): for each block_shape[0] x block_shape[1] block of
  * w [N][K] (fp32, row-major): scale = max(amax, eps)/Qmax, q = encode(w / scale).
- *   q [N][K] codes; scales [N/128][K/128] row-major fp32. block_shape must be {128,128}. */
+ *   q [N][K] codes; scales [N/128][K/128] row-major fp32.
+ * block_shape {128, 128}, or {1, K} for one scale per output channel (the per-channel weight
+ * scales of FP8_Dynamic / W8A8_INT8, [HELION] scope section; K <= 32768): scales [N]. */
 bfq_status bfq_quant_weight_blocks(const float* w, int64_t N, int64_t K,
                                    const int32_t block_shape[2] /* host */, bfq_dtype q_dtype,
                                    void* q, float* scales, float eps,
@@ -153,7 +159,7 @@ bfq_status bfq_quant_weight_blocks(const float* w, int64_t N, int64_t K,
 bfq_status bfq_pack_weights(const void* w_q, int64_t N, int64_t K, bfq_dtype q_dtype,
                             void* w_packed, void* stream);
 
-/* Tile selection ([CONFIG] §4.1-§4.2): exact (N, K, dtype, weight layout, scale format) entry of the loaded
+/* Tile selection ([CONFIG] §4.1-§4.2): exact (N, K, dtype, block shape, weight layout, scale format) entry of the loaded
  * tile table, then the bucket nearest to M (ties to the smaller bucket; M past the grid ->
  * last bucket). No entry -> the compiled-in default rule and BFQ_WARN_DEFAULT_TILE ([CONFIG]
  * §4.1 warns and falls back to a default config). tile_out is a host pointer. */
@@ -191,6 +197,14 @@ size_t bfq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const bfq_tile*
  *   tile NULL -> bfq_select_tile for (w_layout, scale_fmt); an explicit tile must name a
  *   kernel compiled for w_layout whose scale handling allows scale_fmt (else BFQ_ERR_TILE);
  *   workspace may be NULL when the tile needs none.
+ * block_shape {1, K} selects the per-token x per-channel format ([HELION] scope section,
+ * FP8_Dynamic / W8A8_INT8; K <= 32768):
+ *   out[m][n] = ( sum_k a_q[m][k] * w_q[n][k] ) * a_scales[m] * w_scales[n]
+ *   with one scale per token (a_layout row-major: a_scales[m * a_scale_ld], a_scale_ld >= 1;
+ *   column-major: a_scales[m], a_scale_ld >= M) and w_scales [N]; the codes' product is
+ *   accumulated over the whole K (fp8: fp32 MFMA accumulation; int8: exact int32), then
+ *   scaled once. scale_fmt does not change how such scales are applied. Those kernels are
+ *   tiles with sched 4 (variants 0 and 2) or the variant 1 tiles built for this format.
  * Returns BFQ_WARN_DEFAULT_TILE when tile was NULL and the default rule was used. */
 bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
                           int64_t a_scale_ld, const void* w_q, const float* w_scales,
@@ -205,13 +219,15 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
  * concurrently with other calls. NULL reloads the default location. */
 bfq_status bfq_load_tile_table(const char* json_path);
 
-/* Number of compiled kernel configurations usable for (in_dtype, w_layout, scale_fmt), and
- * the i-th one (split_k = 1; any split_k >= 1 may be combined with it). Used by the
- * on-device sweep. */
-int32_t bfq_num_tile_candidates(bfq_dtype in_dtype, bfq_weight_layout w_layout,
-                                bfq_scale_format scale_fmt);
-bfq_status bfq_get_tile_candidate(bfq_dtype in_dtype, bfq_weight_layout w_layout,
-                                  bfq_scale_format scale_fmt, int32_t index, bfq_tile* tile_out);
+/* Number of compiled kernel configurations usable for (block_shape, in_dtype, w_layout,
+ * scale_fmt), and the i-th one (split_k = 1; any split_k >= 1 may be combined with it). Used
+ * by the on-device sweep. block_shape (host) {128, 128}, or {1, k} (any k > 0) for the
+ * per-token x per-channel kernels. */
+int32_t bfq_num_tile_candidates(const int32_t block_shape[2], bfq_dtype in_dtype,
+                                bfq_weight_layout w_layout, bfq_scale_format scale_fmt);
+bfq_status bfq_get_tile_candidate(const int32_t block_shape[2], bfq_dtype in_dtype,
+                                  bfq_weight_layout w_layout, bfq_scale_format scale_fmt,
+                                  int32_t index, bfq_tile* tile_out);
 
 const char* bfq_status_string(bfq_status s);
 const char* bfq_last_error(void);

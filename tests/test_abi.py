@@ -337,3 +337,116 @@ def test_batch_invariant_selection(bfq):
     finally:
         bfq.bfq_set_batch_invariant(False)
     assert not bfq.bfq_get_batch_invariant()
+
+
+# ------------------------------------------- per-token x per-channel format (block_shape {1, K})
+
+def _bs(a, b):
+    return (ctypes.c_int32 * 2)(a, b)
+
+
+def _channel_cands(bfq, qd, wl):
+    ch = bfq.channel_block_shape(7168)
+    return [bfq.bfq_get_tile_candidate(i, qd, wl, 0, block_shape=ch)
+            for i in range(bfq.bfq_num_tile_candidates(qd, wl, 0, block_shape=ch))]
+
+
+def test_channel_gemm_validation_without_launch(bfq):
+    ch = _bs(1, 7168)
+    assert _gemm(bfq, M=0, block_shape=ch, a_scale_ld=1) >= 0
+    assert _gemm(bfq, M=0, block_shape=ch, a_layout=1, a_scale_ld=0) >= 0
+    assert _gemm(bfq, block_shape=_bs(1, 7040)) == bfq.BFQ_ERR_SHAPE       # [1, k], k != K
+    assert _gemm(bfq, block_shape=_bs(2, 7168)) == bfq.BFQ_ERR_SHAPE
+    assert _gemm(bfq, K=32896, block_shape=_bs(1, 32896), a_scale_ld=1) == bfq.BFQ_ERR_SHAPE
+    assert _gemm(bfq, M=0, K=32768, block_shape=_bs(1, 32768), a_scale_ld=1) >= 0
+    assert _gemm(bfq, M=4, block_shape=ch, a_scale_ld=0) == bfq.BFQ_ERR_SHAPE
+    assert _gemm(bfq, M=64, block_shape=ch, a_layout=1, a_scale_ld=63) == bfq.BFQ_ERR_SHAPE
+    # a block-scale tile cannot serve per-channel scales, nor the other way round
+    tb = bfq.bfq_get_tile_candidate(0)
+    assert _gemm(bfq, M=64, block_shape=ch, a_scale_ld=1, tile=ctypes.pointer(tb)) == bfq.BFQ_ERR_TILE
+    tc = _channel_cands(bfq, bfq.BFQ_E4M3FN, 0)[0]
+    assert _gemm(bfq, M=64, tile=ctypes.pointer(tc)) == bfq.BFQ_ERR_TILE
+    assert _gemm(bfq, M=0, block_shape=ch, a_scale_ld=1, tile=ctypes.pointer(tc)) >= 0
+
+
+def test_channel_quant_validation_without_launch(bfq):
+    q = bfq.lib.bfq_quant_tokens
+    # M = 0: validated, nothing launched
+    assert q(FAKE, 0, 7168, 7168, bfq.BFQ_E4M3FN, FAKE, FAKE, 0, 1, 1e-10, 0, None) == bfq.BFQ_OK
+    assert q(FAKE, 0, 7168, 7168, bfq.BFQ_INT8, FAKE, FAKE, 1, 0, 1e-10, 1, None) == bfq.BFQ_OK
+    assert q(FAKE, 4, 7168, 7168, bfq.BFQ_E4M3FN, FAKE, FAKE, 0, 0, 1e-10, 0, None) == bfq.BFQ_ERR_SHAPE
+    assert q(FAKE, 4, 7168, 3584, bfq.BFQ_E4M3FN, FAKE, FAKE, 0, 2, 1e-10, 0, None) == bfq.BFQ_ERR_SHAPE
+    assert q(FAKE, 4, 32896, 32896, bfq.BFQ_E4M3FN, FAKE, FAKE, 0, 1, 1e-10, 0, None) == bfq.BFQ_ERR_SHAPE
+    w = bfq.lib.bfq_quant_weight_blocks
+    assert w(FAKE, 0, 7168, _bs(1, 7168), bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, 0, None) == bfq.BFQ_OK
+    assert w(FAKE, 256, 7168, _bs(1, 7040), bfq.BFQ_E4M3FN, FAKE, FAKE, 1e-10, 0, None) == bfq.BFQ_ERR_SHAPE
+    assert w(FAKE, 256, 32896, _bs(1, 32896), bfq.BFQ_INT8, FAKE, FAKE, 1e-10, 0, None) == bfq.BFQ_ERR_SHAPE
+
+
+@pytest.mark.parametrize("wl", [0, 1])
+def test_channel_candidates(bfq, wl):
+    """Per-channel kernels: the standard and stream-K ones use sched 4 (whole-K accumulation)
+    and no block-format candidate does; the streaming kernels exist for both dtypes."""
+    for qd in (bfq.BFQ_E4M3FN, bfq.BFQ_INT8):
+        cands = _channel_cands(bfq, qd, wl)
+        assert len(cands) >= 8
+        assert {t.variant for t in cands} >= {0, 1}
+        assert all(t.sched == 4 for t in cands if t.variant in (0, 2))
+        for sf in (0, 1):
+            block = [bfq.bfq_get_tile_candidate(i, qd, wl, sf)
+                     for i in range(bfq.bfq_num_tile_candidates(qd, wl, sf))]
+            assert all(t.sched != 4 for t in block)
+    assert bfq.bfq_num_tile_candidates(bfq.BFQ_E4M3FN, 0, 0, block_shape=(64, 64)) == 0
+
+
+def test_channel_default_and_invariant_tiles(bfq, tmp_path):
+    """With no tuned entry the default rule and the batch-invariant mode pick compiled
+    per-channel kernels for every M, both dtypes and both weight layouts."""
+    p = tmp_path / "empty.json"
+    p.write_text(_table([]))
+    bfq.bfq_load_tile_table(str(p))
+    ch = bfq.channel_block_shape(7168)
+    try:
+        for inv in (False, True):
+            bfq.bfq_set_batch_invariant(inv)
+            for qd in (bfq.BFQ_E4M3FN, bfq.BFQ_INT8):
+                for wl in (0, 1):
+                    for M in (1, 16, 31, 64, 200, 513, 4096):
+                        st, t = bfq.bfq_select_tile(M, 24576, 7168, in_dtype=qd, w_layout=wl,
+                                                    block_shape=ch)
+                        assert st == (bfq.BFQ_OK if inv else bfq.BFQ_WARN_DEFAULT_TILE)
+                        assert t.variant == 1 or t.sched == 4
+                        if inv:   # no split-K; variant 1's waves_m is its in-workgroup K split
+                            assert t.split_k == 1 and (t.variant == 0 or t.waves_m == 1)
+                        assert _gemm(bfq, M=0, N=24576, in_dtype=qd, w_layout=wl,
+                                     block_shape=_bs(1, 7168), a_scale_ld=1,
+                                     tile=ctypes.pointer(t)) >= 0, (inv, qd, wl, M, t.as_dict())
+    finally:
+        bfq.bfq_set_batch_invariant(False)
+        bfq.bfq_load_tile_table(None)
+
+
+def test_table_channel_key(bfq, tmp_path):
+    """An entry with "block_shape": [1, K] serves the per-channel format only, must name
+    per-channel kernels and takes no "scales" field."""
+    tc = _channel_cands(bfq, bfq.BFQ_E4M3FN, 0)[0].as_dict()
+    tb = bfq.bfq_get_tile_candidate(0).as_dict()
+    p = tmp_path / "t.json"
+    p.write_text(_table([{"N": 1536, "K": 7168, "dtype": "fp8_w8a8", "block_shape": [1, 7168],
+                          "configs": {"16": dict(tc, split_k=2)}}]))
+    try:
+        assert bfq.bfq_load_tile_table(str(p)) == bfq.BFQ_OK
+        st, t = bfq.bfq_select_tile(16, 1536, 7168, block_shape=bfq.channel_block_shape(7168))
+        assert st == bfq.BFQ_OK and t.as_dict() == dict(tc, split_k=2, bk=128)
+        st, t = bfq.bfq_select_tile(16, 1536, 7168)
+        assert st == bfq.BFQ_WARN_DEFAULT_TILE
+    finally:
+        bfq.bfq_load_tile_table(None)
+    for e in ({"block_shape": [1, 7168], "configs": {"16": tb}},                     # block tile
+              {"block_shape": [1, 1536], "configs": {"16": tc}},                     # [1, k != K]
+              {"block_shape": [1, 7168], "scales": "ue8m0", "configs": {"16": tc}}):
+        bad = tmp_path / "bad.json"
+        bad.write_text(_table([dict({"N": 1536, "K": 7168, "dtype": "fp8_w8a8"}, **e)]))
+        with pytest.raises(bfq.BfqError):
+            bfq.bfq_load_tile_table(str(bad))
+    bfq.bfq_load_tile_table(None)
