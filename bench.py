@@ -49,7 +49,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_name(t, qtype: str, wl: int, out: str = "bf16") -> str:
+def kernel_name(t, qtype: str, wl: int, out: str = "bf16", channel: bool = False) -> str:
     """The demangled name of the device kernel a tile launches (as rocprofv3 prints it)."""
     q = 0 if qtype == "fp8" else 1
     o = {"bf16": 0, "fp16": 1, "fp32": 2}[out]
@@ -61,7 +61,7 @@ def kernel_name(t, qtype: str, wl: int, out: str = "bf16") -> str:
     nwr = d["bn"] // d["waves_n"]
     kern = "gemm_swapab_lds_kernel" if d["sched"] == 1 else "gemm_swapab_kernel"
     return (f"bfq::{kern}<{d['bm']}, {nwr}, {d['waves_n']}, {d['waves_m']}, "
-            f"{d['stages']}, {q}, {o}, {wl}>")
+            f"{d['stages']}, {q}, {o}, {wl}, {int(channel)}>")
 
 
 def grid_threads(t, M, N) -> int:
@@ -89,6 +89,7 @@ def run_gpu(args, wl):
     qd = bfq.BFQ_E4M3FN if wl["qtype"] == "fp8" else bfq.BFQ_INT8
     wlay = bfq.BFQ_W_PACKED16 if args.w_layout == "packed" else bfq.BFQ_W_ROW_MAJOR
     sfmt = bfq.BFQ_SCALE_UE8M0 if args.scales == "ue8m0" else bfq.BFQ_SCALE_FP32
+    channel = args.scales == "channel"       # per-token x per-channel scales
     m_max = max(wl["M"])
     col = args.scale_layout == "col"
     shapes = []
@@ -100,7 +101,7 @@ def run_gpu(args, wl):
         wd = w.to(dev)
         copies = []
         for r in range(args.rotate):
-            qw, sw = bfq.quant_weight_blocks(wd, q_dtype=qd, scale_fmt=sfmt)
+            qw, sw = bfq.quant_weight_blocks(wd, q_dtype=qd, scale_fmt=sfmt, per_channel=channel)
             if wlay == bfq.BFQ_W_PACKED16:        # offline layout step, like the quantization
                 qw = bfq.pack_weights(qw)
             copies.append((qw, sw))
@@ -108,19 +109,20 @@ def run_gpu(args, wl):
         xd = x.to(dev)
         qa = torch.empty((m_max, K), dtype=torch.uint8 if qd == bfq.BFQ_E4M3FN else torch.int8,
                          device=dev)
-        sa = torch.empty((K // 128, m_max) if col else (m_max, K // 128), dtype=torch.float32,
-                         device=dev)
+        G = 1 if channel else K // 128       # activation scales per token
+        bs = bfq.channel_block_shape(K) if channel else bfq.BLOCK_SHAPE
+        sa = torch.empty((G, m_max) if col else (m_max, G), dtype=torch.float32, device=dev)
         out = torch.empty((m_max, N), dtype=torch.bfloat16, device=dev)
         plans = []
         for M in wl["M"]:
             st, tile = bfq.bfq_select_tile(M, N, K, qd, bfq.BFQ_BF16, w_layout=wlay,
-                                           scale_fmt=sfmt)
+                                           scale_fmt=sfmt, block_shape=bs)
             ws_bytes = bfq.bfq_gemm_workspace_bytes(M, N, K, tile)
             plans.append((M, tile, ws_bytes, st))
         ws_max = max(p[2] for p in plans)
         ws = torch.empty(max(ws_max, 16), dtype=torch.uint8, device=dev)
         shapes.append(dict(N=N, K=K, copies=copies, xd=xd, qa=qa, sa=sa, out=out, plans=plans,
-                           ws=ws, ws_max=ws_max))
+                           ws=ws, ws_max=ws_max, bs=bs, group=K if channel else 128))
         host[(N, K)] = (w, x)
     torch.cuda.synchronize()
 
@@ -134,10 +136,12 @@ def run_gpu(args, wl):
                 lay = bfq.BFQ_SCALES_COL_MAJOR if col else bfq.BFQ_SCALES_ROW_MAJOR
                 sa_m = sh["sa"] if col else sh["sa"][:M]
                 bfq.bfq_quant_tokens(sh["xd"][:M], sh["qa"][:M], sa_m, layout=lay,
-                                     scale_ld=sh["sa"].stride(0), scale_fmt=sfmt)
+                                     scale_ld=sh["sa"].stride(0), scale_fmt=sfmt,
+                                     group_size=sh["group"])
                 bfq.bfq_block_gemm(sh["qa"][:M], sa_m, qw, sw, sh["out"][:M], a_layout=lay,
                                    a_scale_ld=sh["sa"].stride(0), tile=tile, workspace=sh["ws"],
-                                   workspace_bytes=sh["ws_max"], w_layout=wlay, scale_fmt=sfmt)
+                                   workspace_bytes=sh["ws_max"], w_layout=wlay, scale_fmt=sfmt,
+                                   block_shape=sh["bs"])
 
     for _ in range(args.warmup):
         one_step()
@@ -188,13 +192,15 @@ def run_gpu(args, wl):
 
             def q_once():
                 bfq.bfq_quant_tokens(sh["xd"][:M], sh["qa"][:M], sa_m, layout=lay,
-                                     scale_ld=sa_all.stride(0), scale_fmt=sfmt)
+                                     scale_ld=sa_all.stride(0), scale_fmt=sfmt,
+                                     group_size=sh["group"])
 
             def g_once(i):
                 qw, sw = sh["copies"][i % len(sh["copies"])]
                 bfq.bfq_block_gemm(sh["qa"][:M], sa_m, qw, sw, sh["out"][:M], a_layout=lay,
                                    a_scale_ld=sa_all.stride(0), tile=tile, workspace=sh["ws"],
-                                   workspace_bytes=sh["ws_max"], w_layout=wlay, scale_fmt=sfmt)
+                                   workspace_bytes=sh["ws_max"], w_layout=wlay, scale_fmt=sfmt,
+                                   block_shape=sh["bs"])
 
             res = {}
             for name, fn in (("q", lambda i: q_once()), ("g", g_once)):
@@ -234,19 +240,20 @@ def run_gpu(args, wl):
                 "gemm_us": round(g * 1e6, 2), "quant_us": round(q * 1e6, 2),
                 "tflops": round(perf.tflops(M, N, K, g), 2),
                 "gbs_page": round(perf.gbs_page(M, N, K, g), 1),
-                "gbs_all": round(perf.gbs_all(M, N, K, g), 1),
-                "bound": perf.bound(M, N, K),
-                "roofline_frac": round(perf.roofline_time_s(M, N, K) / g, 4),
-                "quant_gbs": round(perf.quant_bytes(M, K) / q / 1e9, 1),
+                "gbs_all": round(perf.gbs_all(M, N, K, g, channel=channel), 1),
+                "bound": perf.bound(M, N, K, channel=channel),
+                "roofline_frac": round(perf.roofline_time_s(M, N, K, channel=channel) / g, 4),
+                "quant_gbs": round(perf.quant_bytes(M, K, channel) / q / 1e9, 1),
             })
             gr = groups.setdefault(r["key"], {"t": 0.0, "n": 0, "flops": 0.0, "bytes": 0.0,
-                                              "name": kernel_name(tile, wl["qtype"], wlay),
+                                              "name": kernel_name(tile, wl["qtype"], wlay,
+                                                                  channel=channel),
                                               "grids": set()})
             gr["grids"].add(grid_threads(tile, M, N))
             gr["t"] += sum(r["g"]) * R
             gr["n"] += len(r["g"]) * R
             gr["flops"] += perf.gemm_flops(M, N, K) * len(r["g"]) * R
-            gr["bytes"] += perf.gemm_bytes_all(M, N, K) * len(r["g"]) * R
+            gr["bytes"] += perf.gemm_bytes_all(M, N, K, channel=channel) * len(r["g"]) * R
     dom_key = max(groups, key=lambda k: groups[k]["t"])
     dom = groups[dom_key]
     t_flop = dom["flops"] / (perf.FP8_PEAK_TFLOPS * 1e12)
@@ -302,14 +309,20 @@ def cpu_baseline(wl, host, target_s: float, scales: str = "fp32"):
     (N, K) = wl["shapes"][0]
     w, x = host[(N, K)]
     sf = oracle.SCALE_UE8M0 if scales == "ue8m0" else oracle.SCALE_FP32
+    channel = scales == "channel"
     log(f"[bench] cpu baseline: oracle weight quantization N={N} K={K} (untimed)")
-    qw, sw = oracle.quant_blocks(w.numpy(), qtype=qt, scale_fmt=sf)
+    qw, sw = oracle.quant_blocks(w.numpy(), block=(1, K) if channel else (128, 128), qtype=qt,
+                                 scale_fmt=sf)
     xb = synth.bf16_bits(x)
 
     def run(rows):
         t0 = time.perf_counter()
-        qa, sa = oracle.quant_groups(np.ascontiguousarray(xb[:rows]), qtype=qt, scale_fmt=sf)
-        oracle.block_gemm(qa, sa, qw, sw, qtype=qt)
+        qa, sa = oracle.quant_groups(np.ascontiguousarray(xb[:rows]), group=K if channel else 128,
+                                     qtype=qt, scale_fmt=sf)
+        if channel:
+            oracle.channel_gemm(qa, sa, qw, sw, qtype=qt)
+        else:
+            oracle.block_gemm(qa, sa, qw, sw, qtype=qt)
         return time.perf_counter() - t0
 
     t1 = run(1)
@@ -337,9 +350,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--scale-layout", default="col", choices=["row", "col"],
                     help="activation-scale layout written by the quantizer and read by the GEMM")
-    ap.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0"],
-                    help="block scale format: fp32 amax/Qmax (default), or rounded up to a "
-                         "power of two (UE8M0)")
+    ap.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0", "channel"],
+                    help="scale format: 1x128 / 128x128 block scales as fp32 amax/Qmax "
+                         "(default) or rounded up to a power of two (UE8M0); or 'channel', "
+                         "one fp32 scale per token and per output channel")
     ap.add_argument("--w-layout", default="packed", choices=["row", "packed"],
                     help="weight-code layout in HBM (packed: bfq_pack_weights, done offline)")
     args = ap.parse_args()
@@ -367,7 +381,8 @@ def main():
         "dtype": "fp8_e4m3fn" if wl["qtype"] == "fp8" else "int8",
         "data": "synthetic",
         "config": {"workload": wl["desc"], "shapes_NK": wl["shapes"], "M": wl["M"],
-                   "block_shape": [128, 128], "out_dtype": "bf16",
+                   "block_shape": [1, wl["shapes"][0][1]] if args.scales == "channel" else [128, 128],
+                   "out_dtype": "bf16",
                    "weight_copies_rotated": args.rotate,
                    "activation_scale_layout": args.scale_layout + "_major",
                    "weight_layout": "packed16" if args.w_layout == "packed" else "row_major",

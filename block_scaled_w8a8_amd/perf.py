@@ -5,7 +5,9 @@ The pages' formulas (block GEMM benchmark page, "vLLM DeepGEMM FP8 Block GEMM åŸ
 Â§4.3): TFLOPS = 2*m*n*k / t / 1e12 and GB/s = (m*k + k*n + 2*m*n) / t, i.e. fp8 inputs of one
 byte per element, a bf16 output, and no scale bytes. ``gemm_bytes_all`` also counts the
 fp32 scales and the real output width; it is the algorithmic byte count used for the
-roofline.
+roofline. ``channel`` selects the per-token x per-channel format (Helion linear-backend page,
+scope section): one fp32 scale per token and per output channel instead of per 1x128 group
+and 128x128 block.
 """
 from __future__ import annotations
 
@@ -23,15 +25,20 @@ def gemm_bytes_page(m: int, n: int, k: int) -> float:
     return float(m * k + k * n + 2 * m * n)
 
 
-def gemm_bytes_all(m: int, n: int, k: int, out_bytes: int = 2) -> float:
+def scale_bytes(m: int, n: int, k: int, channel: bool = False) -> float:
+    if channel:
+        return float(4 * m + 4 * n)
+    return float(4 * m * (k // 128) + 4 * (n // 128) * (k // 128))
+
+
+def gemm_bytes_all(m: int, n: int, k: int, out_bytes: int = 2, channel: bool = False) -> float:
     """Every byte the method must move once: codes, fp32 scales, output."""
-    return float(m * k + n * k + 4 * m * (k // 128) + 4 * (n // 128) * (k // 128)
-                 + out_bytes * m * n)
+    return float(m * k + n * k + out_bytes * m * n) + scale_bytes(m, n, k, channel)
 
 
-def quant_bytes(m: int, k: int) -> float:
-    """bf16 in, one code byte out, one fp32 scale per 128 elements."""
-    return float(2 * m * k + m * k + 4 * m * (k // 128))
+def quant_bytes(m: int, k: int, channel: bool = False) -> float:
+    """bf16 in, one code byte out, one fp32 scale per 128 elements (per token: per row)."""
+    return float(2 * m * k + m * k) + (4.0 * m if channel else 4.0 * m * (k // 128))
 
 
 def tflops(m: int, n: int, k: int, seconds: float) -> float:
@@ -42,17 +49,18 @@ def gbs_page(m: int, n: int, k: int, seconds: float) -> float:
     return gemm_bytes_page(m, n, k) / seconds / 1e9
 
 
-def gbs_all(m: int, n: int, k: int, seconds: float, out_bytes: int = 2) -> float:
-    return gemm_bytes_all(m, n, k, out_bytes) / seconds / 1e9
+def gbs_all(m: int, n: int, k: int, seconds: float, out_bytes: int = 2,
+            channel: bool = False) -> float:
+    return gemm_bytes_all(m, n, k, out_bytes, channel) / seconds / 1e9
 
 
-def roofline_time_s(m: int, n: int, k: int, out_bytes: int = 2) -> float:
+def roofline_time_s(m: int, n: int, k: int, out_bytes: int = 2, channel: bool = False) -> float:
     """Lower bound on the GEMM time on MI355X: max(bytes / HBM peak, flops / FP8 peak)."""
-    return max(gemm_bytes_all(m, n, k, out_bytes) / (HBM_PEAK_GBS * 1e9),
+    return max(gemm_bytes_all(m, n, k, out_bytes, channel) / (HBM_PEAK_GBS * 1e9),
                gemm_flops(m, n, k) / (FP8_PEAK_TFLOPS * 1e12))
 
 
-def bound(m: int, n: int, k: int, out_bytes: int = 2) -> str:
-    t_mem = gemm_bytes_all(m, n, k, out_bytes) / (HBM_PEAK_GBS * 1e9)
+def bound(m: int, n: int, k: int, out_bytes: int = 2, channel: bool = False) -> str:
+    t_mem = gemm_bytes_all(m, n, k, out_bytes, channel) / (HBM_PEAK_GBS * 1e9)
     t_mma = gemm_flops(m, n, k) / (FP8_PEAK_TFLOPS * 1e12)
     return "hbm" if t_mem >= t_mma else "mfma"
