@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.orc_block_gemm.argtypes = [p, p, p, p, i64, i64, i64, i32, p, p]
         L.orc_block_gemm_sampled.restype = None
         L.orc_block_gemm_sampled.argtypes = [p, p, p, p, i64, i64, i64, i32, p, p, i64, p]
+        L.orc_pack_scales_ue8m0.restype = None
+        L.orc_pack_scales_ue8m0.argtypes = [p, i64, i64, p, i64]
         L.orc_channel_gemm.restype = None
         L.orc_channel_gemm.argtypes = [p, p, p, p, i64, i64, i64, i32, p, p]
         L.orc_channel_gemm_sampled.restype = None
@@ -172,6 +174,20 @@ def quant_blocks(w: np.ndarray, block=(128, 128), qtype: int = FP8, eps: float =
 
 
 # ------------------------------------------------------------------ GEMM
+
+def pack_scales_ue8m0(s: np.ndarray, ld: int | None = None) -> np.ndarray:
+    """UE8M0 scales [M, G] -> packed words [ceil(G/4), ld] (uint32), ld >= round_up(M, 4)
+    (default round_up(M, 4)): the quantizer's packed scale output of the per-token-group
+    kernel page (output_s_packed)."""
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    M, G = s.shape
+    Mp = (M + 3) // 4 * 4
+    ld = Mp if ld is None else ld
+    assert ld >= Mp
+    words = np.zeros(((G + 3) // 4, ld), dtype=np.uint32)
+    lib().orc_pack_scales_ue8m0(_ptr(s), M, G, _ptr(words), ld)
+    return words
+
 
 def pack16(w: np.ndarray) -> np.ndarray:
     """The packed 16-row fragment layout of weight codes (a byte permutation; the layout is

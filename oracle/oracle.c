@@ -179,6 +179,36 @@ void orc_quant_blocks(const float* w, int64_t N, int64_t K, int64_t bn, int64_t 
     }
 }
 
+/* --------------------------------------------------- packed UE8M0 scale words ---- */
+
+/* [PR] page, per_token_group_quant_8bit_packed: the scales of a token's groups leave the
+ * quantizer as UE8M0 bytes, four consecutive groups to one 32-bit word (output_s_packed),
+ * the words stored token-major with the token count padded for TMA (tma_aligned_mn).
+ * Reading: word (w, m) at words[w * ld + m]; its byte j (bits 8j..8j+7) is the E8M0 code of
+ * the scale of group 4w + j of token m, 0 past the last group; the rows M .. round_up(M, 4)
+ * - 1 hold zero words. The E8M0 code of a power of two 2^e is e + 127; NaN (and, since E8M0
+ * has no infinity, Inf) is 255. */
+static uint32_t e8m0_code(float s) {
+    if (isnan(s) || isinf(s)) return 255u;
+    int e;
+    double f = frexp((double)s, &e);       /* s = f * 2^e, f = 0.5 for a power of two */
+    (void)f;
+    return (uint32_t)(e - 1 + 127);
+}
+
+void orc_pack_scales_ue8m0(const float* s, int64_t M, int64_t G, uint32_t* words, int64_t ld) {
+    int64_t W = (G + 3) / 4, Mp = (M + 3) / 4 * 4;
+    for (int64_t w = 0; w < W; ++w)
+        for (int64_t m = 0; m < Mp; ++m) {
+            uint32_t word = 0;
+            for (int64_t j = 0; j < 4; ++j) {
+                int64_t g = 4 * w + j;
+                if (m < M && g < G) word |= e8m0_code(s[m * G + g]) << (8 * j);
+            }
+            words[w * ld + m] = word;
+        }
+}
+
 /* ------------------------------------------------------------------ GEMM ---- */
 
 static double g_dec[256];

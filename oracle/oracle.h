@@ -58,6 +58,11 @@ void orc_quant_groups(const uint16_t* x, int64_t M, int64_t K, int64_t group,
 void orc_quant_blocks(const float* w, int64_t N, int64_t K, int64_t bn, int64_t bk,
                       int qtype, void* q, float* s, float eps, int scale_fmt);
 
+/* UE8M0 scales s[M][G] (powers of two) -> packed words: word (w, m) at words[w*ld + m],
+ * byte j = E8M0 code (exponent + 127; NaN/Inf -> 255) of group 4w+j, 0 past G; rows
+ * M .. round_up(M,4)-1 zero. ld >= round_up(M, 4). */
+void orc_pack_scales_ue8m0(const float* s, int64_t M, int64_t G, uint32_t* words, int64_t ld);
+
 /* Block-scaled GEMM C[M][N] = sum_kb (sum_{k in kb} A[m,k] W[n,k]) * sa[m,kb] * sw[n/128,kb].
  * qa[M][K], qw[N][K] codes; sa[M][K/128]; sw[N/128][K/128]. Per-block sums are exact
  * (fp64 for fp8, int32 for int8); the running accumulator is fp32 in ascending kb order.

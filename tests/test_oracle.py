@@ -617,3 +617,35 @@ def test_channel_gemm_sampled_matches_full(orc):
     ms = rng.integers(0, 9, 100)
     ns = rng.integers(0, 384, 100)
     assert np.array_equal(orc.channel_gemm_sampled(qa, sa, qw, sw, ms, ns, qtype=orc.INT8), c32[ms, ns])
+
+
+# --------------------------------------------------------- packed UE8M0 scale words
+# Per-token-group kernel page (output_s_packed): four UE8M0 bytes per 32-bit word, words
+# token-major, token count padded to a multiple of 4.
+
+def test_pack_scales_worked_values(orc):
+    """From the E8M0 definition (value 2^(code - 127)): 1 -> 127, 2 -> 128, 0.5 -> 126,
+    2^-42 -> 85, 2^10 -> 137, NaN -> 255; byte j of a word holds group 4w + j."""
+    s = np.array([[1.0, 2.0, 0.5, 2.0 ** -42, 2.0 ** 10, np.nan]], dtype=np.float32)
+    words = orc.pack_scales_ue8m0(s)
+    assert words.shape == (2, 4)
+    assert words[0, 0] == 127 | (128 << 8) | (126 << 16) | (85 << 24)
+    assert words[1, 0] == 137 | (255 << 8)          # groups 6, 7 past G: zero bytes
+    assert (words[:, 1:] == 0).all()                # rows 1..3 pad to a multiple of 4
+
+
+def test_pack_scales_round_trip_and_padding(orc):
+    """On quantizer output: decoding every byte with numpy ldexp gives back the scales; bytes
+    past the last group and rows past M are zero; a wider ld only adds untouched columns."""
+    M, K = 13, 7 * 128
+    _, s = orc.quant_groups(synth.bf16_bits(synth.activations(M, K, seed=31)),
+                            scale_fmt=orc.SCALE_UE8M0)
+    G = s.shape[1]
+    words = orc.pack_scales_ue8m0(s)
+    assert words.shape == (2, 16)
+    codes = np.stack([(words >> (8 * j)) & 0xFF for j in range(4)], axis=1)  # [w, j, m]
+    codes = codes.transpose(2, 0, 1).reshape(16, 8)[:, :G]                    # [m, g]
+    assert np.array_equal(np.ldexp(1.0, codes[:M].astype(np.int64) - 127), s.astype(np.float64))
+    assert (codes[M:] == 0).all() and ((words[1] >> 24) == 0).all()
+    wide = orc.pack_scales_ue8m0(s, ld=21)
+    assert np.array_equal(wide[:, :16], words) and (wide[:, 16:] == 0).all()
