@@ -91,7 +91,12 @@ def run_gpu(args, wl):
     sfmt = bfq.BFQ_SCALE_UE8M0 if args.scales == "ue8m0" else bfq.BFQ_SCALE_FP32
     channel = args.scales == "channel"       # per-token x per-channel scales
     m_max = max(wl["M"])
-    col = args.scale_layout == "col"
+    packed = args.scale_layout == "packed"     # UE8M0 codes, four groups per 32-bit word
+    col = args.scale_layout == "col" or packed  # both address every M through one ld
+    if packed and args.scales != "ue8m0":
+        raise SystemExit("--scale-layout packed needs --scales ue8m0")
+    if packed and wl["qtype"] != "fp8":
+        raise SystemExit("--scale-layout packed is read by the e4m3fn GEMM only")
     shapes = []
     host = {}
     for (N, K) in wl["shapes"]:
@@ -111,7 +116,10 @@ def run_gpu(args, wl):
                          device=dev)
         G = 1 if channel else K // 128       # activation scales per token
         bs = bfq.channel_block_shape(K) if channel else bfq.BLOCK_SHAPE
-        sa = torch.empty((G, m_max) if col else (m_max, G), dtype=torch.float32, device=dev)
+        if packed:
+            sa = torch.empty(((G + 3) // 4, (m_max + 3) // 4 * 4), dtype=torch.int32, device=dev)
+        else:
+            sa = torch.empty((G, m_max) if col else (m_max, G), dtype=torch.float32, device=dev)
         out = torch.empty((m_max, N), dtype=torch.bfloat16, device=dev)
         plans = []
         for M in wl["M"]:
@@ -133,7 +141,8 @@ def run_gpu(args, wl):
             for (M, tile, ws_bytes, _st) in sh["plans"]:
                 qw, sw = sh["copies"][launch_counter[0] % len(sh["copies"])]
                 launch_counter[0] += 1
-                lay = bfq.BFQ_SCALES_COL_MAJOR if col else bfq.BFQ_SCALES_ROW_MAJOR
+                lay = (bfq.BFQ_SCALES_PACKED_UE8M0 if packed else
+                       bfq.BFQ_SCALES_COL_MAJOR if col else bfq.BFQ_SCALES_ROW_MAJOR)
                 sa_m = sh["sa"] if col else sh["sa"][:M]
                 bfq.bfq_quant_tokens(sh["xd"][:M], sh["qa"][:M], sa_m, layout=lay,
                                      scale_ld=sh["sa"].stride(0), scale_fmt=sfmt,
@@ -181,7 +190,8 @@ def run_gpu(args, wl):
     # single launch bracketed by events would add the event overhead (several us) to
     # kernels of ~30 us.
     stream = torch.cuda.current_stream()
-    lay = bfq.BFQ_SCALES_COL_MAJOR if col else bfq.BFQ_SCALES_ROW_MAJOR
+    lay = (bfq.BFQ_SCALES_PACKED_UE8M0 if packed else
+           bfq.BFQ_SCALES_COL_MAJOR if col else bfq.BFQ_SCALES_ROW_MAJOR)
     R = args.launch_reps
     per = {}
     for sh in shapes:
@@ -348,7 +358,7 @@ def main():
     ap.add_argument("--launch-rounds", type=int, default=3, help="graph replays per kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
-    ap.add_argument("--scale-layout", default="col", choices=["row", "col"],
+    ap.add_argument("--scale-layout", default="col", choices=["row", "col", "packed"],
                     help="activation-scale layout written by the quantizer and read by the GEMM")
     ap.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0", "channel"],
                     help="scale format: 1x128 / 128x128 block scales as fp32 amax/Qmax "
@@ -384,7 +394,8 @@ def main():
                    "block_shape": [1, wl["shapes"][0][1]] if args.scales == "channel" else [128, 128],
                    "out_dtype": "bf16",
                    "weight_copies_rotated": args.rotate,
-                   "activation_scale_layout": args.scale_layout + "_major",
+                   "activation_scale_layout": ("packed_ue8m0_words" if args.scale_layout == "packed"
+                                               else args.scale_layout + "_major"),
                    "weight_layout": "packed16" if args.w_layout == "packed" else "row_major",
                    "scales": args.scales},
         "roofline": res["roofline"],

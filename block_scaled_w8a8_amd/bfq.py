@@ -30,6 +30,7 @@ BFQ_BF16, BFQ_FP16, BFQ_FP32, BFQ_E4M3FN, BFQ_INT8, BFQ_INT32 = range(6)
 # scale layouts (bfq_scale_layout)
 BFQ_SCALES_ROW_MAJOR = 0
 BFQ_SCALES_COL_MAJOR = 1
+BFQ_SCALES_PACKED_UE8M0 = 2   # uint32 words of four E8M0 codes (UE8M0 scales only)
 # weight-code layouts (bfq_weight_layout)
 BFQ_W_ROW_MAJOR = 0
 BFQ_W_PACKED16 = 1
@@ -311,7 +312,8 @@ def bfq_debug_encode(x, codes, q_dtype=BFQ_E4M3FN, stream=None) -> int:
 def quant_tokens(x, q_dtype=BFQ_E4M3FN, layout=BFQ_SCALES_ROW_MAJOR, eps=DEFAULT_EPS,
                  stream=None, scale_fmt=BFQ_SCALE_FP32, per_token=False):
     """Allocate (q, scales) with torch and run bfq_quant_tokens. Returns (q, scales); with
-    per_token the scales are [M, 1] (row-major) or [1, M] (column-major)."""
+    per_token the scales are [M, 1] (row-major) or [1, M] (column-major); with
+    BFQ_SCALES_PACKED_UE8M0 they are int32 words [ceil(K/512), round_up(M, 4)]."""
     import torch
     M, K = x.shape
     group = K if per_token else 128
@@ -319,6 +321,9 @@ def quant_tokens(x, q_dtype=BFQ_E4M3FN, layout=BFQ_SCALES_ROW_MAJOR, eps=DEFAULT
                     device=x.device)
     if layout == BFQ_SCALES_ROW_MAJOR:
         s = torch.empty((M, K // group), dtype=torch.float32, device=x.device)
+    elif layout == BFQ_SCALES_PACKED_UE8M0:     # int32 words [ceil(G/4), round_up(M, 4)]
+        s = torch.empty(((K // 128 + 3) // 4, (M + 3) // 4 * 4), dtype=torch.int32,
+                        device=x.device)
     else:
         s = torch.empty((K // group, M), dtype=torch.float32, device=x.device)
     bfq_quant_tokens(x, q, s, layout=layout, scale_ld=s.stride(0), eps=eps, stream=stream,

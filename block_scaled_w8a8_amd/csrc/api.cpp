@@ -118,8 +118,12 @@ bool same_shape(const bfq_tile& a, const bfq_tile& b) {
 // A kernel serves scale format sfmt if it takes any fp32 block scales (S_FP32) or if the block
 // scales are declared powers of two (a S_UE8M0 kernel applies them inside the MFMA);
 // per-token x per-channel scales (S_CHANNEL) need a kernel built for them.
+// Packed UE8M0 activation-scale words (S_PACKED): the swap-AB instances built for them, or any
+// block-scale kernel of variants 0 and 2 (they read packed words through a runtime flag).
 bool serves(const KernelEntry& k, int sfmt) {
     if (sfmt == S_CHANNEL || k.sfmt == S_CHANNEL) return k.sfmt == sfmt;
+    if (sfmt == S_PACKED) return k.sfmt == S_PACKED || k.tile.variant != 1;
+    if (k.sfmt == S_PACKED) return false;
     return k.sfmt == S_FP32 || sfmt == S_UE8M0;
 }
 
@@ -326,11 +330,18 @@ bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t gr
     if (!sfmt_ok(scale_fmt)) return fail(BFQ_ERR_ARG, "unknown scale format");
     const int64_t G = K / group_size;
     int64_t sm, sg;
+    const bool packed = layout == BFQ_SCALES_PACKED_UE8M0;
     if (layout == BFQ_SCALES_ROW_MAJOR) {
         if (scale_ld < G) return fail(BFQ_ERR_SHAPE, "row-major scale_ld must be >= K/group_size");
         sm = scale_ld; sg = 1;
     } else if (layout == BFQ_SCALES_COL_MAJOR) {
         if (scale_ld < M) return fail(BFQ_ERR_SHAPE, "column-major scale_ld must be >= M");
+        sm = 1; sg = scale_ld;
+    } else if (packed) {
+        if (scale_fmt != BFQ_SCALE_UE8M0 || per_token)
+            return fail(BFQ_ERR_ARG, "packed scale words need UE8M0 scales of 1x128 groups");
+        if (scale_ld < (M + 3) / 4 * 4)
+            return fail(BFQ_ERR_SHAPE, "packed scale_ld must be >= M rounded up to a multiple of 4");
         sm = 1; sg = scale_ld;
     } else {
         return fail(BFQ_ERR_ARG, "unknown scale layout");
@@ -340,7 +351,8 @@ bfq_status bfq_quant_tokens(const void* x_bf16, int64_t M, int64_t K, int32_t gr
                        ? launch_quant_rows(x_bf16, 0, q, scales, M, K, qtype_of(q_dtype), sm, eps,
                                            (int)scale_fmt, (hipStream_t)stream)
                        : launch_quant_tokens(x_bf16, q, scales, M, K, qtype_of(q_dtype), sm, sg,
-                                             eps, (int)scale_fmt, (hipStream_t)stream);
+                                             eps, (int)scale_fmt, packed ? 1 : 0,
+                                             (hipStream_t)stream);
     if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
     return BFQ_OK;
 }
@@ -452,12 +464,20 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     } else if (a_layout == BFQ_SCALES_COL_MAJOR) {
         if (a_scale_ld < M) return fail(BFQ_ERR_SHAPE, "column-major a_scale_ld must be >= M");
         ssm = 1; ssk = channel ? 0 : a_scale_ld;
+    } else if (a_layout == BFQ_SCALES_PACKED_UE8M0) {
+        if (channel || scale_fmt != BFQ_SCALE_UE8M0)
+            return fail(BFQ_ERR_ARG, "packed scale words need block scales in the UE8M0 format");
+        if (in_dtype != BFQ_E4M3FN)
+            return fail(BFQ_ERR_DTYPE, "packed scale words are read by the e4m3fn GEMM only");
+        if (a_scale_ld < M) return fail(BFQ_ERR_SHAPE, "packed a_scale_ld must be >= M");
+        ssm = 1; ssk = a_scale_ld;      // words between word rows (4 K blocks each)
     } else {
         return fail(BFQ_ERR_ARG, "unknown scale layout");
     }
     // the kernels address the activation scales of one tile (at most 256 tokens, all K
     // blocks) with 32-bit byte offsets
-    if ((255 * ssm + (KB - 1) * ssk + 1) * 4 >= (int64_t(1) << 32))
+    const int64_t k_rows = a_layout == BFQ_SCALES_PACKED_UE8M0 ? (KB - 1) / 4 : KB - 1;
+    if ((255 * ssm + k_rows * ssk + 1) * 4 >= (int64_t(1) << 32))
         return fail(BFQ_ERR_SHAPE, "activation scales of 256 tokens must span less than 4 GiB");
     const int qtype = qtype_of(in_dtype), otype = otype_of(out_dtype), wl = (int)w_layout;
     bfq_status status = BFQ_OK;
@@ -467,7 +487,9 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     } else {
         status = select_tile(M, N, K, qtype, wl, sf, &t);
     }
-    const KernelEntry* ke = find_kernel(t, qtype, otype, wl, sf);
+    // a packed-word tile is selected like a UE8M0 one, then served by a kernel that reads words
+    const KernelEntry* ke =
+        find_kernel(t, qtype, otype, wl, a_layout == BFQ_SCALES_PACKED_UE8M0 ? S_PACKED : sf);
     if (!ke)
         return fail(BFQ_ERR_TILE, "tile does not name a compiled kernel for this dtype pair, weight "
                                   "layout and scale format / granularity");
@@ -494,6 +516,7 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     ga.sa = a_scales;
     ga.sa_stride_m = ssm;
     ga.sa_stride_k = ssk;
+    ga.sa_packed = a_layout == BFQ_SCALES_PACKED_UE8M0 ? 1 : 0;
     ga.w = w_q;
     ga.sw = w_scales;
     ga.out = out;

@@ -13,15 +13,19 @@ enum OType { O_BF16 = 0, O_FP16 = 1, O_FP32 = 2 };
 enum WLayout { W_ROW = 0, W_PACKED16 = 1 };   // bfq_weight_layout
 // How a kernel applies scales: per 128-wide K block, any fp32 values (S_FP32) or powers of two
 // only (S_UE8M0, bfq_scale_format); or one scale per token and per output channel after the
-// whole-K product (S_CHANNEL, block_shape {1, K}).
-enum ScaleFmt { S_FP32 = 0, S_UE8M0 = 1, S_CHANNEL = 2 };
+// whole-K product (S_CHANNEL, block_shape {1, K}); or UE8M0 block scales whose activation
+// scales arrive as packed words (S_PACKED, BFQ_SCALES_PACKED_UE8M0). The standard and
+// stream-K kernels read packed words through a runtime flag, so every block-scale kernel of
+// variants 0 and 2 also serves S_PACKED; the swap-AB kernels have S_PACKED instances.
+enum ScaleFmt { S_FP32 = 0, S_UE8M0 = 1, S_CHANNEL = 2, S_PACKED = 3 };
 
 // Largest K of the per-token / per-channel format (the row quantizer keeps a row in registers).
 constexpr int64_t kChannelMaxK = 32768;
 
+// packed: BFQ_SCALES_PACKED_UE8M0 words (s_stride_g = words between word rows).
 hipError_t launch_quant_tokens(const void* x, void* q, float* scales, int64_t M, int64_t K,
                                int qtype, int64_t s_stride_m, int64_t s_stride_g, float eps,
-                               int sfmt, hipStream_t stream);
+                               int sfmt, int packed, hipStream_t stream);
 hipError_t launch_quant_weight_blocks(const float* w, void* q, float* scales, int64_t N,
                                       int64_t K, int qtype, float eps, int sfmt,
                                       hipStream_t stream);
@@ -41,7 +45,8 @@ struct GemmArgs {
     const void* a;          // [M][K] codes
     const float* sa;        // activation scales
     int64_t sa_stride_m;    // element stride between tokens
-    int64_t sa_stride_k;    // element stride between K blocks
+    int64_t sa_stride_k;    // element stride between K blocks (packed: between word rows)
+    int sa_packed;          // 1: activation scales are packed UE8M0 words (4 K blocks each)
     const void* w;          // N*K codes, row-major or packed (the kernel's layout)
     const float* sw;        // [N/128][K/128] (S_CHANNEL: [N])
     void* out;              // [M][N]

@@ -104,6 +104,24 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128_e8(const v8i& a, const v8i& b,
 // E8M0 exponent byte of a positive power-of-two fp32 value (its biased exponent field).
 __device__ __forceinline__ uint32_t e8m0_of(float pow2) { return (__float_as_uint(pow2) >> 23) & 0xFFu; }
 
+// Packed UE8M0 activation scales (BFQ_SCALES_PACKED_UE8M0): byte j of a 32-bit word is the
+// E8M0 code of group 4w + j. Its fp32 value is 2^(code - 127): code 0 is 2^-127 (an fp32
+// subnormal), 255 is NaN.
+__device__ __forceinline__ uint32_t e8m0_byte(uint32_t word, int j) { return (word >> (8 * j)) & 0xFFu; }
+__device__ __forceinline__ float e8m0_value(uint32_t code) {
+    // branch-free: bit 22 is set exactly for code 0 (0x00400000) and code 255 (0x7FC00000)
+    const uint32_t edge = ((code + 1u) >> 8) | (1u - ((code + 255u) >> 8));
+    return __uint_as_float((code << 23) | (edge << 22));
+}
+// The activation scale of K block kb from the 32 bits loaded for it: an fp32 value, or (packed)
+// the word holding the codes of blocks 4*(kb/4) .. +3.
+__device__ __forceinline__ float act_scale(float bits, int packed, int64_t kb) {
+    return packed ? e8m0_value(e8m0_byte(__float_as_uint(bits), (int)(kb & 3))) : bits;
+}
+__device__ __forceinline__ int act_scale_e8(float bits, int packed, int64_t kb) {
+    return packed ? (int)e8m0_byte(__float_as_uint(bits), (int)(kb & 3)) : (int)e8m0_of(bits);
+}
+
 // int8: D(16x16, int32) += A(16x64) * B(64x16); 16 bytes of K per lane.
 __device__ __forceinline__ v4i mfma_i8_16x16x64(const v4i& a, const v4i& b, const v4i& c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);

@@ -117,9 +117,13 @@ __device__ __forceinline__ void std_tile(
     // Scale buffers. Activation-scale DMA slot s = wave*64 + lane holds token row
     // r(s) = wm*TM + sm*MF + frow for s = wm*TM + frow*SM + sm, so each lane later reads its
     // SM scales as one contiguous LDS vector. Rows past M and blocks past N read as zero.
+    // Packed UE8M0 scales: one 32-bit word per token and 4 K blocks, so block kb reads word
+    // row kb / 4 and the byte kb % 4 is picked when the scale is used.
     const int64_t ssm = p.sa_stride_m, ssk = p.sa_stride_k;
+    const int packed = p.sa_packed;
+    const int64_t sa_rows = packed ? (KB - 1) / 4 : KB - 1;
     const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
-        p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + (KB - 1) * ssk + 1) * 4));
+        p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + sa_rows * ssk + 1) * 4));
     uint32_t sa_dma_voff;
     {
         const int sl = wave * 64 + lane;
@@ -151,7 +155,8 @@ __device__ __forceinline__ void std_tile(
         const uint32_t sc = (uint32_t)(SC_BASE + stage * SC_STAGE);
         if constexpr (SCHED != 4) {   // sched 4 has no per-block scales
             if (wave < BM / 64)
-                dma4(rsa, lds, sc + wave * 256, sa_dma_voff, (uint32_t)(kb * ssk * 4));
+                dma4(rsa, lds, sc + wave * 256, sa_dma_voff,
+                     (uint32_t)((packed ? kb >> 2 : kb) * ssk * 4));
             if (wave == 0) dma4(rsw, lds, sc + BM * 4, sw_dma_voff, (uint32_t)(kb * 4));
         }
 #pragma unroll
@@ -429,7 +434,8 @@ __device__ __forceinline__ void std_tile(
             ew = (int)e8m0_of(*reinterpret_cast<const float*>(lds + sc + sw_lds));
 #pragma unroll
             for (int sm = 0; sm < SM; ++sm) {
-                ea[sm] = (int)e8m0_of(*reinterpret_cast<const float*>(lds + sc + sa_lds + sm * 4));
+                ea[sm] = act_scale_e8(*reinterpret_cast<const float*>(lds + sc + sa_lds + sm * 4),
+                                      packed, kb);
                 c[sm] = 0.f;
             }
         } else {
@@ -439,11 +445,15 @@ __device__ __forceinline__ void std_tile(
             for (int sm = 0; sm < SM; ++sm) ea[sm] = 0;
             if constexpr (SM == 4) {
                 const v4f sa4 = *reinterpret_cast<const v4f*>(lds + sc + sa_lds);
-                c[0] = sa4.x * swv; c[1] = sa4.y * swv; c[2] = sa4.z * swv; c[3] = sa4.w * swv;
+                c[0] = act_scale(sa4.x, packed, kb) * swv;
+                c[1] = act_scale(sa4.y, packed, kb) * swv;
+                c[2] = act_scale(sa4.z, packed, kb) * swv;
+                c[3] = act_scale(sa4.w, packed, kb) * swv;
             } else {
 #pragma unroll
                 for (int sm = 0; sm < SM; ++sm)
-                    c[sm] = *reinterpret_cast<const float*>(lds + sc + sa_lds + sm * 4) * swv;
+                    c[sm] = act_scale(*reinterpret_cast<const float*>(lds + sc + sa_lds + sm * 4),
+                                      packed, kb) * swv;
             }
         }
         if (kb + 1 < kb_end) issue_stage(kb + 1, stage ^ 1);

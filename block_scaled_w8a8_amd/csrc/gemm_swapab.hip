@@ -28,7 +28,8 @@
 // CH = 1 (per-token x per-channel scales, [HELION] scope section): no scale loads in the K
 // loop; the MFMA accumulates the wave's K range (int8: exact int32 in the accumulator's
 // bits) and each wave scales its partial tile by token and channel scale before the
-// in-workgroup sum.
+// in-workgroup sum. CH = 2: block scales with the activation scales as packed UE8M0 words
+// (four K blocks per word); a compile-time mode, so the other modes keep their registers.
 #include "bfq_internal.h"
 #include "device_common.h"
 
@@ -124,8 +125,10 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
     const __amdgpu_buffer_rsrc_t ra =
         make_rsrc(static_cast<const uint8_t*>(p.a) + m0 * K, (uint32_t)(rows_a * K));
     const int64_t ssm = p.sa_stride_m, ssk = p.sa_stride_k;
-    const __amdgpu_buffer_rsrc_t rsa =
-        make_rsrc(p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + (KB - 1) * ssk + 1) * 4));
+    constexpr bool CHAN = CH == 1, PK = CH == 2;   // PK: block kb in word row kb / 4
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
+        p.sa + m0 * ssm,
+        (uint32_t)(((rows_a - 1) * ssm + (PK ? (KB - 1) / 4 : KB - 1) * ssk + 1) * 4));
     uint32_t a_voff[SM], sa_voff[SM];
 #pragma unroll
     for (int sm = 0; sm < SM; ++sm) {
@@ -140,6 +143,7 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
     v4i abuf[D][SM][2];
     float sab[D][SM];
     float swb[D];
+    int kbs[D];         // PK: K block % 4 of each ring slot (the byte of its scale word)
 
     // the loads of step i (K block kb_begin + i) into ring slot `slot`
     auto fetch = [&](int slot, int64_t i) {
@@ -147,9 +151,10 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
         const int64_t kb = live ? kb_begin + i : kb_hi;
         const uint32_t ws = live ? (uint32_t)kb * KSTEP : kNoLoad;
         const uint32_t as = live ? (uint32_t)kb * 128u : kNoLoad;
-        const uint32_t ss = live ? (uint32_t)(kb * ssk * 4) : kNoLoad;
-        if constexpr (!CH) {
+        const uint32_t ss = live ? (uint32_t)((PK ? kb >> 2 : kb) * ssk * 4) : kNoLoad;
+        if constexpr (!CHAN) {
             swb[slot] = sw_row[kb];
+            if constexpr (PK) kbs[slot] = (int)(kb & 3);
 #pragma unroll
             for (int sm = 0; sm < SM; ++sm) sab[slot][sm] = buf_f32(rsa, sa_voff[sm], ss);
         }
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
         for (int sn = 0; sn < SN; ++sn) acc[sm][sn] = v4f{0.f, 0.f, 0.f, 0.f};
 
     auto consume = [&](int i) {
-        if constexpr (CH) {
+        if constexpr (CHAN) {
 #pragma unroll
             for (int sm = 0; sm < SM; ++sm)
 #pragma unroll
@@ -183,7 +188,8 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
         }
 #pragma unroll
         for (int sm = 0; sm < SM; ++sm) {
-            const float c = sab[i][sm] * swb[i];
+            const float c = (PK ? e8m0_value(e8m0_byte(__float_as_uint(sab[i][sm]), kbs[i]))
+                                : sab[i][sm]) * swb[i];
 #pragma unroll
             for (int sn = 0; sn < SN; ++sn) {
                 v4f pb;
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
         for (int r = 0; r < D; ++r)
             if (r < rem) consume(r);
     }
-    if constexpr (CH) {
+    if constexpr (CHAN) {
         if (wave_live) channel_scale<QT, SM, SN>(acc, p, m0, n0, frow, fgrp);
     }
 
@@ -347,8 +353,10 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
     // so each lane later reads its SM scales as one contiguous run; lane l fills slots l + 64q
     const bool scale_wave = wn == NWAVES - 1;
     const int64_t ssm = p.sa_stride_m, ssk = p.sa_stride_k;
-    const __amdgpu_buffer_rsrc_t rsa =
-        make_rsrc(p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + (KB - 1) * ssk + 1) * 4));
+    constexpr bool CHAN = CH == 1, PK = CH == 2;   // PK: block kb in word row kb / 4
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
+        p.sa + m0 * ssm,
+        (uint32_t)(((rows_a - 1) * ssm + (PK ? (KB - 1) / 4 : KB - 1) * ssk + 1) * 4));
     uint32_t sa_voff[SCW];
 #pragma unroll
     for (int q = 0; q < SCW; ++q) {
@@ -371,8 +379,8 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
         const int64_t kb = live ? kb_begin + i : kb_hi;
         const uint32_t ws = live ? (uint32_t)kb * KSTEP : kNoLoad;
         const uint32_t as = live ? (uint32_t)kb * 128u : kNoLoad;
-        const uint32_t ss = live ? (uint32_t)(kb * ssk * 4) : kNoLoad;
-        if constexpr (!CH) {
+        const uint32_t ss = live ? (uint32_t)((PK ? kb >> 2 : kb) * ssk * 4) : kNoLoad;
+        if constexpr (!CHAN) {
             swb[slot] = sw_row[kb];
 #pragma unroll
             for (int q = 0; q < SCW; ++q) sab[slot][q] = buf_f32(rsa, sa_voff[q], ss);
@@ -403,14 +411,17 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
             const int j = wn + NWAVES * t;
             if (j < AI) *reinterpret_cast<v4i*>(buf + j * 1024 + lane * 16) = abuf[r][t];
         }
-        if (!CH && scale_wave) {
+        if (!CHAN && scale_wave) {
+            // packed words are decoded here, once per token, so every wave reads fp32 scales
 #pragma unroll
             for (int q = 0; q < SCW; ++q)
                 if (lane + 64 * q < MT)
-                    *reinterpret_cast<float*>(buf + MT * 128 + (lane + 64 * q) * 4) = sab[r][q];
+                    *reinterpret_cast<float*>(buf + MT * 128 + (lane + 64 * q) * 4) =
+                        PK ? e8m0_value(e8m0_byte(__float_as_uint(sab[r][q]), (int)((kb_begin + i) & 3)))
+                           : sab[r][q];
         }
         __syncthreads();
-        if (CH && i < L && wave_live) {
+        if (CHAN && i < L && wave_live) {
 #pragma unroll
             for (int sm = 0; sm < SM; ++sm) {
                 const v4i a0 = *reinterpret_cast<const v4i*>(buf + (2 * sm) * 1024 + lane * 16);
@@ -418,7 +429,7 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
 #pragma unroll
                 for (int sn = 0; sn < SN; ++sn) mfma_accumulate<QT>(acc[sm][sn], wbuf[r][sn], a0, a1);
             }
-        } else if (!CH && i < L && wave_live) {
+        } else if (!CHAN && i < L && wave_live) {
             float c[SM];
             const float* sp = reinterpret_cast<const float*>(buf + MT * 128) + frow * SM;
 #pragma unroll
@@ -465,7 +476,7 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
         }
         i0 += D;
     } while (i0 < Lmax);
-    if constexpr (CH) {
+    if constexpr (CHAN) {
         if (wave_live) channel_scale<QT, SM, SN>(acc, p, m0, n0, frow, fgrp);
     }
 
@@ -526,7 +537,8 @@ hipError_t launch_swapab_lds(const GemmArgs& a, hipStream_t stream) {
 // sched 0 = tokens per wave from L2, sched 1 = tokens shared through LDS.
 #define BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, OT, WL, CH)                                  \
     KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 0, 0, 0}, QT, OT, WL,         \
-                (CH) ? S_CHANNEL : S_FP32, &launch_swapab<MT, NWR, NW, KW, D, QT, OT, WL, CH>}
+                (CH) == 1 ? S_CHANNEL : (CH) == 2 ? S_PACKED : S_FP32,                   \
+                &launch_swapab<MT, NWR, NW, KW, D, QT, OT, WL, CH>}
 #define BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, WL, CH)                                    \
     BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, O_BF16, WL, CH),                                 \
         BFQ_SAB_ENTRY(MT, NWR, NW, KW, D, QT, O_FP16, WL, CH),                             \
@@ -536,10 +548,14 @@ hipError_t launch_swapab_lds(const GemmArgs& a, hipStream_t stream) {
 // per-token x per-channel scales
 #define BFQ_SAB_CH(MT, NWR, NW, KW, D, QT)                                                  \
     BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW, 1), BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16, 1)
+// block scales, activation scales as packed UE8M0 words
+#define BFQ_SAB_PK(MT, NWR, NW, KW, D, QT)                                                  \
+    BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW, 2), BFQ_SAB_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16, 2)
 
 #define BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, OT, WL, CH)                                 \
     KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 1, 0, 0}, QT, OT, WL,         \
-                (CH) ? S_CHANNEL : S_FP32, &launch_swapab_lds<MT, NWR, NW, KW, D, QT, OT, WL, CH>}
+                (CH) == 1 ? S_CHANNEL : (CH) == 2 ? S_PACKED : S_FP32,                   \
+                &launch_swapab_lds<MT, NWR, NW, KW, D, QT, OT, WL, CH>}
 #define BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, WL, CH)                                   \
     BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, O_BF16, WL, CH),                                \
         BFQ_SABL_ENTRY(MT, NWR, NW, KW, D, QT, O_FP16, WL, CH),                            \
@@ -548,6 +564,8 @@ hipError_t launch_swapab_lds(const GemmArgs& a, hipStream_t stream) {
     BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW, 0), BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16, 0)
 #define BFQ_SABL_CH(MT, NWR, NW, KW, D, QT)                                                 \
     BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW, 1), BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16, 1)
+#define BFQ_SABL_PK(MT, NWR, NW, KW, D, QT)                                                 \
+    BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_ROW, 2), BFQ_SABL_ALL_OUT(MT, NWR, NW, KW, D, QT, W_PACKED16, 2)
 
 static const KernelEntry kSwapabKernels[] = {
     BFQ_SABL_BOTH(16, 16, 8, 1, 8, Q_FP8),
@@ -622,6 +640,42 @@ static const KernelEntry kSwapabKernels[] = {
     BFQ_SAB_CH(32, 32, 4, 1, 4, Q_INT8),
     BFQ_SAB_CH(16, 16, 1, 4, 4, Q_INT8),
     BFQ_SAB_CH(32, 16, 1, 4, 4, Q_INT8),
+    // fp8 block scales read as packed UE8M0 activation-scale words
+    BFQ_SABL_PK(16, 16, 8, 1, 8, Q_FP8),
+    BFQ_SABL_PK(16, 16, 4, 2, 8, Q_FP8),
+    BFQ_SABL_PK(32, 16, 8, 1, 4, Q_FP8),
+    BFQ_SABL_PK(32, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_PK(32, 16, 4, 2, 4, Q_FP8),
+    BFQ_SABL_PK(64, 16, 8, 1, 4, Q_FP8),
+    BFQ_SABL_PK(64, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_PK(64, 16, 4, 2, 4, Q_FP8),
+    BFQ_SABL_PK(64, 32, 4, 1, 4, Q_FP8),
+    BFQ_SABL_PK(96, 16, 8, 1, 4, Q_FP8),
+    BFQ_SABL_PK(96, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_PK(128, 16, 8, 1, 4, Q_FP8),
+    BFQ_SABL_PK(128, 16, 6, 1, 4, Q_FP8),
+    BFQ_SABL_PK(32, 16, 6, 1, 8, Q_FP8),
+    BFQ_SABL_PK(32, 16, 6, 2, 4, Q_FP8),
+    BFQ_SABL_PK(64, 16, 6, 1, 8, Q_FP8),
+    BFQ_SABL_PK(64, 16, 6, 2, 4, Q_FP8),
+    BFQ_SABL_PK(96, 16, 6, 2, 4, Q_FP8),
+    BFQ_SABL_PK(128, 16, 6, 2, 4, Q_FP8),
+    BFQ_SAB_PK(16, 32, 4, 1, 4, Q_FP8),
+    BFQ_SAB_PK(16, 16, 4, 1, 8, Q_FP8),
+    BFQ_SAB_PK(16, 16, 8, 1, 8, Q_FP8),
+    BFQ_SAB_PK(16, 32, 8, 1, 4, Q_FP8),
+    BFQ_SAB_PK(16, 64, 4, 1, 2, Q_FP8),
+    BFQ_SAB_PK(16, 32, 4, 1, 8, Q_FP8),
+    BFQ_SAB_PK(32, 32, 4, 1, 4, Q_FP8),
+    BFQ_SAB_PK(64, 32, 4, 1, 2, Q_FP8),
+    BFQ_SAB_PK(16, 16, 1, 4, 4, Q_FP8),
+    BFQ_SAB_PK(16, 16, 1, 4, 8, Q_FP8),
+    BFQ_SAB_PK(16, 16, 2, 2, 8, Q_FP8),
+    BFQ_SAB_PK(16, 16, 1, 8, 4, Q_FP8),
+    BFQ_SAB_PK(16, 32, 1, 4, 4, Q_FP8),
+    BFQ_SAB_PK(32, 16, 1, 4, 4, Q_FP8),
+    BFQ_SAB_PK(64, 16, 1, 4, 2, Q_FP8),
+    BFQ_SAB_PK(32, 32, 1, 4, 4, Q_FP8),
 };
 
 const KernelEntry* swapab_kernels(int* count) {

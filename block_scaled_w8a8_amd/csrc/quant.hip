@@ -79,23 +79,28 @@ __device__ __forceinline__ float pow2_ceil(float s) {
     return (u & 0x007FFFFFu) ? __uint_as_float((u & 0xFF800000u) + 0x00800000u) : s;
 }
 
+// packed != 0 (BFQ_SCALES_PACKED_UE8M0, UE8M0 scales): instead of one fp32 per group, the
+// E8M0 codes of groups 4w .. 4w+3 go to one 32-bit word at words[w * s_stride_g + m]. A
+// wave's pass covers exactly such a quartet (groups g0 + 4u, g0 a multiple of 4 in lane 0),
+// so the word is assembled with two cross-lane ORs. The grid then also covers the padding
+// rows M .. round_up(M, 4) - 1, which read nothing and write zero words.
 template <int QT>
 __global__ __launch_bounds__(64 * kQuantWaves) void quant_tokens_kernel(
     const uint4* __restrict__ x, uint2* __restrict__ q, float* __restrict__ scales,
     int64_t M, int64_t K, int64_t G, int64_t s_stride_m, int64_t s_stride_g, float eps,
-    int ue8m0) {
+    int ue8m0, int packed) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t m = blockIdx.x;
+    const bool row_live = m < M;                        // false only for packed padding rows
     const int part = lane & 15;                         // 16-byte slice within the group
     const int64_t g0 = (int64_t)blockIdx.y * kGroupsPerBlock + wave * kGroupsPerWave + (lane >> 4);
-    (void)M;
 
     uint4 raw[kQuantPasses];
 #pragma unroll
     for (int u = 0; u < kQuantPasses; ++u) {
         int64_t g = g0 + 4 * u;
-        if (g < G) raw[u] = x[(m * K + g * 128) / 8 + part];
+        if (g < G && row_live) raw[u] = x[(m * K + g * 128) / 8 + part];
         else raw[u] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -108,7 +113,25 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quant_tokens_kernel(
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 4, 16));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2, 16));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1, 16));
-        if (g >= G) continue;
+        if (packed) {
+            // every lane of the wave takes part in the ORs; lane 0 stores the quartet's word
+            uint32_t code = 0;
+            if (g < G && row_live) {
+                float sp;
+                if (mx < 0x7F800000u >> 16) {
+                    const float amax = __uint_as_float(mx << 16);
+                    sp = pow2_ceil((amax > eps ? amax : eps) / qmax<QT>());
+                } else {
+                    sp = __uint_as_float(0x7FC00000u);   // NaN or Inf group: E8M0 has no Inf
+                }
+                code = e8m0_of(sp);
+            }
+            uint32_t word = code << (8 * (lane >> 4));
+            word |= (uint32_t)__shfl_xor((int)word, 16, 64);
+            word |= (uint32_t)__shfl_xor((int)word, 32, 64);
+            if (lane == 0 && g < G) scales[(g >> 2) * s_stride_g + m] = __uint_as_float(word);
+        }
+        if (g >= G || !row_live) continue;
 
         float xv[8] = {bf16_lo(raw[u].x), bf16_hi(raw[u].x), bf16_lo(raw[u].y), bf16_hi(raw[u].y),
                        bf16_lo(raw[u].z), bf16_hi(raw[u].z), bf16_lo(raw[u].w), bf16_hi(raw[u].w)};
@@ -125,7 +148,7 @@ __global__ __launch_bounds__(64 * kQuantWaves) void quant_tokens_kernel(
             codes = encode8_special<QT>(xv, nan_group);
         }
         q[(m * K + g * 128) / 8 + part] = codes;
-        if (part == 0) scales[m * s_stride_m + g * s_stride_g] = s;
+        if (part == 0 && !packed) scales[m * s_stride_m + g * s_stride_g] = s;
     }
 }
 
@@ -340,17 +363,20 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __rest
 
 hipError_t launch_quant_tokens(const void* x, void* q, float* scales, int64_t M, int64_t K,
                                int qtype, int64_t s_stride_m, int64_t s_stride_g, float eps,
-                               int sfmt, hipStream_t stream) {
+                               int sfmt, int packed, hipStream_t stream) {
     const int64_t G = K / 128;
-    dim3 grid((unsigned)M, (unsigned)((G + kGroupsPerBlock - 1) / kGroupsPerBlock));
+    const int64_t rows = packed ? (M + 3) / 4 * 4 : M;    // packed: zero words up to 4 | rows
+    dim3 grid((unsigned)rows, (unsigned)((G + kGroupsPerBlock - 1) / kGroupsPerBlock));
     dim3 block(64 * kQuantWaves);
     const int ue = sfmt == S_UE8M0;
     if (qtype == Q_FP8)
         hipLaunchKernelGGL(quant_tokens_kernel<Q_FP8>, grid, block, 0, stream,
-                           (const uint4*)x, (uint2*)q, scales, M, K, G, s_stride_m, s_stride_g, eps, ue);
+                           (const uint4*)x, (uint2*)q, scales, M, K, G, s_stride_m, s_stride_g, eps,
+                           ue, packed);
     else
         hipLaunchKernelGGL(quant_tokens_kernel<Q_INT8>, grid, block, 0, stream,
-                           (const uint4*)x, (uint2*)q, scales, M, K, G, s_stride_m, s_stride_g, eps, ue);
+                           (const uint4*)x, (uint2*)q, scales, M, K, G, s_stride_m, s_stride_g, eps,
+                           ue, packed);
     return hipGetLastError();
 }
 

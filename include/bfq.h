@@ -60,10 +60,19 @@ typedef enum {
 } bfq_dtype;
 
 /* Layout of per-(token, group) activation scales, [BENCH] §4.1 (row-major for the Triton
- * kernel, column-major for CUTLASS/DeepGEMM). */
+ * kernel, column-major for CUTLASS/DeepGEMM; the TMA-aligned column-major form is
+ * column-major with ld = M rounded up to a multiple of 4).
+ * BFQ_SCALES_PACKED_UE8M0 ([PR]: the packed output of the per-token-group kernel,
+ * output_s_packed): UE8M0 scales as E8M0 codes (2^(code - 127); NaN and Inf -> 255, E8M0
+ * has no infinity), four groups per 32-bit word: word (w, m) at ((uint32_t*)s)[w * ld + m],
+ * w < ceil(G/4), byte j (bits 8j..8j+7) = group 4w + j, 0 past the last group. The scale
+ * pointer then addresses uint32 words. The quantizer needs ld >= M rounded up to a multiple
+ * of 4 and writes zero words in rows M .. round_up(M, 4) - 1 (TMA row alignment); the GEMM
+ * needs ld >= M. Only with scale_fmt BFQ_SCALE_UE8M0 and 1x128 groups. */
 typedef enum {
-    BFQ_SCALES_ROW_MAJOR = 0,  /* s[m * ld + g], ld >= K/128 */
-    BFQ_SCALES_COL_MAJOR = 1   /* s[g * ld + m], ld >= M     */
+    BFQ_SCALES_ROW_MAJOR = 0,    /* s[m * ld + g], ld >= K/128 */
+    BFQ_SCALES_COL_MAJOR = 1,    /* s[g * ld + m], ld >= M     */
+    BFQ_SCALES_PACKED_UE8M0 = 2  /* words[w * ld + m], see above */
 } bfq_scale_layout;
 
 /* Layout of the weight codes in memory. The values are the same bytes either way; the packed

@@ -450,3 +450,45 @@ def test_table_channel_key(bfq, tmp_path):
         with pytest.raises(bfq.BfqError):
             bfq.bfq_load_tile_table(str(bad))
     bfq.bfq_load_tile_table(None)
+
+
+# ------------------------------------------- packed UE8M0 activation-scale words (layout 2)
+
+def test_packed_scale_validation_without_launch(bfq):
+    P = bfq.BFQ_SCALES_PACKED_UE8M0
+    q = bfq.lib.bfq_quant_tokens
+    # M = 5 needs ld >= 8 (rows padded to a multiple of 4); UE8M0 and 1x128 groups only
+    assert q(FAKE, 0, 7168, 128, bfq.BFQ_E4M3FN, FAKE, FAKE, P, 0, 1e-10, 1, None) == bfq.BFQ_OK
+    assert q(FAKE, 5, 7168, 128, bfq.BFQ_E4M3FN, FAKE, FAKE, P, 7, 1e-10, 1, None) == bfq.BFQ_ERR_SHAPE
+    assert q(FAKE, 5, 7168, 128, bfq.BFQ_E4M3FN, FAKE, FAKE, P, 8, 1e-10, 0, None) == bfq.BFQ_ERR_ARG
+    assert q(FAKE, 5, 7168, 7168, bfq.BFQ_E4M3FN, FAKE, FAKE, P, 8, 1e-10, 1, None) == bfq.BFQ_ERR_ARG
+    assert _gemm(bfq, M=0, a_layout=P, a_scale_ld=0, scale_fmt=1) >= 0
+    assert _gemm(bfq, M=5, a_layout=P, a_scale_ld=4, scale_fmt=1) == bfq.BFQ_ERR_SHAPE
+    assert _gemm(bfq, M=5, a_layout=P, a_scale_ld=8, scale_fmt=0) == bfq.BFQ_ERR_ARG
+    assert _gemm(bfq, M=5, a_layout=P, a_scale_ld=8, scale_fmt=1,
+                 in_dtype=bfq.BFQ_INT8) == bfq.BFQ_ERR_DTYPE
+    assert _gemm(bfq, M=5, a_layout=P, a_scale_ld=8, scale_fmt=1,
+                 block_shape=_bs(1, 7168)) == bfq.BFQ_ERR_ARG
+
+
+@pytest.mark.parametrize("wl", [0, 1])
+def test_packed_scales_every_ue8m0_tile_has_a_kernel(bfq, tmp_path, wl):
+    """Every fp8 tile usable with UE8M0 scales, and every tile the table or the default rule
+    selects for them, names a kernel that reads packed scale words."""
+    P = bfq.BFQ_SCALES_PACKED_UE8M0
+    sf = bfq.BFQ_SCALE_UE8M0
+    tiles = [bfq.bfq_get_tile_candidate(i, bfq.BFQ_E4M3FN, wl, sf)
+             for i in range(bfq.bfq_num_tile_candidates(bfq.BFQ_E4M3FN, wl, sf))]
+    for M in (1, 8, 31, 64, 128, 256, 2048, 4096):
+        tiles.append(bfq.bfq_select_tile(M, 24576, 7168, w_layout=wl, scale_fmt=sf)[1])
+    p = tmp_path / "empty.json"
+    p.write_text(_table([]))
+    bfq.bfq_load_tile_table(str(p))
+    try:
+        for M in (1, 31, 64, 200, 4096):
+            tiles.append(bfq.bfq_select_tile(M, 24576, 7168, w_layout=wl, scale_fmt=sf)[1])
+    finally:
+        bfq.bfq_load_tile_table(None)
+    for t in tiles:
+        assert _gemm(bfq, M=0, N=24576, a_layout=P, a_scale_ld=0, scale_fmt=sf, w_layout=wl,
+                     tile=ctypes.pointer(t)) >= 0, t.as_dict()

@@ -438,3 +438,73 @@ def test_batch_invariant_mode_rows_bitwise(bfq, orc, qname, layout, sfmt):
             assert np.array_equal(o16, full16[:M]), (M, t.as_dict())
     finally:
         bfq.bfq_set_batch_invariant(False)
+
+
+# ------------------------------------------------ packed UE8M0 activation-scale words
+
+def _to_packed_words(bfq, sa_dev, M, ld=None):
+    """Device words [ceil(G/4), ld] from device UE8M0 scales [M, G] (the oracle's packing)."""
+    import oracle
+    ld = ld or (M + 3) // 4 * 4
+    w = oracle.pack_scales_ue8m0(sa_dev.cpu().numpy(), ld=ld)
+    return torch.from_numpy(w.view(np.int32)).to(DEV)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_packed_scale_words_every_candidate(bfq, orc, layout):
+    """Every fp8 kernel that serves UE8M0 scales, and every split, gives bitwise the same
+    output with the activation scales as packed words as with the same scales column-major
+    in fp32 (the decoded values are identical), and meets the bar against the oracle."""
+    from oracle import metrics
+    M, N, K = 83, 640, 768
+    host = _case(orc, M, N, K, 23, orc.FP8, 1)
+    ref32, _ = orc.block_gemm(*host)
+    dq = _to_dev(*host, layout=layout, sfmt=1)
+    words = _to_packed_words(bfq, dq[1], M, ld=M + 5)
+    sa_col = dq[1].t().contiguous()
+    for t in _candidates(bfq, bfq.BFQ_E4M3FN, layout, 1):
+        for s in (1, 3):
+            if t.variant == 2 and s > 1:
+                continue
+            tile = _with_split(t, s)
+            what = (layout, tile.as_dict())
+            print("packed", what, flush=True)
+            for odt in (torch.float32, torch.bfloat16):
+                col = _run(bfq, dq, odt, tile=tile, a_layout=bfq.BFQ_SCALES_COL_MAJOR,
+                           sa_override=sa_col)
+                pk = _run(bfq, dq, odt, tile=tile, a_layout=bfq.BFQ_SCALES_PACKED_UE8M0,
+                          sa_override=words)
+                assert torch.equal(pk.view(torch.int16) if odt == torch.bfloat16 else pk.view(torch.int32),
+                                   col.view(torch.int16) if odt == torch.bfloat16 else col.view(torch.int32)), (what, odt)
+                if odt == torch.float32:
+                    _check_fp32(metrics, pk.cpu().numpy(), ref32, what)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(m, 24576, 7168) for m in (1, 16, 64, 256, 2048, 4096)]
+                         + [(8, 1536, 1536), (4096, 7168, 18432)])
+def test_packed_scale_words_configs(bfq, orc, M, N, K, layout):
+    """The workloads with the quantizer writing packed words and the GEMM reading them
+    (tile selected by the library), sampled against the oracle."""
+    from oracle import metrics
+    print(f"packed config M={M} N={N} K={K} {layout}", flush=True)
+    x = synth.activations(M, K, seed=0)
+    w = synth.weights(N, K, seed=0)
+    qw, sw = bfq.quant_weight_blocks(w.to(DEV), scale_fmt=bfq.BFQ_SCALE_UE8M0)
+    if layout == "packed":
+        qw = bfq.pack_weights(qw)
+    qa, words = bfq.quant_tokens(x.to(DEV), layout=bfq.BFQ_SCALES_PACKED_UE8M0,
+                                 scale_fmt=bfq.BFQ_SCALE_UE8M0)
+    out = bfq.block_gemm(qa, words, qw, sw, out_dtype=torch.float32,
+                         a_layout=bfq.BFQ_SCALES_PACKED_UE8M0, w_layout=_wl(bfq, layout),
+                         scale_fmt=bfq.BFQ_SCALE_UE8M0)
+    torch.cuda.synchronize()
+    qo, so = orc.quant_groups(synth.bf16_bits(x), scale_fmt=orc.SCALE_UE8M0)
+    qwo, swo = orc.quant_blocks(w.numpy(), scale_fmt=orc.SCALE_UE8M0)
+    assert np.array_equal(qa.cpu().numpy(), qo)
+    rng = np.random.default_rng(M + N)
+    ms = np.concatenate([rng.integers(0, M, 2048), [0, M - 1]])
+    ns = np.concatenate([rng.integers(0, N, 2048), [N - 1, 0]])
+    ref = orc.block_gemm_sampled(qo, so, qwo, swo, ms, ns)
+    r = metrics.gemm_fp32_report(out.cpu().numpy()[ms, ns], ref)
+    assert r["ok"], (M, N, K, layout, r)

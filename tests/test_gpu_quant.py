@@ -182,3 +182,46 @@ def test_quant_tokens_m0_is_noop(bfq):
     q = torch.empty((0, 1536), dtype=torch.uint8, device="cuda:0")
     s = torch.empty((0, 12), dtype=torch.float32, device="cuda:0")
     assert bfq.bfq_quant_tokens(x, q, s, scale_ld=12) == bfq.BFQ_OK
+
+
+# ------------------------------------------------------ packed UE8M0 scale words
+
+@pytest.mark.parametrize("M,K", [(1, 7168), (5, 640), (37, 1536), (128, 7168), (4096, 7168),
+                                 (3, 128), (64, 18432)])
+@pytest.mark.parametrize("qname", ["fp8", "int8"])
+def test_quant_tokens_packed_words_bit_exact(bfq, orc, M, K, qname):
+    """BFQ_SCALES_PACKED_UE8M0: the words equal the oracle's packing of its UE8M0 scales
+    (groups past the last one and rows up to a multiple of 4 zero), the codes equal the
+    unpacked quantizer's, and nothing is written past the padded rows."""
+    print(f"quant packed M={M} K={K} {qname}", flush=True)
+    qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
+    qt = orc.FP8 if qname == "fp8" else orc.INT8
+    x = synth.activations(M, K, seed=M * 3 + K)
+    G, Mp = K // 128, (M + 3) // 4 * 4
+    ld = Mp + 3
+    dev = torch.device("cuda:0")
+    q = torch.empty((M, K), dtype=torch.uint8 if qname == "fp8" else torch.int8, device=dev)
+    words = torch.full(((G + 3) // 4, ld), -1431655766, dtype=torch.int32, device=dev)  # 0xAAAAAAAA
+    bfq.bfq_quant_tokens(x.to(dev), q, words, layout=bfq.BFQ_SCALES_PACKED_UE8M0, scale_ld=ld,
+                         scale_fmt=bfq.BFQ_SCALE_UE8M0)
+    torch.cuda.synchronize()
+    qo, so = orc.quant_groups(synth.bf16_bits(x), qtype=qt, scale_fmt=orc.SCALE_UE8M0)
+    want = orc.pack_scales_ue8m0(so)
+    got = words.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got[:, :Mp], want)
+    assert (got[:, Mp:] == 0xAAAAAAAA).all()
+    assert np.array_equal(q.cpu().numpy().view(np.uint8), qo.view(np.uint8))
+
+
+def test_quant_tokens_packed_special_values(bfq, orc):
+    """NaN and Inf groups get code 255 (E8M0 has no infinity); zero and sub-eps groups the
+    code of eps / 448 rounded up to a power of two."""
+    bits = _special_input()
+    M, K = bits.shape
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    q, words = bfq.quant_tokens(x.to("cuda:0"), layout=bfq.BFQ_SCALES_PACKED_UE8M0,
+                                scale_fmt=bfq.BFQ_SCALE_UE8M0)
+    torch.cuda.synchronize()
+    qo, so = orc.quant_groups(bits, scale_fmt=orc.SCALE_UE8M0)
+    assert np.array_equal(words.cpu().numpy().view(np.uint32), orc.pack_scales_ue8m0(so))
+    assert np.array_equal(q.cpu().numpy(), qo)
