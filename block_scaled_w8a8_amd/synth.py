@@ -7,6 +7,9 @@ activations and weights of DeepSeek-V3 projection shapes, block GEMM benchmark p
   cols = randperm(K)[:round(0.02 K)]            generator seed + 1 (outlier channels)
   X  = randn(M_max, K); X[:, cols] *= 20; bf16  generator seed + 2
 Each smaller M takes the first M rows of the M_max draw, so inputs nest across M.
+MoE routing (the expert dimension of the config page's MoE tables, §5): each token picks
+topk distinct experts of E, uniformly: the topk largest of E uniform draws (generator
+seed + 3); expert weights are E independent weight draws (seed + 1000 + e).
 """
 from __future__ import annotations
 
@@ -42,3 +45,16 @@ def activations(M: int, K: int, seed: int = 0, m_max: int | None = None) -> torc
 def bf16_bits(x: torch.Tensor):
     """The uint16 bit patterns of a bf16 tensor, as a numpy array (for the CPU oracle)."""
     return x.contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def routing(T: int, E: int, topk: int, seed: int = 0, t_max: int | None = None) -> torch.Tensor:
+    """int32 [T, topk]: distinct experts per token, uniform over the E experts (rows 0..T-1
+    of a t_max-row draw, so routing nests across T like the activations)."""
+    t_max = max(T, t_max or T)
+    u = torch.rand((t_max, E), generator=_gen(seed + 3), dtype=torch.float32)
+    return u.topk(topk, dim=1).indices[:T].to(torch.int32).contiguous()
+
+
+def expert_weights(E: int, N: int, K: int, seed: int = 0) -> torch.Tensor:
+    """fp32 [E, N, K]: one weights() draw per expert."""
+    return torch.stack([weights(N, K, seed=seed + 1000 + e) for e in range(E)])

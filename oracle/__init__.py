@@ -75,6 +75,12 @@ def lib() -> ctypes.CDLL:
         L.orc_block_gemm_sampled.argtypes = [p, p, p, p, i64, i64, i64, i32, p, p, i64, p]
         L.orc_pack_scales_ue8m0.restype = None
         L.orc_pack_scales_ue8m0.argtypes = [p, i64, i64, p, i64]
+        L.orc_moe_align.restype = None
+        L.orc_moe_align.argtypes = [p, i64, i64, p, p]
+        L.orc_moe_gemm.restype = None
+        L.orc_moe_gemm.argtypes = [p, p, p, i64, i64, p, p, i64, i64, i64, i32, p]
+        L.orc_moe_gemm_sampled.restype = None
+        L.orc_moe_gemm_sampled.argtypes = [p, p, p, i64, p, p, i64, i64, i32, p, p, i64, p]
         L.orc_channel_gemm.restype = None
         L.orc_channel_gemm.argtypes = [p, p, p, p, i64, i64, i64, i32, p, p]
         L.orc_channel_gemm_sampled.restype = None
@@ -269,6 +275,51 @@ def channel_gemm_sampled(qa, sa, qw, sw, ms, ns, qtype: int = FP8):
     out = np.empty(ms.shape, dtype=np.float32)
     lib().orc_channel_gemm_sampled(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, qtype,
                                    _ptr(ms), _ptr(ns), ms.size, _ptr(out))
+    return out
+
+
+def moe_align(topk_ids, E: int):
+    """topk_ids int [T, topk] -> (offsets int32 [E+1], sorted int32 [T*topk]): pair ids
+    q = t*topk + j grouped by expert, ascending within an expert."""
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32).reshape(-1)
+    assert ids.size == 0 or (ids.min() >= 0 and ids.max() < E)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    srt = np.empty(ids.size, dtype=np.int32)
+    lib().orc_moe_align(_ptr(ids), ids.size, E, _ptr(offsets), _ptr(srt))
+    return offsets, srt
+
+
+def _moe_args(qa, sa, topk_ids, qw, sw, qtype):
+    qa = np.ascontiguousarray(qa, dtype=_code_dtype(qtype))
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    qw = np.ascontiguousarray(qw, dtype=_code_dtype(qtype))
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    T, K = qa.shape
+    E, N, K2 = qw.shape
+    assert K == K2 and ids.shape[0] == T and sa.shape == (T, K // 128)
+    assert sw.shape == (E, N // 128, K // 128) and (ids.size == 0 or ids.max() < E)
+    return qa, sa, ids, qw, sw, T, ids.shape[1], E, N, K
+
+
+def moe_gemm(qa, sa, topk_ids, qw, sw, qtype: int = FP8):
+    """MoE grouped block GEMM: qa [T, K], sa [T, K/128], topk_ids [T, topk], qw [E, N, K],
+    sw [E, N/128, K/128] -> c32 [T*topk, N] in pair order."""
+    qa, sa, ids, qw, sw, T, topk, E, N, K = _moe_args(qa, sa, topk_ids, qw, sw, qtype)
+    c32 = np.empty((T * topk, N), dtype=np.float32)
+    lib().orc_moe_gemm(_ptr(qa), _ptr(sa), _ptr(ids), T, topk, _ptr(qw), _ptr(sw), E, N, K,
+                       qtype, _ptr(c32))
+    return c32
+
+
+def moe_gemm_sampled(qa, sa, topk_ids, qw, sw, qs, ns, qtype: int = FP8):
+    qa, sa, ids, qw, sw, T, topk, E, N, K = _moe_args(qa, sa, topk_ids, qw, sw, qtype)
+    qs = np.ascontiguousarray(qs, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    assert (qs >= 0).all() and (qs < T * topk).all() and (ns >= 0).all() and (ns < N).all()
+    out = np.empty(qs.shape, dtype=np.float32)
+    lib().orc_moe_gemm_sampled(_ptr(qa), _ptr(sa), _ptr(ids), topk, _ptr(qw), _ptr(sw), N, K,
+                               qtype, _ptr(qs), _ptr(ns), qs.size, _ptr(out))
     return out
 
 

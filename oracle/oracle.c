@@ -325,6 +325,58 @@ void orc_channel_gemm_sampled(const void* qa, const float* sa, const void* qw, c
         c32[i] = channel_element(qa, sa, qw, sw, ms[i], ns[i], K, qtype);
 }
 
+/* ------------------------------------------------------ MoE grouped GEMM ---- */
+
+/* [CONFIG] §5: the MoE kernels reuse the per-shape, per-batch-size config scheme with an
+ * expert count E in the key. Reading of the grouped GEMM the tables serve: token t routed
+ * to experts topk_ids[t][0..topk-1] forms pairs q = t*topk + j; the pairs are grouped by
+ * expert (a stable counting sort: ascending pair id within an expert), and each pair's
+ * output row is the block-scaled GEMM of its token's quantized row with its expert's
+ * weights, written at row q (pair order). */
+void orc_moe_align(const int32_t* topk_ids, int64_t pairs, int64_t E, int32_t* offsets,
+                   int32_t* sorted) {
+    for (int64_t e = 0; e <= E; ++e) offsets[e] = 0;
+    for (int64_t q = 0; q < pairs; ++q) offsets[topk_ids[q] + 1] += 1;   /* counts */
+    for (int64_t e = 0; e < E; ++e) offsets[e + 1] += offsets[e];         /* prefix */
+    int64_t* cursor = (int64_t*)malloc((size_t)E * sizeof(int64_t));
+    for (int64_t e = 0; e < E; ++e) cursor[e] = offsets[e];
+    for (int64_t q = 0; q < pairs; ++q) sorted[cursor[topk_ids[q]]++] = (int32_t)q;
+    free(cursor);
+}
+
+/* out[q][n] for pair q = t*topk + j routed to expert e: the block GEMM element of token row t
+ * of qa against row n of expert e's weights (qw + e*N*K, sw + e*(N/128)*(K/128)). */
+static float moe_element(const void* qa, const float* sa, const void* qw, const float* sw,
+                         const int32_t* topk_ids, int64_t topk, int64_t q, int64_t n, int64_t N,
+                         int64_t K, int qtype) {
+    int64_t t = q / topk, e = topk_ids[q];
+    int64_t KB = K / 128;
+    const uint8_t* we = (const uint8_t*)qw + e * N * K;
+    const float* swe = sw + e * (N / 128) * KB;
+    return gemm_element(qa, sa, we, swe, t, n, K, qtype);
+}
+
+void orc_moe_gemm(const void* qa, const float* sa, const int32_t* topk_ids, int64_t T,
+                  int64_t topk, const void* qw, const float* sw, int64_t E, int64_t N,
+                  int64_t K, int qtype, float* c32) {
+    (void)E;
+    init_decode_table();
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t q = 0; q < T * topk; ++q)
+        for (int64_t n = 0; n < N; ++n)
+            c32[q * N + n] = moe_element(qa, sa, qw, sw, topk_ids, topk, q, n, N, K, qtype);
+}
+
+void orc_moe_gemm_sampled(const void* qa, const float* sa, const int32_t* topk_ids,
+                          int64_t topk, const void* qw, const float* sw, int64_t N, int64_t K,
+                          int qtype, const int64_t* qs, const int64_t* ns, int64_t count,
+                          float* c32) {
+    init_decode_table();
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < count; ++i)
+        c32[i] = moe_element(qa, sa, qw, sw, topk_ids, topk, qs[i], ns[i], N, K, qtype);
+}
+
 void orc_block_partials_i32(const int8_t* qa, const int8_t* qw, int64_t M, int64_t N,
                             int64_t K, int32_t* out) {
     int64_t KB = K / 128;

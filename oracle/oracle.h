@@ -84,6 +84,24 @@ void orc_channel_gemm_sampled(const void* qa, const float* sa, const void* qw, c
                               int64_t M, int64_t N, int64_t K, int qtype,
                               const int64_t* ms, const int64_t* ns, int64_t count, float* c32);
 
+/* MoE routing: pairs q = t*topk + j with expert topk_ids[q] (flat [T*topk]) grouped by
+ * expert, ascending q within an expert (stable counting sort). offsets[E+1] = prefix sums
+ * of the per-expert counts; sorted[pairs] = pair ids in expert order. */
+void orc_moe_align(const int32_t* topk_ids, int64_t pairs, int64_t E, int32_t* offsets,
+                   int32_t* sorted);
+
+/* MoE grouped block GEMM: out[q][n] (pair order, [T*topk][N]) = the block-scaled GEMM
+ * element of token row q / topk of qa ([T][K], scales sa [T][K/128]) against row n of expert
+ * topk_ids[q]'s weights (qw [E][N][K], sw [E][N/128][K/128]); same arithmetic as
+ * orc_block_gemm. */
+void orc_moe_gemm(const void* qa, const float* sa, const int32_t* topk_ids, int64_t T,
+                  int64_t topk, const void* qw, const float* sw, int64_t E, int64_t N,
+                  int64_t K, int qtype, float* c32);
+void orc_moe_gemm_sampled(const void* qa, const float* sa, const int32_t* topk_ids,
+                          int64_t topk, const void* qw, const float* sw, int64_t N, int64_t K,
+                          int qtype, const int64_t* qs, const int64_t* ns, int64_t count,
+                          float* c32);
+
 /* int8 only: exact per-128-K-block integer partials, layout [K/128][M][N]. */
 void orc_block_partials_i32(const int8_t* qa, const int8_t* qw, int64_t M, int64_t N,
                             int64_t K, int32_t* out);

@@ -649,3 +649,80 @@ def test_pack_scales_round_trip_and_padding(orc):
     assert (codes[M:] == 0).all() and ((words[1] >> 24) == 0).all()
     wide = orc.pack_scales_ue8m0(s, ld=21)
     assert np.array_equal(wide[:, :16], words) and (wide[:, 16:] == 0).all()
+
+
+# ------------------------------------------------------------ MoE grouped GEMM
+# Config page §5: the MoE kernels' tables add an expert count E. Pairs q = t*topk + j are
+# grouped by expert; each pair's output row is its token's block GEMM with its expert.
+
+def test_moe_align_is_a_stable_sort_by_expert(orc):
+    """Against numpy: a stable argsort of the flat expert ids and a bincount prefix."""
+    for T, E, topk, seed in [(1, 8, 2, 0), (37, 16, 4, 1), (300, 256, 8, 2), (5, 3, 1, 3)]:
+        ids = synth.routing(T, E, topk, seed=seed).numpy()
+        off, srt = orc.moe_align(ids, E)
+        flat = ids.reshape(-1)
+        assert np.array_equal(srt, np.argsort(flat, kind="stable").astype(np.int32))
+        cnt = np.bincount(flat, minlength=E)
+        assert np.array_equal(off, np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32))
+        # each token's experts are distinct
+        assert all(len(set(r)) == topk for r in ids.tolist())
+    off, srt = orc.moe_align(np.zeros((0, 4), np.int32), 6)
+    assert (off == 0).all() and srt.size == 0
+
+
+def _moe_case(orc, T, E, topk, N, K, seed, qtype=0):
+    x = synth.activations(T, K, seed=seed)
+    ids = synth.routing(T, E, topk, seed=seed).numpy()
+    w = synth.expert_weights(E, N, K, seed=seed).numpy()
+    qa, sa = orc.quant_groups(synth.bf16_bits(x), qtype=qtype)
+    qs = [orc.quant_blocks(w[e], qtype=qtype) for e in range(E)]
+    return qa, sa, ids, np.stack([q for q, _ in qs]), np.stack([s for _, s in qs])
+
+
+def test_moe_gemm_vs_fp64_per_pair(orc):
+    """Every pair row against an fp64 dequantize-then-matmul of its token with its expert
+    (torch's e4m3fn decode, numpy fp64): within 1e-5 rms."""
+    qa, sa, ids, qw, sw = _moe_case(orc, 9, 6, 3, 256, 384, 41)
+    c = orc.moe_gemm(qa, sa, ids, qw, sw)
+    a = _dequant_fp8(qa) * np.repeat(sa.astype(np.float64), 128, axis=1)
+    for q in range(9 * 3):
+        t, e = q // 3, ids[q // 3, q % 3]
+        b = _dequant_fp8(qw[e]) * np.repeat(np.repeat(sw[e].astype(np.float64), 128, 0), 128, 1)
+        d = a[t] @ b.T
+        assert np.abs(c[q] - d).max() <= 1e-5 * np.sqrt((d * d).mean()), q
+
+
+def test_moe_gemm_exact_integer_case(orc):
+    """Integer codes |v| <= 8 and power-of-two scales that differ per expert: bit-exact with
+    numpy int64 matmuls of each token with its expert, times the scales."""
+    rng = np.random.default_rng(42)
+    T, E, topk, N, K = 7, 5, 2, 128, 256
+    enc = {int(v): torch.tensor([float(v)]).to(torch.float8_e4m3fn).view(torch.uint8).item()
+           for v in range(-8, 9)}
+    ia = rng.integers(-8, 9, size=(T, K))
+    iw = rng.integers(-8, 9, size=(E, N, K))
+    qa = np.vectorize(enc.get)(ia).astype(np.uint8)
+    qw = np.vectorize(enc.get)(iw).astype(np.uint8)
+    sa = np.full((T, K // 128), 2.0 ** -3, dtype=np.float32)
+    sw = np.stack([np.full((N // 128, K // 128), 2.0 ** -(e + 1), dtype=np.float32) for e in range(E)])
+    ids = synth.routing(T, E, topk, seed=42).numpy()
+    c = orc.moe_gemm(qa, sa, ids, qw, sw)
+    for q in range(T * topk):
+        t, e = q // topk, ids[q // topk, q % topk]
+        exact = (iw[e].astype(np.int64) @ ia[t].astype(np.int64)).astype(np.float64)
+        assert np.array_equal(c[q].astype(np.float64), exact * 2.0 ** -3 * 2.0 ** -(e + 1)), q
+
+
+def test_moe_gemm_single_expert_is_the_block_gemm(orc):
+    """E = 1, topk = 1: the grouped GEMM is the plain block GEMM, bit for bit; sampled
+    outputs equal the full ones."""
+    qa, sa, ids, qw, sw = _moe_case(orc, 11, 1, 1, 256, 512, 43)
+    c = orc.moe_gemm(qa, sa, ids, qw, sw)
+    c_dense, _ = orc.block_gemm(qa, sa, qw[0], sw[0])
+    assert np.array_equal(c, c_dense)
+    qa, sa, ids, qw, sw = _moe_case(orc, 9, 4, 2, 128, 256, 44, qtype=orc.INT8)
+    c = orc.moe_gemm(qa, sa, ids, qw, sw, qtype=orc.INT8)
+    rng = np.random.default_rng(2)
+    qs, ns = rng.integers(0, 18, 60), rng.integers(0, 128, 60)
+    assert np.array_equal(orc.moe_gemm_sampled(qa, sa, ids, qw, sw, qs, ns, qtype=orc.INT8),
+                          c[qs, ns])
