@@ -55,6 +55,9 @@ EXPORTED = (
     "bfq_num_tile_candidates", "bfq_get_tile_candidate", "bfq_status_string",
     "bfq_last_error", "bfq_debug_block_partials_i32", "bfq_debug_encode",
     "bfq_set_batch_invariant", "bfq_get_batch_invariant",
+    "bfq_moe_align_workspace_bytes", "bfq_moe_align", "bfq_moe_select_tile",
+    "bfq_moe_gemm_workspace_bytes", "bfq_moe_block_gemm", "bfq_moe_num_tile_candidates",
+    "bfq_moe_get_tile_candidate",
 )
 
 
@@ -118,6 +121,14 @@ def _load():
         "bfq_debug_block_partials_i32": (i32, [p, p, p, i64, i64, i64, p]),
         "bfq_debug_encode": (i32, [p, i64, i32, p, p]),
         "bfq_set_batch_invariant": (None, [i32]),
+        "bfq_moe_align_workspace_bytes": (sz, [i64, i32, i32]),
+        "bfq_moe_align": (i32, [p, i64, i32, i32, p, p, p, sz, p]),
+        "bfq_moe_select_tile": (i32, [i64, i32, i32, i64, i64, bs, i32, i32, i32, i32, tp]),
+        "bfq_moe_gemm_workspace_bytes": (sz, [i64, i32, i64, tp]),
+        "bfq_moe_block_gemm": (i32, [p, p, i32, i64, p, p, i32, p, p, i32, i32, p, i64, i64, i64,
+                                     i32, bs, i32, i32, tp, p, sz, p]),
+        "bfq_moe_num_tile_candidates": (i32, [i32, i32]),
+        "bfq_moe_get_tile_candidate": (i32, [i32, i32, i32, tp]),
         "bfq_get_batch_invariant": (i32, []),
     }
     for name, (res, args) in sig.items():
@@ -278,6 +289,62 @@ def bfq_get_tile_candidate(index, in_dtype=BFQ_E4M3FN, w_layout=BFQ_W_ROW_MAJOR,
     return t
 
 
+def bfq_moe_align(topk_ids, E, expert_offsets, sorted_pairs, workspace=None, stream=None) -> int:
+    """topk_ids int32 [T, topk]; expert_offsets int32 [E+1]; sorted_pairs int32 [T*topk]."""
+    T, topk = topk_ids.shape
+    need = int(lib.bfq_moe_align_workspace_bytes(T, topk, E))
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.bfq_moe_align(_ptr(topk_ids), T, topk, E, _ptr(expert_offsets), _ptr(sorted_pairs),
+                           _ptr(workspace), wb if workspace is not None else need, _stream(stream))
+    return _check(st, "bfq_moe_align")
+
+
+def bfq_moe_select_tile(T, topk, E, N, K, out_dtype=BFQ_BF16, w_layout=BFQ_W_ROW_MAJOR,
+                        scale_fmt=BFQ_SCALE_FP32):
+    """Returns (status, bfq_tile)."""
+    t = bfq_tile()
+    st = lib.bfq_moe_select_tile(T, topk, E, N, K, _block_shape(BLOCK_SHAPE), BFQ_E4M3FN,
+                                 out_dtype, w_layout, scale_fmt, ctypes.byref(t))
+    if st < 0:
+        raise BfqError(st, "bfq_moe_select_tile")
+    return st, t
+
+
+def bfq_moe_gemm_workspace_bytes(T, topk, N, tile) -> int:
+    return int(lib.bfq_moe_gemm_workspace_bytes(T, topk, N, ctypes.byref(tile)))
+
+
+def bfq_moe_block_gemm(a_q, a_scales, sorted_pairs, expert_offsets, topk, w_q, w_scales, out,
+                       a_layout=BFQ_SCALES_ROW_MAJOR, a_scale_ld=None, tile=None, workspace=None,
+                       workspace_bytes=None, stream=None, w_layout=BFQ_W_ROW_MAJOR,
+                       scale_fmt=BFQ_SCALE_FP32) -> int:
+    """a_q [T, K]; w_q [E, N, K] (row-major, or each expert packed); w_scales
+    [E, N/128, K/128]; out [T*topk, N] in pair order."""
+    T, K = a_q.shape
+    E, N = w_q.shape[0], w_q.shape[1]
+    if a_scale_ld is None:
+        a_scale_ld = a_scales.stride(0)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.bfq_moe_block_gemm(_ptr(a_q), _ptr(a_scales), a_layout, a_scale_ld, _ptr(sorted_pairs),
+                                _ptr(expert_offsets), topk, _ptr(w_q), _ptr(w_scales), w_layout,
+                                scale_fmt, _ptr(out), T, N, K, E, _block_shape(BLOCK_SHAPE),
+                                BFQ_E4M3FN, _odtype(out), ctypes.byref(tile) if tile else None,
+                                _ptr(workspace), workspace_bytes, _stream(stream))
+    return _check(st, "bfq_moe_block_gemm", warn_key=("moe", E, N, K))
+
+
+def bfq_moe_num_tile_candidates(w_layout=BFQ_W_ROW_MAJOR, scale_fmt=BFQ_SCALE_FP32) -> int:
+    return int(lib.bfq_moe_num_tile_candidates(w_layout, scale_fmt))
+
+
+def bfq_moe_get_tile_candidate(index, w_layout=BFQ_W_ROW_MAJOR, scale_fmt=BFQ_SCALE_FP32) -> bfq_tile:
+    t = bfq_tile()
+    _check(lib.bfq_moe_get_tile_candidate(w_layout, scale_fmt, index, ctypes.byref(t)),
+           "bfq_moe_get_tile_candidate")
+    return t
+
+
 def bfq_status_string(s: int) -> str:
     return status_string(s)
 
@@ -349,12 +416,48 @@ def quant_weight_blocks(w, q_dtype=BFQ_E4M3FN, eps=DEFAULT_EPS, stream=None,
     return q, s
 
 
+def moe_align(topk_ids, E, stream=None):
+    """Allocate and run bfq_moe_align. Returns (expert_offsets int32 [E+1], sorted_pairs
+    int32 [T*topk])."""
+    import torch
+    T, topk = topk_ids.shape
+    dev = topk_ids.device
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    srt = torch.empty(T * topk, dtype=torch.int32, device=dev)
+    need = int(lib.bfq_moe_align_workspace_bytes(T, topk, E))
+    ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    bfq_moe_align(topk_ids, E, off, srt, workspace=ws, stream=stream)
+    return off, srt
+
+
+def moe_block_gemm(a_q, a_scales, sorted_pairs, expert_offsets, topk, w_q, w_scales,
+                   out_dtype=None, a_layout=BFQ_SCALES_ROW_MAJOR, tile=None, stream=None,
+                   w_layout=BFQ_W_ROW_MAJOR, scale_fmt=BFQ_SCALE_FP32):
+    """Allocate out [T*topk, N] (and split-K workspace) with torch and run bfq_moe_block_gemm."""
+    import torch
+    out_dtype = out_dtype or torch.bfloat16
+    T, K = a_q.shape
+    E, N = w_q.shape[0], w_q.shape[1]
+    out = torch.empty((T * topk, N), dtype=out_dtype, device=a_q.device)
+    if tile is None:
+        st, tile = bfq_moe_select_tile(T, topk, E, N, K, _odtype(out), w_layout, scale_fmt)
+        _check(st, "bfq_moe_select_tile", warn_key=("moe", E, N, K))
+    ws_bytes = bfq_moe_gemm_workspace_bytes(T, topk, N, tile)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=a_q.device) if ws_bytes else None
+    bfq_moe_block_gemm(a_q, a_scales, sorted_pairs, expert_offsets, topk, w_q, w_scales, out,
+                       a_layout=a_layout, tile=tile, workspace=ws, workspace_bytes=ws_bytes,
+                       stream=stream, w_layout=w_layout, scale_fmt=scale_fmt)
+    return out
+
+
 def pack_weights(w_q, stream=None):
-    """Allocate a packed copy of row-major weight codes (same dtype and [N, K] shape) with
-    torch and run bfq_pack_weights."""
+    """Allocate a packed copy of row-major weight codes (same dtype and shape) with torch and
+    run bfq_pack_weights. [E, N, K] expert weights pack as one [E*N, K] matrix, which is each
+    expert packed in turn (16-row fragments never straddle experts, N being a multiple of
+    128)."""
     import torch
     p = torch.empty_like(w_q, memory_format=torch.contiguous_format)
-    bfq_pack_weights(w_q, p, stream=stream)
+    bfq_pack_weights(w_q.reshape(-1, w_q.shape[-1]), p.view(-1, w_q.shape[-1]), stream=stream)
     return p
 
 

@@ -61,13 +61,15 @@ bool read_file(const std::string& path, std::string& text) {
     return true;
 }
 
-const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype, int wlayout, int sfmt);
+const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype, int wlayout, int sfmt,
+                               int moe = 0);
 
 // Every table tile must name a compiled kernel; otherwise the table is rejected.
 bool validate_table(const TileTable& t, std::string& err) {
     for (auto& e : t.entries)
         for (auto& b : e.second) {
-            if (!find_kernel(b.second, e.first.qtype, O_BF16, e.first.wlayout, e.first.sfmt)) {
+            if (!find_kernel(b.second, e.first.qtype, O_BF16, e.first.wlayout, e.first.sfmt,
+                             e.first.E > 0 ? 1 : 0)) {
                 err = "table entry N=" + std::to_string(e.first.N) + " K=" +
                       std::to_string(e.first.K) + " M=" + std::to_string(b.first) +
                       " names a tile that is not compiled";
@@ -127,16 +129,20 @@ bool serves(const KernelEntry& k, int sfmt) {
     return k.sfmt == S_FP32 || sfmt == S_UE8M0;
 }
 
-const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype, int wlayout, int sfmt) {
+// moe = 1: the grouped (MoE) kernels (variants 0 and 1)
+const KernelEntry* find_kernel(const bfq_tile& t, int qtype, int otype, int wlayout, int sfmt,
+                               int moe) {
     if (t.bk != 0 && t.bk != 128) return nullptr;
     int n = 0;
-    const KernelEntry* list = t.variant == 0   ? std_kernels(&n)
-                              : t.variant == 1 ? swapab_kernels(&n)
-                              : t.variant == 2 ? streamk_kernels(&n)
-                                               : nullptr;
+    const KernelEntry* list = nullptr;
+    if (moe) list = t.variant == 0 ? moe_std_kernels(&n) : t.variant == 1 ? moe_swapab_kernels(&n) : nullptr;
+    else list = t.variant == 0   ? std_kernels(&n)
+                : t.variant == 1 ? swapab_kernels(&n)
+                : t.variant == 2 ? streamk_kernels(&n)
+                                 : nullptr;
     for (int i = 0; list && i < n; ++i)
         if (list[i].qtype == qtype && list[i].otype == otype && list[i].wlayout == wlayout &&
-            serves(list[i], sfmt) && same_shape(list[i].tile, t))
+            list[i].moe == moe && serves(list[i], sfmt) && same_shape(list[i].tile, t))
             return &list[i];
     return nullptr;
 }
@@ -226,6 +232,32 @@ bool batch_invariant() {
     return g_batch_invariant == 1;
 }
 
+// Grouped (MoE) default: the tile follows the average rows per active expert, r = pairs /
+// min(E, pairs) (a stand-in for the per-expert M): streaming swap-AB up to 128 rows (each
+// expert's weights are read once; tokens per wave up to 16, shared through LDS above), then
+// standard tiles. No split-K: E experts x N strips already fill the device.
+bfq_tile moe_default_tile(int64_t T, int64_t topk, int64_t E, int sfmt) {
+    const int64_t pairs = T * topk, active = E < pairs ? E : pairs;
+    const int64_t r = active > 0 ? (pairs + active - 1) / active : 1;
+    bfq_tile t{};
+    t.bk = 128;
+    t.split_k = 1;
+    t.group_m = 1;
+    if (r <= 16) {
+        t.variant = 1; t.bm = 16; t.bn = 128; t.waves_m = 1; t.waves_n = 4; t.stages = 4; t.sched = 0;
+    } else if (r <= 128) {
+        t.variant = 1; t.bm = r <= 32 ? 32 : r <= 64 ? 64 : 128; t.bn = 128; t.waves_m = 1;
+        t.waves_n = 8; t.stages = 4; t.sched = 1;
+    } else {
+        t.variant = 0; t.stages = 2;
+        t.sched = (sfmt == S_UE8M0) ? 3 : 0;
+        if (r <= 256) { t.bm = 128; t.bn = 128; t.waves_m = 2; t.waves_n = 2; }
+        else if (t.sched == 3) { t.bm = 256; t.bn = 256; t.waves_m = 4; t.waves_n = 2; }
+        else { t.bm = 128; t.bn = 256; t.waves_m = 2; t.waves_n = 2; }
+    }
+    return t;
+}
+
 int qtype_of(bfq_dtype d) { return d == BFQ_E4M3FN ? Q_FP8 : Q_INT8; }
 
 int otype_of(bfq_dtype d) { return d == BFQ_BF16 ? O_BF16 : d == BFQ_FP16 ? O_FP16 : O_FP32; }
@@ -253,6 +285,34 @@ bfq_status select_tile(int64_t M, int64_t N, int64_t K, int qtype, int wlayout, 
     return BFQ_WARN_DEFAULT_TILE;
 }
 
+// Grouped (MoE) selection: the (E, N, K, dtype, layout, scales) entry, nearest bucket to the
+// token count T; batch-invariant mode as for dense tiles, keyed by the average rows per
+// active expert (every grouped tile it names is compiled); else the default rule + warning.
+bfq_status moe_select_tile(int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K, int qtype,
+                           int wlayout, int sfmt, bfq_tile* out) {
+    const int64_t pairs = T * topk, active = E < pairs ? E : pairs;
+    if (batch_invariant()) {
+        *out = invariant_tile(active > 0 ? (pairs + active - 1) / active : 1, wlayout, sfmt);
+        out->group_m = 1;
+        if (out->variant == 0 && out->bm == 256) {   // largest grouped FMA tile
+            out->bm = 128; out->waves_m = 2;
+        }
+        return BFQ_OK;
+    }
+    ensure_table();
+    {
+        std::lock_guard<std::mutex> lk(g_table_mu);
+        auto it = g_table.entries.find(TableKey{N, K, qtype, wlayout, sfmt, E});
+        if (it != g_table.entries.end()) {
+            *out = it->second.at(nearest_bucket(it->second, T));
+            out->bk = 128;
+            return BFQ_OK;
+        }
+    }
+    *out = moe_default_tile(T, topk, E, sfmt);
+    return BFQ_WARN_DEFAULT_TILE;
+}
+
 // Scale granularity from block_shape ([BENCH] §4.2 block_size; [HELION] scope section):
 // {128, 128} = 1x128 token groups and 128x128 weight blocks; {1, K} = one scale per token and
 // one per output channel (K <= kChannelMaxK). Sets *sfmt to S_CHANNEL for the latter.
@@ -265,6 +325,8 @@ bool scale_mode(const int32_t* bs, int64_t K, int* sfmt) {
     }
     return false;
 }
+
+bool block_shape_ok(const int32_t* bs) { return bs && bs[0] == 128 && bs[1] == 128; }
 
 const char* kBlockShapeMsg =
     "block_shape must be {128, 128} or {1, K} (per-channel, K a multiple of 128 up to 32768)";
@@ -587,6 +649,180 @@ bfq_status bfq_get_tile_candidate(const int32_t block_shape[2], bfq_dtype in_dty
         for (int i = 0; i < ns[l]; ++i) {
             if (lists[l][i].qtype != q || lists[l][i].otype != O_BF16 || lists[l][i].wlayout != wl ||
                 !serves(lists[l][i], sf))
+                continue;
+            if (count == index) { *tile_out = lists[l][i].tile; return BFQ_OK; }
+            ++count;
+        }
+    return fail(BFQ_ERR_ARG, "candidate index out of range");
+}
+
+// ----------------------------------------------------------- MoE grouped GEMM ----
+
+size_t bfq_moe_align_workspace_bytes(int64_t T, int32_t topk, int32_t E) {
+    if (T <= 0 || topk <= 0 || E <= 0) return 0;
+    return moe_align_workspace_bytes(T * topk, E);
+}
+
+bfq_status bfq_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                         int32_t* expert_offsets, int32_t* sorted_pairs, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (!expert_offsets || (T > 0 && (!topk_ids || !sorted_pairs)))
+        return fail(BFQ_ERR_NULL, "topk_ids, expert_offsets and sorted_pairs must be non-NULL");
+    if (T < 0 || topk < 1 || E < 1 || E > kMoeMaxExperts)
+        return fail(BFQ_ERR_SHAPE, "need T >= 0, topk >= 1 and 1 <= E <= 1023");
+    if (T * (int64_t)topk > 0x7FFFFFFF) return fail(BFQ_ERR_SHAPE, "T * topk must be below 2^31");
+    if (!aligned(topk_ids, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_pairs, 4) ||
+        !aligned(workspace, 4))
+        return fail(BFQ_ERR_ALIGN, "int32 buffers must be 4-byte aligned");
+    const size_t need = moe_align_workspace_bytes(T * topk, E);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(BFQ_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
+    hipError_t e = launch_moe_align(topk_ids, T * topk, E, expert_offsets, sorted_pairs,
+                                    static_cast<int32_t*>(workspace), (hipStream_t)stream);
+    if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
+    return BFQ_OK;
+}
+
+bfq_status bfq_moe_select_tile(int64_t T, int32_t topk, int32_t E, int64_t N, int64_t K,
+                               const int32_t block_shape[2], bfq_dtype in_dtype,
+                               bfq_dtype out_dtype, bfq_weight_layout w_layout,
+                               bfq_scale_format scale_fmt, bfq_tile* tile_out) {
+    if (!tile_out || !block_shape) return fail(BFQ_ERR_NULL, "tile_out and block_shape must be non-NULL");
+    if (!block_shape_ok(block_shape)) return fail(BFQ_ERR_SHAPE, "grouped GEMM: block_shape must be {128, 128}");
+    if (in_dtype != BFQ_E4M3FN) return fail(BFQ_ERR_DTYPE, "grouped GEMM: in_dtype must be BFQ_E4M3FN");
+    if (out_dtype != BFQ_BF16 && out_dtype != BFQ_FP16 && out_dtype != BFQ_FP32)
+        return fail(BFQ_ERR_DTYPE, "out_dtype must be BF16, FP16 or FP32");
+    if (T < 0 || topk < 1 || E < 1 || E > kMoeMaxExperts || N <= 0 || K <= 0 || N % 128 != 0 ||
+        K % 128 != 0)
+        return fail(BFQ_ERR_SHAPE, "need T >= 0, topk >= 1, 1 <= E <= 1023, N and K positive multiples of 128");
+    if (!wlayout_ok(w_layout)) return fail(BFQ_ERR_ARG, "unknown weight layout");
+    if (!sfmt_ok(scale_fmt)) return fail(BFQ_ERR_ARG, "unknown scale format");
+    return moe_select_tile(T, topk, E, N, K, Q_FP8, (int)w_layout, (int)scale_fmt, tile_out);
+}
+
+size_t bfq_moe_gemm_workspace_bytes(int64_t T, int32_t topk, int64_t N, const bfq_tile* tile) {
+    if (!tile || T <= 0 || topk <= 0 || N <= 0 || tile->split_k <= 1) return 0;
+    return (size_t)tile->split_k * (size_t)(T * topk) * (size_t)N * sizeof(float);
+}
+
+bfq_status bfq_moe_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
+                              int64_t a_scale_ld, const int32_t* sorted_pairs,
+                              const int32_t* expert_offsets, int32_t topk, const void* w_q,
+                              const float* w_scales, bfq_weight_layout w_layout,
+                              bfq_scale_format scale_fmt, void* out, int64_t T, int64_t N,
+                              int64_t K, int32_t E, const int32_t block_shape[2],
+                              bfq_dtype in_dtype, bfq_dtype out_dtype, const bfq_tile* tile,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (!w_q || !w_scales || !block_shape || !expert_offsets ||
+        (T != 0 && (!a_q || !a_scales || !out || !sorted_pairs)))
+        return fail(BFQ_ERR_NULL, "a_q, a_scales, sorted_pairs, expert_offsets, w_q, w_scales, out "
+                                  "and block_shape must be non-NULL");
+    if (!block_shape_ok(block_shape)) return fail(BFQ_ERR_SHAPE, "grouped GEMM: block_shape must be {128, 128}");
+    if (in_dtype != BFQ_E4M3FN) return fail(BFQ_ERR_DTYPE, "grouped GEMM: in_dtype must be BFQ_E4M3FN");
+    if (out_dtype != BFQ_BF16 && out_dtype != BFQ_FP16 && out_dtype != BFQ_FP32)
+        return fail(BFQ_ERR_DTYPE, "out_dtype must be BF16, FP16 or FP32");
+    if (!wlayout_ok(w_layout)) return fail(BFQ_ERR_ARG, "unknown weight layout");
+    if (!sfmt_ok(scale_fmt)) return fail(BFQ_ERR_ARG, "unknown scale format");
+    if (T < 0 || topk < 1 || E < 1 || E > kMoeMaxExperts || N <= 0 || K <= 0 || N % 128 != 0 ||
+        K % 128 != 0)
+        return fail(BFQ_ERR_SHAPE, "need T >= 0, topk >= 1, 1 <= E <= 1023, N and K positive multiples of 128");
+    const int64_t P = T * topk;
+    // the kernels gather token rows through one 32-bit offset over all of a_q
+    if (T * K >= (int64_t(1) << 31) || P > 0x7FFFFFFF || N > 0x7FFFFFFF)
+        return fail(BFQ_ERR_SHAPE, "T * K must be below 2^31 bytes");
+    if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(out, 16) || !aligned(a_scales, 4) ||
+        !aligned(w_scales, 4) || !aligned(workspace, 16) || !aligned(sorted_pairs, 4) ||
+        !aligned(expert_offsets, 4))
+        return fail(BFQ_ERR_ALIGN, "codes, out and workspace must be 16-byte aligned, scales and int32 arrays 4-byte");
+    const int64_t KB = K / 128;
+    int64_t ssm, ssk;
+    const bool packed = a_layout == BFQ_SCALES_PACKED_UE8M0;
+    if (a_layout == BFQ_SCALES_ROW_MAJOR) {
+        if (a_scale_ld < KB) return fail(BFQ_ERR_SHAPE, "row-major a_scale_ld must be >= K/128");
+        ssm = a_scale_ld; ssk = 1;
+    } else if (a_layout == BFQ_SCALES_COL_MAJOR) {
+        if (a_scale_ld < T) return fail(BFQ_ERR_SHAPE, "column-major a_scale_ld must be >= T");
+        ssm = 1; ssk = a_scale_ld;
+    } else if (packed) {
+        if (scale_fmt != BFQ_SCALE_UE8M0)
+            return fail(BFQ_ERR_ARG, "packed scale words need scales in the UE8M0 format");
+        if (a_scale_ld < T) return fail(BFQ_ERR_SHAPE, "packed a_scale_ld must be >= T");
+        ssm = 1; ssk = a_scale_ld;
+    } else {
+        return fail(BFQ_ERR_ARG, "unknown scale layout");
+    }
+    const int64_t k_rows = packed ? (KB - 1) / 4 : KB - 1;
+    if (T > 0 && ((T - 1) * ssm + k_rows * ssk + 1) * 4 >= (int64_t(1) << 31))
+        return fail(BFQ_ERR_SHAPE, "the activation scales must span less than 2 GiB");
+    const int wl = (int)w_layout, sf = (int)scale_fmt, otype = otype_of(out_dtype);
+    bfq_status status = BFQ_OK;
+    bfq_tile t;
+    if (tile) t = *tile;
+    else status = moe_select_tile(T, topk, E, N, K, Q_FP8, wl, sf, &t);
+    const KernelEntry* ke = find_kernel(t, Q_FP8, otype, wl, packed ? S_PACKED : sf, 1);
+    if (!ke)
+        return fail(BFQ_ERR_TILE, "tile does not name a compiled grouped kernel for this weight "
+                                  "layout and scale format");
+    if (t.split_k < 1 || t.split_k > 256 || t.split_k > KB)
+        return fail(BFQ_ERR_TILE, "split_k must be in [1, min(256, K/128)]");
+    if (moe_max_tiles(P, E, t.bm) > 65535)
+        return fail(BFQ_ERR_SHAPE, "too many row tiles for one grouped launch");
+    const size_t need = t.split_k > 1 ? (size_t)t.split_k * (size_t)P * (size_t)N * sizeof(float) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(BFQ_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
+    if (P == 0) return status;
+
+    GemmArgs ga{};
+    ga.a = a_q;
+    ga.sa = a_scales;
+    ga.sa_stride_m = ssm;
+    ga.sa_stride_k = ssk;
+    ga.sa_packed = packed ? 1 : 0;
+    ga.w = w_q;
+    ga.sw = w_scales;
+    ga.out = out;
+    ga.partials = static_cast<float*>(workspace);
+    ga.M = P;
+    ga.N = N;
+    ga.K = K;
+    ga.split = t.split_k;
+    ga.group_m = 1;
+    ga.raster = 0;
+    ga.moe_rows = sorted_pairs;
+    ga.moe_offsets = expert_offsets;
+    ga.moe_tokens = T;
+    ga.moe_topk = topk;
+    ga.moe_experts = E;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = ke->launch(ga, s);
+    if (e == hipSuccess && t.split_k > 1)
+        e = launch_splitk_reduce(ga.partials, out, P, N, t.split_k, otype, s);
+    if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
+    return status;
+}
+
+int32_t bfq_moe_num_tile_candidates(bfq_weight_layout w_layout, bfq_scale_format scale_fmt) {
+    if (!wlayout_ok(w_layout) || !sfmt_ok(scale_fmt)) return 0;
+    int ns[2] = {0, 0}, count = 0;
+    const KernelEntry* lists[2] = {moe_std_kernels(&ns[0]), moe_swapab_kernels(&ns[1])};
+    for (int l = 0; l < 2; ++l)
+        for (int i = 0; i < ns[l]; ++i)
+            count += (lists[l][i].otype == O_BF16 && lists[l][i].wlayout == (int)w_layout &&
+                      serves(lists[l][i], (int)scale_fmt));
+    return count;
+}
+
+bfq_status bfq_moe_get_tile_candidate(bfq_weight_layout w_layout, bfq_scale_format scale_fmt,
+                                      int32_t index, bfq_tile* tile_out) {
+    if (!tile_out) return fail(BFQ_ERR_NULL, "tile_out must be non-NULL");
+    if (!wlayout_ok(w_layout)) return fail(BFQ_ERR_ARG, "unknown weight layout");
+    if (!sfmt_ok(scale_fmt)) return fail(BFQ_ERR_ARG, "unknown scale format");
+    int ns[2] = {0, 0}, count = 0;
+    const KernelEntry* lists[2] = {moe_std_kernels(&ns[0]), moe_swapab_kernels(&ns[1])};
+    for (int l = 0; l < 2; ++l)
+        for (int i = 0; i < ns[l]; ++i) {
+            if (lists[l][i].otype != O_BF16 || lists[l][i].wlayout != (int)w_layout ||
+                !serves(lists[l][i], (int)scale_fmt))
                 continue;
             if (count == index) { *tile_out = lists[l][i].tile; return BFQ_OK; }
             ++count;

@@ -58,7 +58,24 @@ struct GemmArgs {
     // stream-K schedule (variant 2) only:
     int64_t dp_tiles;       // tiles [0, dp_tiles) taken whole, in rounds of the grid size
     float* sk_slots;        // [grid][2][BM*BN] fp32 partial tiles
+    // MoE grouped GEMM only (M = pairs, the output rows; a holds moe_tokens rows):
+    const int32_t* moe_rows;      // [pairs] pair ids q = t*topk + j, grouped by expert
+    const int32_t* moe_offsets;   // [E + 1] first grouped row of each expert
+    int64_t moe_tokens;           // rows of a and of the activation scales
+    int moe_topk, moe_experts;    // token of pair q = q / topk; E
 };
+
+// MoE routing: stable sort of pair ids by expert (csrc/moe.hip). counts = workspace of
+// moe_align_workspace_bytes(pairs, E) bytes.
+constexpr int kMoeMaxExperts = 1023;
+size_t moe_align_workspace_bytes(int64_t pairs, int E);
+hipError_t launch_moe_align(const int32_t* ids, int64_t pairs, int E, int32_t* offsets,
+                            int32_t* sorted, int32_t* counts, hipStream_t stream);
+// Upper bound on the per-expert row tiles of height bm over `pairs` rows and E experts (the
+// grid height of a grouped launch): sum_e ceil(rows_e / bm) <= ceil(pairs / bm) + min(E, pairs).
+inline int64_t moe_max_tiles(int64_t pairs, int64_t E, int64_t bm) {
+    return (pairs + bm - 1) / bm + (E < pairs ? E : pairs);
+}
 
 typedef hipError_t (*GemmLaunchFn)(const GemmArgs& args, hipStream_t stream);
 
@@ -71,12 +88,16 @@ struct KernelEntry {
     int sfmt;               // S_FP32: any fp32 block scales; S_UE8M0: power-of-two block
                             // scales only; S_CHANNEL: per-token x per-channel scales
     GemmLaunchFn launch;    // writes `out` (split==1) or `partials` (split>1)
+    int moe;                // 1: the grouped (MoE) form of the kernel
 };
 
 // Registries filled by the kernel translation units.
 const KernelEntry* std_kernels(int* count);
 const KernelEntry* swapab_kernels(int* count);
 const KernelEntry* streamk_kernels(int* count);
+// grouped (MoE) forms of variants 0 and 1 (KernelEntry::moe = 1)
+const KernelEntry* moe_std_kernels(int* count);
+const KernelEntry* moe_swapab_kernels(int* count);
 
 // Stream-K: workspace (two fp32 partial-tile slots per workgroup of a `grid`-workgroup grid),
 // the split of `tiles` into whole-tile rounds and the stream-K remainder, and the grid size

@@ -191,6 +191,52 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// MoE grouped GEMM: the grid's row-tile index t walks the per-expert tiles (ceil(rows_e / bm)
+// per expert, experts in order). moe_tile maps t to expert e and grouped rows [p0, p1) by a
+// wave-wide prefix sum over 64 experts at a time; every wave computes the same result
+// (wave-uniform, held in scalar registers). False when t is past the last tile.
+struct MoeSpan {
+    int64_t e, p0, p1;
+};
+// The offsets are clamped to a non-decreasing sequence in [0, pairs], so rows [p0, p1) always
+// index inside the pair list whatever the offsets hold.
+__device__ __forceinline__ bool moe_tile(const int32_t* __restrict__ offsets, int E, int64_t pairs,
+                                         int bm, int64_t t, MoeSpan& sp) {
+    const int lane = threadIdx.x & 63;
+    const int32_t P = (int32_t)pairs;
+    int64_t before = 0;
+    for (int c = 0; c < E; c += 64) {
+        const int e = c + lane;
+        int32_t a = 0, b = 0;
+        if (e < E) {
+            a = min(max(offsets[e], 0), P);
+            b = min(max(offsets[e + 1], a), P);
+        }
+        const int32_t tiles = (b - a + bm - 1) / bm;
+        int32_t inc = tiles;                       // inclusive prefix over the 64 lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t v = __shfl_up(inc, d, 64);
+            if (lane >= d) inc += v;
+        }
+        const int32_t total = __shfl(inc, 63, 64);
+        if (t < before + total) {
+            const int32_t r = (int32_t)(t - before);
+            const int L = __builtin_ctzll(__ballot(inc > r));
+            const int32_t incL = __shfl(inc, L, 64), tilesL = __shfl(tiles, L, 64);
+            const int32_t aL = __shfl(a, L, 64), bL = __shfl(b, L, 64);
+            const int64_t p0 = (int64_t)aL + (int64_t)(r - (incL - tilesL)) * bm;
+            sp.e = uniform_i64(c + L);
+            sp.p0 = uniform_i64(p0);
+            sp.p1 = uniform_i64(p0 + bm < bL ? p0 + bm : bL);
+            return true;
+        }
+        before += total;
+    }
+    return false;
+}
+
+
 // ---------------------------------------------------------------- tile order, LDS swizzle ----
 // Tile id -> (pid_m, pid_n). raster 0: workgroup ids are dealt round-robin to the 8 XCDs, so
 // ids are first remapped to give each XCD a contiguous range of tiles; raster 1: no remap.

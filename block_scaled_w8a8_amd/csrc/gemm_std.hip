@@ -68,11 +68,15 @@ struct StdShape {
 // K blocks [kb_begin, kb_end) of the output tile at (m0, n0) into acc (zeroed here). Every
 // wave of the workgroup calls it with the same arguments; it leaves no LDS DMA in flight and
 // ends on a barrier, so the next call may reuse the LDS at once.
-template <int BM, int BN, int WM, int WN, int QT, int SCHED, int STAGES, int WL>
+// MOE = 1 (grouped GEMM): the tile's rows are grouped rows [sp.p0, sp.p1) of expert sp.e;
+// each A row (and its activation scales) is gathered from token moe_rows[row] / topk, and
+// the weights are expert e's.
+template <int BM, int BN, int WM, int WN, int QT, int SCHED, int STAGES, int WL, int MOE = 0>
 __device__ __forceinline__ void std_tile(
     const GemmArgs& p, uint8_t* lds, int64_t m0, int64_t n0, int64_t kb_begin, int64_t kb_end,
     typename StdShape<BM, BN, WM, WN, SCHED>::AccT (&acc)[StdShape<BM, BN, WM, WN, SCHED>::SM]
-                                                          [StdShape<BM, BN, WM, WN, SCHED>::SN]) {
+                                                          [StdShape<BM, BN, WM, WN, SCHED>::SN],
+    const MoeSpan& sp = MoeSpan{0, 0, 0}) {
     using Shape = StdShape<BM, BN, WM, WN, SCHED>;
     constexpr int NWAVES = Shape::NWAVES;
     constexpr int TM = Shape::TM, TN = Shape::TN;
@@ -82,6 +86,7 @@ __device__ __forceinline__ void std_tile(
                   "the 32x32 schedule is fp8 only, row-major W, and needs 32-multiple wave tiles");
     static_assert(SCHED != 3 || QT == Q_FP8, "the block-scaled MFMA schedule is fp8 only");
     static_assert(SCHED <= 4, "schedules 0-4");
+    static_assert(!MOE || (STAGES == 2 && SCHED != 4), "grouped tiles: two stages, block scales");
     constexpr int STAGE = (BM + BN) * 128;         // bytes per LDS stage
     constexpr int CHUNKS = (BM + BN) / 8;          // 1 KB load chunks per stage
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
@@ -109,10 +114,20 @@ __device__ __forceinline__ void std_tile(
 
     // Buffer resources over this tile's rows: rows past M (N) read as zero and are never
     // stored, so ragged tiles need no clamping. K <= 2^23 keeps every offset below 2^32.
-    const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
+    const int64_t rows_a = MOE ? sp.p1 - sp.p0 : (M - m0) < BM ? (M - m0) : BM;
     const int64_t rows_w = (N - n0) < BN ? (N - n0) : BN;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(static_cast<const uint8_t*>(p.a) + m0 * K, (uint32_t)(rows_a * K));
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(static_cast<const uint8_t*>(p.w) + n0 * K, (uint32_t)(rows_w * K));
+    // grouped: A over every token (rows are gathered), W and its scales those of expert e
+    const __amdgpu_buffer_rsrc_t ra =
+        MOE ? make_rsrc(p.a, (uint32_t)(p.moe_tokens * K))
+            : make_rsrc(static_cast<const uint8_t*>(p.a) + m0 * K, (uint32_t)(rows_a * K));
+    const uint8_t* w_e = static_cast<const uint8_t*>(p.w) + (MOE ? sp.e * N * K : 0);
+    const float* sw_e = p.sw + (MOE ? sp.e * (N / 128) * KB : 0);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_e + n0 * K, (uint32_t)(rows_w * K));
+    constexpr uint32_t kNoLoad = 0x80000000u;   // past every resource: reads zero, no access
+    // grouped: token row of tile row r (rows past the expert's last read nothing)
+    auto src_row = [&](int64_t r) -> int64_t {
+        return r < rows_a ? (int64_t)p.moe_rows[sp.p0 + r] / p.moe_topk : -1;
+    };
 
     // Scale buffers. Activation-scale DMA slot s = wave*64 + lane holds token row
     // r(s) = wm*TM + sm*MF + frow for s = wm*TM + frow*SM + sm, so each lane later reads its
@@ -122,17 +137,23 @@ __device__ __forceinline__ void std_tile(
     const int64_t ssm = p.sa_stride_m, ssk = p.sa_stride_k;
     const int packed = p.sa_packed;
     const int64_t sa_rows = packed ? (KB - 1) / 4 : KB - 1;
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
-        p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + sa_rows * ssk + 1) * 4));
+    const __amdgpu_buffer_rsrc_t rsa =
+        MOE ? make_rsrc(p.sa, (uint32_t)(((p.moe_tokens - 1) * ssm + sa_rows * ssk + 1) * 4))
+            : make_rsrc(p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + sa_rows * ssk + 1) * 4));
     uint32_t sa_dma_voff;
     {
         const int sl = wave * 64 + lane;
         const int swm = sl / TM, rem = sl % TM;
         const int r = swm * TM + (rem % SM) * MF + rem / SM;
-        sa_dma_voff = (uint32_t)(r * ssm * 4);
+        if constexpr (MOE) {
+            const int64_t t = src_row(r);
+            sa_dma_voff = t >= 0 ? (uint32_t)(t * ssm * 4) : kNoLoad;
+        } else {
+            sa_dma_voff = (uint32_t)(r * ssm * 4);
+        }
     }
     const int64_t nb0 = n0 / 128, nbs = (rows_w + 127) / 128;
-    const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.sw + nb0 * KB, (uint32_t)(nbs * KB * 4));
+    const __amdgpu_buffer_rsrc_t rsw = make_rsrc(sw_e + nb0 * KB, (uint32_t)(nbs * KB * 4));
     const uint32_t sw_dma_voff = (uint32_t)(lane * KB * 4);
     const uint32_t sa_lds = (uint32_t)((wm * TM + frow * SM) * 4);
     const uint32_t sw_lds = (uint32_t)(BM * 4 + ((wn * TN) / 128) * 4);
@@ -141,8 +162,18 @@ __device__ __forceinline__ void std_tile(
     // LDS slot (l & 7) of row +(l >> 3), which holds global chunk (l & 7) ^ swz(row). As
     // NWAVES is even, swz(row) = (l >> 3) ^ (wave & 1) for every i, so one per-lane byte
     // offset serves all chunks and the chunk index goes into the scalar offset.
-    const uint32_t dma_voff = (uint32_t)(((lane >> 3) + wave * 8) * K +
-                                         (((lane & 7) ^ (lane >> 3) ^ (wave & 1)) << 4));
+    const uint32_t chunk_off = (uint32_t)(((lane & 7) ^ (lane >> 3) ^ (wave & 1)) << 4);
+    const uint32_t dma_voff = (uint32_t)(((lane >> 3) + wave * 8) * K) + chunk_off;
+    // grouped: the gathered A rows of this lane's load chunks (tile row (lane>>3) + 8*(wave +
+    // NWAVES*i)), as full byte offsets; the K block goes in the scalar offset
+    uint32_t a_voff[MOE ? CPW_A : 1];
+    if constexpr (MOE) {
+#pragma unroll
+        for (int i = 0; i < CPW_A; ++i) {
+            const int64_t t = src_row((lane >> 3) + 8 * (wave + NWAVES * i));
+            a_voff[i] = t >= 0 ? (uint32_t)(t * K) + chunk_off : kNoLoad;
+        }
+    }
     // packed W: lane offset within a 1 KB half, bytes between 16-row fragments
     const uint32_t lane16 = (uint32_t)(lane * 16);
     const uint32_t frag_stride = (uint32_t)(KB * 2048);
@@ -163,7 +194,8 @@ __device__ __forceinline__ void std_tile(
         for (int i = 0; i < CPW; ++i) {
             const uint32_t lds_off = (uint32_t)((wave + NWAVES * i) * 1024 + stage * STAGE);
             if (i < CPW_A) {
-                dma16(ra, lds, lds_off, dma_voff, skb + (uint32_t)(NWAVES * i * 8 * K));
+                if constexpr (MOE) dma16(ra, lds, lds_off, a_voff[i < CPW_A ? i : 0], skb);
+                else dma16(ra, lds, lds_off, dma_voff, skb + (uint32_t)(NWAVES * i * 8 * K));
             } else if constexpr (WL == W_ROW) {
                 dma16(rw, lds, lds_off, dma_voff, skb + (uint32_t)((NWAVES * i - BM / 8) * 8 * K));
             } else {
@@ -548,6 +580,60 @@ __device__ __forceinline__ void std_store(
     }
 }
 
+// Grouped (MoE) store: tile row r < rows holds pair rows[r]; it goes to base[base_off +
+// rows[r]*N + n] (the output in pair order); a pair id outside [0, M) is not stored. 16x16
+// sub-tiles only.
+template <int OT, int BM, int BN, int WM, int WN, int SCHED>
+__device__ __forceinline__ void std_store_rows(
+    void* base, int64_t base_off, int64_t M, int64_t N, int64_t n0, const int32_t* __restrict__ rows,
+    int64_t nrows,
+    const typename StdShape<BM, BN, WM, WN, SCHED>::AccT (
+        &acc)[StdShape<BM, BN, WM, WN, SCHED>::SM][StdShape<BM, BN, WM, WN, SCHED>::SN]) {
+    using Shape = StdShape<BM, BN, WM, WN, SCHED>;
+    constexpr int TM = Shape::TM, TN = Shape::TN, SM = Shape::SM, SN = Shape::SN;
+    static_assert(Shape::MF == 16, "grouped tiles use 16x16 sub-tiles");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int frow = lane & 15, fgrp = lane >> 4;
+#pragma unroll
+    for (int sm = 0; sm < SM; ++sm) {
+        const int64_t r = wm * TM + sm * 16 + frow;
+        if (r >= nrows) continue;
+        const int64_t m = rows[r];
+        if (m < 0 || m >= M) continue;
+#pragma unroll
+        for (int sn = 0; sn < SN; ++sn) {
+            const int64_t n = n0 + wn * TN + sn * 16 + 4 * fgrp;
+            if (n >= N) continue;
+            store4<OT>(base, base_off + m * N + n, acc[sm][sn]);
+        }
+    }
+}
+
+// Grouped (MoE) GEMM, standard tiles: grid = N tiles x moe_max_tiles(pairs, E, BM) x split;
+// blockIdx.y is the per-expert row tile (moe_tile), workgroups past the last tile exit at
+// once (before any LDS traffic, uniformly).
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int WL>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_moe_std_kernel(GemmArgs p) {
+    using Shape = StdShape<BM, BN, WM, WN, SCHED>;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+    MoeSpan sp;
+    if (!moe_tile(p.moe_offsets, p.moe_experts, p.M, BM, blockIdx.y, sp)) return;
+    const int64_t N = p.N, KB = p.K / 128;
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    const int split = p.split, z = blockIdx.z;
+    const int64_t kb_begin = (int64_t)z * KB / split, kb_end = (int64_t)(z + 1) * KB / split;
+    typename Shape::AccT acc[Shape::SM][Shape::SN];
+    std_tile<BM, BN, WM, WN, QT, SCHED, 2, WL, 1>(p, lds, sp.p0, n0, kb_begin, kb_end, acc, sp);
+    const int32_t* rows = p.moe_rows + sp.p0;
+    if (split == 1)
+        std_store_rows<OT, BM, BN, WM, WN, SCHED>(p.out, 0, p.M, N, n0, rows, sp.p1 - sp.p0, acc);
+    else
+        std_store_rows<O_FP32, BM, BN, WM, WN, SCHED>(p.partials, (int64_t)z * p.M * N, p.M, N, n0,
+                                                      rows, sp.p1 - sp.p0, acc);
+}
+
 // One workgroup per (tile, K split): grid = tiles x 1 x split.
 template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int STAGES, int WL>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_std_kernel(GemmArgs p) {
@@ -770,6 +856,24 @@ hipError_t launch_std(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, int QT, int OT, int SCHED, int WL>
+hipError_t launch_moe_std(const GemmArgs& a, hipStream_t stream) {
+    constexpr int LDS_BYTES = StdShape<BM, BN, WM, WN, SCHED>::lds_bytes(2);
+    dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)moe_max_tiles(a.M, a.moe_experts, BM),
+              (unsigned)a.split);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&gemm_moe_std_kernel<BM, BN, WM, WN, QT, OT, SCHED, WL>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((gemm_moe_std_kernel<BM, BN, WM, WN, QT, OT, SCHED, WL>), grid,
+                       dim3(64 * WM * WN), LDS_BYTES, stream, a);
+    return hipGetLastError();
+}
+
 #define BFQ_STD_ENTRY(BM, BN, WM, WN, ST, SC, QT, OT, WL)                                \
     KernelEntry{bfq_tile{0, BM, BN, 128, 1, WM, WN, ST, 8, SC, 0, 0}, QT, OT, WL,         \
                 (SC) == 3 ? S_UE8M0 : (SC) == 4 ? S_CHANNEL : S_FP32,                      \
@@ -850,6 +954,32 @@ static const KernelEntry kStreamKKernels[] = {
     BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 4, Q_FP8, W_PACKED16),
     BFQ_SK_ALL_OUT(256, 256, 4, 2, 2, 4, Q_INT8, W_PACKED16),
 };
+
+#define BFQ_MOE_STD_ENTRY(BM, BN, WM, WN, SC, QT, OT, WL)                                  \
+    KernelEntry{bfq_tile{0, BM, BN, 128, 1, WM, WN, 2, 1, SC, 0, 0}, QT, OT, WL,              \
+                (SC) == 3 ? S_UE8M0 : S_FP32, &launch_moe_std<BM, BN, WM, WN, QT, OT, SC, WL>, 1}
+#define BFQ_MOE_STD(BM, BN, WM, WN, SC, QT)                                                 \
+    BFQ_MOE_STD_ENTRY(BM, BN, WM, WN, SC, QT, O_BF16, W_ROW),                              \
+        BFQ_MOE_STD_ENTRY(BM, BN, WM, WN, SC, QT, O_FP16, W_ROW),                          \
+        BFQ_MOE_STD_ENTRY(BM, BN, WM, WN, SC, QT, O_FP32, W_ROW),                          \
+        BFQ_MOE_STD_ENTRY(BM, BN, WM, WN, SC, QT, O_BF16, W_PACKED16),                     \
+        BFQ_MOE_STD_ENTRY(BM, BN, WM, WN, SC, QT, O_FP16, W_PACKED16),                     \
+        BFQ_MOE_STD_ENTRY(BM, BN, WM, WN, SC, QT, O_FP32, W_PACKED16)
+
+// grouped (MoE) standard tiles, fp8 (the gathered rows cost registers: 256x256 with the FMA
+// schedule spills with packed weights, so 128x256 is the largest FMA tile)
+static const KernelEntry kMoeStdKernels[] = {
+    BFQ_MOE_STD(128, 256, 2, 2, 0, Q_FP8),
+    BFQ_MOE_STD(128, 128, 2, 2, 0, Q_FP8),
+    BFQ_MOE_STD(64, 128, 1, 2, 0, Q_FP8),
+    BFQ_MOE_STD(256, 256, 4, 2, 3, Q_FP8),
+    BFQ_MOE_STD(128, 128, 2, 2, 3, Q_FP8),
+};
+
+const KernelEntry* moe_std_kernels(int* count) {
+    *count = (int)(sizeof(kMoeStdKernels) / sizeof(kMoeStdKernels[0]));
+    return kMoeStdKernels;
+}
 
 const KernelEntry* streamk_kernels(int* count) {
     *count = (int)(sizeof(kStreamKKernels) / sizeof(kStreamKKernels[0]));

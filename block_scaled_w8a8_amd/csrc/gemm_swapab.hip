@@ -81,9 +81,13 @@ __device__ __forceinline__ void mfma_accumulate(v4f& acc, const v4i (&w)[2], con
     }
 }
 
-template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL, int CH>
+// MOE = 1 (grouped GEMM): blockIdx.y is a per-expert row tile (moe_tile); token rows and
+// their scales are gathered through moe_rows, the weights are the expert's, and each output
+// row is scattered to its pair's row.
+template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL, int CH, int MOE = 0>
 __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs p) {
     constexpr int SM = MT / 16, SN = NWR / 16;
+    static_assert(!MOE || CH != 1, "grouped tiles take block scales");
     static_assert(MT % 16 == 0 && NWR % 16 == 0, "tiles are multiples of 16");
     static_assert(128 % NWR == 0, "a wave's rows must lie in one 128-row scale block");
 
@@ -94,7 +98,11 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
 
     const int64_t M = p.M, N = p.N, K = p.K, KB = K / 128;
     const int64_t n0 = ((int64_t)blockIdx.x * NWAVES + wn) * NWR;
-    const int64_t m0 = (int64_t)blockIdx.y * MT;
+    MoeSpan sp{0, 0, 0};
+    if constexpr (MOE) {
+        if (!moe_tile(p.moe_offsets, p.moe_experts, M, MT, blockIdx.y, sp)) return;   // uniform
+    }
+    const int64_t m0 = MOE ? sp.p0 : (int64_t)blockIdx.y * MT;
     const int split = p.split, z = blockIdx.z;
     const int64_t ks0 = (int64_t)z * KB / split, ks1 = (int64_t)(z + 1) * KB / split;
     const int64_t kb_begin = ks0 + (ks1 - ks0) * wk / KW, kb_end = ks0 + (ks1 - ks0) * (wk + 1) / KW;
@@ -108,8 +116,8 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
     constexpr uint32_t HOFF = WL == W_ROW ? 64u : 1024u;     // second half of a fragment
     constexpr uint32_t kNoLoad = 0x80000000u;                 // past every resource here
     const int64_t nb0 = wave_live ? n0 : 0;
-    const __amdgpu_buffer_rsrc_t rw =
-        make_rsrc(static_cast<const uint8_t*>(p.w) + nb0 * K, (uint32_t)(NWR * K));
+    const uint8_t* w_e = static_cast<const uint8_t*>(p.w) + (MOE ? sp.e * N * K : 0);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_e + nb0 * K, (uint32_t)(NWR * K));
     uint32_t w_voff[SN], w_sn[SN];
 #pragma unroll
     for (int sn = 0; sn < SN; ++sn) {
@@ -121,21 +129,31 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
             w_sn[sn] = (uint32_t)(sn * KB * 2048);
         }
     }
-    const int64_t rows_a = (M - m0) < MT ? (M - m0) : MT;
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(static_cast<const uint8_t*>(p.a) + m0 * K, (uint32_t)(rows_a * K));
+    const int64_t rows_a = MOE ? sp.p1 - sp.p0 : (M - m0) < MT ? (M - m0) : MT;
     const int64_t ssm = p.sa_stride_m, ssk = p.sa_stride_k;
     constexpr bool CHAN = CH == 1, PK = CH == 2;   // PK: block kb in word row kb / 4
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
-        p.sa + m0 * ssm,
-        (uint32_t)(((rows_a - 1) * ssm + (PK ? (KB - 1) / 4 : KB - 1) * ssk + 1) * 4));
+    const int64_t sa_krows = PK ? (KB - 1) / 4 : KB - 1;
+    // grouped: resources over every token; a tile row's offsets are those of its token
+    const __amdgpu_buffer_rsrc_t ra =
+        MOE ? make_rsrc(p.a, (uint32_t)(p.moe_tokens * K))
+            : make_rsrc(static_cast<const uint8_t*>(p.a) + m0 * K, (uint32_t)(rows_a * K));
+    const __amdgpu_buffer_rsrc_t rsa =
+        MOE ? make_rsrc(p.sa, (uint32_t)(((p.moe_tokens - 1) * ssm + sa_krows * ssk + 1) * 4))
+            : make_rsrc(p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + sa_krows * ssk + 1) * 4));
     uint32_t a_voff[SM], sa_voff[SM];
 #pragma unroll
     for (int sm = 0; sm < SM; ++sm) {
-        a_voff[sm] = (uint32_t)((sm * 16 + frow) * K + fgrp * 16);
-        sa_voff[sm] = (uint32_t)((sm * 16 + frow) * ssm * 4);
+        const int r = sm * 16 + frow;
+        if constexpr (MOE) {
+            const int64_t t = r < rows_a ? (int64_t)p.moe_rows[sp.p0 + r] / p.moe_topk : -1;
+            a_voff[sm] = t >= 0 ? (uint32_t)(t * K + fgrp * 16) : kNoLoad;
+            sa_voff[sm] = t >= 0 ? (uint32_t)(t * ssm * 4) : kNoLoad;
+        } else {
+            a_voff[sm] = (uint32_t)(r * K + fgrp * 16);
+            sa_voff[sm] = (uint32_t)(r * ssm * 4);
+        }
     }
-    const float* sw_row = p.sw + (nb0 / 128) * KB;
+    const float* sw_row = p.sw + (MOE ? sp.e * (N / 128) * KB : 0) + (nb0 / 128) * KB;
     const int64_t L = kb_end - kb_begin;
     const int64_t kb_hi = L > 0 ? kb_end - 1 : kb_begin < KB ? kb_begin : KB - 1;
 
@@ -264,8 +282,10 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
     if (wk == 0 && wave_live) {
 #pragma unroll
         for (int sm = 0; sm < SM; ++sm) {
-            const int64_t m = m0 + sm * 16 + frow;
-            if (m >= M) continue;
+            const int64_t r = sm * 16 + frow;   // tile row; grouped: pair row moe_rows[p0 + r]
+            if (MOE ? r >= rows_a : m0 + r >= M) continue;
+            const int64_t m = MOE ? (int64_t)p.moe_rows[sp.p0 + r] : m0 + r;
+            if (MOE && (m < 0 || m >= M)) continue;   // a pair id outside the output
 #pragma unroll
             for (int sn = 0; sn < SN; ++sn) {
                 const int64_t n = n0 + sn * 16 + 4 * fgrp;
@@ -287,8 +307,9 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
 // in lane order (conflict-free) for its MFMAs. Buffer i & 1 was last read at step i - 2, before
 // the previous step's barrier. Every wave runs the same number of steps (the longest K slice
 // of the workgroup) so the barriers match; a wave with a shorter slice idles on its last one.
-template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL, int CH>
+template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL, int CH, int MOE = 0>
 __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmArgs p) {
+    static_assert(!MOE || CH != 1, "grouped tiles take block scales");
     constexpr int SM = MT / 16, SN = NWR / 16;
     constexpr int AI = 2 * SM;                              // 1 KB token halves per K block
     constexpr int API = (AI + NWAVES - 1) / NWAVES;         // at most this many per wave
@@ -304,7 +325,11 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
 
     const int64_t M = p.M, N = p.N, K = p.K, KB = K / 128;
     const int64_t n0 = ((int64_t)blockIdx.x * NWAVES + wn) * NWR;
-    const int64_t m0 = (int64_t)blockIdx.y * MT;
+    MoeSpan sp{0, 0, 0};
+    if constexpr (MOE) {
+        if (!moe_tile(p.moe_offsets, p.moe_experts, M, MT, blockIdx.y, sp)) return;   // uniform
+    }
+    const int64_t m0 = MOE ? sp.p0 : (int64_t)blockIdx.y * MT;
     const int split = p.split, z = blockIdx.z;
     const int64_t ks0 = (int64_t)z * KB / split, ks1 = (int64_t)(z + 1) * KB / split;
     const int64_t len = ks1 - ks0;                          // >= 1 (split <= K/128)
@@ -319,8 +344,8 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
     constexpr uint32_t KSTEP = WL == W_ROW ? 128u : 2048u;   // bytes between K blocks
     constexpr uint32_t HOFF = WL == W_ROW ? 64u : 1024u;     // second half of a fragment
     const int64_t nb0 = wave_live ? n0 : 0;
-    const __amdgpu_buffer_rsrc_t rw =
-        make_rsrc(static_cast<const uint8_t*>(p.w) + nb0 * K, (uint32_t)(NWR * K));
+    const uint8_t* w_e = static_cast<const uint8_t*>(p.w) + (MOE ? sp.e * N * K : 0);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_e + nb0 * K, (uint32_t)(NWR * K));
     // weight sub-tile sn: per-lane offset and the scalar offset of K block 0
     uint32_t w_voff[SN];
     uint32_t w_sn[SN];
@@ -334,36 +359,53 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
             w_sn[sn] = (uint32_t)(sn * KB * 2048);
         }
     }
-    const int64_t rows_a = (M - m0) < MT ? (M - m0) : MT;
+    const int64_t rows_a = MOE ? sp.p1 - sp.p0 : (M - m0) < MT ? (M - m0) : MT;
     const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(static_cast<const uint8_t*>(p.a) + m0 * K, (uint32_t)(rows_a * K));
+        MOE ? make_rsrc(p.a, (uint32_t)(p.moe_tokens * K))
+            : make_rsrc(static_cast<const uint8_t*>(p.a) + m0 * K, (uint32_t)(rows_a * K));
     // Every wave issues the same loads every step, so the compiler's count of loads in flight
     // is exact and each wait lets the whole ring stay outstanding; loads a wave does not need
     // use an offset past the resource (they return zero without a memory access).
     constexpr uint32_t kNoLoad = 0x80000000u;   // past every resource here (all < 2^31 bytes)
+    // grouped: the token of tile row r (-1 past the expert's rows)
+    auto src_row = [&](int64_t r) -> int64_t {
+        return r < rows_a ? (int64_t)p.moe_rows[sp.p0 + r] / p.moe_topk : -1;
+    };
     // token halves this wave fetches: j = wn + NWAVES * t (sub-tile j >> 1, K half j & 1)
     uint32_t a_voff[API];
 #pragma unroll
     for (int t = 0; t < API; ++t) {
         const int j = wn + NWAVES * t;
-        a_voff[t] = j < AI ? (uint32_t)((((j >> 1) * 16 + frow) * K) + 64 * (j & 1) + 16 * fgrp)
-                           : kNoLoad;
+        const int64_t r = (j >> 1) * 16 + frow;
+        if constexpr (MOE) {
+            const int64_t tok = j < AI ? src_row(r) : -1;
+            a_voff[t] = tok >= 0 ? (uint32_t)(tok * K + 64 * (j & 1) + 16 * fgrp) : kNoLoad;
+        } else {
+            a_voff[t] = j < AI ? (uint32_t)(r * K + 64 * (j & 1) + 16 * fgrp) : kNoLoad;
+        }
     }
     // token scales (last wave of the group): scale slot x = r * SM + s holds token s * 16 + r,
     // so each lane later reads its SM scales as one contiguous run; lane l fills slots l + 64q
     const bool scale_wave = wn == NWAVES - 1;
     const int64_t ssm = p.sa_stride_m, ssk = p.sa_stride_k;
     constexpr bool CHAN = CH == 1, PK = CH == 2;   // PK: block kb in word row kb / 4
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
-        p.sa + m0 * ssm,
-        (uint32_t)(((rows_a - 1) * ssm + (PK ? (KB - 1) / 4 : KB - 1) * ssk + 1) * 4));
+    const int64_t sa_krows = PK ? (KB - 1) / 4 : KB - 1;
+    const __amdgpu_buffer_rsrc_t rsa =
+        MOE ? make_rsrc(p.sa, (uint32_t)(((p.moe_tokens - 1) * ssm + sa_krows * ssk + 1) * 4))
+            : make_rsrc(p.sa + m0 * ssm, (uint32_t)(((rows_a - 1) * ssm + sa_krows * ssk + 1) * 4));
     uint32_t sa_voff[SCW];
 #pragma unroll
     for (int q = 0; q < SCW; ++q) {
         const int x = lane + 64 * q;
-        sa_voff[q] = scale_wave ? (uint32_t)(((x % SM) * 16 + x / SM) * ssm * 4) : kNoLoad;
+        const int64_t r = (x % SM) * 16 + x / SM;
+        if constexpr (MOE) {
+            const int64_t tok = scale_wave && x < MT ? src_row(r) : -1;
+            sa_voff[q] = tok >= 0 ? (uint32_t)(tok * ssm * 4) : kNoLoad;
+        } else {
+            sa_voff[q] = scale_wave ? (uint32_t)(r * ssm * 4) : kNoLoad;
+        }
     }
-    const float* sw_row = p.sw + (nb0 / 128) * KB;
+    const float* sw_row = p.sw + (MOE ? sp.e * (N / 128) * KB : 0) + (nb0 / 128) * KB;
 
     __shared__ __attribute__((aligned(16))) uint8_t tok[KW][2][SLOT];
 
@@ -502,8 +544,10 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
     if (wk == 0 && wave_live) {
 #pragma unroll
         for (int sm = 0; sm < SM; ++sm) {
-            const int64_t m = m0 + sm * 16 + frow;
-            if (m >= M) continue;
+            const int64_t r = sm * 16 + frow;   // tile row; grouped: pair row moe_rows[p0 + r]
+            if (MOE ? r >= rows_a : m0 + r >= M) continue;
+            const int64_t m = MOE ? (int64_t)p.moe_rows[sp.p0 + r] : m0 + r;
+            if (MOE && (m < 0 || m >= M)) continue;   // a pair id outside the output
 #pragma unroll
             for (int sn = 0; sn < SN; ++sn) {
                 const int64_t n = n0 + sn * 16 + 4 * fgrp;
@@ -528,6 +572,25 @@ hipError_t launch_swapab_lds(const GemmArgs& a, hipStream_t stream) {
     const int64_t strips = (a.N + NWR * NWAVES - 1) / (NWR * NWAVES);
     dim3 grid((unsigned)strips, (unsigned)((a.M + MT - 1) / MT), (unsigned)a.split);
     hipLaunchKernelGGL((gemm_swapab_lds_kernel<MT, NWR, NWAVES, KW, D, QT, OT, WL, CH>), grid,
+                       dim3(64 * NWAVES * KW), 0, stream, a);
+    return hipGetLastError();
+}
+
+// grouped (MoE) forms: grid height = the per-expert row tiles' upper bound
+template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL, int CH>
+hipError_t launch_moe_swapab(const GemmArgs& a, hipStream_t stream) {
+    const int64_t strips = (a.N + NWR * NWAVES - 1) / (NWR * NWAVES);
+    dim3 grid((unsigned)strips, (unsigned)moe_max_tiles(a.M, a.moe_experts, MT), (unsigned)a.split);
+    hipLaunchKernelGGL((gemm_swapab_kernel<MT, NWR, NWAVES, KW, D, QT, OT, WL, CH, 1>), grid,
+                       dim3(64 * NWAVES * KW), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL, int CH>
+hipError_t launch_moe_swapab_lds(const GemmArgs& a, hipStream_t stream) {
+    const int64_t strips = (a.N + NWR * NWAVES - 1) / (NWR * NWAVES);
+    dim3 grid((unsigned)strips, (unsigned)moe_max_tiles(a.M, a.moe_experts, MT), (unsigned)a.split);
+    hipLaunchKernelGGL((gemm_swapab_lds_kernel<MT, NWR, NWAVES, KW, D, QT, OT, WL, CH, 1>), grid,
                        dim3(64 * NWAVES * KW), 0, stream, a);
     return hipGetLastError();
 }
@@ -677,6 +740,48 @@ static const KernelEntry kSwapabKernels[] = {
     BFQ_SAB_PK(64, 16, 1, 4, 2, Q_FP8),
     BFQ_SAB_PK(32, 32, 1, 4, 4, Q_FP8),
 };
+
+// grouped (MoE) swap-AB kernels, fp8, fp32 or UE8M0 block scales (S_FP32 serves both) and
+// packed UE8M0 words
+#define BFQ_MOE_SAB_ENTRY(MT, NWR, NW, KW, D, OT, WL, CH)                                      \
+    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 0, 0, 0}, Q_FP8, OT, WL,         \
+                (CH) == 2 ? S_PACKED : S_FP32, &launch_moe_swapab<MT, NWR, NW, KW, D, Q_FP8, OT, WL, CH>, 1}
+#define BFQ_MOE_SABL_ENTRY(MT, NWR, NW, KW, D, OT, WL, CH)                                     \
+    KernelEntry{bfq_tile{1, MT, NWR * NW, 128, 1, KW, NW, D, 1, 1, 0, 0}, Q_FP8, OT, WL,         \
+                (CH) == 2 ? S_PACKED : S_FP32,                                                 \
+                &launch_moe_swapab_lds<MT, NWR, NW, KW, D, Q_FP8, OT, WL, CH>, 1}
+#define BFQ_MOE_X6(ENTRY, MT, NWR, NW, KW, D, CH)                                               \
+    ENTRY(MT, NWR, NW, KW, D, O_BF16, W_ROW, CH), ENTRY(MT, NWR, NW, KW, D, O_FP16, W_ROW, CH),   \
+        ENTRY(MT, NWR, NW, KW, D, O_FP32, W_ROW, CH),                                          \
+        ENTRY(MT, NWR, NW, KW, D, O_BF16, W_PACKED16, CH),                                     \
+        ENTRY(MT, NWR, NW, KW, D, O_FP16, W_PACKED16, CH),                                     \
+        ENTRY(MT, NWR, NW, KW, D, O_FP32, W_PACKED16, CH)
+#define BFQ_MOE_SAB(MT, NWR, NW, KW, D)                                                        \
+    BFQ_MOE_X6(BFQ_MOE_SAB_ENTRY, MT, NWR, NW, KW, D, 0), BFQ_MOE_X6(BFQ_MOE_SAB_ENTRY, MT, NWR, NW, KW, D, 2)
+#define BFQ_MOE_SABL(MT, NWR, NW, KW, D)                                                       \
+    BFQ_MOE_X6(BFQ_MOE_SABL_ENTRY, MT, NWR, NW, KW, D, 0), BFQ_MOE_X6(BFQ_MOE_SABL_ENTRY, MT, NWR, NW, KW, D, 2)
+
+static const KernelEntry kMoeSwapabKernels[] = {
+    BFQ_MOE_SAB(16, 32, 4, 1, 4),
+    BFQ_MOE_SAB(16, 16, 4, 1, 8),
+    BFQ_MOE_SAB(16, 16, 1, 4, 4),
+    BFQ_MOE_SAB(32, 32, 4, 1, 4),
+    BFQ_MOE_SABL(16, 16, 8, 1, 8),
+    BFQ_MOE_SABL(32, 16, 8, 1, 4),
+    BFQ_MOE_SABL(32, 16, 6, 1, 4),
+    BFQ_MOE_SABL(32, 16, 4, 2, 4),
+    BFQ_MOE_SABL(64, 16, 8, 1, 4),
+    BFQ_MOE_SABL(64, 16, 6, 1, 4),
+    BFQ_MOE_SABL(64, 16, 4, 2, 4),
+    BFQ_MOE_SABL(96, 16, 6, 1, 4),
+    BFQ_MOE_SABL(128, 16, 8, 1, 4),
+    BFQ_MOE_SABL(128, 16, 6, 1, 4),
+};
+
+const KernelEntry* moe_swapab_kernels(int* count) {
+    *count = (int)(sizeof(kMoeSwapabKernels) / sizeof(kMoeSwapabKernels[0]));
+    return kMoeSwapabKernels;
+}
 
 const KernelEntry* swapab_kernels(int* count) {
     *count = (int)(sizeof(kSwapabKernels) / sizeof(kSwapabKernels[0]));

@@ -8,6 +8,8 @@
 //     { "N": 24576, "K": 7168, "dtype": "fp8_w8a8", "block_shape": [128, 128],
 //       "w_layout": "packed16",            (optional; "row_major" when absent)
 //       "scales": "ue8m0",                 (optional; "fp32" when absent; not with [1, K])
+//       "E": 256,                          (optional; expert count of a grouped MoE entry,
+//                                           whose M buckets are token counts; 0 when absent)
 //       "configs": { "1": {"variant": 1, "bm": 16, "bn": 128, "split_k": 2, "waves_m": 1,
 //                          "waves_n": 4, "stages": 4, "group_m": 1}, ... } } ] }
 #include "tile_table.h"
@@ -224,7 +226,11 @@ bool parse_tile_table(const std::string& text, TileTable& out, std::string& err)
             buckets[(int64_t)m] = tl;
         }
         if (buckets.empty()) { err = "entry has no configs"; return false; }
-        t.entries[TableKey{N, K, qtype, wlayout, sfmt}] = std::move(buckets);
+        int64_t E = 0;
+        if (e.get("E") && !get_int(e, "E", E, true, 0, err)) return false;
+        if (E < 0 || E > 1023) { err = "'E' must be in [0, 1023]"; return false; }
+        if (E > 0 && sfmt == 2) { err = "grouped (E > 0) entries take block scales"; return false; }
+        t.entries[TableKey{N, K, qtype, wlayout, sfmt, E}] = std::move(buckets);
     }
     out = std::move(t);
     return true;

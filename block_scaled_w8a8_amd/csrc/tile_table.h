@@ -22,7 +22,9 @@ struct TableKey {
     int qtype;
     int wlayout;   // weight layout the tuned kernels read (W_ROW / W_PACKED16)
     int sfmt;      // scale handling the entry was tuned for (S_FP32 / S_UE8M0 / S_CHANNEL)
+    int64_t E = 0; // expert count of a grouped (MoE) entry, 0 for a dense one ([CONFIG] §5)
     bool operator<(const TableKey& o) const {
+        if (E != o.E) return E < o.E;
         if (N != o.N) return N < o.N;
         if (K != o.K) return K < o.K;
         if (qtype != o.qtype) return qtype < o.qtype;

@@ -20,7 +20,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/gemm_std.hip", "csrc/gemm_swapab.hip", "csrc/quant.hip",
-                  "csrc/device_common.h")
+                  "csrc/moe.hip", "csrc/device_common.h")
 
 
 def source_hash() -> str:

@@ -58,3 +58,12 @@ def routing(T: int, E: int, topk: int, seed: int = 0, t_max: int | None = None) 
 def expert_weights(E: int, N: int, K: int, seed: int = 0) -> torch.Tensor:
     """fp32 [E, N, K]: one weights() draw per expert."""
     return torch.stack([weights(N, K, seed=seed + 1000 + e) for e in range(E)])
+
+
+def expert_weight_on(device, e: int, N: int, K: int, seed: int = 0) -> torch.Tensor:
+    """fp32 [N, K] weights of expert e drawn on `device` with its own seeded generator (the
+    full expert stack of a large MoE layer is too big to draw on the host); the same call
+    gives the same values again, so a checker can re-draw any expert it samples."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) + 1000 + int(e))
+    return torch.randn((N, K), generator=g, device=device, dtype=torch.float32) * 0.02

@@ -238,6 +238,59 @@ bfq_status bfq_get_tile_candidate(const int32_t block_shape[2], bfq_dtype in_dty
                                   bfq_weight_layout w_layout, bfq_scale_format scale_fmt,
                                   int32_t index, bfq_tile* tile_out);
 
+/* ------------------------------------------------------- MoE grouped block GEMM ----
+ * [CONFIG] §5: the MoE kernels take the same per-shape, per-batch-size tuned configs with an
+ * expert count E in the key. Token t routed to experts topk_ids[t][0..topk-1] forms pairs
+ * q = t*topk + j; out[q][n] (pair order, [T*topk][N]) = the block-scaled GEMM (as
+ * bfq_block_gemm) of token row t of a_q with row n of expert topk_ids[t][j]'s weights.
+ * e4m3fn codes, block_shape {128, 128}; the combine over a token's experts is not part of it.
+ */
+
+/* Group the pairs by expert (stable: ascending pair id within an expert), the routing step
+ * the grouped GEMM reads. topk_ids [T][topk] int32 (device); expert_offsets [E+1] int32:
+ * pairs of expert e are sorted_pairs[expert_offsets[e] .. expert_offsets[e+1]);
+ * sorted_pairs [T*topk] int32. An id outside [0, E) goes after every expert (beyond
+ * expert_offsets[E]) and its pair is never computed. 1 <= E <= 1023; workspace of
+ * bfq_moe_align_workspace_bytes bytes (may be NULL when that is 0). Asynchronous. */
+size_t     bfq_moe_align_workspace_bytes(int64_t T, int32_t topk, int32_t E);
+bfq_status bfq_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                         int32_t* expert_offsets, int32_t* sorted_pairs, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Tile of the grouped GEMM: the (E, N, K, dtype, weight layout, scale format) table entry,
+ * bucket nearest to the token count T; else a default rule from the average rows per active
+ * expert and BFQ_WARN_DEFAULT_TILE. Batch-invariant mode applies as in bfq_select_tile. */
+bfq_status bfq_moe_select_tile(int64_t T, int32_t topk, int32_t E, int64_t N, int64_t K,
+                               const int32_t block_shape[2], bfq_dtype in_dtype,
+                               bfq_dtype out_dtype, bfq_weight_layout w_layout,
+                               bfq_scale_format scale_fmt, bfq_tile* tile_out);
+/* split_k * T * topk * N * 4 bytes when the tile's split_k > 1, else 0. */
+size_t     bfq_moe_gemm_workspace_bytes(int64_t T, int32_t topk, int64_t N, const bfq_tile* tile);
+
+/* Grouped GEMM over the expert groups of bfq_moe_align.
+ *   a_q [T][K] codes and a_scales (a_layout/a_scale_ld over the T tokens; packed UE8M0 words
+ *   allowed) as bfq_quant_tokens writes them: each pair's token row is gathered in the kernel;
+ *   sorted_pairs, expert_offsets: bfq_moe_align's output (device);
+ *   w_q [E][N][K] codes in w_layout (each expert's [N][K] matrix row-major, or packed by
+ *   bfq_pack_weights, one after the other); w_scales [E][N/128][K/128];
+ *   out [T*topk][N] in pair order; rows of pairs with an expert outside [0, E) are not written
+ *   with split_k = 1 and are unspecified with split_k > 1.
+ *   tile NULL -> bfq_moe_select_tile. Variants 0 and 1 (grouped forms); T * K < 2^31. */
+bfq_status bfq_moe_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
+                              int64_t a_scale_ld, const int32_t* sorted_pairs,
+                              const int32_t* expert_offsets, int32_t topk, const void* w_q,
+                              const float* w_scales, bfq_weight_layout w_layout,
+                              bfq_scale_format scale_fmt, void* out, int64_t T, int64_t N,
+                              int64_t K, int32_t E, const int32_t block_shape[2] /* host */,
+                              bfq_dtype in_dtype, bfq_dtype out_dtype,
+                              const bfq_tile* tile /* host */, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Compiled grouped kernels usable for (w_layout, scale_fmt) (e4m3fn; split_k = 1). */
+int32_t    bfq_moe_num_tile_candidates(bfq_weight_layout w_layout, bfq_scale_format scale_fmt);
+bfq_status bfq_moe_get_tile_candidate(bfq_weight_layout w_layout, bfq_scale_format scale_fmt,
+                                      int32_t index, bfq_tile* tile_out);
+
 const char* bfq_status_string(bfq_status s);
 const char* bfq_last_error(void);
 

@@ -492,3 +492,97 @@ def test_packed_scales_every_ue8m0_tile_has_a_kernel(bfq, tmp_path, wl):
     for t in tiles:
         assert _gemm(bfq, M=0, N=24576, a_layout=P, a_scale_ld=0, scale_fmt=sf, w_layout=wl,
                      tile=ctypes.pointer(t)) >= 0, t.as_dict()
+
+
+# ------------------------------------------------------------------ MoE grouped GEMM
+
+def _moe(bfq, **kw):
+    a = dict(a_q=FAKE, a_scales=FAKE, a_layout=0, a_scale_ld=56, sorted_pairs=FAKE,
+             expert_offsets=FAKE, topk=8, w_q=FAKE, w_scales=FAKE, w_layout=0, scale_fmt=0,
+             out=FAKE, T=0, N=4096, K=7168, E=256, block_shape=BS, in_dtype=bfq.BFQ_E4M3FN,
+             out_dtype=bfq.BFQ_BF16, tile=None, workspace=None, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return bfq.lib.bfq_moe_block_gemm(*a.values())
+
+
+def test_moe_validation_without_launch(bfq):
+    assert _moe(bfq) >= 0                                          # T = 0: nothing launched
+    assert _moe(bfq, T=4, a_q=None) == bfq.BFQ_ERR_NULL
+    assert _moe(bfq, expert_offsets=None) == bfq.BFQ_ERR_NULL
+    assert _moe(bfq, in_dtype=bfq.BFQ_INT8) == bfq.BFQ_ERR_DTYPE
+    assert _moe(bfq, block_shape=_bs(1, 7168)) == bfq.BFQ_ERR_SHAPE
+    assert _moe(bfq, E=0) == bfq.BFQ_ERR_SHAPE
+    assert _moe(bfq, E=1024) == bfq.BFQ_ERR_SHAPE
+    assert _moe(bfq, topk=0) == bfq.BFQ_ERR_SHAPE
+    assert _moe(bfq, N=1000) == bfq.BFQ_ERR_SHAPE
+    assert _moe(bfq, T=300000) == bfq.BFQ_ERR_SHAPE               # T * K >= 2^31
+    assert _moe(bfq, a_scale_ld=10) == bfq.BFQ_ERR_SHAPE
+    assert _moe(bfq, T=64, a_layout=1, a_scale_ld=63) == bfq.BFQ_ERR_SHAPE
+    assert _moe(bfq, a_layout=2, a_scale_ld=0) == bfq.BFQ_ERR_ARG  # packed needs UE8M0
+    assert _moe(bfq, a_layout=2, a_scale_ld=0, scale_fmt=1) >= 0
+    assert _moe(bfq, sorted_pairs=FAKE + 2, T=4) == bfq.BFQ_ERR_ALIGN
+    dense = bfq.bfq_get_tile_candidate(0)
+    dense.variant = 2                                              # no grouped stream-K
+    assert _moe(bfq, T=4, tile=ctypes.pointer(dense)) == bfq.BFQ_ERR_TILE
+    t = bfq.bfq_moe_get_tile_candidate(0)
+    t.split_k = 2
+    assert _moe(bfq, T=4, tile=ctypes.pointer(t)) == bfq.BFQ_ERR_WORKSPACE
+    al = bfq.lib.bfq_moe_align
+    assert al(FAKE, 4, 8, 0, FAKE, FAKE, FAKE, 1 << 20, None) == bfq.BFQ_ERR_SHAPE
+    assert al(FAKE, 4, 8, 256, None, FAKE, FAKE, 1 << 20, None) == bfq.BFQ_ERR_NULL
+    assert al(FAKE, 4, 8, 256, FAKE, FAKE, None, 0, None) == bfq.BFQ_ERR_WORKSPACE
+    assert bfq.lib.bfq_moe_align_workspace_bytes(4096, 8, 256) == 257 * 32 * 4
+
+
+@pytest.mark.parametrize("wl", [0, 1])
+def test_moe_candidates_default_and_invariant_tiles(bfq, tmp_path, wl):
+    """Grouped kernels exist for both layouts; the default rule and the batch-invariant mode
+    name compiled grouped kernels for every token count, fp32 / UE8M0 / packed scales."""
+    for sf in (0, 1):
+        n = bfq.bfq_moe_num_tile_candidates(wl, sf)
+        cands = [bfq.bfq_moe_get_tile_candidate(i, wl, sf) for i in range(n)]
+        assert n >= 10 and {t.variant for t in cands} == {0, 1}
+        assert len({tuple(t.as_dict().values()) for t in cands}) == n
+    p = tmp_path / "empty.json"
+    p.write_text(_table([]))
+    bfq.bfq_load_tile_table(str(p))
+    try:
+        for inv in (False, True):
+            bfq.bfq_set_batch_invariant(inv)
+            for sf, lay, ld in ((0, 0, 56), (1, 0, 56), (1, 2, 0)):
+                for T in (1, 4, 32, 128, 512, 2048, 4096, 16384):
+                    st, t = bfq.bfq_moe_select_tile(T, 8, 256, 4096, 7168, w_layout=wl, scale_fmt=sf)
+                    assert st == (bfq.BFQ_OK if inv else bfq.BFQ_WARN_DEFAULT_TILE)
+                    assert t.split_k == 1 and t.variant in (0, 1)
+                    assert _moe(bfq, w_layout=wl, scale_fmt=sf, a_layout=lay, a_scale_ld=ld,
+                                tile=ctypes.pointer(t)) >= 0, (inv, sf, lay, T, t.as_dict())
+    finally:
+        bfq.bfq_set_batch_invariant(False)
+        bfq.bfq_load_tile_table(None)
+
+
+def test_table_moe_key(bfq, tmp_path):
+    """An entry with "E" serves grouped selection for that expert count only (buckets are
+    token counts); its tiles must name grouped kernels."""
+    tm = bfq.bfq_moe_get_tile_candidate(3).as_dict()
+    p = tmp_path / "t.json"
+    p.write_text(_table([{"N": 4096, "K": 7168, "dtype": "fp8_w8a8", "E": 256,
+                          "configs": {"64": tm, "1024": dict(tm, split_k=2)}}]))
+    try:
+        assert bfq.bfq_load_tile_table(str(p)) == bfq.BFQ_OK
+        st, t = bfq.bfq_moe_select_tile(70, 8, 256, 4096, 7168)
+        assert st == bfq.BFQ_OK and t.as_dict() == dict(tm, bk=128)
+        st, t = bfq.bfq_moe_select_tile(900, 8, 256, 4096, 7168)
+        assert st == bfq.BFQ_OK and t.split_k == 2
+        assert bfq.bfq_moe_select_tile(70, 8, 128, 4096, 7168)[0] == bfq.BFQ_WARN_DEFAULT_TILE
+        assert bfq.bfq_select_tile(70, 4096, 7168)[0] == bfq.BFQ_WARN_DEFAULT_TILE   # dense
+    finally:
+        bfq.bfq_load_tile_table(None)
+    bad = tmp_path / "bad.json"
+    stream_k = next(bfq.bfq_get_tile_candidate(i).as_dict() for i in range(bfq.bfq_num_tile_candidates())
+                    if bfq.bfq_get_tile_candidate(i).variant == 2)
+    bad.write_text(_table([{"N": 4096, "K": 7168, "dtype": "fp8_w8a8", "E": 256,
+                            "configs": {"64": stream_k}}]))
+    with pytest.raises(bfq.BfqError):
+        bfq.bfq_load_tile_table(str(bad))
+    bfq.bfq_load_tile_table(None)
