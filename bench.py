@@ -42,6 +42,11 @@ WORKLOADS = {
     "int8": {"shapes": [(1536, 7168)], "M": [1, 16, 128, 1024, 4096], "qtype": "int8",
              "desc": "int8_w8a8 block variant N=1536 K=7168"},
     "tiny": {"shapes": [(1536, 1536)], "M": [8], "qtype": "fp8", "desc": "M=8 N=1536 K=1536"},
+    "moe": {"kind": "moe", "E": 256, "topk": 8, "shapes": [(4096, 7168)], "M": M_GRID,
+            "qtype": "fp8",
+            "desc": "MoE grouped block-FP8, DeepSeek-V3 routed experts E=256 top-8, gate+up "
+                    "N=4096 K=7168, tokens T over the 18-point grid: token-group quant + routing "
+                    "sort + grouped GEMM per T (uniform synthetic routing)"},
 }
 
 
@@ -292,6 +297,213 @@ def run_gpu(args, wl):
     }
 
 
+def run_gpu_moe(args, wl):
+    """The grouped (MoE) workload: per token count T, quantize T tokens, sort their top-k
+    routes by expert, run the grouped GEMM. Expert weights are drawn and quantized on the
+    device before timing (offline, like the dense weights); launches rotate over
+    args.rotate copies of the 7.5 GB expert stack."""
+    import torch
+
+    from block_scaled_w8a8_amd import bfq, perf, synth
+
+    dev = torch.device("cuda:0")
+    E, topk = wl["E"], wl["topk"]
+    (N, K), = wl["shapes"]
+    wlay = bfq.BFQ_W_PACKED16 if args.w_layout == "packed" else bfq.BFQ_W_ROW_MAJOR
+    sfmt = bfq.BFQ_SCALE_UE8M0 if args.scales == "ue8m0" else bfq.BFQ_SCALE_FP32
+    if args.scales == "channel":
+        raise SystemExit("the grouped GEMM takes block scales")
+    t_max = max(wl["M"])
+    log(f"[bench] moe setup: {E} experts of N={N} K={K}, {args.rotate} copies")
+    copies = []
+    for r in range(args.rotate):
+        qw = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+        sw = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
+        for e in range(E):
+            q, s_ = bfq.quant_weight_blocks(synth.expert_weight_on(dev, e, N, K, seed=0),
+                                            scale_fmt=sfmt)
+            qw[e].copy_(q)
+            sw[e].copy_(s_)
+        if wlay == bfq.BFQ_W_PACKED16:
+            qw = bfq.pack_weights(qw)
+        copies.append((qw, sw))
+    torch.cuda.synchronize()
+    x = synth.activations(t_max, K, seed=0)
+    ids_host = synth.routing(t_max, E, topk, seed=0)
+    xd, ids = x.to(dev), ids_host.to(dev)
+    qa = torch.empty((t_max, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((K // 128, t_max), dtype=torch.float32, device=dev)   # column-major
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    srt = torch.empty(t_max * topk, dtype=torch.int32, device=dev)
+    aws = torch.empty(max(int(bfq.lib.bfq_moe_align_workspace_bytes(t_max, topk, E)), 16),
+                      dtype=torch.uint8, device=dev)
+    out = torch.empty((t_max * topk, N), dtype=torch.bfloat16, device=dev)
+    plans = []
+    for T in wl["M"]:
+        st, tile = bfq.bfq_moe_select_tile(T, topk, E, N, K, bfq.BFQ_BF16, wlay, sfmt)
+        plans.append((T, tile, bfq.bfq_moe_gemm_workspace_bytes(T, topk, N, tile), st))
+    ws_max = max(p_[2] for p_ in plans)
+    ws = torch.empty(max(ws_max, 16), dtype=torch.uint8, device=dev)
+    col = bfq.BFQ_SCALES_COL_MAJOR
+    counter = [0]
+
+    def q_once(T):
+        bfq.bfq_quant_tokens(xd[:T], qa[:T], sa, layout=col, scale_ld=t_max, scale_fmt=sfmt)
+
+    def a_once(T):
+        bfq.bfq_moe_align(ids[:T], E, off, srt, workspace=aws)
+
+    def g_once(T, tile, i):
+        qw, sw = copies[i % len(copies)]
+        bfq.bfq_moe_block_gemm(qa[:T], sa, srt, off, topk, qw, sw, out[:T * topk], a_layout=col,
+                               a_scale_ld=t_max, tile=tile, workspace=ws, workspace_bytes=ws_max,
+                               w_layout=wlay, scale_fmt=sfmt)
+
+    def one_step():
+        for (T, tile, _b, _st) in plans:
+            q_once(T)
+            a_once(T)
+            g_once(T, tile, counter[0])
+            counter[0] += 1
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    counter[0] = 0
+    with torch.cuda.graph(graph):
+        one_step()
+    torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stream = torch.cuda.current_stream()
+    R = args.launch_reps
+    rows, groups = [], {}
+    flops_step = 0.0
+    for (T, tile, _b, st) in plans:
+        res = {}
+        for name, fn in (("q", lambda i: q_once(T)), ("a", lambda i: a_once(T)),
+                         ("g", lambda i: g_once(T, tile, i))):
+            fn(0)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for i in range(R):
+                    fn(i)
+            gr.replay()
+            torch.cuda.synchronize()
+            vals = []
+            for _ in range(args.launch_rounds):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                gr.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                vals.append(e0.elapsed_time(e1) * 1e-3 / R)
+            del gr
+            res[name] = sum(vals) / len(vals)
+        P = T * topk
+        active = len(set(ids_host[:T].reshape(-1).tolist()))
+        flops = perf.gemm_flops(P, N, K)
+        byts = perf.moe_gemm_bytes(T, topk, active, N, K)
+        flops_step += flops
+        g = res["g"]
+        rows.append({"T": T, "pairs": P, "active_experts": active, "tile": tile.as_dict(),
+                     "tuned": st == 0, "gemm_us": round(g * 1e6, 2),
+                     "quant_us": round(res["q"] * 1e6, 2), "align_us": round(res["a"] * 1e6, 2),
+                     "tflops": round(flops / g / 1e12, 2), "gbs_all": round(byts / g / 1e9, 1),
+                     "roofline_frac": round(max(byts / (perf.HBM_PEAK_GBS * 1e9),
+                                                flops / (perf.FP8_PEAK_TFLOPS * 1e12)) / g, 4)})
+        key = tile_key(tile)
+        gr_ = groups.setdefault(key, {"t": 0.0, "flops": 0.0, "bytes": 0.0, "n": 0,
+                                      "name": moe_kernel_name(tile, wlay)})
+        gr_["t"] += g
+        gr_["flops"] += flops
+        gr_["bytes"] += byts
+        gr_["n"] += 1
+    dom_key = max(groups, key=lambda k: groups[k]["t"])
+    dom = groups[dom_key]
+    if dom["flops"] / (perf.FP8_PEAK_TFLOPS * 1e12) >= dom["bytes"] / (perf.HBM_PEAK_GBS * 1e9):
+        a_ = dom["flops"] / dom["t"] / 1e12
+        roof = {"bound": "mfma", "achieved": round(a_, 2), "peak": perf.FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(a_ / perf.FP8_PEAK_TFLOPS, 4)}
+    else:
+        a_ = dom["bytes"] / dom["t"] / 1e9
+        roof = {"bound": "hbm", "achieved": round(a_, 1), "peak": perf.HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(a_ / perf.HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": None, "kernel": dom["name"], "tile": dom_key,
+                 "avg_launch_us": round(dom["t"] / dom["n"] * 1e6, 2), "launches": dom["n"] * R})
+    step_s = wall / args.steps
+    return {"value": flops_step / step_s / 1e12, "ms_per_step": step_s * 1e3, "rows": rows,
+            "roofline": roof, "host": {"moe": (x, ids_host)}}
+
+
+def moe_kernel_name(t, wl: int) -> str:
+    d = t.as_dict()
+    if d["variant"] == 0:
+        return (f"bfq::gemm_moe_std_kernel<{d['bm']}, {d['bn']}, {d['waves_m']}, {d['waves_n']}, "
+                f"0, 0, {d['sched']}, {wl}>")
+    nwr = d["bn"] // d["waves_n"]
+    kern = "gemm_swapab_lds_kernel" if d["sched"] == 1 else "gemm_swapab_kernel"
+    return (f"bfq::{kern}<{d['bm']}, {nwr}, {d['waves_n']}, {d['waves_m']}, {d['stages']}, "
+            f"0, 0, {wl}, 0, 1>")
+
+
+def cpu_baseline_moe(wl, host, target_s: float, scales: str = "fp32"):
+    """The oracle on a bounded sample of the grouped workload: quantization and grouped GEMM of
+    the first r tokens against their experts' weights (only those experts are drawn and
+    quantized, untimed)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from block_scaled_w8a8_amd import perf, synth
+
+    E, topk = wl["E"], wl["topk"]
+    (N, K), = wl["shapes"]
+    x, ids = host["moe"]
+    sf = oracle.SCALE_UE8M0 if scales == "ue8m0" else oracle.SCALE_FP32
+    xb = synth.bf16_bits(x)
+    cache = {}
+
+    def experts_for(rows):
+        used = list(dict.fromkeys(ids[:rows].reshape(-1).tolist()))
+        for e in used:
+            if e not in cache:
+                cache[e] = oracle.quant_blocks(
+                    synth.expert_weight_on("cuda:0", e, N, K, seed=0).cpu().numpy(), scale_fmt=sf)
+        remap = {e: i for i, e in enumerate(used)}
+        sub = np.vectorize(remap.get)(ids[:rows].numpy()).astype(np.int32)
+        return (np.stack([cache[e][0] for e in used]), np.stack([cache[e][1] for e in used]), sub)
+
+    def run(rows):
+        qw, sw, sub = experts_for(rows)
+        t0 = time.perf_counter()
+        qa, sa = oracle.quant_groups(np.ascontiguousarray(xb[:rows]), scale_fmt=sf)
+        oracle.moe_gemm(qa, sa, sub, qw, sw)
+        return time.perf_counter() - t0
+
+    # a few tokens (their experts are drawn on the device and quantized by the oracle,
+    # untimed), the timed part repeated to about target_s
+    rows = 8
+    run(rows)
+    reps, total = 0, 0.0
+    while total < target_s and reps < 10000:
+        total += run(rows)
+        reps += 1
+    t = total / reps
+    log(f"[bench] cpu baseline (moe): {rows} tokens, {reps} repetitions, {t:.3f} s each")
+    return {"value": perf.gemm_flops(rows * topk, N, K) / t / 1e12, "unit": "TFLOPS",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"quant + grouped GEMM of {rows} tokens x top-{topk} against their experts "
+                      f"(N={N} K={K}), {reps} repetitions, {total:.1f} s"}
+
+
 def traffic_for(args, dom, wl):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 --pmc summary,
     if it was taken on this kernel (same name, same grid sizes, same kernel sources)."""
@@ -373,10 +585,14 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
     wl = WORKLOADS[args.workload]
-    res = run_gpu(args, wl)
+    moe = wl.get("kind") == "moe"
+    if moe and args.rotate == 3:
+        args.rotate = 2          # 2 x 7.5 GB of expert weights already spill the 256 MB cache
+    res = run_gpu_moe(args, wl) if moe else run_gpu(args, wl)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, res["host"], args.cpu_seconds, args.scales)
+        cpu = (cpu_baseline_moe if moe else cpu_baseline)(wl, res["host"], args.cpu_seconds,
+                                                          args.scales)
     line = {
         "metric": METRIC,
         "value": round(res["value"], 3),
@@ -391,6 +607,7 @@ def main():
         "dtype": "fp8_e4m3fn" if wl["qtype"] == "fp8" else "int8",
         "data": "synthetic",
         "config": {"workload": wl["desc"], "shapes_NK": wl["shapes"], "M": wl["M"],
+                   **({"E": wl["E"], "topk": wl["topk"], "M_is": "tokens"} if moe else {}),
                    "block_shape": [1, wl["shapes"][0][1]] if args.scales == "channel" else [128, 128],
                    "out_dtype": "bf16",
                    "weight_copies_rotated": args.rotate,

@@ -64,3 +64,10 @@ def bound(m: int, n: int, k: int, out_bytes: int = 2, channel: bool = False) -> 
     t_mem = gemm_bytes_all(m, n, k, out_bytes, channel) / (HBM_PEAK_GBS * 1e9)
     t_mma = gemm_flops(m, n, k) / (FP8_PEAK_TFLOPS * 1e12)
     return "hbm" if t_mem >= t_mma else "mfma"
+
+
+def moe_gemm_bytes(T: int, topk: int, active: int, N: int, K: int, out_bytes: int = 2) -> float:
+    """Grouped (MoE) GEMM: each active expert's weight codes and block scales once, each
+    token's codes and group scales once, one output row per (token, expert) pair."""
+    return float(active * (N * K + 4 * (N // 128) * (K // 128)) + T * (K + 4 * (K // 128))
+                 + out_bytes * T * topk * N)

@@ -5,6 +5,8 @@
                                              [--w-layout row|packed] [--out PATH]
   python -m block_scaled_w8a8_amd.sweep run   --M 4096 --N 24576 --K 7168 [--tile JSON] [--iters 50]
                                              [--w-layout row|packed]
+  python -m block_scaled_w8a8_amd.sweep tune-moe [--E 256 --topk 8 --shape 4096,7168]
+                                             [--w-layout row|packed] [--scales fp32|ue8m0]
   python -m block_scaled_w8a8_amd.sweep copy  [--bytes N]   (byte-counter calibration)
 
 `tune` follows the tuning flow of the config-mechanism page ("vLLM 量化 Kernel 配置机制 ...",
@@ -213,6 +215,149 @@ def tune_shape(N, K, qname, grid, budget_s, w_layout="row", scales="fp32"):
     return results
 
 
+class MoeProblem:
+    """Device buffers of a grouped (MoE) layer: E experts of [N, K] (drawn and quantized on
+    the device), t_max tokens with their routing, sorted per token count on demand."""
+
+    def __init__(self, E, topk, N, K, t_max, w_layout="row", scales="fp32"):
+        import torch
+
+        from . import bfq, synth
+        self.E, self.topk, self.N, self.K = E, topk, N, K
+        dev = torch.device("cuda:0")
+        self.sf = bfq.BFQ_SCALE_UE8M0 if scales == "ue8m0" else bfq.BFQ_SCALE_FP32
+        self.wl = bfq.BFQ_W_PACKED16 if w_layout == "packed" else bfq.BFQ_W_ROW_MAJOR
+        qw = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+        sw = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
+        for e in range(E):
+            q, s_ = bfq.quant_weight_blocks(synth.expert_weight_on(dev, e, N, K, seed=0),
+                                            scale_fmt=self.sf)
+            qw[e].copy_(q)
+            sw[e].copy_(s_)
+        self.qw = bfq.pack_weights(qw) if self.wl == bfq.BFQ_W_PACKED16 else qw
+        self.sw = sw
+        self.qa, self.sa = bfq.quant_tokens(synth.activations(t_max, K, seed=0).to(dev),
+                                            layout=bfq.BFQ_SCALES_COL_MAJOR, scale_fmt=self.sf)
+        self.ids = synth.routing(t_max, E, topk, seed=0).to(dev)
+        self.out = torch.empty((t_max * topk, N), dtype=torch.float32, device=dev)
+        self.ws = None
+        self.ws_bytes = 0
+        torch.cuda.synchronize()
+
+    def route(self, T):
+        from . import bfq
+        self.off, self.srt = bfq.moe_align(self.ids[:T].contiguous(), self.E)
+
+    def launch(self, T, tile):
+        import torch
+
+        from . import bfq
+        need = bfq.bfq_moe_gemm_workspace_bytes(T, self.topk, self.N, tile)
+        if need > self.ws_bytes:
+            self.ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+            self.ws_bytes = need
+        return bfq.bfq_moe_block_gemm(self.qa[:T], self.sa, self.srt, self.off, self.topk, self.qw,
+                                      self.sw, self.out[:T * self.topk],
+                                      a_layout=bfq.BFQ_SCALES_COL_MAJOR, a_scale_ld=self.sa.stride(0),
+                                      tile=tile, workspace=self.ws if need else None,
+                                      workspace_bytes=need, w_layout=self.wl, scale_fmt=self.sf)
+
+    def time_us(self, T, tile, iters=20, reps=3):
+        import torch
+        self.launch(T, tile)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(iters):
+                self.launch(T, tile)
+        g.replay()
+        torch.cuda.synchronize()
+        res = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            res.append(a.elapsed_time(b) * 1e3 / iters)
+        del g
+        return sorted(res)[len(res) // 2]
+
+
+def moe_candidates(wl, sf, T, topk, E, K):
+    """Grouped kernels x split-K {1, 2, 4} (split only while rows per expert are few)."""
+    from . import bfq
+    out = []
+    pairs = T * topk
+    rows = -(-pairs // min(E, pairs))
+    for i in range(bfq.bfq_moe_num_tile_candidates(wl, sf)):
+        t = bfq.bfq_moe_get_tile_candidate(i, wl, sf)
+        if t.variant == 1 and rows > 4 * t.bm:
+            continue
+        if t.variant == 0 and rows <= 16:
+            continue
+        for s in (1, 2, 4):
+            if s > 1 and (rows > 64 or K // 128 // s < 4):
+                continue
+            d = t.as_dict()
+            d["split_k"] = s
+            out.append(bfq.bfq_tile.from_dict(d))
+    return out
+
+
+def cmd_tune_moe(args):
+    import torch
+
+    from . import bfq
+    N, K = (int(v) for v in args.shape.split(","))
+    grid = args.grid or M_GRID
+    prob = MoeProblem(args.E, args.topk, N, K, max(grid), args.w_layout, args.scales)
+    results = {}
+    for T in grid:
+        t0 = time.time()
+        prob.route(T)
+        _, ref_tile = bfq.bfq_moe_select_tile(T, args.topk, args.E, N, K, bfq.BFQ_FP32, prob.wl, prob.sf)
+        prob.launch(T, ref_tile)
+        torch.cuda.synchronize()
+        ref = prob.out[:T * args.topk].clone()
+        best = None
+        for tile in moe_candidates(prob.wl, prob.sf, T, args.topk, args.E, K):
+            if time.time() - t0 > args.budget:
+                break
+            try:
+                prob.launch(T, tile)
+                torch.cuda.synchronize()
+            except bfq.BfqError:
+                continue
+            if not agrees(prob.out[:T * args.topk], ref):
+                log(f"  parity gate rejected {tile.as_dict()} at T={T}")
+                continue
+            us = prob.time_us(T, tile)
+            if best is None or us < best[0]:
+                best = (us, tile)
+        results[T] = (best[0], best[1].as_dict())
+        d = best[1].as_dict()
+        log(f"  moe E={args.E} N={N} K={K} T={T:5d}: {best[0]:9.2f} us  variant={d['variant']} "
+            f"bm={d['bm']} bn={d['bn']} sched={d['sched']} split={d['split_k']} ({time.time() - t0:.1f} s)")
+    table = load_table(args.out)
+    wname = "packed16" if args.w_layout == "packed" else "row_major"
+    entry = {"N": N, "K": K, "dtype": "fp8_w8a8", "block_shape": [128, 128], "E": args.E,
+             "configs": {str(T): {k: v for k, v in t.items() if k != "bk"} for T, (us, t) in results.items()},
+             "us": {str(T): round(us, 3) for T, (us, t) in results.items()}}
+    if wname != "row_major":
+        entry["w_layout"] = wname
+    if args.scales == "ue8m0":
+        entry["scales"] = "ue8m0"
+
+    def key(e):
+        return (e.get("E", 0), e["N"], e["K"], e["dtype"], e.get("w_layout", "row_major"),
+                e.get("scales", "fp32"), e.get("block_shape", [128, 128])[0])
+    table["entries"] = [e for e in table["entries"] if key(e) != key(entry)] + [entry]
+    save_table(args.out, table)
+    print(json.dumps({"table": args.out, "entries": len(table["entries"])}))
+
+
 def load_table(path):
     if os.path.exists(path):
         with open(path) as f:
@@ -236,13 +381,13 @@ def cmd_tune(args):
     dname = "fp8_w8a8" if qname == "fp8" else "int8_w8a8"
     wname = "packed16" if args.w_layout == "packed" else "row_major"
 
-    def key(e):
+    def key(e):   # grouped (E > 0) entries are other keys
         sc = "channel" if e.get("block_shape", [128, 128])[0] == 1 else e.get("scales", "fp32")
-        return (e["N"], e["K"], e["dtype"], e.get("w_layout", "row_major"), sc)
+        return (e["N"], e["K"], e["dtype"], e.get("w_layout", "row_major"), sc, e.get("E", 0))
 
     done = {key(e) for e in table["entries"]}
     for (N, K) in shapes:
-        if (N, K, dname, wname, args.scales) in done and not args.force:
+        if (N, K, dname, wname, args.scales, 0) in done and not args.force:
             log(f"[sweep] N={N} K={K} {dname} {wname} {args.scales}: already in {args.out}, skipped")
             continue
         log(f"[sweep] N={N} K={K} {dname} {wname} {args.scales}")
@@ -257,7 +402,7 @@ def cmd_tune(args):
         if args.scales == "ue8m0":
             entry["scales"] = args.scales
         table["entries"] = [e for e in table["entries"]
-                            if key(e) != (N, K, dname, wname, args.scales)] + [entry]
+                            if key(e) != (N, K, dname, wname, args.scales, 0)] + [entry]
         save_table(args.out, table)
     print(json.dumps({"table": args.out, "entries": len(table["entries"])}))
 
@@ -328,11 +473,20 @@ def main():
     r.add_argument("--layout", default="col", choices=["row", "col"], help="activation scales")
     r.add_argument("--w-layout", default="row", choices=["row", "packed"])
     r.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0", "channel"])
+    tm = sub.add_parser("tune-moe")
+    tm.add_argument("--E", type=int, default=256)
+    tm.add_argument("--topk", type=int, default=8)
+    tm.add_argument("--shape", default="4096,7168", help="N,K of one expert")
+    tm.add_argument("--grid", type=int, nargs="*")
+    tm.add_argument("--out", default=DEFAULT_TABLE)
+    tm.add_argument("--budget", type=float, default=20.0, help="seconds per token count")
+    tm.add_argument("--w-layout", default="row", choices=["row", "packed"])
+    tm.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0"])
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=1 << 30)
     c.add_argument("--iters", type=int, default=3)
     args = ap.parse_args()
-    {"tune": cmd_tune, "run": cmd_run, "copy": cmd_copy}[args.cmd](args)
+    {"tune": cmd_tune, "tune-moe": cmd_tune_moe, "run": cmd_run, "copy": cmd_copy}[args.cmd](args)
 
 
 if __name__ == "__main__":
