@@ -901,6 +901,9 @@ static const KernelEntry kStdKernels[] = {
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8, W_PACKED16),
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8, W_PACKED16),
     BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 0, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 1, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(256, 128, 4, 2, 2, 0, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(256, 128, 4, 2, 2, 1, Q_FP8, W_PACKED16),
     BFQ_STD_ALL_OUT(128, 128, 2, 2, 2, 0, Q_FP8, W_PACKED16),
     BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 0, Q_FP8, W_PACKED16),
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_INT8, W_PACKED16),

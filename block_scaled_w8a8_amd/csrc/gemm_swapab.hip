@@ -650,6 +650,9 @@ static const KernelEntry kSwapabKernels[] = {
     BFQ_SABL_BOTH(64, 16, 6, 2, 4, Q_FP8),
     BFQ_SABL_BOTH(96, 16, 6, 2, 4, Q_FP8),
     BFQ_SABL_BOTH(128, 16, 6, 2, 4, Q_FP8),
+    BFQ_SABL_BOTH(96, 32, 4, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(128, 32, 4, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(128, 32, 6, 1, 4, Q_FP8),
     BFQ_SABL_BOTH(16, 16, 8, 1, 8, Q_INT8),
     BFQ_SABL_BOTH(32, 16, 8, 1, 4, Q_INT8),
     BFQ_SABL_BOTH(64, 16, 8, 1, 4, Q_INT8),
@@ -704,6 +707,9 @@ static const KernelEntry kSwapabKernels[] = {
     BFQ_SAB_CH(16, 16, 1, 4, 4, Q_INT8),
     BFQ_SAB_CH(32, 16, 1, 4, 4, Q_INT8),
     // fp8 block scales read as packed UE8M0 activation-scale words
+    BFQ_SABL_PK(96, 32, 4, 1, 4, Q_FP8),
+    BFQ_SABL_PK(128, 32, 4, 1, 4, Q_FP8),
+    BFQ_SABL_PK(128, 32, 6, 1, 4, Q_FP8),
     BFQ_SABL_PK(16, 16, 8, 1, 8, Q_FP8),
     BFQ_SABL_PK(16, 16, 4, 2, 8, Q_FP8),
     BFQ_SABL_PK(32, 16, 8, 1, 4, Q_FP8),
