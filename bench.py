@@ -294,6 +294,7 @@ def run_gpu(args, wl):
         "rows": rows,
         "roofline": roof,
         "host": host,
+        "batch_invariant": bfq.bfq_get_batch_invariant(),
     }
 
 
@@ -440,7 +441,8 @@ def run_gpu_moe(args, wl):
                  "avg_launch_us": round(dom["t"] / dom["n"] * 1e6, 2), "launches": dom["n"] * R})
     step_s = wall / args.steps
     return {"value": flops_step / step_s / 1e12, "ms_per_step": step_s * 1e3, "rows": rows,
-            "roofline": roof, "host": {"moe": (x, ids_host)}}
+            "roofline": roof, "host": {"moe": (x, ids_host)},
+            "batch_invariant": bfq.bfq_get_batch_invariant()}
 
 
 def moe_kernel_name(t, wl: int) -> str:
@@ -614,6 +616,7 @@ def main():
                    "activation_scale_layout": ("packed_ue8m0_words" if args.scale_layout == "packed"
                                                else args.scale_layout + "_major"),
                    "weight_layout": "packed16" if args.w_layout == "packed" else "row_major",
+                   "batch_invariant": bool(res.get("batch_invariant")),
                    "scales": args.scales},
         "roofline": res["roofline"],
         "cpu_baseline": cpu,

@@ -196,15 +196,17 @@ def test_moe_invalid_expert_rows_untouched(bfq, orc):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("T", [1, 16, 128, 1024, 4096])
-def test_moe_deepseek_config_sampled(bfq, orc, T, layout):
-    """DeepSeek-V3 routed experts at full size (E=256, top-8, gate+up N=4096, K=7168): tokens
-    quantized and routed on the device, weights drawn and quantized on the device; outputs of
-    pairs of three sampled experts checked against the oracle, which re-draws and quantizes
-    those experts itself."""
+@pytest.mark.parametrize("T,N,K", [(1, 4096, 7168), (16, 4096, 7168), (128, 4096, 7168),
+                                   (1024, 4096, 7168), (4096, 4096, 7168),
+                                   (16, 7168, 2048), (1024, 7168, 2048)])
+def test_moe_deepseek_config_sampled(bfq, orc, T, N, K, layout):
+    """DeepSeek-V3 routed experts at full size (E=256, top-8; gate+up N=4096, K=7168 and the
+    down projection N=7168, K=2048): tokens quantized and routed on the device, weights drawn
+    and quantized on the device; outputs of pairs of three sampled experts checked against the
+    oracle, which re-draws and quantizes those experts itself."""
     from oracle import metrics
-    print(f"moe config T={T} {layout}", flush=True)
-    E, topk, N, K = 256, 8, 4096, 7168
+    print(f"moe config T={T} N={N} K={K} {layout}", flush=True)
+    E, topk = 256, 8
     x = synth.activations(T, K, seed=0)
     ids = synth.routing(T, E, topk, seed=0)
     qw = torch.empty((E, N, K), dtype=torch.uint8, device=DEV)
