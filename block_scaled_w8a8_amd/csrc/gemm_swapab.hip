@@ -653,6 +653,7 @@ static const KernelEntry kSwapabKernels[] = {
     BFQ_SABL_BOTH(96, 32, 4, 1, 4, Q_FP8),
     BFQ_SABL_BOTH(128, 32, 4, 1, 4, Q_FP8),
     BFQ_SABL_BOTH(128, 32, 6, 1, 4, Q_FP8),
+    BFQ_SABL_BOTH(64, 32, 6, 2, 4, Q_FP8),
     BFQ_SABL_BOTH(16, 16, 8, 1, 8, Q_INT8),
     BFQ_SABL_BOTH(32, 16, 8, 1, 4, Q_INT8),
     BFQ_SABL_BOTH(64, 16, 8, 1, 4, Q_INT8),
@@ -710,6 +711,7 @@ static const KernelEntry kSwapabKernels[] = {
     BFQ_SABL_PK(96, 32, 4, 1, 4, Q_FP8),
     BFQ_SABL_PK(128, 32, 4, 1, 4, Q_FP8),
     BFQ_SABL_PK(128, 32, 6, 1, 4, Q_FP8),
+    BFQ_SABL_PK(64, 32, 6, 2, 4, Q_FP8),
     BFQ_SABL_PK(16, 16, 8, 1, 8, Q_FP8),
     BFQ_SABL_PK(16, 16, 4, 2, 8, Q_FP8),
     BFQ_SABL_PK(32, 16, 8, 1, 4, Q_FP8),

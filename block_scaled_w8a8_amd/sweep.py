@@ -387,7 +387,9 @@ def cmd_tune(args):
 
     done = {key(e) for e in table["entries"]}
     for (N, K) in shapes:
-        if (N, K, dname, wname, args.scales, 0) in done and not args.force:
+        k0 = (N, K, dname, wname, args.scales, 0)
+        old = next((e for e in table["entries"] if key(e) == k0), None)
+        if k0 in done and not (args.force or args.merge):
             log(f"[sweep] N={N} K={K} {dname} {wname} {args.scales}: already in {args.out}, skipped")
             continue
         log(f"[sweep] N={N} K={K} {dname} {wname} {args.scales}")
@@ -401,8 +403,12 @@ def cmd_tune(args):
             entry["w_layout"] = wname
         if args.scales == "ue8m0":
             entry["scales"] = args.scales
-        table["entries"] = [e for e in table["entries"]
-                            if key(e) != (N, K, dname, wname, args.scales, 0)] + [entry]
+        if args.merge and old is not None:
+            # retuned batch sizes replace theirs; the entry's other M keep their configs
+            for f in ("configs", "us"):
+                merged = dict(old.get(f, {}), **entry[f])
+                entry[f] = {m: merged[m] for m in sorted(merged, key=int)}
+        table["entries"] = [e for e in table["entries"] if key(e) != k0] + [entry]
         save_table(args.out, table)
     print(json.dumps({"table": args.out, "entries": len(table["entries"])}))
 
@@ -459,6 +465,8 @@ def main():
     t.add_argument("--out", default=DEFAULT_TABLE)
     t.add_argument("--budget", type=float, default=20.0, help="seconds per (shape, M)")
     t.add_argument("--force", action="store_true")
+    t.add_argument("--merge", action="store_true",
+                   help="retune only the --grid batch sizes of an existing entry, keep its other M")
     t.add_argument("--w-layout", default="row", choices=["row", "packed"])
     t.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0", "channel"])
     r = sub.add_parser("run")
