@@ -353,9 +353,19 @@ def cmd_tune_moe(args):
     def key(e):
         return (e.get("E", 0), e["N"], e["K"], e["dtype"], e.get("w_layout", "row_major"),
                 e.get("scales", "fp32"), e.get("block_shape", [128, 128])[0])
+    old = next((e for e in table["entries"] if key(e) == key(entry)), None)
+    if args.merge and old is not None:
+        merge_configs(old, entry)
     table["entries"] = [e for e in table["entries"] if key(e) != key(entry)] + [entry]
     save_table(args.out, table)
     print(json.dumps({"table": args.out, "entries": len(table["entries"])}))
+
+
+def merge_configs(old, entry):
+    """Retuned batch sizes of `entry` replace theirs in `old`; old's other sizes are kept."""
+    for f in ("configs", "us"):
+        merged = dict(old.get(f, {}), **entry[f])
+        entry[f] = {m: merged[m] for m in sorted(merged, key=int)}
 
 
 def load_table(path):
@@ -404,10 +414,7 @@ def cmd_tune(args):
         if args.scales == "ue8m0":
             entry["scales"] = args.scales
         if args.merge and old is not None:
-            # retuned batch sizes replace theirs; the entry's other M keep their configs
-            for f in ("configs", "us"):
-                merged = dict(old.get(f, {}), **entry[f])
-                entry[f] = {m: merged[m] for m in sorted(merged, key=int)}
+            merge_configs(old, entry)
         table["entries"] = [e for e in table["entries"] if key(e) != k0] + [entry]
         save_table(args.out, table)
     print(json.dumps({"table": args.out, "entries": len(table["entries"])}))
@@ -490,6 +497,8 @@ def main():
     tm.add_argument("--budget", type=float, default=20.0, help="seconds per token count")
     tm.add_argument("--w-layout", default="row", choices=["row", "packed"])
     tm.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0"])
+    tm.add_argument("--merge", action="store_true",
+                    help="retune only the --grid token counts of an existing entry, keep the rest")
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=1 << 30)
     c.add_argument("--iters", type=int, default=3)
