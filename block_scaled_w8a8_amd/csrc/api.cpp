@@ -294,7 +294,7 @@ bfq_status moe_select_tile(int64_t T, int64_t topk, int64_t E, int64_t N, int64_
     if (batch_invariant()) {
         *out = invariant_tile(active > 0 ? (pairs + active - 1) / active : 1, wlayout, sfmt);
         out->group_m = 1;
-        if (out->variant == 0 && out->bm == 256) {   // largest grouped FMA tile
+        if (out->variant == 0 && out->bm == 256) {   // grouped 256x256 is sched 1 only
             out->bm = 128; out->waves_m = 2;
         }
         return BFQ_OK;

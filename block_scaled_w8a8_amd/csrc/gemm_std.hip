@@ -969,12 +969,15 @@ static const KernelEntry kStreamKKernels[] = {
         BFQ_MOE_STD_ENTRY(BM, BN, WM, WN, SC, QT, O_FP16, W_PACKED16),                     \
         BFQ_MOE_STD_ENTRY(BM, BN, WM, WN, SC, QT, O_FP32, W_PACKED16)
 
-// grouped (MoE) standard tiles, fp8 (the gathered rows cost registers: 256x256 with the FMA
-// schedule spills with packed weights, so 128x256 is the largest FMA tile)
+// grouped (MoE) standard tiles, fp8 (the gathered rows cost registers: 256x256 with sched 0
+// spills with packed weights, the software-pipelined sched 1 fits in 240 VGPRs; it takes
+// large token counts, where one 256-row tile covers each expert's rows and its weights
+// stream once per expert)
 static const KernelEntry kMoeStdKernels[] = {
     BFQ_MOE_STD(128, 256, 2, 2, 0, Q_FP8),
     BFQ_MOE_STD(128, 128, 2, 2, 0, Q_FP8),
     BFQ_MOE_STD(64, 128, 1, 2, 0, Q_FP8),
+    BFQ_MOE_STD(256, 256, 4, 2, 1, Q_FP8),
     BFQ_MOE_STD(256, 256, 4, 2, 3, Q_FP8),
     BFQ_MOE_STD(128, 128, 2, 2, 3, Q_FP8),
 };
