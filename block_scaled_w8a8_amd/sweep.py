@@ -3,10 +3,12 @@
   python -m block_scaled_w8a8_amd.sweep tune  [--shapes N,K ...] [--dtype fp8|int8]
                                              [--scales fp32|ue8m0|channel]
                                              [--w-layout row|packed] [--out PATH]
+                                             [--grid M ...] [--force | --merge]
   python -m block_scaled_w8a8_amd.sweep run   --M 4096 --N 24576 --K 7168 [--tile JSON] [--iters 50]
                                              [--w-layout row|packed]
   python -m block_scaled_w8a8_amd.sweep tune-moe [--E 256 --topk 8 --shape 4096,7168]
                                              [--w-layout row|packed] [--scales fp32|ue8m0]
+                                             [--grid T ...] [--merge]
   python -m block_scaled_w8a8_amd.sweep copy  [--bytes N]   (byte-counter calibration)
 
 `tune` follows the tuning flow of the config-mechanism page ("vLLM 量化 Kernel 配置机制 ...",
@@ -15,7 +17,9 @@
 one whose output agrees with a reference configuration is kept. Configurations the library
 rejects (grid or workspace limits) are skipped, like the page's OutOfResources candidates.
 Results are written to a JSON tile table after every shape, and shapes already present in the
-output file are skipped, so an interrupted sweep resumes where it stopped. Each weight layout
+output file are skipped, so an interrupted sweep resumes where it stopped (--force retunes
+them; --merge retunes only the --grid sizes of an existing entry and keeps its other
+configurations, e.g. after a new kernel is added for some range of M). Each weight layout
 (row-major or packed) and scale format has entries of its own; "channel" is the per-token x
 per-channel format (block_shape [1, K]).
 
