@@ -91,7 +91,12 @@ __device__ __forceinline__ void std_tile(
     constexpr int CHUNKS = (BM + BN) / 8;          // 1 KB load chunks per stage
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert(BM % 16 == 0, "the W region must start on a 16-row boundary");
-    static_assert(128 % TN == 0, "a wave's columns must lie in one 128-wide scale block");
+    // A wave's columns lie in one 128-wide weight-scale block, or (SPLIT_SW: 96-column wave
+    // tiles of 192-wide tiles, fp8 FMA schedules) in at most two adjacent ones: the sub-tiles
+    // before the wave-uniform boundary sn_split take the first block's scale, the rest the next.
+    constexpr bool SPLIT_SW = 128 % TN != 0;
+    static_assert(!SPLIT_SW || (TN == 96 && QT == Q_FP8 && SCHED <= 1 && !MOE),
+                  "a wave's columns must lie in one 128-wide scale block (or 96 of them in two)");
     static_assert(CHUNKS % NWAVES == 0, "load chunks must divide evenly over waves");
     static_assert((BM / 8) % NWAVES == 0, "A chunks must divide evenly over waves");
     static_assert(NWAVES % 2 == 0, "the swizzle phase of a lane's chunks needs an even wave count");
@@ -156,7 +161,13 @@ __device__ __forceinline__ void std_tile(
     const __amdgpu_buffer_rsrc_t rsw = make_rsrc(sw_e + nb0 * KB, (uint32_t)(nbs * KB * 4));
     const uint32_t sw_dma_voff = (uint32_t)(lane * KB * 4);
     const uint32_t sa_lds = (uint32_t)((wm * TM + frow * SM) * 4);
-    const uint32_t sw_lds = (uint32_t)(BM * 4 + ((wn * TN) / 128) * 4);
+    // the wave's first column n0 + wn*TN is a multiple of 32 (n0 of 64), so 16-column
+    // sub-tiles never straddle a scale block
+    const int64_t wcol0 = n0 + (int64_t)wn * TN;
+    const uint32_t sw_lds = SPLIT_SW ? (uint32_t)(BM * 4 + (wcol0 / 128 - nb0) * 4)
+                                     : (uint32_t)(BM * 4 + ((wn * TN) / 128) * 4);
+    const int sn_split = SPLIT_SW ? (int)((128 - wcol0 % 128) / 16) : SN;   // may exceed SN
+    (void)sn_split;
 
     // Load chunk i of this wave covers region rows 8*(wave + NWAVES*i) .. +7; lane l writes
     // LDS slot (l & 7) of row +(l >> 3), which holds global chunk (l & 7) ^ swz(row). As
@@ -251,6 +262,13 @@ __device__ __forceinline__ void std_tile(
 
     auto lds16 = [&](uint32_t off) { return *reinterpret_cast<const v4i*>(lds + off); };
 
+    // SPLIT_SW: c2[sm] is the scale product with the next block's weight scale
+    float c2[SM];
+    auto cs = [&](const float (&c)[SM], int sm, int sn) {
+        if constexpr (SPLIT_SW) return sn < sn_split ? c[sm] : c2[sm];
+        else { (void)sn; return c[sm]; }
+    };
+    (void)cs;
     // One K block on LDS stage `stage`: fragments from LDS, MFMA, scale fusion. c[sm] is the
     // scale product of sub-tile row sm (sched 0-2); ea[sm] and ew the E8M0 exponents of the
     // token and weight scales (sched 3).
@@ -401,7 +419,7 @@ __device__ __forceinline__ void std_tile(
                 for (int sn = 0; sn < SN; ++sn) {
                     const v8i wf = read_w(sn);
 #pragma unroll
-                    for (int sm = 0; sm < SM; ++sm) fma4(acc[sm][sn], mfma_fp8_16x16x128(wf, af[sm]), c[sm]);
+                    for (int sm = 0; sm < SM; ++sm) fma4(acc[sm][sn], mfma_fp8_16x16x128(wf, af[sm]), cs(c, sm, sn));
                 }
             } else {
                 // software-pipelined: MFMAs of sub-tile sn, the read of sn+1, then the scale
@@ -416,11 +434,11 @@ __device__ __forceinline__ void std_tile(
                     if (sn + 1 < SN) wf = read_w(sn + 1);
                     if (sn > 0) {
 #pragma unroll
-                        for (int sm = 0; sm < SM; ++sm) fma4(acc[sm][sn - 1], pb[(sn - 1) & 1][sm], c[sm]);
+                        for (int sm = 0; sm < SM; ++sm) fma4(acc[sm][sn - 1], pb[(sn - 1) & 1][sm], cs(c, sm, sn - 1));
                     }
                 }
 #pragma unroll
-                for (int sm = 0; sm < SM; ++sm) fma4(acc[sm][SN - 1], pb[(SN - 1) & 1][sm], c[sm]);
+                for (int sm = 0; sm < SM; ++sm) fma4(acc[sm][SN - 1], pb[(SN - 1) & 1][sm], cs(c, sm, SN - 1));
 #pragma unroll
                 for (int sn = 0; sn < SN; ++sn) {
                     __builtin_amdgcn_sched_group_barrier(0x008, SM, 0);          // MFMA
@@ -475,7 +493,17 @@ __device__ __forceinline__ void std_tile(
             const float swv = *reinterpret_cast<const float*>(lds + sc + sw_lds);
 #pragma unroll
             for (int sm = 0; sm < SM; ++sm) ea[sm] = 0;
-            if constexpr (SM == 4) {
+            if constexpr (SPLIT_SW) {
+                // the next block's slot is staged whenever the wave reaches into it (else unused)
+                const float swv2 = *reinterpret_cast<const float*>(lds + sc + sw_lds + 4);
+#pragma unroll
+                for (int sm = 0; sm < SM; ++sm) {
+                    const float a = act_scale(*reinterpret_cast<const float*>(lds + sc + sa_lds + sm * 4),
+                                              packed, kb);
+                    c[sm] = a * swv;
+                    c2[sm] = a * swv2;
+                }
+            } else if constexpr (SM == 4) {
                 const v4f sa4 = *reinterpret_cast<const v4f*>(lds + sc + sa_lds);
                 c[0] = act_scale(sa4.x, packed, kb) * swv;
                 c[1] = act_scale(sa4.y, packed, kb) * swv;
@@ -887,6 +915,7 @@ hipError_t launch_moe_std(const GemmArgs& a, hipStream_t stream) {
 static const KernelEntry kStdKernels[] = {
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8, W_ROW),
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8, W_ROW),
+    BFQ_STD_ALL_OUT(256, 192, 4, 2, 2, 0, Q_FP8, W_ROW),
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 3, 1, Q_FP8, W_ROW),
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 2, Q_FP8, W_ROW),
     BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 2, Q_FP8, W_ROW),
@@ -900,6 +929,7 @@ static const KernelEntry kStdKernels[] = {
     BFQ_STD_ALL_OUT(64, 128, 1, 2, 2, 0, Q_INT8, W_ROW),
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 0, Q_FP8, W_PACKED16),
     BFQ_STD_ALL_OUT(256, 256, 4, 2, 2, 1, Q_FP8, W_PACKED16),
+    BFQ_STD_ALL_OUT(256, 192, 4, 2, 2, 0, Q_FP8, W_PACKED16),
     BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 0, Q_FP8, W_PACKED16),
     BFQ_STD_ALL_OUT(128, 256, 2, 2, 2, 1, Q_FP8, W_PACKED16),
     BFQ_STD_ALL_OUT(256, 128, 4, 2, 2, 0, Q_FP8, W_PACKED16),
