@@ -726,19 +726,18 @@ struct SlotIO {
                 for (int q = 0; q < NQ; ++q)
                     buf_store_v4f(r, piece(acc[sm][sn], q), voff, (uint32_t)(((sm * SN + sn) * NQ + q) * NT * 16));
     }
-    // acc = slot (first) or acc + slot
-    static __device__ __forceinline__ void add(float* slots, int64_t slot, bool first, AccT (&acc)[SM][SN]) {
+    // row band sm of the tile: acc_row = slot (first) or acc_row + slot
+    static __device__ __forceinline__ void add_row(float* slots, int64_t slot, bool first, int sm,
+                                                   AccT (&acc_row)[SN]) {
         const __amdgpu_buffer_rsrc_t r = rsrc(slots, slot);
         const uint32_t voff = threadIdx.x * 16;
 #pragma unroll
-        for (int sm = 0; sm < SM; ++sm)
+        for (int sn = 0; sn < SN; ++sn)
 #pragma unroll
-            for (int sn = 0; sn < SN; ++sn)
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) {
-                    const v4f v = buf_load_v4f(r, voff, (uint32_t)(((sm * SN + sn) * NQ + q) * NT * 16));
-                    set_piece(acc[sm][sn], q, first ? v : piece(acc[sm][sn], q) + v);
-                }
+            for (int q = 0; q < NQ; ++q) {
+                const v4f v = buf_load_v4f(r, voff, (uint32_t)(((sm * SN + sn) * NQ + q) * NT * 16));
+                set_piece(acc_row[sn], q, first ? v : piece(acc_row[sn], q) + v);
+            }
     }
 };
 
@@ -790,30 +789,58 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_streamk_kernel(GemmArgs p) 
     }
 }
 
-// One workgroup per stream-K tile: a tile split over several workgroups is summed from their
-// parked slots in K order (ascending owner) and stored; a tile one workgroup covered whole
-// was stored by it already. Same block shape as the GEMM, so each thread reads back exactly
-// the accumulator pieces it will store.
+// One workgroup per (stream-K tile, sub-tile row band sm = blockIdx.y): a tile split over
+// several workgroups is summed from their parked slots in K order (ascending owner) and
+// stored, one band of SM per workgroup so the sum fills the chip; a tile one workgroup covered
+// whole was stored by it already. Same block shape as the GEMM, so each thread reads back
+// exactly the accumulator pieces it will store.
 template <int BM, int BN, int WM, int WN, int OT, int SCHED>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_streamk_fixup_kernel(GemmArgs p, int grid) {
     using Shape = StdShape<BM, BN, WM, WN, SCHED>;
     using IO = SlotIO<BM, BN, WM, WN, SCHED>;
+    constexpr int TM = Shape::TM, TN = Shape::TN, MF = Shape::MF, SN = Shape::SN;
     const int64_t M = p.M, N = p.N, KB = p.K / 128;
     const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const int64_t tiles = tiles_m * tiles_n;
     const int64_t ts = blockIdx.x;
+    const int sm = blockIdx.y;
     const int64_t I = (tiles - p.dp_tiles) * KB;
     const int64_t Gs = I < grid ? I : grid;
     const int64_t w_first = sk_owner(ts * KB, Gs, I), w_last = sk_owner(ts * KB + KB - 1, Gs, I);
     if (w_first == w_last) return;
-    typename Shape::AccT acc[Shape::SM][Shape::SN];
+    typename Shape::AccT acc[SN];
     for (int64_t ws = w_first; ws <= w_last; ++ws) {
         const int sl = ts == (ws * I / Gs) / KB ? 0 : 1;
-        IO::add(p.sk_slots, ws * 2 + sl, ws == w_first, acc);
+        IO::add_row(p.sk_slots, ws * 2 + sl, ws == w_first, sm, acc);
     }
     int64_t pm, pn;
     tile_coords(p.dp_tiles + ts, tiles_m, tiles_n, p.group_m, p.raster, pm, pn);
-    std_store<OT, BM, BN, WM, WN, SCHED>(p.out, 0, M, N, pm * BM, pn * BN, acc);
+    // the rows of band sm, as std_store writes them
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int frow = lane & (MF - 1), fgrp = lane >> 4, khalf = lane >> 5;
+    const int64_t m = pm * BM + wm * TM + sm * MF + frow;
+    if (m >= M) return;
+    const int64_t n0 = pn * BN + wn * TN;
+#pragma unroll
+    for (int sn = 0; sn < SN; ++sn) {
+        if constexpr (MF == 32) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t n = n0 + sn * 32 + 8 * j + 4 * khalf;
+                if (n >= N) continue;
+                const auto& a = acc[sn];
+                const v4f v = {a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]};
+                store4<OT>(p.out, m * N + n, v);
+            }
+        } else {
+            (void)khalf;
+            const int64_t n = n0 + sn * 16 + 4 * fgrp;
+            if (n >= N) continue;
+            store4<OT>(p.out, m * N + n, acc[sn]);
+        }
+    }
 }
 
 // Whole rounds first; only the tiles of the last, partial round are split (each split tile
@@ -862,7 +889,8 @@ hipError_t launch_streamk(const GemmArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || tiles == b.dp_tiles) return e;
     hipLaunchKernelGGL((gemm_streamk_fixup_kernel<BM, BN, WM, WN, OT, SCHED>),
-                       dim3((unsigned)(tiles - b.dp_tiles)), dim3(64 * WM * WN), 0, stream, b, (int)grid);
+                       dim3((unsigned)(tiles - b.dp_tiles), (unsigned)StdShape<BM, BN, WM, WN, SCHED>::SM),
+                       dim3(64 * WM * WN), 0, stream, b, (int)grid);
     return hipGetLastError();
 }
 
