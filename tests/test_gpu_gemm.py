@@ -92,6 +92,37 @@ def _check_fp32(orc_metrics, out, ref, what):
     assert r["ok"], (what, r)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_sampled(bfq, orc, seed):
+    """Seeded random shapes (M in [1, 700), N and K random multiples of 128, so M and N end in
+    ragged tiles of every kernel family), both weight layouts, both scale formats and both
+    code types: the library's own tile choice and a random compiled candidate with a random
+    split, fp32 out, sampled against the oracle."""
+    from oracle import metrics
+    rng = np.random.default_rng(1000 + seed)
+    M = int(rng.integers(1, 700))
+    N = 128 * int(rng.integers(1, 25))
+    K = 128 * int(rng.integers(1, 33))
+    layout, sfmt = LAYOUTS[seed % 2], (seed // 2) % 2
+    qname = "int8" if seed >= 6 else "fp8"
+    qd = bfq.BFQ_INT8 if qname == "int8" else bfq.BFQ_E4M3FN
+    qt = orc.INT8 if qname == "int8" else orc.FP8
+    print(f"random shape M={M} N={N} K={K} {layout} sfmt={sfmt} {qname}", flush=True)
+    host = _case(orc, M, N, K, 31 + seed, qt, sfmt)
+    dq = _to_dev(*host, layout=layout, sfmt=sfmt)
+    ms = np.concatenate([rng.integers(0, M, 400), [0, M - 1, M - 1]])
+    ns = np.concatenate([rng.integers(0, N, 400), [0, N - 1, 0]])
+    ref = orc.block_gemm_sampled(*host, ms, ns, qtype=qt)
+    cands = _candidates(bfq, qd, layout, sfmt)
+    t = cands[int(rng.integers(0, len(cands)))]
+    split = 1 if t.variant == 2 else int(rng.integers(1, min(4, K // 128) + 1))
+    for tile in (None, _with_split(t, split)):
+        what = (M, N, K, layout, sfmt, qname, tile.as_dict() if tile is not None else "selected")
+        o = _run(bfq, dq, torch.float32, tile=tile).cpu().numpy()
+        r = metrics.gemm_fp32_report(o[ms, ns], ref)
+        assert r["ok"], (what, r)
+
+
 @pytest.mark.parametrize("sfmt", [0, 1])
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("qname", ["fp8", "int8"])
