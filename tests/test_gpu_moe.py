@@ -128,6 +128,36 @@ def test_moe_every_candidate_and_split(bfq, orc, layout, sfmt):
             assert np.array_equal(o16, orc.f32_to_bf16_bits_array(o32)), what
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_moe_random_shapes_sampled(bfq, orc, seed):
+    """Seeded random grouped problems (T in [1, 600), E in [2, 64], top-k up to 8, N and K
+    random multiples of 128), both weight layouts and scale formats: the library's own tile
+    choice and a random grouped candidate with a random split, sampled against the oracle."""
+    from oracle import metrics
+    rng = np.random.default_rng(2000 + seed)
+    T = int(rng.integers(1, 600))
+    E = int(rng.integers(2, 65))
+    topk = int(rng.integers(1, min(8, E) + 1))
+    N = 128 * int(rng.integers(1, 13))
+    K = 128 * int(rng.integers(1, 17))
+    layout, sfmt = LAYOUTS[seed % 2], (seed // 2) % 2
+    print(f"moe random T={T} E={E} topk={topk} N={N} K={K} {layout} sfmt={sfmt}", flush=True)
+    host = _moe_host(orc, T, E, topk, N, K, 61 + seed, sfmt)
+    d = _moe_dev(bfq, *host, layout, E)
+    qs = np.concatenate([rng.integers(0, T * topk, 400), [0, T * topk - 1]])
+    ns = np.concatenate([rng.integers(0, N, 400), [N - 1, 0]])
+    ref = orc.moe_gemm_sampled(*host, qs, ns)
+    wl = _wl(bfq, layout)
+    cands = [bfq.bfq_moe_get_tile_candidate(i, wl, sfmt)
+             for i in range(bfq.bfq_moe_num_tile_candidates(wl, sfmt))]
+    t = cands[int(rng.integers(0, len(cands)))]
+    for tile in (None, _with_split(t, int(rng.integers(1, min(2, K // 128) + 1)))):
+        what = (T, E, topk, N, K, layout, sfmt, tile.as_dict() if tile is not None else "selected")
+        o = _moe_run(bfq, d, torch.float32, tile, layout, sfmt).cpu().numpy()
+        r = metrics.gemm_fp32_report(o[qs, ns], ref)
+        assert r["ok"], (what, r)
+
+
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_moe_scale_layouts(bfq, orc, layout):
     """Column-major (padded ld) and packed UE8M0 activation scales give bitwise the result of
