@@ -225,3 +225,53 @@ def test_quant_tokens_packed_special_values(bfq, orc):
     qo, so = orc.quant_groups(bits, scale_fmt=orc.SCALE_UE8M0)
     assert np.array_equal(words.cpu().numpy().view(np.uint32), orc.pack_scales_ue8m0(so))
     assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def _reciprocal_straddles(orc, qmax, encode, want=24, trials=20000, seed=5):
+    """(amax, x) bf16 pairs for which the code of x * fl(1/s) differs from the code of the IEEE
+    quotient x / s (s = fl(amax / qmax)): the products land on the other side of a rounding
+    midpoint. Found by search over every positive bf16 x <= amax, all in numpy float32."""
+    rng = np.random.default_rng(seed)
+    allx = ((np.arange(1, 0x7F80, dtype=np.uint32)) << 16).view(np.float32)
+    hits = []
+    for _ in range(trials):
+        amax = np.float32(np.ldexp(rng.uniform(1.0, 2.0), int(rng.integers(-30, 30))))
+        amax = (np.array([amax]).view(np.uint32) & 0xFFFF0000).view(np.float32)[0]   # a bf16
+        s = np.float32(amax) / np.float32(qmax)
+        xs = allx[allx <= amax]
+        q = xs / s
+        p = xs * (np.float32(1.0) / s)
+        bad = np.nonzero(encode(q) != encode(p))[0]
+        hits += [(amax, xs[i]) for i in bad[:2]]
+        if len(hits) >= want:
+            break
+    return hits
+
+
+@pytest.mark.parametrize("qname", ["fp8", "int8"])
+def test_quant_tokens_quotients_near_rounding_midpoints(bfq, orc, qname):
+    """Groups built so that a reciprocal-multiply would round some elements to the wrong
+    code (the values straddle a rounding midpoint between x * (1/s) and x / s): the device
+    codes still equal the oracle's IEEE-quotient codes bit for bit."""
+    qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
+    ot = orc.FP8 if qname == "fp8" else orc.INT8
+    qmax = 448.0 if qname == "fp8" else 127.0
+    enc = orc.e4m3_encode_array if qname == "fp8" else orc.int8_encode_array
+    hits = _reciprocal_straddles(orc, qmax, enc)
+    assert len(hits) >= 8, len(hits)
+    rng = np.random.default_rng(9)
+    G = 4
+    rows = (len(hits) + G - 1) // G
+    x = np.zeros((rows, G * 128), dtype=np.float32)
+    for i, (amax, v) in enumerate(hits):
+        grp = x[i // G, (i % G) * 128:(i % G + 1) * 128]
+        grp[:] = rng.uniform(-1.0, 1.0, 128).astype(np.float32) * amax * 0.9
+        grp[0] = amax
+        sign = -1.0 if i % 2 else 1.0
+        grp[1 + (i % 127)] = sign * v
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    assert float(xt.float().abs().max()) > 0
+    qg, sg = _gpu_quant_tokens(bfq, xt, qd, bfq.BFQ_SCALES_COL_MAJOR)
+    qo, so = orc.quant_groups(synth.bf16_bits(xt), qtype=ot)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(qg.view(np.uint8), qo.view(np.uint8))
