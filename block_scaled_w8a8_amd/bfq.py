@@ -174,6 +174,128 @@ def _ptr(t) -> int:
     return t.data_ptr()
 
 
+# ------------------------------------------------------------------ argument checks
+# The kernels take raw device addresses and assume the layouts stated in include/bfq.h (rows
+# of codes and outputs packed at stride K or N, scales at the stated leading dimension). The
+# wrappers below check every tensor against those assumptions before the C call, so that a
+# host tensor, a strided view or a buffer of the wrong size raises here instead of handing a
+# kernel an address it would read or write past. Order: type, dtype, shape, strides, device
+# (a tensor that passes all but the device check is a host tensor). Plain int addresses are
+# passed through unchecked: the caller vouches for them.
+
+class BfqArgumentError(ValueError):
+    """A tensor argument does not match what the kernel will read or write."""
+
+
+U8_CODES = ("uint8", "float8_e4m3fn")
+
+
+def _dt(t) -> str:
+    return str(t.dtype).replace("torch.", "")
+
+
+def _tensor(t, name, dtypes):
+    if isinstance(t, int):
+        return False
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise BfqArgumentError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if _dt(t) not in dtypes:
+        raise BfqArgumentError(f"{name} has dtype {_dt(t)}; expected one of {', '.join(dtypes)}")
+    return True
+
+
+def _devices(**tensors):
+    """Last check of a wrapper: every tensor argument is on the current GPU."""
+    for name, t in tensors.items():
+        if t is not None and not isinstance(t, int):
+            _on_device(t, name)
+
+
+def _on_device(t, name):
+    import torch
+    if not t.is_cuda:
+        raise BfqArgumentError(f"{name} is on device {t.device}; the kernels need a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise BfqArgumentError(f"{name} is on {t.device}, not the current device "
+                               f"cuda:{torch.cuda.current_device()}")
+
+
+def _rows(t, name, dtypes, rows, cols):
+    """A [rows, cols] matrix whose rows are packed at stride cols (what the kernels index)."""
+    if not _tensor(t, name, dtypes):
+        return
+    if t.dim() != 2 or tuple(t.shape) != (rows, cols):
+        raise BfqArgumentError(f"{name} has shape {tuple(t.shape)}; expected ({rows}, {cols})")
+    if rows > 0 and cols > 0 and (t.stride(1) != 1 or (rows > 1 and t.stride(0) != cols)):
+        raise BfqArgumentError(f"{name} has strides {t.stride()}; its rows must be contiguous "
+                               f"at stride {cols} (call .contiguous())")
+
+
+def _flat(t, name, dtypes, numel, exact=True):
+    """A contiguous buffer of exactly (or at least) numel elements, any shape."""
+    if not _tensor(t, name, dtypes):
+        return
+    if (t.numel() != numel) if exact else (t.numel() < numel):
+        raise BfqArgumentError(f"{name} holds {t.numel()} elements; expected "
+                               f"{'' if exact else 'at least '}{numel}")
+    if not t.is_contiguous():
+        raise BfqArgumentError(f"{name} must be contiguous")
+
+
+def _scales(t, name, layout, ld, m, groups, write):
+    """Activation scales in `layout` with leading dimension ld over m tokens and `groups`
+    scales per token: the 2-D view must cover every element the kernel touches, at stride
+    (ld, 1). Packed words: int32, ceil(groups/4) word rows of ld words, ld >= m rounded up to
+    4 when the quantizer writes them (>= m when the GEMM reads them)."""
+    if layout == BFQ_SCALES_PACKED_UE8M0:
+        if not _tensor(t, name, ("int32", "uint32")):
+            return
+        need = ((groups + 3) // 4, (m + 3) // 4 * 4 if write else m)
+    else:
+        if not _tensor(t, name, ("float32",)):
+            return
+        need = (m, groups) if layout == BFQ_SCALES_ROW_MAJOR else (groups, m)
+    if t.dim() != 2:
+        raise BfqArgumentError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.shape[0] < need[0] or t.shape[1] < need[1]:
+        raise BfqArgumentError(f"{name} has shape {tuple(t.shape)}; the layout needs at least "
+                               f"{need}")
+    if t.shape[0] > 1 and t.stride(0) != ld:
+        raise BfqArgumentError(f"{name} has row stride {t.stride(0)} but scale_ld is {ld}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise BfqArgumentError(f"{name} must have unit stride along its second dimension")
+
+
+def _workspace(t, nbytes):
+    if t is None or isinstance(t, int):
+        return
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise BfqArgumentError("workspace must be a torch.Tensor")
+    if t.numel() * t.element_size() < nbytes or not t.is_contiguous():
+        raise BfqArgumentError(f"workspace holds {t.numel() * t.element_size()} bytes "
+                               f"(contiguous: {t.is_contiguous()}); {nbytes} are declared")
+
+
+CODE_DTYPES = U8_CODES + ("int8",)
+OUT_DTYPES = ("bfloat16", "float16", "float32")
+
+
+def _shape2(t, name):
+    if not hasattr(t, "dim") or t.dim() != 2:
+        raise BfqArgumentError(f"{name} must be a 2-D tensor")
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _same_codes(a, w):
+    """Token and weight codes must be the same code type (e4m3fn bytes or int8)."""
+    if isinstance(a, int) or isinstance(w, int):
+        return
+    if (_dt(a) == "int8") != (_dt(w) == "int8"):
+        raise BfqArgumentError(f"a_q ({_dt(a)}) and w_q ({_dt(w)}) hold different code types")
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -187,7 +309,7 @@ def _qdtype(t) -> int:
         return BFQ_E4M3FN
     if t.dtype == torch.int8:
         return BFQ_INT8
-    raise TypeError(f"code tensor dtype {t.dtype} is neither e4m3fn/uint8 nor int8")
+    raise BfqArgumentError(f"code tensor dtype {t.dtype} is neither e4m3fn/uint8 nor int8")
 
 
 def _odtype(t) -> int:
@@ -203,9 +325,14 @@ def bfq_quant_tokens(x, q, scales, layout=BFQ_SCALES_ROW_MAJOR, scale_ld=None,
     """x: bf16 [M, K]; q: uint8/float8_e4m3fn (e4m3fn codes) or int8 [M, K];
     scales: fp32, [M, ld] (row-major) or [K/group_size, ld] (column-major). group_size 128,
     or K for one scale per token."""
-    M, K = x.shape
+    M, K = _shape2(x, "x")
     if scale_ld is None:
         scale_ld = scales.stride(0)
+    _rows(x, "x", ("bfloat16",), M, K)
+    _rows(q, "q", CODE_DTYPES, M, K)
+    if group_size > 0 and K % group_size == 0:
+        _scales(scales, "scales", layout, scale_ld, M, K // group_size, write=True)
+    _devices(x=x, q=q, scales=scales)
     st = lib.bfq_quant_tokens(_ptr(x), M, K, group_size, _qdtype(q), _ptr(q), _ptr(scales),
                               layout, scale_ld, eps, scale_fmt, _stream(stream))
     return _check(st, "bfq_quant_tokens")
@@ -215,7 +342,12 @@ def bfq_quant_weight_blocks(w, q, scales, eps=DEFAULT_EPS, block_shape=BLOCK_SHA
                             stream=None, scale_fmt=BFQ_SCALE_FP32) -> int:
     """w: fp32 [N, K]; q: codes [N, K]; scales: fp32 [N/128, K/128], or [N] (any shape of N
     contiguous floats) with block_shape (1, K)."""
-    N, K = w.shape
+    N, K = _shape2(w, "w")
+    _rows(w, "w", ("float32",), N, K)
+    _rows(q, "q", CODE_DTYPES, N, K)
+    per_channel = tuple(block_shape)[0] == 1
+    _flat(scales, "scales", ("float32",), N if per_channel else (N // 128) * (K // 128))
+    _devices(w=w, q=q, scales=scales)
     st = lib.bfq_quant_weight_blocks(_ptr(w), N, K, _block_shape(block_shape), _qdtype(q),
                                      _ptr(q), _ptr(scales), eps, scale_fmt, _stream(stream))
     return _check(st, "bfq_quant_weight_blocks")
@@ -224,9 +356,12 @@ def bfq_quant_weight_blocks(w, q, scales, eps=DEFAULT_EPS, block_shape=BLOCK_SHA
 def bfq_pack_weights(w_q, w_packed, stream=None) -> int:
     """w_q: row-major codes [N, K]; w_packed: a separate N*K-byte buffer (any shape with that
     many bytes, e.g. [N, K] uint8) that receives the BFQ_W_PACKED16 layout."""
-    N, K = w_q.shape
-    if w_packed.numel() * w_packed.element_size() != N * K:
-        raise ValueError("w_packed must hold exactly N*K bytes")
+    N, K = _shape2(w_q, "w_q")
+    _rows(w_q, "w_q", CODE_DTYPES, N, K)
+    if _tensor(w_packed, "w_packed", CODE_DTYPES):
+        if w_packed.numel() * w_packed.element_size() != N * K or not w_packed.is_contiguous():
+            raise BfqArgumentError("w_packed must be a contiguous buffer of exactly N*K bytes")
+    _devices(w_q=w_q, w_packed=w_packed)
     st = lib.bfq_pack_weights(_ptr(w_q), N, K, _qdtype(w_q), _ptr(w_packed), _stream(stream))
     return _check(st, "bfq_pack_weights")
 
@@ -255,12 +390,22 @@ def bfq_block_gemm(a_q, a_scales, w_q, w_scales, out, a_layout=BFQ_SCALES_ROW_MA
     out [M, N] (bf16 / fp16 / fp32). scale_fmt BFQ_SCALE_UE8M0 declares every scale a power
     of two. block_shape (1, K): per-token a_scales ([M, 1] or [1, M]) and per-channel
     w_scales [N]. Returns the status (>= 0)."""
-    M, K = a_q.shape
-    N = w_q.shape[0]
+    M, K = _shape2(a_q, "a_q")
+    N = _shape2(w_q, "w_q")[0]
     if a_scale_ld is None:
         a_scale_ld = a_scales.stride(0)
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _rows(a_q, "a_q", CODE_DTYPES, M, K)
+    _rows(w_q, "w_q", CODE_DTYPES, N, K)
+    _same_codes(a_q, w_q)
+    per_channel = tuple(block_shape)[0] == 1
+    _scales(a_scales, "a_scales", a_layout, a_scale_ld, M, 1 if per_channel else K // 128,
+            write=False)
+    _flat(w_scales, "w_scales", ("float32",), N if per_channel else (N // 128) * (K // 128))
+    _rows(out, "out", OUT_DTYPES, M, N)
+    _workspace(workspace, workspace_bytes)
+    _devices(a_q=a_q, a_scales=a_scales, w_q=w_q, w_scales=w_scales, out=out, workspace=workspace)
     st = lib.bfq_block_gemm(_ptr(a_q), _ptr(a_scales), a_layout, a_scale_ld, _ptr(w_q),
                             _ptr(w_scales), w_layout, scale_fmt, _ptr(out), M, N, K,
                             _block_shape(block_shape),
@@ -291,9 +436,15 @@ def bfq_get_tile_candidate(index, in_dtype=BFQ_E4M3FN, w_layout=BFQ_W_ROW_MAJOR,
 
 def bfq_moe_align(topk_ids, E, expert_offsets, sorted_pairs, workspace=None, stream=None) -> int:
     """topk_ids int32 [T, topk]; expert_offsets int32 [E+1]; sorted_pairs int32 [T*topk]."""
-    T, topk = topk_ids.shape
+    T, topk = _shape2(topk_ids, "topk_ids")
     need = int(lib.bfq_moe_align_workspace_bytes(T, topk, E))
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _rows(topk_ids, "topk_ids", ("int32",), T, topk)
+    _flat(expert_offsets, "expert_offsets", ("int32",), E + 1)
+    _flat(sorted_pairs, "sorted_pairs", ("int32",), T * topk)
+    _workspace(workspace, need)
+    _devices(topk_ids=topk_ids, expert_offsets=expert_offsets, sorted_pairs=sorted_pairs,
+             workspace=workspace)
     st = lib.bfq_moe_align(_ptr(topk_ids), T, topk, E, _ptr(expert_offsets), _ptr(sorted_pairs),
                            _ptr(workspace), wb if workspace is not None else need, _stream(stream))
     return _check(st, "bfq_moe_align")
@@ -320,12 +471,27 @@ def bfq_moe_block_gemm(a_q, a_scales, sorted_pairs, expert_offsets, topk, w_q, w
                        scale_fmt=BFQ_SCALE_FP32) -> int:
     """a_q [T, K]; w_q [E, N, K] (row-major, or each expert packed); w_scales
     [E, N/128, K/128]; out [T*topk, N] in pair order."""
-    T, K = a_q.shape
+    T, K = _shape2(a_q, "a_q")
+    if not hasattr(w_q, "dim") or w_q.dim() != 3:
+        raise BfqArgumentError("w_q must be a 3-D [E, N, K] tensor")
     E, N = w_q.shape[0], w_q.shape[1]
     if a_scale_ld is None:
         a_scale_ld = a_scales.stride(0)
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _rows(a_q, "a_q", U8_CODES, T, K)
+    if w_q.shape[2] != K:
+        raise BfqArgumentError(f"w_q has shape {tuple(w_q.shape)}; its last dimension must be K={K}")
+    _flat(w_q, "w_q", U8_CODES, E * N * K)
+    _scales(a_scales, "a_scales", a_layout, a_scale_ld, T, K // 128, write=False)
+    _flat(w_scales, "w_scales", ("float32",), E * (N // 128) * (K // 128))
+    _flat(sorted_pairs, "sorted_pairs", ("int32",), T * topk)
+    _flat(expert_offsets, "expert_offsets", ("int32",), E + 1)
+    _rows(out, "out", OUT_DTYPES, T * topk, N)
+    _workspace(workspace, workspace_bytes)
+    _devices(a_q=a_q, a_scales=a_scales, sorted_pairs=sorted_pairs,
+             expert_offsets=expert_offsets, w_q=w_q, w_scales=w_scales, out=out,
+             workspace=workspace)
     st = lib.bfq_moe_block_gemm(_ptr(a_q), _ptr(a_scales), a_layout, a_scale_ld, _ptr(sorted_pairs),
                                 _ptr(expert_offsets), topk, _ptr(w_q), _ptr(w_scales), w_layout,
                                 scale_fmt, _ptr(out), T, N, K, E, _block_shape(BLOCK_SHAPE),
@@ -362,14 +528,21 @@ def bfq_last_error() -> str:
 
 
 def bfq_debug_block_partials_i32(a_q, w_q, partials, stream=None) -> int:
-    M, K = a_q.shape
-    N = w_q.shape[0]
+    M, K = _shape2(a_q, "a_q")
+    N = _shape2(w_q, "w_q")[0]
+    _rows(a_q, "a_q", ("int8",), M, K)
+    _rows(w_q, "w_q", ("int8",), N, K)
+    _flat(partials, "partials", ("int32",), (K // 128) * M * N)
+    _devices(a_q=a_q, w_q=w_q, partials=partials)
     st = lib.bfq_debug_block_partials_i32(_ptr(a_q), _ptr(w_q), _ptr(partials), M, N, K,
                                           _stream(stream))
     return _check(st, "bfq_debug_block_partials_i32")
 
 
 def bfq_debug_encode(x, codes, q_dtype=BFQ_E4M3FN, stream=None) -> int:
+    _flat(x, "x", ("float32",), x.numel())
+    _flat(codes, "codes", CODE_DTYPES, x.numel())
+    _devices(x=x, codes=codes)
     st = lib.bfq_debug_encode(_ptr(x), x.numel(), q_dtype, _ptr(codes), _stream(stream))
     return _check(st, "bfq_debug_encode")
 

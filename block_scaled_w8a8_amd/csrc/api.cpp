@@ -154,8 +154,10 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Compiled-in default ([CONFIG] §4.1: no tuned entry -> a fixed default config). Below 32
 // tokens the swap-AB streaming kernel ([HELION]: the Hopper rule dispatches swap-AB for
 // M < 32), else the standard kernel with the largest tile that still yields one workgroup
-// per CU. Split-K is added until the grid covers the CUs, keeping >= 4 K blocks per split.
-bfq_tile default_tile(int64_t M, int64_t N, int64_t K, int qtype, int sfmt) {
+// per CU, among the tiles compiled for this code type, weight layout and scale format (the
+// int8 kernels, for one, have no 128x256 tile). Split-K is added until the grid covers the
+// CUs, keeping >= 4 K blocks per split.
+bfq_tile default_tile(int64_t M, int64_t N, int64_t K, int qtype, int wlayout, int sfmt) {
     const int64_t KB = K / 128;
     bfq_tile t{};
     t.bk = 128;
@@ -172,19 +174,32 @@ bfq_tile default_tile(int64_t M, int64_t N, int64_t K, int qtype, int sfmt) {
         ctas = ceil_div(N, t.bn) * ceil_div(M, t.bm);
     } else {
         static const int shapes[4][4] = {{256, 256, 4, 2}, {128, 256, 2, 2}, {128, 128, 2, 2}, {64, 128, 1, 2}};
-        int pick = 3;
-        for (int i = 0; i < 4; ++i)
-            if (ceil_div(M, shapes[i][0]) * ceil_div(N, shapes[i][1]) >= kNumCUs) { pick = i; break; }
         t.variant = 0;
-        t.bm = shapes[pick][0];
-        t.bn = shapes[pick][1];
-        t.waves_m = shapes[pick][2];
-        t.waves_n = shapes[pick][3];
         t.stages = 2;
         t.group_m = 8;
-        // power-of-two fp8 scales: the block-scaled MFMA schedule where it is compiled;
-        // per-token x per-channel scales: the whole-K accumulation schedule
-        t.sched = sfmt == S_CHANNEL ? 4 : (qtype == Q_FP8 && sfmt == S_UE8M0 && pick < 3) ? 3 : 0;
+        // the shape's schedule: per-token x per-channel scales accumulate the whole K (sched 4);
+        // power-of-two fp8 scales use the block-scaled MFMA (sched 3) where it is compiled;
+        // otherwise the per-block FMA (sched 0)
+        auto shaped = [&](int i) {
+            bfq_tile s = t;
+            s.bm = shapes[i][0];
+            s.bn = shapes[i][1];
+            s.waves_m = shapes[i][2];
+            s.waves_n = shapes[i][3];
+            s.sched = sfmt == S_CHANNEL ? 4 : 0;
+            if (sfmt == S_UE8M0 && qtype == Q_FP8) {
+                s.sched = 3;
+                if (!find_kernel(s, qtype, O_BF16, wlayout, sfmt)) s.sched = 0;
+            }
+            return s;
+        };
+        int pick = -1, last = -1;
+        for (int i = 0; i < 4; ++i) {
+            if (!find_kernel(shaped(i), qtype, O_BF16, wlayout, sfmt)) continue;
+            last = i;
+            if (ceil_div(M, shapes[i][0]) * ceil_div(N, shapes[i][1]) >= kNumCUs) { pick = i; break; }
+        }
+        t = shaped(pick >= 0 ? pick : last >= 0 ? last : 3);
         ctas = ceil_div(M, t.bm) * ceil_div(N, t.bn);
     }
     while (ctas * t.split_k < kNumCUs && KB / (t.split_k * 2) >= 4) t.split_k *= 2;
@@ -278,7 +293,7 @@ bfq_status select_tile(int64_t M, int64_t N, int64_t K, int qtype, int wlayout, 
             return BFQ_OK;
         }
     }
-    *out = default_tile(M, N, K, qtype, sfmt);
+    *out = default_tile(M, N, K, qtype, wlayout, sfmt);
     if (std::getenv("BFQ_LOG"))
         std::fprintf(stderr, "[bfq] no tuned entry for N=%lld K=%lld layout=%d scales=%d; using default tile\n",
                      (long long)N, (long long)K, wlayout, sfmt);
@@ -727,9 +742,12 @@ bfq_status bfq_moe_block_gemm(const void* a_q, const float* a_scales, bfq_scale_
         K % 128 != 0)
         return fail(BFQ_ERR_SHAPE, "need T >= 0, topk >= 1, 1 <= E <= 1023, N and K positive multiples of 128");
     const int64_t P = T * topk;
-    // the kernels gather token rows through one 32-bit offset over all of a_q
+    // the kernels gather token rows through one 32-bit offset over all of a_q, and address
+    // up to 256 weight rows of an expert (and a K block's offset) in 32 bits, as the dense
+    // kernels do
     if (T * K >= (int64_t(1) << 31) || P > 0x7FFFFFFF || N > 0x7FFFFFFF)
         return fail(BFQ_ERR_SHAPE, "T * K must be below 2^31 bytes");
+    if (K > (1 << 23)) return fail(BFQ_ERR_SHAPE, "K must be at most 2^23");
     if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(out, 16) || !aligned(a_scales, 4) ||
         !aligned(w_scales, 4) || !aligned(workspace, 16) || !aligned(sorted_pairs, 4) ||
         !aligned(expert_offsets, 4))

@@ -296,6 +296,44 @@ def test_default_rule(bfq, tmp_path):
         bfq.bfq_load_tile_table(None)
 
 
+# (M, N) pairs that reach each pick of the default rule's standard-tile list at K = 7168:
+# 256x256 fills the CUs; 128x256 does (fp8) and int8 falls through to 128x128; only 128x128
+# does; none does (the smallest compiled tile, plus split-K); and the swap-AB rule below 32.
+DEFAULT_PICKS = [(4096, 24576), (512, 24576), (2048, 4096), (300, 4096), (200, 4096),
+                 (32, 24576), (31, 1536), (1, 7168)]
+
+
+@pytest.mark.parametrize("qname", ["fp8", "int8"])
+def test_default_rule_names_compiled_kernels(bfq, tmp_path, qname):
+    """With an empty table, every default tile names a kernel compiled for the code type,
+    weight layout and scale format (fp32 / UE8M0 block scales, packed UE8M0 words, per-token x
+    per-channel), so the GEMM accepts it. The int8 kernels have no 128x256 tile: at M=2048,
+    N=4096 the rule passes over it to 128x128."""
+    qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
+    p = tmp_path / "empty.json"
+    p.write_text(_table([]))
+    bfq.bfq_load_tile_table(str(p))
+    try:
+        for wl in (bfq.BFQ_W_ROW_MAJOR, bfq.BFQ_W_PACKED16):
+            for sf, lay, ld, bs in ((0, 0, 56, BS), (1, 0, 56, BS), (1, 2, 4096, BS),
+                                    (0, 0, 1, _bs(1, 7168))):
+                if lay == 2 and qd == bfq.BFQ_INT8:
+                    continue                # packed words are read by the e4m3fn GEMM only
+                for M, N in DEFAULT_PICKS:
+                    st, t = bfq.bfq_select_tile(M, N, 7168, qd, w_layout=wl, scale_fmt=sf,
+                                                block_shape=tuple(bs))
+                    what = (qname, wl, sf, lay, tuple(bs), M, N, t.as_dict())
+                    assert st == bfq.BFQ_WARN_DEFAULT_TILE, what
+                    assert _gemm(bfq, M=0, N=N, in_dtype=qd, w_layout=wl, scale_fmt=sf,
+                                 a_layout=lay, a_scale_ld=ld, block_shape=bs,
+                                 tile=ctypes.pointer(t)) >= 0, (what, bfq.last_error())
+        st, t = bfq.bfq_select_tile(2048, 4096, 7168, qd)
+        want = (128, 256) if qname == "fp8" else (128, 128)
+        assert (t.variant, t.bm, t.bn) == (0, *want), t.as_dict()
+    finally:
+        bfq.bfq_load_tile_table(None)
+
+
 def test_metric_formulas_reproduce_pages_table():
     """P10: the pages' TFLOPS and GB/s formulas (block GEMM benchmark page §4.3) recompute
     every printed row of §3.2 from its (m, n, k, us) within the rounding of the print."""
@@ -516,6 +554,10 @@ def test_moe_validation_without_launch(bfq):
     assert _moe(bfq, topk=0) == bfq.BFQ_ERR_SHAPE
     assert _moe(bfq, N=1000) == bfq.BFQ_ERR_SHAPE
     assert _moe(bfq, T=300000) == bfq.BFQ_ERR_SHAPE               # T * K >= 2^31
+    # K beyond 2^23: 256 weight rows x K would wrap the 32-bit weight offsets
+    assert _moe(bfq, T=1, K=1 << 24, a_scale_ld=1 << 17) == bfq.BFQ_ERR_SHAPE
+    assert "2^23" in bfq.last_error()
+    assert _moe(bfq, T=0, K=1 << 24, a_scale_ld=1 << 17) == bfq.BFQ_ERR_SHAPE
     assert _moe(bfq, a_scale_ld=10) == bfq.BFQ_ERR_SHAPE
     assert _moe(bfq, T=64, a_layout=1, a_scale_ld=63) == bfq.BFQ_ERR_SHAPE
     assert _moe(bfq, a_layout=2, a_scale_ld=0) == bfq.BFQ_ERR_ARG  # packed needs UE8M0
