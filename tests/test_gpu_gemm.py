@@ -355,20 +355,32 @@ def _full_inputs(bfq, N, K, m_max, qname, sfmt=0):
         xd, wd = x.to(DEV), w.to(DEV)
         qw, sw = bfq.quant_weight_blocks(wd, q_dtype=qd, scale_fmt=sfmt)
         qa, sa = bfq.quant_tokens(xd, q_dtype=qd, scale_fmt=sfmt)
+        # the timed layout: the quantizer writes the scales column-major, ld = m_max
+        qa_c, sa_col = bfq.quant_tokens(xd, q_dtype=qd, scale_fmt=sfmt,
+                                        layout=bfq.BFQ_SCALES_COL_MAJOR)
         qwp = bfq.pack_weights(qw)
         torch.cuda.synchronize()
-        del wd
+        assert torch.equal(qa_c, qa) and torch.equal(sa_col.t().view(torch.int32),
+                                                     sa.view(torch.int32))
+        del wd, qa_c
         _cache[key] = (qa, sa, qw, sw, qa.cpu().numpy(), sa.cpu().numpy(), qw.cpu().numpy(),
-                       sw.cpu().numpy(), qwp)
+                       sw.cpu().numpy(), qwp, sa_col)
     return _cache[key]
 
 
 def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096, tile=None, layout="row",
-                   sfmt=0):
+                   sfmt=0, scale_layout="row"):
+    """scale_layout "col": the activation scales column-major with ld = m_max, as the
+    benchmark lays them out (every M reads the first M columns of one [K/128, m_max] array)."""
     from oracle import metrics
     qt = orc.FP8 if qname == "fp8" else orc.INT8
-    qa, sa, qw, sw, qa_h, sa_h, qw_h, sw_h, qwp = _full_inputs(bfq, N, K, m_max, qname, sfmt)
+    qa, sa, qw, sw, qa_h, sa_h, qw_h, sw_h, qwp, sa_col = _full_inputs(bfq, N, K, m_max, qname,
+                                                                       sfmt)
     wl = _wl(bfq, layout)
+    if scale_layout == "col":
+        a_lay, sa_arg = bfq.BFQ_SCALES_COL_MAJOR, sa_col
+    else:
+        a_lay, sa_arg = bfq.BFQ_SCALES_ROW_MAJOR, sa[:M]
     qw_arg = qwp if layout == "packed" else qw
     out32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
     out16 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
@@ -377,10 +389,10 @@ def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096, tile=None, l
                                        scale_fmt=sfmt)
     ws_bytes = bfq.bfq_gemm_workspace_bytes(M, N, K, tile)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
-    bfq.bfq_block_gemm(qa[:M], sa[:M], qw_arg, sw, out32, tile=tile, workspace=ws,
-                       workspace_bytes=ws_bytes, w_layout=wl, scale_fmt=sfmt)
-    bfq.bfq_block_gemm(qa[:M], sa[:M], qw_arg, sw, out16, tile=tile, workspace=ws,
-                       workspace_bytes=ws_bytes, w_layout=wl, scale_fmt=sfmt)
+    bfq.bfq_block_gemm(qa[:M], sa_arg, qw_arg, sw, out32, tile=tile, workspace=ws,
+                       workspace_bytes=ws_bytes, w_layout=wl, scale_fmt=sfmt, a_layout=a_lay)
+    bfq.bfq_block_gemm(qa[:M], sa_arg, qw_arg, sw, out16, tile=tile, workspace=ws,
+                       workspace_bytes=ws_bytes, w_layout=wl, scale_fmt=sfmt, a_layout=a_lay)
     torch.cuda.synchronize()
     rng = np.random.default_rng(M * 7 + N)
     ms = np.concatenate([rng.integers(0, M, n_samples), [0, M - 1, M - 1]])
@@ -389,7 +401,7 @@ def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096, tile=None, l
     o32 = out32.cpu().numpy()
     got = o32[ms, ns]
     r = metrics.gemm_fp32_report(got, ref)
-    assert r["ok"], (M, N, K, layout, sfmt, tile.as_dict(), r)
+    assert r["ok"], (M, N, K, layout, sfmt, scale_layout, tile.as_dict(), r)
     o16 = out16.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(o16, orc.f32_to_bf16_bits_array(o32)), (M, N, K)
     # quantized inputs were produced on the device: they must equal the oracle's
@@ -539,3 +551,145 @@ def test_packed_scale_words_configs(bfq, orc, M, N, K, layout):
     ref = orc.block_gemm_sampled(qo, so, qwo, swo, ms, ns)
     r = metrics.gemm_fp32_report(out.cpu().numpy()[ms, ns], ref)
     assert r["ok"], (M, N, K, layout, r)
+
+
+# ------------------------------------------------ the configuration the benchmark times
+# The benchmark runs packed weights, activation scales written column-major by the quantizer
+# with ld = M_max (the layout of the block GEMM benchmark page's §4.1 for CUTLASS/DeepGEMM),
+# and the tuned tile of each M. These tests run exactly that, at full size, through the tile
+# the library selects, sampled against the oracle.
+
+TIMED_MGRID = [1, 64, 128, 256, 512, 1024, 1536, 2048, 3072, 4096]
+
+
+@pytest.mark.parametrize("M", TIMED_MGRID)
+def test_timed_config_mgrid(bfq, orc, M):
+    print(f"timed config M={M} N=24576 K=7168 packed col-major ld=4096", flush=True)
+    _sampled_check(bfq, orc, M, 24576, 7168, 4096, "fp8", layout="packed", scale_layout="col")
+
+
+@pytest.mark.parametrize("N,K", [(7168, 18432), (18432, 7168)])
+def test_timed_config_dense_4096(bfq, orc, N, K):
+    print(f"timed config M=4096 N={N} K={K} packed col-major", flush=True)
+    _sampled_check(bfq, orc, 4096, N, K, 4096, "fp8", layout="packed", scale_layout="col")
+
+
+@pytest.mark.parametrize("M", [1, 128, 4096])
+def test_timed_config_int8(bfq, orc, M):
+    print(f"timed config int8 M={M} N=1536 K=7168 packed col-major", flush=True)
+    _sampled_check(bfq, orc, M, 1536, 7168, 4096, "int8", layout="packed", scale_layout="col")
+
+
+@pytest.mark.parametrize("sfmt", [0, 1])
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("qname", ["fp8", "int8"])
+def test_every_candidate_col_major_full_tiles(bfq, orc, qname, layout, sfmt):
+    """Column-major activation scales with a padded ld at M = 600, which fills whole 256-row
+    tiles (and ends in a ragged one): every compiled kernel and split {1, 2} against the
+    oracle, so each row range of the scale staging (rows 0-255 of a tile and beyond) is read
+    in the layout the benchmark uses."""
+    from oracle import metrics
+    qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
+    qt = orc.FP8 if qname == "fp8" else orc.INT8
+    M, N, K = 600, 640, 768
+    host = _case(orc, M, N, K, 27, qt, sfmt)
+    ref32, _ = orc.block_gemm(*host, qtype=qt)
+    dq = _to_dev(*host, layout=layout, sfmt=sfmt)
+    sa_col = torch.full((K // 128, M + 7), float("nan"), device=DEV)
+    sa_col[:, :M] = dq[1].t()
+    for t in _candidates(bfq, qd, layout, sfmt):
+        for s in (1, 2):
+            if t.variant == 2 and s > 1:
+                continue
+            tile = _with_split(t, s)
+            what = (qname, layout, sfmt, tile.as_dict())
+            print("col-major candidate", what, flush=True)
+            o = _run(bfq, dq, torch.float32, tile=tile, a_layout=bfq.BFQ_SCALES_COL_MAJOR,
+                     sa_override=sa_col).cpu().numpy()
+            _check_fp32(metrics, o, ref32, what)
+
+
+# ------------------------------------------------ int8: exact partials in the product tiles
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("K", [128, 1024])
+def test_int8_full_range_partials_exact_every_candidate(bfq, orc, K, layout):
+    """The product int8 tiles keep each 128-wide block partial as an exact int32 (the int8
+    block variant of the config page, §1): codes over the full range [-127, 127] (rows and
+    columns of all +127 / -127 reach the extreme partial 128 * 127^2 = 2,064,512) with one
+    power-of-two scale for every block. Every partial, every scaled partial and every running
+    sum of up to 8 blocks is then an integer multiple of 2^-8 below 2^16, exact in fp32, so
+    the fp32 output of every int8 kernel and split (split partials and their fixed-order sum
+    included) must equal the int64 matmul times 2^-8 bit for bit."""
+    rng = np.random.default_rng(K + 17)
+    M, N = 83, 640
+    ia = rng.integers(-127, 128, size=(M, K))
+    iw = rng.integers(-127, 128, size=(N, K))
+    ia[0], ia[1], iw[0], iw[1] = 127, -127, 127, -127
+    exact = (ia.astype(np.int64) @ iw.T.astype(np.int64))
+    assert np.abs(exact).max() == 127 * 127 * K
+    exact = exact.astype(np.float64) * 2.0 ** -8
+    sa = np.full((M, K // 128), 2.0 ** -3, dtype=np.float32)
+    sw = np.full((N // 128, K // 128), 2.0 ** -5, dtype=np.float32)
+    dq = _to_dev(ia.astype(np.int8), sa, iw.astype(np.int8), sw, layout=layout)
+    cands = _candidates(bfq, bfq.BFQ_INT8, layout)
+    assert cands
+    for t in cands:
+        for s in (1, 2, 4):
+            if (t.variant == 2 and s > 1) or s > K // 128:
+                continue
+            tile = _with_split(t, s)
+            o32 = _run(bfq, dq, torch.float32, tile=tile).cpu().numpy().astype(np.float64)
+            assert np.array_equal(o32, exact), (K, layout, tile.as_dict())
+
+
+# ------------------------------------------------ guard bands around outputs and workspace
+
+SENTINEL = 0xA5
+
+
+def _guarded(n_bytes, front, back):
+    """A device byte buffer of front + n_bytes + back sentinel bytes; returns (buf, view)."""
+    buf = torch.full((front + n_bytes + back,), SENTINEL, dtype=torch.uint8, device=DEV)
+    return buf, buf[front:front + n_bytes]
+
+
+def _untouched(buf, front, n_bytes):
+    h = buf.cpu().numpy()
+    return bool((h[:front] == SENTINEL).all() and (h[front + n_bytes:] == SENTINEL).all())
+
+
+@pytest.mark.parametrize("odt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("qname", ["fp8", "int8"])
+def test_guard_bands_every_candidate(bfq, orc, qname, layout, odt):
+    """Ragged M (83) and N (640: 2.5 tiles of 256, 3.3 of 192) for every compiled kernel with
+    split {1, 3}: the output [M, N] sits inside a larger sentinel-filled buffer and the split-K
+    / stream-K workspace inside one too. No byte before or after either is written, and the
+    output still meets the bar against the oracle."""
+    from oracle import metrics
+    qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
+    qt = orc.FP8 if qname == "fp8" else orc.INT8
+    M, N, K = 83, 640, 768
+    host = _case(orc, M, N, K, 29, qt)
+    ref32, _ = orc.block_gemm(*host, qtype=qt)
+    qa, sa, qw, sw, _, _ = _to_dev(*host, layout=layout)
+    esz = torch.tensor([], dtype=odt).element_size()
+    front, back = 4096, 64 * 1024
+    for t in _candidates(bfq, qd, layout):
+        for s in (1, 3):
+            if t.variant == 2 and s > 1:
+                continue
+            tile = _with_split(t, s)
+            what = (qname, layout, str(odt), tile.as_dict())
+            obuf, oview = _guarded(M * N * esz, front, back)
+            out = oview.view(odt).view(M, N)
+            need = bfq.bfq_gemm_workspace_bytes(M, N, K, tile)
+            wbuf, wview = _guarded(max(need, 16), front, back)
+            bfq.bfq_block_gemm(qa, sa, qw, sw, out, tile=tile, workspace=wview,
+                               workspace_bytes=need, w_layout=_wl(bfq, layout))
+            torch.cuda.synchronize()
+            assert _untouched(obuf, front, M * N * esz), ("output guard", what)
+            assert _untouched(wbuf, front, max(need, 16)), ("workspace guard", what)
+            if odt == torch.float32:
+                _check_fp32(metrics, out.cpu().numpy(), ref32, what)
