@@ -210,15 +210,18 @@ def run_gpu(args, wl):
                                      scale_ld=sa_all.stride(0), scale_fmt=sfmt,
                                      group_size=sh["group"])
 
-            def g_once(i):
-                qw, sw = sh["copies"][i % len(sh["copies"])]
+            def g_once(i, rotate=True):
+                qw, sw = sh["copies"][i % len(sh["copies"]) if rotate else 0]
                 bfq.bfq_block_gemm(sh["qa"][:M], sa_m, qw, sw, sh["out"][:M], a_layout=lay,
                                    a_scale_ld=sa_all.stride(0), tile=tile, workspace=sh["ws"],
                                    workspace_bytes=sh["ws_max"], w_layout=wlay, scale_fmt=sfmt,
                                    block_shape=sh["bs"])
 
             res = {}
-            for name, fn in (("q", lambda i: q_once()), ("g", g_once)):
+            # "h": the same GEMM with one weight copy for every launch (hot caches, the pages'
+            # style of timing), a secondary figure beside the rotating one
+            for name, fn in (("q", lambda i: q_once()), ("g", g_once),
+                             ("h", lambda i: g_once(i, rotate=False))):
                 fn(0)
                 torch.cuda.synchronize()
                 gr = torch.cuda.CUDAGraph()
@@ -237,7 +240,7 @@ def run_gpu(args, wl):
                     vals.append(e0.elapsed_time(e1) * 1e-3 / R)
                 del gr
                 res[name] = vals
-            per[(N, K, M)] = {"key": tile_key(tile), "q": res["q"], "g": res["g"]}
+            per[(N, K, M)] = {"key": tile_key(tile), "q": res["q"], "g": res["g"], "h": res["h"]}
 
     flops_step = sum(perf.gemm_flops(M, sh["N"], sh["K"]) for sh in shapes
                      for (M, *_r) in sh["plans"])
@@ -252,7 +255,9 @@ def run_gpu(args, wl):
             q = sum(r["q"]) / len(r["q"])
             rows.append({
                 "M": M, "N": N, "K": K, "tile": tile.as_dict(), "tuned": st == 0,
-                "gemm_us": round(g * 1e6, 2), "quant_us": round(q * 1e6, 2),
+                "gemm_us": round(g * 1e6, 2),
+                "gemm_us_hot": round(sum(r["h"]) / len(r["h"]) * 1e6, 2),
+                "quant_us": round(q * 1e6, 2),
                 "tflops": round(perf.tflops(M, N, K, g), 2),
                 "gbs_page": round(perf.gbs_page(M, N, K, g), 1),
                 "gbs_all": round(perf.gbs_all(M, N, K, g, channel=channel), 1),
@@ -293,9 +298,47 @@ def run_gpu(args, wl):
         "ms_per_step": step_s * 1e3,
         "rows": rows,
         "roofline": roof,
+        "ceilings": measured_ceilings(),
         "host": host,
         "batch_invariant": bfq.bfq_get_batch_invariant(),
     }
+
+
+def measured_ceilings():
+    """What this GPU sustains in practice, beside the published peaks: the fp8 MFMA-only probe
+    of the library (register operands, no memory traffic, 16 waves per CU) and a plain 1 GiB
+    device-to-device copy (torch's copy kernel; bytes read + bytes written per second). Each
+    is the best of three event-timed launches on the current stream."""
+    import torch
+
+    from block_scaled_w8a8_amd import bfq
+    stream = torch.cuda.current_stream()
+    blocks, iters = 512, 20000
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda:0")
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+
+    flops = float(bfq.lib.bfq_probe_mfma_flops(blocks, iters))
+    t_mfma = best(lambda: bfq.bfq_probe_mfma_peak(blocks, iters, out))
+    t_copy = best(lambda: dst.copy_(src))
+    del src, dst, out
+    return {"mfma_fp8_tflops": round(flops / t_mfma / 1e12, 1),
+            "copy_gbs": round(2 * (1 << 30) / t_copy / 1e9, 1),
+            "how": "fp8 16x16x128 MFMA chains on register operands, 512 workgroups x 8 waves; "
+                   "1 GiB device copy, read + write bytes"}
 
 
 def run_gpu_moe(args, wl):
@@ -619,6 +662,7 @@ def main():
                    "batch_invariant": bool(res.get("batch_invariant")),
                    "scales": args.scales},
         "roofline": res["roofline"],
+        "ceilings": res.get("ceilings"),
         "cpu_baseline": cpu,
         "per_m": res["rows"],
     }

@@ -57,7 +57,7 @@ EXPORTED = (
     "bfq_set_batch_invariant", "bfq_get_batch_invariant",
     "bfq_moe_align_workspace_bytes", "bfq_moe_align", "bfq_moe_select_tile",
     "bfq_moe_gemm_workspace_bytes", "bfq_moe_block_gemm", "bfq_moe_num_tile_candidates",
-    "bfq_moe_get_tile_candidate",
+    "bfq_moe_get_tile_candidate", "bfq_probe_mfma_peak", "bfq_probe_mfma_flops",
 )
 
 
@@ -130,6 +130,8 @@ def _load():
         "bfq_moe_num_tile_candidates": (i32, [i32, i32]),
         "bfq_moe_get_tile_candidate": (i32, [i32, i32, i32, tp]),
         "bfq_get_batch_invariant": (i32, []),
+        "bfq_probe_mfma_peak": (i32, [i64, i64, p, p]),
+        "bfq_probe_mfma_flops": (ctypes.c_double, [i64, i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -537,6 +539,16 @@ def bfq_debug_block_partials_i32(a_q, w_q, partials, stream=None) -> int:
     st = lib.bfq_debug_block_partials_i32(_ptr(a_q), _ptr(w_q), _ptr(partials), M, N, K,
                                           _stream(stream))
     return _check(st, "bfq_debug_block_partials_i32")
+
+
+def bfq_probe_mfma_peak(blocks, iters, out, stream=None) -> float:
+    """Launch the MFMA-only probe (out: >= blocks * 512 fp32 on the device); returns the
+    flops of the launch."""
+    _flat(out, "out", ("float32",), blocks * 512, exact=False)
+    _devices(out=out)
+    _check(lib.bfq_probe_mfma_peak(blocks, iters, _ptr(out), _stream(stream)),
+           "bfq_probe_mfma_peak")
+    return float(lib.bfq_probe_mfma_flops(blocks, iters))
 
 
 def bfq_debug_encode(x, codes, q_dtype=BFQ_E4M3FN, stream=None) -> int:

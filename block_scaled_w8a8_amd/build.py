@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(HERE, "libbfq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["quant.hip", "gemm_std.hip", "gemm_swapab.hip", "moe.hip", "api.cpp", "tile_table.cpp"]
+SOURCES = ["quant.hip", "gemm_std.hip", "gemm_swapab.hip", "moe.hip", "probe.hip", "api.cpp",
+           "tile_table.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(REPO, "include")]

@@ -863,6 +863,21 @@ bfq_status bfq_debug_block_partials_i32(const void* a_q, const void* w_q, int32_
     return BFQ_OK;
 }
 
+bfq_status bfq_probe_mfma_peak(int64_t blocks, int64_t iters, float* out, void* stream) {
+    if (!out) return fail(BFQ_ERR_NULL, "out must be non-NULL");
+    if (blocks < 1 || blocks >= (int64_t(1) << 31) || iters < 1 || iters >= (int64_t(1) << 40))
+        return fail(BFQ_ERR_SHAPE, "blocks must be in [1, 2^31) and iters in [1, 2^40)");
+    if (!aligned(out, 4)) return fail(BFQ_ERR_ALIGN, "out must be 4-byte aligned");
+    hipError_t e = launch_mfma_peak(blocks, iters, out, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(BFQ_ERR_HIP, hipGetErrorString(e));
+    return BFQ_OK;
+}
+
+double bfq_probe_mfma_flops(int64_t blocks, int64_t iters) {
+    const double waves = (double)blocks * (mfma_peak_threads_per_block() / 64);
+    return waves * (double)iters * mfma_peak_mfmas_per_wave_iter() * (2.0 * 16 * 16 * 128);
+}
+
 bfq_status bfq_debug_encode(const float* x, int64_t n, bfq_dtype q_dtype, void* codes,
                             void* stream) {
     if (!x || !codes) return fail(BFQ_ERR_NULL, "x and codes must be non-NULL");

@@ -111,6 +111,11 @@ int streamk_grid();
 hipError_t launch_splitk_reduce(const float* partials, void* out, int64_t M, int64_t N,
                                 int split, int otype, hipStream_t stream);
 
+// Measurement support (csrc/probe.hip): fp8 MFMA chains with no memory traffic.
+hipError_t launch_mfma_peak(int64_t blocks, int64_t iters, float* out, hipStream_t stream);
+int mfma_peak_threads_per_block();
+int mfma_peak_mfmas_per_wave_iter();
+
 // int8 per-K-block int32 partials [K/128][M][N] (test support).
 hipError_t launch_block_partials_i32(const void* a, const void* w, int32_t* out, int64_t M,
                                      int64_t N, int64_t K, hipStream_t stream);

@@ -298,6 +298,15 @@ const char* bfq_last_error(void);
 bfq_status bfq_debug_block_partials_i32(const void* a_q, const void* w_q, int32_t* partials,
                                         int64_t M, int64_t N, int64_t K, void* stream);
 
+/* Measurement support: `blocks` workgroups of 8 waves, each wave running 8 independent
+ * chains of `iters` fp8 16x16x128 MFMAs on register operands and nothing else, so that
+ * flops / elapsed is the matrix-core throughput the GPU sustains (at the clock it holds under
+ * that load), stated beside the published peak. out: blocks * 512 floats (device), written
+ * once per lane to keep the chains live; its values mean nothing. Flops of one launch:
+ * bfq_probe_mfma_flops(blocks, iters). blocks in [1, 2^31), iters in [1, 2^40). */
+bfq_status bfq_probe_mfma_peak(int64_t blocks, int64_t iters, float* out, void* stream);
+double     bfq_probe_mfma_flops(int64_t blocks, int64_t iters);
+
 /* Test support: the element encoder the quantizers use, applied to n fp32 values that are
  * finite with |x| < 464 (e4m3fn) or finite (int8). codes [n] bytes. */
 bfq_status bfq_debug_encode(const float* x, int64_t n, bfq_dtype q_dtype, void* codes,

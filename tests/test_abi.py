@@ -628,3 +628,13 @@ def test_table_moe_key(bfq, tmp_path):
     with pytest.raises(bfq.BfqError):
         bfq.bfq_load_tile_table(str(bad))
     bfq.bfq_load_tile_table(None)
+
+
+def test_probe_validation_without_launch(bfq):
+    f = bfq.lib.bfq_probe_mfma_peak
+    assert f(4, 10, None, None) == bfq.BFQ_ERR_NULL
+    assert f(0, 10, FAKE, None) == bfq.BFQ_ERR_SHAPE
+    assert f(4, 0, FAKE, None) == bfq.BFQ_ERR_SHAPE
+    assert f(4, 10, FAKE + 2, None) == bfq.BFQ_ERR_ALIGN
+    # 8 waves x 8 chains x iters x (2 * 16 * 16 * 128) flops per workgroup
+    assert bfq.lib.bfq_probe_mfma_flops(3, 5) == 3 * 8 * 8 * 5 * 65536
