@@ -57,7 +57,8 @@ EXPORTED = (
     "bfq_set_batch_invariant", "bfq_get_batch_invariant",
     "bfq_moe_align_workspace_bytes", "bfq_moe_align", "bfq_moe_select_tile",
     "bfq_moe_gemm_workspace_bytes", "bfq_moe_block_gemm", "bfq_moe_num_tile_candidates",
-    "bfq_moe_get_tile_candidate", "bfq_probe_mfma_peak", "bfq_probe_mfma_flops",
+    "bfq_moe_get_tile_candidate", "bfq_block_gemm_noalloc", "bfq_noalloc_scratch_bytes",
+    "bfq_probe_mfma_peak", "bfq_probe_mfma_flops",
 )
 
 
@@ -130,6 +131,9 @@ def _load():
         "bfq_moe_num_tile_candidates": (i32, [i32, i32]),
         "bfq_moe_get_tile_candidate": (i32, [i32, i32, i32, tp]),
         "bfq_get_batch_invariant": (i32, []),
+        "bfq_block_gemm_noalloc": (i32, [p, p, i32, i64, p, p, i32, i32, p, i64, i64, i64, bs,
+                                         i32, i32, tp, p]),
+        "bfq_noalloc_scratch_bytes": (sz, []),
         "bfq_probe_mfma_peak": (i32, [i64, i64, p, p]),
         "bfq_probe_mfma_flops": (ctypes.c_double, [i64, i64]),
     }
@@ -414,6 +418,36 @@ def bfq_block_gemm(a_q, a_scales, w_q, w_scales, out, a_layout=BFQ_SCALES_ROW_MA
                             _qdtype(a_q), _odtype(out), ctypes.byref(tile) if tile else None,
                             _ptr(workspace), workspace_bytes, _stream(stream))
     return _check(st, "bfq_block_gemm", warn_key=(N, K))
+
+
+def bfq_block_gemm_noalloc(a_q, a_scales, w_q, w_scales, out, a_layout=BFQ_SCALES_ROW_MAJOR,
+                           a_scale_ld=None, tile=None, block_shape=BLOCK_SHAPE, stream=None,
+                           w_layout=BFQ_W_ROW_MAJOR, scale_fmt=BFQ_SCALE_FP32) -> int:
+    """bfq_block_gemm without a workspace argument: split-K partials and stream-K slots use the
+    library's static device buffer (bfq_noalloc_scratch_bytes()). No allocation anywhere on
+    this path; calls that overlap on one GPU race."""
+    M, K = _shape2(a_q, "a_q")
+    N = _shape2(w_q, "w_q")[0]
+    if a_scale_ld is None:
+        a_scale_ld = a_scales.stride(0)
+    _rows(a_q, "a_q", CODE_DTYPES, M, K)
+    _rows(w_q, "w_q", CODE_DTYPES, N, K)
+    _same_codes(a_q, w_q)
+    per_channel = tuple(block_shape)[0] == 1
+    _scales(a_scales, "a_scales", a_layout, a_scale_ld, M, 1 if per_channel else K // 128,
+            write=False)
+    _flat(w_scales, "w_scales", ("float32",), N if per_channel else (N // 128) * (K // 128))
+    _rows(out, "out", OUT_DTYPES, M, N)
+    _devices(a_q=a_q, a_scales=a_scales, w_q=w_q, w_scales=w_scales, out=out)
+    st = lib.bfq_block_gemm_noalloc(_ptr(a_q), _ptr(a_scales), a_layout, a_scale_ld, _ptr(w_q),
+                                    _ptr(w_scales), w_layout, scale_fmt, _ptr(out), M, N, K,
+                                    _block_shape(block_shape), _qdtype(a_q), _odtype(out),
+                                    ctypes.byref(tile) if tile else None, _stream(stream))
+    return _check(st, "bfq_block_gemm_noalloc", warn_key=(N, K))
+
+
+def bfq_noalloc_scratch_bytes() -> int:
+    return int(lib.bfq_noalloc_scratch_bytes())
 
 
 def bfq_load_tile_table(path=None) -> int:

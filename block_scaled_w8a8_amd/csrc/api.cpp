@@ -23,6 +23,10 @@
 
 using namespace bfq;
 
+// Workspace of the allocation-free GEMM entry point (bfq_block_gemm_noalloc, below).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -358,6 +362,49 @@ size_t workspace_for(int64_t M, int64_t N, const bfq_tile& t) {
     return t.split_k > 1 ? (size_t)t.split_k * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
+// ------------------------------------------------------ allocation-free entry point ----
+// The workspace of bfq_block_gemm_noalloc: a device array of this file, one copy per GPU,
+// resident from the library's load until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: its device address on the current GPU comes from
+// hipGetSymbolAddress (looked up once per device, on the first call that needs it) and only
+// that address is ever handed to a kernel. Every call on one GPU shares the array, so calls
+// that overlap on one GPU race; nothing in it needs to start at zero (split-K partials and
+// stream-K slots are written before they are read).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_on_current_device(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// A selected tile made to fit the static scratch: stream-K becomes the plain grid of the same
+// tile (when that kernel is compiled), and the K split drops until its partials fit.
+bfq_tile fit_scratch(bfq_tile t, int64_t M, int64_t N, int qtype, int otype, int wl, int sf) {
+    if (t.variant == 2 && workspace_for(M, N, t) > kNoAllocScratchBytes) {
+        bfq_tile p = t;
+        p.variant = 0;
+        p.split_k = 1;
+        if (find_kernel(p, qtype, otype, wl, sf)) t = p;
+    }
+    while (t.variant != 2 && t.split_k > 1 && workspace_for(M, N, t) > kNoAllocScratchBytes)
+        --t.split_k;
+    return t;
+}
+
 }  // namespace
 
 // ================================================================== C-ABI ====
@@ -506,12 +553,19 @@ size_t bfq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const bfq_tile*
     return workspace_for(M, N, t);
 }
 
-bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
-                          int64_t a_scale_ld, const void* w_q, const float* w_scales,
-                          bfq_weight_layout w_layout, bfq_scale_format scale_fmt, void* out,
-                          int64_t M, int64_t N, int64_t K, const int32_t block_shape[2],
-                          bfq_dtype in_dtype, bfq_dtype out_dtype, const bfq_tile* tile,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The block GEMM behind bfq_block_gemm and bfq_block_gemm_noalloc. noalloc: the workspace is
+// the library's static scratch (kNoAllocScratchBytes); a selected (tile == NULL) tile whose
+// workspace would not fit it is reduced to one that does, an explicit one is rejected.
+bfq_status block_gemm_impl(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
+                           int64_t a_scale_ld, const void* w_q, const float* w_scales,
+                           bfq_weight_layout w_layout, bfq_scale_format scale_fmt, void* out,
+                           int64_t M, int64_t N, int64_t K, const int32_t block_shape[2],
+                           bfq_dtype in_dtype, bfq_dtype out_dtype, const bfq_tile* tile,
+                           void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
     if (!w_q || !w_scales || !block_shape || (M != 0 && (!a_q || !a_scales || !out)))
         return fail(BFQ_ERR_NULL, "a_q, a_scales, w_q, w_scales, out and block_shape must be non-NULL");
     int sf = (int)scale_fmt;
@@ -565,8 +619,9 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
         status = select_tile(M, N, K, qtype, wl, sf, &t);
     }
     // a packed-word tile is selected like a UE8M0 one, then served by a kernel that reads words
-    const KernelEntry* ke =
-        find_kernel(t, qtype, otype, wl, a_layout == BFQ_SCALES_PACKED_UE8M0 ? S_PACKED : sf);
+    const int ksf = a_layout == BFQ_SCALES_PACKED_UE8M0 ? S_PACKED : sf;
+    if (noalloc && !tile) t = fit_scratch(t, M, N, qtype, otype, wl, ksf);
+    const KernelEntry* ke = find_kernel(t, qtype, otype, wl, ksf);
     if (!ke)
         return fail(BFQ_ERR_TILE, "tile does not name a compiled kernel for this dtype pair, weight "
                                   "layout and scale format / granularity");
@@ -577,7 +632,11 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
     if (t.variant != 1 && (t.group_m < 1 || t.raster < 0 || t.raster > 1))
         return fail(BFQ_ERR_TILE, "group_m must be >= 1 and raster 0 or 1");
     const size_t need = workspace_for(M, N, t);
-    if (need > 0 && (!workspace || workspace_bytes < need))
+    if (noalloc && need > kNoAllocScratchBytes)
+        return fail(BFQ_ERR_WORKSPACE, "the tile needs " + std::to_string(need) +
+                                           " bytes of workspace; the allocation-free entry point "
+                                           "holds " + std::to_string(kNoAllocScratchBytes));
+    if (!noalloc && need > 0 && (!workspace || workspace_bytes < need))
         return fail(BFQ_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
     // grid-size limits of the launchers
     if (t.variant != 1) {
@@ -587,6 +646,10 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
         return fail(BFQ_ERR_SHAPE, "M too large for the swap-AB kernel; use a standard tile");
     }
     if (M == 0) return status;
+    if (noalloc && need > 0) {
+        hipError_t e = scratch_on_current_device(&workspace);
+        if (e != hipSuccess) return fail(BFQ_ERR_HIP, std::string("scratch lookup: ") + hipGetErrorString(e));
+    }
 
     GemmArgs ga;
     ga.a = a_q;
@@ -616,6 +679,34 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
                      (long long)M, (long long)N, (long long)K, wl, sf, t.variant, t.bm, t.bn, t.split_k);
     return status;
 }
+
+}  // namespace
+
+extern "C" {
+
+bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
+                          int64_t a_scale_ld, const void* w_q, const float* w_scales,
+                          bfq_weight_layout w_layout, bfq_scale_format scale_fmt, void* out,
+                          int64_t M, int64_t N, int64_t K, const int32_t block_shape[2],
+                          bfq_dtype in_dtype, bfq_dtype out_dtype, const bfq_tile* tile,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return block_gemm_impl(a_q, a_scales, a_layout, a_scale_ld, w_q, w_scales, w_layout,
+                           scale_fmt, out, M, N, K, block_shape, in_dtype, out_dtype, tile,
+                           workspace, workspace_bytes, stream, false);
+}
+
+bfq_status bfq_block_gemm_noalloc(const void* a_q, const float* a_scales,
+                                  bfq_scale_layout a_layout, int64_t a_scale_ld, const void* w_q,
+                                  const float* w_scales, bfq_weight_layout w_layout,
+                                  bfq_scale_format scale_fmt, void* out, int64_t M, int64_t N,
+                                  int64_t K, const int32_t block_shape[2], bfq_dtype in_dtype,
+                                  bfq_dtype out_dtype, const bfq_tile* tile, void* stream) {
+    return block_gemm_impl(a_q, a_scales, a_layout, a_scale_ld, w_q, w_scales, w_layout,
+                           scale_fmt, out, M, N, K, block_shape, in_dtype, out_dtype, tile,
+                           nullptr, 0, stream, true);
+}
+
+size_t bfq_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 bfq_status bfq_load_tile_table(const char* json_path) {
     std::lock_guard<std::mutex> lk(g_table_mu);

@@ -13,7 +13,7 @@
  * Conventions for every entry point:
  *  - Device pointers unless marked "host". Every buffer is allocated and freed by the
  *    caller; the library never allocates, frees or synchronizes device memory. It owns only
- *    its host-side tile table.
+ *    its host-side tile table and the static device buffer of bfq_block_gemm_noalloc.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is enqueued
  *    asynchronously; the call returns once the launches are enqueued.
  *  - All arguments are validated before anything is enqueued. On a negative status nothing
@@ -222,6 +222,29 @@ bfq_status bfq_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layo
                           const int32_t block_shape[2] /* host */, bfq_dtype in_dtype,
                           bfq_dtype out_dtype, const bfq_tile* tile /* host */,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* The block GEMM for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments and
+ * result as bfq_block_gemm without a workspace; split-K partials and stream-K slots go to a
+ * static device buffer of the library (bfq_noalloc_scratch_bytes() = 32 MiB, one per GPU,
+ * held from the library's load until the process ends). It calls no allocator.
+ *   tile NULL -> the tile bfq_select_tile gives, made to fit the buffer: a stream-K tile runs
+ *   as the plain grid of the same tile, and the K split drops until the partials fit (the
+ *   result stays within the parity bar; it may differ in the last bits from bfq_block_gemm,
+ *   which runs the selected tile as is).
+ *   An explicit tile whose workspace exceeds the buffer -> BFQ_ERR_WORKSPACE (nothing
+ *   launched).
+ * Every call on one GPU shares that GPU's buffer: calls that overlap on one GPU (different
+ * streams, or host threads) race and must be serialised by the caller. The buffer keeps the
+ * last call's contents; no call reads what an earlier one left. */
+bfq_status bfq_block_gemm_noalloc(const void* a_q, const float* a_scales,
+                                  bfq_scale_layout a_layout, int64_t a_scale_ld, const void* w_q,
+                                  const float* w_scales, bfq_weight_layout w_layout,
+                                  bfq_scale_format scale_fmt, void* out, int64_t M, int64_t N,
+                                  int64_t K, const int32_t block_shape[2] /* host */,
+                                  bfq_dtype in_dtype, bfq_dtype out_dtype,
+                                  const bfq_tile* tile /* host */, void* stream);
+size_t bfq_noalloc_scratch_bytes(void);
 
 /* Load a tile table (JSON, host path) and replace the current one ([CONFIG] §2 schema:
  * per (N, K, dtype, block_shape) a map "M bucket -> launch parameters"). Must not run

@@ -638,3 +638,32 @@ def test_probe_validation_without_launch(bfq):
     assert f(4, 10, FAKE + 2, None) == bfq.BFQ_ERR_ALIGN
     # 8 waves x 8 chains x iters x (2 * 16 * 16 * 128) flops per workgroup
     assert bfq.lib.bfq_probe_mfma_flops(3, 5) == 3 * 8 * 8 * 5 * 65536
+
+
+def test_noalloc_validation_without_launch(bfq):
+    """The allocation-free GEMM validates like bfq_block_gemm and rejects, before any launch,
+    explicit tiles whose workspace exceeds its static buffer (stream-K slots, large split-K)."""
+    f = bfq.lib.bfq_block_gemm_noalloc
+    base = [FAKE, FAKE, 0, 56, FAKE, FAKE, 0, 0, FAKE, 0, 24576, 7168, BS, bfq.BFQ_E4M3FN,
+            bfq.BFQ_BF16, None, None]
+
+    def call(**kw):
+        a = list(base)
+        names = ["a_q", "a_scales", "a_layout", "ld", "w_q", "w_scales", "w_layout", "sfmt",
+                 "out", "M", "N", "K", "bs", "qd", "od", "tile", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert bfq.bfq_noalloc_scratch_bytes() == 32 << 20
+    assert call() >= 0                                   # M = 0: nothing launched
+    assert call(w_q=None) == bfq.BFQ_ERR_NULL
+    assert call(K=7000) == bfq.BFQ_ERR_SHAPE
+    assert call(w_q=FAKE + 8) == bfq.BFQ_ERR_ALIGN
+    cands = [bfq.bfq_get_tile_candidate(i) for i in range(bfq.bfq_num_tile_candidates())]
+    sk = next(t for t in cands if t.variant == 2)
+    assert call(M=1024, tile=ctypes.pointer(sk)) == bfq.BFQ_ERR_WORKSPACE
+    assert "allocation-free" in bfq.last_error()
+    t = bfq.bfq_get_tile_candidate(0)
+    t.split_k = 4                                        # 4 * 1024 * 24576 * 4 bytes
+    assert call(M=1024, tile=ctypes.pointer(t)) == bfq.BFQ_ERR_WORKSPACE
