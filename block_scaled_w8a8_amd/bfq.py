@@ -10,7 +10,9 @@ import os
 import warnings
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libbfq.so")
+# BFQ_LIBRARY names another build of the same library (for example one whose host code is
+# built with sanitizers); by default the in-tree libbfq.so.
+LIB_PATH = os.environ.get("BFQ_LIBRARY") or os.path.join(HERE, "libbfq.so")
 
 # status codes (bfq_status)
 BFQ_OK = 0

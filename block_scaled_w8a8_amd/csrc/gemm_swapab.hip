@@ -299,8 +299,8 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_kernel(GemmArgs 
 // Swap-AB with the token fragments shared through LDS (sched 1). The waves of a workgroup
 // that work on the same K slice (the NWAVES strips of one wk group) need the same token
 // fragments, so instead of every wave fetching them from L2 (MT/NWR times the bytes of its
-// weight stream), each K block's MT x 128 token bytes are fetched once per wk group: the 2*SM
-// fragment halves of 1 KB are dealt over the group's waves, and the token scales go to the
+// weight stream), each K block's MT x 128 token bytes are fetched once per wk group: the MT/8
+// loads of 8 whole token rows (1 KB) are dealt over the group's waves, and the token scales go to the
 // group's last wave. Those loads travel in the same D-deep register ring as the weights (so
 // the in-order completion of vector loads never shortens the weight prefetch distance); at
 // step i they are written to LDS buffer i & 1, one barrier later every wave reads them back
@@ -311,7 +311,7 @@ template <int MT, int NWR, int NWAVES, int KW, int D, int QT, int OT, int WL, in
 __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmArgs p) {
     static_assert(!MOE || CH != 1, "grouped tiles take block scales");
     constexpr int SM = MT / 16, SN = NWR / 16;
-    constexpr int AI = 2 * SM;                              // 1 KB token halves per K block
+    constexpr int AI = 2 * SM;                              // 1 KB token loads per K block
     constexpr int API = (AI + NWAVES - 1) / NWAVES;         // at most this many per wave
     constexpr int SLOT = MT * 128 + MT * 4;                 // token codes + token scales
     constexpr int SCW = (MT + 63) / 64;                     // token scales per lane of the scale wave
@@ -371,17 +371,25 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
     auto src_row = [&](int64_t r) -> int64_t {
         return r < rows_a ? (int64_t)p.moe_rows[sp.p0 + r] / p.moe_topk : -1;
     };
-    // token halves this wave fetches: j = wn + NWAVES * t (sub-tile j >> 1, K half j & 1)
-    uint32_t a_voff[API];
+    // Token rows this wave fetches: load t covers the 8 rows 8q .. 8q+7 of a K block
+    // (q = wn + NWAVES * t), each as one whole 128-byte line: lane l reads row 8q + (l & 7),
+    // bytes 16c .. 16c+15 with c = l >> 3. (Loading fragment halves directly would request
+    // every line twice, 64 bytes each time.) In LDS those bytes belong to fragment half
+    // j = 2*(r/16) + c/4 at the slot of the lane that feeds row r % 16 with K chunk c % 4,
+    // so the readers below take lane-ordered fragment halves; the 8 lanes of one chunk write
+    // 128 contiguous bytes (no bank conflicts).
+    uint32_t a_voff[API], a_lds[API];
 #pragma unroll
     for (int t = 0; t < API; ++t) {
-        const int j = wn + NWAVES * t;
-        const int64_t r = (j >> 1) * 16 + frow;
+        const int q = wn + NWAVES * t;
+        const int c = lane >> 3;
+        const int64_t r = q * 8 + (lane & 7);
+        a_lds[t] = (uint32_t)((2 * (r >> 4) + (c >> 2)) * 1024 + ((c & 3) * 16 + (r & 15)) * 16);
         if constexpr (MOE) {
-            const int64_t tok = j < AI ? src_row(r) : -1;
-            a_voff[t] = tok >= 0 ? (uint32_t)(tok * K + 64 * (j & 1) + 16 * fgrp) : kNoLoad;
+            const int64_t tok = q < AI ? src_row(r) : -1;
+            a_voff[t] = tok >= 0 ? (uint32_t)(tok * K + 16 * c) : kNoLoad;
         } else {
-            a_voff[t] = j < AI ? (uint32_t)(r * K + 64 * (j & 1) + 16 * fgrp) : kNoLoad;
+            a_voff[t] = q < AI ? (uint32_t)(r * K + 16 * c) : kNoLoad;
         }
     }
     // token scales (last wave of the group): scale slot x = r * SM + s holds token s * 16 + r,
@@ -449,10 +457,8 @@ __global__ __launch_bounds__(64 * NWAVES * KW) void gemm_swapab_lds_kernel(GemmA
     auto step = [&](int r, int64_t i) {
         uint8_t* buf = tok[wk][i & 1];
 #pragma unroll
-        for (int t = 0; t < API; ++t) {
-            const int j = wn + NWAVES * t;
-            if (j < AI) *reinterpret_cast<v4i*>(buf + j * 1024 + lane * 16) = abuf[r][t];
-        }
+        for (int t = 0; t < API; ++t)
+            if (wn + NWAVES * t < AI) *reinterpret_cast<v4i*>(buf + a_lds[t]) = abuf[r][t];
         if (!CHAN && scale_wave) {
             // packed words are decoded here, once per token, so every wave reads fp32 scales
 #pragma unroll
