@@ -56,5 +56,52 @@ def build(jobs: int = 8) -> str:
     return LIB_PATH
 
 
+# A build whose host code (argument validation, tile selection, the tile-table parser) runs
+# under AddressSanitizer and UndefinedBehaviorSanitizer; the device code is the same. Loaded
+# through BFQ_LIBRARY by a process that preloads the sanitizer runtime (sanitizer_runtime());
+# the CPU tests run against it (tests/test_sanitizers.py).
+ASAN_LIB_PATH = os.path.join(HERE, "libbfq_asan.so")
+HOST_SOURCES = ("api.cpp", "tile_table.cpp")
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-O1"]
+def sanitizer_runtime() -> str:
+    """The clang AddressSanitizer runtime matching hipcc (it carries the UBSan handlers)."""
+    import glob
+    hits = glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "lib", "llvm", "lib",
+                                  "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no clang AddressSanitizer runtime found next to hipcc")
+    return sorted(hits)[-1]
+
+
+def build_sanitized(jobs: int = 8) -> str:
+    """libbfq_asan.so: the host sources built with -fsanitize=address,undefined, linked with
+    the kernel objects of the regular build (compiled first if they are missing)."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    objs = []
+    todo = []
+    for src in SOURCES:
+        obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+        if src in HOST_SOURCES:
+            obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".asan.o")
+            cmd = [HIPCC, *COMMON, *DEVICE, *SANITIZE, "-c", os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
+        elif not os.path.exists(obj):
+            todo.append(src)
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(_compile, todo))
+    tmp = ASAN_LIB_PATH + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs, "-ldl",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-shared-libsan"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, ASAN_LIB_PATH)
+    return ASAN_LIB_PATH
+
+
 if __name__ == "__main__":
     print(build())

@@ -50,13 +50,17 @@ typedef enum {
     BFQ_ERR_ARG = -9            /* invalid scalar argument (eps, enum value, index) */
 } bfq_status;
 
+/* The *_INT32_RANGE_ enumerators below are not values of their enums: they make each enum a
+ * 32-bit type in which every int32 is representable, so that an out-of-range argument from a
+ * C or ctypes caller is rejected (BFQ_ERR_ARG / BFQ_ERR_DTYPE) rather than undefined. */
 typedef enum {
     BFQ_BF16 = 0,
     BFQ_FP16 = 1,
     BFQ_FP32 = 2,
     BFQ_E4M3FN = 3,   /* OCP float8 e4m3fn, max 448 */
     BFQ_INT8 = 4,     /* symmetric int8 in [-127, 127] */
-    BFQ_INT32 = 5
+    BFQ_INT32 = 5,
+    BFQ_DTYPE_INT32_RANGE_ = 0x7FFFFFFF  /* not a dtype: see below */
 } bfq_dtype;
 
 /* Layout of per-(token, group) activation scales, [BENCH] §4.1 (row-major for the Triton
@@ -72,7 +76,8 @@ typedef enum {
 typedef enum {
     BFQ_SCALES_ROW_MAJOR = 0,    /* s[m * ld + g], ld >= K/128 */
     BFQ_SCALES_COL_MAJOR = 1,    /* s[g * ld + m], ld >= M     */
-    BFQ_SCALES_PACKED_UE8M0 = 2  /* words[w * ld + m], see above */
+    BFQ_SCALES_PACKED_UE8M0 = 2, /* words[w * ld + m], see above */
+    BFQ_SCALES_INT32_RANGE_ = 0x7FFFFFFF
 } bfq_scale_layout;
 
 /* Layout of the weight codes in memory. The values are the same bytes either way; the packed
@@ -86,7 +91,8 @@ typedef enum {
  *                    The whole matrix still spans N*K bytes, rows in blocks of 16. */
 typedef enum {
     BFQ_W_ROW_MAJOR = 0,
-    BFQ_W_PACKED16 = 1
+    BFQ_W_PACKED16 = 1,
+    BFQ_W_INT32_RANGE_ = 0x7FFFFFFF
 } bfq_weight_layout;
 
 /* Format of the fp32 scales. UE8M0: every scale is a power of two — the block's
@@ -97,7 +103,8 @@ typedef enum {
  * block-scaled MFMA instead of with one fp32 FMA per output and K block. */
 typedef enum {
     BFQ_SCALE_FP32 = 0,
-    BFQ_SCALE_UE8M0 = 1
+    BFQ_SCALE_UE8M0 = 1,
+    BFQ_SCALE_INT32_RANGE_ = 0x7FFFFFFF
 } bfq_scale_format;
 
 /* One launch configuration of the block GEMM ([CONFIG] §2: per-M launch parameters).

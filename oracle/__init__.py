@@ -19,7 +19,10 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 BUILD_DIR = os.path.join(HERE, "_build")
-LIB_PATH = os.path.join(BUILD_DIR, "liboracle.so")
+# ORACLE_LIBRARY names another build of oracle.c (the sanitizer build below); by default the
+# gcc build.
+LIB_PATH = os.environ.get("ORACLE_LIBRARY") or os.path.join(BUILD_DIR, "liboracle.so")
+ASAN_LIB_PATH = os.path.join(BUILD_DIR, "liboracle_asan.so")
 
 FP8 = 0
 INT8 = 1
@@ -40,6 +43,21 @@ def build(force: bool = True) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+def build_sanitized(clang: str = "/opt/rocm/llvm/bin/clang") -> str:
+    """oracle.c under AddressSanitizer and UndefinedBehaviorSanitizer, built with the clang
+    whose sanitizer runtime the process preloads (the same runtime as the library's
+    sanitizer build). Same arithmetic flags as build(); OpenMP from clang's libomp."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tmp = ASAN_LIB_PATH + ".tmp"
+    cmd = [clang, "-std=c11", "-O1", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+           "-shared", "-Wall", "-Wextra", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-shared-libsan",
+           "-o", tmp, os.path.join(HERE, "oracle.c"), "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, ASAN_LIB_PATH)
+    return ASAN_LIB_PATH
 
 
 _lib = None
