@@ -1,7 +1,7 @@
 """On-device tile sweep that fills the tile table, and a single-shape runner for profiling.
 
-  python -m block_scaled_w8a8_amd.sweep tune  [--shapes N,K ...] [--dtype fp8|int8]
-                                             [--scales fp32|ue8m0|channel]
+  python -m block_scaled_w8a8_amd.sweep tune  --reference PATH [--shapes N,K ...]
+                                             [--dtype fp8|int8] [--scales fp32|ue8m0|channel]
                                              [--w-layout row|packed] [--out PATH]
                                              [--grid M ...] [--force | --merge]
   python -m block_scaled_w8a8_amd.sweep run   --M 4096 --N 24576 --K 7168 [--tile JSON] [--iters 50]
@@ -14,7 +14,10 @@
 `tune` follows the tuning flow of the config-mechanism page ("vLLM 量化 Kernel 配置机制 ...",
 §3.3): for every (N, K) and every M of the 18-point grid, every compiled kernel configuration
 (combined with split-K factors) is launched after warm-up and timed with events; the fastest
-one whose output agrees with a reference configuration is kept. Configurations the library
+one whose output meets the parity bar against expected values is kept. The expected values
+are the oracle's fp32 outputs at seeded sample positions of the same seeded inputs, read
+from a numpy file that `python -m oracle.sweep_reference` writes (--reference); this module
+never imports the oracle. Configurations the library
 rejects (grid or workspace limits) are skipped, like the page's OutOfResources candidates.
 Results are written to a JSON tile table after every shape, and shapes already present in the
 output file are skipped, so an interrupted sweep resumes where it stopped (--force retunes
@@ -167,7 +170,7 @@ def candidates(qd, M, N, K, wl=0, sf=0, block_shape=(128, 128)):
 
 def agrees(a, b) -> bool:
     """Parity gate between two fp32 outputs of the same inputs (different tiles): relative
-    Frobenius <= 1e-3 and max |diff| <= 2^-7 rms + 1e-3."""
+    Frobenius <= 1e-3 and max |diff| <= 2^-7 rms + 1e-3. Used by the grouped (MoE) tuner."""
     import torch
     a64, b64 = a.double(), b.double()
     den = torch.linalg.norm(b64)
@@ -177,7 +180,48 @@ def agrees(a, b) -> bool:
     return rf <= 1e-3 and md <= 2.0 ** -7 * rms + 1e-3
 
 
-def tune_shape(N, K, qname, grid, budget_s, w_layout="row", scales="fp32"):
+def reference_key(N, K, dtype, scales, M) -> str:
+    """Key of one (shape, code type, scale format, M) in the expected-value file that the
+    oracle's sweep_reference script writes."""
+    return f"{N}x{K}:{dtype}:{scales}:{M}"
+
+
+def meets_bar(got, ref) -> bool:
+    """The parity bar on sampled fp32 outputs against the expected values: relative
+    Frobenius <= 1e-3 and max |diff| <= 2^-7 * rms(expected) + 1e-3."""
+    import numpy as np
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    if g.shape != r.shape or not np.isfinite(g).all():
+        return False
+    den = np.linalg.norm(r)
+    rf = np.linalg.norm(g - r) / den if den > 0 else np.linalg.norm(g)
+    md = np.abs(g - r).max() if g.size else 0.0
+    rms = np.sqrt((r * r).mean()) if r.size else 0.0
+    return bool(rf <= 1e-3 and md <= 2.0 ** -7 * rms + 1e-3)
+
+
+class Reference:
+    """Expected sampled outputs (numpy .npz written by the oracle's sweep_reference script)."""
+
+    def __init__(self, path):
+        import numpy as np
+        self.path = path
+        self.data = np.load(path, allow_pickle=False)
+
+    def get(self, N, K, dtype, scales, M):
+        k = reference_key(N, K, dtype, scales, M)
+        if k + ":ref" not in self.data.files:
+            raise SystemExit(f"{self.path} has no expected values for {k}; write them with "
+                             f"python -m oracle.sweep_reference --out {self.path} "
+                             f"--shapes {N},{K} --dtype {dtype} --scales {scales}")
+        return self.data[k + ":ms"], self.data[k + ":ns"], self.data[k + ":ref"]
+
+
+def tune_shape(N, K, qname, grid, budget_s, reference, w_layout="row", scales="fp32"):
+    """Every candidate of every M of the grid: launched, gated on the expected values (the
+    oracle's, at sampled positions, from `reference`), then timed; the fastest passing one
+    is kept."""
     import torch
 
     from . import bfq
@@ -185,11 +229,9 @@ def tune_shape(N, K, qname, grid, budget_s, w_layout="row", scales="fp32"):
     results = {}
     for M in grid:
         t0 = time.time()
-        _, ref_tile = bfq.bfq_select_tile(M, N, K, prob.qd, bfq.BFQ_FP32, w_layout=prob.wl,
-                                          scale_fmt=prob.sf, block_shape=prob.bs)
-        prob.launch(M, ref_tile, out32=True)
-        torch.cuda.synchronize()
-        ref = prob.out32[:M].clone()
+        ms, ns, ref = reference.get(N, K, qname, scales, M)
+        ms_d = torch.from_numpy(ms).to("cuda:0")
+        ns_d = torch.from_numpy(ns).to("cuda:0")
         best = None
         trials = []
         for tile in candidates(prob.qd, M, N, K, prob.wl, prob.sf, prob.bs):
@@ -200,7 +242,7 @@ def tune_shape(N, K, qname, grid, budget_s, w_layout="row", scales="fp32"):
                 torch.cuda.synchronize()
             except bfq.BfqError:
                 continue                           # rejected: limits of this configuration
-            if not agrees(prob.out32[:M], ref):
+            if not meets_bar(prob.out32[ms_d, ns_d].cpu().numpy(), ref):
                 log(f"  parity gate rejected {tile.as_dict()} at M={M}")
                 continue
             us = prob.time_us(M, tile)
@@ -389,6 +431,7 @@ def save_table(path, table):
 
 def cmd_tune(args):
     qname = args.dtype
+    reference = Reference(args.reference)
     shapes = [tuple(int(v) for v in s.split(",")) for s in args.shapes] if args.shapes \
         else DEFAULT_SHAPES[qname]
     table = load_table(args.out)
@@ -407,7 +450,8 @@ def cmd_tune(args):
             log(f"[sweep] N={N} K={K} {dname} {wname} {args.scales}: already in {args.out}, skipped")
             continue
         log(f"[sweep] N={N} K={K} {dname} {wname} {args.scales}")
-        res = tune_shape(N, K, qname, args.grid or M_GRID, args.budget, args.w_layout, args.scales)
+        res = tune_shape(N, K, qname, args.grid or M_GRID, args.budget, reference, args.w_layout,
+                         args.scales)
         entry = {"N": N, "K": K, "dtype": dname,
                  "block_shape": [1, K] if args.scales == "channel" else [128, 128],
                  "configs": {str(M): {k: v for k, v in t.items() if k != "bk"}
@@ -480,6 +524,8 @@ def main():
                    help="retune only the --grid batch sizes of an existing entry, keep its other M")
     t.add_argument("--w-layout", default="row", choices=["row", "packed"])
     t.add_argument("--scales", default="fp32", choices=["fp32", "ue8m0", "channel"])
+    t.add_argument("--reference", required=True,
+                   help="expected sampled outputs (python -m oracle.sweep_reference --out PATH)")
     r = sub.add_parser("run")
     r.add_argument("--M", type=int, required=True)
     r.add_argument("--N", type=int, required=True)
