@@ -157,8 +157,7 @@ def run_gpu(args, wl):
                                    workspace_bytes=sh["ws_max"], w_layout=wlay, scale_fmt=sfmt,
                                    block_shape=sh["bs"])
 
-    for _ in range(args.warmup):
-        one_step()
+    one_step()                        # eager reference result for the graph check
     torch.cuda.synchronize()
     eager_out = [sh["out"].clone() for sh in shapes]
 
@@ -177,6 +176,12 @@ def run_gpu(args, wl):
             graph.replay()
         else:
             one_step()
+
+    # untimed warm-up steps (the pages' protocol warms up 100 iterations before timing; the
+    # first tens of milliseconds of sustained load run measurably slower)
+    for _ in range(args.warmup):
+        replay()
+    torch.cuda.synchronize()
 
     # timed region: wall clock around exactly `steps` steps, fenced by synchronize
     torch.cuda.synchronize()
@@ -410,14 +415,15 @@ def run_gpu_moe(args, wl):
             g_once(T, tile, counter[0])
             counter[0] += 1
 
-    for _ in range(args.warmup):
-        one_step()
+    one_step()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     counter[0] = 0
     with torch.cuda.graph(graph):
         one_step()
     torch.cuda.synchronize()
+    for _ in range(args.warmup):      # untimed warm-up steps
+        graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -605,8 +611,9 @@ def cpu_baseline(wl, host, target_s: float, scales: str = "fp32"):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps before the timed ones (the pages warm up 100 iterations)")
     ap.add_argument("--workload", default="mgrid", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=3, help="weight copies rotated per launch")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
