@@ -642,6 +642,8 @@ static const KernelEntry kSwapabKernels[] = {
     BFQ_SABL_BOTH(32, 16, 8, 1, 4, Q_FP8),
     BFQ_SABL_BOTH(32, 16, 6, 1, 4, Q_FP8),
     BFQ_SABL_BOTH(32, 16, 4, 2, 4, Q_FP8),
+    BFQ_SABL_BOTH(48, 16, 6, 2, 4, Q_FP8),
+    BFQ_SABL_BOTH(48, 16, 6, 1, 4, Q_FP8),
     BFQ_SABL_BOTH(64, 16, 8, 1, 4, Q_FP8),
     BFQ_SABL_BOTH(64, 16, 6, 1, 4, Q_FP8),
     BFQ_SABL_BOTH(64, 16, 4, 2, 4, Q_FP8),
@@ -723,6 +725,8 @@ static const KernelEntry kSwapabKernels[] = {
     BFQ_SABL_PK(32, 16, 8, 1, 4, Q_FP8),
     BFQ_SABL_PK(32, 16, 6, 1, 4, Q_FP8),
     BFQ_SABL_PK(32, 16, 4, 2, 4, Q_FP8),
+    BFQ_SABL_PK(48, 16, 6, 2, 4, Q_FP8),
+    BFQ_SABL_PK(48, 16, 6, 1, 4, Q_FP8),
     BFQ_SABL_PK(64, 16, 8, 1, 4, Q_FP8),
     BFQ_SABL_PK(64, 16, 6, 1, 4, Q_FP8),
     BFQ_SABL_PK(64, 16, 4, 2, 4, Q_FP8),

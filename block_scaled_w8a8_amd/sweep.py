@@ -218,6 +218,23 @@ class Reference:
         return self.data[k + ":ms"], self.data[k + ":ns"], self.data[k + ":ref"]
 
 
+def warm_up(prob, M, seconds=1.0):
+    """About a second of sustained launches before anything is timed: the engine clock ramps
+    up over the first fraction of a second under load, which would otherwise make the first
+    candidates look slower than they are."""
+    import torch
+
+    from . import bfq
+    _, tile = bfq.bfq_select_tile(M, prob.N, prob.K, prob.qd, bfq.BFQ_BF16, w_layout=prob.wl,
+                                  scale_fmt=prob.sf, block_shape=prob.bs)
+    t0, i = time.time(), 0
+    while time.time() - t0 < seconds:
+        for _ in range(8):
+            prob.launch(M, tile, i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def tune_shape(N, K, qname, grid, budget_s, reference, w_layout="row", scales="fp32"):
     """Every candidate of every M of the grid: launched, gated on the expected values (the
     oracle's, at sampled positions, from `reference`), then timed; the fastest passing one
@@ -226,6 +243,7 @@ def tune_shape(N, K, qname, grid, budget_s, reference, w_layout="row", scales="f
 
     from . import bfq
     prob = Problem(N, K, max(grid), qname, w_layout=w_layout, scales=scales)
+    warm_up(prob, max(grid))
     results = {}
     for M in grid:
         t0 = time.time()
