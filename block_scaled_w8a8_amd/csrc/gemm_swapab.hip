@@ -807,30 +807,59 @@ const KernelEntry* swapab_kernels(int* count) {
 }
 
 // ------------------------------------------------------------ split-K reduce ----
-template <int OT>
+// out[i] = sum over z of part[z][i], added in z order (so results are run-to-run identical
+// and do not depend on the split kernel's timing). The partial loads of B splits are all
+// issued before any is waited on (B >= split: one memory round trip, rather than one per
+// split, which is what the reduce of a small output costs); slots past the last split
+// re-read the last partial, which stays in cache, and are not added.
+template <int OT, int B>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             void* __restrict__ out,
                                                             int64_t MN, int split) {
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= MN) return;                       // MN is a multiple of 128
-    v4f s = *reinterpret_cast<const v4f*>(part + i);
-    for (int z = 1; z < split; ++z) {
-        const v4f t = *reinterpret_cast<const v4f*>(part + (int64_t)z * MN + i);
-        s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+    const float* p = part + i;
+    v4f s = *reinterpret_cast<const v4f*>(p);
+    for (int z0 = 1; z0 < split; z0 += B) {
+        v4f t[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int z = z0 + j < split ? z0 + j : split - 1;
+            t[j] = *reinterpret_cast<const v4f*>(p + (int64_t)z * MN);
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const bool live = z0 + j < split;
+            const v4f u = {s.x + t[j].x, s.y + t[j].y, s.z + t[j].z, s.w + t[j].w};
+            s = live ? u : s;
+        }
     }
     store4<OT>(out, i, s);
+}
+
+template <int OT>
+static void launch_reduce_ot(const float* partials, void* out, int64_t MN, int split,
+                             hipStream_t stream) {
+    dim3 grid((unsigned)((MN / 4 + 255) / 256));
+    if (split <= 3)
+        hipLaunchKernelGGL((splitk_reduce_kernel<OT, 2>), grid, dim3(256), 0, stream, partials, out, MN, split);
+    else if (split <= 5)
+        hipLaunchKernelGGL((splitk_reduce_kernel<OT, 4>), grid, dim3(256), 0, stream, partials, out, MN, split);
+    else if (split <= 9)
+        hipLaunchKernelGGL((splitk_reduce_kernel<OT, 8>), grid, dim3(256), 0, stream, partials, out, MN, split);
+    else
+        hipLaunchKernelGGL((splitk_reduce_kernel<OT, 16>), grid, dim3(256), 0, stream, partials, out, MN, split);
 }
 
 hipError_t launch_splitk_reduce(const float* partials, void* out, int64_t M, int64_t N,
                                 int split, int otype, hipStream_t stream) {
     const int64_t MN = M * N;
-    dim3 grid((unsigned)((MN / 4 + 255) / 256));
     if (otype == O_BF16)
-        hipLaunchKernelGGL(splitk_reduce_kernel<O_BF16>, grid, dim3(256), 0, stream, partials, out, MN, split);
+        launch_reduce_ot<O_BF16>(partials, out, MN, split, stream);
     else if (otype == O_FP16)
-        hipLaunchKernelGGL(splitk_reduce_kernel<O_FP16>, grid, dim3(256), 0, stream, partials, out, MN, split);
+        launch_reduce_ot<O_FP16>(partials, out, MN, split, stream);
     else
-        hipLaunchKernelGGL(splitk_reduce_kernel<O_FP32>, grid, dim3(256), 0, stream, partials, out, MN, split);
+        launch_reduce_ot<O_FP32>(partials, out, MN, split, stream);
     return hipGetLastError();
 }
 
