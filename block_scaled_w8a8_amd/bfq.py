@@ -479,7 +479,7 @@ def bfq_moe_align(topk_ids, E, expert_offsets, sorted_pairs, workspace=None, str
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _rows(topk_ids, "topk_ids", ("int32",), T, topk)
     _flat(expert_offsets, "expert_offsets", ("int32",), E + 1)
-    _flat(sorted_pairs, "sorted_pairs", ("int32",), T * topk)
+    _flat(sorted_pairs, "sorted_pairs", ("int32",), T * topk, exact=False)
     _workspace(workspace, need)
     _devices(topk_ids=topk_ids, expert_offsets=expert_offsets, sorted_pairs=sorted_pairs,
              workspace=workspace)
@@ -523,7 +523,7 @@ def bfq_moe_block_gemm(a_q, a_scales, sorted_pairs, expert_offsets, topk, w_q, w
     _flat(w_q, "w_q", U8_CODES, E * N * K)
     _scales(a_scales, "a_scales", a_layout, a_scale_ld, T, K // 128, write=False)
     _flat(w_scales, "w_scales", ("float32",), E * (N // 128) * (K // 128))
-    _flat(sorted_pairs, "sorted_pairs", ("int32",), T * topk)
+    _flat(sorted_pairs, "sorted_pairs", ("int32",), T * topk, exact=False)
     _flat(expert_offsets, "expert_offsets", ("int32",), E + 1)
     _rows(out, "out", OUT_DTYPES, T * topk, N)
     _workspace(workspace, workspace_bytes)

@@ -279,7 +279,8 @@ bfq_status bfq_get_tile_candidate(const int32_t block_shape[2], bfq_dtype in_dty
 /* Group the pairs by expert (stable: ascending pair id within an expert), the routing step
  * the grouped GEMM reads. topk_ids [T][topk] int32 (device); expert_offsets [E+1] int32:
  * pairs of expert e are sorted_pairs[expert_offsets[e] .. expert_offsets[e+1]);
- * sorted_pairs [T*topk] int32. An id outside [0, E) goes after every expert (beyond
+ * sorted_pairs int32, at least T*topk entries (the first T*topk are written). An id
+ * outside [0, E) goes after every expert (beyond
  * expert_offsets[E]) and its pair is never computed. 1 <= E <= 1023; workspace of
  * bfq_moe_align_workspace_bytes bytes (may be NULL when that is 0). Asynchronous. */
 size_t     bfq_moe_align_workspace_bytes(int64_t T, int32_t topk, int32_t E);

@@ -91,14 +91,19 @@ def test_moe_and_debug_checks(bfq):
     _err(bfq, "3-D", g, a, sa, srt, off, topk, w[0], sw, out)
     _err(bfq, "dtype int8", g, a.view(torch.int8), sa, srt, off, topk, w, sw, out)
     _err(bfq, "last dimension", g, a, sa, srt, off, topk, w[:, :, :128], sw, out)
-    _err(bfq, "elements", g, a, sa, srt[:3], off, topk, w, sw, out)
+    _err(bfq, "at least", g, a, sa, srt[:3], off, topk, w, sw, out)
     _err(bfq, "elements", g, a, sa, srt, off[:E], topk, w, sw, out)
     _err(bfq, "dtype int64", g, a, sa, srt.long(), off, topk, w, sw, out)
     _err(bfq, "shape", g, a, sa, srt, off, topk, w, sw, out[:T])
     _err(bfq, "device", g, a, sa, srt, off, topk, w, sw, out)
+    # a pair list preallocated for more tokens is fine (only the first T*topk entries are read)
+    big = torch.zeros(16 * T * topk, dtype=torch.int32)
+    _err(bfq, "device", g, a, sa, big, off, topk, w, sw, out)
     ids = torch.zeros((T, topk), dtype=torch.int32)
     _err(bfq, "dtype int64", bfq.bfq_moe_align, ids.long(), E, off, srt)
     _err(bfq, "elements", bfq.bfq_moe_align, ids, E, off[:2], srt)
+    _err(bfq, "at least", bfq.bfq_moe_align, ids, E, off, srt[:T * topk - 1])
+    _err(bfq, "device", bfq.bfq_moe_align, ids, E, off, big)
     _err(bfq, "device", bfq.bfq_moe_align, ids, E, off, srt)
     ai = torch.zeros((T, K), dtype=torch.int8)
     _err(bfq, "elements", bfq.bfq_debug_block_partials_i32, ai, torch.zeros((N, K), dtype=torch.int8),
