@@ -59,8 +59,11 @@ def build(jobs: int = 8) -> str:
 # A build whose host code (argument validation, tile selection, the tile-table parser) runs
 # under AddressSanitizer and UndefinedBehaviorSanitizer; the device code is the same. Loaded
 # through BFQ_LIBRARY by a process that preloads the sanitizer runtime (sanitizer_runtime());
-# the CPU tests run against it (tests/test_sanitizers.py).
-ASAN_LIB_PATH = os.path.join(HERE, "libbfq_asan.so")
+# the CPU tests run against it (tests/test_sanitizers.py). It lives in the build folder, not
+# beside the package (no GPU run loads it), so its loader names the tile table with
+# BFQ_TILE_TABLE (TABLE_PATH).
+ASAN_LIB_PATH = os.path.join(REPO, "_build", "sanitize", "libbfq_asan.so")
+TABLE_PATH = os.path.join(HERE, "tables", "gfx950.json")
 HOST_SOURCES = ("api.cpp", "tile_table.cpp")
 SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
@@ -94,6 +97,7 @@ def build_sanitized(jobs: int = 8) -> str:
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(_compile, todo))
+    os.makedirs(os.path.dirname(ASAN_LIB_PATH), exist_ok=True)
     tmp = ASAN_LIB_PATH + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs, "-ldl",
            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",

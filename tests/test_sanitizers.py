@@ -24,6 +24,7 @@ def test_cpu_suite_under_asan_and_ubsan(tmp_path):
     env["ASAN_OPTIONS"] = f"detect_leaks=0:log_path={log}"
     env["UBSAN_OPTIONS"] = f"print_stacktrace=1:log_path={log}"
     env["BFQ_LIBRARY"] = lib
+    env["BFQ_TILE_TABLE"] = build.TABLE_PATH      # the library is not beside the package
     env["ORACLE_LIBRARY"] = orc
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-m", "not gpu", "-p",
                         "no:cacheprovider", "--ignore", os.path.join(HERE, "test_sanitizers.py"),
