@@ -42,6 +42,13 @@ WORKLOADS = {
     "int8": {"shapes": [(1536, 7168)], "M": [1, 16, 128, 1024, 4096], "qtype": "int8",
              "desc": "int8_w8a8 block variant N=1536 K=7168"},
     "tiny": {"shapes": [(1536, 1536)], "M": [8], "qtype": "fp8", "desc": "M=8 N=1536 K=1536"},
+    # one GPU's share of an 8-way tensor-parallel split: the 24576x7168 layer column-parallel
+    # (N/8 per GPU, no exchange) and the 7168x18432 layer row-parallel (K/8 per GPU, whose
+    # fp32 partials an all-reduce would then sum: not measured here)
+    "tp8": {"shapes": [(3072, 7168), (7168, 2304)], "M": M_GRID, "qtype": "fp8",
+            "desc": "per-GPU shard shapes of 8-way tensor parallelism: N=3072 K=7168 "
+                    "(column-parallel 24576x7168) and N=7168 K=2304 (row-parallel 7168x18432), "
+                    "M grid 1..4096"},
     "moe": {"kind": "moe", "E": 256, "topk": 8, "shapes": [(4096, 7168)], "M": M_GRID,
             "qtype": "fp8",
             "desc": "MoE grouped block-FP8, DeepSeek-V3 routed experts E=256 top-8, gate+up "

@@ -41,7 +41,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_TABLE = os.path.join(HERE, "tables", "gfx950.json")
 M_GRID = [1, 2, 4, 8, 16, 24, 32, 48, 64, 96, 128, 256, 512, 1024, 1536, 2048, 3072, 4096]
 DEFAULT_SHAPES = {"fp8": [(24576, 7168), (7168, 1536), (1536, 7168), (4096, 7168), (7168, 18432),
-                          (18432, 7168), (1536, 1536)],
+                          (18432, 7168), (1536, 1536), (3072, 7168), (7168, 2304)],
                   "int8": [(1536, 7168)]}
 SPLITS = (1, 2, 3, 4, 6, 8, 12, 16)
 NUM_CUS = 256

@@ -77,7 +77,7 @@ def main():
     shapes = ([tuple(int(v) for v in s.split(",")) for s in args.shapes] if args.shapes else
               ([(1536, 7168)] if args.dtype == "int8" else
                [(24576, 7168), (7168, 1536), (1536, 7168), (4096, 7168), (7168, 18432),
-                (18432, 7168), (1536, 1536)]))
+                (18432, 7168), (1536, 1536), (3072, 7168), (7168, 2304)]))
     data = {}
     if os.path.exists(args.out):
         with np.load(args.out, allow_pickle=False) as old:

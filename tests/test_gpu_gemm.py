@@ -574,6 +574,14 @@ def test_timed_config_dense_4096(bfq, orc, N, K):
     _sampled_check(bfq, orc, 4096, N, K, 4096, "fp8", layout="packed", scale_layout="col")
 
 
+@pytest.mark.parametrize("N,K", [(3072, 7168), (7168, 2304)])
+@pytest.mark.parametrize("M", [1, 64, 512, 4096])
+def test_timed_config_tp8_shards(bfq, orc, M, N, K):
+    """The per-GPU shard shapes of 8-way tensor parallelism the benchmark also times."""
+    print(f"timed config M={M} N={N} K={K} packed col-major", flush=True)
+    _sampled_check(bfq, orc, M, N, K, 4096, "fp8", layout="packed", scale_layout="col")
+
+
 @pytest.mark.parametrize("M", [1, 128, 4096])
 def test_timed_config_int8(bfq, orc, M):
     print(f"timed config int8 M={M} N=1536 K=7168 packed col-major", flush=True)
