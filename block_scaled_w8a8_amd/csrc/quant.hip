@@ -35,12 +35,26 @@ __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
 }
 
-// Encode 8 values x[0..7] divided by scale s; finite-amax groups only.
+// Encode 8 values x[0..7] divided by scale s; finite-amax groups only (|x| <= amax of the
+// group or row that s was formed from). The quotient is taken as q = x * r with r = 1 / s,
+// one IEEE division per lane instead of one per value, then corrected once by the exact
+// remainder e = x - q * s (a fused multiply-add): q + e * r, with the sign of x (the
+// correction never changes the sign of a nonzero value; it restores -0, which q + e * r would
+// turn into +0). For every finite bf16 amax and every bf16 x with |x| <= amax, with fp32 or
+// power-of-two scales and either code type, the code of this value equals the code of the
+// IEEE quotient x / s (checked exhaustively on the CPU: tests/native/quotient_codes.c); where
+// the two fp32 values differ at all (subnormal x in a group whose amax is below eps) both
+// encode to zero. (r names the return value below; rs is the reciprocal.)
 template <int QT>
 __device__ __forceinline__ uint2 encode8(const float* x, float s) {
+    const float rs = 1.0f / s;                         // IEEE division, once per lane
     float y[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = x[i] / s;     // IEEE division
+    for (int i = 0; i < 8; ++i) {
+        const float q = x[i] * rs;
+        const float e = __builtin_fmaf(-q, s, x[i]);   // exact
+        y[i] = __builtin_copysignf(__builtin_fmaf(e, rs, q), x[i]);
+    }
     uint2 r;
     if constexpr (QT == Q_FP8) {
         r.x = enc_fp8x4(y[0], y[1], y[2], y[3]);
