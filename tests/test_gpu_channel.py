@@ -96,7 +96,7 @@ def test_quant_per_token_scale_layouts(bfq, orc, layout):
     M, K = 45, 1536
     x = synth.activations(M, K, seed=8)
     lay = bfq.BFQ_SCALES_ROW_MAJOR if layout == "row" else bfq.BFQ_SCALES_COL_MAJOR
-    q = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+    q = torch.full((M, K), 0x55, dtype=torch.uint8, device=DEV)
     if layout == "row":
         s = torch.full((M, 3), float("nan"), device=DEV)
     else:

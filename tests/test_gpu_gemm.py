@@ -382,8 +382,9 @@ def _sampled_check(bfq, orc, M, N, K, m_max, qname, n_samples=4096, tile=None, l
     else:
         a_lay, sa_arg = bfq.BFQ_SCALES_ROW_MAJOR, sa[:M]
     qw_arg = qwp if layout == "packed" else qw
-    out32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
-    out16 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    # NaN-prefilled, so an element a tile fails to write cannot pass on stale memory
+    out32 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    out16 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
     if tile is None:
         st, tile = bfq.bfq_select_tile(M, N, K, bfq._qdtype(qa), bfq.BFQ_FP32, w_layout=wl,
                                        scale_fmt=sfmt)

@@ -112,8 +112,9 @@ def test_quant_weight_blocks_bit_exact(bfq, orc, N, K, qname, sfmt):
     ot = orc.FP8 if qname == "fp8" else orc.INT8
     w = synth.weights(N, K, seed=N ^ K)
     wg = w.to("cuda:0")
-    q = torch.empty((N, K), dtype=torch.uint8 if qname == "fp8" else torch.int8, device="cuda:0")
-    s = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda:0")
+    # sentinel-filled, so an element the kernel fails to write cannot pass on stale memory
+    q = torch.full((N, K), 0x55, dtype=torch.uint8 if qname == "fp8" else torch.int8, device="cuda:0")
+    s = torch.full((N // 128, K // 128), float("nan"), dtype=torch.float32, device="cuda:0")
     bfq.bfq_quant_weight_blocks(wg, q, s, scale_fmt=sfmt)
     torch.cuda.synchronize()
     qo, so = orc.quant_blocks(w.numpy(), qtype=ot, scale_fmt=sfmt)
@@ -130,8 +131,8 @@ def test_weight_blocks_special_values(bfq, orc, sfmt):
     w[201, 8] = -np.inf
     w[130:256, 130:256] *= 1e-30
     wg = torch.from_numpy(w).to("cuda:0")
-    q = torch.empty((256, 256), dtype=torch.uint8, device="cuda:0")
-    s = torch.empty((2, 2), dtype=torch.float32, device="cuda:0")
+    q = torch.full((256, 256), 0x55, dtype=torch.uint8, device="cuda:0")
+    s = torch.full((2, 2), float("nan"), dtype=torch.float32, device="cuda:0")
     bfq.bfq_quant_weight_blocks(wg, q, s, scale_fmt=sfmt)
     torch.cuda.synchronize()
     qo, so = orc.quant_blocks(w, scale_fmt=sfmt)
@@ -157,7 +158,7 @@ def _encode_class_inputs():
 def test_device_fp8_encoder_all_rounding_classes(bfq, orc):
     x = _encode_class_inputs()
     xg = torch.from_numpy(x).to("cuda:0")
-    out = torch.empty(x.size, dtype=torch.uint8, device="cuda:0")
+    out = torch.full((x.size,), 0x55, dtype=torch.uint8, device="cuda:0")
     bfq.bfq_debug_encode(xg, out, bfq.BFQ_E4M3FN)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
@@ -171,7 +172,7 @@ def test_device_int8_encoder(bfq, orc):
     x = np.concatenate([np.arange(-300, 300, 0.25, dtype=np.float32),
                         (rng.standard_normal(1 << 20) * 100).astype(np.float32)])
     xg = torch.from_numpy(x).to("cuda:0")
-    out = torch.empty(x.size, dtype=torch.int8, device="cuda:0")
+    out = torch.full((x.size,), 0x55, dtype=torch.int8, device="cuda:0")
     bfq.bfq_debug_encode(xg, out, bfq.BFQ_INT8)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), orc.int8_encode_array(x))
@@ -200,7 +201,7 @@ def test_quant_tokens_packed_words_bit_exact(bfq, orc, M, K, qname):
     G, Mp = K // 128, (M + 3) // 4 * 4
     ld = Mp + 3
     dev = torch.device("cuda:0")
-    q = torch.empty((M, K), dtype=torch.uint8 if qname == "fp8" else torch.int8, device=dev)
+    q = torch.full((M, K), 0x55, dtype=torch.uint8 if qname == "fp8" else torch.int8, device=dev)
     words = torch.full(((G + 3) // 4, ld), -1431655766, dtype=torch.int32, device=dev)  # 0xAAAAAAAA
     bfq.bfq_quant_tokens(x.to(dev), q, words, layout=bfq.BFQ_SCALES_PACKED_UE8M0, scale_ld=ld,
                          scale_fmt=bfq.BFQ_SCALE_UE8M0)
