@@ -10,6 +10,9 @@ Each smaller M takes the first M rows of the M_max draw, so inputs nest across M
 MoE routing (the expert dimension of the config page's MoE tables, §5): each token picks
 topk distinct experts of E, uniformly: the topk largest of E uniform draws (generator
 seed + 3); expert weights are E independent weight draws (seed + 1000 + e).
+GEMM inputs drawn directly, for cases too large to quantize on the host (a GEMM takes any
+codes and positive scales): codes uniform over the code points (int8 -127..127; fp8 every
+byte but the two NaN encodings 0x7F and 0xFF), scales 2^u with u uniform in [-10, -4).
 """
 from __future__ import annotations
 
@@ -67,3 +70,21 @@ def expert_weight_on(device, e: int, N: int, K: int, seed: int = 0) -> torch.Ten
     g = torch.Generator(device=device)
     g.manual_seed(int(seed) + 1000 + int(e))
     return torch.randn((N, K), generator=g, device=device, dtype=torch.float32) * 0.02
+
+
+def codes(rows: int, cols: int, int8: bool = False, seed: int = 0, device="cpu") -> torch.Tensor:
+    """[rows, cols] uniform random codes drawn on `device` (int8, or uint8 e4m3fn bytes)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    if int8:
+        return torch.randint(-127, 128, (rows, cols), generator=g, device=device, dtype=torch.int8)
+    r = torch.randint(0, 254, (rows, cols), generator=g, device=device, dtype=torch.uint8)
+    return r + (r >= 0x7F).to(torch.uint8)      # 0..0xFE without 0x7F
+
+
+def scales(rows: int, cols: int, seed: int = 0, device="cpu") -> torch.Tensor:
+    """fp32 [rows, cols] = 2^u, u uniform in [-10, -4), drawn on `device`."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    u = torch.rand((rows, cols), generator=g, device=device, dtype=torch.float32)
+    return torch.exp2(-10.0 + 6.0 * u)
