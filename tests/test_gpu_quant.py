@@ -167,6 +167,38 @@ def test_device_fp8_encoder_all_rounding_classes(bfq, orc):
     assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(ref[i])) for i in bad[:8]]
 
 
+@pytest.mark.parametrize("qname", ["fp8", "int8"])
+def test_device_encoder_every_fp32_pattern(bfq, orc, qname):
+    """The device encoder on every fp32 bit pattern of its stated domain (e4m3fn: finite with
+    |x| < 464, subnormals and both zeros included; int8: every finite value), swept over all
+    2^32 patterns in 16 chunks of 2^28, against the oracle's encoder (itself pinned on all
+    2^32 patterns to a brute-force search from the format definition): every code equal."""
+    qd = bfq.BFQ_E4M3FN if qname == "fp8" else bfq.BFQ_INT8
+    enc = orc.e4m3_encode_array if qname == "fp8" else orc.int8_encode_array
+    limit = 0x43E80000 if qname == "fp8" else 0x7F800000    # |x| below 464 / below +Inf
+    CH = 1 << 28
+    out = torch.empty(CH, dtype=torch.uint8 if qname == "fp8" else torch.int8, device="cuda:0")
+    covered = 0
+    for hi in range(16):
+        start = hi * CH
+        print(f"{qname} encoder patterns {start:#010x}..{start + CH - 1:#010x}", flush=True)
+        bits = torch.arange(start, start + CH, dtype=torch.int64, device="cuda:0")
+        bits = torch.where(bits >= (1 << 31), bits - (1 << 32), bits).to(torch.int32)
+        out.fill_(0x55)
+        bfq.bfq_debug_encode(bits.view(torch.float32), out, qd)
+        torch.cuda.synchronize()
+        del bits
+        got = out.cpu().numpy()
+        u = np.arange(start, start + CH, dtype=np.uint64).astype(np.uint32)
+        keep = (u & np.uint32(0x7FFFFFFF)) < np.uint32(limit)
+        covered += int(keep.sum())
+        ref = enc(u.view(np.float32))
+        bad = np.nonzero(keep & (got != ref))[0]
+        assert bad.size == 0, [(hex(start + int(i)), int(got[i]), int(ref[i])) for i in bad[:8]]
+    expect = 2 * limit
+    assert covered == expect, (covered, expect)
+
+
 def test_device_int8_encoder(bfq, orc):
     rng = np.random.default_rng(3)
     x = np.concatenate([np.arange(-300, 300, 0.25, dtype=np.float32),
