@@ -38,6 +38,14 @@ bfq_status fail(bfq_status s, const std::string& msg) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Largest output count (M * N, grouped: T * topk * N) the GEMMs take: 2^40 elements, far past
+// any device memory, keeps split-K workspace sizes (256 splits of fp32) and the reduce
+// kernel's one-dimensional grid within range.
+constexpr int64_t kMaxOutputs = int64_t(1) << 40;
+
+// a * b >= kMaxOutputs for positive a, b, without overflow
+bool too_many_outputs(int64_t a, int64_t b) { return a > 0 && b > 0 && a > (kMaxOutputs - 1) / b; }
+
 // ------------------------------------------------------------------ tile table ----
 std::mutex g_table_mu;
 TileTable g_table;
@@ -355,6 +363,7 @@ bool wlayout_ok(bfq_weight_layout w) { return w == BFQ_W_ROW_MAJOR || w == BFQ_W
 bool sfmt_ok(bfq_scale_format f) { return f == BFQ_SCALE_FP32 || f == BFQ_SCALE_UE8M0; }
 
 size_t workspace_for(int64_t M, int64_t N, const bfq_tile& t) {
+    if (too_many_outputs(M, N)) return SIZE_MAX;   // a shape the GEMM rejects
     if (t.variant == 2) {
         if (M == 0 || t.bm <= 0 || t.bn <= 0) return 0;
         return streamk_workspace_bytes(t.bm, t.bn, streamk_grid());
@@ -581,6 +590,7 @@ bfq_status block_gemm_impl(const void* a_q, const float* a_scales, bfq_scale_lay
         return fail(BFQ_ERR_SHAPE, "need M >= 0 and N, K positive multiples of 128");
     if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > (1 << 23))
         return fail(BFQ_ERR_SHAPE, "M and N must be below 2^31 and K at most 2^23");
+    if (too_many_outputs(M, N)) return fail(BFQ_ERR_SHAPE, "M * N must be below 2^40");
     if (a_scale_ld > (1 << 23)) return fail(BFQ_ERR_SHAPE, "a_scale_ld must be at most 2^23");
     if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(out, 16) || !aligned(a_scales, 4) ||
         !aligned(w_scales, 4) || !aligned(workspace, 16))
@@ -808,6 +818,7 @@ bfq_status bfq_moe_select_tile(int64_t T, int32_t topk, int32_t E, int64_t N, in
 
 size_t bfq_moe_gemm_workspace_bytes(int64_t T, int32_t topk, int64_t N, const bfq_tile* tile) {
     if (!tile || T <= 0 || topk <= 0 || N <= 0 || tile->split_k <= 1) return 0;
+    if (too_many_outputs(T, topk) || too_many_outputs(T * topk, N)) return SIZE_MAX;
     return (size_t)tile->split_k * (size_t)(T * topk) * (size_t)N * sizeof(float);
 }
 
@@ -838,6 +849,7 @@ bfq_status bfq_moe_block_gemm(const void* a_q, const float* a_scales, bfq_scale_
     // kernels do
     if (T * K >= (int64_t(1) << 31) || P > 0x7FFFFFFF || N > 0x7FFFFFFF)
         return fail(BFQ_ERR_SHAPE, "T * K must be below 2^31 bytes");
+    if (too_many_outputs(P, N)) return fail(BFQ_ERR_SHAPE, "T * topk * N must be below 2^40");
     if (K > (1 << 23)) return fail(BFQ_ERR_SHAPE, "K must be at most 2^23");
     if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(out, 16) || !aligned(a_scales, 4) ||
         !aligned(w_scales, 4) || !aligned(workspace, 16) || !aligned(sorted_pairs, 4) ||

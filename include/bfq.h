@@ -20,9 +20,9 @@
  *    was launched and no output was touched; bfq_last_error() holds a detail string
  *    (thread-local). A positive status is success with a warning.
  *  - M = 0 is valid and launches nothing.
- *  - Shapes are int64; K and N must be multiples of 128 (GEMM: K <= 2^23, scale ld <= 2^23,
- *    and the activation scales of 256 tokens over all K blocks span less than 4 GiB), and
- *    x/q/w/out 16-byte aligned.
+ *  - Shapes are int64; K and N must be multiples of 128 (GEMM: M, N < 2^31, M * N < 2^40,
+ *    K <= 2^23, scale ld <= 2^23, and the activation scales of 256 tokens over all K blocks
+ *    span less than 4 GiB), and x/q/w/out 16-byte aligned.
  *  - Two calls on one stream are ordered; calls on different streams that share an output
  *    or workspace race.
  */
@@ -198,7 +198,8 @@ int32_t bfq_get_batch_invariant(void);
 
 /* Bytes of device workspace bfq_block_gemm needs for this shape and tile (split-K fp32
  * partials: split_k * M * N * 4 when split_k > 1; stream-K: two partial tiles per compute
- * unit; else 0). tile NULL -> the tile selected for e4m3fn codes in the row-major layout. */
+ * unit; else 0). tile NULL -> the tile selected for e4m3fn codes in the row-major layout.
+ * SIZE_MAX when M * N >= 2^40, a shape bfq_block_gemm rejects. */
 size_t bfq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const bfq_tile* tile);
 
 /* Block-scaled GEMM ([BENCH] §4.2, w8a8 block-scaled matmul):
@@ -295,7 +296,8 @@ bfq_status bfq_moe_select_tile(int64_t T, int32_t topk, int32_t E, int64_t N, in
                                const int32_t block_shape[2], bfq_dtype in_dtype,
                                bfq_dtype out_dtype, bfq_weight_layout w_layout,
                                bfq_scale_format scale_fmt, bfq_tile* tile_out);
-/* split_k * T * topk * N * 4 bytes when the tile's split_k > 1, else 0. */
+/* split_k * T * topk * N * 4 bytes when the tile's split_k > 1, else 0; SIZE_MAX when
+ * T * topk * N >= 2^40, a shape bfq_moe_block_gemm rejects. */
 size_t     bfq_moe_gemm_workspace_bytes(int64_t T, int32_t topk, int64_t N, const bfq_tile* tile);
 
 /* Grouped GEMM over the expert groups of bfq_moe_align.
@@ -306,7 +308,8 @@ size_t     bfq_moe_gemm_workspace_bytes(int64_t T, int32_t topk, int64_t N, cons
  *   bfq_pack_weights, one after the other); w_scales [E][N/128][K/128];
  *   out [T*topk][N] in pair order; rows of pairs with an expert outside [0, E) are not written
  *   with split_k = 1 and are unspecified with split_k > 1.
- *   tile NULL -> bfq_moe_select_tile. Variants 0 and 1 (grouped forms); T * K < 2^31. */
+ *   tile NULL -> bfq_moe_select_tile. Variants 0 and 1 (grouped forms); T * K < 2^31,
+ *   T * topk * N < 2^40. */
 bfq_status bfq_moe_block_gemm(const void* a_q, const float* a_scales, bfq_scale_layout a_layout,
                               int64_t a_scale_ld, const int32_t* sorted_pairs,
                               const int32_t* expert_offsets, int32_t topk, const void* w_q,

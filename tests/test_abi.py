@@ -57,6 +57,19 @@ def test_gemm_validation_errors_without_launch(bfq):
     assert _gemm(bfq, a_scales=FAKE + 2) == bfq.BFQ_ERR_ALIGN
     assert _gemm(bfq, a_scale_ld=10) == bfq.BFQ_ERR_SHAPE
     assert _gemm(bfq, M=64, a_layout=1, a_scale_ld=63) == bfq.BFQ_ERR_SHAPE
+    # at most 2^40 outputs: 2^21 x 2^19 is rejected, one row fewer passes the shape checks
+    big = dict(N=1 << 19, K=128, a_scale_ld=1)
+    assert _gemm(bfq, M=1 << 21, **big) == bfq.BFQ_ERR_SHAPE
+    assert "2^40" in bfq.last_error()
+    # the size queries answer SIZE_MAX for such shapes (never a wrapped product)
+    size_max = ctypes.c_size_t(-1).value
+    t = bfq.bfq_tile(variant=0, bm=256, bn=256, bk=128, split_k=256, waves_m=4, waves_n=2,
+                     stages=2, group_m=8, sched=0, raster=0)
+    assert bfq.lib.bfq_gemm_workspace_bytes(1 << 21, 1 << 19, 128, ctypes.byref(t)) == size_max
+    assert bfq.lib.bfq_gemm_workspace_bytes(1 << 40, 1 << 40, 128, ctypes.byref(t)) == size_max
+    assert bfq.lib.bfq_gemm_workspace_bytes((1 << 21) - 1, 1 << 19, 128, ctypes.byref(t)) == \
+        256 * ((1 << 21) - 1) * (1 << 19) * 4
+    assert bfq.lib.bfq_moe_gemm_workspace_bytes(1 << 40, 8, 1 << 30, ctypes.byref(t)) == size_max
     assert _gemm(bfq, a_layout=7) == bfq.BFQ_ERR_ARG
     assert _gemm(bfq, w_layout=2) == bfq.BFQ_ERR_ARG
     assert _gemm(bfq, scale_fmt=2) == bfq.BFQ_ERR_ARG
