@@ -270,6 +270,9 @@ def tune_shape(N, K, qname, grid, budget_s, reference, w_layout="row", scales="f
         trials.sort(key=lambda t: t[0])
         for us, d in trials[:4]:
             log(f"    {us:9.2f} us  {d}")
+        if best is None:
+            raise RuntimeError(f"no candidate passed the parity gate for N={N} K={K} {qname} "
+                               f"M={M} within {budget_s} s")
         results[M] = (best[0], best[1].as_dict())
         d = best[1].as_dict()
         log(f"  N={N} K={K} M={M:5d}: {best[0]:9.2f} us  variant={d['variant']} bm={d['bm']} "
@@ -400,6 +403,9 @@ def cmd_tune_moe(args):
             us = prob.time_us(T, tile)
             if best is None or us < best[0]:
                 best = (us, tile)
+        if best is None:
+            raise RuntimeError(f"no grouped candidate passed the parity gate for E={args.E} N={N} "
+                               f"K={K} T={T} within {args.budget} s")
         results[T] = (best[0], best[1].as_dict())
         d = best[1].as_dict()
         log(f"  moe E={args.E} N={N} K={K} T={T:5d}: {best[0]:9.2f} us  variant={d['variant']} "
