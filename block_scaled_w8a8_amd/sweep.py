@@ -10,6 +10,8 @@
                                              [--w-layout row|packed] [--scales fp32|ue8m0]
                                              [--grid T ...] [--merge]
   python -m block_scaled_w8a8_amd.sweep copy  [--bytes N]   (byte-counter calibration)
+  python -m block_scaled_w8a8_amd.sweep libref --M 4096 --N 24576 --K 7168 [--eager 10]
+                                             (the vendor library's per-tensor fp8 GEMM)
 
 `tune` follows the tuning flow of the config-mechanism page ("vLLM 量化 Kernel 配置机制 ...",
 §3.3): for every (N, K) and every M of the 18-point grid, every compiled kernel configuration
@@ -534,6 +536,48 @@ def cmd_copy(args):
     print(json.dumps({"copy_bytes": n, "iters": args.iters}), flush=True)
 
 
+def cmd_libref(args):
+    """A reference point, not this library: the vendor library's fp8 GEMM with one scale per
+    tensor (torch._scaled_mm, hipBLASLt on ROCm) on codes of the same shape, bf16 out. torch
+    offers no 1x128 / 128x128 block-scaled form on ROCm, so this is the nearest library
+    kernel. Times --iters launches (weights rotated like `run`) or, with --eager, only
+    launches them (for a profiler)."""
+    import torch
+
+    from . import synth
+    dev = "cuda:0"
+    M, N, K = args.M, args.N, args.K
+    a = synth.codes(M, K, seed=1, device=dev).view(torch.float8_e4m3fn)
+    copies = [synth.codes(N, K, seed=2 + r, device=dev).view(torch.float8_e4m3fn)
+              for r in range(args.rotate)]
+    one = torch.ones((), device=dev)
+
+    def f(i):
+        return torch._scaled_mm(a, copies[i % len(copies)].t(), scale_a=one, scale_b=one,
+                                out_dtype=torch.bfloat16)
+    f(0)
+    torch.cuda.synchronize()
+    if args.eager:
+        for i in range(args.eager):
+            f(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"M": M, "N": N, "K": K, "eager": args.eager}), flush=True)
+        return
+    t0 = time.time()
+    while time.time() - t0 < 1.0:
+        f(0)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.iters):
+        f(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.iters
+    print(json.dumps({"M": M, "N": N, "K": K, "us": round(us, 2),
+                      "tflops": round(2 * M * N * K / us / 1e6, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -576,8 +620,16 @@ def main():
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=1 << 30)
     c.add_argument("--iters", type=int, default=3)
+    lr = sub.add_parser("libref")
+    lr.add_argument("--M", type=int, required=True)
+    lr.add_argument("--N", type=int, required=True)
+    lr.add_argument("--K", type=int, required=True)
+    lr.add_argument("--iters", type=int, default=20)
+    lr.add_argument("--rotate", type=int, default=3)
+    lr.add_argument("--eager", type=int, default=0, help="launch this many times without timing")
     args = ap.parse_args()
-    {"tune": cmd_tune, "tune-moe": cmd_tune_moe, "run": cmd_run, "copy": cmd_copy}[args.cmd](args)
+    {"tune": cmd_tune, "tune-moe": cmd_tune_moe, "run": cmd_run, "copy": cmd_copy,
+     "libref": cmd_libref}[args.cmd](args)
 
 
 if __name__ == "__main__":
